@@ -1,0 +1,28 @@
+"""fp64 CPU oracle for the SO(2) equivariant message-passing layer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything from here; the
+product path (the HIP library and its Python binding) never does, and shares
+no code, table or constant with it.
+
+Every function follows a passage of the pages it is written from:
+
+* "Distributed Equivariant Graph Neural Networks for Large-Scale Electronic
+  Structure Prediction" (pith.science review of arXiv 2507.03840), "What
+  carries the argument": the incoming-edge layout, attention and aggregation
+  over the edges directed into a node.
+* "MALOQ" (arXiv 2606.28911v1): Sec. III (workflow of Fig. 2(a)), Sec. III-B1
+  Eq. (1) (Clebsch-Gordan decomposition of Hamiltonian sub-blocks),
+  Sec. III-C1 and Fig. 3(b,c) (Wigner-D rotation of every edge to +y),
+  Sec. III-D (messages n_i (+) n_j; target node owns its edges),
+  Sec. II-B1 (SO(3) -> SO(2) reduction, eSCN).
+
+Where the pages leave a step open the plainest reading is taken; each such
+reading is named in the docstring of the function that takes it.
+
+Modules:
+  neighbors  -- brute-force periodic / open cutoff graph, destination-sorted CSR
+  so3        -- real spherical harmonics, Wigner-D, edge frame, real CG couplings
+  layer      -- layer forward and analytic backward
+  decode     -- Label -> Matrix: Hamiltonian blocks from irreps
+"""

@@ -1,0 +1,343 @@
+"""Seeded synthetic inputs for the SO(2) message-passing layer.
+
+This module only draws random numbers and lays them out; it holds none of the
+layer's arithmetic.  Both the fp64 oracle (``oracle/``) and the HIP path read
+what it produces, so the two sides see bit-identical inputs.
+
+The workloads stand in for the DFT structures of the pages (amorphous HfO2
+and GeSbTe cells, MALOQ Table II; the 8,064-atom GST cell of the
+"Distributed Equivariant GNNs" review, abstract and GST application), whose
+data is not available: positions come from random sequential addition (RSA)
+with a 1.8 A minimum spacing, node irreps are N(0,1) and weights are
+N(0, 1/fan_in).
+
+Streams per config seed s (``numpy.random.default_rng``): ``s`` draws the
+positions (RSA proposals, owned atoms then ghosts) and then the species;
+``(s, 1)`` the node irreps x; ``(s, 2)`` the layer weights in packed order,
+layer by layer; ``(s, 3)`` the decode weights; ``(s, 4)`` the cotangent G.
+"""
+from __future__ import annotations
+
+import hashlib
+import json
+import os
+from dataclasses import dataclass, field, asdict
+
+import numpy as np
+
+__all__ = ["Config", "CONFIGS", "Structure", "make_structure", "make_layer_inputs",
+           "make_decode_weights", "make_cotangent", "layer_weight_sizes",
+           "round_storage", "bf16_round"]
+
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    seed: int
+    counts: tuple            # atoms per species (owned atoms)
+    box: tuple               # periodic cell, or owned slab extent when open
+    periodic: bool
+    r_cut: float
+    lmax: int
+    mmax: int
+    C: int
+    n_rbf: int = 8
+    storage: str = "f32"     # "f32" or "bf16"
+    layers: int = 1
+    min_sep: float = 1.8
+    halo: float = 0.0        # ghost shell thickness around an open slab
+    geometry_seed: int | None = None   # reuse another config's positions/x/weights
+    note: str = ""
+
+    @property
+    def n_owned(self):
+        return int(sum(self.counts))
+
+    @property
+    def K(self):
+        return (self.lmax + 1) ** 2
+
+
+CONFIGS = {
+    "tiny": Config("tiny", 1, (32, 32), (9.0, 9.0, 9.0), True, 5.0, 2, 2, 8,
+                   note="64 atoms, 2 species Bernoulli(1/2), 9 A periodic cube, r_c 5 A"),
+    "tiny_l4": Config("tiny_l4", 1, (32, 32), (9.0, 9.0, 9.0), True, 5.0, 4, 2, 8,
+                      note="tiny geometry at lmax 4 / mmax 2 / C 8 (m-truncation, decode)"),
+    "hfo2": Config("hfo2", 2, (1000, 2000), (32.8, 32.8, 32.8), True, 8.0, 4, 2, 64,
+                   note="HfO2-like: 1,000 Hf + 2,000 O in a 32.8 A periodic cube, r_c 8 A"),
+    "gst": Config("gst", 3, (1792, 1792, 4480), (62.5, 62.5, 62.5), True, 10.0, 4, 2, 128,
+                  storage="bf16", layers=3,
+                  note="GeSbTe-like: 8,064 atoms in a 62.5 A periodic cube, r_c 10 A, 3 layers"),
+    "halo": Config("halo", 4, (10000, 10000, 10000), (100.0, 100.0, 60.0), False, 8.0, 4, 2, 64,
+                   halo=8.0,
+                   note="one GPU's share: 30,000 owned atoms in a 100x100x60 A slab, "
+                        "ghost sources in the 8 A shell, open boundary"),
+    "train": Config("train", 5, (1000, 2000), (32.8, 32.8, 32.8), True, 8.0, 4, 2, 64,
+                    geometry_seed=2,
+                    note="HfO2-like training step: fwd + bwd + Hamiltonian blocks"),
+}
+
+# Species are drawn as a random assignment of the fixed counts, except for the
+# tiny cell whose two species are Bernoulli(1/2).
+_BERNOULLI = {"tiny", "tiny_l4"}
+
+
+def bf16_round(a):
+    """Round float32 values to the nearest bfloat16 (ties to even), kept as float32."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    u = (u + 0x7FFF + lsb) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).reshape(a.shape)
+
+
+def round_storage(a, storage):
+    """Values as the storage type holds them, returned as float32."""
+    a = np.asarray(a, dtype=np.float64).astype(np.float32)
+    return bf16_round(a) if storage == "bf16" else a
+
+
+@dataclass
+class Structure:
+    pos: np.ndarray          # [n_src, 3] float64; owned atoms first, ghosts after
+    n_dst: int
+    box: np.ndarray          # [3] float64 (periodic cell; for open systems the padded extent)
+    periodic_mask: int       # bit a set = axis a periodic
+    species: np.ndarray      # [n_src] int32
+    r_cut: float
+
+    @property
+    def n_src(self):
+        return self.pos.shape[0]
+
+
+def _rsa(rng, n, lo, hi, min_sep, accepted, box, periodic, reject=None, batch=4096):
+    """Random sequential addition of n points uniform in [lo, hi).
+
+    A proposal is kept when its distance to every point already accepted is
+    at least min_sep (minimum image on periodic axes).  ``reject(p)`` may veto
+    proposals (used for the ghost shell around a slab).  Returns the grown
+    list of accepted points.
+    """
+    lo = np.asarray(lo, float)
+    hi = np.asarray(hi, float)
+    cell = min_sep
+    if periodic:
+        ncell = np.maximum(1, np.floor(np.asarray(box) / cell).astype(int))
+        origin = np.zeros(3)
+        csize = np.asarray(box) / ncell
+    else:
+        origin = lo - cell
+        span = (hi - lo) + 2 * cell
+        ncell = np.maximum(1, np.ceil(span / cell).astype(int))
+        csize = np.full(3, cell)
+    grid = {}
+
+    def key(p):
+        c = np.floor((p - origin) / csize).astype(int)
+        if periodic:
+            c %= ncell
+        return tuple(int(v) for v in c)
+
+    pts = list(accepted)
+    for i, p in enumerate(pts):
+        grid.setdefault(key(p), []).append(i)
+    ms2 = min_sep * min_sep
+    need = n
+    while need > 0:
+        props = lo + rng.random((batch, 3)) * (hi - lo)
+        for p in props:
+            if need == 0:
+                break
+            if reject is not None and reject(p):
+                continue
+            c = key(p)
+            ok = True
+            for dx in (-1, 0, 1):
+                for dy in (-1, 0, 1):
+                    for dz in (-1, 0, 1):
+                        cc = [c[0] + dx, c[1] + dy, c[2] + dz]
+                        if periodic:
+                            cc = [cc[a] % ncell[a] for a in range(3)]
+                        lst = grid.get(tuple(cc))
+                        if not lst:
+                            continue
+                        q = np.asarray([pts[j] for j in lst])
+                        d = p - q
+                        if periodic:
+                            d -= np.round(d / box) * box
+                        if np.min(np.einsum("ij,ij->i", d, d)) < ms2:
+                            ok = False
+                            break
+                    if not ok:
+                        break
+                if not ok:
+                    break
+            if ok:
+                grid.setdefault(c, []).append(len(pts))
+                pts.append(p.copy())
+                need -= 1
+    return pts
+
+
+_CACHE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), ".synth_cache")
+
+
+def _cache_path(tag):
+    h = hashlib.sha1(tag.encode()).hexdigest()[:16]
+    return os.path.join(_CACHE_DIR, f"{h}.npz")
+
+
+def _draw_structure(cfg: Config, rng) -> Structure:
+    box = np.asarray(cfg.box, dtype=np.float64)
+    n = cfg.n_owned
+    if cfg.periodic:
+        pts = _rsa(rng, n, np.zeros(3), box, cfg.min_sep, [], box, True)
+        pos = np.asarray(pts, dtype=np.float64)
+        n_src = n
+        mask = 7
+        extent = box
+    else:
+        pts = _rsa(rng, n, np.zeros(3), box, cfg.min_sep, [], box, False)
+        h = cfg.halo
+        lo, hi = -h * np.ones(3), box + h
+        vol_shell = np.prod(hi - lo) - np.prod(box)
+        density = n / np.prod(box)
+        n_ghost = int(round(density * vol_shell))
+
+        def inside_slab(p):
+            return bool(np.all(p >= 0.0) and np.all(p < box))
+
+        pts = _rsa(rng, n_ghost, lo, hi, cfg.min_sep, pts, box, False, reject=inside_slab)
+        pos = np.asarray(pts, dtype=np.float64)
+        n_src = pos.shape[0]
+        mask = 0
+        extent = hi - lo
+    # species
+    if cfg.name in _BERNOULLI:
+        sp_owned = (rng.random(n) < 0.5).astype(np.int32)
+    else:
+        sp_owned = np.repeat(np.arange(len(cfg.counts), dtype=np.int32), cfg.counts)
+        rng.shuffle(sp_owned)
+    if n_src > n:
+        sp_ghost = rng.integers(0, len(cfg.counts), size=n_src - n).astype(np.int32)
+        species = np.concatenate([sp_owned, sp_ghost])
+    else:
+        species = sp_owned
+    return Structure(pos=pos, n_dst=n, box=np.asarray(extent, np.float64) if not cfg.periodic else box,
+                     periodic_mask=mask, species=species, r_cut=float(cfg.r_cut))
+
+
+def layer_weight_sizes(lmax, mmax, C, n_rbf):
+    """Sizes (out, in) of the packed weight blocks of one layer, in packed order.
+
+    Order: W0, then (W_m1, W_m2) for m = 1..mmax, then W_rad [n_rbf][n_pairs][2C]
+    and w_att [C].  n_pairs = number of (m, l) with 0 <= m <= mmax, m <= l <= lmax.
+    """
+    blocks = [("W0", ((lmax + 1) * C, (lmax + 1) * 2 * C))]
+    for m in range(1, mmax + 1):
+        nl = lmax - m + 1
+        blocks.append((f"W{m}_1", (nl * C, nl * 2 * C)))
+        blocks.append((f"W{m}_2", (nl * C, nl * 2 * C)))
+    n_pairs = sum(lmax - m + 1 for m in range(mmax + 1))
+    blocks.append(("W_rad", (n_rbf, n_pairs * 2 * C)))
+    blocks.append(("w_att", (1, C)))
+    return blocks
+
+
+def _fan_in(name, shape):
+    if name.startswith("W") and name[1:2].isdigit() and name != "W0":
+        return 2 * shape[1]          # W_m1 and W_m2 both feed each output
+    if name == "W_rad":
+        return shape[0]
+    return shape[1]
+
+
+def _tag(cfg: Config, what):
+    return json.dumps({"cfg": asdict(cfg), "what": what, "v": 3}, sort_keys=True)
+
+
+def make_structure(cfg: Config | str, use_cache=True) -> Structure:
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    seed = cfg.geometry_seed if cfg.geometry_seed is not None else cfg.seed
+    gcfg = cfg
+    if cfg.geometry_seed is not None:
+        gcfg = next(c for c in CONFIGS.values() if c.seed == seed and c.geometry_seed is None)
+    tag = _tag(gcfg, "structure")
+    path = _cache_path(tag)
+    if use_cache and os.path.exists(path):
+        z = np.load(path)
+        return Structure(pos=z["pos"], n_dst=int(z["n_dst"]), box=z["box"],
+                         periodic_mask=int(z["mask"]), species=z["species"], r_cut=float(z["r_cut"]))
+    rng = np.random.default_rng(seed)
+    s = _draw_structure(gcfg, rng)
+    if use_cache:
+        os.makedirs(_CACHE_DIR, exist_ok=True)
+        np.savez(path, pos=s.pos, n_dst=s.n_dst, box=s.box, mask=s.periodic_mask,
+                 species=s.species, r_cut=s.r_cut)
+    return s
+
+
+def _stream_cfg(cfg: Config):
+    """The config whose seed draws positions, x and layer weights."""
+    if cfg.geometry_seed is None:
+        return cfg
+    return next(c for c in CONFIGS.values() if c.seed == cfg.geometry_seed and c.geometry_seed is None)
+
+
+def make_layer_inputs(cfg: Config | str, n_src=None, use_cache=True):
+    """Node irreps x [n_src][K][C] and the packed weights of each layer.
+
+    Returns (x, [w_layer0, w_layer1, ...]) as float32 arrays already rounded
+    to the storage type (bf16-representable when storage is bf16).
+    For a config that reuses another's geometry, x and the weights are the
+    other config's, drawn with its seed, but shaped by this config's
+    (lmax, mmax, C) which must match.
+    """
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    tag = _tag(cfg, "layer_inputs")
+    path = _cache_path(tag)
+    if use_cache and os.path.exists(path):
+        z = np.load(path)
+        return z["x"], [z[f"w{i}"] for i in range(cfg.layers)]
+    gcfg = _stream_cfg(cfg)
+    if n_src is None:
+        n_src = make_structure(cfg, use_cache=use_cache).n_src
+    rng = np.random.default_rng((gcfg.seed, 1))
+    x = rng.standard_normal((n_src, cfg.K, cfg.C))
+    x = round_storage(x, cfg.storage)
+    rng = np.random.default_rng((gcfg.seed, 2))
+    ws = []
+    for _ in range(cfg.layers):
+        parts = []
+        for name, shape in layer_weight_sizes(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf):
+            fan = _fan_in(name, shape)
+            parts.append(rng.standard_normal(shape).ravel() / np.sqrt(fan))
+        ws.append(round_storage(np.concatenate(parts), cfg.storage))
+    if use_cache:
+        os.makedirs(_CACHE_DIR, exist_ok=True)
+        np.savez(path, x=x, **{f"w{i}": w for i, w in enumerate(ws)})
+    return x, ws
+
+
+def make_decode_weights(cfg: Config | str, n_label=(9, 17, 13, 5, 1)):
+    """Decode weights W_dec,L [n_L][C] for edges and for nodes (seed of cfg).
+
+    Stream (seed, 3): edge weights for L = 0..4, then node weights, N(0, 1/C).
+    """
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    rng = np.random.default_rng((cfg.seed, 3))
+    we = [round_storage(rng.standard_normal((n, cfg.C)) / np.sqrt(cfg.C), "f32") for n in n_label]
+    wn = [round_storage(rng.standard_normal((n, cfg.C)) / np.sqrt(cfg.C), "f32") for n in n_label]
+    return we, wn
+
+
+def make_cotangent(cfg: Config | str, n_dst):
+    """Seeded cotangent G = dL/dx' [n_dst][K][C] (the loss is <G, x'>)."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    rng = np.random.default_rng((cfg.seed, 4))
+    return round_storage(rng.standard_normal((n_dst, cfg.K, cfg.C)), "f32")
