@@ -1,0 +1,214 @@
+"""MI355X-native SO(2) equivariant message-passing layer: Python binding of libegnn.so.
+
+The functions here carry the names of the C ABI (include/egnn.h) and only
+marshal arguments: torch supplies device memory and the current HIP stream,
+and every step of the computation runs in the library's HIP kernels.  There
+is no fallback path: if libegnn.so is missing, or the tensors are not on a
+GPU, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import EGNN_BF16, EGNN_F32, EgnnError
+
+__all__ = ["Graph", "layer_desc", "egnn_build_graph", "egnn_edge_geom", "egnn_geom_stride",
+           "egnn_layer_weight_count", "egnn_layer_sizes", "egnn_layer_fwd", "egnn_layer_bwd",
+           "egnn_hblocks", "egnn_hblocks_label_rows", "EgnnError", "EGNN_F32", "EGNN_BF16"]
+
+_STORAGE = {EGNN_F32: torch.float32, EGNN_BF16: torch.bfloat16}
+
+
+def _stream():
+    return ct.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ct.c_void_p(t.data_ptr())
+
+
+def _d3(v):
+    return (ct.c_double * 3)(*[float(a) for a in v])
+
+
+@dataclass
+class Graph:
+    """Destination-sorted CSR (incoming-edge layout) held in torch tensors."""
+    n_dst: int
+    n_src: int
+    n_edges: int
+    row_ptr: torch.Tensor
+    src: torch.Tensor
+    shift: torch.Tensor
+    vec: torch.Tensor
+    dist: torch.Tensor
+    src_ptr: torch.Tensor
+    src_perm: torch.Tensor
+
+    def c_struct(self):
+        g = _lib.EgnnGraph()
+        g.n_dst, g.n_src = self.n_dst, self.n_src
+        g.capacity = self.src.numel()
+        g.n_edges = self.n_edges
+        for f in ("row_ptr", "src", "shift", "vec", "dist", "src_ptr", "src_perm"):
+            setattr(g, f, self.__dict__[f].data_ptr())
+        return g
+
+
+def layer_desc(lmax, mmax, C, n_rbf, r_cut, storage=EGNN_F32):
+    return _lib.EgnnLayerDesc(lmax, mmax, C, n_rbf, float(r_cut), storage)
+
+
+def egnn_build_graph(pos, n_dst, lo, box, periodic_mask, r_cut, capacity=None):
+    """Build the graph of positions pos [n_src][3] (float64, on the GPU).
+
+    Runs the two-phase protocol of the C call: an edge count (capacity 0
+    unless given), then the fill into arrays of exactly that size.
+    """
+    lib = _lib.load()
+    dev = pos.device
+    n_src = pos.shape[0]
+    row_ptr = torch.empty(n_dst + 1, dtype=torch.int32, device=dev)
+    cap = 0 if capacity is None else int(capacity)
+
+    def arrays(c):
+        return dict(src=torch.empty(max(c, 1), dtype=torch.int32, device=dev),
+                    shift=torch.empty((max(c, 1), 3), dtype=torch.int8, device=dev),
+                    vec=torch.empty((max(c, 1), 3), dtype=torch.float32, device=dev),
+                    dist=torch.empty(max(c, 1), dtype=torch.float32, device=dev),
+                    src_ptr=torch.empty(n_src + 1, dtype=torch.int32, device=dev),
+                    src_perm=torch.empty(max(c, 1), dtype=torch.int32, device=dev))
+
+    lo3, box3 = _d3(lo), _d3(box)
+    for _ in range(2):
+        a = arrays(cap)
+        g = _lib.EgnnGraph()
+        g.n_dst, g.n_src, g.capacity = n_dst, n_src, cap
+        g.row_ptr = row_ptr.data_ptr()
+        g.src_ptr = a["src_ptr"].data_ptr()
+        for f in ("src", "shift", "vec", "dist", "src_perm"):
+            setattr(g, f, a[f].data_ptr() if cap > 0 else None)
+        ws_bytes = ct.c_size_t()
+        _lib.check("egnn_build_graph_workspace", lib.egnn_build_graph_workspace(
+            n_dst, n_src, lo3, box3, periodic_mask, float(r_cut), cap, ct.byref(ws_bytes)))
+        ws = torch.empty(max(ws_bytes.value, 1), dtype=torch.uint8, device=dev)
+        st = lib.egnn_build_graph(_ptr(pos), lo3, box3, periodic_mask, float(r_cut), ct.byref(g),
+                                  _ptr(ws), ws_bytes.value, _stream())
+        if st == _lib.EGNN_E_CAPACITY:
+            cap = int(g.n_edges)
+            continue
+        _lib.check("egnn_build_graph", st)
+        E = int(g.n_edges)
+        return Graph(n_dst, n_src, E, row_ptr, a["src"][:E], a["shift"][:E], a["vec"][:E], a["dist"][:E],
+                     a["src_ptr"], a["src_perm"][:E])
+    raise RuntimeError("egnn_build_graph: edge count changed between the two passes")
+
+
+def egnn_geom_stride(desc):
+    return int(_lib.load().egnn_geom_stride(ct.byref(desc)))
+
+
+def egnn_layer_weight_count(desc):
+    return int(_lib.load().egnn_layer_weight_count(ct.byref(desc)))
+
+
+def egnn_edge_geom(desc, graph: Graph, out=None):
+    """Per-edge Wigner rows, radial basis and destination row: [E][stride] float32."""
+    lib = _lib.load()
+    stride = egnn_geom_stride(desc)
+    if out is None:
+        out = torch.empty((max(graph.n_edges, 1), stride), dtype=torch.float32, device=graph.row_ptr.device)
+    g = graph.c_struct()
+    _lib.check("egnn_edge_geom", lib.egnn_edge_geom(ct.byref(desc), ct.byref(g), _ptr(out), _stream()))
+    return out
+
+
+def egnn_layer_sizes(desc, graph: Graph):
+    lib = _lib.load()
+    s, f, b = ct.c_size_t(), ct.c_size_t(), ct.c_size_t()
+    g = graph.c_struct()
+    _lib.check("egnn_layer_sizes", lib.egnn_layer_sizes(ct.byref(desc), ct.byref(g), ct.byref(s), ct.byref(f),
+                                                         ct.byref(b)))
+    return s.value, f.value, b.value
+
+
+class LayerBuffers:
+    """Saved activations and workspaces for one layer on one graph (allocated by torch)."""
+
+    def __init__(self, desc, graph: Graph, train=True):
+        saved, wsf, wsb = egnn_layer_sizes(desc, graph)
+        dev = graph.row_ptr.device
+        self.saved = torch.empty(max(saved, 1), dtype=torch.uint8, device=dev) if train else None
+        self.ws = torch.empty(max(wsf, wsb if train else 0, 1), dtype=torch.uint8, device=dev)
+
+
+def egnn_layer_fwd(desc, graph: Graph, geom, weights, x, x_out=None, edge_out=False, buffers=None):
+    """x_out [n_dst][K][C] (and edge_out [E][K][C] if requested) of one layer."""
+    lib = _lib.load()
+    K = (desc.lmax + 1) ** 2
+    dt = _STORAGE[desc.storage]
+    if x.dtype != dt or weights.dtype != torch.float32:
+        raise ValueError("x must use the storage dtype and weights float32")
+    if buffers is None:
+        buffers = LayerBuffers(desc, graph, train=False)
+    if x_out is None:
+        x_out = torch.empty((graph.n_dst, K, desc.C), dtype=dt, device=x.device)
+    eo = torch.empty((max(graph.n_edges, 1), K, desc.C), dtype=dt, device=x.device) if edge_out else None
+    g = graph.c_struct()
+    _lib.check("egnn_layer_fwd", lib.egnn_layer_fwd(
+        ct.byref(desc), ct.byref(g), _ptr(geom), _ptr(weights), _ptr(x), _ptr(x_out), _ptr(eo),
+        _ptr(buffers.saved), _ptr(buffers.ws), buffers.ws.numel(), _stream()))
+    return (x_out, eo[:graph.n_edges] if eo is not None else None), buffers
+
+
+def egnn_layer_bwd(desc, graph: Graph, geom, weights, x, buffers, grad_out, grad_x=None, grad_w=None):
+    """(dL/dx [n_src][K][C], dL/dweights) for the loss <grad_out, x_out>."""
+    lib = _lib.load()
+    K = (desc.lmax + 1) ** 2
+    if grad_x is None:
+        grad_x = torch.empty((graph.n_src, K, desc.C), dtype=torch.float32, device=x.device)
+    if grad_w is None:
+        grad_w = torch.empty(egnn_layer_weight_count(desc), dtype=torch.float32, device=x.device)
+    g = graph.c_struct()
+    _lib.check("egnn_layer_bwd", lib.egnn_layer_bwd(
+        ct.byref(desc), ct.byref(g), _ptr(geom), _ptr(weights), _ptr(x), _ptr(buffers.saved), _ptr(grad_out),
+        _ptr(grad_x), _ptr(grad_w), _ptr(buffers.ws), buffers.ws.numel(), _stream()))
+    return grad_x, grad_w
+
+
+def _hdesc(lmax, C, shell_l, storage):
+    arr = (ct.c_int32 * len(shell_l))(*shell_l)
+    h = _lib.EgnnHDesc(lmax, C, len(shell_l), arr, storage)
+    h._keep = arr
+    return h
+
+
+def egnn_hblocks_label_rows(lmax, C, shell_l=(0, 0, 1, 1, 2), storage=EGNN_F32):
+    return int(_lib.load().egnn_hblocks_label_rows(ct.byref(_hdesc(lmax, C, shell_l, storage))))
+
+
+def egnn_hblocks(lmax, C, w_edge, w_node, edge_irreps, node_irreps, shell_l=(0, 0, 1, 1, 2), storage=EGNN_F32):
+    """Orbital blocks [E][n_orb][n_orb] and [N][n_orb][n_orb] from irreps."""
+    lib = _lib.load()
+    h = _hdesc(lmax, C, shell_l, storage)
+    n_orb = sum(2 * l + 1 for l in shell_l)
+    E = 0 if edge_irreps is None else edge_irreps.shape[0]
+    N = 0 if node_irreps is None else node_irreps.shape[0]
+    dev = (edge_irreps if edge_irreps is not None else node_irreps).device
+    he = torch.empty((max(E, 1), n_orb, n_orb), dtype=torch.float32, device=dev)
+    hn = torch.empty((max(N, 1), n_orb, n_orb), dtype=torch.float32, device=dev)
+    _lib.check("egnn_hblocks", lib.egnn_hblocks(
+        ct.byref(h), E, N, _ptr(w_edge) if E else None, _ptr(w_node) if N else None,
+        _ptr(edge_irreps) if E else None, _ptr(node_irreps) if N else None, _ptr(he) if E else None,
+        _ptr(hn) if N else None, _stream()))
+    return he[:E], hn[:N]

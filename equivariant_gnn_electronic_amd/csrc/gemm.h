@@ -1,0 +1,22 @@
+// MFMA GEMM used by the SO(2) convolution (forward) and its backward.
+//
+//   C[m][n] (+)= sum_k A(m,k) B(n,k)
+// A(m,k) = A[m*lda + k] when a_kcontig, else A[k*lda + m]; B likewise.
+// C is fp32 [M][ldc].  With splits > 1 the K range is cut into `splits`
+// slices and slice z writes its partial product to C + z*split_stride
+// (reduced afterwards in a fixed order, so results are deterministic).
+#pragma once
+
+#include "common.h"
+
+namespace egnn {
+
+hipError_t gemm_f32(int M, int N, int K, const float *A, int lda, bool a_kcontig, const float *B, int ldb,
+                    bool b_kcontig, float *C, int ldc, int splits, int64_t split_stride, hipStream_t stream);
+
+// bf16 operands (raw 16-bit), fp32 accumulate; both operands K-contiguous.
+// C is written as bf16 when c_bf16, else fp32.
+hipError_t gemm_bf16_nt(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
+                        int ldc, bool c_bf16, hipStream_t stream);
+
+}  // namespace egnn

@@ -1,0 +1,195 @@
+// MFMA GEMMs for the per-|m| SO(2) channel mixing.
+//
+// The eSCN reduction turns the SO(3) tensor product into linear maps per
+// order m (MALOQ Sec. II-B1, Sec. III: "constrained linear layers"); over all
+// edges of a layer those maps are dense products with M = number of edges,
+// which is the one step of the layer that is a real contraction.
+//
+// fp32: v_mfma_f32_32x32x2_f32.  Block tile 128x128, 4 waves in a 2x2
+// arrangement, 64x64 per wave (2x2 MFMA tiles), K step 16, operands staged
+// k-major in LDS (double-buffered) so every fragment read is a
+// conflict-free row of LDS.  Tiles are assigned XCD-aware: consecutive
+// tiles that share an A row-block are given to workgroups that land on the
+// same XCD, so the A block is fetched from HBM once and then hits that
+// XCD's L2.
+#include "gemm.h"
+
+namespace egnn {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 128, BN = 128, BK = 16;
+constexpr int PAD = 4;  // LDS row padding (floats)
+constexpr int kXcd = 8;
+
+struct TileMap {
+  int mt, nt;
+  bool valid;
+};
+
+// Workgroup b runs on XCD b % 8.  Give XCD x the contiguous tile range
+// [x*per, (x+1)*per) in (m-major, n-minor) order.
+__device__ inline TileMap map_tile(int b, int tiles_m, int tiles_n) {
+  const int total = tiles_m * tiles_n;
+  const int per = (total + kXcd - 1) / kXcd;
+  const int t = (b % kXcd) * per + b / kXcd;
+  TileMap r;
+  r.valid = t < total;
+  r.mt = r.valid ? t / tiles_n : 0;
+  r.nt = r.valid ? t % tiles_n : 0;
+  return r;
+}
+
+// Load one BKxBM (or BKxBN) operand tile into registers: 2 float4 per thread.
+template <bool KCONTIG>
+__device__ inline void load_tile(const float *P, int ld, int rows, int row0, int k0, int k_end, f32x4 (&r)[2]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int f = t + h * 256;  // float4 index within the 128x16 tile
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (KCONTIG) {
+      const int m = f >> 2, kq = f & 3;
+      const int gm = row0 + m, gk = k0 + kq * 4;
+      if (gm < rows && gk < k_end) v = *reinterpret_cast<const f32x4 *>(P + static_cast<int64_t>(gm) * ld + gk);
+    } else {
+      const int k = f >> 5, mq = f & 31;
+      const int gk = k0 + k, gm = row0 + mq * 4;
+      if (gk < k_end && gm < rows) {
+        const float *p = P + static_cast<int64_t>(gk) * ld + gm;
+        if (gm + 3 < rows) {
+          v = *reinterpret_cast<const f32x4 *>(p);
+        } else {
+          for (int j = 0; j < 4; ++j) v[j] = (gm + j < rows) ? p[j] : 0.f;
+        }
+      }
+    }
+    r[h] = v;
+  }
+}
+
+// Store the register tile into LDS laid out [BK][BM + PAD].
+template <bool KCONTIG>
+__device__ inline void store_tile(float *S, const f32x4 (&r)[2]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int f = t + h * 256;
+    if (KCONTIG) {
+      const int m = f >> 2, kq = f & 3;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[(kq * 4 + j) * (BM + PAD) + m] = r[h][j];
+    } else {
+      const int k = f >> 5, mq = f & 31;
+      *reinterpret_cast<f32x4 *>(S + k * (BM + PAD) + mq * 4) = r[h];
+    }
+  }
+}
+
+template <bool AK, bool BK_>
+__global__ void __launch_bounds__(256, 2) gemm_f32_kernel(int M, int N, int K, const float *__restrict__ A, int lda,
+                                                          const float *__restrict__ B, int ldb, float *__restrict__ C,
+                                                          int ldc, int k_per_split, int64_t split_stride) {
+  __shared__ float As[2][BK * (BM + PAD)];
+  __shared__ float Bs[2][BK * (BN + PAD)];
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n);
+  if (!tm.valid) return;
+  const int z = blockIdx.y;
+  const int k_begin = z * k_per_split;
+  const int k_end = min(K, k_begin + k_per_split);
+  C += z * split_stride;
+  const int row0 = tm.mt * BM, col0 = tm.nt * BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int fr = lane & 31, fk = lane >> 5;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  f32x4 ra[2], rb[2];
+  int buf = 0;
+  if (k_begin < k_end) {
+    load_tile<AK>(A, lda, M, row0, k_begin, k_end, ra);
+    load_tile<BK_>(B, ldb, N, col0, k_begin, k_end, rb);
+    store_tile<AK>(As[0], ra);
+    store_tile<BK_>(Bs[0], rb);
+  }
+  __syncthreads();
+  for (int k0 = k_begin; k0 < k_end; k0 += BK) {
+    const bool more = k0 + BK < k_end;
+    if (more) {
+      load_tile<AK>(A, lda, M, row0, k0 + BK, k_end, ra);
+      load_tile<BK_>(B, ldb, N, col0, k0 + BK, k_end, rb);
+    }
+    const float *as = As[buf];
+    const float *bs = Bs[buf];
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 2) {
+      float a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = as[(kk + fk) * (BM + PAD) + wm + 32 * i + fr];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = bs[(kk + fk) * (BN + PAD) + wn + 32 * j + fr];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      store_tile<AK>(As[buf ^ 1], ra);
+      store_tile<BK_>(Bs[buf ^ 1], rb);
+    }
+    __syncthreads();
+    buf ^= 1;
+  }
+  // 32x32 accumulator layout: column = lane % 32, row = 8*(r/4) + 4*(lane/32) + r%4
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = col0 + wn + 32 * j + fr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + wm + 32 * i + 8 * (r >> 2) + 4 * fk + (r & 3);
+        if (row < M) C[static_cast<int64_t>(row) * ldc + col] = acc[i][j][r];
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t gemm_f32(int M, int N, int K, const float *A, int lda, bool a_kcontig, const float *B, int ldb,
+                    bool b_kcontig, float *C, int ldc, int splits, int64_t split_stride, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (splits < 1) splits = 1;
+  int kps = (K + splits - 1) / splits;
+  kps = (kps + BK - 1) / BK * BK;
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int per = (tiles + kXcd - 1) / kXcd;
+  dim3 grid(per * kXcd, splits);
+  if (a_kcontig && b_kcontig)
+    gemm_f32_kernel<true, true><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, kps, split_stride);
+  else if (!a_kcontig && !b_kcontig)
+    gemm_f32_kernel<false, false><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, kps, split_stride);
+  else if (a_kcontig)
+    gemm_f32_kernel<true, false><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, kps, split_stride);
+  else
+    gemm_f32_kernel<false, true><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, kps, split_stride);
+  return hipGetLastError();
+}
+
+hipError_t gemm_bf16_nt(int, int, int, const uint16_t *, int, const uint16_t *, int, void *, int, bool,
+                        hipStream_t) {
+  return hipErrorNotSupported;
+}
+
+}  // namespace egnn

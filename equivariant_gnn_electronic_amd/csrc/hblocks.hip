@@ -1,0 +1,360 @@
+// Label -> Matrix: orbital Hamiltonian blocks from edge / node irreps.
+//
+// MALOQ Sec. III-B1, Eq. (1): the block between a shell of degree la and one
+// of degree lb is la (x) lb, written through Clebsch-Gordan coefficients as
+// the direct sum of degrees L = |la-lb|..la+lb; all |L,M> of a block form its
+// label vector.  Sec. III-B2 describes a CUDA kernel with one thread per
+// matrix element and one thread block per node or edge, driven by a
+// precomputed orbital template.  Here one 64-lane wave owns a row (edge or
+// node): the row's irreps are staged in LDS, lanes first form the labels
+// h_L = W_L f^L (one label per lane), then lanes form the block entries from a
+// precomputed sparse list of real CG terms per entry (the orbital template).
+//
+// The real couplings are built on the host: complex CG coefficients from
+// Racah's closed formula, changed to the real basis of the irreps (polar axis
+// y, degree 1 ~ (x, y, z), no Condon-Shortley phase), made real by removing a
+// global phase, normalised, and signed so that the first entry of magnitude
+// > 1e-9 in row-major (i, j, M) order is positive.
+#include <cmath>
+#include <complex>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+
+namespace egnn {
+namespace {
+
+constexpr int kSlots = 8;
+constexpr int kMaxOrb = 32;
+constexpr int kMaxEntries = kMaxOrb * kMaxOrb;
+constexpr int kMaxTerms = 8192;
+constexpr int kMaxLab = kMaxEntries;
+
+struct Table {
+  int term_start[kMaxEntries + 1];
+  float term_coef[kMaxTerms];
+  unsigned short term_idx[kMaxTerms];
+  unsigned short lab_w[kMaxLab];   // weight row of label q
+  unsigned short lab_f[kMaxLab];   // irreps coefficient index L^2 + L + M of label q
+};
+
+__device__ Table g_tables[kSlots];
+
+double fact(int n) {
+  double r = 1.0;
+  for (int i = 2; i <= n; ++i) r *= i;
+  return r;
+}
+
+// <j1 m1 j2 m2 | J M>, integer angular momenta, Condon-Shortley convention.
+double cg_complex(int j1, int m1, int j2, int m2, int J, int M) {
+  if (M != m1 + m2) return 0.0;
+  if (J < std::abs(j1 - j2) || J > j1 + j2) return 0.0;
+  if (std::abs(m1) > j1 || std::abs(m2) > j2 || std::abs(M) > J) return 0.0;
+  double pre = std::sqrt((2.0 * J + 1.0) * fact(J + j1 - j2) * fact(J - j1 + j2) * fact(j1 + j2 - J) /
+                         fact(j1 + j2 + J + 1));
+  pre *= std::sqrt(fact(J + M) * fact(J - M) * fact(j1 - m1) * fact(j1 + m1) * fact(j2 - m2) * fact(j2 + m2));
+  double sum = 0.0;
+  for (int k = 0; k <= j1 + j2 + J; ++k) {
+    int a[6] = {k, j1 + j2 - J - k, j1 - m1 - k, j2 + m2 - k, J - j2 + m1 + k, J - j1 - m2 + k};
+    bool ok = true;
+    for (int v : a) ok = ok && v >= 0;
+    if (!ok) continue;
+    double den = 1.0;
+    for (int v : a) den *= fact(v);
+    sum += ((k & 1) ? -1.0 : 1.0) / den;
+  }
+  return pre * sum;
+}
+
+// Row m (= -l..l) of the complex -> real change of basis: S_m = sum_mu U[m][mu] Y_mu.
+std::complex<double> U(int l, int m, int mu) {
+  const double r2 = 1.0 / std::sqrt(2.0);
+  const std::complex<double> I(0.0, 1.0);
+  if (m == 0) return mu == 0 ? 1.0 : 0.0;
+  if (m > 0) {
+    if (mu == m) return ((m & 1) ? -1.0 : 1.0) * r2;
+    if (mu == -m) return r2;
+    return 0.0;
+  }
+  const int a = -m;
+  if (mu == a) return ((a & 1) ? -1.0 : 1.0) * r2 / I;
+  if (mu == -a) return -r2 / I;
+  return 0.0;
+}
+
+// Real coupling Q[i][j][M] (i: la, j: lb, M: L), row-major.
+std::vector<double> real_coupling(int la, int lb, int L) {
+  const int na = 2 * la + 1, nb = 2 * lb + 1, nL = 2 * L + 1;
+  std::vector<std::complex<double>> q(static_cast<size_t>(na) * nb * nL);
+  for (int i = -la; i <= la; ++i)
+    for (int j = -lb; j <= lb; ++j)
+      for (int N = -L; N <= L; ++N) {
+        std::complex<double> acc = 0.0;
+        for (int a = -la; a <= la; ++a) {
+          std::complex<double> ua = U(la, i, a);
+          if (ua == 0.0) continue;
+          for (int b = -lb; b <= lb; ++b) {
+            std::complex<double> ub = U(lb, j, b);
+            if (ub == 0.0) continue;
+            const int M = a + b;
+            if (std::abs(M) > L) continue;
+            acc += ua * ub * cg_complex(la, a, lb, b, L, M) * std::conj(U(L, N, M));
+          }
+        }
+        q[((i + la) * nb + (j + lb)) * nL + (N + L)] = acc;
+      }
+  size_t big = 0;
+  for (size_t t = 0; t < q.size(); ++t)
+    if (std::abs(q[t]) > std::abs(q[big])) big = t;
+  const std::complex<double> phase = q[big] / std::abs(q[big]);
+  std::vector<double> r(q.size());
+  for (size_t t = 0; t < q.size(); ++t) r[t] = (q[t] / phase).real();
+  double nrm = 0.0;
+  for (int i = 0; i < na; ++i)
+    for (int j = 0; j < nb; ++j) nrm += r[(i * nb + j) * nL] * r[(i * nb + j) * nL];
+  nrm = std::sqrt(nrm);
+  for (double &v : r) v /= nrm;
+  for (double v : r)
+    if (std::fabs(v) > 1e-9) {
+      if (v < 0)
+        for (double &w : r) w = -w;
+      break;
+    }
+  return r;
+}
+
+struct Layout {
+  int n_orb = 0, n_w = 0, n_lab = 0;
+  std::vector<int> nL, woff;  // label rows per L, first weight row of L
+  Table t;
+};
+
+bool build_layout(const int *shell_l, int n_shells, Layout *out) {
+  std::vector<int> off(n_shells);
+  int o = 0, lmx = 0;
+  for (int a = 0; a < n_shells; ++a) {
+    if (shell_l[a] < 0 || shell_l[a] > 2) return false;
+    off[a] = o;
+    o += 2 * shell_l[a] + 1;
+    lmx = std::max(lmx, shell_l[a]);
+  }
+  if (o > kMaxOrb) return false;
+  const int Lmax = 2 * lmx;
+  out->n_orb = o;
+  out->nL.assign(Lmax + 1, 0);
+  struct Item { int a, b, L, k; };
+  std::vector<Item> items;
+  for (int a = 0; a < n_shells; ++a)
+    for (int b = 0; b < n_shells; ++b)
+      for (int L = std::abs(shell_l[a] - shell_l[b]); L <= shell_l[a] + shell_l[b]; ++L)
+        items.push_back({a, b, L, out->nL[L]++});
+  out->woff.assign(Lmax + 2, 0);
+  for (int L = 0; L <= Lmax; ++L) out->woff[L + 1] = out->woff[L] + out->nL[L];
+  out->n_w = out->woff[Lmax + 1];
+  // label q enumerates (L, M, k): offset(L) + (M + L) * n_L + k
+  std::vector<int> hoff(Lmax + 2, 0);
+  for (int L = 0; L <= Lmax; ++L) hoff[L + 1] = hoff[L] + (2 * L + 1) * out->nL[L];
+  out->n_lab = hoff[Lmax + 1];
+  if (out->n_lab > kMaxLab || out->n_w > 65535) return false;
+  Table &t = out->t;
+  std::memset(&t, 0, sizeof(t));
+  for (int L = 0; L <= Lmax; ++L)
+    for (int M = -L; M <= L; ++M)
+      for (int k = 0; k < out->nL[L]; ++k) {
+        const int q = hoff[L] + (M + L) * out->nL[L] + k;
+        t.lab_w[q] = static_cast<unsigned short>(out->woff[L] + k);
+        t.lab_f[q] = static_cast<unsigned short>(L * L + L + M);
+      }
+  // sparse terms per block entry
+  std::vector<std::vector<std::pair<float, int>>> terms(static_cast<size_t>(o) * o);
+  for (const Item &it : items) {
+    const int la = shell_l[it.a], lb = shell_l[it.b];
+    std::vector<double> Q = real_coupling(la, lb, it.L);
+    const int nb = 2 * lb + 1, nLL = 2 * it.L + 1;
+    for (int i = 0; i < 2 * la + 1; ++i)
+      for (int j = 0; j < nb; ++j)
+        for (int M = 0; M < nLL; ++M) {
+          const double c = Q[(i * nb + j) * nLL + M];
+          if (std::fabs(c) < 1e-12) continue;
+          const int q = hoff[it.L] + M * out->nL[it.L] + it.k;
+          terms[(off[it.a] + i) * o + (off[it.b] + j)].push_back({static_cast<float>(c), q});
+        }
+  }
+  int n = 0;
+  for (int r = 0; r < o * o; ++r) {
+    t.term_start[r] = n;
+    for (auto &p : terms[r]) {
+      if (n >= kMaxTerms) return false;
+      t.term_coef[n] = p.first;
+      t.term_idx[n] = static_cast<unsigned short>(p.second);
+      ++n;
+    }
+  }
+  t.term_start[o * o] = n;
+  return true;
+}
+
+struct SlotKey {
+  int device;
+  int n;
+  int l[16];
+};
+struct SlotCache {
+  std::mutex mu;
+  SlotKey keys[64][kSlots];
+  int used[64] = {0};
+};
+SlotCache g_cache;
+
+// Slot of the table for (device, shell list); fills it on first use.
+egnn_status table_slot(const int *shell_l, int n_shells, int *slot, Layout *lay) {
+  int dev = 0;
+  EGNN_TRY_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) {
+    set_error("device index %d out of range", dev);
+    return EGNN_E_UNSUPPORTED;
+  }
+  if (!build_layout(shell_l, n_shells, lay)) {
+    set_error("shell list not supported (each l <= 2, at most %d orbitals)", kMaxOrb);
+    return EGNN_E_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_cache.mu);
+  for (int s = 0; s < g_cache.used[dev]; ++s) {
+    const SlotKey &k = g_cache.keys[dev][s];
+    if (k.n == n_shells && std::memcmp(k.l, shell_l, sizeof(int) * n_shells) == 0) {
+      *slot = s;
+      return EGNN_OK;
+    }
+  }
+  if (g_cache.used[dev] >= kSlots) {
+    set_error("more than %d distinct shell lists on one device", kSlots);
+    return EGNN_E_UNSUPPORTED;
+  }
+  const int s = g_cache.used[dev];
+  EGNN_TRY_HIP(hipMemcpyToSymbol(HIP_SYMBOL(g_tables), &lay->t, sizeof(Table), sizeof(Table) * s,
+                                 hipMemcpyHostToDevice));
+  SlotKey &k = g_cache.keys[dev][s];
+  k.device = dev;
+  k.n = n_shells;
+  std::memcpy(k.l, shell_l, sizeof(int) * n_shells);
+  g_cache.used[dev] = s + 1;
+  *slot = s;
+  return EGNN_OK;
+}
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+
+template <typename T>
+__global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64_t rows, const T *__restrict__ irreps,
+                                                                  int K, int C, const float *__restrict__ W, int n_w,
+                                                                  int n_lab, int n_ent, float *__restrict__ H) {
+  extern __shared__ float smem[];
+  const Table &tb = g_tables[slot];
+  float *Wt = smem;                                   // [C][n_w]
+  float *fs_all = Wt + C * n_w;                       // [kWaves][K][C+1]
+  float *hs_all = fs_all + kWaves * K * (C + 1);      // [kWaves][n_lab]
+  for (int i = threadIdx.x; i < C * n_w; i += blockDim.x) {
+    const int c = i / n_w, w = i % n_w;
+    Wt[i] = W[static_cast<int64_t>(w) * C + c];
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  float *fs = fs_all + wave * K * (C + 1);
+  float *hs = hs_all + wave * n_lab;
+  for (int64_t r = static_cast<int64_t>(blockIdx.x) * kWaves + wave; r < rows;
+       r += static_cast<int64_t>(gridDim.x) * kWaves) {
+    const T *f = irreps + r * K * C;
+    for (int i = lane; i < K * C; i += kWave) fs[(i / C) * (C + 1) + (i % C)] = Store<T>::ld(f + i);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    for (int q = lane; q < n_lab; q += kWave) {
+      const int wr = tb.lab_w[q];
+      const float *fr = fs + tb.lab_f[q] * (C + 1);
+      float acc = 0.0f;
+      for (int c = 0; c < C; ++c) acc += Wt[c * n_w + wr] * fr[c];
+      hs[q] = acc;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    float *out = H + r * n_ent;
+    for (int q = lane; q < n_ent; q += kWave) {
+      float acc = 0.0f;
+      for (int t = tb.term_start[q]; t < tb.term_start[q + 1]; ++t) acc += tb.term_coef[t] * hs[tb.term_idx[t]];
+      out[q] = acc;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  }
+}
+
+template <typename T>
+egnn_status launch_hblocks(int slot, int64_t rows, const void *irreps, int K, int C, const float *W, int n_w,
+                           int n_lab, int n_ent, float *H, hipStream_t stream) {
+  if (rows <= 0) return EGNN_OK;
+  const size_t smem = sizeof(float) * (static_cast<size_t>(C) * n_w + kWaves * K * (C + 1) + kWaves * n_lab);
+  if (smem > 150 * 1024) {
+    set_error("decode needs %zu bytes of LDS; reduce C or the shell list", smem);
+    return EGNN_E_UNSUPPORTED;
+  }
+  int64_t blocks = (rows + kWaves - 1) / kWaves;
+  if (blocks > 4096) blocks = 4096;
+  hblocks_kernel<T><<<static_cast<unsigned>(blocks), kWave * kWaves, smem, stream>>>(
+      slot, rows, static_cast<const T *>(irreps), K, C, W, n_w, n_lab, n_ent, H);
+  EGNN_CHECK_LAUNCH();
+  return EGNN_OK;
+}
+
+}  // namespace
+}  // namespace egnn
+
+using namespace egnn;
+
+static bool valid_hdesc(const egnn_hdesc *h) {
+  if (!h || !h->shell_l) return false;
+  if (h->n_shells < 1 || h->n_shells > 16) return false;
+  if (h->lmax < 0 || h->lmax > 8) return false;
+  if (h->C < 8 || h->C > 256 || h->C % 8 != 0) return false;
+  if (h->storage != EGNN_F32 && h->storage != EGNN_BF16) return false;
+  int lmx = 0;
+  for (int i = 0; i < h->n_shells; ++i) {
+    if (h->shell_l[i] < 0 || h->shell_l[i] > 2) return false;
+    lmx = std::max(lmx, h->shell_l[i]);
+  }
+  return h->lmax >= 2 * lmx;
+}
+
+extern "C" int32_t egnn_hblocks_label_rows(const egnn_hdesc *h) {
+  if (!valid_hdesc(h)) return 0;
+  Layout lay;
+  if (!build_layout(h->shell_l, h->n_shells, &lay)) return 0;
+  return lay.n_w;
+}
+
+extern "C" egnn_status egnn_hblocks(const egnn_hdesc *h, int64_t n_edges, int32_t n_nodes, const float *w_edge,
+                                    const float *w_node, const void *edge_irreps, const void *node_irreps,
+                                    float *h_edge, float *h_onsite, hipStream_t stream) {
+  clear_error();
+  EGNN_REQUIRE(valid_hdesc(h), "invalid decode description");
+  EGNN_REQUIRE(n_edges >= 0 && n_nodes >= 0, "negative row count");
+  if (n_edges > 0) EGNN_REQUIRE(w_edge && edge_irreps && h_edge, "edge pointers are null");
+  if (n_nodes > 0) EGNN_REQUIRE(w_node && node_irreps && h_onsite, "node pointers are null");
+  if (n_edges == 0 && n_nodes == 0) return EGNN_OK;
+  int slot = 0;
+  Layout lay;
+  egnn_status st = table_slot(h->shell_l, h->n_shells, &slot, &lay);
+  if (st != EGNN_OK) return st;
+  const int K = (h->lmax + 1) * (h->lmax + 1);
+  const int n_ent = lay.n_orb * lay.n_orb;
+  auto run = [&](int64_t rows, const void *irr, const float *W, float *H) -> egnn_status {
+    if (h->storage == EGNN_BF16)
+      return launch_hblocks<uint16_t>(slot, rows, irr, K, h->C, W, lay.n_w, lay.n_lab, n_ent, H, stream);
+    return launch_hblocks<float>(slot, rows, irr, K, h->C, W, lay.n_w, lay.n_lab, n_ent, H, stream);
+  };
+  st = run(n_edges, edge_irreps, w_edge, h_edge);
+  if (st != EGNN_OK) return st;
+  return run(n_nodes, node_irreps, w_node, h_onsite);
+}

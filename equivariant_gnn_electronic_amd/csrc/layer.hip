@@ -1,0 +1,942 @@
+// One SO(2)-reduced equivariant message-passing layer in the incoming-edge
+// layout: forward and backward.
+//
+// Forward (review of arXiv 2507.03840, "What carries the argument"; MALOQ
+// Sec. III, III-C1, III-D, II-B1):
+//   rotate_in   per edge: messages n_i (+) n_j rotated into the edge frame by
+//               the edge's Wigner rows (|m| <= mmax only), times radial gates
+//               -> GEMM operands A_m, one array per |m|
+//   GEMMs       Y_m = A_m B_m^T, the SO(2) channel mixing per |m| (MFMA)
+//   attention   per destination row: logits from the invariant output
+//               channels, softmax over the row (the row is owned, so no
+//               exchange is needed)
+//   aggregate   per destination row: rotate back, scale by alpha and sum into
+//               the destination with a register accumulator (no atomics)
+// Backward: the reverse of each step; every reduction over edges runs in a
+// fixed order (per-row/per-source waves, split-K partials summed in order).
+//
+// Data layout in HBM (E = edges, C = channels, nl(m) = lmax - m + 1):
+//   A_0 [E][nl(0) * 2C]          column (l) * 2C + slot
+//   A_m [E][2 * nl(m) * 2C]      column (sign * nl(m) + l - m) * 2C + slot, sign 0 = +m, 1 = -m
+//   Y_0 [E][nl(0) * C], Y_m [E][2 * nl(m) * C]   same pattern with C
+// slot 0..C-1 = source channels, C..2C-1 = destination channels.
+#include <cstring>
+
+#include "common.h"
+#include "gemm.h"
+
+namespace egnn {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / kWave;
+
+template <int LMAX, int MMAX>
+struct Lay {
+  static constexpr int K = (LMAX + 1) * (LMAX + 1);
+  static constexpr int ND = d_count(LMAX, MMAX);
+  static constexpr int KEPT = kept_count(LMAX, MMAX);
+  static constexpr int NP = pair_count(LMAX, MMAX);
+  __host__ __device__ static constexpr int nl(int mu) { return LMAX - mu + 1; }
+  __host__ __device__ static constexpr int doff(int l, int m, int mp) {
+    return d_block_offset(l, MMAX) + (m + cmin(l, MMAX)) * (2 * l + 1) + (mp + l);
+  }
+  // column block of kept (l, m) within A_|m| / Y_|m|
+  __host__ __device__ static constexpr int col(int l, int m) {
+    return m == 0 ? l : ((m > 0 ? 0 : 1) * nl(cabs(m)) + (l - cabs(m)));
+  }
+  // width of A_mu (in slots of 2C) or Y_mu (in slots of C)
+  __host__ __device__ static constexpr int blocks(int mu) { return mu == 0 ? nl(0) : 2 * nl(mu); }
+  // running index of kept (l, m)
+  __host__ __device__ static constexpr int kidx(int l, int m) {
+    int n = 0;
+    for (int j = 0; j < l; ++j) n += 2 * cmin(j, MMAX) + 1;
+    return n + m + cmin(l, MMAX);
+  }
+};
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ inline float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
+__device__ inline float silu(float z) { return z * sigmoidf_(z); }
+__device__ inline float dsilu(float z) {
+  float s = sigmoidf_(z);
+  return s * (1.0f + z * (1.0f - s));
+}
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+struct Ptr3 {
+  void *p[3];
+};
+struct CPtr3 {
+  const void *p[3];
+};
+
+// ---------------------------------------------------------------- weights --
+// B_m [2 nl C][2 nl 2C] from W_m1, W_m2 [nl C][nl 2C]:
+//   B[+][+] = W_m1, B[+][-] = -W_m2, B[-][+] = W_m2, B[-][-] = W_m1
+template <typename TB>
+__global__ void expand_weights_kernel(const float *w1, const float *w2, int rows, int cols, TB *B) {
+  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t n = static_cast<int64_t>(4) * rows * cols;
+  if (i >= n) return;
+  const int k = static_cast<int>(i % (2 * cols));
+  const int r = static_cast<int>(i / (2 * cols));
+  const int so = r / rows, no = r % rows, si = k / cols, ki = k % cols;
+  const int64_t o = static_cast<int64_t>(no) * cols + ki;
+  float v = (so == si) ? w1[o] : (so == 0 ? -w2[o] : w2[o]);
+  Store<TB>::st(B + i, v);
+}
+
+__global__ void to_bf16_kernel(const float *in, int64_t n, uint16_t *out) {
+  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = f32_to_bf16(in[i]);
+}
+
+// --------------------------------------------------------------- forward --
+template <int LMAX, int MMAX, typename T, typename TA>
+__global__ void __launch_bounds__(kThreads) rotate_in_kernel(const int *__restrict__ src, const float *__restrict__ geom,
+                                                             int gstride, int64_t E, const T *__restrict__ x, int C,
+                                                             const float *__restrict__ wrad, int n_rbf, Ptr3 A) {
+  using L = Lay<LMAX, MMAX>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t e64 = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+  if (e64 >= E) return;
+  const int e = uniform(static_cast<int>(e64));
+  const float *gr = geom + static_cast<int64_t>(e) * gstride;
+  const int s = uniform(src[e]);
+  const int d = uniform(__float_as_int(gr[L::ND + n_rbf]));
+  float phi[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) phi[k] = k < n_rbf ? gr[L::ND + k] : 0.0f;
+  const int C2 = 2 * C;
+  for (int j = lane; j < C2; j += kWave) {
+    const bool is_src = j < C;
+    const int c = is_src ? j : j - C;
+    const T *xr = x + static_cast<int64_t>(is_src ? s : d) * L::K * C + c;
+    float xv[L::K];
+#pragma unroll
+    for (int k = 0; k < L::K; ++k) xv[k] = Store<T>::ld(xr + k * C);
+    float g[L::NP];
+#pragma unroll
+    for (int p = 0; p < L::NP; ++p) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (k < n_rbf) acc += phi[k] * wrad[(static_cast<int64_t>(k) * L::NP + p) * C2 + j];
+      g[p] = acc;
+    }
+#pragma unroll
+    for (int l = 0; l <= LMAX; ++l) {
+#pragma unroll
+      for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+        float v = 0.0f;
+#pragma unroll
+        for (int mp = -l; mp <= l; ++mp) v += gr[L::doff(l, m, mp)] * xv[l * l + l + mp];
+        v *= g[pair_index(cabs(m), l, LMAX)];
+        const int mu = cabs(m);
+        TA *Am = static_cast<TA *>(A.p[mu]);
+        const int64_t width = static_cast<int64_t>(L::blocks(mu)) * C2;
+        Store<TA>::st(Am + static_cast<int64_t>(e) * width + L::col(l, m) * C2 + j, v);
+      }
+    }
+  }
+}
+
+// logits a_e = sum_c w_att[c] SiLU(Y0[e][c]) and the row softmax (one wave per row,
+// one edge per lane, online max/sum over chunks of 64 edges)
+__global__ void __launch_bounds__(kThreads) attention_kernel(const int *__restrict__ row_ptr, int n_dst,
+                                                             const float *__restrict__ Y0, int ldy0, int C,
+                                                             const float *__restrict__ w_att, float *logit,
+                                                             float *alpha) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int d = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (d >= n_dst) return;
+  const int b = row_ptr[d], end = row_ptr[d + 1];
+  float M = -INFINITY, S = 0.0f;
+  for (int base = b; base < end; base += kWave) {
+    const int e = base + lane;
+    float a = -INFINITY;
+    if (e < end) {
+      const float *y = Y0 + static_cast<int64_t>(e) * ldy0;
+      float acc = 0.0f;
+      for (int c = 0; c < C; c += 4) {
+        float4 v = *reinterpret_cast<const float4 *>(y + c);
+        acc += w_att[c] * silu(v.x) + w_att[c + 1] * silu(v.y) + w_att[c + 2] * silu(v.z) + w_att[c + 3] * silu(v.w);
+      }
+      a = acc;
+      logit[e] = a;
+    }
+    const float mc = wave_max(a);
+    const float Mn = fmaxf(M, mc);
+    const float ex = e < end ? expf(a - Mn) : 0.0f;
+    S = S * expf(M - Mn) + wave_sum(ex);
+    M = Mn;
+  }
+  const float inv = 1.0f / S;
+  for (int e = b + lane; e < end; e += kWave) alpha[e] = expf(logit[e] - M) * inv;
+}
+
+// x_out[d] = x[d] + sum_e alpha_e D_e^T Yhat_e ; edge_out[e] = D_e^T Yhat_e
+template <int LMAX, int MMAX, int CPL, typename T>
+__global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restrict__ row_ptr, int n_dst,
+                                                             const float *__restrict__ geom, int gstride,
+                                                             const float *__restrict__ alpha, CPtr3 Y, int C,
+                                                             const T *__restrict__ x, T *__restrict__ x_out,
+                                                             T *__restrict__ edge_out) {
+  using L = Lay<LMAX, MMAX>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int d = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (d >= n_dst) return;
+  const int b = uniform(row_ptr[d]), end = uniform(row_ptr[d + 1]);
+  float acc[CPL][L::K];
+#pragma unroll
+  for (int t = 0; t < CPL; ++t)
+#pragma unroll
+    for (int k = 0; k < L::K; ++k) acc[t][k] = 0.0f;
+  for (int e = b; e < end; ++e) {
+    const float a = alpha[e];
+    const float *gr = geom + static_cast<int64_t>(e) * gstride;
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      const int c = lane + kWave * t;
+      if (c >= C) continue;
+      float y[L::KEPT];
+#pragma unroll
+      for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+        for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+          const int mu = cabs(m);
+          const float *Ym = static_cast<const float *>(Y.p[mu]);
+          y[L::kidx(l, m)] = Ym[static_cast<int64_t>(e) * L::blocks(mu) * C + L::col(l, m) * C + c];
+        }
+#pragma unroll
+      for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+        for (int mp = -l; mp <= l; ++mp) {
+          float msg = 0.0f;
+#pragma unroll
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) msg += gr[L::doff(l, m, mp)] * y[L::kidx(l, m)];
+          acc[t][l * l + l + mp] += a * msg;
+          if (edge_out) Store<T>::st(edge_out + (static_cast<int64_t>(e) * L::K + l * l + l + mp) * C + c, msg);
+        }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) {
+    const int c = lane + kWave * t;
+    if (c >= C) continue;
+#pragma unroll
+    for (int k = 0; k < L::K; ++k) {
+      const int64_t o = (static_cast<int64_t>(d) * L::K + k) * C + c;
+      Store<T>::st(x_out + o, Store<T>::ld(x + o) + acc[t][k]);
+    }
+  }
+}
+
+// -------------------------------------------------------------- backward --
+// Per destination row: T_e = trunc(D_e G_d); dalpha_e = <Y_e, T_e>;
+// da_e = alpha_e (dalpha_e - sum_row alpha dalpha);
+// dY_e = alpha_e T_e + da_e w_att SiLU'(Y_e[0,0]) on (l=0, m=0);
+// w_att partial of the row = sum_e da_e SiLU(Y_e[0,0]).
+template <int LMAX, int MMAX, int CPL>
+__global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict__ row_ptr, int n_dst,
+                                                           const float *__restrict__ geom, int gstride,
+                                                           const float *__restrict__ alpha, CPtr3 Y, int C,
+                                                           const float *__restrict__ G, const float *__restrict__ w_att,
+                                                           Ptr3 dY, float *dalpha, float *watt_part) {
+  using L = Lay<LMAX, MMAX>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int d = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (d >= n_dst) return;
+  const int b = uniform(row_ptr[d]), end = uniform(row_ptr[d + 1]);
+  float gd[CPL][L::K];
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) {
+    const int c = lane + kWave * t;
+#pragma unroll
+    for (int k = 0; k < L::K; ++k) gd[t][k] = c < C ? G[(static_cast<int64_t>(d) * L::K + k) * C + c] : 0.0f;
+  }
+  auto edge_T = [&](const float *gr, int t, float (&T)[L::KEPT]) {
+#pragma unroll
+    for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+      for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+        float v = 0.0f;
+#pragma unroll
+        for (int mp = -l; mp <= l; ++mp) v += gr[L::doff(l, m, mp)] * gd[t][l * l + l + mp];
+        T[L::kidx(l, m)] = v;
+      }
+  };
+  auto yaddr = [&](int e, int l, int m, int c) -> int64_t {
+    return static_cast<int64_t>(e) * L::blocks(cabs(m)) * C + L::col(l, m) * C + c;
+  };
+  float s_row = 0.0f;
+  for (int e = b; e < end; ++e) {
+    const float *gr = geom + static_cast<int64_t>(e) * gstride;
+    float p = 0.0f;
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      const int c = lane + kWave * t;
+      if (c >= C) continue;
+      float T[L::KEPT];
+      edge_T(gr, t, T);
+#pragma unroll
+      for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+        for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
+          p += static_cast<const float *>(Y.p[cabs(m)])[yaddr(e, l, m, c)] * T[L::kidx(l, m)];
+    }
+    p = wave_sum(p);
+    dalpha[e] = p;  // every lane stores the same value and later reads its own store
+    s_row += alpha[e] * p;
+  }
+  float wacc[CPL];
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) wacc[t] = 0.0f;
+  for (int e = b; e < end; ++e) {
+    const float *gr = geom + static_cast<int64_t>(e) * gstride;
+    const float a = alpha[e];
+    const float da = a * (dalpha[e] - s_row);
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      const int c = lane + kWave * t;
+      if (c >= C) continue;
+      float T[L::KEPT];
+      edge_T(gr, t, T);
+#pragma unroll
+      for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+        for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+          float v = a * T[L::kidx(l, m)];
+          if (l == 0) {
+            const float y00 = static_cast<const float *>(Y.p[0])[yaddr(e, 0, 0, c)];
+            v += da * w_att[c] * dsilu(y00);
+            wacc[t] += da * silu(y00);
+          }
+          static_cast<float *>(dY.p[cabs(m)])[yaddr(e, l, m, c)] = v;
+        }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) {
+    const int c = lane + kWave * t;
+    if (c < C) watt_part[static_cast<int64_t>(d) * C + c] = wacc[t];
+  }
+}
+
+// Per edge: recompute Xt (edge-frame input before the gate) and g; the GEMM
+// gradient dX (in dA) becomes dXt = g * dX in place; dg = sum_{+-m} dX * Xt.
+template <int LMAX, int MMAX, typename T>
+__global__ void __launch_bounds__(kThreads) bwd_gate_kernel(const int *__restrict__ src, const float *__restrict__ geom,
+                                                            int gstride, int64_t E, const T *__restrict__ x, int C,
+                                                            const float *__restrict__ wrad, int n_rbf, Ptr3 dA,
+                                                            float *__restrict__ dg) {
+  using L = Lay<LMAX, MMAX>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t e64 = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+  if (e64 >= E) return;
+  const int e = uniform(static_cast<int>(e64));
+  const float *gr = geom + static_cast<int64_t>(e) * gstride;
+  const int s = uniform(src[e]);
+  const int d = uniform(__float_as_int(gr[L::ND + n_rbf]));
+  float phi[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) phi[k] = k < n_rbf ? gr[L::ND + k] : 0.0f;
+  const int C2 = 2 * C;
+  for (int j = lane; j < C2; j += kWave) {
+    const bool is_src = j < C;
+    const int c = is_src ? j : j - C;
+    const T *xr = x + static_cast<int64_t>(is_src ? s : d) * L::K * C + c;
+    float xv[L::K];
+#pragma unroll
+    for (int k = 0; k < L::K; ++k) xv[k] = Store<T>::ld(xr + k * C);
+    float dgp[L::NP];
+#pragma unroll
+    for (int p = 0; p < L::NP; ++p) dgp[p] = 0.0f;
+#pragma unroll
+    for (int l = 0; l <= LMAX; ++l) {
+#pragma unroll
+      for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+        float xt = 0.0f;
+#pragma unroll
+        for (int mp = -l; mp <= l; ++mp) xt += gr[L::doff(l, m, mp)] * xv[l * l + l + mp];
+        const int mu = cabs(m);
+        const int p = pair_index(mu, l, LMAX);
+        float g = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if (k < n_rbf) g += phi[k] * wrad[(static_cast<int64_t>(k) * L::NP + p) * C2 + j];
+        float *Am = static_cast<float *>(dA.p[mu]);
+        const int64_t o = static_cast<int64_t>(e) * L::blocks(mu) * C2 + L::col(l, m) * C2 + j;
+        const float dx = Am[o];
+        dgp[p] += dx * xt;
+        Am[o] = g * dx;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < L::NP; ++p) dg[(static_cast<int64_t>(e) * L::NP + p) * C2 + j] = dgp[p];
+  }
+}
+
+// Per node n: grad_x[n] = G[n] (owned rows) + sum over its incoming edges of
+// D_e^T dXt_e[destination half] + sum over its outgoing edges (the source
+// grouping) of D_e^T dXt_e[source half].
+template <int LMAX, int MMAX, int CPL>
+__global__ void __launch_bounds__(kThreads) bwd_node_kernel(const int *__restrict__ row_ptr, int n_dst, int n_src,
+                                                            const int *__restrict__ src_ptr,
+                                                            const int *__restrict__ src_perm,
+                                                            const float *__restrict__ geom, int gstride, CPtr3 dA,
+                                                            int C, const float *__restrict__ G, float *__restrict__ gx) {
+  using L = Lay<LMAX, MMAX>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (n >= n_src) return;
+  const int C2 = 2 * C;
+  float acc[CPL][L::K];
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) {
+    const int c = lane + kWave * t;
+#pragma unroll
+    for (int k = 0; k < L::K; ++k)
+      acc[t][k] = (n < n_dst && c < C) ? G[(static_cast<int64_t>(n) * L::K + k) * C + c] : 0.0f;
+  }
+  auto add_edge = [&](int e, int half) {
+    const float *gr = geom + static_cast<int64_t>(e) * gstride;
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      const int c = lane + kWave * t;
+      if (c >= C) continue;
+      const int j = half * C + c;
+      float v[L::KEPT];
+#pragma unroll
+      for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+        for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+          const int mu = cabs(m);
+          v[L::kidx(l, m)] = static_cast<const float *>(dA.p[mu])[static_cast<int64_t>(e) * L::blocks(mu) * C2 +
+                                                                   L::col(l, m) * C2 + j];
+        }
+#pragma unroll
+      for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+        for (int mp = -l; mp <= l; ++mp) {
+          float s = 0.0f;
+#pragma unroll
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) s += gr[L::doff(l, m, mp)] * v[L::kidx(l, m)];
+          acc[t][l * l + l + mp] += s;
+        }
+    }
+  };
+  if (n < n_dst) {
+    const int b = uniform(row_ptr[n]), end = uniform(row_ptr[n + 1]);
+    for (int e = b; e < end; ++e) add_edge(e, 1);
+  }
+  {
+    const int b = uniform(src_ptr[n]), end = uniform(src_ptr[n + 1]);
+    for (int i = b; i < end; ++i) add_edge(uniform(src_perm[i]), 0);
+  }
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) {
+    const int c = lane + kWave * t;
+    if (c >= C) continue;
+#pragma unroll
+    for (int k = 0; k < L::K; ++k) gx[(static_cast<int64_t>(n) * L::K + k) * C + c] = acc[t][k];
+  }
+}
+
+// out[c] = sum_{r < R} in[r*ld + c] in a fixed order (4 row-strided partials, then a fixed tree).
+__global__ void __launch_bounds__(256) colsum_kernel(const float *__restrict__ in, int R, int64_t ncol, int64_t ld,
+                                                     float *__restrict__ out) {
+  __shared__ float part[4][64];
+  const int cx = threadIdx.x & 63, ry = threadIdx.x >> 6;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + cx;
+  float s = 0.0f;
+  if (c < ncol)
+    for (int r = ry; r < R; r += 4) s += in[static_cast<int64_t>(r) * ld + c];
+  part[ry][cx] = s;
+  __syncthreads();
+  if (ry == 0 && c < ncol) out[c] = (part[0][cx] + part[1][cx]) + (part[2][cx] + part[3][cx]);
+}
+
+// dW_m1 = P[+][+] + P[-][-],  dW_m2 = -P[+][-] + P[-][+]   (P reduced over splits)
+__global__ void fold_dw_kernel(const float *P, int rows, int cols, float *dw1, float *dw2) {
+  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(rows) * cols) return;
+  const int no = static_cast<int>(i / cols), ki = static_cast<int>(i % cols);
+  const int64_t ld = 2 * static_cast<int64_t>(cols);
+  const float pp = P[no * ld + ki], pm = P[no * ld + cols + ki];
+  const float mp = P[(rows + no) * ld + ki], mm = P[(rows + no) * ld + cols + ki];
+  dw1[i] = pp + mm;
+  dw2[i] = -pm + mp;
+}
+
+// Partial radial-weight gradient of one edge split: part[z][k][col] = sum_e phi_e[k] dg[e][col].
+__global__ void __launch_bounds__(256) wrad_partial_kernel(const float *__restrict__ geom, int gstride, int nd,
+                                                           int n_rbf, int64_t E, const float *__restrict__ dg,
+                                                           int ncol, int edges_per_split, float *__restrict__ part) {
+  const int col = blockIdx.x * blockDim.x + threadIdx.x;
+  const int z = blockIdx.y;
+  const int64_t e0 = static_cast<int64_t>(z) * edges_per_split;
+  const int64_t e1 = e0 + edges_per_split < E ? e0 + edges_per_split : E;
+  float acc[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
+  if (col < ncol) {
+    for (int64_t e = e0; e < e1; ++e) {
+      const float v = dg[e * ncol + col];
+      const float *ph = geom + e * gstride + nd;
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (k < n_rbf) acc[k] += ph[k] * v;
+    }
+    for (int k = 0; k < n_rbf; ++k) part[(static_cast<int64_t>(z) * n_rbf + k) * ncol + col] = acc[k];
+  }
+}
+
+__global__ void fill_f32(float *p, int64_t n, float v) {
+  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// ------------------------------------------------------------ buffers --
+size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Carver {
+  char *base;
+  size_t off = 0;
+  template <typename T>
+  T *take(size_t count) {
+    T *r = base ? reinterpret_cast<T *>(base + off) : nullptr;
+    off += a256(count * sizeof(T));
+    return r;
+  }
+};
+
+struct Acts {  // what the backward needs from the forward
+  void *A[3];
+  float *Y[3];
+  float *alpha;
+};
+
+Acts carve_acts(Carver &cv, const LayerShape &s, int64_t E) {
+  Acts a{};
+  const size_t ab = s.storage == EGNN_BF16 ? 2 : 4;
+  for (int m = 0; m <= s.mmax; ++m) {
+    a.A[m] = cv.take<char>(static_cast<size_t>(E) * s.Kg[m] * ab);
+  }
+  for (int m = 0; m <= s.mmax; ++m) a.Y[m] = cv.take<float>(static_cast<size_t>(E) * s.Ng[m]);
+  a.alpha = cv.take<float>(E);
+  return a;
+}
+
+struct FwdWs {
+  void *B[3];      // expanded weights per m (B[0] may alias W0 for fp32)
+  float *logit;
+};
+
+FwdWs carve_fwd_ws(Carver &cv, const LayerShape &s, int64_t E) {
+  FwdWs w{};
+  const size_t bb = s.storage == EGNN_BF16 ? 2 : 4;
+  for (int m = 0; m <= s.mmax; ++m) {
+    if (m == 0 && s.storage == EGNN_F32) {
+      w.B[0] = nullptr;
+      continue;
+    }
+    w.B[m] = cv.take<char>(static_cast<size_t>(s.Ng[m]) * s.Kg[m] * bb);
+  }
+  w.logit = cv.take<float>(E);
+  return w;
+}
+
+int dw_splits(int64_t E) {
+  int64_t s = E / 8192;
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;
+  return static_cast<int>(s);
+}
+constexpr int kWradSplits = 128;
+
+struct BwdWs {
+  float *B[3];
+  float *dY[3];
+  float *dA[3];
+  float *dalpha;
+  float *dg;
+  float *watt_part;
+  float *P;        // split partials of the largest m
+  float *Pred;     // reduced partials
+  float *wrad_part;
+};
+
+BwdWs carve_bwd_ws(Carver &cv, const LayerShape &s, int64_t E, int n_dst) {
+  BwdWs w{};
+  size_t pmax = 0;
+  for (int m = 0; m <= s.mmax; ++m) {
+    w.B[m] = m == 0 ? nullptr : cv.take<float>(static_cast<size_t>(s.Ng[m]) * s.Kg[m]);
+    w.dY[m] = cv.take<float>(static_cast<size_t>(E) * s.Ng[m]);
+    w.dA[m] = cv.take<float>(static_cast<size_t>(E) * s.Kg[m]);
+    pmax = pmax > static_cast<size_t>(s.Ng[m]) * s.Kg[m] ? pmax : static_cast<size_t>(s.Ng[m]) * s.Kg[m];
+  }
+  w.dalpha = cv.take<float>(E);
+  w.dg = cv.take<float>(static_cast<size_t>(E) * s.n_pairs * 2 * s.C);
+  w.watt_part = cv.take<float>(static_cast<size_t>(n_dst > 0 ? n_dst : 1) * s.C);
+  w.P = cv.take<float>(pmax * dw_splits(E));
+  w.Pred = cv.take<float>(pmax);
+  w.wrad_part = cv.take<float>(static_cast<size_t>(kWradSplits) * s.n_rbf * s.n_pairs * 2 * s.C);
+  return w;
+}
+
+struct WOff {  // offsets of the packed weight blocks
+  size_t W0, W1[3], W2[3], wrad, watt, total;
+};
+WOff weight_offsets(const LayerShape &s) {
+  WOff o{};
+  size_t p = 0;
+  o.W0 = p;
+  p += static_cast<size_t>(s.Ng[0]) * s.Kg[0];
+  for (int m = 1; m <= s.mmax; ++m) {
+    size_t blk = static_cast<size_t>(s.Ng[m] / 2) * (s.Kg[m] / 2);
+    o.W1[m] = p;
+    p += blk;
+    o.W2[m] = p;
+    p += blk;
+  }
+  o.wrad = p;
+  p += static_cast<size_t>(s.n_rbf) * s.n_pairs * 2 * s.C;
+  o.watt = p;
+  p += s.C;
+  o.total = p;
+  return o;
+}
+
+// ------------------------------------------------------------ launchers --
+template <int LMAX, int MMAX>
+struct Launch {
+  template <typename T, typename TA>
+  static void rotate_in(const egnn_graph *g, const LayerShape &s, const float *geom, const T *x, const float *wrad,
+                        const Acts &a, hipStream_t st) {
+    Ptr3 A{{a.A[0], a.A[1], a.A[2]}};
+    rotate_in_kernel<LMAX, MMAX, T, TA><<<ceil_div(g->n_edges, kWavesPerBlock), kThreads, 0, st>>>(
+        g->src, geom, s.gstride, g->n_edges, x, s.C, wrad, s.n_rbf, A);
+  }
+  template <typename T>
+  static void aggregate(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const T *x,
+                        T *x_out, T *edge_out, hipStream_t st) {
+    CPtr3 Y{{a.Y[0], a.Y[1], a.Y[2]}};
+    const unsigned grid = ceil_div(g->n_dst, kWavesPerBlock);
+    if (s.C <= 64)
+      aggregate_kernel<LMAX, MMAX, 1, T><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y,
+                                                                    s.C, x, x_out, edge_out);
+    else if (s.C <= 128)
+      aggregate_kernel<LMAX, MMAX, 2, T><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y,
+                                                                    s.C, x, x_out, edge_out);
+    else
+      aggregate_kernel<LMAX, MMAX, 4, T><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y,
+                                                                    s.C, x, x_out, edge_out);
+  }
+  static void bwd_row(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const float *G,
+                      const float *w_att, const BwdWs &w, hipStream_t st) {
+    CPtr3 Y{{a.Y[0], a.Y[1], a.Y[2]}};
+    Ptr3 dY{{w.dY[0], w.dY[1], w.dY[2]}};
+    const unsigned grid = ceil_div(g->n_dst, kWavesPerBlock);
+    if (s.C <= 64)
+      bwd_row_kernel<LMAX, MMAX, 1><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C,
+                                                               G, w_att, dY, w.dalpha, w.watt_part);
+    else if (s.C <= 128)
+      bwd_row_kernel<LMAX, MMAX, 2><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C,
+                                                               G, w_att, dY, w.dalpha, w.watt_part);
+    else
+      bwd_row_kernel<LMAX, MMAX, 4><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C,
+                                                               G, w_att, dY, w.dalpha, w.watt_part);
+  }
+  static void bwd_gate(const egnn_graph *g, const LayerShape &s, const float *geom, const float *x, const float *wrad,
+                       const BwdWs &w, hipStream_t st) {
+    Ptr3 dA{{w.dA[0], w.dA[1], w.dA[2]}};
+    bwd_gate_kernel<LMAX, MMAX, float><<<ceil_div(g->n_edges, kWavesPerBlock), kThreads, 0, st>>>(
+        g->src, geom, s.gstride, g->n_edges, x, s.C, wrad, s.n_rbf, dA, w.dg);
+  }
+  static void bwd_node(const egnn_graph *g, const LayerShape &s, const float *geom, const float *G, const BwdWs &w,
+                       float *gx, hipStream_t st) {
+    CPtr3 dA{{w.dA[0], w.dA[1], w.dA[2]}};
+    const unsigned grid = ceil_div(g->n_src, kWavesPerBlock);
+    if (s.C <= 64)
+      bwd_node_kernel<LMAX, MMAX, 1><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, g->n_src, g->src_ptr, g->src_perm,
+                                                                geom, s.gstride, dA, s.C, G, gx);
+    else if (s.C <= 128)
+      bwd_node_kernel<LMAX, MMAX, 2><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, g->n_src, g->src_ptr, g->src_perm,
+                                                                geom, s.gstride, dA, s.C, G, gx);
+    else
+      bwd_node_kernel<LMAX, MMAX, 4><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, g->n_src, g->src_ptr, g->src_perm,
+                                                                geom, s.gstride, dA, s.C, G, gx);
+  }
+};
+
+template <int LMAX, int MMAX, typename T, typename TA>
+void launch_rotate_in(const egnn_graph *g, const LayerShape &s, const float *geom, const void *x, const float *wrad,
+                      const Acts &a, hipStream_t st) {
+  Launch<LMAX, MMAX>::template rotate_in<T, TA>(g, s, geom, static_cast<const T *>(x), wrad, a, st);
+}
+template <int LMAX, int MMAX>
+void rotate_in_f32(const egnn_graph *g, const LayerShape &s, const float *geom, const void *x, const float *wrad,
+                   const Acts &a, hipStream_t st) {
+  launch_rotate_in<LMAX, MMAX, float, float>(g, s, geom, x, wrad, a, st);
+}
+template <int LMAX, int MMAX>
+void rotate_in_bf16(const egnn_graph *g, const LayerShape &s, const float *geom, const void *x, const float *wrad,
+                    const Acts &a, hipStream_t st) {
+  launch_rotate_in<LMAX, MMAX, uint16_t, uint16_t>(g, s, geom, x, wrad, a, st);
+}
+template <int LMAX, int MMAX>
+void aggregate_f32(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const void *x,
+                   void *x_out, void *edge_out, hipStream_t st) {
+  Launch<LMAX, MMAX>::template aggregate<float>(g, s, geom, a, static_cast<const float *>(x),
+                                                static_cast<float *>(x_out), static_cast<float *>(edge_out), st);
+}
+template <int LMAX, int MMAX>
+void aggregate_bf16(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const void *x,
+                    void *x_out, void *edge_out, hipStream_t st) {
+  Launch<LMAX, MMAX>::template aggregate<uint16_t>(g, s, geom, a, static_cast<const uint16_t *>(x),
+                                                   static_cast<uint16_t *>(x_out), static_cast<uint16_t *>(edge_out),
+                                                   st);
+}
+template <int LMAX, int MMAX>
+void bwd_row_launch(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const float *G,
+                    const float *w_att, const BwdWs &w, hipStream_t st) {
+  Launch<LMAX, MMAX>::bwd_row(g, s, geom, a, G, w_att, w, st);
+}
+template <int LMAX, int MMAX>
+void bwd_gate_launch(const egnn_graph *g, const LayerShape &s, const float *geom, const float *x, const float *wrad,
+                     const BwdWs &w, hipStream_t st) {
+  Launch<LMAX, MMAX>::bwd_gate(g, s, geom, x, wrad, w, st);
+}
+template <int LMAX, int MMAX>
+void bwd_node_launch(const egnn_graph *g, const LayerShape &s, const float *geom, const float *G, const BwdWs &w,
+                     float *gx, hipStream_t st) {
+  Launch<LMAX, MMAX>::bwd_node(g, s, geom, G, w, gx, st);
+}
+
+egnn_status check_graph(const egnn_graph *g) {
+  EGNN_REQUIRE(g, "graph is null");
+  EGNN_REQUIRE(g->n_dst >= 0 && g->n_src >= g->n_dst, "graph sizes invalid");
+  EGNN_REQUIRE(g->n_edges >= 0 && g->n_edges <= g->capacity, "graph n_edges out of range");
+  EGNN_REQUIRE(g->n_edges < (int64_t(1) << 31), "more than 2^31 edges");
+  EGNN_REQUIRE(g->row_ptr, "row_ptr is null");
+  if (g->n_edges > 0) EGNN_REQUIRE(g->src && g->src_ptr && g->src_perm, "graph arrays are null");
+  return EGNN_OK;
+}
+
+}  // namespace
+}  // namespace egnn
+
+using namespace egnn;
+
+extern "C" egnn_status egnn_layer_sizes(const egnn_layer_desc *d, const egnn_graph *g, size_t *saved_bytes,
+                                        size_t *ws_fwd_bytes, size_t *ws_bwd_bytes) {
+  clear_error();
+  LayerShape s;
+  EGNN_REQUIRE(make_shape(d, &s), "invalid layer description");
+  egnn_status st = check_graph(g);
+  if (st != EGNN_OK) return st;
+  const int64_t E = g->n_edges;
+  if (saved_bytes) {
+    Carver cv{nullptr};
+    carve_acts(cv, s, E);
+    *saved_bytes = cv.off;
+  }
+  if (ws_fwd_bytes) {
+    Carver cv{nullptr};
+    carve_fwd_ws(cv, s, E);
+    carve_acts(cv, s, E);  // used when no saved buffer is given
+    *ws_fwd_bytes = cv.off;
+  }
+  if (ws_bwd_bytes) {
+    Carver cv{nullptr};
+    carve_bwd_ws(cv, s, E, g->n_dst);
+    *ws_bwd_bytes = cv.off;
+  }
+  return EGNN_OK;
+}
+
+extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph *g, const float *geom,
+                                      const float *weights, const void *x_in, void *x_out, void *edge_out,
+                                      void *saved, void *ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  LayerShape s;
+  EGNN_REQUIRE(make_shape(d, &s), "invalid layer description");
+  egnn_status st = check_graph(g);
+  if (st != EGNN_OK) return st;
+  EGNN_REQUIRE(weights && x_in && x_out, "null pointer");
+  EGNN_REQUIRE(x_in != x_out, "x_out must not alias x_in");
+  const int64_t E = g->n_edges;
+  if (E > 0) EGNN_REQUIRE(geom, "geom is null");
+  Carver cw{static_cast<char *>(ws)};
+  FwdWs fw = carve_fwd_ws(cw, s, E);
+  Acts acts;
+  if (saved) {
+    Carver cs{static_cast<char *>(saved)};
+    acts = carve_acts(cs, s, E);
+  } else {
+    acts = carve_acts(cw, s, E);
+  }
+  if (!ws || ws_bytes < cw.off) {
+    set_error("workspace of %zu bytes, need %zu", ws_bytes, cw.off);
+    return EGNN_E_WORKSPACE;
+  }
+  const WOff wo = weight_offsets(s);
+  const bool bf = s.storage == EGNN_BF16;
+  const int T = 256;
+  // expanded weights
+  for (int m = 0; m <= s.mmax; ++m) {
+    if (m == 0) {
+      if (bf) {
+        const int64_t n = static_cast<int64_t>(s.Ng[0]) * s.Kg[0];
+        to_bf16_kernel<<<ceil_div(n, T), T, 0, stream>>>(weights + wo.W0, n, static_cast<uint16_t *>(fw.B[0]));
+      }
+      continue;
+    }
+    const int rows = s.Ng[m] / 2, cols = s.Kg[m] / 2;
+    const int64_t n = static_cast<int64_t>(4) * rows * cols;
+    if (bf)
+      expand_weights_kernel<uint16_t><<<ceil_div(n, T), T, 0, stream>>>(weights + wo.W1[m], weights + wo.W2[m], rows,
+                                                                      cols, static_cast<uint16_t *>(fw.B[m]));
+    else
+      expand_weights_kernel<float><<<ceil_div(n, T), T, 0, stream>>>(weights + wo.W1[m], weights + wo.W2[m], rows, cols,
+                                                                   static_cast<float *>(fw.B[m]));
+  }
+  if (E > 0) {
+    if (bf) {
+      EGNN_DISPATCH_LM(s.lmax, s.mmax, rotate_in_bf16, g, s, geom, x_in, weights + wo.wrad, acts, stream);
+    } else {
+      EGNN_DISPATCH_LM(s.lmax, s.mmax, rotate_in_f32, g, s, geom, x_in, weights + wo.wrad, acts, stream);
+    }
+    for (int m = 0; m <= s.mmax; ++m) {
+      hipError_t e;
+      if (bf) {
+        e = gemm_bf16_nt(static_cast<int>(E), s.Ng[m], s.Kg[m], static_cast<const uint16_t *>(acts.A[m]), s.Kg[m],
+                         static_cast<const uint16_t *>(fw.B[m]), s.Kg[m], acts.Y[m], s.Ng[m], false, stream);
+      } else {
+        const float *B = m == 0 ? weights + wo.W0 : static_cast<const float *>(fw.B[m]);
+        e = gemm_f32(static_cast<int>(E), s.Ng[m], s.Kg[m], static_cast<const float *>(acts.A[m]), s.Kg[m], true, B,
+                     s.Kg[m], true, acts.Y[m], s.Ng[m], 1, 0, stream);
+      }
+      if (e != hipSuccess) {
+        set_error("GEMM launch failed: %s", hipGetErrorString(e));
+        return e == hipErrorNotSupported ? EGNN_E_UNSUPPORTED : EGNN_E_HIP;
+      }
+    }
+  }
+  if (g->n_dst > 0) {
+    if (E > 0)
+      attention_kernel<<<ceil_div(g->n_dst, kWavesPerBlock), kThreads, 0, stream>>>(
+          g->row_ptr, g->n_dst, acts.Y[0], s.Ng[0], s.C, weights + wo.watt, fw.logit, acts.alpha);
+    if (bf) {
+      EGNN_DISPATCH_LM(s.lmax, s.mmax, aggregate_bf16, g, s, geom, acts, x_in, x_out, edge_out, stream);
+    } else {
+      EGNN_DISPATCH_LM(s.lmax, s.mmax, aggregate_f32, g, s, geom, acts, x_in, x_out, edge_out, stream);
+    }
+  }
+  EGNN_CHECK_LAUNCH();
+  return EGNN_OK;
+}
+
+extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph *g, const float *geom,
+                                      const float *weights, const void *x_in, const void *saved,
+                                      const float *grad_out, float *grad_x_in, float *grad_weights, void *ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  LayerShape s;
+  EGNN_REQUIRE(make_shape(d, &s), "invalid layer description");
+  egnn_status st = check_graph(g);
+  if (st != EGNN_OK) return st;
+  if (s.storage != EGNN_F32) {
+    set_error("the backward pass supports fp32 storage only");
+    return EGNN_E_UNSUPPORTED;
+  }
+  EGNN_REQUIRE(weights && x_in && saved && grad_x_in && grad_weights, "null pointer");
+  EGNN_REQUIRE(g->n_dst == 0 || grad_out, "grad_out is null");
+  const int64_t E = g->n_edges;
+  if (E > 0) EGNN_REQUIRE(geom, "geom is null");
+  Carver cs{static_cast<char *>(const_cast<void *>(saved))};
+  const Acts acts = carve_acts(cs, s, E);
+  Carver cw{static_cast<char *>(ws)};
+  const BwdWs w = carve_bwd_ws(cw, s, E, g->n_dst);
+  if (!ws || ws_bytes < cw.off) {
+    set_error("workspace of %zu bytes, need %zu", ws_bytes, cw.off);
+    return EGNN_E_WORKSPACE;
+  }
+  const WOff wo = weight_offsets(s);
+  const int T = 256;
+  const float *x = static_cast<const float *>(x_in);
+  fill_f32<<<ceil_div(wo.total, T), T, 0, stream>>>(grad_weights, wo.total, 0.0f);
+  for (int m = 1; m <= s.mmax; ++m) {
+    const int rows = s.Ng[m] / 2, cols = s.Kg[m] / 2;
+    const int64_t n = static_cast<int64_t>(4) * rows * cols;
+    expand_weights_kernel<float><<<ceil_div(n, T), T, 0, stream>>>(weights + wo.W1[m], weights + wo.W2[m], rows, cols,
+                                                                 w.B[m]);
+  }
+  if (g->n_dst > 0 && E > 0) {
+    EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_row_launch, g, s, geom, acts, grad_out, weights + wo.watt, w, stream);
+    // w_att gradient: fixed-order sum of the per-row partials
+    colsum_kernel<<<ceil_div(s.C, 64), 256, 0, stream>>>(w.watt_part, g->n_dst, s.C, s.C, grad_weights + wo.watt);
+  }
+  if (E > 0) {
+    const int splits = dw_splits(E);
+    for (int m = 0; m <= s.mmax; ++m) {
+      const float *B = m == 0 ? weights + wo.W0 : w.B[m];
+      // dA_m = dY_m B_m
+      hipError_t e = gemm_f32(static_cast<int>(E), s.Kg[m], s.Ng[m], w.dY[m], s.Ng[m], true, B, s.Kg[m], false,
+                              w.dA[m], s.Kg[m], 1, 0, stream);
+      if (e != hipSuccess) {
+        set_error("GEMM launch failed: %s", hipGetErrorString(e));
+        return EGNN_E_HIP;
+      }
+      // dB_m = dY_m^T A_m, split over edges, then summed in order
+      const int64_t pn = static_cast<int64_t>(s.Ng[m]) * s.Kg[m];
+      e = gemm_f32(s.Ng[m], s.Kg[m], static_cast<int>(E), w.dY[m], s.Ng[m], false,
+                   static_cast<const float *>(acts.A[m]), s.Kg[m], false, w.P, s.Kg[m], splits, pn, stream);
+      if (e != hipSuccess) {
+        set_error("GEMM launch failed: %s", hipGetErrorString(e));
+        return EGNN_E_HIP;
+      }
+      if (m == 0) {
+        colsum_kernel<<<ceil_div(pn, 64), 256, 0, stream>>>(w.P, splits, pn, pn, grad_weights + wo.W0);
+      } else {
+        colsum_kernel<<<ceil_div(pn, 64), 256, 0, stream>>>(w.P, splits, pn, pn, w.Pred);
+        const int rows = s.Ng[m] / 2, cols = s.Kg[m] / 2;
+        fold_dw_kernel<<<ceil_div(static_cast<int64_t>(rows) * cols, T), T, 0, stream>>>(
+            w.Pred, rows, cols, grad_weights + wo.W1[m], grad_weights + wo.W2[m]);
+      }
+    }
+    EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_gate_launch, g, s, geom, x, weights + wo.wrad, w, stream);
+    const int ncol = s.n_pairs * 2 * s.C;
+    const int eps = static_cast<int>((E + kWradSplits - 1) / kWradSplits);
+    wrad_partial_kernel<<<dim3(ceil_div(ncol, 256), kWradSplits), 256, 0, stream>>>(geom, s.gstride, s.nD, s.n_rbf, E,
+                                                                                   w.dg, ncol, eps, w.wrad_part);
+    const int64_t nw = static_cast<int64_t>(s.n_rbf) * ncol;
+    colsum_kernel<<<ceil_div(nw, 64), 256, 0, stream>>>(w.wrad_part, kWradSplits, nw, nw, grad_weights + wo.wrad);
+  }
+  if (g->n_src > 0) {
+    if (E == 0) {
+      // no edges: dx = G on owned rows, 0 on ghosts
+      const int64_t n = static_cast<int64_t>(g->n_src) * s.K * s.C;
+      fill_f32<<<ceil_div(n, T), T, 0, stream>>>(grad_x_in, n, 0.0f);
+      if (g->n_dst > 0)
+        EGNN_TRY_HIP(hipMemcpyAsync(grad_x_in, grad_out, sizeof(float) * g->n_dst * s.K * s.C, hipMemcpyDeviceToDevice,
+                                    stream));
+    } else {
+      EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_node_launch, g, s, geom, grad_out, w, grad_x_in, stream);
+    }
+  }
+  EGNN_CHECK_LAUNCH();
+  return EGNN_OK;
+}

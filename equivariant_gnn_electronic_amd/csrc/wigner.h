@@ -1,0 +1,117 @@
+// Edge frame and Wigner-D rows, as inline host+device code.
+//
+// MALOQ Sec. III-C1 / Fig. 3(b,c): every edge is rotated onto +y; the
+// embedding of degree l is multiplied by D^l(R) of that rotation.
+//
+// D^l is built from D^1 = R by the Ivanic-Ruedenberg recursion for real
+// spherical harmonics (J. Ivanic, K. Ruedenberg, J. Phys. Chem. 100, 6342
+// (1996), with the 1998 erratum): every entry of D^l is a combination of
+// products of D^1 entries with entries of D^(l-1) in neighbouring rows.
+// In the basis used here (polar axis y, degree 1 proportional to (x, y, z),
+// no Condon-Shortley phase) the recursion applies with D^1 = R itself.
+#pragma once
+
+#include "common.h"
+
+namespace egnn {
+
+// R_e = (R_y(a) R_x(b))^T taking the unit edge direction to +y, zero roll.
+__host__ __device__ inline void edge_rotation(float vx, float vy, float vz, float R[3][3]) {
+  float n2 = vx * vx + vy * vy + vz * vz;
+  float inv = 1.0f / sqrtf(n2);
+  float x = vx * inv, y = vy * inv, z = vz * inv;
+  float s = sqrtf(x * x + z * z);
+  float ca = 1.0f, sa = 0.0f;
+  if (s > 0.0f) {
+    ca = z / s;
+    sa = x / s;
+  }
+  float cb = y, sb = s;
+  R[0][0] = ca;      R[0][1] = 0.0f; R[0][2] = -sa;
+  R[1][0] = sa * sb; R[1][1] = cb;   R[1][2] = ca * sb;
+  R[2][0] = sa * cb; R[2][1] = -sb;  R[2][2] = ca * cb;
+}
+
+// One level of the recursion: rows |m| <= MROWS of D^L from the full D^(L-1).
+// Dp: (2L-1)^2 row-major, Dl: (2L+1)^2 row-major (only rows |m| <= MROWS written).
+template <int L, int MROWS>
+__host__ __device__ inline void ir_level(const float (&R1)[3][3], const float *Dp, float *Dl) {
+  constexpr int WP = 2 * L - 1;
+  auto rp = [&](int mu, int nu) -> float { return Dp[(mu + L - 1) * WP + (nu + L - 1)]; };
+  auto r1 = [&](int i, int j) -> float { return R1[i + 1][j + 1]; };
+  auto P = [&](int i, int mu, int mp) -> float {
+    if (mp == L) return r1(i, 1) * rp(mu, L - 1) - r1(i, -1) * rp(mu, -L + 1);
+    if (mp == -L) return r1(i, 1) * rp(mu, -L + 1) + r1(i, -1) * rp(mu, L - 1);
+    return r1(i, 0) * rp(mu, mp);
+  };
+#pragma unroll
+  for (int m = -MROWS; m <= MROWS; ++m) {
+#pragma unroll
+    for (int mp = -L; mp <= L; ++mp) {
+      const int am = cabs(m);
+      const float denom = (cabs(mp) == L) ? float((2 * L) * (2 * L - 1)) : float((L + mp) * (L - mp));
+      const float d0 = (m == 0) ? 1.0f : 0.0f;
+      const float u = sqrtf(float((L + m) * (L - m)) / denom);
+      const float v = 0.5f * sqrtf((1.0f + d0) * float((L + am - 1) * (L + am)) / denom) * (1.0f - 2.0f * d0);
+      const float w = -0.5f * sqrtf(float((L - am - 1) * (L - am)) / denom) * (1.0f - d0);
+      float val = 0.0f;
+      if ((L + m) * (L - m) != 0) val += u * P(0, m, mp);
+      if (m == 0) {
+        val += v * (P(1, 1, mp) + P(-1, -1, mp));
+      } else if (m > 0) {
+        float V = P(1, m - 1, mp) * (m == 1 ? 1.41421356237309515f : 1.0f);
+        if (m != 1) V -= P(-1, -m + 1, mp);
+        val += v * V;
+        if ((L - am - 1) * (L - am) != 0) val += w * (P(1, m + 1, mp) + P(-1, -m - 1, mp));
+      } else {
+        float V = P(-1, -m - 1, mp) * (m == -1 ? 1.41421356237309515f : 1.0f);
+        if (m != -1) V += P(1, m + 1, mp);
+        val += v * V;
+        if ((L - am - 1) * (L - am) != 0) val += w * (P(1, m - 1, mp) - P(-1, -m + 1, mp));
+      }
+      Dl[(m + L) * (2 * L + 1) + (mp + L)] = val;
+    }
+  }
+}
+
+// Stored rows |m| <= MMAX of D^l(R), l = 0..LMAX, in the layout of egnn_edge_geom.
+template <int LMAX, int MMAX>
+__host__ __device__ inline void wigner_rows(const float (&R)[3][3], float *out) {
+  out[0] = 1.0f;
+  if (LMAX < 1) return;
+  float D1[9], D2[25], D3[49], D4[81];
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) D1[i * 3 + j] = R[i][j];
+  auto store = [&](int l, const float *Dl) {
+    const int mr = cmin(l, MMAX);
+    const int off = d_block_offset(l, MMAX);
+#pragma unroll
+    for (int m = -mr; m <= mr; ++m)
+#pragma unroll
+      for (int mp = -l; mp <= l; ++mp)
+        out[off + (m + mr) * (2 * l + 1) + (mp + l)] = Dl[(m + l) * (2 * l + 1) + (mp + l)];
+  };
+  store(1, D1);
+  if (LMAX < 2) return;
+  ir_level<2, (LMAX > 2 ? 2 : cmin(2, MMAX))>(R, D1, D2);
+  store(2, D2);
+  if (LMAX < 3) return;
+  ir_level<3, (LMAX > 3 ? 3 : cmin(3, MMAX))>(R, D2, D3);
+  store(3, D3);
+  if (LMAX < 4) return;
+  ir_level<4, cmin(4, MMAX)>(R, D3, D4);
+  store(4, D4);
+}
+
+// Gaussian radial basis with cosine envelope.
+__host__ __device__ inline float rbf_value(float d, int k, int n_rbf, float r_cut) {
+  const float step = r_cut / float(n_rbf - 1);
+  const float mu = float(k) * step;
+  const float t = (d - mu) / step;
+  const float env = 0.5f * (cosf(3.14159265358979323846f * d / r_cut) + 1.0f);
+  return expf(-0.5f * t * t) * env;
+}
+
+}  // namespace egnn

@@ -1,0 +1,231 @@
+/*
+ * egnn.h -- C ABI of the MI355X (gfx950) SO(2) equivariant message-passing layer.
+ *
+ * One eSCN-style layer in the incoming-edge layout, its neighbour-list
+ * builder, the per-edge Wigner-D generator and the Clebsch-Gordan decode of
+ * irreps into orbital Hamiltonian blocks.  Sources the calls follow:
+ *
+ *   [Review]  "Distributed Equivariant Graph Neural Networks for Large-Scale
+ *             Electronic Structure Prediction" (pith.science review of arXiv
+ *             2507.03840), "What carries the argument": each node owns every
+ *             edge directed into it; attention and aggregation run over
+ *             those edges.
+ *   [MALOQ]   "MALOQ: Massively Accelerated Learning of Operators for Quantum
+ *             Transport" (arXiv 2606.28911v1): Sec. III and Fig. 2(a)
+ *             (workflow), Sec. III-B1 Eq. (1) (CG transform of H blocks),
+ *             Sec. III-C1 / Fig. 3(b,c) (Wigner-D rotation of each edge to +y),
+ *             Sec. III-D (messages n_i (+) n_j, target node owns its edges),
+ *             Sec. II-B1 (SO(3) -> SO(2) reduction).
+ *
+ * Conventions shared by every call
+ *   - Every pointer is a DEVICE pointer unless marked "host".  The caller
+ *     owns every buffer; the library keeps no pointer after a call returns
+ *     and allocates no device memory inside a call.  Workspace sizes come
+ *     from the *_sizes / *_workspace queries.  Constant tables (CG
+ *     couplings) are built once per device on first use.
+ *   - All argument checks run on the host before any launch.  A failing
+ *     check returns a status and launches nothing; nothing aborts and no C++
+ *     exception crosses the ABI.  HIP failures map to EGNN_E_HIP with the
+ *     runtime's text in egnn_last_error() (thread-local).
+ *   - Work is enqueued on `stream` (NULL = the default stream) and is
+ *     asynchronous, except egnn_build_graph, which synchronises once to read
+ *     the edge count.
+ *   - Irreps are row-major [row][k][C], k = l*l + l + m, m = -l..l, in the
+ *     real spherical-harmonic basis whose polar axis is y (the axis every
+ *     edge is rotated onto) and whose degree-1 block is proportional to
+ *     (x, y, z).  Storage type is fp32 or bf16 (EGNN_BF16, x/x_out/edge_out
+ *     only); arithmetic accumulates in fp32.
+ *   - Calls on one stream may be issued from one thread at a time.
+ */
+#ifndef EGNN_H
+#define EGNN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum {
+  EGNN_OK = 0,
+  EGNN_E_ARG = 1,          /* invalid argument (null pointer, bad size, bad flag)     */
+  EGNN_E_CAPACITY = 2,     /* graph capacity too small; n_edges holds the need        */
+  EGNN_E_HIP = 3,          /* HIP runtime error; see egnn_last_error()                */
+  EGNN_E_UNSUPPORTED = 4,  /* valid request the library does not implement            */
+  EGNN_E_WORKSPACE = 5     /* workspace or saved buffer smaller than the query said   */
+} egnn_status;
+
+typedef enum { EGNN_F32 = 0, EGNN_BF16 = 1 } egnn_dtype;
+
+/* Static text for a status code (never NULL). */
+const char *egnn_status_string(int status);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *egnn_last_error(void);
+/* Library ABI version (major*100 + minor). */
+int egnn_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Neighbour graph in the incoming-edge layout  [Review; MALOQ Sec. III-D, III-D2]
+ *
+ * Rows are destinations (owned atoms 0..n_dst-1); sources are atoms
+ * 0..n_src-1, the owned atoms first and then ghosts (ghosts are never rows).
+ * Edge (s -> d, image S in Z^3) exists iff
+ *     |x_d - (x_s + S*box)| < r_cut  and not (s == d and S == 0),
+ * evaluated in fp64 as  p_a = x_s,a + S_a*box_a;  delta_a = x_d,a - p_a;
+ * d2 = (delta_x^2 + delta_y^2) + delta_z^2  (no fused multiply-add), compared
+ * with r_cut*r_cut.  Every periodic image within the cutoff is an edge (not
+ * only the minimum image).  Within a row edges are sorted by (s, S_x, S_y, S_z).
+ *   vec  = (float)delta  (source image -> destination),
+ *   dist = (float)sqrt(d2),
+ *   src_ptr/src_perm = the edge ids of each source in ascending order
+ *   (a CSR over sources, used by the backward pass).
+ * The output is deterministic (bit-identical between runs).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t n_dst, n_src;        /* rows; sources (owned first, then ghosts)                  */
+  int64_t capacity;            /* in: edges the arrays below can hold                       */
+  int64_t n_edges;             /* out: edge count (also set on EGNN_E_CAPACITY)             */
+  int32_t *row_ptr;            /* [n_dst+1]                                                 */
+  int32_t *src;                /* [capacity]                                                */
+  int8_t  *shift;              /* [capacity][3] image shift S in cell lengths               */
+  float   *vec;                /* [capacity][3] x_dst - (x_src + S*box)                     */
+  float   *dist;               /* [capacity]                                                */
+  int32_t *src_ptr;            /* [n_src+1]                                                 */
+  int32_t *src_perm;           /* [capacity]                                                */
+} egnn_graph;
+
+/* Workspace bytes for egnn_build_graph with the given capacity (host args).
+ * The cell grid covers [lo, lo+box) on every axis; periodic axes wrap with
+ * period box[a]; on open axes atoms outside the range are still handled
+ * (they fall into the border cells). */
+egnn_status egnn_build_graph_workspace(int32_t n_dst, int32_t n_src, const double lo[3] /*host*/,
+                                       const double box[3] /*host*/, uint32_t periodic_mask,
+                                       double r_cut, int64_t capacity, size_t *bytes /*host*/);
+
+/* Build the graph from positions pos [n_src][3] (fp64, device).
+ * periodic_mask: bit a set = axis a periodic.  g->n_dst, g->n_src and
+ * g->capacity are inputs.  If the graph needs more than g->capacity edges,
+ * returns EGNN_E_CAPACITY with g->n_edges = the need and writes only
+ * row_ptr; call again with larger arrays and workspace.  Calling with
+ * capacity 0 and NULL edge arrays is the way to learn the edge count
+ * (row_ptr and src_ptr, whose sizes do not depend on it, are always needed).
+ * A row or source with more than 65535 edges returns EGNN_E_UNSUPPORTED. */
+egnn_status egnn_build_graph(const double *pos, const double lo[3] /*host*/,
+                             const double box[3] /*host*/, uint32_t periodic_mask, double r_cut,
+                             egnn_graph *g /*host struct, device arrays*/, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Layer description
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t lmax;     /* degrees 0..lmax, K = (lmax+1)^2 coefficients; 1 <= lmax <= 4            */
+  int32_t mmax;     /* orders kept in the edge frame, 0 <= mmax <= min(lmax, 2)               */
+  int32_t C;        /* channels per coefficient; multiple of 8, 8 <= C <= 256                 */
+  int32_t n_rbf;    /* Gaussian radial basis size, 2 <= n_rbf <= 16                            */
+  double  r_cut;    /* cutoff of the radial envelope (same as the graph's)                    */
+  int32_t storage;  /* egnn_dtype of x / x_out / edge_out / saved activations                 */
+} egnn_layer_desc;
+
+/* Packed fp32 weight count of one layer.  Order and row-major shapes:
+ *   W0      [(lmax+1) C][(lmax+1) 2C]           (m = 0)
+ *   W_m1, W_m2 for m = 1..mmax, each [(lmax-m+1) C][(lmax-m+1) 2C]
+ *   W_rad   [n_rbf][n_pairs][2C], pairs (m, l): m = 0..mmax, l = m..lmax
+ *   w_att   [C]
+ * Row index of a W block = (l_out - m) C + c_out, column = (l_in - m) 2C + c_in,
+ * input channels 0..C-1 = source, C..2C-1 = destination.  Returns 0 for an
+ * invalid description. */
+size_t egnn_layer_weight_count(const egnn_layer_desc *d);
+
+/* ---------------------------------------------------------------------------
+ * Edge geometry ("Compute Wigners", MALOQ Sec. III and III-C1, Fig. 3(b,c))
+ *
+ * Per edge: the rotation R_e taking vec/|vec| to +y with zero roll,
+ *   r = (x,y,z), s = sqrt(x^2+z^2), (cos a, sin a) = (z/s, x/s) or (1,0),
+ *   cos b = y, sin b = s,  R_e = (R_y(a) R_x(b))^T,
+ * its Wigner blocks D^l(R_e) (defined by D^l(R) Y^l(r) = Y^l(R r)), of which
+ * only the rows |m| <= mmax are stored, and the radial basis
+ *   phi_k(d) = exp(-(d - mu_k)^2 / (2 sigma^2)) (cos(pi d / r_cut) + 1) / 2,
+ *   mu_k = k r_cut / (n_rbf - 1), sigma = r_cut / (n_rbf - 1).
+ * Layout: geom [n_edges][stride] fp32, stride = egnn_geom_stride(d):
+ *   for l = 0..lmax, rows m = -min(l,mmax)..min(l,mmax), columns m' = -l..l
+ *   (row-major within l, l blocks consecutive), then phi[0..n_rbf), then the
+ *   edge's destination row as int32 bits, then zero padding.
+ * One geometry serves every layer on the same graph.
+ * ------------------------------------------------------------------------- */
+int32_t egnn_geom_stride(const egnn_layer_desc *d);     /* floats per edge, 0 if invalid */
+egnn_status egnn_edge_geom(const egnn_layer_desc *d, const egnn_graph *g, float *geom,
+                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * One message-passing layer, forward  [Review; MALOQ Sec. III, III-D, II-B1]
+ *
+ *   Xt_e  = trunc_{|m|<=mmax}( D_e x_src(e) (+) D_e x_dst(e) )      [K'][2C]
+ *   X_e   = g_e * Xt_e,  g_e[(|m|,l), c'] = sum_k phi_k(d_e) W_rad[k][(|m|,l)][c']
+ *   Y_e   : m = 0:  Y0 = W0 X0;  m >= 1:  Y+ = W_m1 X+ - W_m2 X-,
+ *                                         Y- = W_m2 X+ + W_m1 X-        [K'][C]
+ *   a_e   = sum_c w_att[c] SiLU(Y_e[l=0,m=0,c]);  alpha = softmax of a over each row
+ *   msg_e = D_e^T Yhat_e  (Yhat = Y zero-padded to K)
+ *   x_out[d] = x_in[d] + sum_{e in row d} alpha_e msg_e
+ *   edge_out[e] = msg_e   (optional; the per-edge message an edge block consumes)
+ * x_in [n_src][K][C], x_out [n_dst][K][C], edge_out [n_edges][K][C] or NULL,
+ * weights packed fp32 (egnn_layer_weight_count).  `saved` (NULL for
+ * inference) receives what egnn_layer_bwd needs; `ws` is scratch.
+ * x_out must not alias x_in.
+ * ------------------------------------------------------------------------- */
+egnn_status egnn_layer_sizes(const egnn_layer_desc *d, const egnn_graph *g,
+                             size_t *saved_bytes /*host*/, size_t *ws_fwd_bytes /*host*/,
+                             size_t *ws_bwd_bytes /*host*/);
+egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph *g, const float *geom,
+                           const float *weights, const void *x_in, void *x_out, void *edge_out,
+                           void *saved, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward of the same layer for the loss <grad_out, x_out>:
+ *   grad_x_in [n_src][K][C] (fp32, overwritten) = dL/dx_in,
+ *   grad_weights (fp32, packed like the weights, overwritten) = dL/dweights.
+ * `saved` is what egnn_layer_fwd wrote for the same inputs; grad_out
+ * [n_dst][K][C] fp32.  Reductions over edges run in a fixed order (no
+ * floating-point atomics), so results are bit-identical between runs. */
+egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph *g, const float *geom,
+                           const float *weights, const void *x_in, const void *saved,
+                           const float *grad_out, float *grad_x_in, float *grad_weights,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Label -> Matrix: Hamiltonian blocks  [MALOQ Sec. III-B1 Eq. (1), Sec. III-B2]
+ *
+ * Shells (host list shell_l, each l <= 2; n_orb = sum(2l+1) <= 32).  For
+ * ordered shell pairs (a, b) in lexicographic order and L = |la-lb|..la+lb
+ * ascending, label channel k(a,b,L) counts the earlier pairs carrying L;
+ * n_L = number of pairs carrying L.  Labels are h_L = W_L f^L (C -> n_L) and
+ *   H[off_a+i][off_b+j] = sum_{L,M} Q^{(la,lb,L)}[i][j][M] h_L[M][k(a,b,L)]
+ * with Q the real CG coupling ((D^la (x) D^lb) Q = Q D^L, orthonormal in M,
+ * first entry of magnitude > 1e-9 in row-major (i,j,M) order positive).
+ * Weights w_edge / w_node: fp32 [sum_L n_L][C], L ascending, rows k.
+ * Edge blocks read edge irreps [n_edges][K][C] (rows = source orbitals,
+ * columns = destination orbitals); on-site blocks read node irreps
+ * [n_nodes][K][C].  Either part may be skipped with n = 0 / NULL.
+ * Requires lmax >= 2*max(shell_l).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t lmax;              /* degree range of the irreps (K = (lmax+1)^2)   */
+  int32_t C;                 /* channels, multiple of 8, <= 256               */
+  int32_t n_shells;          /* 1..16                                         */
+  const int32_t *shell_l;    /* host [n_shells]                               */
+  int32_t storage;           /* egnn_dtype of the irreps                      */
+} egnn_hdesc;
+
+/* Label rows sum_L n_L for the shells (0 if invalid). */
+int32_t egnn_hblocks_label_rows(const egnn_hdesc *h);
+egnn_status egnn_hblocks(const egnn_hdesc *h, int64_t n_edges, int32_t n_nodes,
+                         const float *w_edge, const float *w_node, const void *edge_irreps,
+                         const void *node_irreps, float *h_edge /*[n_edges][n_orb][n_orb]*/,
+                         float *h_onsite /*[n_nodes][n_orb][n_orb]*/, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EGNN_H */

@@ -1,0 +1,193 @@
+"""HIP path vs the fp64 oracle, through the C ABI (needs an MI355X).
+
+Tolerances: integer graph arrays and vec bit-exact, dist within 1 ulp;
+Wigner rows and radial basis <= 1e-6 absolute; fp32 layer outputs and
+gradients <= 1e-4 normwise relative and max-abs <= 1e-4 * max|ref|;
+bf16 storage <= 2e-2 normwise against the oracle on the bf16-rounded inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import decode as odec
+from oracle import layer as olayer
+from oracle import so3
+from tests.helpers import assert_close, desc_of, grid_box, oracle_graph, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+eg = pytest.importorskip("equivariant_gnn_electronic_amd")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def gpu_graph(struct, dev):
+    lo, box = grid_box(struct)
+    pos = torch.from_numpy(struct.pos).to(dev)
+    if struct.periodic_mask == 7:
+        return eg.egnn_build_graph(pos, struct.n_dst, lo, box, 7, struct.r_cut)
+    return eg.egnn_build_graph(pos, struct.n_dst, lo, box, 0, struct.r_cut)
+
+
+def host(g):
+    return {k: getattr(g, k).cpu().numpy() for k in ("row_ptr", "src", "shift", "vec", "dist", "src_ptr", "src_perm")}
+
+
+def _check_rows(gg, og, rows):
+    for i, r in enumerate(rows):
+        b, e = gg["row_ptr"][r], gg["row_ptr"][r + 1]
+        ob, oe = og["row_ptr"][i], og["row_ptr"][i + 1]
+        assert e - b == oe - ob, f"row {r}: {e - b} vs {oe - ob} edges"
+        np.testing.assert_array_equal(gg["src"][b:e], og["src"][ob:oe])
+        np.testing.assert_array_equal(gg["shift"][b:e], og["shift"][ob:oe])
+        np.testing.assert_array_equal(gg["vec"][b:e], og["vec"][ob:oe])
+        ulp = np.abs(gg["dist"][b:e].view(np.int32) - og["dist"][ob:oe].view(np.int32))
+        assert ulp.max(initial=0) <= 1
+
+
+def _check_src_grouping(gg, n_src):
+    order = np.argsort(gg["src"], kind="stable")
+    np.testing.assert_array_equal(gg["src_perm"], order)
+    cnt = np.bincount(gg["src"], minlength=n_src)
+    np.testing.assert_array_equal(gg["src_ptr"], np.concatenate([[0], np.cumsum(cnt)]))
+
+
+@pytest.mark.parametrize("name,nrows", [("tiny", None), ("hfo2", None), ("gst", 400), ("halo", 400)])
+def test_graph_bit_exact(dev, name, nrows):
+    s = synth.make_structure(name)
+    g = gpu_graph(s, dev)
+    gg = host(g)
+    rows = np.arange(s.n_dst) if nrows is None else sample_rows(s.n_dst, nrows, 11)
+    og = oracle_graph(s, rows=None if nrows is None else rows)
+    if nrows is None:
+        assert g.n_edges == len(og["src"])
+        np.testing.assert_array_equal(gg["row_ptr"], og["row_ptr"])
+    _check_rows(gg, og, rows)
+    _check_src_grouping(gg, s.n_src)
+    # deterministic: a second build is bit-identical
+    gg2 = host(gpu_graph(s, dev))
+    for k in gg:
+        np.testing.assert_array_equal(gg[k], gg2[k])
+
+
+def test_graph_capacity_protocol_and_empty(dev):
+    s = synth.make_structure("tiny")
+    g = gpu_graph(s, dev)
+    assert g.n_edges > 0
+    # isolated atoms (open boundary, far apart): zero edges, empty rows
+    pos = torch.tensor([[0.0, 0, 0], [50.0, 0, 0], [0, 50.0, 0]], dtype=torch.float64, device=dev)
+    g0 = eg.egnn_build_graph(pos, 3, [0, 0, 0], [60.0, 60.0, 60.0], 0, 5.0)
+    assert g0.n_edges == 0
+    assert g0.row_ptr.cpu().tolist() == [0, 0, 0, 0]
+    assert g0.src_ptr.cpu().tolist() == [0, 0, 0, 0]
+
+
+def _oracle_geom_rows(vec, dist, cfg):
+    d = desc_of(cfg)
+    D = olayer.edge_wigner(vec.astype(np.float64), cfg.lmax)
+    parts = []
+    for l in range(cfg.lmax + 1):
+        mr = min(l, cfg.mmax)
+        parts.append(D[l][:, l - mr:l + mr + 1, :].reshape(len(vec), -1))
+    return np.concatenate(parts, axis=1), olayer.radial_basis(dist, d)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_l4", "hfo2"])
+def test_edge_geom(dev, name):
+    cfg = synth.CONFIGS[name]
+    s = synth.make_structure(cfg)
+    g = gpu_graph(s, dev)
+    desc = eg.layer_desc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut)
+    geom = eg.egnn_edge_geom(desc, g).cpu().numpy()
+    gg = host(g)
+    idx = np.arange(g.n_edges) if g.n_edges < 50000 else sample_rows(g.n_edges, 20000, 3)
+    Dref, phiref = _oracle_geom_rows(gg["vec"][idx], gg["dist"][idx], cfg)
+    nD = Dref.shape[1]
+    assert np.max(np.abs(geom[idx, :nD] - Dref)) <= 1e-6
+    assert np.max(np.abs(geom[idx, nD:nD + cfg.n_rbf] - phiref)) <= 1e-6
+    dst = np.repeat(np.arange(s.n_dst), np.diff(gg["row_ptr"]))
+    np.testing.assert_array_equal(geom[:g.n_edges, nD + cfg.n_rbf].view(np.int32), dst)
+
+
+def _gpu_forward(cfg, dev, edge_out=False, train=False, layer=0):
+    s = synth.make_structure(cfg)
+    x, ws = synth.make_layer_inputs(cfg)
+    g = gpu_graph(s, dev)
+    storage = eg.EGNN_BF16 if cfg.storage == "bf16" else eg.EGNN_F32
+    desc = eg.layer_desc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut, storage)
+    geom = eg.egnn_edge_geom(desc, g)
+    xt = torch.from_numpy(x).to(dev)
+    if storage == eg.EGNN_BF16:
+        xt = xt.to(torch.bfloat16)
+    wt = torch.from_numpy(ws[layer]).to(dev)
+    buf = eg.LayerBuffers(desc, g, train=train) if train else None
+    (xo, eo), buf = eg.egnn_layer_fwd(desc, g, geom, wt, xt, edge_out=edge_out, buffers=buf)
+    torch.cuda.synchronize()
+    return dict(s=s, x=x, w=ws[layer], g=g, desc=desc, geom=geom, xt=xt, wt=wt, buf=buf, xo=xo, eo=eo)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_l4"])
+def test_layer_forward_full(dev, name):
+    cfg = synth.CONFIGS[name]
+    r = _gpu_forward(cfg, dev, edge_out=True)
+    og = oracle_graph(r["s"])
+    ref = olayer.layer_forward(og, r["x"].astype(np.float64), r["w"].astype(np.float64), desc_of(cfg))
+    xo = r["xo"].float().cpu().numpy()
+    assert_close(xo, ref["x_out"], 1e-4, "x_out")
+    assert_close(xo - r["x"][:r["s"].n_dst], ref["x_out"] - r["x"][:r["s"].n_dst], 1e-4, "aggregate")
+    assert_close(r["eo"].float().cpu().numpy(), ref["edge_out"], 1e-4, "edge_out")
+
+
+def test_layer_forward_hfo2_sampled_rows(dev):
+    cfg = synth.CONFIGS["hfo2"]
+    r = _gpu_forward(cfg, dev)
+    rows = sample_rows(r["s"].n_dst, 200, 5)
+    og = oracle_graph(r["s"], rows=rows)
+    xo_ref, _ = olayer.layer_forward_rows(og, r["x"].astype(np.float64), r["w"].astype(np.float64), desc_of(cfg))
+    xo = r["xo"].float().cpu().numpy()[rows]
+    assert_close(xo, xo_ref, 1e-4, "x_out rows")
+    assert_close(xo - r["x"][rows], xo_ref - r["x"][rows], 1e-4, "aggregate rows")
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_l4"])
+def test_layer_backward_full(dev, name):
+    cfg = synth.CONFIGS[name]
+    r = _gpu_forward(cfg, dev, train=True)
+    G = synth.make_cotangent(cfg, r["s"].n_dst)
+    gx, gw = eg.egnn_layer_bwd(r["desc"], r["g"], r["geom"], r["wt"], r["xt"], r["buf"],
+                               torch.from_numpy(G).to(dev))
+    torch.cuda.synchronize()
+    og = oracle_graph(r["s"])
+    x64, w64 = r["x"].astype(np.float64), r["w"].astype(np.float64)
+    fwd = olayer.layer_forward(og, x64, w64, desc_of(cfg))
+    dx, dw = olayer.layer_backward(og, x64, w64, desc_of(cfg), fwd, G.astype(np.float64))
+    assert_close(gx.cpu().numpy(), dx, 1e-4, "grad x")
+    o = 0
+    for bname, shape in synth.layer_weight_sizes(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf):
+        n = int(np.prod(shape))
+        assert_close(gw.cpu().numpy()[o:o + n], dw[o:o + n], 1e-4, f"grad {bname}")
+        o += n
+    # deterministic
+    gx2, gw2 = eg.egnn_layer_bwd(r["desc"], r["g"], r["geom"], r["wt"], r["xt"], r["buf"],
+                                 torch.from_numpy(G).to(dev))
+    assert torch.equal(gx, gx2) and torch.equal(gw, gw2)
+
+
+def test_hblocks(dev):
+    cfg = synth.CONFIGS["tiny_l4"]
+    r = _gpu_forward(cfg, dev, edge_out=True)
+    we, wn = synth.make_decode_weights(cfg)
+    wet = torch.from_numpy(np.concatenate(we)).to(dev)
+    wnt = torch.from_numpy(np.concatenate(wn)).to(dev)
+    he, hn = eg.egnn_hblocks(4, cfg.C, wet, wnt, r["eo"], r["xo"])
+    torch.cuda.synchronize()
+    he_ref = odec.hblocks(r["eo"].cpu().numpy(), we)
+    hn_ref = odec.hblocks(r["xo"].cpu().numpy(), wn)
+    assert_close(he.cpu().numpy(), he_ref, 1e-5, "edge blocks")
+    assert_close(hn.cpu().numpy(), hn_ref, 1e-5, "on-site blocks")
