@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Throughput of the SO(2) message-passing layer on one MI355X.
+
+One step is one pass of the whole hot path over one synthetic structure,
+with inputs already resident in HBM:
+  neighbour graph build -> edge geometry (Wigner rows, radial basis) ->
+  layer forward (saving activations) -> layer backward -> Hamiltonian blocks
+  (edge and on-site).
+The default workload is the HfO2-like training step: 3,000 atoms (1,000 Hf +
+2,000 O) in a 32.8 A periodic cube, cutoff 8 A (~547k directed edges),
+lmax 4, mmax 2, C 64, fp32, one layer forward + backward, then the decode
+into 13x13 orbital blocks.  `value` is edges per second of whole steps.
+
+Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}
+FP32_VALU_PEAK_TFLOPS = 78.6   # 256 CU x 4 SIMD x 16 lanes x 2 FLOP x 2.4 GHz (no packed fp32)
+
+WORKLOADS = {
+    "train": dict(cfg="train", backward=True, decode=True, layers=1,
+                  desc="HfO2-like training step: graph + geometry + 1 layer fwd/bwd + 13x13 blocks"),
+    "hfo2": dict(cfg="hfo2", backward=False, decode=False, layers=1,
+                 desc="HfO2-like forward: graph + geometry + 1 layer fwd"),
+    "halo": dict(cfg="halo", backward=False, decode=False, layers=1,
+                 desc="one GPU's share with ghost halo: graph + geometry + 1 layer fwd"),
+    "gst": dict(cfg="gst", backward=False, decode=False, layers=3,
+                desc="GeSbTe-like 3-layer forward, bf16 storage"),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="train", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=500, help="rows of the oracle's timed sample")
+    return ap.parse_args()
+
+
+def grid_of(struct):
+    if struct.periodic_mask == 7:
+        return np.zeros(3), np.asarray(struct.box, np.float64)
+    lo = struct.pos.min(axis=0)
+    return lo, (struct.pos.max(axis=0) - lo) * (1 + 1e-12) + 1e-9
+
+
+class Step:
+    """Everything one step needs, allocated once."""
+
+    def __init__(self, wl, dev):
+        import torch
+        import synth
+        import equivariant_gnn_electronic_amd as eg
+        self.eg, self.torch = eg, torch
+        self.wl = wl
+        cfg = self.cfg = synth.CONFIGS[wl["cfg"]]
+        s = self.struct = synth.make_structure(cfg)
+        x, ws = synth.make_layer_inputs(cfg)
+        lo, box = grid_of(s)
+        self.pos = torch.from_numpy(s.pos).to(dev)
+        g0 = eg.egnn_build_graph(self.pos, s.n_dst, lo, box, s.periodic_mask, s.r_cut)
+        self.E = g0.n_edges
+        self.builder = eg.GraphBuilder(s.n_dst, s.n_src, lo, box, s.periodic_mask, s.r_cut, self.E, dev)
+        self.storage = eg.EGNN_BF16 if cfg.storage == "bf16" else eg.EGNN_F32
+        self.desc = eg.layer_desc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut, self.storage)
+        dt = torch.bfloat16 if self.storage == eg.EGNN_BF16 else torch.float32
+        self.x = torch.from_numpy(x).to(dev).to(dt)
+        self.w = [torch.from_numpy(w).to(dev) for w in ws]
+        g = self.builder.build(self.pos)
+        self.geom = eg.egnn_edge_geom(self.desc, g)
+        self.buf = eg.LayerBuffers(self.desc, g, train=wl["backward"])
+        K = cfg.K
+        # layer outputs; for a stack, ghosts keep their input irreps between layers
+        self.xs = [self.x] + [torch.empty((s.n_src, K, cfg.C), dtype=dt, device=dev) for _ in range(wl["layers"])]
+        for t in self.xs[1:]:
+            t[s.n_dst:] = self.x[s.n_dst:]
+        self.edge_out = torch.empty((max(self.E, 1), K, cfg.C), dtype=dt, device=dev) if wl["decode"] else None
+        if wl["backward"]:
+            self.G = torch.from_numpy(synth.make_cotangent(cfg, s.n_dst)).to(dev)
+            self.gx = torch.empty((s.n_src, K, cfg.C), dtype=torch.float32, device=dev)
+            self.gw = torch.empty(eg.egnn_layer_weight_count(self.desc), dtype=torch.float32, device=dev)
+        if wl["decode"]:
+            we, wn = synth.make_decode_weights(cfg)
+            self.we = torch.from_numpy(np.concatenate(we)).to(dev)
+            self.wn = torch.from_numpy(np.concatenate(wn)).to(dev)
+
+    def __call__(self):
+        eg = self.eg
+        s = self.struct
+        g = self.builder.build(self.pos)
+        eg.egnn_edge_geom(self.desc, g, out=self.geom)
+        for i in range(self.wl["layers"]):
+            last = i == self.wl["layers"] - 1
+            eo = self.edge_out if (last and self.wl["decode"]) else None
+            self._fwd(g, i, eo)
+        if self.wl["backward"]:
+            eg.egnn_layer_bwd(self.desc, g, self.geom, self.w[0], self.xs[0], self.buf, self.G,
+                              grad_x=self.gx, grad_w=self.gw)
+        if self.wl["decode"]:
+            eg.egnn_hblocks(self.cfg.lmax, self.cfg.C, self.we, self.wn, self.edge_out[:self.E],
+                            self.xs[-1][:s.n_dst])
+        return g
+
+    def _fwd(self, g, i, eo):
+        import ctypes as ct
+        eg = self.eg
+        lib = eg._lib.load()
+        gs = g.c_struct()
+        xin, xout = self.xs[i], self.xs[i + 1]
+        eg._lib.check("egnn_layer_fwd", lib.egnn_layer_fwd(
+            ct.byref(self.desc), ct.byref(gs), eg._ptr(self.geom), eg._ptr(self.w[i]), eg._ptr(xin),
+            eg._ptr(xout), eg._ptr(eo) if eo is not None else None,
+            eg._ptr(self.buf.saved) if self.buf.saved is not None else None, eg._ptr(self.buf.ws),
+            self.buf.ws.numel(), eg._stream()))
+
+
+def roofline(timing, dtype):
+    """Dominant kernel family by total time, with its achieved rate against the peak."""
+    fam, t = max(timing.items(), key=lambda kv: kv[1]["total_ms"])
+    per_launch_ms = t["total_ms"] / t["launches"]
+    if t["flops"] > 0:
+        achieved = t["flops"] / t["launches"] / (per_launch_ms * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS["bf16" if "bf16" in fam else "f32"]
+        return fam, dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                         frac=round(achieved / peak, 4), traffic=None)
+    achieved = t["bytes"] / t["launches"] / (per_launch_ms * 1e-3) / 1e9
+    return fam, dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
+
+
+def cpu_baseline(wl, rows_n):
+    """The fp64 oracle on a sample of destination rows of the same structure.
+
+    The sampled rows become the first rows of a relabelled problem (all atoms
+    stay sources), so the oracle does exactly the per-edge work of the full
+    step for the sampled rows' edges: brute-force neighbour rows, layer
+    forward, backward and decode.
+    """
+    import synth
+    from oracle import decode, layer, neighbors
+    cfg = synth.CONFIGS[wl["cfg"]]
+    s = synth.make_structure(cfg)
+    x, ws = synth.make_layer_inputs(cfg)
+    rows = np.sort(np.random.default_rng(0).choice(s.n_dst, min(rows_n, s.n_dst), replace=False))
+    perm = np.concatenate([rows, np.setdiff1d(np.arange(s.n_src), rows)])
+    pos, xp = s.pos[perm], x[perm].astype(np.float64)
+    d = layer.LayerDesc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut)
+    t0 = time.perf_counter()
+    g = neighbors.build_graph(pos, len(rows), s.box, s.periodic_mask, s.r_cut)
+    xl = xp
+    for i in range(wl["layers"]):
+        f = layer.layer_forward(g, xl, ws[i].astype(np.float64), d)
+        xl = np.concatenate([f["x_out"], xl[len(rows):]])
+    if wl["backward"]:
+        G = synth.make_cotangent(cfg, s.n_dst)[rows].astype(np.float64)
+        layer.layer_backward(g, xp, ws[0].astype(np.float64), d, f, G)
+    if wl["decode"]:
+        we, wn = synth.make_decode_weights(cfg)
+        decode.hblocks(f["edge_out"], we)
+        decode.hblocks(f["x_out"], wn)
+    dt = time.perf_counter() - t0
+    E = len(g["src"])
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return dict(value=round(E / dt, 2), unit="edges/s", cores=int(threads), kind="oracle",
+                sample=f"{len(rows)} destination rows ({E} edges) of the same structure, fp64 numpy, "
+                       f"{dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is not built",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    wl = WORKLOADS[args.workload]
+    step = Step(wl, dev)
+    eg = step.eg
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    eg.egnn_timing_reset()
+    eg.egnn_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    eg.egnn_timing_enable(False)
+    timing, dropped = eg.egnn_timing_collect()
+    ms = (t1 - t0) * 1e3 / args.steps
+    E = step.E
+    cfg = step.cfg
+    dtype = "bf16" if cfg.storage == "bf16" else "f32"
+    fam, roof = roofline(timing, dtype)
+    kernels = {k: dict(launches_per_step=v["launches"] / args.steps, ms_per_step=round(v["total_ms"] / args.steps, 4))
+               for k, v in sorted(timing.items(), key=lambda kv: -kv[1]["total_ms"])}
+    out = {
+        "metric": "edges/s per SO(2) message-passing layer (fwd+bwd) + % of HBM/MFMA roofline",
+        "value": round(E * args.steps / (t1 - t0), 1),
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded RSA structure, N(0,1) irreps, N(0,1/fan_in) weights)",
+        "config": {"workload": args.workload, "description": wl["desc"], "atoms": step.struct.n_dst,
+                   "sources": step.struct.n_src, "edges": E, "lmax": cfg.lmax, "mmax": cfg.mmax, "C": cfg.C,
+                   "layers": wl["layers"], "r_cut": cfg.r_cut, "storage": cfg.storage,
+                   "nodes_per_s": round(step.struct.n_dst * args.steps / (t1 - t0), 1)},
+        "roofline": dict(kernel=fam, **roof),
+        "kernels": kernels,
+        "timing_events_dropped": dropped,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

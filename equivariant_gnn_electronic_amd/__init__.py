@@ -18,7 +18,8 @@ from ._lib import EGNN_BF16, EGNN_F32, EgnnError
 
 __all__ = ["Graph", "layer_desc", "egnn_build_graph", "egnn_edge_geom", "egnn_geom_stride",
            "egnn_layer_weight_count", "egnn_layer_sizes", "egnn_layer_fwd", "egnn_layer_bwd",
-           "egnn_hblocks", "egnn_hblocks_label_rows", "EgnnError", "EGNN_F32", "EGNN_BF16"]
+           "egnn_hblocks", "egnn_hblocks_label_rows", "egnn_timing_enable", "egnn_timing_collect",
+           "egnn_timing_reset", "GraphBuilder", "LayerBuffers", "EgnnError", "EGNN_F32", "EGNN_BF16"]
 
 _STORAGE = {EGNN_F32: torch.float32, EGNN_BF16: torch.bfloat16}
 
@@ -112,6 +113,65 @@ def egnn_build_graph(pos, n_dst, lo, box, periodic_mask, r_cut, capacity=None):
         return Graph(n_dst, n_src, E, row_ptr, a["src"][:E], a["shift"][:E], a["vec"][:E], a["dist"][:E],
                      a["src_ptr"], a["src_perm"][:E])
     raise RuntimeError("egnn_build_graph: edge count changed between the two passes")
+
+
+class GraphBuilder:
+    """Repeated egnn_build_graph calls on one structure size with preallocated arrays.
+
+    The arrays and workspace are sized for `capacity` edges once; each
+    build() is a single C call (one edge count + fill).
+    """
+
+    def __init__(self, n_dst, n_src, lo, box, periodic_mask, r_cut, capacity, device):
+        self.n_dst, self.n_src, self.mask, self.r_cut = n_dst, n_src, periodic_mask, float(r_cut)
+        self.lo3, self.box3 = _d3(lo), _d3(box)
+        c = max(int(capacity), 1)
+        self.cap = int(capacity)
+        self.row_ptr = torch.empty(n_dst + 1, dtype=torch.int32, device=device)
+        self.src = torch.empty(c, dtype=torch.int32, device=device)
+        self.shift = torch.empty((c, 3), dtype=torch.int8, device=device)
+        self.vec = torch.empty((c, 3), dtype=torch.float32, device=device)
+        self.dist = torch.empty(c, dtype=torch.float32, device=device)
+        self.src_ptr = torch.empty(n_src + 1, dtype=torch.int32, device=device)
+        self.src_perm = torch.empty(c, dtype=torch.int32, device=device)
+        ws_bytes = ct.c_size_t()
+        _lib.check("egnn_build_graph_workspace", _lib.load().egnn_build_graph_workspace(
+            n_dst, n_src, self.lo3, self.box3, periodic_mask, self.r_cut, self.cap, ct.byref(ws_bytes)))
+        self.ws = torch.empty(max(ws_bytes.value, 1), dtype=torch.uint8, device=device)
+        self.g = _lib.EgnnGraph()
+        g = self.g
+        g.n_dst, g.n_src, g.capacity = n_dst, n_src, self.cap
+        for f in ("row_ptr", "src", "shift", "vec", "dist", "src_ptr", "src_perm"):
+            setattr(g, f, getattr(self, f).data_ptr())
+
+    def build(self, pos):
+        _lib.check("egnn_build_graph", _lib.load().egnn_build_graph(
+            _ptr(pos), self.lo3, self.box3, self.mask, self.r_cut, ct.byref(self.g), _ptr(self.ws),
+            self.ws.numel(), _stream()))
+        E = int(self.g.n_edges)
+        return Graph(self.n_dst, self.n_src, E, self.row_ptr, self.src[:E], self.shift[:E], self.vec[:E],
+                     self.dist[:E], self.src_ptr, self.src_perm[:E])
+
+
+def egnn_timing_enable(on=True):
+    _lib.check("egnn_timing_enable", _lib.load().egnn_timing_enable(1 if on else 0))
+
+
+def egnn_timing_reset():
+    _lib.load().egnn_timing_reset()
+
+
+def egnn_timing_collect():
+    """{kernel family: {launches, total_ms, flops, bytes}} accumulated so far (waits for the GPU)."""
+    out = (_lib.EgnnTimingEntry * 64)()
+    dropped = ct.c_int64()
+    n = _lib.load().egnn_timing_collect(out, 64, ct.byref(dropped))
+    res = {}
+    for i in range(n):
+        e = out[i]
+        res[e.name.decode()] = dict(launches=int(e.launches), total_ms=float(e.total_ms), flops=float(e.flops),
+                                    bytes=float(e.bytes))
+    return res, int(dropped.value)
 
 
 def egnn_geom_stride(desc):

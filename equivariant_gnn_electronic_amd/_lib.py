@@ -29,6 +29,11 @@ class EgnnHDesc(ct.Structure):
                 ("shell_l", ct.POINTER(ct.c_int32)), ("storage", ct.c_int32)]
 
 
+class EgnnTimingEntry(ct.Structure):
+    _fields_ = [("name", ct.c_char * 48), ("launches", ct.c_int64), ("total_ms", ct.c_double),
+                ("flops", ct.c_double), ("bytes", ct.c_double)]
+
+
 _D3 = ct.POINTER(ct.c_double)
 _G = ct.POINTER(EgnnGraph)
 _L = ct.POINTER(EgnnLayerDesc)
@@ -49,6 +54,9 @@ SIGNATURES = {
     "egnn_layer_bwd": (ct.c_int, [_L, _G, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "egnn_hblocks_label_rows": (ct.c_int32, [_H]),
     "egnn_hblocks": (ct.c_int, [_H, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "egnn_timing_enable": (ct.c_int, [ct.c_int]),
+    "egnn_timing_collect": (ct.c_int, [ct.POINTER(EgnnTimingEntry), ct.c_int, ct.POINTER(ct.c_int64)]),
+    "egnn_timing_reset": (None, []),
 }
 
 _lib = None

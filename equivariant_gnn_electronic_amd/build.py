@@ -21,13 +21,13 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libegnn.so")
 
-SOURCES = ["common.hip", "graph.hip", "geom.hip", "gemm.hip", "layer.hip", "hblocks.hip"]
+SOURCES = ["common.hip", "timing.hip", "graph.hip", "geom.hip", "gemm.hip", "layer.hip", "hblocks.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-    # packed fp32 instructions stay off ("Build")
+    # no packed-fp32 (v_pk_*_f32) instructions in the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
     f"-I{INCLUDE}", f"-I{CSRC}",

@@ -8,6 +8,7 @@
 // rows |m| <= mmax that the layer consumes are stored, plus the radial basis.
 #include "common.h"
 #include "wigner.h"
+#include "timing.h"
 
 namespace egnn {
 namespace {
@@ -61,6 +62,7 @@ extern "C" egnn_status egnn_edge_geom(const egnn_layer_desc *d, const egnn_graph
   EGNN_REQUIRE(g->n_edges >= 0 && g->n_edges <= g->capacity, "graph n_edges out of range");
   if (g->n_edges == 0) return EGNN_OK;
   EGNN_REQUIRE(geom && g->vec && g->dist && g->row_ptr, "null pointer");
+  Timed t(stream, "edge_geom", 0.0, double(g->n_edges) * (16.0 + s.gstride * 4.0));
   EGNN_DISPATCH_LM(s.lmax, s.mmax, launch_geom, g, s, geom, stream);
   EGNN_CHECK_LAUNCH();
   return EGNN_OK;

@@ -16,6 +16,7 @@
 #pragma clang fp contract(off)
 
 #include "common.h"
+#include "timing.h"
 
 namespace egnn {
 namespace {
@@ -364,6 +365,9 @@ extern "C" egnn_status egnn_build_graph(const double *pos, const double lo[3], c
   }
   const double rc2 = r_cut * r_cut;
   const int T = 256;
+  const int rows_per_block = T / kWave;
+  {
+  Timed t_count(stream, "graph_count", 0.0, double(n_src) * 24.0 + double(n_dst) * 4.0);
   // cells
   fill_int<<<ceil_div(g.n_cells, T), T, 0, stream>>>(w.cell_count, g.n_cells, 0);
   fill_int<<<ceil_div(g.n_cells, T), T, 0, stream>>>(w.cell_cursor, g.n_cells, 0);
@@ -376,12 +380,12 @@ extern "C" egnn_status egnn_build_graph(const double *pos, const double lo[3], c
     scatter_atoms<<<ceil_div(n_src, T), T, 0, stream>>>(n_src, w.atom_cell, w.cell_start, w.cell_cursor,
                                                         w.cell_atoms);
   // rows: count, scan
-  const int rows_per_block = T / kWave;
   if (n_dst > 0)
     row_pass<0><<<ceil_div(n_dst, rows_per_block), T, 0, stream>>>(
         pos, n_dst, g, rc2, w.ucell, w.cell_start, w.cell_atoms, w.row_count, nullptr, nullptr, w.scalars + 2);
   scan_exclusive<<<1, kScanThreads, 0, stream>>>(w.row_count, gr->row_ptr, n_dst, w.scalars + 0, w.scalars + 1);
   EGNN_CHECK_LAUNCH();
+  }
   int host[4];
   EGNN_TRY_HIP(hipMemcpyAsync(host, w.scalars, sizeof(host), hipMemcpyDeviceToHost, stream));
   EGNN_TRY_HIP(hipStreamSynchronize(stream));
@@ -405,6 +409,7 @@ extern "C" egnn_status egnn_build_graph(const double *pos, const double lo[3], c
     return EGNN_E_CAPACITY;
   }
   // rows: fill keys, sort, write
+  Timed t_fill(stream, "graph_fill", 0.0, double(E) * (4.0 + 3.0 + 12.0 + 4.0 + 4.0) + double(n_src) * 4.0);
   if (n_dst > 0 && E > 0) {
     row_pass<1><<<ceil_div(n_dst, rows_per_block), T, 0, stream>>>(
         pos, n_dst, g, rc2, w.ucell, w.cell_start, w.cell_atoms, nullptr, gr->row_ptr, w.keys, w.scalars + 2);

@@ -22,6 +22,7 @@
 #include <vector>
 
 #include "common.h"
+#include "timing.h"
 
 namespace egnn {
 namespace {
@@ -300,6 +301,8 @@ egnn_status launch_hblocks(int slot, int64_t rows, const void *irreps, int K, in
     set_error("decode needs %zu bytes of LDS; reduce C or the shell list", smem);
     return EGNN_E_UNSUPPORTED;
   }
+  Timed t(stream, "hblocks", 0.0,
+          double(rows) * (double(K) * C * sizeof(T) + double(n_ent) * 4.0) + double(C) * n_w * 4.0);
   int64_t blocks = (rows + kWaves - 1) / kWaves;
   if (blocks > 4096) blocks = 4096;
   hblocks_kernel<T><<<static_cast<unsigned>(blocks), kWave * kWaves, smem, stream>>>(

@@ -24,6 +24,7 @@
 
 #include "common.h"
 #include "gemm.h"
+#include "timing.h"
 
 namespace egnn {
 namespace {
@@ -103,38 +104,63 @@ __global__ void to_bf16_kernel(const float *in, int64_t n, uint16_t *out) {
 }
 
 // --------------------------------------------------------------- forward --
-template <int LMAX, int MMAX, typename T, typename TA>
+// Persistent layout of the per-edge kernels: a wave owns one 64-slot chunk
+// of the 2C message channels (slot 0..C-1 = source, C..2C-1 = destination)
+// and walks a strided stream of edges.  The radial weights of its slots stay
+// in registers for the whole stream, so a gate costs n_rbf FMAs and no loads.
+struct EdgeStreams {
+  int nchunks;   // 64-slot chunks of the 2C channels
+  int nstreams;  // edge streams; wave gw serves chunk gw % nchunks of stream gw / nchunks
+};
+__host__ __device__ inline EdgeStreams edge_streams(int64_t E, int C, int max_streams) {
+  EdgeStreams r;
+  r.nchunks = (2 * C + kWave - 1) / kWave;
+  int64_t ns = E < max_streams ? E : max_streams;
+  r.nstreams = static_cast<int>(ns < 1 ? 1 : ns);
+  return r;
+}
+constexpr int kFwdStreams = 4096;
+constexpr int kBwdStreams = 2048;
+
+template <int LMAX, int MMAX, int NRBF, typename T, typename TA>
 __global__ void __launch_bounds__(kThreads) rotate_in_kernel(const int *__restrict__ src, const float *__restrict__ geom,
                                                              int gstride, int64_t E, const T *__restrict__ x, int C,
-                                                             const float *__restrict__ wrad, int n_rbf, Ptr3 A) {
+                                                             const float *__restrict__ wrad, int n_rbf, EdgeStreams es,
+                                                             Ptr3 A) {
   using L = Lay<LMAX, MMAX>;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t e64 = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-  if (e64 >= E) return;
-  const int e = uniform(static_cast<int>(e64));
-  const float *gr = geom + static_cast<int64_t>(e) * gstride;
-  const int s = uniform(src[e]);
-  const int d = uniform(__float_as_int(gr[L::ND + n_rbf]));
-  float phi[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) phi[k] = k < n_rbf ? gr[L::ND + k] : 0.0f;
+  const int gw = uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  if (gw >= es.nchunks * es.nstreams) return;
+  const int chunk = gw % es.nchunks, stream = gw / es.nchunks;
   const int C2 = 2 * C;
-  for (int j = lane; j < C2; j += kWave) {
-    const bool is_src = j < C;
-    const int c = is_src ? j : j - C;
-    const T *xr = x + static_cast<int64_t>(is_src ? s : d) * L::K * C + c;
+  const int j = chunk * kWave + lane;
+  const bool active = j < C2;
+  const bool is_src = j < C;
+  const int c = is_src ? j : j - C;
+  float wr[NRBF][L::NP];
+#pragma unroll
+  for (int k = 0; k < NRBF; ++k)
+#pragma unroll
+    for (int p = 0; p < L::NP; ++p)
+      wr[k][p] = (active && k < n_rbf) ? wrad[(static_cast<int64_t>(k) * L::NP + p) * C2 + j] : 0.0f;
+  for (int64_t e64 = stream; e64 < E; e64 += es.nstreams) {
+    const int e = static_cast<int>(e64);
+    const float *gr = geom + static_cast<int64_t>(e) * gstride;
+    const int node = is_src ? src[e] : __float_as_int(gr[L::ND + n_rbf]);
+    float g[L::NP];
+#pragma unroll
+    for (int p = 0; p < L::NP; ++p) g[p] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NRBF; ++k) {
+      const float ph = k < n_rbf ? gr[L::ND + k] : 0.0f;
+#pragma unroll
+      for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[k][p];
+    }
+    if (!active) continue;
+    const T *xr = x + static_cast<int64_t>(node) * L::K * C + c;
     float xv[L::K];
 #pragma unroll
     for (int k = 0; k < L::K; ++k) xv[k] = Store<T>::ld(xr + k * C);
-    float g[L::NP];
-#pragma unroll
-    for (int p = 0; p < L::NP; ++p) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k)
-        if (k < n_rbf) acc += phi[k] * wrad[(static_cast<int64_t>(k) * L::NP + p) * C2 + j];
-      g[p] = acc;
-    }
 #pragma unroll
     for (int l = 0; l <= LMAX; ++l) {
 #pragma unroll
@@ -335,28 +361,42 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
 }
 
 // Per edge: recompute Xt (edge-frame input before the gate) and g; the GEMM
-// gradient dX (in dA) becomes dXt = g * dX in place; dg = sum_{+-m} dX * Xt.
-template <int LMAX, int MMAX, typename T>
+// gradient dX (in dA) becomes dXt = g * dX in place; dg = sum_{+-m} dX * Xt,
+// and the radial-weight gradient sum_e phi_e[k] dg_e is accumulated in
+// registers along the wave's edge stream and written once per stream
+// (part[stream][k][pair][slot]); the streams are summed later in a fixed order.
+template <int LMAX, int MMAX, int NRBF, typename T>
 __global__ void __launch_bounds__(kThreads) bwd_gate_kernel(const int *__restrict__ src, const float *__restrict__ geom,
                                                             int gstride, int64_t E, const T *__restrict__ x, int C,
-                                                            const float *__restrict__ wrad, int n_rbf, Ptr3 dA,
-                                                            float *__restrict__ dg) {
+                                                            const float *__restrict__ wrad, int n_rbf, EdgeStreams es,
+                                                            Ptr3 dA, float *__restrict__ part) {
   using L = Lay<LMAX, MMAX>;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t e64 = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-  if (e64 >= E) return;
-  const int e = uniform(static_cast<int>(e64));
-  const float *gr = geom + static_cast<int64_t>(e) * gstride;
-  const int s = uniform(src[e]);
-  const int d = uniform(__float_as_int(gr[L::ND + n_rbf]));
-  float phi[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) phi[k] = k < n_rbf ? gr[L::ND + k] : 0.0f;
+  const int gw = uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  if (gw >= es.nchunks * es.nstreams) return;
+  const int chunk = gw % es.nchunks, stream = gw / es.nchunks;
   const int C2 = 2 * C;
-  for (int j = lane; j < C2; j += kWave) {
-    const bool is_src = j < C;
-    const int c = is_src ? j : j - C;
-    const T *xr = x + static_cast<int64_t>(is_src ? s : d) * L::K * C + c;
+  const int j = chunk * kWave + lane;
+  const bool active = j < C2;
+  const bool is_src = j < C;
+  const int c = is_src ? j : j - C;
+  float wr[NRBF][L::NP], acc[NRBF][L::NP];
+#pragma unroll
+  for (int k = 0; k < NRBF; ++k)
+#pragma unroll
+    for (int p = 0; p < L::NP; ++p) {
+      wr[k][p] = (active && k < n_rbf) ? wrad[(static_cast<int64_t>(k) * L::NP + p) * C2 + j] : 0.0f;
+      acc[k][p] = 0.0f;
+    }
+  for (int64_t e64 = stream; e64 < E; e64 += es.nstreams) {
+    const int e = static_cast<int>(e64);
+    const float *gr = geom + static_cast<int64_t>(e) * gstride;
+    const int node = is_src ? src[e] : __float_as_int(gr[L::ND + n_rbf]);
+    float ph[NRBF];
+#pragma unroll
+    for (int k = 0; k < NRBF; ++k) ph[k] = k < n_rbf ? gr[L::ND + k] : 0.0f;
+    if (!active) continue;
+    const T *xr = x + static_cast<int64_t>(node) * L::K * C + c;
     float xv[L::K];
 #pragma unroll
     for (int k = 0; k < L::K; ++k) xv[k] = Store<T>::ld(xr + k * C);
@@ -374,8 +414,7 @@ __global__ void __launch_bounds__(kThreads) bwd_gate_kernel(const int *__restric
         const int p = pair_index(mu, l, LMAX);
         float g = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 16; ++k)
-          if (k < n_rbf) g += phi[k] * wrad[(static_cast<int64_t>(k) * L::NP + p) * C2 + j];
+        for (int k = 0; k < NRBF; ++k) g += ph[k] * wr[k][p];
         float *Am = static_cast<float *>(dA.p[mu]);
         const int64_t o = static_cast<int64_t>(e) * L::blocks(mu) * C2 + L::col(l, m) * C2 + j;
         const float dx = Am[o];
@@ -384,8 +423,16 @@ __global__ void __launch_bounds__(kThreads) bwd_gate_kernel(const int *__restric
       }
     }
 #pragma unroll
-    for (int p = 0; p < L::NP; ++p) dg[(static_cast<int64_t>(e) * L::NP + p) * C2 + j] = dgp[p];
+    for (int k = 0; k < NRBF; ++k)
+#pragma unroll
+      for (int p = 0; p < L::NP; ++p) acc[k][p] += ph[k] * dgp[p];
   }
+  if (!active) return;
+#pragma unroll
+  for (int k = 0; k < NRBF; ++k)
+#pragma unroll
+    for (int p = 0; p < L::NP; ++p)
+      if (k < n_rbf) part[((static_cast<int64_t>(stream) * n_rbf + k) * L::NP + p) * C2 + j] = acc[k][p];
 }
 
 // Per node n: grad_x[n] = G[n] (owned rows) + sum over its incoming edges of
@@ -480,29 +527,6 @@ __global__ void fold_dw_kernel(const float *P, int rows, int cols, float *dw1, f
   dw2[i] = -pm + mp;
 }
 
-// Partial radial-weight gradient of one edge split: part[z][k][col] = sum_e phi_e[k] dg[e][col].
-__global__ void __launch_bounds__(256) wrad_partial_kernel(const float *__restrict__ geom, int gstride, int nd,
-                                                           int n_rbf, int64_t E, const float *__restrict__ dg,
-                                                           int ncol, int edges_per_split, float *__restrict__ part) {
-  const int col = blockIdx.x * blockDim.x + threadIdx.x;
-  const int z = blockIdx.y;
-  const int64_t e0 = static_cast<int64_t>(z) * edges_per_split;
-  const int64_t e1 = e0 + edges_per_split < E ? e0 + edges_per_split : E;
-  float acc[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
-  if (col < ncol) {
-    for (int64_t e = e0; e < e1; ++e) {
-      const float v = dg[e * ncol + col];
-      const float *ph = geom + e * gstride + nd;
-#pragma unroll
-      for (int k = 0; k < 16; ++k)
-        if (k < n_rbf) acc[k] += ph[k] * v;
-    }
-    for (int k = 0; k < n_rbf; ++k) part[(static_cast<int64_t>(z) * n_rbf + k) * ncol + col] = acc[k];
-  }
-}
-
 __global__ void fill_f32(float *p, int64_t n, float v) {
   int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -564,14 +588,12 @@ int dw_splits(int64_t E) {
   if (s > 64) s = 64;
   return static_cast<int>(s);
 }
-constexpr int kWradSplits = 128;
 
 struct BwdWs {
   float *B[3];
   float *dY[3];
   float *dA[3];
   float *dalpha;
-  float *dg;
   float *watt_part;
   float *P;        // split partials of the largest m
   float *Pred;     // reduced partials
@@ -588,11 +610,11 @@ BwdWs carve_bwd_ws(Carver &cv, const LayerShape &s, int64_t E, int n_dst) {
     pmax = pmax > static_cast<size_t>(s.Ng[m]) * s.Kg[m] ? pmax : static_cast<size_t>(s.Ng[m]) * s.Kg[m];
   }
   w.dalpha = cv.take<float>(E);
-  w.dg = cv.take<float>(static_cast<size_t>(E) * s.n_pairs * 2 * s.C);
   w.watt_part = cv.take<float>(static_cast<size_t>(n_dst > 0 ? n_dst : 1) * s.C);
   w.P = cv.take<float>(pmax * dw_splits(E));
   w.Pred = cv.take<float>(pmax);
-  w.wrad_part = cv.take<float>(static_cast<size_t>(kWradSplits) * s.n_rbf * s.n_pairs * 2 * s.C);
+  w.wrad_part = cv.take<float>(static_cast<size_t>(edge_streams(E, s.C, kBwdStreams).nstreams) * s.n_rbf *
+                               s.n_pairs * 2 * s.C);
   return w;
 }
 
@@ -626,8 +648,14 @@ struct Launch {
   static void rotate_in(const egnn_graph *g, const LayerShape &s, const float *geom, const T *x, const float *wrad,
                         const Acts &a, hipStream_t st) {
     Ptr3 A{{a.A[0], a.A[1], a.A[2]}};
-    rotate_in_kernel<LMAX, MMAX, T, TA><<<ceil_div(g->n_edges, kWavesPerBlock), kThreads, 0, st>>>(
-        g->src, geom, s.gstride, g->n_edges, x, s.C, wrad, s.n_rbf, A);
+    const EdgeStreams es = edge_streams(g->n_edges, s.C, kFwdStreams);
+    const unsigned grid = ceil_div(static_cast<int64_t>(es.nchunks) * es.nstreams, kWavesPerBlock);
+    if (s.n_rbf <= 8)
+      rotate_in_kernel<LMAX, MMAX, 8, T, TA><<<grid, kThreads, 0, st>>>(g->src, geom, s.gstride, g->n_edges, x, s.C,
+                                                                        wrad, s.n_rbf, es, A);
+    else
+      rotate_in_kernel<LMAX, MMAX, 16, T, TA><<<grid, kThreads, 0, st>>>(g->src, geom, s.gstride, g->n_edges, x, s.C,
+                                                                         wrad, s.n_rbf, es, A);
   }
   template <typename T>
   static void aggregate(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const T *x,
@@ -662,8 +690,14 @@ struct Launch {
   static void bwd_gate(const egnn_graph *g, const LayerShape &s, const float *geom, const float *x, const float *wrad,
                        const BwdWs &w, hipStream_t st) {
     Ptr3 dA{{w.dA[0], w.dA[1], w.dA[2]}};
-    bwd_gate_kernel<LMAX, MMAX, float><<<ceil_div(g->n_edges, kWavesPerBlock), kThreads, 0, st>>>(
-        g->src, geom, s.gstride, g->n_edges, x, s.C, wrad, s.n_rbf, dA, w.dg);
+    const EdgeStreams es = edge_streams(g->n_edges, s.C, kBwdStreams);
+    const unsigned grid = ceil_div(static_cast<int64_t>(es.nchunks) * es.nstreams, kWavesPerBlock);
+    if (s.n_rbf <= 8)
+      bwd_gate_kernel<LMAX, MMAX, 8, float><<<grid, kThreads, 0, st>>>(g->src, geom, s.gstride, g->n_edges, x, s.C,
+                                                                       wrad, s.n_rbf, es, dA, w.wrad_part);
+    else
+      bwd_gate_kernel<LMAX, MMAX, 16, float><<<grid, kThreads, 0, st>>>(g->src, geom, s.gstride, g->n_edges, x, s.C,
+                                                                        wrad, s.n_rbf, es, dA, w.wrad_part);
   }
   static void bwd_node(const egnn_graph *g, const LayerShape &s, const float *geom, const float *G, const BwdWs &w,
                        float *gx, hipStream_t st) {
@@ -813,14 +847,27 @@ extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph
       expand_weights_kernel<float><<<ceil_div(n, T), T, 0, stream>>>(weights + wo.W1[m], weights + wo.W2[m], rows, cols,
                                                                    static_cast<float *>(fw.B[m]));
   }
+  const double xb = bf ? 2.0 : 4.0;
+  double sumK = 0, sumN = 0;
+  for (int m = 0; m <= s.mmax; ++m) {
+    sumK += s.Kg[m];
+    sumN += s.Ng[m];
+  }
   if (E > 0) {
-    if (bf) {
-      EGNN_DISPATCH_LM(s.lmax, s.mmax, rotate_in_bf16, g, s, geom, x_in, weights + wo.wrad, acts, stream);
-    } else {
-      EGNN_DISPATCH_LM(s.lmax, s.mmax, rotate_in_f32, g, s, geom, x_in, weights + wo.wrad, acts, stream);
+    {
+      const double bytes = double(g->n_src) * s.K * s.C * xb + double(E) * (s.nD + s.n_rbf + 1) * 4.0 +
+                           double(E) * 4.0 + double(E) * sumK * xb;
+      Timed t(stream, "rotate_in", 0.0, bytes);
+      if (bf) {
+        EGNN_DISPATCH_LM(s.lmax, s.mmax, rotate_in_bf16, g, s, geom, x_in, weights + wo.wrad, acts, stream);
+      } else {
+        EGNN_DISPATCH_LM(s.lmax, s.mmax, rotate_in_f32, g, s, geom, x_in, weights + wo.wrad, acts, stream);
+      }
     }
     for (int m = 0; m <= s.mmax; ++m) {
       hipError_t e;
+      Timed t(stream, bf ? "gemm_nt_bf16" : "gemm_nt_f32", 2.0 * double(E) * s.Ng[m] * s.Kg[m],
+              double(E) * (s.Kg[m] * xb + s.Ng[m] * 4.0));
       if (bf) {
         e = gemm_bf16_nt(static_cast<int>(E), s.Ng[m], s.Kg[m], static_cast<const uint16_t *>(acts.A[m]), s.Kg[m],
                          static_cast<const uint16_t *>(fw.B[m]), s.Kg[m], acts.Y[m], s.Ng[m], false, stream);
@@ -836,9 +883,14 @@ extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph
     }
   }
   if (g->n_dst > 0) {
-    if (E > 0)
+    if (E > 0) {
+      Timed t(stream, "attention", 0.0, double(E) * (s.C * 4.0 + 8.0));
       attention_kernel<<<ceil_div(g->n_dst, kWavesPerBlock), kThreads, 0, stream>>>(
           g->row_ptr, g->n_dst, acts.Y[0], s.Ng[0], s.C, weights + wo.watt, fw.logit, acts.alpha);
+    }
+    const double bytes = double(E) * (sumN * 4.0 + s.nD * 4.0 + 4.0) + 2.0 * g->n_dst * s.K * s.C * xb +
+                         (edge_out ? double(E) * s.K * s.C * xb : 0.0);
+    Timed t(stream, "aggregate", 0.0, bytes);
     if (bf) {
       EGNN_DISPATCH_LM(s.lmax, s.mmax, aggregate_bf16, g, s, geom, acts, x_in, x_out, edge_out, stream);
     } else {
@@ -884,8 +936,18 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
     expand_weights_kernel<float><<<ceil_div(n, T), T, 0, stream>>>(weights + wo.W1[m], weights + wo.W2[m], rows, cols,
                                                                  w.B[m]);
   }
+  double sumK = 0, sumN = 0;
+  for (int m = 0; m <= s.mmax; ++m) {
+    sumK += s.Kg[m];
+    sumN += s.Ng[m];
+  }
   if (g->n_dst > 0 && E > 0) {
-    EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_row_launch, g, s, geom, acts, grad_out, weights + wo.watt, w, stream);
+    {
+      const double bytes = double(g->n_dst) * s.K * s.C * 4.0 * 1.0 + double(E) * (2.0 * sumN * 4.0 + s.nD * 4.0 + 12.0) +
+                           double(g->n_dst) * s.C * 4.0;
+      Timed t(stream, "bwd_row", 0.0, bytes);
+      EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_row_launch, g, s, geom, acts, grad_out, weights + wo.watt, w, stream);
+    }
     // w_att gradient: fixed-order sum of the per-row partials
     colsum_kernel<<<ceil_div(s.C, 64), 256, 0, stream>>>(w.watt_part, g->n_dst, s.C, s.C, grad_weights + wo.watt);
   }
@@ -894,16 +956,24 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
     for (int m = 0; m <= s.mmax; ++m) {
       const float *B = m == 0 ? weights + wo.W0 : w.B[m];
       // dA_m = dY_m B_m
-      hipError_t e = gemm_f32(static_cast<int>(E), s.Kg[m], s.Ng[m], w.dY[m], s.Ng[m], true, B, s.Kg[m], false,
+      hipError_t e;
+      {
+        Timed t(stream, "gemm_nn_f32", 2.0 * double(E) * s.Ng[m] * s.Kg[m], double(E) * (s.Ng[m] + s.Kg[m]) * 4.0);
+        e = gemm_f32(static_cast<int>(E), s.Kg[m], s.Ng[m], w.dY[m], s.Ng[m], true, B, s.Kg[m], false,
                               w.dA[m], s.Kg[m], 1, 0, stream);
+      }
       if (e != hipSuccess) {
         set_error("GEMM launch failed: %s", hipGetErrorString(e));
         return EGNN_E_HIP;
       }
       // dB_m = dY_m^T A_m, split over edges, then summed in order
       const int64_t pn = static_cast<int64_t>(s.Ng[m]) * s.Kg[m];
-      e = gemm_f32(s.Ng[m], s.Kg[m], static_cast<int>(E), w.dY[m], s.Ng[m], false,
-                   static_cast<const float *>(acts.A[m]), s.Kg[m], false, w.P, s.Kg[m], splits, pn, stream);
+      {
+        Timed t(stream, "gemm_tn_f32", 2.0 * double(E) * s.Ng[m] * s.Kg[m],
+                double(E) * (s.Ng[m] + s.Kg[m]) * 4.0 + double(splits) * pn * 4.0);
+        e = gemm_f32(s.Ng[m], s.Kg[m], static_cast<int>(E), w.dY[m], s.Ng[m], false,
+                     static_cast<const float *>(acts.A[m]), s.Kg[m], false, w.P, s.Kg[m], splits, pn, stream);
+      }
       if (e != hipSuccess) {
         set_error("GEMM launch failed: %s", hipGetErrorString(e));
         return EGNN_E_HIP;
@@ -917,13 +987,16 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
             w.Pred, rows, cols, grad_weights + wo.W1[m], grad_weights + wo.W2[m]);
       }
     }
-    EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_gate_launch, g, s, geom, x, weights + wo.wrad, w, stream);
     const int ncol = s.n_pairs * 2 * s.C;
-    const int eps = static_cast<int>((E + kWradSplits - 1) / kWradSplits);
-    wrad_partial_kernel<<<dim3(ceil_div(ncol, 256), kWradSplits), 256, 0, stream>>>(geom, s.gstride, s.nD, s.n_rbf, E,
-                                                                                   w.dg, ncol, eps, w.wrad_part);
+    {
+      const double bytes = double(g->n_src) * s.K * s.C * 4.0 + double(E) * (s.nD + s.n_rbf + 1) * 4.0 + double(E) * 4.0 +
+                           2.0 * double(E) * sumK * 4.0;
+      Timed t(stream, "bwd_gate", 0.0, bytes);
+      EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_gate_launch, g, s, geom, x, weights + wo.wrad, w, stream);
+    }
     const int64_t nw = static_cast<int64_t>(s.n_rbf) * ncol;
-    colsum_kernel<<<ceil_div(nw, 64), 256, 0, stream>>>(w.wrad_part, kWradSplits, nw, nw, grad_weights + wo.wrad);
+    const int ns = edge_streams(E, s.C, kBwdStreams).nstreams;
+    colsum_kernel<<<ceil_div(nw, 64), 256, 0, stream>>>(w.wrad_part, ns, nw, nw, grad_weights + wo.wrad);
   }
   if (g->n_src > 0) {
     if (E == 0) {
@@ -934,6 +1007,9 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
         EGNN_TRY_HIP(hipMemcpyAsync(grad_x_in, grad_out, sizeof(float) * g->n_dst * s.K * s.C, hipMemcpyDeviceToDevice,
                                     stream));
     } else {
+      const double bytes = double(E) * (sumK * 4.0 + s.nD * 4.0 + 8.0) + double(g->n_dst) * s.K * s.C * 4.0 +
+                           double(g->n_src) * s.K * s.C * 4.0;
+      Timed t(stream, "bwd_node", 0.0, bytes);
       EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_node_launch, g, s, geom, grad_out, w, grad_x_in, stream);
     }
   }

@@ -225,6 +225,30 @@ egnn_status egnn_hblocks(const egnn_hdesc *h, int64_t n_edges, int32_t n_nodes,
                          const void *node_irreps, float *h_edge /*[n_edges][n_orb][n_orb]*/,
                          float *h_onsite /*[n_nodes][n_orb][n_orb]*/, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Kernel timing (observability)
+ *
+ * When enabled, every entry point brackets each kernel launch with a pair of
+ * HIP events recorded on the call's stream, tagged with the kernel family
+ * and the launch's algorithmic work (FLOPs for the GEMMs, bytes each array is
+ * read or written once for the rest).  egnn_timing_collect waits for the
+ * recorded events, adds their elapsed times into per-family totals and
+ * recycles the events; it returns the number of families written to `out`
+ * (at most max_entries).  Events beyond an internal pool of 16384 are not
+ * recorded (counted in `dropped`).  Process-wide; thread-safe.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  char name[48];        /* kernel family, e.g. "gemm_nt_f32", "rotate_in"  */
+  int64_t launches;
+  double total_ms;
+  double flops;         /* algorithmic FLOPs summed over the launches       */
+  double bytes;         /* algorithmic HBM bytes summed over the launches   */
+} egnn_timing_entry;
+
+egnn_status egnn_timing_enable(int on);
+int egnn_timing_collect(egnn_timing_entry *out /*host*/, int max_entries, int64_t *dropped /*host*/);
+void egnn_timing_reset(void);
+
 #ifdef __cplusplus
 }
 #endif
