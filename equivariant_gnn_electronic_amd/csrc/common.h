@@ -61,6 +61,13 @@ template <> struct Store<uint16_t> {
   __device__ static inline void st(uint16_t *p, float v) { *p = f32_to_bf16(v); }
 };
 
+// LDS writes and reads of one wave execute in issue order; this only keeps
+// the compiler from moving LDS accesses across the point (no memory wait).
+__device__ inline void wave_lds_order() {
+  __builtin_amdgcn_wave_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 __host__ __device__ constexpr int cmin(int a, int b) { return a < b ? a : b; }
 __host__ __device__ constexpr int cabs(int a) { return a < 0 ? -a : a; }
 

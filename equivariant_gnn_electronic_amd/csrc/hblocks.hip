@@ -255,12 +255,28 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
                                                                   int n_lab, int n_ent, float *__restrict__ H) {
   extern __shared__ float smem[];
   const Table &tb = g_tables[slot];
-  float *Wt = smem;                                   // [C][n_w]
-  float *fs_all = Wt + C * n_w;                       // [kWaves][K][C+1]
-  float *hs_all = fs_all + kWaves * K * (C + 1);      // [kWaves][n_lab]
+  const int n_terms = tb.term_start[n_ent];
+  // LDS: the orbital template (term lists, label maps), W^T, then per-wave rows
+  int *t_start = reinterpret_cast<int *>(smem);                        // [n_ent + 1]
+  float *t_coef = reinterpret_cast<float *>(t_start + n_ent + 1);     // [n_terms]
+  int *t_idx = reinterpret_cast<int *>(t_coef + n_terms);              // [n_terms]
+  int *l_w = t_idx + n_terms;                                          // [n_lab]
+  int *l_f = l_w + n_lab;                                              // [n_lab]
+  float *Wt = reinterpret_cast<float *>(l_f + n_lab);                  // [C][n_w]
+  float *fs_all = Wt + C * n_w;                                        // [kWaves][K][C+1]
+  float *hs_all = fs_all + kWaves * K * (C + 1);                       // [kWaves][n_lab]
+  for (int i = threadIdx.x; i <= n_ent; i += blockDim.x) t_start[i] = tb.term_start[i];
+  for (int i = threadIdx.x; i < n_terms; i += blockDim.x) {
+    t_coef[i] = tb.term_coef[i];
+    t_idx[i] = tb.term_idx[i];
+  }
+  for (int i = threadIdx.x; i < n_lab; i += blockDim.x) {
+    l_w[i] = tb.lab_w[i];
+    l_f[i] = tb.lab_f[i] * (C + 1);
+  }
   for (int i = threadIdx.x; i < C * n_w; i += blockDim.x) {
-    const int c = i / n_w, w = i % n_w;
-    Wt[i] = W[static_cast<int64_t>(w) * C + c];
+    const int w = i / C, c = i % C;          // coalesced read of W[w][c]
+    Wt[c * n_w + w] = W[i];
   }
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -270,33 +286,32 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
        r += static_cast<int64_t>(gridDim.x) * kWaves) {
     const T *f = irreps + r * K * C;
     for (int i = lane; i < K * C; i += kWave) fs[(i / C) * (C + 1) + (i % C)] = Store<T>::ld(f + i);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    wave_lds_order();
     for (int q = lane; q < n_lab; q += kWave) {
-      const int wr = tb.lab_w[q];
-      const float *fr = fs + tb.lab_f[q] * (C + 1);
+      const float *wr = Wt + l_w[q];
+      const float *fr = fs + l_f[q];
       float acc = 0.0f;
-      for (int c = 0; c < C; ++c) acc += Wt[c * n_w + wr] * fr[c];
+      for (int c = 0; c < C; ++c) acc += wr[c * n_w] * fr[c];
       hs[q] = acc;
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    wave_lds_order();
     float *out = H + r * n_ent;
     for (int q = lane; q < n_ent; q += kWave) {
       float acc = 0.0f;
-      for (int t = tb.term_start[q]; t < tb.term_start[q + 1]; ++t) acc += tb.term_coef[t] * hs[tb.term_idx[t]];
+      const int t1 = t_start[q + 1];
+      for (int t = t_start[q]; t < t1; ++t) acc += t_coef[t] * hs[t_idx[t]];
       out[q] = acc;
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    wave_lds_order();
   }
 }
 
 template <typename T>
 egnn_status launch_hblocks(int slot, int64_t rows, const void *irreps, int K, int C, const float *W, int n_w,
-                           int n_lab, int n_ent, float *H, hipStream_t stream) {
+                           int n_lab, int n_ent, int n_terms, float *H, hipStream_t stream) {
   if (rows <= 0) return EGNN_OK;
-  const size_t smem = sizeof(float) * (static_cast<size_t>(C) * n_w + kWaves * K * (C + 1) + kWaves * n_lab);
+  const size_t smem = sizeof(float) * (static_cast<size_t>(n_ent + 1) + 2 * n_terms + 2 * n_lab +
+                                       static_cast<size_t>(C) * n_w + kWaves * K * (C + 1) + kWaves * n_lab);
   if (smem > 150 * 1024) {
     set_error("decode needs %zu bytes of LDS; reduce C or the shell list", smem);
     return EGNN_E_UNSUPPORTED;
@@ -354,8 +369,10 @@ extern "C" egnn_status egnn_hblocks(const egnn_hdesc *h, int64_t n_edges, int32_
   const int n_ent = lay.n_orb * lay.n_orb;
   auto run = [&](int64_t rows, const void *irr, const float *W, float *H) -> egnn_status {
     if (h->storage == EGNN_BF16)
-      return launch_hblocks<uint16_t>(slot, rows, irr, K, h->C, W, lay.n_w, lay.n_lab, n_ent, H, stream);
-    return launch_hblocks<float>(slot, rows, irr, K, h->C, W, lay.n_w, lay.n_lab, n_ent, H, stream);
+      return launch_hblocks<uint16_t>(slot, rows, irr, K, h->C, W, lay.n_w, lay.n_lab, n_ent, lay.t.term_start[n_ent], H,
+                                      stream);
+    return launch_hblocks<float>(slot, rows, irr, K, h->C, W, lay.n_w, lay.n_lab, n_ent, lay.t.term_start[n_ent], H,
+                                 stream);
   };
   st = run(n_edges, edge_irreps, w_edge, h_edge);
   if (st != EGNN_OK) return st;

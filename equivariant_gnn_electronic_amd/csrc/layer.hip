@@ -104,77 +104,139 @@ __global__ void to_bf16_kernel(const float *in, int64_t n, uint16_t *out) {
 }
 
 // --------------------------------------------------------------- forward --
-// Persistent layout of the per-edge kernels: a wave owns one 64-slot chunk
-// of the 2C message channels (slot 0..C-1 = source, C..2C-1 = destination)
-// and walks a strided stream of edges.  The radial weights of its slots stay
-// in registers for the whole stream, so a gate costs n_rbf FMAs and no loads.
-struct EdgeStreams {
-  int nchunks;   // 64-slot chunks of the 2C channels
-  int nstreams;  // edge streams; wave gw serves chunk gw % nchunks of stream gw / nchunks
-};
-__host__ __device__ inline EdgeStreams edge_streams(int64_t E, int C, int max_streams) {
-  EdgeStreams r;
-  r.nchunks = (2 * C + kWave - 1) / kWave;
-  int64_t ns = E < max_streams ? E : max_streams;
-  r.nstreams = static_cast<int>(ns < 1 ? 1 : ns);
-  return r;
-}
-constexpr int kFwdStreams = 4096;
-constexpr int kBwdStreams = 2048;
+// Node-centric edge work.  Every edge's message has a source half (slots
+// 0..C-1) and a destination half (slots C..2C-1).  A wave owns one
+// (node, half, 64-slot chunk): for half 0 it walks the node's outgoing edges
+// (the source grouping), for half 1 its incoming edges (its CSR row).  Either
+// way the only node irreps it needs are the node's own row, loaded once, so
+// there are no per-edge gathers.  The edges' geometry rows are staged into
+// LDS in batches with coalesced vector loads, and the radial weights of the
+// wave's slots stay in registers.
+constexpr int kBatch = 8;
 
-template <int LMAX, int MMAX, int NRBF, typename T, typename TA>
-__global__ void __launch_bounds__(kThreads) rotate_in_kernel(const int *__restrict__ src, const float *__restrict__ geom,
-                                                             int gstride, int64_t E, const T *__restrict__ x, int C,
-                                                             const float *__restrict__ wrad, int n_rbf, EdgeStreams es,
-                                                             Ptr3 A) {
-  using L = Lay<LMAX, MMAX>;
+struct NodeWave {
+  int node, half, chunk;
+};
+__device__ inline NodeWave node_wave(int gw, int nch) {
+  NodeWave w;
+  const int per_node = 2 * nch;
+  w.node = gw / per_node;
+  const int r = gw % per_node;
+  w.half = r / nch;
+  w.chunk = r % nch;
+  return w;
+}
+
+// Edges of (node, half): half 1 = incoming (row), half 0 = outgoing (source group).
+struct EdgeList {
+  const int *perm;  // null for a contiguous row
+  int begin, count;
+  __device__ inline int at(int i) const { return perm ? perm[begin + i] : begin + i; }
+};
+__device__ inline EdgeList edge_list(int node, int half, int n_dst, const int *row_ptr, const int *src_ptr,
+                                     const int *src_perm) {
+  EdgeList l;
+  if (half == 1) {
+    l.perm = nullptr;
+    l.begin = node < n_dst ? row_ptr[node] : 0;
+    l.count = node < n_dst ? row_ptr[node + 1] - l.begin : 0;
+  } else {
+    l.perm = src_perm;
+    l.begin = src_ptr[node];
+    l.count = src_ptr[node + 1] - l.begin;
+  }
+  l.begin = __builtin_amdgcn_readfirstlane(l.begin);
+  l.count = __builtin_amdgcn_readfirstlane(l.count);
+  return l;
+}
+
+// Stage the geometry rows (first gs4 float4 of each) of edges [base, base+cnt)
+// of `el` into the wave's LDS buffer; edge ids go to eid[].
+__device__ inline void stage_geom(const EdgeList &el, int base, int cnt, const float *geom, int gstride, int gs4,
+                                  int lds_row, float4 *buf, int *eid) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int gw = uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-  if (gw >= es.nchunks * es.nstreams) return;
-  const int chunk = gw % es.nchunks, stream = gw / es.nchunks;
-  const int C2 = 2 * C;
-  const int j = chunk * kWave + lane;
-  const bool active = j < C2;
-  const bool is_src = j < C;
-  const int c = is_src ? j : j - C;
-  float wr[NRBF][L::NP];
+  if (lane < cnt) eid[lane] = el.at(base + lane);
+  wave_lds_order();
+  const float4 *g4 = reinterpret_cast<const float4 *>(geom);
+  const int s4 = gstride / 4;
+  for (int t = lane; t < cnt * gs4; t += kWave) {
+    const int i = t / gs4, q = t - i * gs4;
+    buf[i * lds_row + q] = g4[static_cast<int64_t>(eid[i]) * s4 + q];
+  }
+  wave_lds_order();
+}
+
+template <int LMAX, int MMAX, int NRBF>
+__device__ inline void load_wrad(const float *wrad, int n_rbf, int C2, int j, bool active, float (&wr)[NRBF][pair_count(LMAX, MMAX)]) {
+  constexpr int NP = pair_count(LMAX, MMAX);
 #pragma unroll
   for (int k = 0; k < NRBF; ++k)
 #pragma unroll
-    for (int p = 0; p < L::NP; ++p)
-      wr[k][p] = (active && k < n_rbf) ? wrad[(static_cast<int64_t>(k) * L::NP + p) * C2 + j] : 0.0f;
-  for (int64_t e64 = stream; e64 < E; e64 += es.nstreams) {
-    const int e = static_cast<int>(e64);
-    const float *gr = geom + static_cast<int64_t>(e) * gstride;
-    const int node = is_src ? src[e] : __float_as_int(gr[L::ND + n_rbf]);
-    float g[L::NP];
+    for (int p = 0; p < NP; ++p)
+      wr[k][p] = (active && k < n_rbf) ? wrad[(static_cast<int64_t>(k) * NP + p) * C2 + j] : 0.0f;
+}
+
+// A[e] = g_e * trunc(D_e x) for the wave's half of every edge of its node.
+template <int LMAX, int MMAX, int NRBF, typename T, typename TA>
+__global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restrict__ row_ptr,
+                                                              const int *__restrict__ src_ptr,
+                                                              const int *__restrict__ src_perm,
+                                                              const float *__restrict__ geom, int gstride, int n_dst,
+                                                              int n_src, const T *__restrict__ x, int C,
+                                                              const float *__restrict__ wrad, int n_rbf, Ptr3 A) {
+  using L = Lay<LMAX, MMAX>;
+  constexpr int GS4 = (L::ND + NRBF + 3) / 4;
+  const int gs4 = (L::ND + n_rbf + 3) / 4;
+  __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
+  __shared__ int eids[kWavesPerBlock][kBatch];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int nch = (C + kWave - 1) / kWave;
+  const NodeWave nw = node_wave(blockIdx.x * kWavesPerBlock + wave, nch);
+  if (nw.node >= n_src) return;
+  const EdgeList el = edge_list(nw.node, nw.half, n_dst, row_ptr, src_ptr, src_perm);
+  if (el.count == 0) return;
+  const int C2 = 2 * C;
+  const int c = nw.chunk * kWave + lane;
+  const bool active = c < C;
+  const int j = nw.half * C + c;
+  float xv[L::K];
 #pragma unroll
-    for (int p = 0; p < L::NP; ++p) g[p] = 0.0f;
+  for (int k = 0; k < L::K; ++k) xv[k] = active ? Store<T>::ld(x + (static_cast<int64_t>(nw.node) * L::K + k) * C + c) : 0.0f;
+  float wr[NRBF][L::NP];
+  load_wrad<LMAX, MMAX, NRBF>(wrad, n_rbf, C2, j, active, wr);
+  const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
+  for (int base = 0; base < el.count; base += kBatch) {
+    const int cnt = min(kBatch, el.count - base);
+    stage_geom(el, base, cnt, geom, gstride, gs4, GS4, gbuf[wave], eids[wave]);
+    for (int i = 0; i < cnt; ++i) {
+      const int e = uniform(eids[wave][i]);
+      const float *gr = gb + i * GS4 * 4;
+      float g[L::NP];
 #pragma unroll
-    for (int k = 0; k < NRBF; ++k) {
-      const float ph = k < n_rbf ? gr[L::ND + k] : 0.0f;
+      for (int p = 0; p < L::NP; ++p) g[p] = 0.0f;
 #pragma unroll
-      for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[k][p];
-    }
-    if (!active) continue;
-    const T *xr = x + static_cast<int64_t>(node) * L::K * C + c;
-    float xv[L::K];
+      for (int k = 0; k < NRBF; ++k) {
+        const float ph = k < n_rbf ? gr[L::ND + k] : 0.0f;
 #pragma unroll
-    for (int k = 0; k < L::K; ++k) xv[k] = Store<T>::ld(xr + k * C);
+        for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[k][p];
+      }
+      if (!active) continue;
 #pragma unroll
-    for (int l = 0; l <= LMAX; ++l) {
+      for (int l = 0; l <= LMAX; ++l) {
 #pragma unroll
-      for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
-        float v = 0.0f;
+        for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+          float v = 0.0f;
 #pragma unroll
-        for (int mp = -l; mp <= l; ++mp) v += gr[L::doff(l, m, mp)] * xv[l * l + l + mp];
-        v *= g[pair_index(cabs(m), l, LMAX)];
-        const int mu = cabs(m);
-        TA *Am = static_cast<TA *>(A.p[mu]);
-        const int64_t width = static_cast<int64_t>(L::blocks(mu)) * C2;
-        Store<TA>::st(Am + static_cast<int64_t>(e) * width + L::col(l, m) * C2 + j, v);
+          for (int mp = -l; mp <= l; ++mp) v += gr[L::doff(l, m, mp)] * xv[l * l + l + mp];
+          v *= g[pair_index(cabs(m), l, LMAX)];
+          const int mu = cabs(m);
+          TA *Am = static_cast<TA *>(A.p[mu]);
+          const int64_t width = static_cast<int64_t>(L::blocks(mu)) * C2;
+          Store<TA>::st(Am + static_cast<int64_t>(e) * width + L::col(l, m) * C2 + j, v);
+        }
       }
     }
+    wave_lds_order();
   }
 }
 
@@ -212,7 +274,26 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const int *__restri
   for (int e = b + lane; e < end; e += kWave) alpha[e] = expf(logit[e] - M) * inv;
 }
 
-// x_out[d] = x[d] + sum_e alpha_e D_e^T Yhat_e ; edge_out[e] = D_e^T Yhat_e
+// Sum of per-wave register partials through LDS, in wave order (deterministic).
+// part: [kWavesPerBlock][n][64] floats; every wave writes its n values per lane,
+// then wave w reduces entries k = w, w + 4, ... and hands them to `emit`.
+template <int N, typename Emit>
+__device__ inline void block_reduce_rows(float *part, const float (&v)[N], Emit emit) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < N; ++k) part[(wave * N + k) * kWave + lane] = v[k];
+  __syncthreads();
+  for (int k = wave; k < N; k += kWavesPerBlock) {
+    float s = part[(0 * N + k) * kWave + lane];
+#pragma unroll
+    for (int w = 1; w < kWavesPerBlock; ++w) s += part[(w * N + k) * kWave + lane];
+    emit(k, s);
+  }
+  __syncthreads();
+}
+
+// x_out[d] = x[d] + sum_e alpha_e D_e^T Yhat_e ; edge_out[e] = D_e^T Yhat_e.
+// One 4-wave block per destination row; wave w takes edges b + w, b + w + 4, ...
 template <int LMAX, int MMAX, int CPL, typename T>
 __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restrict__ row_ptr, int n_dst,
                                                              const float *__restrict__ geom, int gstride,
@@ -220,22 +301,21 @@ __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restri
                                                              const T *__restrict__ x, T *__restrict__ x_out,
                                                              T *__restrict__ edge_out) {
   using L = Lay<LMAX, MMAX>;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int d = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  __shared__ float part[kWavesPerBlock * L::K * kWave];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int d = blockIdx.x;
   if (d >= n_dst) return;
   const int b = uniform(row_ptr[d]), end = uniform(row_ptr[d + 1]);
-  float acc[CPL][L::K];
 #pragma unroll
-  for (int t = 0; t < CPL; ++t)
+  for (int t = 0; t < CPL; ++t) {
+    const int c = lane + kWave * t;
+    const bool on = c < C;
+    float acc[L::K];
 #pragma unroll
-    for (int k = 0; k < L::K; ++k) acc[t][k] = 0.0f;
-  for (int e = b; e < end; ++e) {
-    const float a = alpha[e];
-    const float *gr = geom + static_cast<int64_t>(e) * gstride;
-#pragma unroll
-    for (int t = 0; t < CPL; ++t) {
-      const int c = lane + kWave * t;
-      if (c >= C) continue;
+    for (int k = 0; k < L::K; ++k) acc[k] = 0.0f;
+    for (int e = b + wave; e < end; e += kWavesPerBlock) {
+      const float a = alpha[e];
+      const float *gr = geom + static_cast<int64_t>(e) * gstride;
       float y[L::KEPT];
 #pragma unroll
       for (int l = 0; l <= LMAX; ++l)
@@ -243,7 +323,7 @@ __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restri
         for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
           const int mu = cabs(m);
           const float *Ym = static_cast<const float *>(Y.p[mu]);
-          y[L::kidx(l, m)] = Ym[static_cast<int64_t>(e) * L::blocks(mu) * C + L::col(l, m) * C + c];
+          y[L::kidx(l, m)] = on ? Ym[static_cast<int64_t>(e) * L::blocks(mu) * C + L::col(l, m) * C + c] : 0.0f;
         }
 #pragma unroll
       for (int l = 0; l <= LMAX; ++l)
@@ -252,20 +332,15 @@ __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restri
           float msg = 0.0f;
 #pragma unroll
           for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) msg += gr[L::doff(l, m, mp)] * y[L::kidx(l, m)];
-          acc[t][l * l + l + mp] += a * msg;
-          if (edge_out) Store<T>::st(edge_out + (static_cast<int64_t>(e) * L::K + l * l + l + mp) * C + c, msg);
+          acc[l * l + l + mp] += a * msg;
+          if (edge_out && on) Store<T>::st(edge_out + (static_cast<int64_t>(e) * L::K + l * l + l + mp) * C + c, msg);
         }
     }
-  }
-#pragma unroll
-  for (int t = 0; t < CPL; ++t) {
-    const int c = lane + kWave * t;
-    if (c >= C) continue;
-#pragma unroll
-    for (int k = 0; k < L::K; ++k) {
+    block_reduce_rows<L::K>(part, acc, [&](int k, float sum) {
+      if (!on) return;
       const int64_t o = (static_cast<int64_t>(d) * L::K + k) * C + c;
-      Store<T>::st(x_out + o, Store<T>::ld(x + o) + acc[t][k]);
-    }
+      Store<T>::st(x_out + o, Store<T>::ld(x + o) + sum);
+    });
   }
 }
 
@@ -274,6 +349,7 @@ __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restri
 // da_e = alpha_e (dalpha_e - sum_row alpha dalpha);
 // dY_e = alpha_e T_e + da_e w_att SiLU'(Y_e[0,0]) on (l=0, m=0);
 // w_att partial of the row = sum_e da_e SiLU(Y_e[0,0]).
+// One 4-wave block per row; wave w owns edges b + w + 4i in both passes.
 template <int LMAX, int MMAX, int CPL>
 __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict__ row_ptr, int n_dst,
                                                            const float *__restrict__ geom, int gstride,
@@ -281,8 +357,10 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
                                                            const float *__restrict__ G, const float *__restrict__ w_att,
                                                            Ptr3 dY, float *dalpha, float *watt_part) {
   using L = Lay<LMAX, MMAX>;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int d = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  __shared__ float red[kWavesPerBlock * CPL * kWave];
+  __shared__ float srow[kWavesPerBlock];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int d = blockIdx.x;
   if (d >= n_dst) return;
   const int b = uniform(row_ptr[d]), end = uniform(row_ptr[d + 1]);
   float gd[CPL][L::K];
@@ -306,8 +384,8 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
   auto yaddr = [&](int e, int l, int m, int c) -> int64_t {
     return static_cast<int64_t>(e) * L::blocks(cabs(m)) * C + L::col(l, m) * C + c;
   };
-  float s_row = 0.0f;
-  for (int e = b; e < end; ++e) {
+  float s_wave = 0.0f;
+  for (int e = b + wave; e < end; e += kWavesPerBlock) {
     const float *gr = geom + static_cast<int64_t>(e) * gstride;
     float p = 0.0f;
 #pragma unroll
@@ -324,12 +402,15 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
     }
     p = wave_sum(p);
     dalpha[e] = p;  // every lane stores the same value and later reads its own store
-    s_row += alpha[e] * p;
+    s_wave += alpha[e] * p;
   }
+  if (lane == 0) srow[wave] = s_wave;
+  __syncthreads();
+  const float s_row = (srow[0] + srow[1]) + (srow[2] + srow[3]);
   float wacc[CPL];
 #pragma unroll
   for (int t = 0; t < CPL; ++t) wacc[t] = 0.0f;
-  for (int e = b; e < end; ++e) {
+  for (int e = b + wave; e < end; e += kWavesPerBlock) {
     const float *gr = geom + static_cast<int64_t>(e) * gstride;
     const float a = alpha[e];
     const float da = a * (dalpha[e] - s_row);
@@ -354,78 +435,93 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
     }
   }
 #pragma unroll
-  for (int t = 0; t < CPL; ++t) {
-    const int c = lane + kWave * t;
-    if (c < C) watt_part[static_cast<int64_t>(d) * C + c] = wacc[t];
+  for (int t = 0; t < CPL; ++t) red[(wave * CPL + t) * kWave + lane] = wacc[t];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      const int c = lane + kWave * t;
+      float v = red[(0 * CPL + t) * kWave + lane];
+#pragma unroll
+      for (int w = 1; w < kWavesPerBlock; ++w) v += red[(w * CPL + t) * kWave + lane];
+      if (c < C) watt_part[static_cast<int64_t>(d) * C + c] = v;
+    }
   }
 }
 
-// Per edge: recompute Xt (edge-frame input before the gate) and g; the GEMM
-// gradient dX (in dA) becomes dXt = g * dX in place; dg = sum_{+-m} dX * Xt,
-// and the radial-weight gradient sum_e phi_e[k] dg_e is accumulated in
-// registers along the wave's edge stream and written once per stream
-// (part[stream][k][pair][slot]); the streams are summed later in a fixed order.
+// Radial-weight gradient: dW_rad[k][p][j] = sum_e phi_e[k] dg_e[p][j] with
+// dg_e[p] = sum_{+-m} dX_e[l,+-m] * Xt_e[l,+-m] (Xt = edge-frame input before
+// the gate).  Node-centric waves as in scatter_in; wave (node, half, chunk)
+// recomputes Xt of its half from its node's row.  Each wave walks a strided
+// stream of nodes and keeps its partial sums in registers; partials are
+// written per stream and summed later in a fixed order.
 template <int LMAX, int MMAX, int NRBF, typename T>
-__global__ void __launch_bounds__(kThreads) bwd_gate_kernel(const int *__restrict__ src, const float *__restrict__ geom,
-                                                            int gstride, int64_t E, const T *__restrict__ x, int C,
-                                                            const float *__restrict__ wrad, int n_rbf, EdgeStreams es,
-                                                            Ptr3 dA, float *__restrict__ part) {
+__global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restrict__ row_ptr,
+                                                             const int *__restrict__ src_ptr,
+                                                             const int *__restrict__ src_perm,
+                                                             const float *__restrict__ geom, int gstride, int n_dst,
+                                                             int n_src, const T *__restrict__ x, int C, int n_rbf,
+                                                             CPtr3 dA, int n_streams, float *__restrict__ part) {
   using L = Lay<LMAX, MMAX>;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int gw = uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-  if (gw >= es.nchunks * es.nstreams) return;
-  const int chunk = gw % es.nchunks, stream = gw / es.nchunks;
+  constexpr int GS4 = (L::ND + NRBF + 3) / 4;
+  const int gs4 = (L::ND + n_rbf + 3) / 4;
+  __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
+  __shared__ int eids[kWavesPerBlock][kBatch];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int nch = (C + kWave - 1) / kWave;
+  const int per_node = 2 * nch;
+  const int gw = uniform(blockIdx.x * kWavesPerBlock + wave);
+  if (gw >= n_streams * per_node) return;
+  const int stream = gw / per_node, r = gw % per_node;
+  const int half = r / nch, chunk = r % nch;
   const int C2 = 2 * C;
-  const int j = chunk * kWave + lane;
-  const bool active = j < C2;
-  const bool is_src = j < C;
-  const int c = is_src ? j : j - C;
-  float wr[NRBF][L::NP], acc[NRBF][L::NP];
+  const int c = chunk * kWave + lane;
+  const bool active = c < C;
+  const int j = half * C + c;
+  float acc[NRBF][L::NP];
 #pragma unroll
   for (int k = 0; k < NRBF; ++k)
 #pragma unroll
-    for (int p = 0; p < L::NP; ++p) {
-      wr[k][p] = (active && k < n_rbf) ? wrad[(static_cast<int64_t>(k) * L::NP + p) * C2 + j] : 0.0f;
-      acc[k][p] = 0.0f;
-    }
-  for (int64_t e64 = stream; e64 < E; e64 += es.nstreams) {
-    const int e = static_cast<int>(e64);
-    const float *gr = geom + static_cast<int64_t>(e) * gstride;
-    const int node = is_src ? src[e] : __float_as_int(gr[L::ND + n_rbf]);
-    float ph[NRBF];
-#pragma unroll
-    for (int k = 0; k < NRBF; ++k) ph[k] = k < n_rbf ? gr[L::ND + k] : 0.0f;
-    if (!active) continue;
-    const T *xr = x + static_cast<int64_t>(node) * L::K * C + c;
+    for (int p = 0; p < L::NP; ++p) acc[k][p] = 0.0f;
+  const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
+  for (int node = stream; node < n_src; node += n_streams) {
+    const EdgeList el = edge_list(node, half, n_dst, row_ptr, src_ptr, src_perm);
+    if (el.count == 0) continue;
     float xv[L::K];
 #pragma unroll
-    for (int k = 0; k < L::K; ++k) xv[k] = Store<T>::ld(xr + k * C);
-    float dgp[L::NP];
+    for (int k = 0; k < L::K; ++k) xv[k] = active ? Store<T>::ld(x + (static_cast<int64_t>(node) * L::K + k) * C + c) : 0.0f;
+    for (int base = 0; base < el.count; base += kBatch) {
+      const int cnt = min(kBatch, el.count - base);
+      stage_geom(el, base, cnt, geom, gstride, gs4, GS4, gbuf[wave], eids[wave]);
+      for (int i = 0; i < cnt; ++i) {
+        const int e = uniform(eids[wave][i]);
+        const float *gr = gb + i * GS4 * 4;
+        float dg[L::NP];
 #pragma unroll
-    for (int p = 0; p < L::NP; ++p) dgp[p] = 0.0f;
+        for (int p = 0; p < L::NP; ++p) dg[p] = 0.0f;
+        if (active) {
 #pragma unroll
-    for (int l = 0; l <= LMAX; ++l) {
+          for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
-      for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
-        float xt = 0.0f;
+            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+              float xt = 0.0f;
 #pragma unroll
-        for (int mp = -l; mp <= l; ++mp) xt += gr[L::doff(l, m, mp)] * xv[l * l + l + mp];
-        const int mu = cabs(m);
-        const int p = pair_index(mu, l, LMAX);
-        float g = 0.0f;
+              for (int mp = -l; mp <= l; ++mp) xt += gr[L::doff(l, m, mp)] * xv[l * l + l + mp];
+              const int mu = cabs(m);
+              const float dx = static_cast<const float *>(dA.p[mu])[static_cast<int64_t>(e) * L::blocks(mu) * C2 +
+                                                                    L::col(l, m) * C2 + j];
+              dg[pair_index(mu, l, LMAX)] += dx * xt;
+            }
+        }
 #pragma unroll
-        for (int k = 0; k < NRBF; ++k) g += ph[k] * wr[k][p];
-        float *Am = static_cast<float *>(dA.p[mu]);
-        const int64_t o = static_cast<int64_t>(e) * L::blocks(mu) * C2 + L::col(l, m) * C2 + j;
-        const float dx = Am[o];
-        dgp[p] += dx * xt;
-        Am[o] = g * dx;
+        for (int k = 0; k < NRBF; ++k) {
+          const float ph = k < n_rbf ? gr[L::ND + k] : 0.0f;
+#pragma unroll
+          for (int p = 0; p < L::NP; ++p) acc[k][p] += ph * dg[p];
+        }
       }
+      wave_lds_order();
     }
-#pragma unroll
-    for (int k = 0; k < NRBF; ++k)
-#pragma unroll
-      for (int p = 0; p < L::NP; ++p) acc[k][p] += ph[k] * dgp[p];
   }
   if (!active) return;
 #pragma unroll
@@ -435,69 +531,92 @@ __global__ void __launch_bounds__(kThreads) bwd_gate_kernel(const int *__restric
       if (k < n_rbf) part[((static_cast<int64_t>(stream) * n_rbf + k) * L::NP + p) * C2 + j] = acc[k][p];
 }
 
-// Per node n: grad_x[n] = G[n] (owned rows) + sum over its incoming edges of
-// D_e^T dXt_e[destination half] + sum over its outgoing edges (the source
-// grouping) of D_e^T dXt_e[source half].
-template <int LMAX, int MMAX, int CPL>
-__global__ void __launch_bounds__(kThreads) bwd_node_kernel(const int *__restrict__ row_ptr, int n_dst, int n_src,
-                                                            const int *__restrict__ src_ptr,
-                                                            const int *__restrict__ src_perm,
-                                                            const float *__restrict__ geom, int gstride, CPtr3 dA,
-                                                            int C, const float *__restrict__ G, float *__restrict__ gx) {
+// grad_x[n] = G[n] (owned rows) + sum over the node's incoming edges of
+// D_e^T (g_e * dX_e)[destination half] + sum over its outgoing edges of
+// D_e^T (g_e * dX_e)[source half], with dX the GEMM gradient of the gated
+// edge-frame input.  The waves of one node (two halves x channel chunks) sit
+// in one block and their partial sums are added through LDS in a fixed order.
+template <int LMAX, int MMAX, int NRBF>
+__global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__restrict__ row_ptr,
+                                                               const int *__restrict__ src_ptr,
+                                                               const int *__restrict__ src_perm,
+                                                               const float *__restrict__ geom, int gstride, int n_dst,
+                                                               int n_src, int C, const float *__restrict__ wrad,
+                                                               int n_rbf, CPtr3 dA, const float *__restrict__ G,
+                                                               float *__restrict__ gx) {
   using L = Lay<LMAX, MMAX>;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int n = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (n >= n_src) return;
+  constexpr int GS4 = (L::ND + NRBF + 3) / 4;
+  const int gs4 = (L::ND + n_rbf + 3) / 4;
+  __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
+  __shared__ int eids[kWavesPerBlock][kBatch];
+  __shared__ float red[kWavesPerBlock][L::K * kWave];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int nch = (C + kWave - 1) / kWave;
+  const NodeWave nw = node_wave(blockIdx.x * kWavesPerBlock + wave, nch);
+  const bool live = nw.node < n_src;
   const int C2 = 2 * C;
-  float acc[CPL][L::K];
+  const int c = nw.chunk * kWave + lane;
+  const bool active = live && c < C;
+  const int j = nw.half * C + c;
+  float acc[L::K];
 #pragma unroll
-  for (int t = 0; t < CPL; ++t) {
-    const int c = lane + kWave * t;
+  for (int k = 0; k < L::K; ++k) acc[k] = 0.0f;
+  if (live) {
+    const EdgeList el = edge_list(nw.node, nw.half, n_dst, row_ptr, src_ptr, src_perm);
+    float wr[NRBF][L::NP];
+    load_wrad<LMAX, MMAX, NRBF>(wrad, n_rbf, C2, j, active, wr);
+    const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
+    for (int base = 0; base < el.count; base += kBatch) {
+      const int cnt = min(kBatch, el.count - base);
+      stage_geom(el, base, cnt, geom, gstride, gs4, GS4, gbuf[wave], eids[wave]);
+      for (int i = 0; i < cnt; ++i) {
+        const int e = uniform(eids[wave][i]);
+        const float *gr = gb + i * GS4 * 4;
+        if (!active) continue;
+        float dxt[L::KEPT];
 #pragma unroll
-    for (int k = 0; k < L::K; ++k)
-      acc[t][k] = (n < n_dst && c < C) ? G[(static_cast<int64_t>(n) * L::K + k) * C + c] : 0.0f;
-  }
-  auto add_edge = [&](int e, int half) {
-    const float *gr = geom + static_cast<int64_t>(e) * gstride;
+        for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
-    for (int t = 0; t < CPL; ++t) {
-      const int c = lane + kWave * t;
-      if (c >= C) continue;
-      const int j = half * C + c;
-      float v[L::KEPT];
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+            const int mu = cabs(m);
+            dxt[L::kidx(l, m)] = static_cast<const float *>(dA.p[mu])[static_cast<int64_t>(e) * L::blocks(mu) * C2 +
+                                                                      L::col(l, m) * C2 + j];
+          }
+        float g[L::NP];
 #pragma unroll
-      for (int l = 0; l <= LMAX; ++l)
+        for (int p = 0; p < L::NP; ++p) g[p] = 0.0f;
 #pragma unroll
-        for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
-          const int mu = cabs(m);
-          v[L::kidx(l, m)] = static_cast<const float *>(dA.p[mu])[static_cast<int64_t>(e) * L::blocks(mu) * C2 +
-                                                                   L::col(l, m) * C2 + j];
+        for (int k = 0; k < NRBF; ++k) {
+          const float ph = k < n_rbf ? gr[L::ND + k] : 0.0f;
+#pragma unroll
+          for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[k][p];
         }
 #pragma unroll
-      for (int l = 0; l <= LMAX; ++l)
+        for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
-        for (int mp = -l; mp <= l; ++mp) {
-          float s = 0.0f;
+          for (int mp = -l; mp <= l; ++mp) {
+            float s = 0.0f;
 #pragma unroll
-          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) s += gr[L::doff(l, m, mp)] * v[L::kidx(l, m)];
-          acc[t][l * l + l + mp] += s;
-        }
+            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
+              s += gr[L::doff(l, m, mp)] * g[pair_index(cabs(m), l, LMAX)] * dxt[L::kidx(l, m)];
+            acc[l * l + l + mp] += s;
+          }
+      }
+      wave_lds_order();
     }
-  };
-  if (n < n_dst) {
-    const int b = uniform(row_ptr[n]), end = uniform(row_ptr[n + 1]);
-    for (int e = b; e < end; ++e) add_edge(e, 1);
   }
-  {
-    const int b = uniform(src_ptr[n]), end = uniform(src_ptr[n + 1]);
-    for (int i = b; i < end; ++i) add_edge(uniform(src_perm[i]), 0);
-  }
+  // half 1 hands its partial to half 0 of the same chunk
 #pragma unroll
-  for (int t = 0; t < CPL; ++t) {
-    const int c = lane + kWave * t;
-    if (c >= C) continue;
+  for (int k = 0; k < L::K; ++k) red[wave][k * kWave + lane] = acc[k];
+  __syncthreads();
+  if (active && nw.half == 0) {
+    const int partner = wave + nch;  // same node, same chunk, half 1
 #pragma unroll
-    for (int k = 0; k < L::K; ++k) gx[(static_cast<int64_t>(n) * L::K + k) * C + c] = acc[t][k];
+    for (int k = 0; k < L::K; ++k) {
+      const int64_t o = (static_cast<int64_t>(nw.node) * L::K + k) * C + c;
+      const float g0 = nw.node < n_dst ? G[o] : 0.0f;
+      gx[o] = g0 + (acc[k] + red[partner][k * kWave + lane]);
+    }
   }
 }
 
@@ -600,7 +719,11 @@ struct BwdWs {
   float *wrad_part;
 };
 
-BwdWs carve_bwd_ws(Carver &cv, const LayerShape &s, int64_t E, int n_dst) {
+// node streams of the radial-weight gradient (fixed by the node count, so the
+// summation order of its partials is reproducible)
+int wrad_streams(int n_src) { return n_src < 1024 ? (n_src > 0 ? n_src : 1) : 1024; }
+
+BwdWs carve_bwd_ws(Carver &cv, const LayerShape &s, int64_t E, int n_dst, int n_src) {
   BwdWs w{};
   size_t pmax = 0;
   for (int m = 0; m <= s.mmax; ++m) {
@@ -613,8 +736,7 @@ BwdWs carve_bwd_ws(Carver &cv, const LayerShape &s, int64_t E, int n_dst) {
   w.watt_part = cv.take<float>(static_cast<size_t>(n_dst > 0 ? n_dst : 1) * s.C);
   w.P = cv.take<float>(pmax * dw_splits(E));
   w.Pred = cv.take<float>(pmax);
-  w.wrad_part = cv.take<float>(static_cast<size_t>(edge_streams(E, s.C, kBwdStreams).nstreams) * s.n_rbf *
-                               s.n_pairs * 2 * s.C);
+  w.wrad_part = cv.take<float>(static_cast<size_t>(wrad_streams(n_src)) * s.n_rbf * s.n_pairs * 2 * s.C);
   return w;
 }
 
@@ -648,20 +770,20 @@ struct Launch {
   static void rotate_in(const egnn_graph *g, const LayerShape &s, const float *geom, const T *x, const float *wrad,
                         const Acts &a, hipStream_t st) {
     Ptr3 A{{a.A[0], a.A[1], a.A[2]}};
-    const EdgeStreams es = edge_streams(g->n_edges, s.C, kFwdStreams);
-    const unsigned grid = ceil_div(static_cast<int64_t>(es.nchunks) * es.nstreams, kWavesPerBlock);
+    const int nch = (s.C + kWave - 1) / kWave;
+    const unsigned grid = ceil_div(static_cast<int64_t>(g->n_src) * 2 * nch, kWavesPerBlock);
     if (s.n_rbf <= 8)
-      rotate_in_kernel<LMAX, MMAX, 8, T, TA><<<grid, kThreads, 0, st>>>(g->src, geom, s.gstride, g->n_edges, x, s.C,
-                                                                        wrad, s.n_rbf, es, A);
+      scatter_in_kernel<LMAX, MMAX, 8, T, TA><<<grid, kThreads, 0, st>>>(
+          g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride, g->n_dst, g->n_src, x, s.C, wrad, s.n_rbf, A);
     else
-      rotate_in_kernel<LMAX, MMAX, 16, T, TA><<<grid, kThreads, 0, st>>>(g->src, geom, s.gstride, g->n_edges, x, s.C,
-                                                                         wrad, s.n_rbf, es, A);
+      scatter_in_kernel<LMAX, MMAX, 16, T, TA><<<grid, kThreads, 0, st>>>(
+          g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride, g->n_dst, g->n_src, x, s.C, wrad, s.n_rbf, A);
   }
   template <typename T>
   static void aggregate(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const T *x,
                         T *x_out, T *edge_out, hipStream_t st) {
     CPtr3 Y{{a.Y[0], a.Y[1], a.Y[2]}};
-    const unsigned grid = ceil_div(g->n_dst, kWavesPerBlock);
+    const unsigned grid = static_cast<unsigned>(g->n_dst);
     if (s.C <= 64)
       aggregate_kernel<LMAX, MMAX, 1, T><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y,
                                                                     s.C, x, x_out, edge_out);
@@ -676,7 +798,7 @@ struct Launch {
                       const float *w_att, const BwdWs &w, hipStream_t st) {
     CPtr3 Y{{a.Y[0], a.Y[1], a.Y[2]}};
     Ptr3 dY{{w.dY[0], w.dY[1], w.dY[2]}};
-    const unsigned grid = ceil_div(g->n_dst, kWavesPerBlock);
+    const unsigned grid = static_cast<unsigned>(g->n_dst);
     if (s.C <= 64)
       bwd_row_kernel<LMAX, MMAX, 1><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C,
                                                                G, w_att, dY, w.dalpha, w.watt_part);
@@ -689,29 +811,31 @@ struct Launch {
   }
   static void bwd_gate(const egnn_graph *g, const LayerShape &s, const float *geom, const float *x, const float *wrad,
                        const BwdWs &w, hipStream_t st) {
-    Ptr3 dA{{w.dA[0], w.dA[1], w.dA[2]}};
-    const EdgeStreams es = edge_streams(g->n_edges, s.C, kBwdStreams);
-    const unsigned grid = ceil_div(static_cast<int64_t>(es.nchunks) * es.nstreams, kWavesPerBlock);
-    if (s.n_rbf <= 8)
-      bwd_gate_kernel<LMAX, MMAX, 8, float><<<grid, kThreads, 0, st>>>(g->src, geom, s.gstride, g->n_edges, x, s.C,
-                                                                       wrad, s.n_rbf, es, dA, w.wrad_part);
-    else
-      bwd_gate_kernel<LMAX, MMAX, 16, float><<<grid, kThreads, 0, st>>>(g->src, geom, s.gstride, g->n_edges, x, s.C,
-                                                                        wrad, s.n_rbf, es, dA, w.wrad_part);
-  }
-  static void bwd_node(const egnn_graph *g, const LayerShape &s, const float *geom, const float *G, const BwdWs &w,
-                       float *gx, hipStream_t st) {
+    (void)wrad;
     CPtr3 dA{{w.dA[0], w.dA[1], w.dA[2]}};
-    const unsigned grid = ceil_div(g->n_src, kWavesPerBlock);
-    if (s.C <= 64)
-      bwd_node_kernel<LMAX, MMAX, 1><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, g->n_src, g->src_ptr, g->src_perm,
-                                                                geom, s.gstride, dA, s.C, G, gx);
-    else if (s.C <= 128)
-      bwd_node_kernel<LMAX, MMAX, 2><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, g->n_src, g->src_ptr, g->src_perm,
-                                                                geom, s.gstride, dA, s.C, G, gx);
+    const int nch = (s.C + kWave - 1) / kWave;
+    const int ns = wrad_streams(g->n_src);
+    const unsigned grid = ceil_div(static_cast<int64_t>(ns) * 2 * nch, kWavesPerBlock);
+    if (s.n_rbf <= 8)
+      wrad_grad_kernel<LMAX, MMAX, 8, float><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom,
+                                                                        s.gstride, g->n_dst, g->n_src, x, s.C, s.n_rbf,
+                                                                        dA, ns, w.wrad_part);
     else
-      bwd_node_kernel<LMAX, MMAX, 4><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, g->n_src, g->src_ptr, g->src_perm,
-                                                                geom, s.gstride, dA, s.C, G, gx);
+      wrad_grad_kernel<LMAX, MMAX, 16, float><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom,
+                                                                         s.gstride, g->n_dst, g->n_src, x, s.C, s.n_rbf,
+                                                                         dA, ns, w.wrad_part);
+  }
+  static void bwd_node(const egnn_graph *g, const LayerShape &s, const float *geom, const float *G, const float *wrad,
+                       const BwdWs &w, float *gx, hipStream_t st) {
+    CPtr3 dA{{w.dA[0], w.dA[1], w.dA[2]}};
+    const int nch = (s.C + kWave - 1) / kWave;
+    const unsigned grid = ceil_div(static_cast<int64_t>(g->n_src) * 2 * nch, kWavesPerBlock);
+    if (s.n_rbf <= 8)
+      gather_grad_kernel<LMAX, MMAX, 8><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride,
+                                                                   g->n_dst, g->n_src, s.C, wrad, s.n_rbf, dA, G, gx);
+    else
+      gather_grad_kernel<LMAX, MMAX, 16><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride,
+                                                                    g->n_dst, g->n_src, s.C, wrad, s.n_rbf, dA, G, gx);
   }
 };
 
@@ -754,9 +878,9 @@ void bwd_gate_launch(const egnn_graph *g, const LayerShape &s, const float *geom
   Launch<LMAX, MMAX>::bwd_gate(g, s, geom, x, wrad, w, st);
 }
 template <int LMAX, int MMAX>
-void bwd_node_launch(const egnn_graph *g, const LayerShape &s, const float *geom, const float *G, const BwdWs &w,
-                     float *gx, hipStream_t st) {
-  Launch<LMAX, MMAX>::bwd_node(g, s, geom, G, w, gx, st);
+void bwd_node_launch(const egnn_graph *g, const LayerShape &s, const float *geom, const float *G, const float *wrad,
+                     const BwdWs &w, float *gx, hipStream_t st) {
+  Launch<LMAX, MMAX>::bwd_node(g, s, geom, G, wrad, w, gx, st);
 }
 
 egnn_status check_graph(const egnn_graph *g) {
@@ -795,7 +919,7 @@ extern "C" egnn_status egnn_layer_sizes(const egnn_layer_desc *d, const egnn_gra
   }
   if (ws_bwd_bytes) {
     Carver cv{nullptr};
-    carve_bwd_ws(cv, s, E, g->n_dst);
+    carve_bwd_ws(cv, s, E, g->n_dst, g->n_src);
     *ws_bwd_bytes = cv.off;
   }
   return EGNN_OK;
@@ -914,6 +1038,10 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
     set_error("the backward pass supports fp32 storage only");
     return EGNN_E_UNSUPPORTED;
   }
+  if (s.C > 128) {
+    set_error("the backward pass supports C <= 128");
+    return EGNN_E_UNSUPPORTED;
+  }
   EGNN_REQUIRE(weights && x_in && saved && grad_x_in && grad_weights, "null pointer");
   EGNN_REQUIRE(g->n_dst == 0 || grad_out, "grad_out is null");
   const int64_t E = g->n_edges;
@@ -921,7 +1049,7 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
   Carver cs{static_cast<char *>(const_cast<void *>(saved))};
   const Acts acts = carve_acts(cs, s, E);
   Carver cw{static_cast<char *>(ws)};
-  const BwdWs w = carve_bwd_ws(cw, s, E, g->n_dst);
+  const BwdWs w = carve_bwd_ws(cw, s, E, g->n_dst, g->n_src);
   if (!ws || ws_bytes < cw.off) {
     set_error("workspace of %zu bytes, need %zu", ws_bytes, cw.off);
     return EGNN_E_WORKSPACE;
@@ -995,7 +1123,7 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
       EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_gate_launch, g, s, geom, x, weights + wo.wrad, w, stream);
     }
     const int64_t nw = static_cast<int64_t>(s.n_rbf) * ncol;
-    const int ns = edge_streams(E, s.C, kBwdStreams).nstreams;
+    const int ns = wrad_streams(g->n_src);
     colsum_kernel<<<ceil_div(nw, 64), 256, 0, stream>>>(w.wrad_part, ns, nw, nw, grad_weights + wo.wrad);
   }
   if (g->n_src > 0) {
@@ -1010,7 +1138,7 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
       const double bytes = double(E) * (sumK * 4.0 + s.nD * 4.0 + 8.0) + double(g->n_dst) * s.K * s.C * 4.0 +
                            double(g->n_src) * s.K * s.C * 4.0;
       Timed t(stream, "bwd_node", 0.0, bytes);
-      EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_node_launch, g, s, geom, grad_out, w, grad_x_in, stream);
+      EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_node_launch, g, s, geom, grad_out, weights + wo.wrad, w, grad_x_in, stream);
     }
   }
   EGNN_CHECK_LAUNCH();
