@@ -274,57 +274,57 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const int *__restri
   for (int e = b + lane; e < end; e += kWave) alpha[e] = expf(logit[e] - M) * inv;
 }
 
-// Sum of per-wave register partials through LDS, in wave order (deterministic).
-// part: [kWavesPerBlock][n][64] floats; every wave writes its n values per lane,
-// then wave w reduces entries k = w, w + 4, ... and hands them to `emit`.
-template <int N, typename Emit>
-__device__ inline void block_reduce_rows(float *part, const float (&v)[N], Emit emit) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int k = 0; k < N; ++k) part[(wave * N + k) * kWave + lane] = v[k];
-  __syncthreads();
-  for (int k = wave; k < N; k += kWavesPerBlock) {
-    float s = part[(0 * N + k) * kWave + lane];
-#pragma unroll
-    for (int w = 1; w < kWavesPerBlock; ++w) s += part[(w * N + k) * kWave + lane];
-    emit(k, s);
-  }
-  __syncthreads();
-}
-
 // x_out[d] = x[d] + sum_e alpha_e D_e^T Yhat_e ; edge_out[e] = D_e^T Yhat_e.
-// One 4-wave block per destination row; wave w takes edges b + w, b + w + 4, ...
-template <int LMAX, int MMAX, int CPL, typename T>
+// One wave per (destination row, 64-channel chunk): it walks the row's
+// contiguous edges, staging their geometry rows (and alpha) into LDS in
+// batches; the accumulator stays in registers (no atomics, no partials).
+template <int LMAX, int MMAX, typename T>
 __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restrict__ row_ptr, int n_dst,
-                                                             const float *__restrict__ geom, int gstride,
+                                                             const float *__restrict__ geom, int gstride, int nd_rbf,
                                                              const float *__restrict__ alpha, CPtr3 Y, int C,
                                                              const T *__restrict__ x, T *__restrict__ x_out,
                                                              T *__restrict__ edge_out) {
   using L = Lay<LMAX, MMAX>;
-  __shared__ float part[kWavesPerBlock * L::K * kWave];
+  constexpr int GS4 = (L::ND + 3) / 4;
+  __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
+  __shared__ int eids[kWavesPerBlock][kBatch];
+  __shared__ float abuf[kWavesPerBlock][kBatch];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const int d = blockIdx.x;
+  const int nch = (C + kWave - 1) / kWave;
+  const int gw = uniform(blockIdx.x * kWavesPerBlock + wave);
+  const int d = gw / nch, chunk = gw % nch;
   if (d >= n_dst) return;
-  const int b = uniform(row_ptr[d]), end = uniform(row_ptr[d + 1]);
+  const int c = chunk * kWave + lane;
+  const bool on = c < C;
+  const int cl = on ? c : C - 1;  // clamped channel for loads
+  EdgeList el;
+  el.perm = nullptr;
+  el.begin = uniform(row_ptr[d]);
+  el.count = uniform(row_ptr[d + 1]) - el.begin;
+  const int gs4 = (L::ND + 3) / 4;
+  (void)nd_rbf;
+  float acc[L::K];
 #pragma unroll
-  for (int t = 0; t < CPL; ++t) {
-    const int c = lane + kWave * t;
-    const bool on = c < C;
-    float acc[L::K];
-#pragma unroll
-    for (int k = 0; k < L::K; ++k) acc[k] = 0.0f;
-    for (int e = b + wave; e < end; e += kWavesPerBlock) {
-      const float a = alpha[e];
-      const float *gr = geom + static_cast<int64_t>(e) * gstride;
+  for (int k = 0; k < L::K; ++k) acc[k] = 0.0f;
+  const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
+  for (int base = 0; base < el.count; base += kBatch) {
+    const int cnt = min(kBatch, el.count - base);
+    if (lane < cnt) abuf[wave][lane] = alpha[el.begin + base + lane];
+    stage_geom(el, base, cnt, geom, gstride, gs4, GS4, gbuf[wave], eids[wave]);
+    for (int i = 0; i < cnt; ++i) {
+      const int e = el.begin + base + i;
+      const float a = abuf[wave][i];
+      const float *gr = gb + i * GS4 * 4;
       float y[L::KEPT];
 #pragma unroll
       for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
         for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
           const int mu = cabs(m);
-          const float *Ym = static_cast<const float *>(Y.p[mu]);
-          y[L::kidx(l, m)] = on ? Ym[static_cast<int64_t>(e) * L::blocks(mu) * C + L::col(l, m) * C + c] : 0.0f;
+          const float *row = static_cast<const float *>(Y.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
+          y[L::kidx(l, m)] = row[L::col(l, m) * C + cl];
         }
+      T *eo = edge_out ? edge_out + static_cast<int64_t>(e) * L::K * C : nullptr;
 #pragma unroll
       for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
@@ -333,14 +333,16 @@ __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restri
 #pragma unroll
           for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) msg += gr[L::doff(l, m, mp)] * y[L::kidx(l, m)];
           acc[l * l + l + mp] += a * msg;
-          if (edge_out && on) Store<T>::st(edge_out + (static_cast<int64_t>(e) * L::K + l * l + l + mp) * C + c, msg);
+          if (eo && on) Store<T>::st(eo + (l * l + l + mp) * C + c, msg);
         }
     }
-    block_reduce_rows<L::K>(part, acc, [&](int k, float sum) {
-      if (!on) return;
-      const int64_t o = (static_cast<int64_t>(d) * L::K + k) * C + c;
-      Store<T>::st(x_out + o, Store<T>::ld(x + o) + sum);
-    });
+    wave_lds_order();
+  }
+  if (!on) return;
+#pragma unroll
+  for (int k = 0; k < L::K; ++k) {
+    const int64_t o = (static_cast<int64_t>(d) * L::K + k) * C + c;
+    Store<T>::st(x_out + o, Store<T>::ld(x + o) + acc[k]);
   }
 }
 
@@ -349,7 +351,8 @@ __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restri
 // da_e = alpha_e (dalpha_e - sum_row alpha dalpha);
 // dY_e = alpha_e T_e + da_e w_att SiLU'(Y_e[0,0]) on (l=0, m=0);
 // w_att partial of the row = sum_e da_e SiLU(Y_e[0,0]).
-// One 4-wave block per row; wave w owns edges b + w + 4i in both passes.
+// One wave per row; lanes = channels (CPL per lane), geometry rows staged in
+// LDS in batches as in the forward aggregate.
 template <int LMAX, int MMAX, int CPL>
 __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict__ row_ptr, int n_dst,
                                                            const float *__restrict__ geom, int gstride,
@@ -357,16 +360,23 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
                                                            const float *__restrict__ G, const float *__restrict__ w_att,
                                                            Ptr3 dY, float *dalpha, float *watt_part) {
   using L = Lay<LMAX, MMAX>;
-  __shared__ float red[kWavesPerBlock * CPL * kWave];
-  __shared__ float srow[kWavesPerBlock];
+  constexpr int GS4 = (L::ND + 3) / 4;
+  __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
+  __shared__ int eids[kWavesPerBlock][kBatch];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  const int d = blockIdx.x;
+  const int d = uniform(blockIdx.x * kWavesPerBlock + wave);
   if (d >= n_dst) return;
-  const int b = uniform(row_ptr[d]), end = uniform(row_ptr[d + 1]);
+  EdgeList el;
+  el.perm = nullptr;
+  el.begin = uniform(row_ptr[d]);
+  el.count = uniform(row_ptr[d + 1]) - el.begin;
+  const int gs4 = (L::ND + 3) / 4;
   float gd[CPL][L::K];
+  int cl[CPL];
 #pragma unroll
   for (int t = 0; t < CPL; ++t) {
     const int c = lane + kWave * t;
+    cl[t] = c < C ? c : C - 1;
 #pragma unroll
     for (int k = 0; k < L::K; ++k) gd[t][k] = c < C ? G[(static_cast<int64_t>(d) * L::K + k) * C + c] : 0.0f;
   }
@@ -381,71 +391,73 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
         T[L::kidx(l, m)] = v;
       }
   };
-  auto yaddr = [&](int e, int l, int m, int c) -> int64_t {
-    return static_cast<int64_t>(e) * L::blocks(cabs(m)) * C + L::col(l, m) * C + c;
-  };
-  float s_wave = 0.0f;
-  for (int e = b + wave; e < end; e += kWavesPerBlock) {
-    const float *gr = geom + static_cast<int64_t>(e) * gstride;
-    float p = 0.0f;
+  const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
+  float s_row = 0.0f;
+  for (int base = 0; base < el.count; base += kBatch) {
+    const int cnt = min(kBatch, el.count - base);
+    stage_geom(el, base, cnt, geom, gstride, gs4, GS4, gbuf[wave], eids[wave]);
+    for (int i = 0; i < cnt; ++i) {
+      const int e = el.begin + base + i;
+      const float *gr = gb + i * GS4 * 4;
+      float p = 0.0f;
 #pragma unroll
-    for (int t = 0; t < CPL; ++t) {
-      const int c = lane + kWave * t;
-      if (c >= C) continue;
-      float T[L::KEPT];
-      edge_T(gr, t, T);
+      for (int t = 0; t < CPL; ++t) {
+        float T[L::KEPT];
+        edge_T(gr, t, T);
 #pragma unroll
-      for (int l = 0; l <= LMAX; ++l)
+        for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
-        for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
-          p += static_cast<const float *>(Y.p[cabs(m)])[yaddr(e, l, m, c)] * T[L::kidx(l, m)];
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+            const int mu = cabs(m);
+            const float *row = static_cast<const float *>(Y.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
+            p += row[L::col(l, m) * C + cl[t]] * T[L::kidx(l, m)];  // gd is 0 on clamped lanes, so T is too
+          }
+      }
+      p = wave_sum(p);
+      dalpha[e] = p;  // every lane stores the same value and later reads its own store
+      s_row += alpha[e] * p;
     }
-    p = wave_sum(p);
-    dalpha[e] = p;  // every lane stores the same value and later reads its own store
-    s_wave += alpha[e] * p;
+    wave_lds_order();
   }
-  if (lane == 0) srow[wave] = s_wave;
-  __syncthreads();
-  const float s_row = (srow[0] + srow[1]) + (srow[2] + srow[3]);
   float wacc[CPL];
 #pragma unroll
   for (int t = 0; t < CPL; ++t) wacc[t] = 0.0f;
-  for (int e = b + wave; e < end; e += kWavesPerBlock) {
-    const float *gr = geom + static_cast<int64_t>(e) * gstride;
-    const float a = alpha[e];
-    const float da = a * (dalpha[e] - s_row);
+  for (int base = 0; base < el.count; base += kBatch) {
+    const int cnt = min(kBatch, el.count - base);
+    stage_geom(el, base, cnt, geom, gstride, gs4, GS4, gbuf[wave], eids[wave]);
+    for (int i = 0; i < cnt; ++i) {
+      const int e = el.begin + base + i;
+      const float *gr = gb + i * GS4 * 4;
+      const float a = alpha[e];
+      const float da = a * (dalpha[e] - s_row);
 #pragma unroll
-    for (int t = 0; t < CPL; ++t) {
-      const int c = lane + kWave * t;
-      if (c >= C) continue;
-      float T[L::KEPT];
-      edge_T(gr, t, T);
+      for (int t = 0; t < CPL; ++t) {
+        const int c = lane + kWave * t;
+        float T[L::KEPT];
+        edge_T(gr, t, T);
+        const float y00 = static_cast<const float *>(Y.p[0])[static_cast<int64_t>(e) * L::blocks(0) * C + cl[t]];
+        const float wat = w_att[cl[t]];
 #pragma unroll
-      for (int l = 0; l <= LMAX; ++l)
+        for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
-        for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
-          float v = a * T[L::kidx(l, m)];
-          if (l == 0) {
-            const float y00 = static_cast<const float *>(Y.p[0])[yaddr(e, 0, 0, c)];
-            v += da * w_att[c] * dsilu(y00);
-            wacc[t] += da * silu(y00);
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+            float v = a * T[L::kidx(l, m)];
+            if (l == 0) {
+              v += da * wat * dsilu(y00);
+              if (c < C) wacc[t] += da * silu(y00);
+            }
+            const int mu = cabs(m);
+            float *row = static_cast<float *>(dY.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
+            if (c < C) row[L::col(l, m) * C + c] = v;
           }
-          static_cast<float *>(dY.p[cabs(m)])[yaddr(e, l, m, c)] = v;
-        }
+      }
     }
+    wave_lds_order();
   }
 #pragma unroll
-  for (int t = 0; t < CPL; ++t) red[(wave * CPL + t) * kWave + lane] = wacc[t];
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int t = 0; t < CPL; ++t) {
-      const int c = lane + kWave * t;
-      float v = red[(0 * CPL + t) * kWave + lane];
-#pragma unroll
-      for (int w = 1; w < kWavesPerBlock; ++w) v += red[(w * CPL + t) * kWave + lane];
-      if (c < C) watt_part[static_cast<int64_t>(d) * C + c] = v;
-    }
+  for (int t = 0; t < CPL; ++t) {
+    const int c = lane + kWave * t;
+    if (c < C) watt_part[static_cast<int64_t>(d) * C + c] = wacc[t];
   }
 }
 
@@ -783,22 +795,16 @@ struct Launch {
   static void aggregate(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const T *x,
                         T *x_out, T *edge_out, hipStream_t st) {
     CPtr3 Y{{a.Y[0], a.Y[1], a.Y[2]}};
-    const unsigned grid = static_cast<unsigned>(g->n_dst);
-    if (s.C <= 64)
-      aggregate_kernel<LMAX, MMAX, 1, T><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y,
-                                                                    s.C, x, x_out, edge_out);
-    else if (s.C <= 128)
-      aggregate_kernel<LMAX, MMAX, 2, T><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y,
-                                                                    s.C, x, x_out, edge_out);
-    else
-      aggregate_kernel<LMAX, MMAX, 4, T><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y,
-                                                                    s.C, x, x_out, edge_out);
+    const int nch = (s.C + kWave - 1) / kWave;
+    const unsigned grid = ceil_div(static_cast<int64_t>(g->n_dst) * nch, kWavesPerBlock);
+    aggregate_kernel<LMAX, MMAX, T><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, s.nD + s.n_rbf,
+                                                               a.alpha, Y, s.C, x, x_out, edge_out);
   }
   static void bwd_row(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const float *G,
                       const float *w_att, const BwdWs &w, hipStream_t st) {
     CPtr3 Y{{a.Y[0], a.Y[1], a.Y[2]}};
     Ptr3 dY{{w.dY[0], w.dY[1], w.dY[2]}};
-    const unsigned grid = static_cast<unsigned>(g->n_dst);
+    const unsigned grid = ceil_div(g->n_dst, kWavesPerBlock);
     if (s.C <= 64)
       bwd_row_kernel<LMAX, MMAX, 1><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C,
                                                                G, w_att, dY, w.dalpha, w.watt_part);
