@@ -1,0 +1,183 @@
+"""C ABI checks that need no GPU: every declared symbol is exported, host-side
+size queries agree with the documented layouts, and invalid arguments are
+rejected on the host with a status and a message (nothing is launched)."""
+import ctypes as ct
+import os
+import re
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "egnn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from equivariant_gnn_electronic_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from equivariant_gnn_electronic_amd import build
+        build.build(verbose=False)
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(egnn_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from equivariant_gnn_electronic_amd import _lib
+    names = declared_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in egnn.h but not exported"
+    # and the binding declares a signature for each of them
+    assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
+
+
+def test_status_strings(lib):
+    assert lib.egnn_version() >= 100
+    for code in range(6):
+        assert lib.egnn_status_string(code)
+    assert lib.egnn_status_string(99) == b"unknown status"
+
+
+def _desc(lmax, mmax, C, n_rbf=8, r_cut=5.0, storage=0):
+    from equivariant_gnn_electronic_amd import _lib
+    return _lib.EgnnLayerDesc(lmax, mmax, C, n_rbf, r_cut, storage)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_l4", "hfo2", "gst", "halo"])
+def test_weight_count_matches_packed_layout(lib, name):
+    cfg = synth.CONFIGS[name]
+    d = _desc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut)
+    n = sum(int(a * b) for _, (a, b) in synth.layer_weight_sizes(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf))
+    assert lib.egnn_layer_weight_count(ct.byref(d)) == n
+
+
+def test_geom_stride(lib):
+    # rows |m| <= mmax of D^l for l <= lmax, then n_rbf, then the destination, padded to 16
+    for lmax, mmax in [(1, 0), (2, 2), (3, 1), (4, 2), (4, 0)]:
+        nd = sum((2 * min(l, mmax) + 1) * (2 * l + 1) for l in range(lmax + 1))
+        d = _desc(lmax, mmax, 16)
+        assert lib.egnn_geom_stride(ct.byref(d)) == (nd + 8 + 1 + 15) // 16 * 16
+    assert nd == 25 and lib.egnn_geom_stride(ct.byref(_desc(4, 2, 64))) == 128
+
+
+@pytest.mark.parametrize("bad", [dict(lmax=5), dict(lmax=0), dict(mmax=3), dict(C=12), dict(C=0),
+                                 dict(n_rbf=1), dict(n_rbf=17), dict(storage=7)])
+def test_invalid_layer_desc_rejected(lib, bad):
+    from equivariant_gnn_electronic_amd import _lib
+    kw = dict(lmax=4, mmax=2, C=64, n_rbf=8, r_cut=8.0, storage=0)
+    kw.update(bad)
+    d = _lib.EgnnLayerDesc(kw["lmax"], kw["mmax"], kw["C"], kw["n_rbf"], kw["r_cut"], kw["storage"])
+    assert lib.egnn_layer_weight_count(ct.byref(d)) == 0
+    g = _fake_graph(10, 10, 100)
+    st = lib.egnn_layer_fwd(ct.byref(d), ct.byref(g), None, None, None, None, None, None, None, 0, None)
+    assert st == _lib.EGNN_E_ARG
+    assert b"invalid layer description" in lib.egnn_last_error()
+
+
+def _fake_graph(n_dst, n_src, E):
+    """A graph struct with placeholder (never dereferenced) device pointers."""
+    from equivariant_gnn_electronic_amd import _lib
+    g = _lib.EgnnGraph()
+    g.n_dst, g.n_src, g.capacity, g.n_edges = n_dst, n_src, E, E
+    for f in ("row_ptr", "src", "shift", "vec", "dist", "src_ptr", "src_perm"):
+        setattr(g, f, 0x1000)
+    return g
+
+
+def test_layer_sizes_scale_with_edges(lib):
+    d = _desc(4, 2, 64)
+    sizes = []
+    for E in (1000, 2000):
+        s, f, b = ct.c_size_t(), ct.c_size_t(), ct.c_size_t()
+        g = _fake_graph(100, 100, E)
+        assert lib.egnn_layer_sizes(ct.byref(d), ct.byref(g), ct.byref(s), ct.byref(f), ct.byref(b)) == 0
+        sizes.append((s.value, f.value, b.value))
+    # saved = A_m + Y_m + alpha per edge: (19*2C + 19*C) * 4 + 4 bytes at C=64 (plus alignment)
+    per_edge = (19 * 128 + 19 * 64) * 4 + 4
+    assert abs((sizes[1][0] - sizes[0][0]) - 1000 * per_edge) < 8 * 256
+    assert sizes[1][1] > sizes[0][1] and sizes[1][2] > sizes[0][2]
+
+
+def test_graph_argument_checks(lib):
+    from equivariant_gnn_electronic_amd import _lib
+    lo = (ct.c_double * 3)(0, 0, 0)
+    box = (ct.c_double * 3)(10, 10, 10)
+    nb = ct.c_size_t()
+    assert lib.egnn_build_graph_workspace(10, 20, lo, box, 7, 3.0, 100, ct.byref(nb)) == 0 and nb.value > 0
+    nb0 = ct.c_size_t()
+    lib.egnn_build_graph_workspace(10, 20, lo, box, 7, 3.0, 0, ct.byref(nb0))
+    assert nb.value - nb0.value >= 100 * 8 - 256    # the key buffer grows with capacity (256 B alignment)
+    assert lib.egnn_build_graph_workspace(30, 20, lo, box, 7, 3.0, 0, ct.byref(nb)) == _lib.EGNN_E_ARG
+    assert lib.egnn_build_graph_workspace(10, 20, lo, box, 8, 3.0, 0, ct.byref(nb)) == _lib.EGNN_E_ARG
+    bad_box = (ct.c_double * 3)(10, 0, 10)
+    assert lib.egnn_build_graph_workspace(10, 20, lo, bad_box, 7, 3.0, 0, ct.byref(nb)) == _lib.EGNN_E_ARG
+    g = _fake_graph(10, 20, 0)
+    g.capacity = 50
+    g.src = None  # capacity > 0 needs the edge arrays
+    st = lib.egnn_build_graph(ct.c_void_p(0x1000), lo, box, 7, 3.0, ct.byref(g), ct.c_void_p(0x1000),
+                              1 << 30, None)
+    assert st == _lib.EGNN_E_ARG and b"edge arrays" in lib.egnn_last_error()
+    g = _fake_graph(10, 20, 0)
+    st = lib.egnn_build_graph(ct.c_void_p(0x1000), lo, box, 7, 3.0, ct.byref(g), None, 0, None)
+    assert st == _lib.EGNN_E_WORKSPACE
+
+
+def test_backward_rejects_unsupported_storage(lib):
+    from equivariant_gnn_electronic_amd import _lib
+    d = _desc(4, 2, 64, storage=1)
+    g = _fake_graph(10, 10, 100)
+    p = ct.c_void_p(0x1000)
+    st = lib.egnn_layer_bwd(ct.byref(d), ct.byref(g), p, p, p, p, p, p, p, p, 1 << 30, None)
+    assert st == _lib.EGNN_E_UNSUPPORTED
+
+
+def test_workspace_too_small_rejected(lib):
+    from equivariant_gnn_electronic_amd import _lib
+    d = _desc(4, 2, 64)
+    g = _fake_graph(10, 10, 100)
+    p = ct.c_void_p(0x1000)
+    st = lib.egnn_layer_fwd(ct.byref(d), ct.byref(g), p, p, p, ct.c_void_p(0x2000), None, None, p, 16, None)
+    assert st == _lib.EGNN_E_WORKSPACE
+    assert b"workspace" in lib.egnn_last_error()
+    st = lib.egnn_layer_fwd(ct.byref(d), ct.byref(g), p, p, p, p, None, None, p, 1 << 40, None)
+    assert st == _lib.EGNN_E_ARG   # x_out aliases x_in
+
+
+def test_decode_description_checks(lib):
+    from equivariant_gnn_electronic_amd import _lib
+    arr = (ct.c_int32 * 5)(0, 0, 1, 1, 2)
+    h = _lib.EgnnHDesc(4, 64, 5, arr, 0)
+    assert lib.egnn_hblocks_label_rows(ct.byref(h)) == 9 + 17 + 13 + 5 + 1
+    h_small = _lib.EgnnHDesc(3, 64, 5, arr, 0)          # lmax must cover 2 * max shell l
+    assert lib.egnn_hblocks_label_rows(ct.byref(h_small)) == 0
+    assert lib.egnn_hblocks(ct.byref(h_small), 1, 1, None, None, None, None, None, None, None) == _lib.EGNN_E_ARG
+    arr3 = (ct.c_int32 * 1)(3)                            # f shells are not supported
+    h3 = _lib.EgnnHDesc(8, 64, 1, arr3, 0)
+    assert lib.egnn_hblocks_label_rows(ct.byref(h3)) == 0
+    # nothing to do is fine
+    assert lib.egnn_hblocks(ct.byref(h), 0, 0, None, None, None, None, None, None, None) == 0
+
+
+def test_timing_collect_without_events(lib):
+    from equivariant_gnn_electronic_amd import _lib
+    out = (_lib.EgnnTimingEntry * 4)()
+    dropped = ct.c_int64(-1)
+    lib.egnn_timing_reset()
+    assert lib.egnn_timing_collect(out, 4, ct.byref(dropped)) == 0
+    assert dropped.value == 0
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    import equivariant_gnn_electronic_amd as eg
+    with pytest.raises(ValueError):
+        eg._ptr(torch.zeros(3))
