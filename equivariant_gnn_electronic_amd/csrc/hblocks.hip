@@ -33,7 +33,14 @@ constexpr int kMaxEntries = kMaxOrb * kMaxOrb;
 constexpr int kMaxTerms = 8192;
 constexpr int kMaxLab = kMaxEntries;
 
+constexpr int kMaxLab2 = 4;            // labels up to L = 2 * 2
+constexpr int kMaxNL = 64;             // label channels per degree (4 MFMA column tiles)
+
 struct Table {
+  int lmax_lab;                        // 2 * max shell degree
+  int nL[2 * kMaxLab2 + 1];            // label channels per L
+  int woff[2 * kMaxLab2 + 2];          // first weight row of L
+  int hoff[2 * kMaxLab2 + 2];          // first label of L in the (L, M, k) order
   int term_start[kMaxEntries + 1];
   float term_coef[kMaxTerms];
   unsigned short term_idx[kMaxTerms];
@@ -160,8 +167,18 @@ bool build_layout(const int *shell_l, int n_shells, Layout *out) {
   for (int L = 0; L <= Lmax; ++L) hoff[L + 1] = hoff[L] + (2 * L + 1) * out->nL[L];
   out->n_lab = hoff[Lmax + 1];
   if (out->n_lab > kMaxLab || out->n_w > 65535) return false;
+  for (int L = 0; L <= Lmax; ++L)
+    if (out->nL[L] > kMaxNL) return false;
   Table &t = out->t;
   std::memset(&t, 0, sizeof(t));
+  t.lmax_lab = Lmax;
+  for (int L = 0; L <= Lmax; ++L) {
+    t.nL[L] = out->nL[L];
+    t.woff[L] = out->woff[L];
+    t.hoff[L] = hoff[L];
+  }
+  t.woff[Lmax + 1] = out->woff[Lmax + 1];
+  t.hoff[Lmax + 1] = hoff[Lmax + 1];
   for (int L = 0; L <= Lmax; ++L)
     for (int M = -L; M <= L; ++M)
       for (int k = 0; k < out->nL[L]; ++k) {
@@ -249,58 +266,103 @@ egnn_status table_slot(const int *shell_l, int n_shells, int *slot, Layout *lay)
 constexpr int kWave = 64;
 constexpr int kWaves = 4;
 
-template <typename T>
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kTile = 16;  // rows per wave tile (the MFMA M dimension)
+
+// Labels by MFMA, entries from the LDS-resident template.  For each (L, M),
+// the 16 rows x C channels of the tile times W_L^T (C x n_L) is a chain of
+// v_mfma_f32_16x16x4f32 over S = C/4 channel steps.  Lane l feeds row l % 16
+// and channels (l / 16) * S + s at step s, so each lane reads one contiguous
+// run of S channels of its row (vector loads, issued before the chain); W is
+// staged once per block in LDS (rows padded by 4 floats) and read in the same
+// channel order.
+template <int S, typename T>
+__device__ inline void load_run(const T *p, float (&a)[S]) {
+  if constexpr (sizeof(T) == 4 && S % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < S / 4; ++i) {
+      const float4 v = reinterpret_cast<const float4 *>(p)[i];
+      a[4 * i] = v.x;
+      a[4 * i + 1] = v.y;
+      a[4 * i + 2] = v.z;
+      a[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < S; ++i) a[i] = Store<T>::ld(p + i);
+  }
+}
+
+template <int S, typename T>
 __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64_t rows, const T *__restrict__ irreps,
-                                                                  int K, int C, const float *__restrict__ W, int n_w,
+                                                                  int K, const float *__restrict__ W, int n_w,
                                                                   int n_lab, int n_ent, float *__restrict__ H) {
+  constexpr int C = 4 * S;
+  constexpr int WLD = C + 4;  // padded LDS row of W
   extern __shared__ float smem[];
   const Table &tb = g_tables[slot];
   const int n_terms = tb.term_start[n_ent];
-  // LDS: the orbital template (term lists, label maps), W^T, then per-wave rows
   int *t_start = reinterpret_cast<int *>(smem);                        // [n_ent + 1]
   float *t_coef = reinterpret_cast<float *>(t_start + n_ent + 1);     // [n_terms]
   int *t_idx = reinterpret_cast<int *>(t_coef + n_terms);              // [n_terms]
-  int *l_w = t_idx + n_terms;                                          // [n_lab]
-  int *l_f = l_w + n_lab;                                              // [n_lab]
-  float *Wt = reinterpret_cast<float *>(l_f + n_lab);                  // [C][n_w]
-  float *fs_all = Wt + C * n_w;                                        // [kWaves][K][C+1]
-  float *hs_all = fs_all + kWaves * K * (C + 1);                       // [kWaves][n_lab]
+  float *wl = reinterpret_cast<float *>(t_idx + n_terms);              // [n_w + 16][WLD] (zero rows after n_w)
+  wl = reinterpret_cast<float *>((reinterpret_cast<uintptr_t>(wl) + 15) & ~uintptr_t(15));
+  float *hs_all = wl + (n_w + 16) * WLD;                               // [kWaves][kTile][n_lab]
   for (int i = threadIdx.x; i <= n_ent; i += blockDim.x) t_start[i] = tb.term_start[i];
   for (int i = threadIdx.x; i < n_terms; i += blockDim.x) {
     t_coef[i] = tb.term_coef[i];
     t_idx[i] = tb.term_idx[i];
   }
-  for (int i = threadIdx.x; i < n_lab; i += blockDim.x) {
-    l_w[i] = tb.lab_w[i];
-    l_f[i] = tb.lab_f[i] * (C + 1);
-  }
-  for (int i = threadIdx.x; i < C * n_w; i += blockDim.x) {
-    const int w = i / C, c = i % C;          // coalesced read of W[w][c]
-    Wt[c * n_w + w] = W[i];
+  for (int i = threadIdx.x; i < (n_w + 16) * WLD; i += blockDim.x) {
+    const int r = i / WLD, c = i - r * WLD;
+    wl[i] = (r < n_w && c < C) ? W[static_cast<int64_t>(r) * C + c] : 0.0f;
   }
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  float *fs = fs_all + wave * K * (C + 1);
-  float *hs = hs_all + wave * n_lab;
-  for (int64_t r = static_cast<int64_t>(blockIdx.x) * kWaves + wave; r < rows;
-       r += static_cast<int64_t>(gridDim.x) * kWaves) {
-    const T *f = irreps + r * K * C;
-    for (int i = lane; i < K * C; i += kWave) fs[(i / C) * (C + 1) + (i % C)] = Store<T>::ld(f + i);
-    wave_lds_order();
-    for (int q = lane; q < n_lab; q += kWave) {
-      const float *wr = Wt + l_w[q];
-      const float *fr = fs + l_f[q];
-      float acc = 0.0f;
-      for (int c = 0; c < C; ++c) acc += wr[c * n_w] * fr[c];
-      hs[q] = acc;
+  float *hs = hs_all + wave * kTile * n_lab;
+  const int grp = lane / 16, i16 = lane % 16;
+  const int lmax_lab = tb.lmax_lab;
+  const int64_t n_tiles = (rows + kTile - 1) / kTile;
+  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kWaves + wave; tile < n_tiles;
+       tile += static_cast<int64_t>(gridDim.x) * kWaves) {
+    const int64_t e0 = tile * kTile;
+    const int64_t ea = min(e0 + i16, rows - 1);  // clamped row for loads
+    const T *frow = irreps + ea * K * C + grp * S;
+    for (int L = 0; L <= lmax_lab; ++L) {
+      const int nL = tb.nL[L];
+      if (nL == 0) continue;
+      const int ntile = (nL + 15) / 16;
+      const int woff = tb.woff[L], hoff = tb.hoff[L];
+      for (int M = -L; M <= L; ++M) {
+        float a[S];
+        load_run<S>(frow + (L * L + L + M) * C, a);
+        for (int t = 0; t < ntile; ++t) {
+          // rows beyond n_L read the zero rows of the pad (or the next L's rows, discarded below)
+          const float *brow = wl + (woff + 16 * t + i16) * WLD + grp * S;
+          float b[S];
+#pragma unroll
+          for (int i = 0; i < S; ++i) b[i] = brow[i];
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < S; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+          // D[i][j]: row i = 4 * (lane / 16) + r, column j = lane % 16
+          const int k = 16 * t + i16;
+          if (k < nL) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hs[(4 * grp + r) * n_lab + hoff + (M + L) * nL + k] = acc[r];
+          }
+        }
+      }
     }
     wave_lds_order();
-    float *out = H + r * n_ent;
-    for (int q = lane; q < n_ent; q += kWave) {
+    for (int q = lane; q < kTile * n_ent; q += kWave) {
+      const int el = q / n_ent, ent = q - el * n_ent;
+      if (e0 + el >= rows) break;
+      const float *h = hs + el * n_lab;
       float acc = 0.0f;
-      const int t1 = t_start[q + 1];
-      for (int t = t_start[q]; t < t1; ++t) acc += t_coef[t] * hs[t_idx[t]];
-      out[q] = acc;
+      const int t1 = t_start[ent + 1];
+      for (int t = t_start[ent]; t < t1; ++t) acc += t_coef[t] * h[t_idx[t]];
+      H[(e0 + el) * n_ent + ent] = acc;
     }
     wave_lds_order();
   }
@@ -310,18 +372,31 @@ template <typename T>
 egnn_status launch_hblocks(int slot, int64_t rows, const void *irreps, int K, int C, const float *W, int n_w,
                            int n_lab, int n_ent, int n_terms, float *H, hipStream_t stream) {
   if (rows <= 0) return EGNN_OK;
-  const size_t smem = sizeof(float) * (static_cast<size_t>(n_ent + 1) + 2 * n_terms + 2 * n_lab +
-                                       static_cast<size_t>(C) * n_w + kWaves * K * (C + 1) + kWaves * n_lab);
+  const size_t smem = sizeof(float) * (static_cast<size_t>(n_ent + 1) + 2 * n_terms + 4 +
+                                       static_cast<size_t>(n_w + 16) * (C + 4) +
+                                       static_cast<size_t>(kWaves) * kTile * n_lab);
   if (smem > 150 * 1024) {
     set_error("decode needs %zu bytes of LDS; reduce C or the shell list", smem);
     return EGNN_E_UNSUPPORTED;
   }
   Timed t(stream, "hblocks", 0.0,
           double(rows) * (double(K) * C * sizeof(T) + double(n_ent) * 4.0) + double(C) * n_w * 4.0);
-  int64_t blocks = (rows + kWaves - 1) / kWaves;
-  if (blocks > 4096) blocks = 4096;
-  hblocks_kernel<T><<<static_cast<unsigned>(blocks), kWave * kWaves, smem, stream>>>(
-      slot, rows, static_cast<const T *>(irreps), K, C, W, n_w, n_lab, n_ent, H);
+  int64_t blocks = ((rows + kTile - 1) / kTile + kWaves - 1) / kWaves;
+  if (blocks > 2048) blocks = 2048;
+  const unsigned g = static_cast<unsigned>(blocks);
+  const unsigned nt = kWave * kWaves;
+  const T *irr = static_cast<const T *>(irreps);
+  switch (C) {
+    case 8: hblocks_kernel<2, T><<<g, nt, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
+    case 16: hblocks_kernel<4, T><<<g, nt, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
+    case 32: hblocks_kernel<8, T><<<g, nt, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
+    case 64: hblocks_kernel<16, T><<<g, nt, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
+    case 128: hblocks_kernel<32, T><<<g, nt, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
+    case 256: hblocks_kernel<64, T><<<g, nt, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
+    default:
+      set_error("decode supports C in {8, 16, 32, 64, 128, 256}");
+      return EGNN_E_UNSUPPORTED;
+  }
   EGNN_CHECK_LAUNCH();
   return EGNN_OK;
 }
@@ -335,7 +410,7 @@ static bool valid_hdesc(const egnn_hdesc *h) {
   if (!h || !h->shell_l) return false;
   if (h->n_shells < 1 || h->n_shells > 16) return false;
   if (h->lmax < 0 || h->lmax > 8) return false;
-  if (h->C < 8 || h->C > 256 || h->C % 8 != 0) return false;
+  if (h->C < 8 || h->C > 256 || (h->C & (h->C - 1)) != 0) return false;  // C/4 channel steps per lane group
   if (h->storage != EGNN_F32 && h->storage != EGNN_BF16) return false;
   int lmx = 0;
   for (int i = 0; i < h->n_shells; ++i) {

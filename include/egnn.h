@@ -212,7 +212,7 @@ egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph *g, const 
  * ------------------------------------------------------------------------- */
 typedef struct {
   int32_t lmax;              /* degree range of the irreps (K = (lmax+1)^2)   */
-  int32_t C;                 /* channels, multiple of 8, <= 256               */
+  int32_t C;                 /* channels: 8, 16, 32, 64, 128 or 256           */
   int32_t n_shells;          /* 1..16                                         */
   const int32_t *shell_l;    /* host [n_shells]                               */
   int32_t storage;           /* egnn_dtype of the irreps                      */
