@@ -14,6 +14,16 @@ namespace egnn {
 hipError_t gemm_f32(int M, int N, int K, const float *A, int lda, bool a_kcontig, const float *B, int ldb,
                     bool b_kcontig, float *C, int ldc, int splits, int64_t split_stride, hipStream_t stream);
 
+// Complex product by three real products (see gemm.hip):
+//   Cre + i Cim = sum_k (U+ + i U-)(m,k) (V+ + i V-)(n,k),  m < M, n < N.
+// U+/U- at Up/Um (same layout, ldu).  If V3 is given, V1 = V+, V2 = V- - V+,
+// V3 = V+ + V- are precomputed; otherwise V+ = V1 and V- = vsign * V2.
+// Supported layouts: (U, V) K-contiguous with precomputed V; U K-contiguous,
+// V not, precomputed; neither K-contiguous with V from data.  Split-K as gemm_f32.
+hipError_t cgemm_f32(int M, int N, int K, const float *Up, const float *Um, int ldu, bool u_kcontig, const float *V1,
+                     const float *V2, const float *V3, int ldv, bool v_kcontig, float vsign, float *Cre, float *Cim,
+                     int ldc, int splits, int64_t split_stride, hipStream_t stream);
+
 // bf16 operands (raw 16-bit), fp32 accumulate; both operands K-contiguous.
 // C is written as bf16 when c_bf16, else fp32.
 hipError_t gemm_bf16_nt(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,

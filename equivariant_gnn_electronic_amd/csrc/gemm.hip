@@ -165,6 +165,163 @@ __global__ void __launch_bounds__(256, 2) gemm_f32_kernel(int M, int N, int K, c
     }
 }
 
+// ------------------------------------------------------------------------
+// Complex products by Gauss's three-multiplication form.
+//
+// For |m| >= 1 the SO(2) map is a complex multiplication (W_m1 + i W_m2) by
+// (X+ + i X-); its input gradient is a multiplication by the conjugate and
+// its weight gradient a sum of conj-products.  All three are
+//   Re + i Im = sum_k (U+ + i U-)(m,k) (V+ + i V-)(n,k),
+// computed with three real products instead of four:
+//   k1 = sum (U+ + U-) V+,  k2 = sum U+ (V- - V+),  k3 = sum U- (V+ + V-),
+//   Re = k1 - k3,  Im = k1 + k2.
+// U is data with its two halves at a pointer offset; V is either three
+// precomputed matrices (V+, V- - V+, V+ + V-) or data whose second half,
+// times vsign, is V-.  The sums are formed while a tile goes from registers
+// to LDS.  Tile 128 x 128 (per part), K step 8, 4 waves of 64 x 64 x 3 parts.
+constexpr int CBK = 8;
+
+template <bool KCONTIG>
+__device__ inline f32x4 load_ctile(const float *P, int ld, int rows, int row0, int k0, int k_end) {
+  const int f = threadIdx.x;  // one float4 of the 128 x 8 tile per thread
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if (KCONTIG) {
+    const int m = f >> 1, kq = f & 1;
+    const int gm = row0 + m, gk = k0 + kq * 4;
+    if (gm < rows && gk < k_end) v = *reinterpret_cast<const f32x4 *>(P + static_cast<int64_t>(gm) * ld + gk);
+  } else {
+    const int k = f >> 5, mq = f & 31;
+    const int gk = k0 + k, gm = row0 + mq * 4;
+    if (gk < k_end && gm < rows) {
+      const float *p = P + static_cast<int64_t>(gk) * ld + gm;
+      if (gm + 3 < rows) {
+        v = *reinterpret_cast<const f32x4 *>(p);
+      } else {
+        for (int j = 0; j < 4; ++j) v[j] = (gm + j < rows) ? p[j] : 0.f;
+      }
+    }
+  }
+  return v;
+}
+
+template <bool KCONTIG>
+__device__ inline void store_ctile(float *S, const f32x4 &v) {
+  const int f = threadIdx.x;
+  if (KCONTIG) {
+    const int m = f >> 1, kq = f & 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) S[(kq * 4 + j) * (BM + PAD) + m] = v[j];
+  } else {
+    const int k = f >> 5, mq = f & 31;
+    *reinterpret_cast<f32x4 *>(S + k * (BM + PAD) + mq * 4) = v;
+  }
+}
+
+template <bool UK, bool VK, bool VPRE>
+__global__ void __launch_bounds__(256, 2) cgemm_f32_kernel(int M, int N, int K, const float *__restrict__ Up,
+                                                           const float *__restrict__ Um, int ldu,
+                                                           const float *__restrict__ V1, const float *__restrict__ V2,
+                                                           const float *__restrict__ V3, int ldv, float vsign,
+                                                           float *__restrict__ Cre, float *__restrict__ Cim, int ldc,
+                                                           int k_per_split, int64_t split_stride) {
+  constexpr int LT = CBK * (BM + PAD);
+  __shared__ float Us[2][3][LT];
+  __shared__ float Vs[2][3][LT];
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n);
+  if (!tm.valid) return;
+  const int z = blockIdx.y;
+  const int k_begin = z * k_per_split;
+  const int k_end = min(K, k_begin + k_per_split);
+  Cre += z * split_stride;
+  Cim += z * split_stride;
+  const int row0 = tm.mt * BM, col0 = tm.nt * BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int fr = lane & 31, fk = lane >> 5;
+
+  f32x16 acc[3][2][2];
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[q][i][j][r] = 0.f;
+
+  f32x4 up, um, va, vb, vc;
+  auto load = [&](int k0) {
+    up = load_ctile<UK>(Up, ldu, M, row0, k0, k_end);
+    um = load_ctile<UK>(Um, ldu, M, row0, k0, k_end);
+    va = load_ctile<VK>(V1, ldv, N, col0, k0, k_end);
+    vb = load_ctile<VK>(V2, ldv, N, col0, k0, k_end);
+    if (VPRE) vc = load_ctile<VK>(V3, ldv, N, col0, k0, k_end);
+  };
+  auto store = [&](int b) {
+    store_ctile<UK>(Us[b][0], up + um);
+    store_ctile<UK>(Us[b][1], up);
+    store_ctile<UK>(Us[b][2], um);
+    if (VPRE) {
+      store_ctile<VK>(Vs[b][0], va);
+      store_ctile<VK>(Vs[b][1], vb);
+      store_ctile<VK>(Vs[b][2], vc);
+    } else {
+      const f32x4 vm = vb * vsign;  // V- from the second half
+      store_ctile<VK>(Vs[b][0], va);
+      store_ctile<VK>(Vs[b][1], vm - va);
+      store_ctile<VK>(Vs[b][2], va + vm);
+    }
+  };
+  int buf = 0;
+  if (k_begin < k_end) {
+    load(k_begin);
+    store(0);
+  }
+  __syncthreads();
+  for (int k0 = k_begin; k0 < k_end; k0 += CBK) {
+    const bool more = k0 + CBK < k_end;
+    if (more) load(k0 + CBK);
+#pragma unroll
+    for (int kk = 0; kk < CBK; kk += 2) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const float *us = Us[buf][q];
+        const float *vs = Vs[buf][q];
+        float a[2], b[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) a[i] = us[(kk + fk) * (BM + PAD) + wm + 32 * i + fr];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b[j] = vs[(kk + fk) * (BN + PAD) + wn + 32 * j + fr];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[q][i][j], 0, 0, 0);
+      }
+    }
+    if (more) store(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = col0 + wn + 32 * j + fr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + wm + 32 * i + 8 * (r >> 2) + 4 * fk + (r & 3);
+        if (row < M) {
+          const int64_t o = static_cast<int64_t>(row) * ldc + col;
+          Cre[o] = acc[0][i][j][r] - acc[2][i][j][r];
+          Cim[o] = acc[0][i][j][r] + acc[1][i][j][r];
+        }
+      }
+    }
+}
+
 }  // namespace
 
 hipError_t gemm_f32(int M, int N, int K, const float *A, int lda, bool a_kcontig, const float *B, int ldb,
@@ -184,6 +341,28 @@ hipError_t gemm_f32(int M, int N, int K, const float *A, int lda, bool a_kcontig
     gemm_f32_kernel<true, false><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, kps, split_stride);
   else
     gemm_f32_kernel<false, true><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, kps, split_stride);
+  return hipGetLastError();
+}
+
+hipError_t cgemm_f32(int M, int N, int K, const float *Up, const float *Um, int ldu, bool u_kcontig, const float *V1,
+                     const float *V2, const float *V3, int ldv, bool v_kcontig, float vsign, float *Cre, float *Cim,
+                     int ldc, int splits, int64_t split_stride, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (splits < 1) splits = 1;
+  int kps = (K + splits - 1) / splits;
+  kps = (kps + CBK - 1) / CBK * CBK;
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int per = (tiles + kXcd - 1) / kXcd;
+  dim3 grid(per * kXcd, splits);
+  const bool pre = V3 != nullptr;
+#define EGNN_CG(UKc, VKc, PREc)                                                                           \
+  cgemm_f32_kernel<UKc, VKc, PREc><<<grid, 256, 0, stream>>>(M, N, K, Up, Um, ldu, V1, V2, V3, ldv, vsign, Cre, Cim, \
+                                                            ldc, kps, split_stride)
+  if (u_kcontig && v_kcontig && pre) EGNN_CG(true, true, true);
+  else if (u_kcontig && !v_kcontig && pre) EGNN_CG(true, false, true);
+  else if (!u_kcontig && !v_kcontig && !pre) EGNN_CG(false, false, false);
+  else return hipErrorInvalidValue;
+#undef EGNN_CG
   return hipGetLastError();
 }
 

@@ -98,6 +98,16 @@ __global__ void expand_weights_kernel(const float *w1, const float *w2, int rows
   Store<TB>::st(B + i, v);
 }
 
+// V2 = a2 W1 + b2 W2, V3 = a3 W1 + b3 W2: the precomputed weight sums of the
+// three-product complex GEMM (see gemm.hip).
+__global__ void combo_weights_kernel(const float *w1, const float *w2, int64_t n, float a2, float b2, float a3,
+                                     float b3, float *v2, float *v3) {
+  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  v2[i] = a2 * w1[i] + b2 * w2[i];
+  v3[i] = a3 * w1[i] + b3 * w2[i];
+}
+
 __global__ void to_bf16_kernel(const float *in, int64_t n, uint16_t *out) {
   int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) out[i] = f32_to_bf16(in[i]);
@@ -646,18 +656,6 @@ __global__ void __launch_bounds__(256) colsum_kernel(const float *__restrict__ i
   if (ry == 0 && c < ncol) out[c] = (part[0][cx] + part[1][cx]) + (part[2][cx] + part[3][cx]);
 }
 
-// dW_m1 = P[+][+] + P[-][-],  dW_m2 = -P[+][-] + P[-][+]   (P reduced over splits)
-__global__ void fold_dw_kernel(const float *P, int rows, int cols, float *dw1, float *dw2) {
-  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= static_cast<int64_t>(rows) * cols) return;
-  const int no = static_cast<int>(i / cols), ki = static_cast<int>(i % cols);
-  const int64_t ld = 2 * static_cast<int64_t>(cols);
-  const float pp = P[no * ld + ki], pm = P[no * ld + cols + ki];
-  const float mp = P[(rows + no) * ld + ki], mm = P[(rows + no) * ld + cols + ki];
-  dw1[i] = pp + mm;
-  dw2[i] = -pm + mp;
-}
-
 __global__ void fill_f32(float *p, int64_t n, float v) {
   int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -707,7 +705,10 @@ FwdWs carve_fwd_ws(Carver &cv, const LayerShape &s, int64_t E) {
       w.B[0] = nullptr;
       continue;
     }
-    w.B[m] = cv.take<char>(static_cast<size_t>(s.Ng[m]) * s.Kg[m] * bb);
+    // bf16: expanded [[W1, -W2], [W2, W1]]; fp32 (m >= 1): V2 and V3 of the complex GEMM
+    const size_t n = s.storage == EGNN_BF16 ? static_cast<size_t>(s.Ng[m]) * s.Kg[m]
+                                             : static_cast<size_t>(s.Ng[m]) * s.Kg[m] / 2;
+    w.B[m] = cv.take<char>(n * bb);
   }
   w.logit = cv.take<float>(E);
   return w;
@@ -726,8 +727,7 @@ struct BwdWs {
   float *dA[3];
   float *dalpha;
   float *watt_part;
-  float *P;        // split partials of the largest m
-  float *Pred;     // reduced partials
+  float *P;        // split partials (real and imaginary parts for m >= 1)
   float *wrad_part;
 };
 
@@ -739,7 +739,7 @@ BwdWs carve_bwd_ws(Carver &cv, const LayerShape &s, int64_t E, int n_dst, int n_
   BwdWs w{};
   size_t pmax = 0;
   for (int m = 0; m <= s.mmax; ++m) {
-    w.B[m] = m == 0 ? nullptr : cv.take<float>(static_cast<size_t>(s.Ng[m]) * s.Kg[m]);
+    w.B[m] = m == 0 ? nullptr : cv.take<float>(static_cast<size_t>(s.Ng[m]) * s.Kg[m] / 2);
     w.dY[m] = cv.take<float>(static_cast<size_t>(E) * s.Ng[m]);
     w.dA[m] = cv.take<float>(static_cast<size_t>(E) * s.Kg[m]);
     pmax = pmax > static_cast<size_t>(s.Ng[m]) * s.Kg[m] ? pmax : static_cast<size_t>(s.Ng[m]) * s.Kg[m];
@@ -747,7 +747,6 @@ BwdWs carve_bwd_ws(Carver &cv, const LayerShape &s, int64_t E, int n_dst, int n_
   w.dalpha = cv.take<float>(E);
   w.watt_part = cv.take<float>(static_cast<size_t>(n_dst > 0 ? n_dst : 1) * s.C);
   w.P = cv.take<float>(pmax * dw_splits(E));
-  w.Pred = cv.take<float>(pmax);
   w.wrad_part = cv.take<float>(static_cast<size_t>(wrad_streams(n_src)) * s.n_rbf * s.n_pairs * 2 * s.C);
   return w;
 }
@@ -970,12 +969,16 @@ extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph
     }
     const int rows = s.Ng[m] / 2, cols = s.Kg[m] / 2;
     const int64_t n = static_cast<int64_t>(4) * rows * cols;
-    if (bf)
+    if (bf) {
       expand_weights_kernel<uint16_t><<<ceil_div(n, T), T, 0, stream>>>(weights + wo.W1[m], weights + wo.W2[m], rows,
                                                                       cols, static_cast<uint16_t *>(fw.B[m]));
-    else
-      expand_weights_kernel<float><<<ceil_div(n, T), T, 0, stream>>>(weights + wo.W1[m], weights + wo.W2[m], rows, cols,
-                                                                   static_cast<float *>(fw.B[m]));
+    } else {
+      // V+ = W1, V- = W2: V2 = W2 - W1, V3 = W1 + W2
+      const int64_t nb = static_cast<int64_t>(rows) * cols;
+      float *v = static_cast<float *>(fw.B[m]);
+      combo_weights_kernel<<<ceil_div(nb, T), T, 0, stream>>>(weights + wo.W1[m], weights + wo.W2[m], nb, -1.f, 1.f,
+                                                              1.f, 1.f, v, v + nb);
+    }
   }
   const double xb = bf ? 2.0 : 4.0;
   double sumK = 0, sumN = 0;
@@ -996,6 +999,21 @@ extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph
     }
     for (int m = 0; m <= s.mmax; ++m) {
       hipError_t e;
+      if (!bf && m > 0) {
+        // complex product, three real products (executed FLOPs = 3/4 of the four-product count)
+        const int Np = s.Ng[m] / 2, Kp = s.Kg[m] / 2;
+        const float *A = static_cast<const float *>(acts.A[m]);
+        const float *v = static_cast<const float *>(fw.B[m]);
+        const int64_t nb = static_cast<int64_t>(Np) * Kp;
+        Timed t(stream, "cgemm_fwd_f32", 3.0 * 2.0 * double(E) * Np * Kp, double(E) * (s.Kg[m] * xb + s.Ng[m] * 4.0));
+        e = cgemm_f32(static_cast<int>(E), Np, Kp, A, A + Kp, s.Kg[m], true, weights + wo.W1[m], v, v + nb, Kp, true,
+                      1.0f, acts.Y[m], acts.Y[m] + Np, s.Ng[m], 1, 0, stream);
+        if (e != hipSuccess) {
+          set_error("GEMM launch failed: %s", hipGetErrorString(e));
+          return EGNN_E_HIP;
+        }
+        continue;
+      }
       Timed t(stream, bf ? "gemm_nt_bf16" : "gemm_nt_f32", 2.0 * double(E) * s.Ng[m] * s.Kg[m],
               double(E) * (s.Kg[m] * xb + s.Ng[m] * 4.0));
       if (bf) {
@@ -1065,10 +1083,10 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
   const float *x = static_cast<const float *>(x_in);
   fill_f32<<<ceil_div(wo.total, T), T, 0, stream>>>(grad_weights, wo.total, 0.0f);
   for (int m = 1; m <= s.mmax; ++m) {
-    const int rows = s.Ng[m] / 2, cols = s.Kg[m] / 2;
-    const int64_t n = static_cast<int64_t>(4) * rows * cols;
-    expand_weights_kernel<float><<<ceil_div(n, T), T, 0, stream>>>(weights + wo.W1[m], weights + wo.W2[m], rows, cols,
-                                                                 w.B[m]);
+    // input gradient multiplies by conj(W): V+ = W1, V- = -W2, so V2 = -W1 - W2, V3 = W1 - W2
+    const int64_t nb = static_cast<int64_t>(s.Ng[m] / 2) * (s.Kg[m] / 2);
+    combo_weights_kernel<<<ceil_div(nb, T), T, 0, stream>>>(weights + wo.W1[m], weights + wo.W2[m], nb, -1.f, -1.f,
+                                                            1.f, -1.f, w.B[m], w.B[m] + nb);
   }
   double sumK = 0, sumN = 0;
   for (int m = 0; m <= s.mmax; ++m) {
@@ -1088,9 +1106,38 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
   if (E > 0) {
     const int splits = dw_splits(E);
     for (int m = 0; m <= s.mmax; ++m) {
-      const float *B = m == 0 ? weights + wo.W0 : w.B[m];
-      // dA_m = dY_m B_m
       hipError_t e;
+      if (m > 0) {
+        const int Np = s.Ng[m] / 2, Kp = s.Kg[m] / 2;
+        const int64_t nb = static_cast<int64_t>(Np) * Kp;
+        const float *A = static_cast<const float *>(acts.A[m]);
+        {
+          // (dX+ + i dX-) = sum_n (dY+ + i dY-)(n) conj(W)(n, k)
+          Timed t(stream, "cgemm_dx_f32", 3.0 * 2.0 * double(E) * Np * Kp, double(E) * (s.Ng[m] + s.Kg[m]) * 4.0);
+          e = cgemm_f32(static_cast<int>(E), Kp, Np, w.dY[m], w.dY[m] + Np, s.Ng[m], true, weights + wo.W1[m], w.B[m],
+                        w.B[m] + nb, Kp, false, 1.0f, w.dA[m], w.dA[m] + Kp, s.Kg[m], 1, 0, stream);
+        }
+        if (e != hipSuccess) {
+          set_error("GEMM launch failed: %s", hipGetErrorString(e));
+          return EGNN_E_HIP;
+        }
+        {
+          // dW1 + i dW2 = sum_e (dY+ + i dY-)^T (X+ - i X-), split over edges
+          Timed t(stream, "cgemm_dw_f32", 3.0 * 2.0 * double(E) * Np * Kp,
+                  double(E) * (s.Ng[m] + s.Kg[m]) * 4.0 + 2.0 * double(splits) * nb * 4.0);
+          e = cgemm_f32(Np, Kp, static_cast<int>(E), w.dY[m], w.dY[m] + Np, s.Ng[m], false, A, A + Kp, nullptr,
+                        s.Kg[m], false, -1.0f, w.P, w.P + splits * nb, Kp, splits, nb, stream);
+        }
+        if (e != hipSuccess) {
+          set_error("GEMM launch failed: %s", hipGetErrorString(e));
+          return EGNN_E_HIP;
+        }
+        colsum_kernel<<<ceil_div(nb, 64), 256, 0, stream>>>(w.P, splits, nb, nb, grad_weights + wo.W1[m]);
+        colsum_kernel<<<ceil_div(nb, 64), 256, 0, stream>>>(w.P + splits * nb, splits, nb, nb, grad_weights + wo.W2[m]);
+        continue;
+      }
+      const float *B = weights + wo.W0;
+      // dA_0 = dY_0 W0
       {
         Timed t(stream, "gemm_nn_f32", 2.0 * double(E) * s.Ng[m] * s.Kg[m], double(E) * (s.Ng[m] + s.Kg[m]) * 4.0);
         e = gemm_f32(static_cast<int>(E), s.Kg[m], s.Ng[m], w.dY[m], s.Ng[m], true, B, s.Kg[m], false,
@@ -1112,14 +1159,7 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
         set_error("GEMM launch failed: %s", hipGetErrorString(e));
         return EGNN_E_HIP;
       }
-      if (m == 0) {
-        colsum_kernel<<<ceil_div(pn, 64), 256, 0, stream>>>(w.P, splits, pn, pn, grad_weights + wo.W0);
-      } else {
-        colsum_kernel<<<ceil_div(pn, 64), 256, 0, stream>>>(w.P, splits, pn, pn, w.Pred);
-        const int rows = s.Ng[m] / 2, cols = s.Kg[m] / 2;
-        fold_dw_kernel<<<ceil_div(static_cast<int64_t>(rows) * cols, T), T, 0, stream>>>(
-            w.Pred, rows, cols, grad_weights + wo.W1[m], grad_weights + wo.W2[m]);
-      }
+      colsum_kernel<<<ceil_div(pn, 64), 256, 0, stream>>>(w.P, splits, pn, pn, grad_weights + wo.W0);
     }
     const int ncol = s.n_pairs * 2 * s.C;
     {
