@@ -322,6 +322,103 @@ __global__ void __launch_bounds__(256, 2) cgemm_f32_kernel(int M, int N, int K, 
     }
 }
 
+// ------------------------------------------------------------------------
+// bf16 operands, fp32 accumulate: v_mfma_f32_32x32x16_bf16.  Both operands
+// K-contiguous; tiles are staged in LDS in the same [row][k] order (rows
+// padded by 8 bf16), and each lane reads its 8 consecutive k values of a
+// fragment row as one 16-byte LDS read.  Tile 128 x 128, K step 32, 4 waves
+// of 64 x 64, XCD-aware tile order as above.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr int HBM_ = 128, HBN = 128, HBK = 32, HPAD = 8;
+constexpr int HLD = HBK + HPAD;  // LDS row length (bf16)
+
+__device__ inline uint4 load_bf16_chunk(const uint16_t *P, int ld, int rows, int row, int k, int K) {
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (row < rows && k < K) v = *reinterpret_cast<const uint4 *>(P + static_cast<int64_t>(row) * ld + k);
+  return v;
+}
+
+template <bool CBF16>
+__global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(int M, int N, int K, const uint16_t *__restrict__ A, int lda,
+                                                           const uint16_t *__restrict__ B, int ldb, void *__restrict__ C,
+                                                           int ldc) {
+  __shared__ uint16_t As[2][HBM_ * HLD];
+  __shared__ uint16_t Bs[2][HBN * HLD];
+  const int tiles_m = (M + HBM_ - 1) / HBM_, tiles_n = (N + HBN - 1) / HBN;
+  const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n);
+  if (!tm.valid) return;
+  const int row0 = tm.mt * HBM_, col0 = tm.nt * HBN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  // each thread moves two 16-byte chunks of each 128 x 32 tile: chunk c -> row c / 4, k (c % 4) * 8
+  const int c0 = threadIdx.x, c1 = threadIdx.x + 256;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  uint4 ra0, ra1, rb0, rb1;
+  auto load = [&](int k0) {
+    ra0 = load_bf16_chunk(A, lda, M, row0 + c0 / 4, k0 + (c0 % 4) * 8, K);
+    ra1 = load_bf16_chunk(A, lda, M, row0 + c1 / 4, k0 + (c1 % 4) * 8, K);
+    rb0 = load_bf16_chunk(B, ldb, N, col0 + c0 / 4, k0 + (c0 % 4) * 8, K);
+    rb1 = load_bf16_chunk(B, ldb, N, col0 + c1 / 4, k0 + (c1 % 4) * 8, K);
+  };
+  auto store = [&](int b) {
+    *reinterpret_cast<uint4 *>(&As[b][(c0 / 4) * HLD + (c0 % 4) * 8]) = ra0;
+    *reinterpret_cast<uint4 *>(&As[b][(c1 / 4) * HLD + (c1 % 4) * 8]) = ra1;
+    *reinterpret_cast<uint4 *>(&Bs[b][(c0 / 4) * HLD + (c0 % 4) * 8]) = rb0;
+    *reinterpret_cast<uint4 *>(&Bs[b][(c1 / 4) * HLD + (c1 % 4) * 8]) = rb1;
+  };
+  int buf = 0;
+  if (K > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int k0 = 0; k0 < K; k0 += HBK) {
+    const bool more = k0 + HBK < K;
+    if (more) load(k0 + HBK);
+#pragma unroll
+    for (int kk = 0; kk < HBK; kk += 16) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const bf16x8 *>(&As[buf][(wm + 32 * i + fr) * HLD + kk + fk]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][(wn + 32 * j + fr) * HLD + kk + fk]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) store(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = col0 + wn + 32 * j + fr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row >= M) continue;
+        const int64_t o = static_cast<int64_t>(row) * ldc + col;
+        if (CBF16)
+          static_cast<uint16_t *>(C)[o] = f32_to_bf16(acc[i][j][r]);
+        else
+          static_cast<float *>(C)[o] = acc[i][j][r];
+      }
+    }
+}
+
 }  // namespace
 
 hipError_t gemm_f32(int M, int N, int K, const float *A, int lda, bool a_kcontig, const float *B, int ldb,
@@ -366,9 +463,17 @@ hipError_t cgemm_f32(int M, int N, int K, const float *Up, const float *Um, int 
   return hipGetLastError();
 }
 
-hipError_t gemm_bf16_nt(int, int, int, const uint16_t *, int, const uint16_t *, int, void *, int, bool,
-                        hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t gemm_bf16_nt(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C, int ldc,
+                        bool c_bf16, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (K % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0) return hipErrorInvalidValue;
+  const int tiles = ((M + HBM_ - 1) / HBM_) * ((N + HBN - 1) / HBN);
+  const int per = (tiles + kXcd - 1) / kXcd;
+  if (c_bf16)
+    gemm_bf16_kernel<true><<<per * kXcd, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+  else
+    gemm_bf16_kernel<false><<<per * kXcd, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+  return hipGetLastError();
 }
 
 }  // namespace egnn

@@ -252,8 +252,9 @@ __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restr
 
 // logits a_e = sum_c w_att[c] SiLU(Y0[e][c]) and the row softmax (one wave per row,
 // one edge per lane, online max/sum over chunks of 64 edges)
+template <typename T>
 __global__ void __launch_bounds__(kThreads) attention_kernel(const int *__restrict__ row_ptr, int n_dst,
-                                                             const float *__restrict__ Y0, int ldy0, int C,
+                                                             const T *__restrict__ Y0, int ldy0, int C,
                                                              const float *__restrict__ w_att, float *logit,
                                                              float *alpha) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -265,12 +266,9 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const int *__restri
     const int e = base + lane;
     float a = -INFINITY;
     if (e < end) {
-      const float *y = Y0 + static_cast<int64_t>(e) * ldy0;
+      const T *y = Y0 + static_cast<int64_t>(e) * ldy0;
       float acc = 0.0f;
-      for (int c = 0; c < C; c += 4) {
-        float4 v = *reinterpret_cast<const float4 *>(y + c);
-        acc += w_att[c] * silu(v.x) + w_att[c + 1] * silu(v.y) + w_att[c + 2] * silu(v.z) + w_att[c + 3] * silu(v.w);
-      }
+      for (int c = 0; c < C; ++c) acc += w_att[c] * silu(Store<T>::ld(y + c));
       a = acc;
       logit[e] = a;
     }
@@ -331,8 +329,8 @@ __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restri
 #pragma unroll
         for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
           const int mu = cabs(m);
-          const float *row = static_cast<const float *>(Y.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
-          y[L::kidx(l, m)] = row[L::col(l, m) * C + cl];
+          const T *row = static_cast<const T *>(Y.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
+          y[L::kidx(l, m)] = Store<T>::ld(row + L::col(l, m) * C + cl);
         }
       T *eo = edge_out ? edge_out + static_cast<int64_t>(e) * L::K * C : nullptr;
 #pragma unroll
@@ -677,7 +675,7 @@ struct Carver {
 
 struct Acts {  // what the backward needs from the forward
   void *A[3];
-  float *Y[3];
+  void *Y[3];      // fp32, or bf16 when the storage is bf16
   float *alpha;
 };
 
@@ -687,7 +685,7 @@ Acts carve_acts(Carver &cv, const LayerShape &s, int64_t E) {
   for (int m = 0; m <= s.mmax; ++m) {
     a.A[m] = cv.take<char>(static_cast<size_t>(E) * s.Kg[m] * ab);
   }
-  for (int m = 0; m <= s.mmax; ++m) a.Y[m] = cv.take<float>(static_cast<size_t>(E) * s.Ng[m]);
+  for (int m = 0; m <= s.mmax; ++m) a.Y[m] = cv.take<char>(static_cast<size_t>(E) * s.Ng[m] * ab);
   a.alpha = cv.take<float>(E);
   return a;
 }
@@ -1007,7 +1005,8 @@ extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph
         const int64_t nb = static_cast<int64_t>(Np) * Kp;
         Timed t(stream, "cgemm_fwd_f32", 3.0 * 2.0 * double(E) * Np * Kp, double(E) * (s.Kg[m] * xb + s.Ng[m] * 4.0));
         e = cgemm_f32(static_cast<int>(E), Np, Kp, A, A + Kp, s.Kg[m], true, weights + wo.W1[m], v, v + nb, Kp, true,
-                      1.0f, acts.Y[m], acts.Y[m] + Np, s.Ng[m], 1, 0, stream);
+                      1.0f, static_cast<float *>(acts.Y[m]), static_cast<float *>(acts.Y[m]) + Np, s.Ng[m], 1, 0,
+                      stream);
         if (e != hipSuccess) {
           set_error("GEMM launch failed: %s", hipGetErrorString(e));
           return EGNN_E_HIP;
@@ -1018,11 +1017,11 @@ extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph
               double(E) * (s.Kg[m] * xb + s.Ng[m] * 4.0));
       if (bf) {
         e = gemm_bf16_nt(static_cast<int>(E), s.Ng[m], s.Kg[m], static_cast<const uint16_t *>(acts.A[m]), s.Kg[m],
-                         static_cast<const uint16_t *>(fw.B[m]), s.Kg[m], acts.Y[m], s.Ng[m], false, stream);
+                         static_cast<const uint16_t *>(fw.B[m]), s.Kg[m], acts.Y[m], s.Ng[m], true, stream);
       } else {
         const float *B = m == 0 ? weights + wo.W0 : static_cast<const float *>(fw.B[m]);
         e = gemm_f32(static_cast<int>(E), s.Ng[m], s.Kg[m], static_cast<const float *>(acts.A[m]), s.Kg[m], true, B,
-                     s.Kg[m], true, acts.Y[m], s.Ng[m], 1, 0, stream);
+                     s.Kg[m], true, static_cast<float *>(acts.Y[m]), s.Ng[m], 1, 0, stream);
       }
       if (e != hipSuccess) {
         set_error("GEMM launch failed: %s", hipGetErrorString(e));
@@ -1033,8 +1032,14 @@ extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph
   if (g->n_dst > 0) {
     if (E > 0) {
       Timed t(stream, "attention", 0.0, double(E) * (s.C * 4.0 + 8.0));
-      attention_kernel<<<ceil_div(g->n_dst, kWavesPerBlock), kThreads, 0, stream>>>(
-          g->row_ptr, g->n_dst, acts.Y[0], s.Ng[0], s.C, weights + wo.watt, fw.logit, acts.alpha);
+      if (bf)
+        attention_kernel<uint16_t><<<ceil_div(g->n_dst, kWavesPerBlock), kThreads, 0, stream>>>(
+            g->row_ptr, g->n_dst, static_cast<const uint16_t *>(acts.Y[0]), s.Ng[0], s.C, weights + wo.watt, fw.logit,
+            acts.alpha);
+      else
+        attention_kernel<float><<<ceil_div(g->n_dst, kWavesPerBlock), kThreads, 0, stream>>>(
+            g->row_ptr, g->n_dst, static_cast<const float *>(acts.Y[0]), s.Ng[0], s.C, weights + wo.watt, fw.logit,
+            acts.alpha);
     }
     const double bytes = double(E) * (sumN * 4.0 + s.nD * 4.0 + 4.0) + 2.0 * g->n_dst * s.K * s.C * xb +
                          (edge_out ? double(E) * s.K * s.C * xb : 0.0);

@@ -63,6 +63,8 @@ CONFIGS = {
                    note="64 atoms, 2 species Bernoulli(1/2), 9 A periodic cube, r_c 5 A"),
     "tiny_l4": Config("tiny_l4", 1, (32, 32), (9.0, 9.0, 9.0), True, 5.0, 4, 2, 8,
                       note="tiny geometry at lmax 4 / mmax 2 / C 8 (m-truncation, decode)"),
+    "tiny_stack": Config("tiny_stack", 1, (32, 32), (9.0, 9.0, 9.0), True, 5.0, 4, 2, 16, storage="bf16",
+                         layers=3, note="tiny geometry, 3 stacked layers, bf16 storage"),
     "hfo2": Config("hfo2", 2, (1000, 2000), (32.8, 32.8, 32.8), True, 8.0, 4, 2, 64,
                    note="HfO2-like: 1,000 Hf + 2,000 O in a 32.8 A periodic cube, r_c 8 A"),
     "gst": Config("gst", 3, (1792, 1792, 4480), (62.5, 62.5, 62.5), True, 10.0, 4, 2, 128,
@@ -79,7 +81,7 @@ CONFIGS = {
 
 # Species are drawn as a random assignment of the fixed counts, except for the
 # tiny cell whose two species are Bernoulli(1/2).
-_BERNOULLI = {"tiny", "tiny_l4"}
+_BERNOULLI = {"tiny", "tiny_l4", "tiny_stack"}
 
 
 def bf16_round(a):

@@ -191,3 +191,83 @@ def test_hblocks(dev):
     hn_ref = odec.hblocks(r["xo"].cpu().numpy(), wn)
     assert_close(he.cpu().numpy(), he_ref, 1e-5, "edge blocks")
     assert_close(hn.cpu().numpy(), hn_ref, 1e-5, "on-site blocks")
+
+
+def _rotate_irreps(a, Q, lmax):
+    out = np.empty_like(a)
+    for l in range(lmax + 1):
+        sl = slice(l * l, (l + 1) ** 2)
+        out[:, sl, :] = np.einsum("mn,enc->emc", so3.wigner_d(l, Q), a[:, sl, :])
+    return out
+
+
+def _run_stack(cfg, dev, g, geom, x_t, ws):
+    """The layers of cfg chained through the ABI (bf16 or fp32 storage)."""
+    storage = eg.EGNN_BF16 if cfg.storage == "bf16" else eg.EGNN_F32
+    desc = eg.layer_desc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut, storage)
+    xs = x_t
+    for w in ws:
+        (xs, _), _ = eg.egnn_layer_fwd(desc, g, geom, torch.from_numpy(w).to(dev), xs)
+    torch.cuda.synchronize()
+    return xs
+
+
+def test_layer_stack_bf16_tiny(dev):
+    """Three layers with bf16 storage against the oracle on the same bf16 inputs."""
+    cfg = synth.CONFIGS["tiny_stack"]
+    s = synth.make_structure(cfg)
+    x, ws = synth.make_layer_inputs(cfg)
+    g = gpu_graph(s, dev)
+    desc = eg.layer_desc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut, eg.EGNN_BF16)
+    geom = eg.egnn_edge_geom(desc, g)
+    xo = _run_stack(cfg, dev, g, geom, torch.from_numpy(x).to(dev).to(torch.bfloat16), ws).float().cpu().numpy()
+    og = oracle_graph(s)
+    xr = x.astype(np.float64)
+    for w in ws:
+        xr = olayer.layer_forward(og, xr, w.astype(np.float64), desc_of(cfg))["x_out"]
+    assert_close(xo, xr, 2e-2, "3-layer bf16 x_out")
+
+
+def test_layer_forward_gst_bf16_sampled_rows(dev):
+    """First layer of the 8,064-atom GeSbTe-like cell (bf16 storage, C 128) on sampled rows."""
+    cfg = synth.CONFIGS["gst"]
+    r = _gpu_forward(cfg, dev)
+    rows = sample_rows(r["s"].n_dst, 120, 7)
+    og = oracle_graph(r["s"], rows=rows)
+    xo_ref, _ = olayer.layer_forward_rows(og, r["x"].astype(np.float64), r["w"].astype(np.float64), desc_of(cfg))
+    xo = r["xo"].float().cpu().numpy()[rows]
+    assert_close(xo, xo_ref, 2e-2, "gst x_out rows")
+
+
+def test_layer_forward_halo_sampled_rows(dev):
+    """One GPU's share: 30,000 owned rows, 21,133 ghost sources, open boundary, fp32."""
+    cfg = synth.CONFIGS["halo"]
+    r = _gpu_forward(cfg, dev)
+    assert r["g"].n_src > r["g"].n_dst
+    rows = sample_rows(r["s"].n_dst, 200, 9)
+    og = oracle_graph(r["s"], rows=rows)
+    xo_ref, _ = olayer.layer_forward_rows(og, r["x"].astype(np.float64), r["w"].astype(np.float64), desc_of(cfg))
+    xo = r["xo"].float().cpu().numpy()[rows]
+    assert_close(xo, xo_ref, 1e-4, "halo x_out rows")
+    assert_close(xo - r["x"][rows], xo_ref - r["x"][rows], 1e-4, "halo aggregate rows")
+
+
+def test_gst_stack_equivariance_full_size(dev):
+    """Full 8,064-atom, 3-layer bf16 stack: rotating every edge vector and input irrep by Q
+    rotates the output by D(Q) (a property that holds at any size)."""
+    from scipy.spatial.transform import Rotation as Rot
+    cfg = synth.CONFIGS["gst"]
+    s = synth.make_structure(cfg)
+    x, ws = synth.make_layer_inputs(cfg)
+    g = gpu_graph(s, dev)
+    desc = eg.layer_desc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut, eg.EGNN_BF16)
+    geom = eg.egnn_edge_geom(desc, g)
+    base = _run_stack(cfg, dev, g, geom, torch.from_numpy(x).to(dev).to(torch.bfloat16), ws).float().cpu().numpy()
+    Q = Rot.random(random_state=11).as_matrix()
+    vec = g.vec.cpu().numpy().astype(np.float64) @ Q.T
+    g2 = eg.Graph(g.n_dst, g.n_src, g.n_edges, g.row_ptr, g.src, g.shift,
+                  torch.from_numpy(vec.astype(np.float32)).to(dev), g.dist, g.src_ptr, g.src_perm)
+    geom2 = eg.egnn_edge_geom(desc, g2)
+    xr = synth.bf16_round(_rotate_irreps(x.astype(np.float64), Q, cfg.lmax).astype(np.float32))
+    rot = _run_stack(cfg, dev, g2, geom2, torch.from_numpy(xr).to(dev).to(torch.bfloat16), ws).float().cpu().numpy()
+    assert_close(rot, _rotate_irreps(base, Q, cfg.lmax), 2e-2, "rotated 3-layer output")
