@@ -252,34 +252,66 @@ __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restr
 
 // logits a_e = sum_c w_att[c] SiLU(Y0[e][c]) and the row softmax (one wave per row,
 // one edge per lane, online max/sum over chunks of 64 edges)
+// Logits and softmax over one destination row per wave.  Sixteen lanes share
+// an edge (16-byte loads of its invariant output plane, reduced with four
+// butterfly steps), so four edges are read per pass with coalesced rows.
+// Lane 16g keeps a running (max, sum) over the edges it owns; the row's
+// softmax combines them in a fixed order, and the same lanes write alpha.
 template <typename T>
 __global__ void __launch_bounds__(kThreads) attention_kernel(const int *__restrict__ row_ptr, int n_dst,
                                                              const T *__restrict__ Y0, int ldy0, int C,
                                                              const float *__restrict__ w_att, float *logit,
                                                              float *alpha) {
+  constexpr int VW = 16 / sizeof(T);  // channels per 16-byte load
+  constexpr int U = 2;                // edge groups in flight per lane
   const int lane = threadIdx.x & (kWave - 1);
   const int d = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (d >= n_dst) return;
   const int b = row_ptr[d], end = row_ptr[d + 1];
+  if (b == end) return;
+  const int grp = lane >> 4, sub = lane & 15;
   float M = -INFINITY, S = 0.0f;
-  for (int base = b; base < end; base += kWave) {
-    const int e = base + lane;
-    float a = -INFINITY;
-    if (e < end) {
-      const T *y = Y0 + static_cast<int64_t>(e) * ldy0;
-      float acc = 0.0f;
-      for (int c = 0; c < C; ++c) acc += w_att[c] * silu(Store<T>::ld(y + c));
-      a = acc;
-      logit[e] = a;
+  for (int base = b; base < end; base += 4 * U) {
+    float acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc[u] = 0.0f;
+      const int e = base + 4 * u + grp;
+      if (e < end) {
+        const T *y = Y0 + static_cast<int64_t>(e) * ldy0;
+        for (int c0 = sub * VW; c0 < C; c0 += 16 * VW) {
+          const uint4 raw = *reinterpret_cast<const uint4 *>(y + c0);
+          T v[VW];
+          memcpy(v, &raw, sizeof(raw));
+#pragma unroll
+          for (int j = 0; j < VW; ++j) acc[u] += w_att[c0 + j] * silu(Store<T>::ld(&v[j]));
+        }
+      }
     }
-    const float mc = wave_max(a);
-    const float Mn = fmaxf(M, mc);
-    const float ex = e < end ? expf(a - Mn) : 0.0f;
-    S = S * expf(M - Mn) + wave_sum(ex);
-    M = Mn;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float a = acc[u];
+      a += __shfl_xor(a, 8);
+      a += __shfl_xor(a, 4);
+      a += __shfl_xor(a, 2);
+      a += __shfl_xor(a, 1);
+      const int e = base + 4 * u + grp;
+      if (sub == 0 && e < end) {
+        logit[e] = a;
+        const float Mn = fmaxf(M, a);
+        S = S * expf(M - Mn) + expf(a - Mn);
+        M = Mn;
+      }
+    }
   }
-  const float inv = 1.0f / S;
-  for (int e = b + lane; e < end; e += kWave) alpha[e] = expf(logit[e] - M) * inv;
+  const float Mrow = wave_max(M);
+  const float Srow = wave_sum(M == -INFINITY ? 0.0f : S * expf(M - Mrow));
+  const float inv = 1.0f / Srow;
+  if (sub == 0)
+    for (int base = b; base < end; base += 4) {
+      const int e = base + grp;
+      if (e < end) alpha[e] = expf(logit[e] - Mrow) * inv;
+    }
 }
 
 // x_out[d] = x[d] + sum_e alpha_e D_e^T Yhat_e ; edge_out[e] = D_e^T Yhat_e.
@@ -1003,7 +1035,7 @@ extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph
         const float *A = static_cast<const float *>(acts.A[m]);
         const float *v = static_cast<const float *>(fw.B[m]);
         const int64_t nb = static_cast<int64_t>(Np) * Kp;
-        Timed t(stream, "cgemm_fwd_f32", 3.0 * 2.0 * double(E) * Np * Kp, double(E) * (s.Kg[m] * xb + s.Ng[m] * 4.0));
+        Timed t(stream, "cgemm_fwd_f32", 2.0 * double(E) * s.Ng[m] * s.Kg[m], double(E) * (s.Kg[m] * xb + s.Ng[m] * 4.0));
         e = cgemm_f32(static_cast<int>(E), Np, Kp, A, A + Kp, s.Kg[m], true, weights + wo.W1[m], v, v + nb, Kp, true,
                       1.0f, static_cast<float *>(acts.Y[m]), static_cast<float *>(acts.Y[m]) + Np, s.Ng[m], 1, 0,
                       stream);
@@ -1041,7 +1073,7 @@ extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph
             g->row_ptr, g->n_dst, static_cast<const float *>(acts.Y[0]), s.Ng[0], s.C, weights + wo.watt, fw.logit,
             acts.alpha);
     }
-    const double bytes = double(E) * (sumN * 4.0 + s.nD * 4.0 + 4.0) + 2.0 * g->n_dst * s.K * s.C * xb +
+    const double bytes = double(E) * (sumN * xb + s.nD * 4.0 + 4.0) + 2.0 * g->n_dst * s.K * s.C * xb +
                          (edge_out ? double(E) * s.K * s.C * xb : 0.0);
     Timed t(stream, "aggregate", 0.0, bytes);
     if (bf) {
@@ -1118,7 +1150,7 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
         const float *A = static_cast<const float *>(acts.A[m]);
         {
           // (dX+ + i dX-) = sum_n (dY+ + i dY-)(n) conj(W)(n, k)
-          Timed t(stream, "cgemm_dx_f32", 3.0 * 2.0 * double(E) * Np * Kp, double(E) * (s.Ng[m] + s.Kg[m]) * 4.0);
+          Timed t(stream, "cgemm_dx_f32", 2.0 * double(E) * s.Ng[m] * s.Kg[m], double(E) * (s.Ng[m] + s.Kg[m]) * 4.0);
           e = cgemm_f32(static_cast<int>(E), Kp, Np, w.dY[m], w.dY[m] + Np, s.Ng[m], true, weights + wo.W1[m], w.B[m],
                         w.B[m] + nb, Kp, false, 1.0f, w.dA[m], w.dA[m] + Kp, s.Kg[m], 1, 0, stream);
         }
@@ -1128,7 +1160,7 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
         }
         {
           // dW1 + i dW2 = sum_e (dY+ + i dY-)^T (X+ - i X-), split over edges
-          Timed t(stream, "cgemm_dw_f32", 3.0 * 2.0 * double(E) * Np * Kp,
+          Timed t(stream, "cgemm_dw_f32", 2.0 * double(E) * s.Ng[m] * s.Kg[m],
                   double(E) * (s.Ng[m] + s.Kg[m]) * 4.0 + 2.0 * double(splits) * nb * 4.0);
           e = cgemm_f32(Np, Kp, static_cast<int>(E), w.dY[m], w.dY[m] + Np, s.Ng[m], false, A, A + Kp, nullptr,
                         s.Kg[m], false, -1.0f, w.P, w.P + splits * nb, Kp, splits, nb, stream);

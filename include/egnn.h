@@ -81,8 +81,14 @@ int egnn_version(void);
  *   vec  = (float)delta  (source image -> destination),
  *   dist = (float)sqrt(d2),
  *   src_ptr/src_perm = the edge ids of each source in ascending order
- *   (a CSR over sources, used by the backward pass).
+ *   (a CSR over sources, used by the forward source gather and the backward).
  * The output is deterministic (bit-identical between runs).
+ * A graph handed to the layer calls must be consistent: row_ptr[n_dst] ==
+ * n_edges, src_ptr[n_src] == n_edges, and src_perm a permutation of
+ * 0..n_edges-1 grouped as above.  egnn_build_graph always produces such a
+ * graph; a caller that assembles one itself (a prefix of rows, say) must
+ * rebuild src_ptr/src_perm for its edges.  The kernels index with these
+ * arrays without re-checking them.
  * ------------------------------------------------------------------------- */
 typedef struct {
   int32_t n_dst, n_src;        /* rows; sources (owned first, then ghosts)                  */
