@@ -47,6 +47,12 @@ def parse():
     ap.add_argument("--workload", default="train", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=500, help="rows of the oracle's timed sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=1024,
+                    help="size of the plain elementwise copy (y = -x, float32) timed before the steps; it gives "
+                         "the measured copy bandwidth, and a counter run sees it as a kernel of known traffic")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="(no GPU) turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script into "
+                         "the traffic summary under profiles/ and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="saturation sweep: layer forward and edge geometry time vs edge count, on the first "
                          "rows of the one-GPU-share (halo) graph; prints one JSON line")
@@ -130,7 +136,116 @@ class Step:
             self.buf.ws.numel(), eg._stream()))
 
 
-def roofline(timing, dtype):
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "equivariant_gnn_electronic_amd", "csrc")
+COPY_KERNEL_TAG = "neg_kernel"
+
+
+def kernel_source_hash():
+    """sha256 over every HIP source and header of the library (a traffic figure is
+    only reported for the sources it was measured on)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+
+
+def read_traffic(workload, family):
+    """HBM bytes per launch of `family` from the committed counter summary, or None
+    when there is none, it covers another kernel, or the sources changed since."""
+    try:
+        with open(traffic_path(workload)) as fh:
+            kv = dict(line.split(": ", 1) for line in fh.read().splitlines() if ": " in line and not line.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("kernel") != family or kv.get("source_sha256") != kernel_source_hash():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def _pmc_per_dispatch(d, counter):
+    """{dispatch id: (kernel name, value)} from a rocprofv3 csv counter collection."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = r["Dispatch_Id"]
+                name, v = out.get(k, (r["Kernel_Name"], 0.0))
+                out[k] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def summarize_traffic(fetch_dir, write_dir, workload, copy_mib, family, argv):
+    """Write profiles/traffic_<workload>.txt: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) of the dominant kernel family, each scaled by the ratio of the
+    known bytes of the copy probe to what the same counter read for it."""
+    fetch = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_dir, "WRITE_SIZE")
+    copy_bytes = copy_mib * 2 ** 20
+
+    def pick(tab, pred):
+        return [v for name, v in tab.values() if pred(name)]
+
+    cf = pick(fetch, lambda n: COPY_KERNEL_TAG in n)
+    cw = pick(write, lambda n: COPY_KERNEL_TAG in n)
+    if not cf or not cw:
+        raise SystemExit("no copy-probe dispatch in the counter runs")
+    sf, sw = copy_bytes / (cf[0] * 1024), copy_bytes / (cw[0] * 1024)
+    tag = FAMILY_KERNELS[family]
+    kf = pick(fetch, lambda n: tag in n)
+    kw = pick(write, lambda n: tag in n)
+    if not kf or len(kf) != len(kw):
+        raise SystemExit(f"no dispatches of {family} ({tag}) in the counter runs")
+    f_kib, w_kib = float(np.mean(kf)), float(np.mean(kw))
+    traffic = (f_kib * sf + w_kib * sw) * 1024
+    lines = [
+        f"# HBM traffic of the dominant kernel ({family}) in the {workload} step, from rocprofv3 counters",
+        "# made by:",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o run -- python bench.py "
+        f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --copy-probe-mib {copy_mib}",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o run -- python bench.py "
+        f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --copy-probe-mib {copy_mib}",
+        f"#   python {' '.join(argv)}",
+        f"# copy probe: {copy_mib} MiB read + {copy_mib} MiB written; counters read "
+        f"{cf[0]:.0f} KiB fetched, {cw[0]:.0f} KiB written -> scale fetch {sf:.4f}, write {sw:.4f}",
+        f"# {len(kf)} dispatches of {tag}; per dispatch: FETCH_SIZE {f_kib:.0f} KiB, WRITE_SIZE {w_kib:.0f} KiB",
+        f"kernel: {family}",
+        f"workload: {workload}",
+        f"source_sha256: {kernel_source_hash()}",
+        f"fetch_kib_per_launch: {f_kib:.1f}",
+        f"write_kib_per_launch: {w_kib:.1f}",
+        f"copy_scale_fetch: {sf:.5f}",
+        f"copy_scale_write: {sw:.5f}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+    ]
+    os.makedirs(os.path.dirname(traffic_path(workload)), exist_ok=True)
+    with open(traffic_path(workload), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# timing family -> substring of its kernel's symbol name
+FAMILY_KERNELS = {
+    "cgemm_dw_f32": "cgemm_f32_kernel<false, false, false>",
+    "cgemm_fwd_f32": "cgemm_f32_kernel<true, true, true>",
+    "cgemm_dx_f32": "cgemm_f32_kernel<true, false, true>",
+    "gemm_nt_bf16": "gemm_bf16_kernel",
+}
+
+
+def roofline(timing, dtype, workload):
     """Dominant kernel family by total time, with its achieved rate against the peak."""
     fam, t = max(timing.items(), key=lambda kv: kv[1]["total_ms"])
     per_launch_ms = t["total_ms"] / t["launches"]
@@ -138,14 +253,14 @@ def roofline(timing, dtype):
         achieved = t["flops"] / t["launches"] / (per_launch_ms * 1e-3) / 1e12
         peak = MFMA_PEAK_TFLOPS["bf16" if "bf16" in fam else "f32"]
         r = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
-                 frac=round(achieved / peak, 4), traffic=None)
+                 frac=round(achieved / peak, 4), traffic=read_traffic(workload, fam))
         if fam.startswith("cgemm"):
             # the complex products run as three real GEMMs: 3/4 of the algorithmic FLOPs execute
             r["executed_frac"] = round(0.75 * achieved / peak, 4)
         return fam, r
     achieved = t["bytes"] / t["launches"] / (per_launch_ms * 1e-3) / 1e9
     return fam, dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
+                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=read_traffic(workload, fam))
 
 
 def cpu_baseline(wl, rows_n):
@@ -188,6 +303,21 @@ def cpu_baseline(wl, rows_n):
     return dict(value=round(E / dt, 2), unit="edges/s", cores=int(threads), kind="oracle",
                 sample=f"{len(rows)} destination rows ({E} edges) of the same structure, fp64 numpy, "
                        f"{dt:.1f} s")
+
+
+def copy_bandwidth(torch, dev, mib):
+    """Measured HBM rate of a plain elementwise copy (y = -x, float32, `mib` MiB
+    read and written), GB/s counting both directions; a practical ceiling beside
+    the 8 TB/s peak."""
+    n = mib * 2 ** 20 // 4
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    ms = _median_ms(torch, lambda: torch.neg(x, out=y), 2, 10)
+    del x, y
+    torch.cuda.empty_cache()
+    return round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)
 
 
 def _median_ms(torch, fn, warmup, reps):
@@ -242,6 +372,11 @@ def sweep(dev, warmup, reps):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        fam = os.environ.get("EGNN_TRAFFIC_KERNEL", "cgemm_dw_f32")
+        summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.workload,
+                          args.copy_probe_mib, fam, sys.argv)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is not built",
               file=sys.stderr)
@@ -256,6 +391,7 @@ def main():
         return
     wl = WORKLOADS[args.workload]
     step = Step(wl, dev)
+    copy_gbs = copy_bandwidth(torch, dev, args.copy_probe_mib)
     eg = step.eg
     for _ in range(args.warmup):
         step()
@@ -274,9 +410,13 @@ def main():
     E = step.E
     cfg = step.cfg
     dtype = "bf16" if cfg.storage == "bf16" else "f32"
-    fam, roof = roofline(timing, dtype)
-    kernels = {k: dict(launches_per_step=v["launches"] / args.steps, ms_per_step=round(v["total_ms"] / args.steps, 4))
-               for k, v in sorted(timing.items(), key=lambda kv: -kv[1]["total_ms"])}
+    fam, roof = roofline(timing, dtype, args.workload)
+    kernels = {}
+    for k, v in sorted(timing.items(), key=lambda kv: -kv[1]["total_ms"]):
+        sec = v["total_ms"] * 1e-3
+        kernels[k] = dict(launches_per_step=v["launches"] / args.steps, ms_per_step=round(v["total_ms"] / args.steps, 4),
+                          tflops=round(v["flops"] / sec / 1e12, 2) if v["flops"] > 0 else None,
+                          algorithmic_gbs=round(v["bytes"] / sec / 1e9, 1) if v["bytes"] > 0 else None)
     out = {
         "metric": "edges/s per SO(2) message-passing layer (fwd+bwd) + % of HBM/MFMA roofline",
         "value": round(E * wl["layers"] * args.steps / (t1 - t0), 1),
@@ -296,6 +436,7 @@ def main():
                    "nodes_per_s": round(step.struct.n_dst * wl["layers"] * args.steps / (t1 - t0), 1),
                    "ms_per_layer": round(ms / wl["layers"], 3)},
         "roofline": dict(kernel=fam, **roof),
+        "hbm_copy_gbs": copy_gbs,
         "kernels": kernels,
         "timing_events_dropped": dropped,
     }

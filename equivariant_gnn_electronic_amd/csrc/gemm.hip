@@ -25,21 +25,39 @@ constexpr int PAD = 4;  // LDS row padding (floats)
 constexpr int kXcd = 8;
 
 struct TileMap {
-  int mt, nt;
+  int mt, nt, z;
   bool valid;
 };
 
-// Workgroup b runs on XCD b % 8.  Give XCD x the contiguous tile range
-// [x*per, (x+1)*per) in (m-major, n-minor) order.
-__device__ inline TileMap map_tile(int b, int tiles_m, int tiles_n) {
+// Workgroup b runs on XCD b % 8.  Without split-K, XCD x gets the contiguous
+// tile range [x*per, (x+1)*per) in (m-major, n-minor) order, so the n-tiles of
+// one m-tile share that XCD's L2.  With split-K, every tile of split z runs on
+// XCD z % 8: the tiles of one split read the same K-range of both operands,
+// which then comes from HBM once instead of once per tile.
+__device__ inline TileMap map_tile(int b, int tiles_m, int tiles_n, int splits) {
   const int total = tiles_m * tiles_n;
-  const int per = (total + kXcd - 1) / kXcd;
-  const int t = (b % kXcd) * per + b / kXcd;
+  const int x = b % kXcd, i = b / kXcd;
   TileMap r;
-  r.valid = t < total;
+  int t;
+  if (splits == 1) {
+    const int per = (total + kXcd - 1) / kXcd;
+    t = x * per + i;
+    r.z = 0;
+    r.valid = t < total;
+  } else {
+    t = i % total;
+    r.z = x + kXcd * (i / total);
+    r.valid = r.z < splits;
+  }
   r.mt = r.valid ? t / tiles_n : 0;
   r.nt = r.valid ? t % tiles_n : 0;
   return r;
+}
+
+// Grid size matching map_tile.
+inline int tile_grid(int tiles, int splits) {
+  if (splits == 1) return (tiles + kXcd - 1) / kXcd * kXcd;
+  return (splits + kXcd - 1) / kXcd * kXcd * tiles;
 }
 
 // Load one BKxBM (or BKxBN) operand tile into registers: 2 float4 per thread.
@@ -91,13 +109,13 @@ __device__ inline void store_tile(float *S, const f32x4 (&r)[2]) {
 template <bool AK, bool BK_>
 __global__ void __launch_bounds__(256, 2) gemm_f32_kernel(int M, int N, int K, const float *__restrict__ A, int lda,
                                                           const float *__restrict__ B, int ldb, float *__restrict__ C,
-                                                          int ldc, int k_per_split, int64_t split_stride) {
+                                                          int ldc, int splits, int k_per_split, int64_t split_stride) {
   __shared__ float As[2][BK * (BM + PAD)];
   __shared__ float Bs[2][BK * (BN + PAD)];
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n);
+  const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n, splits);
   if (!tm.valid) return;
-  const int z = blockIdx.y;
+  const int z = tm.z;
   const int k_begin = z * k_per_split;
   const int k_end = min(K, k_begin + k_per_split);
   C += z * split_stride;
@@ -223,14 +241,14 @@ __global__ void __launch_bounds__(256, 2) cgemm_f32_kernel(int M, int N, int K, 
                                                            const float *__restrict__ V1, const float *__restrict__ V2,
                                                            const float *__restrict__ V3, int ldv, float vsign,
                                                            float *__restrict__ Cre, float *__restrict__ Cim, int ldc,
-                                                           int k_per_split, int64_t split_stride) {
+                                                           int splits, int k_per_split, int64_t split_stride) {
   constexpr int LT = CBK * (BM + PAD);
   __shared__ float Us[2][3][LT];
   __shared__ float Vs[2][3][LT];
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n);
+  const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n, splits);
   if (!tm.valid) return;
-  const int z = blockIdx.y;
+  const int z = tm.z;
   const int k_begin = z * k_per_split;
   const int k_end = min(K, k_begin + k_per_split);
   Cre += z * split_stride;
@@ -345,7 +363,7 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(int M, int N, int K, 
   __shared__ uint16_t As[2][HBM_ * HLD];
   __shared__ uint16_t Bs[2][HBN * HLD];
   const int tiles_m = (M + HBM_ - 1) / HBM_, tiles_n = (N + HBN - 1) / HBN;
-  const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n);
+  const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n, 1);
   if (!tm.valid) return;
   const int row0 = tm.mt * HBM_, col0 = tm.nt * HBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -428,16 +446,15 @@ hipError_t gemm_f32(int M, int N, int K, const float *A, int lda, bool a_kcontig
   int kps = (K + splits - 1) / splits;
   kps = (kps + BK - 1) / BK * BK;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const int per = (tiles + kXcd - 1) / kXcd;
-  dim3 grid(per * kXcd, splits);
+  const int grid = tile_grid(tiles, splits);
   if (a_kcontig && b_kcontig)
-    gemm_f32_kernel<true, true><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, kps, split_stride);
+    gemm_f32_kernel<true, true><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
   else if (!a_kcontig && !b_kcontig)
-    gemm_f32_kernel<false, false><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, kps, split_stride);
+    gemm_f32_kernel<false, false><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
   else if (a_kcontig)
-    gemm_f32_kernel<true, false><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, kps, split_stride);
+    gemm_f32_kernel<true, false><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
   else
-    gemm_f32_kernel<false, true><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, kps, split_stride);
+    gemm_f32_kernel<false, true><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
   return hipGetLastError();
 }
 
@@ -449,12 +466,11 @@ hipError_t cgemm_f32(int M, int N, int K, const float *Up, const float *Um, int 
   int kps = (K + splits - 1) / splits;
   kps = (kps + CBK - 1) / CBK * CBK;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const int per = (tiles + kXcd - 1) / kXcd;
-  dim3 grid(per * kXcd, splits);
+  const int grid = tile_grid(tiles, splits);
   const bool pre = V3 != nullptr;
 #define EGNN_CG(UKc, VKc, PREc)                                                                           \
   cgemm_f32_kernel<UKc, VKc, PREc><<<grid, 256, 0, stream>>>(M, N, K, Up, Um, ldu, V1, V2, V3, ldv, vsign, Cre, Cim, \
-                                                            ldc, kps, split_stride)
+                                                            ldc, splits, kps, split_stride)
   if (u_kcontig && v_kcontig && pre) EGNN_CG(true, true, true);
   else if (u_kcontig && !v_kcontig && pre) EGNN_CG(true, false, true);
   else if (!u_kcontig && !v_kcontig && !pre) EGNN_CG(false, false, false);
@@ -468,11 +484,11 @@ hipError_t gemm_bf16_nt(int M, int N, int K, const uint16_t *A, int lda, const u
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0) return hipErrorInvalidValue;
   const int tiles = ((M + HBM_ - 1) / HBM_) * ((N + HBN - 1) / HBN);
-  const int per = (tiles + kXcd - 1) / kXcd;
+  const int grid = tile_grid(tiles, 1);
   if (c_bf16)
-    gemm_bf16_kernel<true><<<per * kXcd, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+    gemm_bf16_kernel<true><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
   else
-    gemm_bf16_kernel<false><<<per * kXcd, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+    gemm_bf16_kernel<false><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
   return hipGetLastError();
 }
 

@@ -250,8 +250,6 @@ __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restr
   }
 }
 
-// logits a_e = sum_c w_att[c] SiLU(Y0[e][c]) and the row softmax (one wave per row,
-// one edge per lane, online max/sum over chunks of 64 edges)
 // Logits and softmax over one destination row per wave.  Sixteen lanes share
 // an edge (16-byte loads of its invariant output plane, reduced with four
 // butterfly steps), so four edges are read per pass with coalesced rows.
@@ -744,10 +742,13 @@ FwdWs carve_fwd_ws(Carver &cv, const LayerShape &s, int64_t E) {
   return w;
 }
 
+// Split-K count of the weight-gradient GEMMs (K = edges); a multiple of 8
+// from 8 up, so each XCD takes the same number of splits.
 int dw_splits(int64_t E) {
   int64_t s = E / 8192;
   if (s < 1) s = 1;
   if (s > 64) s = 64;
+  if (s >= 8) s = s / 8 * 8;
   return static_cast<int>(s);
 }
 
