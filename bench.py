@@ -160,15 +160,16 @@ def traffic_path(workload):
 
 def read_traffic(workload, family):
     """HBM bytes per launch of `family` from the committed counter summary, or None
-    when there is none, it covers another kernel, or the sources changed since."""
+    when there is none, it does not cover that kernel, or the sources changed since."""
     try:
         with open(traffic_path(workload)) as fh:
             kv = dict(line.split(": ", 1) for line in fh.read().splitlines() if ": " in line and not line.startswith("#"))
     except OSError:
         return None
-    if kv.get("kernel") != family or kv.get("source_sha256") != kernel_source_hash():
+    key = f"traffic_bytes_per_launch[{family}]"
+    if key not in kv or kv.get("source_sha256") != kernel_source_hash():
         return None
-    return float(kv["traffic_bytes_per_launch"])
+    return float(kv[key])
 
 
 def _pmc_per_dispatch(d, counter):
@@ -187,49 +188,44 @@ def _pmc_per_dispatch(d, counter):
     return out
 
 
-def summarize_traffic(fetch_dir, write_dir, workload, copy_mib, family, argv):
+def summarize_traffic(fetch_dir, write_dir, workload, copy_mib, argv):
     """Write profiles/traffic_<workload>.txt: FETCH_SIZE and WRITE_SIZE (KiB per
-    dispatch) of the dominant kernel family, each scaled by the ratio of the
-    known bytes of the copy probe to what the same counter read for it."""
+    dispatch) of each kernel family below, each scaled by the ratio of the known
+    bytes of the copy probe to what the same counter read for it."""
     fetch = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = _pmc_per_dispatch(write_dir, "WRITE_SIZE")
     copy_bytes = copy_mib * 2 ** 20
 
-    def pick(tab, pred):
-        return [v for name, v in tab.values() if pred(name)]
+    def pick(tab, tag):
+        return [v for name, v in tab.values() if tag in name]
 
-    cf = pick(fetch, lambda n: COPY_KERNEL_TAG in n)
-    cw = pick(write, lambda n: COPY_KERNEL_TAG in n)
+    cf, cw = pick(fetch, COPY_KERNEL_TAG), pick(write, COPY_KERNEL_TAG)
     if not cf or not cw:
         raise SystemExit("no copy-probe dispatch in the counter runs")
     sf, sw = copy_bytes / (cf[0] * 1024), copy_bytes / (cw[0] * 1024)
-    tag = FAMILY_KERNELS[family]
-    kf = pick(fetch, lambda n: tag in n)
-    kw = pick(write, lambda n: tag in n)
-    if not kf or len(kf) != len(kw):
-        raise SystemExit(f"no dispatches of {family} ({tag}) in the counter runs")
-    f_kib, w_kib = float(np.mean(kf)), float(np.mean(kw))
-    traffic = (f_kib * sf + w_kib * sw) * 1024
+    cmd = (f"python bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline "
+           f"--copy-probe-mib {copy_mib}")
     lines = [
-        f"# HBM traffic of the dominant kernel ({family}) in the {workload} step, from rocprofv3 counters",
-        "# made by:",
-        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o run -- python bench.py "
-        f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --copy-probe-mib {copy_mib}",
-        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o run -- python bench.py "
-        f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --copy-probe-mib {copy_mib}",
+        f"# HBM traffic per launch of the main kernels of the {workload} step, from rocprofv3 counters",
+        "# made by (from the repository root, on one MI355X):",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o run -- {cmd}",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o run -- {cmd}",
         f"#   python {' '.join(argv)}",
-        f"# copy probe: {copy_mib} MiB read + {copy_mib} MiB written; counters read "
+        f"# copy probe (y = -x, float32): {copy_mib} MiB read + {copy_mib} MiB written; the counters read "
         f"{cf[0]:.0f} KiB fetched, {cw[0]:.0f} KiB written -> scale fetch {sf:.4f}, write {sw:.4f}",
-        f"# {len(kf)} dispatches of {tag}; per dispatch: FETCH_SIZE {f_kib:.0f} KiB, WRITE_SIZE {w_kib:.0f} KiB",
-        f"kernel: {family}",
         f"workload: {workload}",
         f"source_sha256: {kernel_source_hash()}",
-        f"fetch_kib_per_launch: {f_kib:.1f}",
-        f"write_kib_per_launch: {w_kib:.1f}",
         f"copy_scale_fetch: {sf:.5f}",
         f"copy_scale_write: {sw:.5f}",
-        f"traffic_bytes_per_launch: {traffic:.0f}",
     ]
+    for fam, tag in FAMILY_KERNELS.items():
+        kf, kw = pick(fetch, tag), pick(write, tag)
+        if not kf or len(kf) != len(kw):
+            continue
+        f_kib, w_kib = float(np.mean(kf)), float(np.mean(kw))
+        lines.append(f"# {fam}: {len(kf)} dispatches of {tag}; per dispatch FETCH_SIZE {f_kib:.0f} KiB, "
+                     f"WRITE_SIZE {w_kib:.0f} KiB")
+        lines.append(f"traffic_bytes_per_launch[{fam}]: {(f_kib * sf + w_kib * sw) * 1024:.0f}")
     os.makedirs(os.path.dirname(traffic_path(workload)), exist_ok=True)
     with open(traffic_path(workload), "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -241,7 +237,13 @@ FAMILY_KERNELS = {
     "cgemm_dw_f32": "cgemm_f32_kernel<false, false, false>",
     "cgemm_fwd_f32": "cgemm_f32_kernel<true, true, true>",
     "cgemm_dx_f32": "cgemm_f32_kernel<true, false, true>",
+    "gemm_tn_f32": "gemm_f32_kernel<false, false>",
+    "gemm_nt_f32": "gemm_f32_kernel<true, true>",
+    "gemm_nn_f32": "gemm_f32_kernel<true, false>",
     "gemm_nt_bf16": "gemm_bf16_kernel",
+    "rotate_in": "scatter_in_kernel",
+    "aggregate": "aggregate_kernel",
+    "hblocks": "hblocks_kernel",
 }
 
 
@@ -373,9 +375,8 @@ def sweep(dev, warmup, reps):
 def main():
     args = parse()
     if args.summarize_traffic:
-        fam = os.environ.get("EGNN_TRAFFIC_KERNEL", "cgemm_dw_f32")
         summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.workload,
-                          args.copy_probe_mib, fam, sys.argv)
+                          args.copy_probe_mib, sys.argv)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is not built",
