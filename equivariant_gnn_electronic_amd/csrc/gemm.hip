@@ -14,6 +14,8 @@
 // XCD's L2.
 #include "gemm.h"
 
+#include <type_traits>
+
 namespace egnn {
 namespace {
 
@@ -437,6 +439,177 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(int M, int N, int K, 
     }
 }
 
+// bf16, large tiles, operands brought into LDS by the gfx950 direct loads
+// (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS
+// base + 16 * lane, with no register staging).  S stages form a ring, so
+// S - 1 K-tiles are in flight while one is multiplied; every stage is its
+// own LDS object, which lets the compiler's wait-count pass see that reads
+// of one stage do not depend on the loads still filling the others.  A
+// wave's 1 KB of each load covers whole rows of the tile, so rows cannot be
+// padded; instead the 16-byte chunks of a row are XOR-swizzled by the row
+// index, which makes the 32-row fragment reads conflict-free.
+// Requires K % BK == 0, lda and ldb multiples of 8, 16-byte aligned bases.
+template <int I, int N, typename F>
+__device__ inline void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// vmcnt(n), other counters left alone
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without the release fence of __syncthreads (the fence
+// would wait for every outstanding direct load).  Each wave waits for its
+// own loads with wait_vmcnt before arriving; the empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ inline void barrier_no_fence() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+template <int CPR>
+__device__ inline int chunk_swizzle(int row) {
+  static_assert(CPR == 4 || CPR == 8, "32 or 64 bf16 per row");
+  return CPR == 4 ? ((row >> 2) & 3) : ((row >> 1) & 7);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int S, bool CBF16>
+__global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, int N, int K,
+                                                                      const uint16_t *__restrict__ A, int lda,
+                                                                      const uint16_t *__restrict__ B, int ldb,
+                                                                      void *__restrict__ C, int ldc) {
+  constexpr int NW = WM * WN, CPR = BK / 8;
+  static_assert(S >= 2 && S <= 4, "stages");
+  __shared__ uint16_t A0[BM * BK], A1[BM * BK], A2[S > 2 ? BM * BK : 8], A3[S > 3 ? BM * BK : 8];
+  __shared__ uint16_t B0[BN * BK], B1[BN * BK], B2[S > 2 ? BN * BK : 8], B3[S > 3 ? BN * BK : 8];
+  auto as = [&](auto st) -> uint16_t * {
+    if constexpr (decltype(st)::value == 0) return A0;
+    else if constexpr (decltype(st)::value == 1) return A1;
+    else if constexpr (decltype(st)::value == 2) return A2;
+    else return A3;
+  };
+  auto bs = [&](auto st) -> uint16_t * {
+    if constexpr (decltype(st)::value == 0) return B0;
+    else if constexpr (decltype(st)::value == 1) return B1;
+    else if constexpr (decltype(st)::value == 2) return B2;
+    else return B3;
+  };
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n, 1);
+  if (!tm.valid) return;
+  const int row0 = tm.mt * BM, col0 = tm.nt * BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+  const int wm = (wave / WN) * WTM, wn = (wave % WN) * WTN;
+  const int fr = lane & 31, fh = lane >> 5;
+  // direct loads: the A tile is BM * CPR chunks = BM * CPR / 64 wave loads, spread over the waves
+  constexpr int LA = BM * CPR / 64 / NW, LB = BN * CPR / 64 / NW;
+  static_assert(LA >= 1 && LB >= 1 && (BM * CPR) % (64 * NW) == 0 && (BN * CPR) % (64 * NW) == 0, "tile");
+  const uint16_t *ga[LA];
+  const uint16_t *gb[LB];
+  int la[LA], lb[LB];
+#pragma unroll
+  for (int h = 0; h < LA; ++h) {
+    const int slot0 = (h * NW + wave) * 64, sl = slot0 + lane, r = sl / CPR;
+    ga[h] = A + static_cast<int64_t>(min(row0 + r, M - 1)) * lda + ((sl % CPR) ^ chunk_swizzle<CPR>(r)) * 8;
+    la[h] = slot0 * 8;
+  }
+#pragma unroll
+  for (int h = 0; h < LB; ++h) {
+    const int slot0 = (h * NW + wave) * 64, sl = slot0 + lane, r = sl / CPR;
+    gb[h] = B + static_cast<int64_t>(min(col0 + r, N - 1)) * ldb + ((sl % CPR) ^ chunk_swizzle<CPR>(r)) * 8;
+    lb[h] = slot0 * 8;
+  }
+  auto issue = [&](auto st, int kt) {
+#pragma unroll
+    for (int h = 0; h < LA; ++h)
+      __builtin_amdgcn_global_load_lds(static_cast<const void *>(ga[h] + static_cast<int64_t>(kt) * BK),
+                                       static_cast<void *>(as(st) + la[h]), 16, 0, 0);
+#pragma unroll
+    for (int h = 0; h < LB; ++h)
+      __builtin_amdgcn_global_load_lds(static_cast<const void *>(gb[h] + static_cast<int64_t>(kt) * BK),
+                                       static_cast<void *>(bs(st) + lb[h]), 16, 0, 0);
+  };
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto compute = [&](auto st) {
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      bf16x8 a[TM], b[TN];
+      const int c = s * 2 + fh;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm + 32 * i + fr;
+        a[i] = *reinterpret_cast<const bf16x8 *>(as(st) + r * BK + (c ^ chunk_swizzle<CPR>(r)) * 8);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn + 32 * j + fr;
+        b[j] = *reinterpret_cast<const bf16x8 *>(bs(st) + r * BK + (c ^ chunk_swizzle<CPR>(r)) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  constexpr int L = LA + LB;  // direct loads per K-tile per wave
+  const int nk = K / BK;
+  // prologue: K-tiles 0 .. S-2 in flight, wait for tile 0
+  static_for<0, S - 1>([&](auto st) {
+    if (decltype(st)::value < nk) issue(st, decltype(st)::value);
+  });
+  if (nk >= S - 1) wait_vmcnt<(S - 2) * L>();
+  else wait_vmcnt<0>();
+  barrier_no_fence();
+  // iteration i multiplies stage i % S, then refills the stage of tile i - 1
+  // (free since the last barrier) with tile i + S - 1, then waits for tile i + 1
+  for (int it = 0; it < nk; it += S) {
+    static_for<0, S>([&](auto d) {
+      constexpr int dd = decltype(d)::value;
+      const int i = it + dd;
+      if (i >= nk) return;
+      compute(d);
+      if (i + S - 1 < nk) {
+        issue(std::integral_constant<int, (dd + S - 1) % S>{}, i + S - 1);
+        wait_vmcnt<(S - 2) * L>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      barrier_no_fence();
+    });
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = col0 + wn + 32 * j + fr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + wm + 32 * i + 8 * (r >> 2) + 4 * fh + (r & 3);
+        if (row >= M) continue;
+        const int64_t o = static_cast<int64_t>(row) * ldc + col;
+        if (CBF16)
+          static_cast<uint16_t *>(C)[o] = f32_to_bf16(acc[i][j][r]);
+        else
+          static_cast<float *>(C)[o] = acc[i][j][r];
+      }
+    }
+}
+
 }  // namespace
 
 hipError_t gemm_f32(int M, int N, int K, const float *A, int lda, bool a_kcontig, const float *B, int ldb,
@@ -483,12 +656,31 @@ hipError_t gemm_bf16_nt(int M, int N, int K, const uint16_t *A, int lda, const u
                         bool c_bf16, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0) return hipErrorInvalidValue;
-  const int tiles = ((M + HBM_ - 1) / HBM_) * ((N + HBN - 1) / HBN);
-  const int grid = tile_grid(tiles, 1);
-  if (c_bf16)
-    gemm_bf16_kernel<true><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
-  else
-    gemm_bf16_kernel<false><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+  const bool aligned = (reinterpret_cast<uintptr_t>(A) % 16 == 0) && (reinterpret_cast<uintptr_t>(B) % 16 == 0);
+  const int waste256 = (N + 255) / 256 * 256 - N, waste128 = (N + 127) / 128 * 128 - N;
+  const int tiles_m = (M + 255) / 256;
+  if (aligned && K % 64 == 0 && (waste128 < waste256 || K % 32 != 0)) {
+    // 256 x 128 x 64, 8 waves (4 x 2, 64 x 64 each), 3 stages (144 KB LDS)
+    const int grid = tile_grid(tiles_m * ((N + 127) / 128), 1);
+    if (c_bf16)
+      gemm_bf16_lds_kernel<256, 128, 64, 4, 2, 3, true><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+    else
+      gemm_bf16_lds_kernel<256, 128, 64, 4, 2, 3, false><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+  } else if (aligned && K % 32 == 0) {
+    // 256 x 256 x 32, 8 waves (2 x 4, 128 x 64 each), 4 stages (128 KB LDS)
+    const int grid = tile_grid(tiles_m * ((N + 255) / 256), 1);
+    if (c_bf16)
+      gemm_bf16_lds_kernel<256, 256, 32, 2, 4, 4, true><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+    else
+      gemm_bf16_lds_kernel<256, 256, 32, 2, 4, 4, false><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+  } else {
+    const int tiles = ((M + HBM_ - 1) / HBM_) * ((N + HBN - 1) / HBN);
+    const int grid = tile_grid(tiles, 1);
+    if (c_bf16)
+      gemm_bf16_kernel<true><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+    else
+      gemm_bf16_kernel<false><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+  }
   return hipGetLastError();
 }
 
