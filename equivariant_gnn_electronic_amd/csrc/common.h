@@ -45,10 +45,17 @@ void clear_error();
 __host__ __device__ inline float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
+// Round to nearest even.  On the device the conversion compiles to the gfx950
+// v_cvt_pk_bf16_f32 instruction; the host version is the same rounding on
+// the bits (finite values).
 __host__ __device__ inline uint16_t f32_to_bf16(float f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+#else
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
+#endif
 }
 
 template <typename T> struct Store;

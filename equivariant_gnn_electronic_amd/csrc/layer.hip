@@ -226,11 +226,18 @@ __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restr
       for (int p = 0; p < L::NP; ++p) g[p] = 0.0f;
 #pragma unroll
       for (int k = 0; k < NRBF; ++k) {
-        const float ph = k < n_rbf ? gr[L::ND + k] : 0.0f;
+        // unconditional LDS read, then select: no branch per basis function
+        const float raw = gr[L::ND + k];
+        const float ph = k < n_rbf ? raw : 0.0f;
 #pragma unroll
         for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[k][p];
       }
       if (!active) continue;
+      // wave-uniform row pointers; the lane offsets below stay 32-bit
+      TA *rowp[MMAX + 1];
+#pragma unroll
+      for (int mu = 0; mu <= MMAX; ++mu)
+        rowp[mu] = static_cast<TA *>(A.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
 #pragma unroll
       for (int l = 0; l <= LMAX; ++l) {
 #pragma unroll
@@ -239,10 +246,7 @@ __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restr
 #pragma unroll
           for (int mp = -l; mp <= l; ++mp) v += gr[L::doff(l, m, mp)] * xv[l * l + l + mp];
           v *= g[pair_index(cabs(m), l, LMAX)];
-          const int mu = cabs(m);
-          TA *Am = static_cast<TA *>(A.p[mu]);
-          const int64_t width = static_cast<int64_t>(L::blocks(mu)) * C2;
-          Store<TA>::st(Am + static_cast<int64_t>(e) * width + L::col(l, m) * C2 + j, v);
+          Store<TA>::st(rowp[cabs(m)] + static_cast<uint32_t>(L::col(l, m) * C2 + j), v);
         }
       }
     }
