@@ -452,7 +452,8 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
           for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
             const int mu = cabs(m);
             const float *row = static_cast<const float *>(Y.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
-            p += row[L::col(l, m) * C + cl[t]] * T[L::kidx(l, m)];  // gd is 0 on clamped lanes, so T is too
+            // gd is 0 on clamped lanes, so T is too
+            p += row[static_cast<uint32_t>(L::col(l, m) * C + cl[t])] * T[L::kidx(l, m)];
           }
       }
       p = wave_sum(p);
@@ -490,7 +491,7 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
             }
             const int mu = cabs(m);
             float *row = static_cast<float *>(dY.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
-            if (c < C) row[L::col(l, m) * C + c] = v;
+            if (c < C) row[static_cast<uint32_t>(L::col(l, m) * C + c)] = v;
           }
       }
     }
@@ -554,6 +555,10 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
 #pragma unroll
         for (int p = 0; p < L::NP; ++p) dg[p] = 0.0f;
         if (active) {
+          const float *rowp[MMAX + 1];  // wave-uniform row bases, 32-bit lane offsets
+#pragma unroll
+          for (int mu = 0; mu <= MMAX; ++mu)
+            rowp[mu] = static_cast<const float *>(dA.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
 #pragma unroll
           for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
@@ -561,15 +566,14 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
               float xt = 0.0f;
 #pragma unroll
               for (int mp = -l; mp <= l; ++mp) xt += gr[L::doff(l, m, mp)] * xv[l * l + l + mp];
-              const int mu = cabs(m);
-              const float dx = static_cast<const float *>(dA.p[mu])[static_cast<int64_t>(e) * L::blocks(mu) * C2 +
-                                                                    L::col(l, m) * C2 + j];
-              dg[pair_index(mu, l, LMAX)] += dx * xt;
+              const float dx = rowp[cabs(m)][static_cast<uint32_t>(L::col(l, m) * C2 + j)];
+              dg[pair_index(cabs(m), l, LMAX)] += dx * xt;
             }
         }
 #pragma unroll
         for (int k = 0; k < NRBF; ++k) {
-          const float ph = k < n_rbf ? gr[L::ND + k] : 0.0f;
+          const float raw = gr[L::ND + k];  // in the staged row; select, no branch
+          const float ph = k < n_rbf ? raw : 0.0f;
 #pragma unroll
           for (int p = 0; p < L::NP; ++p) acc[k][p] += ph * dg[p];
         }
@@ -627,21 +631,23 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
         const int e = uniform(eids[wave][i]);
         const float *gr = gb + i * GS4 * 4;
         if (!active) continue;
+        const float *rowp[MMAX + 1];  // wave-uniform row bases, 32-bit lane offsets
+#pragma unroll
+        for (int mu = 0; mu <= MMAX; ++mu)
+          rowp[mu] = static_cast<const float *>(dA.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
         float dxt[L::KEPT];
 #pragma unroll
         for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
-          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
-            const int mu = cabs(m);
-            dxt[L::kidx(l, m)] = static_cast<const float *>(dA.p[mu])[static_cast<int64_t>(e) * L::blocks(mu) * C2 +
-                                                                      L::col(l, m) * C2 + j];
-          }
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
+            dxt[L::kidx(l, m)] = rowp[cabs(m)][static_cast<uint32_t>(L::col(l, m) * C2 + j)];
         float g[L::NP];
 #pragma unroll
         for (int p = 0; p < L::NP; ++p) g[p] = 0.0f;
 #pragma unroll
         for (int k = 0; k < NRBF; ++k) {
-          const float ph = k < n_rbf ? gr[L::ND + k] : 0.0f;
+          const float raw = gr[L::ND + k];  // in the staged row; select, no branch
+          const float ph = k < n_rbf ? raw : 0.0f;
 #pragma unroll
           for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[k][p];
         }
@@ -1205,8 +1211,9 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
     }
     const int ncol = s.n_pairs * 2 * s.C;
     {
+      // dA read once; the edge-frame input is recomputed from each node's own row
       const double bytes = double(g->n_src) * s.K * s.C * 4.0 + double(E) * (s.nD + s.n_rbf + 1) * 4.0 + double(E) * 4.0 +
-                           2.0 * double(E) * sumK * 4.0;
+                           double(E) * sumK * 4.0;
       Timed t(stream, "bwd_gate", 0.0, bytes);
       EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_gate_launch, g, s, geom, x, weights + wo.wrad, w, stream);
     }
