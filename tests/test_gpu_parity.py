@@ -12,6 +12,7 @@ import torch
 import synth
 from oracle import decode as odec
 from oracle import layer as olayer
+from oracle import neighbors as onb
 from oracle import so3
 from tests.helpers import assert_close, desc_of, grid_box, oracle_graph, sample_rows
 
@@ -271,3 +272,83 @@ def test_gst_stack_equivariance_full_size(dev):
     xr = synth.bf16_round(_rotate_irreps(x.astype(np.float64), Q, cfg.lmax).astype(np.float32))
     rot = _run_stack(cfg, dev, g2, geom2, torch.from_numpy(xr).to(dev).to(torch.bfloat16), ws).float().cpu().numpy()
     assert_close(rot, _rotate_irreps(base, Q, cfg.lmax), 2e-2, "rotated 3-layer output")
+
+
+def _relabelled_rows(struct, rows):
+    """Positions with `rows` moved to the front (they become destinations
+    0..len(rows)-1); every other atom stays a source, ghosts last."""
+    rest = np.setdiff1d(np.arange(struct.n_src), rows)
+    perm = np.concatenate([rows, rest])
+    return perm, onb.build_graph(struct.pos[perm], len(rows), struct.box, struct.periodic_mask, struct.r_cut)
+
+
+def test_layer_backward_hfo2_sampled_nodes(dev):
+    """Full-size training layer (544k edges, the launch the training step times):
+    dL/dx of sampled atoms against the oracle's exact gradient.  The oracle runs
+    on every row that touches a sampled atom (its own row and the rows of all
+    its outgoing edges), which holds every term of that atom's gradient."""
+    cfg = synth.CONFIGS["train"]
+    r = _gpu_forward(cfg, dev, train=True)
+    s = r["s"]
+    G = synth.make_cotangent(cfg, s.n_dst)
+    gx, _ = eg.egnn_layer_bwd(r["desc"], r["g"], r["geom"], r["wt"], r["xt"], r["buf"], torch.from_numpy(G).to(dev))
+    torch.cuda.synchronize()
+    gx = gx.cpu().numpy()
+    gg = host(r["g"])
+    dst = np.repeat(np.arange(s.n_dst), np.diff(gg["row_ptr"]))
+    nodes = sample_rows(s.n_dst, 2, 21)
+    rows = np.unique(np.concatenate([nodes, dst[np.isin(gg["src"], nodes)]]))
+    perm, og = _relabelled_rows(s, rows)
+    x64, w64 = r["x"][perm].astype(np.float64), r["w"].astype(np.float64)
+    fwd = olayer.layer_forward(og, x64, w64, desc_of(cfg))
+    dx, _ = olayer.layer_backward(og, x64, w64, desc_of(cfg), fwd, G[rows].astype(np.float64))
+    where = np.searchsorted(rows, nodes)  # sampled atoms sit at these relabelled positions
+    assert_close(gx[nodes], dx[where], 1e-4, "grad x of sampled atoms")
+
+
+def test_weight_gradient_hfo2_directional(dev):
+    """Full-size weight gradient: <dL/dW, v> against the central difference of
+    L(W) = <G, x'(W)> along a random direction v, both from the GPU forward
+    (a property that holds at any size; fp32 forward, so 1e-2)."""
+    cfg = synth.CONFIGS["train"]
+    r = _gpu_forward(cfg, dev, train=True)
+    G = synth.make_cotangent(cfg, r["s"].n_dst)
+    Gt = torch.from_numpy(G).to(dev)
+    _, gw = eg.egnn_layer_bwd(r["desc"], r["g"], r["geom"], r["wt"], r["xt"], r["buf"], Gt)
+    v = torch.from_numpy(np.random.default_rng(3).standard_normal(r["w"].size).astype(np.float32)).to(dev)
+    v *= r["wt"].norm() / v.norm()
+    eps = 1e-3
+
+    def loss(w):
+        (xo, _), _ = eg.egnn_layer_fwd(r["desc"], r["g"], r["geom"], w, r["xt"])
+        return float((xo.double() * Gt.double()).sum())
+
+    fd = (loss(r["wt"] + eps * v) - loss(r["wt"] - eps * v)) / (2 * eps)
+    an = float((gw.double() * v.double()).sum())
+    assert abs(fd - an) <= 1e-2 * abs(an), (fd, an)
+
+
+def test_hblocks_hfo2_sampled_edges(dev):
+    """Decode at full size (544k edges, 13x13 blocks): sampled edges and atoms
+    against the oracle's Label->Matrix on the same irreps."""
+    cfg = synth.CONFIGS["train"]
+    r = _gpu_forward(cfg, dev, edge_out=True)
+    we, wn = synth.make_decode_weights(cfg)
+    wet = torch.from_numpy(np.concatenate(we)).to(dev)
+    wnt = torch.from_numpy(np.concatenate(wn)).to(dev)
+    he, hn = eg.egnn_hblocks(cfg.lmax, cfg.C, wet, wnt, r["eo"], r["xo"])
+    torch.cuda.synchronize()
+    ei = sample_rows(r["g"].n_edges, 3000, 5)
+    ni = sample_rows(r["s"].n_dst, 300, 6)
+    eo = r["eo"][torch.from_numpy(ei).to(dev)].cpu().numpy().astype(np.float64)
+    xo = r["xo"][torch.from_numpy(ni).to(dev)].cpu().numpy().astype(np.float64)
+    assert_close(he[torch.from_numpy(ei).to(dev)].cpu().numpy(), odec.hblocks(eo, we), 1e-5, "edge blocks")
+    assert_close(hn[torch.from_numpy(ni).to(dev)].cpu().numpy(), odec.hblocks(xo, wn), 1e-5, "on-site blocks")
+    # the per-edge messages themselves at the sampled edges' rows
+    gg = host(r["g"])
+    rows = np.unique(np.searchsorted(gg["row_ptr"], ei, side="right") - 1)[:40]
+    og = oracle_graph(r["s"], rows=rows)
+    sel = np.concatenate([np.arange(gg["row_ptr"][q], gg["row_ptr"][q + 1]) for q in rows])
+    ef = olayer.edge_forward(og, r["x"].astype(np.float64), olayer.unpack_weights(r["w"].astype(np.float64), desc_of(cfg)),
+                             desc_of(cfg), r["x"][np.repeat(rows, np.diff(og["row_ptr"]))].astype(np.float64))
+    assert_close(r["eo"][torch.from_numpy(sel).to(dev)].cpu().numpy(), ef["msg"], 1e-4, "edge messages")
