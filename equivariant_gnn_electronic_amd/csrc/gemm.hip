@@ -22,7 +22,7 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 16;
+constexpr int BK = 16;
 constexpr int PAD = 4;  // LDS row padding (floats)
 constexpr int kXcd = 8;
 
@@ -62,119 +62,130 @@ inline int tile_grid(int tiles, int splits) {
   return (splits + kXcd - 1) / kXcd * kXcd * tiles;
 }
 
-// Load one BKxBM (or BKxBN) operand tile into registers: 2 float4 per thread.
-template <bool KCONTIG>
-__device__ inline void load_tile(const float *P, int ld, int rows, int row0, int k0, int k_end, f32x4 (&r)[2]) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int f = t + h * 256;  // float4 index within the 128x16 tile
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (KCONTIG) {
-      const int m = f >> 2, kq = f & 3;
-      const int gm = row0 + m, gk = k0 + kq * 4;
-      if (gm < rows && gk < k_end) v = *reinterpret_cast<const f32x4 *>(P + static_cast<int64_t>(gm) * ld + gk);
-    } else {
-      const int k = f >> 5, mq = f & 31;
-      const int gk = k0 + k, gm = row0 + mq * 4;
-      if (gk < k_end && gm < rows) {
-        const float *p = P + static_cast<int64_t>(gk) * ld + gm;
-        if (gm + 3 < rows) {
-          v = *reinterpret_cast<const f32x4 *>(p);
-        } else {
-          for (int j = 0; j < 4; ++j) v[j] = (gm + j < rows) ? p[j] : 0.f;
-        }
+// Operand tiles of ROWS x KT floats move through registers as float4s, NF per
+// thread of the 256-thread block (the last one guarded when the tile holds
+// fewer than 256 float4s).  In LDS they are laid out [KT][ROWS + PAD].
+template <int ROWS, int KT>
+struct TileShape {
+  static constexpr int F4 = ROWS * KT / 4;            // float4s in the tile
+  static constexpr int NF = (F4 + 255) / 256;         // per thread
+  static constexpr int LD = ROWS + PAD;               // LDS row length
+};
+
+template <bool KCONTIG, int ROWS, int KT>
+__device__ inline f32x4 load_f4(const float *P, int ld, int rows, int row0, int k0, int k_end, int f) {
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if (f >= TileShape<ROWS, KT>::F4) return v;
+  if (KCONTIG) {
+    const int m = f / (KT / 4), kq = f % (KT / 4);
+    const int gm = row0 + m, gk = k0 + kq * 4;
+    if (gm < rows && gk < k_end) v = *reinterpret_cast<const f32x4 *>(P + static_cast<int64_t>(gm) * ld + gk);
+  } else {
+    const int k = f / (ROWS / 4), mq = f % (ROWS / 4);
+    const int gk = k0 + k, gm = row0 + mq * 4;
+    if (gk < k_end && gm < rows) {
+      const float *p = P + static_cast<int64_t>(gk) * ld + gm;
+      if (gm + 3 < rows) {
+        v = *reinterpret_cast<const f32x4 *>(p);
+      } else {
+        for (int j = 0; j < 4; ++j) v[j] = (gm + j < rows) ? p[j] : 0.f;
       }
     }
-    r[h] = v;
+  }
+  return v;
+}
+
+template <bool KCONTIG, int ROWS, int KT>
+__device__ inline void store_f4(float *S, const f32x4 &v, int f) {
+  using TS = TileShape<ROWS, KT>;
+  if (f >= TS::F4) return;
+  if (KCONTIG) {
+    const int m = f / (KT / 4), kq = f % (KT / 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) S[(kq * 4 + j) * TS::LD + m] = v[j];
+  } else {
+    const int k = f / (ROWS / 4), mq = f % (ROWS / 4);
+    *reinterpret_cast<f32x4 *>(S + k * TS::LD + mq * 4) = v;
   }
 }
 
-// Store the register tile into LDS laid out [BK][BM + PAD].
-template <bool KCONTIG>
-__device__ inline void store_tile(float *S, const f32x4 (&r)[2]) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int f = t + h * 256;
-    if (KCONTIG) {
-      const int m = f >> 2, kq = f & 3;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) S[(kq * 4 + j) * (BM + PAD) + m] = r[h][j];
-    } else {
-      const int k = f >> 5, mq = f & 31;
-      *reinterpret_cast<f32x4 *>(S + k * (BM + PAD) + mq * 4) = r[h];
-    }
-  }
-}
-
-template <bool AK, bool BK_>
+// Block tile (64 TMt) x (64 TNt), 4 waves in a 2 x 2 arrangement, each
+// (32 TMt) x (32 TNt) in TMt x TNt MFMA tiles.  The 64-wide variants serve
+// dimensions such as 192 and 320 that 128-wide tiles would pad by 25-33%.
+template <bool AK, bool BK_, int TMt, int TNt>
 __global__ void __launch_bounds__(256, 2) gemm_f32_kernel(int M, int N, int K, const float *__restrict__ A, int lda,
                                                           const float *__restrict__ B, int ldb, float *__restrict__ C,
                                                           int ldc, int splits, int k_per_split, int64_t split_stride) {
-  __shared__ float As[2][BK * (BM + PAD)];
-  __shared__ float Bs[2][BK * (BN + PAD)];
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  constexpr int TBM = 64 * TMt, TBN = 64 * TNt;
+  using SA = TileShape<TBM, BK>;
+  using SB = TileShape<TBN, BK>;
+  __shared__ float As[2][BK * SA::LD];
+  __shared__ float Bs[2][BK * SB::LD];
+  const int tiles_m = (M + TBM - 1) / TBM, tiles_n = (N + TBN - 1) / TBN;
   const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n, splits);
   if (!tm.valid) return;
   const int z = tm.z;
   const int k_begin = z * k_per_split;
   const int k_end = min(K, k_begin + k_per_split);
   C += z * split_stride;
-  const int row0 = tm.mt * BM, col0 = tm.nt * BN;
+  const int row0 = tm.mt * TBM, col0 = tm.nt * TBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave >> 1) * 32 * TMt, wn = (wave & 1) * 32 * TNt;
   const int fr = lane & 31, fk = lane >> 5;
 
-  f32x16 acc[2][2];
+  f32x16 acc[TMt][TNt];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TMt; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TNt; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  f32x4 ra[2], rb[2];
+  f32x4 ra[SA::NF], rb[SB::NF];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < SA::NF; ++h) ra[h] = load_f4<AK, TBM, BK>(A, lda, M, row0, k0, k_end, threadIdx.x + 256 * h);
+#pragma unroll
+    for (int h = 0; h < SB::NF; ++h) rb[h] = load_f4<BK_, TBN, BK>(B, ldb, N, col0, k0, k_end, threadIdx.x + 256 * h);
+  };
+  auto store = [&](int b) {
+#pragma unroll
+    for (int h = 0; h < SA::NF; ++h) store_f4<AK, TBM, BK>(As[b], ra[h], threadIdx.x + 256 * h);
+#pragma unroll
+    for (int h = 0; h < SB::NF; ++h) store_f4<BK_, TBN, BK>(Bs[b], rb[h], threadIdx.x + 256 * h);
+  };
   int buf = 0;
   if (k_begin < k_end) {
-    load_tile<AK>(A, lda, M, row0, k_begin, k_end, ra);
-    load_tile<BK_>(B, ldb, N, col0, k_begin, k_end, rb);
-    store_tile<AK>(As[0], ra);
-    store_tile<BK_>(Bs[0], rb);
+    load(k_begin);
+    store(0);
   }
   __syncthreads();
   for (int k0 = k_begin; k0 < k_end; k0 += BK) {
     const bool more = k0 + BK < k_end;
-    if (more) {
-      load_tile<AK>(A, lda, M, row0, k0 + BK, k_end, ra);
-      load_tile<BK_>(B, ldb, N, col0, k0 + BK, k_end, rb);
-    }
+    if (more) load(k0 + BK);
     const float *as = As[buf];
     const float *bs = Bs[buf];
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 2) {
-      float a[2], b[2];
+      float a[TMt], b[TNt];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = as[(kk + fk) * (BM + PAD) + wm + 32 * i + fr];
+      for (int i = 0; i < TMt; ++i) a[i] = as[(kk + fk) * SA::LD + wm + 32 * i + fr];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = bs[(kk + fk) * (BN + PAD) + wn + 32 * j + fr];
+      for (int j = 0; j < TNt; ++j) b[j] = bs[(kk + fk) * SB::LD + wn + 32 * j + fr];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TMt; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TNt; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      store_tile<AK>(As[buf ^ 1], ra);
-      store_tile<BK_>(Bs[buf ^ 1], rb);
-    }
+    if (more) store(buf ^ 1);
     __syncthreads();
     buf ^= 1;
   }
   // 32x32 accumulator layout: column = lane % 32, row = 8*(r/4) + 4*(lane/32) + r%4
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TMt; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TNt; ++j) {
       const int col = col0 + wn + 32 * j + fr;
       if (col >= N) continue;
 #pragma unroll
@@ -201,53 +212,19 @@ __global__ void __launch_bounds__(256, 2) gemm_f32_kernel(int M, int N, int K, c
 // to LDS.  Tile 128 x 128 (per part), K step 8, 4 waves of 64 x 64 x 3 parts.
 constexpr int CBK = 8;
 
-template <bool KCONTIG>
-__device__ inline f32x4 load_ctile(const float *P, int ld, int rows, int row0, int k0, int k_end) {
-  const int f = threadIdx.x;  // one float4 of the 128 x 8 tile per thread
-  f32x4 v = {0.f, 0.f, 0.f, 0.f};
-  if (KCONTIG) {
-    const int m = f >> 1, kq = f & 1;
-    const int gm = row0 + m, gk = k0 + kq * 4;
-    if (gm < rows && gk < k_end) v = *reinterpret_cast<const f32x4 *>(P + static_cast<int64_t>(gm) * ld + gk);
-  } else {
-    const int k = f >> 5, mq = f & 31;
-    const int gk = k0 + k, gm = row0 + mq * 4;
-    if (gk < k_end && gm < rows) {
-      const float *p = P + static_cast<int64_t>(gk) * ld + gm;
-      if (gm + 3 < rows) {
-        v = *reinterpret_cast<const f32x4 *>(p);
-      } else {
-        for (int j = 0; j < 4; ++j) v[j] = (gm + j < rows) ? p[j] : 0.f;
-      }
-    }
-  }
-  return v;
-}
-
-template <bool KCONTIG>
-__device__ inline void store_ctile(float *S, const f32x4 &v) {
-  const int f = threadIdx.x;
-  if (KCONTIG) {
-    const int m = f >> 1, kq = f & 1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) S[(kq * 4 + j) * (BM + PAD) + m] = v[j];
-  } else {
-    const int k = f >> 5, mq = f & 31;
-    *reinterpret_cast<f32x4 *>(S + k * (BM + PAD) + mq * 4) = v;
-  }
-}
-
-template <bool UK, bool VK, bool VPRE>
+template <bool UK, bool VK, bool VPRE, int TMt, int TNt>
 __global__ void __launch_bounds__(256, 2) cgemm_f32_kernel(int M, int N, int K, const float *__restrict__ Up,
                                                            const float *__restrict__ Um, int ldu,
                                                            const float *__restrict__ V1, const float *__restrict__ V2,
                                                            const float *__restrict__ V3, int ldv, float vsign,
                                                            float *__restrict__ Cre, float *__restrict__ Cim, int ldc,
                                                            int splits, int k_per_split, int64_t split_stride) {
-  constexpr int LT = CBK * (BM + PAD);
-  __shared__ float Us[2][3][LT];
-  __shared__ float Vs[2][3][LT];
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  constexpr int TBM = 64 * TMt, TBN = 64 * TNt;
+  using SU = TileShape<TBM, CBK>;
+  using SV = TileShape<TBN, CBK>;
+  __shared__ float Us[2][3][CBK * SU::LD];
+  __shared__ float Vs[2][3][CBK * SV::LD];
+  const int tiles_m = (M + TBM - 1) / TBM, tiles_n = (N + TBN - 1) / TBN;
   const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n, splits);
   if (!tm.valid) return;
   const int z = tm.z;
@@ -255,42 +232,58 @@ __global__ void __launch_bounds__(256, 2) cgemm_f32_kernel(int M, int N, int K, 
   const int k_end = min(K, k_begin + k_per_split);
   Cre += z * split_stride;
   Cim += z * split_stride;
-  const int row0 = tm.mt * BM, col0 = tm.nt * BN;
+  const int row0 = tm.mt * TBM, col0 = tm.nt * TBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave >> 1) * 32 * TMt, wn = (wave & 1) * 32 * TNt;
   const int fr = lane & 31, fk = lane >> 5;
 
-  f32x16 acc[3][2][2];
+  f32x16 acc[3][TMt][TNt];
 #pragma unroll
   for (int q = 0; q < 3; ++q)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TMt; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TNt; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[q][i][j][r] = 0.f;
 
-  f32x4 up, um, va, vb, vc;
+  f32x4 up[SU::NF], um[SU::NF], va[SV::NF], vb[SV::NF], vc[SV::NF];
   auto load = [&](int k0) {
-    up = load_ctile<UK>(Up, ldu, M, row0, k0, k_end);
-    um = load_ctile<UK>(Um, ldu, M, row0, k0, k_end);
-    va = load_ctile<VK>(V1, ldv, N, col0, k0, k_end);
-    vb = load_ctile<VK>(V2, ldv, N, col0, k0, k_end);
-    if (VPRE) vc = load_ctile<VK>(V3, ldv, N, col0, k0, k_end);
+#pragma unroll
+    for (int h = 0; h < SU::NF; ++h) {
+      const int f = threadIdx.x + 256 * h;
+      up[h] = load_f4<UK, TBM, CBK>(Up, ldu, M, row0, k0, k_end, f);
+      um[h] = load_f4<UK, TBM, CBK>(Um, ldu, M, row0, k0, k_end, f);
+    }
+#pragma unroll
+    for (int h = 0; h < SV::NF; ++h) {
+      const int f = threadIdx.x + 256 * h;
+      va[h] = load_f4<VK, TBN, CBK>(V1, ldv, N, col0, k0, k_end, f);
+      vb[h] = load_f4<VK, TBN, CBK>(V2, ldv, N, col0, k0, k_end, f);
+      if (VPRE) vc[h] = load_f4<VK, TBN, CBK>(V3, ldv, N, col0, k0, k_end, f);
+    }
   };
   auto store = [&](int b) {
-    store_ctile<UK>(Us[b][0], up + um);
-    store_ctile<UK>(Us[b][1], up);
-    store_ctile<UK>(Us[b][2], um);
-    if (VPRE) {
-      store_ctile<VK>(Vs[b][0], va);
-      store_ctile<VK>(Vs[b][1], vb);
-      store_ctile<VK>(Vs[b][2], vc);
-    } else {
-      const f32x4 vm = vb * vsign;  // V- from the second half
-      store_ctile<VK>(Vs[b][0], va);
-      store_ctile<VK>(Vs[b][1], vm - va);
-      store_ctile<VK>(Vs[b][2], va + vm);
+#pragma unroll
+    for (int h = 0; h < SU::NF; ++h) {
+      const int f = threadIdx.x + 256 * h;
+      store_f4<UK, TBM, CBK>(Us[b][0], up[h] + um[h], f);
+      store_f4<UK, TBM, CBK>(Us[b][1], up[h], f);
+      store_f4<UK, TBM, CBK>(Us[b][2], um[h], f);
+    }
+#pragma unroll
+    for (int h = 0; h < SV::NF; ++h) {
+      const int f = threadIdx.x + 256 * h;
+      if (VPRE) {
+        store_f4<VK, TBN, CBK>(Vs[b][0], va[h], f);
+        store_f4<VK, TBN, CBK>(Vs[b][1], vb[h], f);
+        store_f4<VK, TBN, CBK>(Vs[b][2], vc[h], f);
+      } else {
+        const f32x4 vm = vb[h] * vsign;  // V- from the second half
+        store_f4<VK, TBN, CBK>(Vs[b][0], va[h], f);
+        store_f4<VK, TBN, CBK>(Vs[b][1], vm - va[h], f);
+        store_f4<VK, TBN, CBK>(Vs[b][2], va[h] + vm, f);
+      }
     }
   };
   int buf = 0;
@@ -308,15 +301,15 @@ __global__ void __launch_bounds__(256, 2) cgemm_f32_kernel(int M, int N, int K, 
       for (int q = 0; q < 3; ++q) {
         const float *us = Us[buf][q];
         const float *vs = Vs[buf][q];
-        float a[2], b[2];
+        float a[TMt], b[TNt];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) a[i] = us[(kk + fk) * (BM + PAD) + wm + 32 * i + fr];
+        for (int i = 0; i < TMt; ++i) a[i] = us[(kk + fk) * SU::LD + wm + 32 * i + fr];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) b[j] = vs[(kk + fk) * (BN + PAD) + wn + 32 * j + fr];
+        for (int j = 0; j < TNt; ++j) b[j] = vs[(kk + fk) * SV::LD + wn + 32 * j + fr];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < TMt; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < TNt; ++j)
             acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[q][i][j], 0, 0, 0);
       }
     }
@@ -325,9 +318,9 @@ __global__ void __launch_bounds__(256, 2) cgemm_f32_kernel(int M, int N, int K, 
     buf ^= 1;
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TMt; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TNt; ++j) {
       const int col = col0 + wn + 32 * j + fr;
       if (col >= N) continue;
 #pragma unroll
@@ -612,22 +605,62 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, i
 
 }  // namespace
 
+namespace {
+
+// 128-wide tiles (2 MFMA tiles per wave) unless they would pad the dimension
+// by more than 10% and 64-wide ones pad less (192 and 320 here).
+int tile_count(int n) {
+  const int r128 = (n + 127) / 128 * 128, pad128 = r128 - n, pad64 = (n + 63) / 64 * 64 - n;
+  return (pad64 < pad128 && 10 * pad128 > r128) ? 1 : 2;
+}
+
+template <bool AK, bool BK_>
+void launch_gemm(int tmt, int tnt, int M, int N, int K, const float *A, int lda, const float *B, int ldb, float *C,
+                 int ldc, int splits, int kps, int64_t split_stride, hipStream_t stream) {
+  const int tiles = ((M + 64 * tmt - 1) / (64 * tmt)) * ((N + 64 * tnt - 1) / (64 * tnt));
+  const int grid = tile_grid(tiles, splits);
+#define EGNN_G(TM_, TN_) \
+  gemm_f32_kernel<AK, BK_, TM_, TN_><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride)
+  if (tmt == 2 && tnt == 2) EGNN_G(2, 2);
+  else if (tmt == 2) EGNN_G(2, 1);
+  else if (tnt == 2) EGNN_G(1, 2);
+  else EGNN_G(1, 1);
+#undef EGNN_G
+}
+
+template <bool UK, bool VK, bool PRE>
+void launch_cgemm(int tmt, int tnt, int M, int N, int K, const float *Up, const float *Um, int ldu, const float *V1,
+                  const float *V2, const float *V3, int ldv, float vsign, float *Cre, float *Cim, int ldc, int splits,
+                  int kps, int64_t split_stride, hipStream_t stream) {
+  const int tiles = ((M + 64 * tmt - 1) / (64 * tmt)) * ((N + 64 * tnt - 1) / (64 * tnt));
+  const int grid = tile_grid(tiles, splits);
+#define EGNN_C(TM_, TN_)                                                                                           \
+  cgemm_f32_kernel<UK, VK, PRE, TM_, TN_><<<grid, 256, 0, stream>>>(M, N, K, Up, Um, ldu, V1, V2, V3, ldv, vsign, Cre, \
+                                                                    Cim, ldc, splits, kps, split_stride)
+  if (tmt == 2 && tnt == 2) EGNN_C(2, 2);
+  else if (tmt == 2) EGNN_C(2, 1);
+  else if (tnt == 2) EGNN_C(1, 2);
+  else EGNN_C(1, 1);
+#undef EGNN_C
+}
+
+}  // namespace
+
 hipError_t gemm_f32(int M, int N, int K, const float *A, int lda, bool a_kcontig, const float *B, int ldb,
                     bool b_kcontig, float *C, int ldc, int splits, int64_t split_stride, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (splits < 1) splits = 1;
   int kps = (K + splits - 1) / splits;
   kps = (kps + BK - 1) / BK * BK;
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const int grid = tile_grid(tiles, splits);
+  const int tmt = tile_count(M), tnt = tile_count(N);
   if (a_kcontig && b_kcontig)
-    gemm_f32_kernel<true, true><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
+    launch_gemm<true, true>(tmt, tnt, M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride, stream);
   else if (!a_kcontig && !b_kcontig)
-    gemm_f32_kernel<false, false><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
+    launch_gemm<false, false>(tmt, tnt, M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride, stream);
   else if (a_kcontig)
-    gemm_f32_kernel<true, false><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
+    launch_gemm<true, false>(tmt, tnt, M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride, stream);
   else
-    gemm_f32_kernel<false, true><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
+    launch_gemm<false, true>(tmt, tnt, M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride, stream);
   return hipGetLastError();
 }
 
@@ -638,17 +671,19 @@ hipError_t cgemm_f32(int M, int N, int K, const float *Up, const float *Um, int 
   if (splits < 1) splits = 1;
   int kps = (K + splits - 1) / splits;
   kps = (kps + CBK - 1) / CBK * CBK;
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const int grid = tile_grid(tiles, splits);
+  const int tmt = tile_count(M), tnt = tile_count(N);
   const bool pre = V3 != nullptr;
-#define EGNN_CG(UKc, VKc, PREc)                                                                           \
-  cgemm_f32_kernel<UKc, VKc, PREc><<<grid, 256, 0, stream>>>(M, N, K, Up, Um, ldu, V1, V2, V3, ldv, vsign, Cre, Cim, \
-                                                            ldc, splits, kps, split_stride)
-  if (u_kcontig && v_kcontig && pre) EGNN_CG(true, true, true);
-  else if (u_kcontig && !v_kcontig && pre) EGNN_CG(true, false, true);
-  else if (!u_kcontig && !v_kcontig && !pre) EGNN_CG(false, false, false);
-  else return hipErrorInvalidValue;
-#undef EGNN_CG
+  if (u_kcontig && v_kcontig && pre)
+    launch_cgemm<true, true, true>(tmt, tnt, M, N, K, Up, Um, ldu, V1, V2, V3, ldv, vsign, Cre, Cim, ldc, splits, kps,
+                                   split_stride, stream);
+  else if (u_kcontig && !v_kcontig && pre)
+    launch_cgemm<true, false, true>(tmt, tnt, M, N, K, Up, Um, ldu, V1, V2, V3, ldv, vsign, Cre, Cim, ldc, splits, kps,
+                                    split_stride, stream);
+  else if (!u_kcontig && !v_kcontig && !pre)
+    launch_cgemm<false, false, false>(tmt, tnt, M, N, K, Up, Um, ldu, V1, V2, V3, ldv, vsign, Cre, Cim, ldc, splits,
+                                      kps, split_stride, stream);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
