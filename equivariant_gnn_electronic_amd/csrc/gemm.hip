@@ -473,7 +473,7 @@ __device__ inline int chunk_swizzle(int row) {
   return CPR == 4 ? ((row >> 2) & 3) : ((row >> 1) & 7);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int S, bool CBF16>
+template <int BM, int BN, int BK, int WM, int WN, int S, int U, bool CBF16>
 __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, int N, int K,
                                                                       const uint16_t *__restrict__ A, int lda,
                                                                       const uint16_t *__restrict__ B, int ldb,
@@ -568,13 +568,16 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, i
   else wait_vmcnt<0>();
   barrier_no_fence();
   // iteration i multiplies stage i % S, then refills the stage of tile i - 1
-  // (free since the last barrier) with tile i + S - 1, then waits for tile i + 1
-  for (int it = 0; it < nk; it += S) {
-    static_for<0, S>([&](auto d) {
-      constexpr int dd = decltype(d)::value;
-      const int i = it + dd;
+  // (free since the last barrier) with tile i + S - 1, then waits for tile i + 1.
+  // The loop body is U rounds of the ring: at the loop head the compiler's
+  // wait-count tracking merges both paths and waits for every load in flight,
+  // so a longer body drains the pipeline less often.
+  for (int it = 0; it < nk; it += S * U) {
+    static_for<0, S * U>([&](auto du) {
+      constexpr int dd = decltype(du)::value % S;
+      const int i = it + decltype(du)::value;
       if (i >= nk) return;
-      compute(d);
+      compute(std::integral_constant<int, dd>{});
       if (i + S - 1 < nk) {
         issue(std::integral_constant<int, (dd + S - 1) % S>{}, i + S - 1);
         wait_vmcnt<(S - 2) * L>();
@@ -698,16 +701,16 @@ hipError_t gemm_bf16_nt(int M, int N, int K, const uint16_t *A, int lda, const u
     // 256 x 128 x 64, 8 waves (4 x 2, 64 x 64 each), 3 stages (144 KB LDS)
     const int grid = tile_grid(tiles_m * ((N + 127) / 128), 1);
     if (c_bf16)
-      gemm_bf16_lds_kernel<256, 128, 64, 4, 2, 3, true><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+      gemm_bf16_lds_kernel<256, 128, 64, 4, 2, 3, 1, true><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
     else
-      gemm_bf16_lds_kernel<256, 128, 64, 4, 2, 3, false><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+      gemm_bf16_lds_kernel<256, 128, 64, 4, 2, 3, 1, false><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
   } else if (aligned && K % 32 == 0) {
-    // 256 x 256 x 32, 8 waves (2 x 4, 128 x 64 each), 4 stages (128 KB LDS)
+    // 256 x 256 x 32, 8 waves (2 x 4, 128 x 64 each), 4 stages (128 KB LDS), loop body of 4 rings
     const int grid = tile_grid(tiles_m * ((N + 255) / 256), 1);
     if (c_bf16)
-      gemm_bf16_lds_kernel<256, 256, 32, 2, 4, 4, true><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+      gemm_bf16_lds_kernel<256, 256, 32, 2, 4, 4, 4, true><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
     else
-      gemm_bf16_lds_kernel<256, 256, 32, 2, 4, 4, false><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+      gemm_bf16_lds_kernel<256, 256, 32, 2, 4, 4, 4, false><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
   } else {
     const int tiles = ((M + HBM_ - 1) / HBM_) * ((N + HBN - 1) / HBN);
     const int grid = tile_grid(tiles, 1);
