@@ -21,6 +21,7 @@
 //   Y_0 [E][nl(0) * C], Y_m [E][2 * nl(m) * C]   same pattern with C
 // slot 0..C-1 = source channels, C..2C-1 = destination channels.
 #include <cstring>
+#include <type_traits>
 
 #include "common.h"
 #include "gemm.h"
@@ -186,6 +187,27 @@ __device__ inline void load_wrad(const float *wrad, int n_rbf, int C2, int j, bo
       wr[k][p] = (active && k < n_rbf) ? wrad[(static_cast<int64_t>(k) * NP + p) * C2 + j] : 0.0f;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Radial weights of one lane's slot as bf16 pairs over the basis index
+// (k = 2q, 2q + 1), for the bf16-storage forward: the gate then takes
+// NRBF / 2 packed dot products (v_dot2_f32_bf16, fp32 accumulate) per pair
+// and half the registers of the fp32 form.
+template <int LMAX, int MMAX, int NRBF>
+__device__ inline void load_wrad_bf16(const float *wrad, int n_rbf, int C2, int j, bool active,
+                                      bf16x2 (&wr)[NRBF / 2][pair_count(LMAX, MMAX)]) {
+  constexpr int NP = pair_count(LMAX, MMAX);
+#pragma unroll
+  for (int q = 0; q < NRBF / 2; ++q)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int k0 = 2 * q, k1 = 2 * q + 1;
+      const float w0 = (active && k0 < n_rbf) ? wrad[(static_cast<int64_t>(k0) * NP + p) * C2 + j] : 0.0f;
+      const float w1 = (active && k1 < n_rbf) ? wrad[(static_cast<int64_t>(k1) * NP + p) * C2 + j] : 0.0f;
+      wr[q][p] = bf16x2{static_cast<__bf16>(w0), static_cast<__bf16>(w1)};
+    }
+}
+
 // A[e] = g_e * trunc(D_e x) for the wave's half of every edge of its node.
 template <int LMAX, int MMAX, int NRBF, typename T, typename TA>
 __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restrict__ row_ptr,
@@ -212,8 +234,14 @@ __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restr
   float xv[L::K];
 #pragma unroll
   for (int k = 0; k < L::K; ++k) xv[k] = active ? Store<T>::ld(x + (static_cast<int64_t>(nw.node) * L::K + k) * C + c) : 0.0f;
-  float wr[NRBF][L::NP];
-  load_wrad<LMAX, MMAX, NRBF>(wrad, n_rbf, C2, j, active, wr);
+  // fp32 storage: fp32 radial weights; bf16 storage: bf16 pairs (see load_wrad_bf16)
+  constexpr bool kPacked = std::is_same<TA, uint16_t>::value;
+  float wr[kPacked ? 1 : NRBF][kPacked ? 1 : L::NP];
+  bf16x2 wp[kPacked ? NRBF / 2 : 1][kPacked ? L::NP : 1];
+  if constexpr (kPacked)
+    load_wrad_bf16<LMAX, MMAX, NRBF>(wrad, n_rbf, C2, j, active, wp);
+  else
+    load_wrad<LMAX, MMAX, NRBF>(wrad, n_rbf, C2, j, active, wr);
   const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
   for (int base = 0; base < el.count; base += kBatch) {
     const int cnt = min(kBatch, el.count - base);
@@ -224,13 +252,25 @@ __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restr
       float g[L::NP];
 #pragma unroll
       for (int p = 0; p < L::NP; ++p) g[p] = 0.0f;
+      if constexpr (kPacked) {
 #pragma unroll
-      for (int k = 0; k < NRBF; ++k) {
-        // unconditional LDS read, then select: no branch per basis function
-        const float raw = gr[L::ND + k];
-        const float ph = k < n_rbf ? raw : 0.0f;
+        for (int q = 0; q < NRBF / 2; ++q) {
+          // unconditional LDS reads, then selects: no branch per basis function
+          const float r0 = gr[L::ND + 2 * q], r1 = gr[L::ND + 2 * q + 1];
+          const bf16x2 ph{static_cast<__bf16>(2 * q < n_rbf ? r0 : 0.0f),
+                          static_cast<__bf16>(2 * q + 1 < n_rbf ? r1 : 0.0f)};
 #pragma unroll
-        for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[k][p];
+          for (int p = 0; p < L::NP; ++p) g[p] = __builtin_amdgcn_fdot2_f32_bf16(ph, wp[q][p], g[p], false);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < NRBF; ++k) {
+          // unconditional LDS read, then select: no branch per basis function
+          const float raw = gr[L::ND + k];
+          const float ph = k < n_rbf ? raw : 0.0f;
+#pragma unroll
+          for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[k][p];
+        }
       }
       if (!active) continue;
       // wave-uniform row pointers; the lane offsets below stay 32-bit
