@@ -240,7 +240,7 @@ FAMILY_KERNELS = {
     "gemm_tn_f32": "gemm_f32_kernel<false, false>",
     "gemm_nt_f32": "gemm_f32_kernel<true, true>",
     "gemm_nn_f32": "gemm_f32_kernel<true, false>",
-    "gemm_nt_bf16": "gemm_bf16_kernel",
+    "gemm_nt_bf16": "gemm_bf16",
     "rotate_in": "scatter_in_kernel",
     "aggregate": "aggregate_kernel",
     "hblocks": "hblocks_kernel",

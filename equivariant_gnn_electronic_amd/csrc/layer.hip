@@ -1097,7 +1097,7 @@ extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph
         continue;
       }
       Timed t(stream, bf ? "gemm_nt_bf16" : "gemm_nt_f32", 2.0 * double(E) * s.Ng[m] * s.Kg[m],
-              double(E) * (s.Kg[m] * xb + s.Ng[m] * 4.0));
+              double(E) * (s.Kg[m] + s.Ng[m]) * xb);
       if (bf) {
         e = gemm_bf16_nt(static_cast<int>(E), s.Ng[m], s.Kg[m], static_cast<const uint16_t *>(acts.A[m]), s.Kg[m],
                          static_cast<const uint16_t *>(fw.B[m]), s.Kg[m], acts.Y[m], s.Ng[m], true, stream);
