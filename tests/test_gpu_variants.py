@@ -1,0 +1,136 @@
+"""HIP path vs the fp64 oracle over the layer's shape space (needs an MI355X).
+
+The 64-atom periodic cell (several images per pair) carries every
+(lmax, mmax, C, n_rbf, storage) combination below, so each kernel
+instantiation the ABI dispatches to is exercised: lmax 1-4, mmax 0-2, C with
+a partial 64-channel chunk (24, 96) and two chunks (128), 4/8/12/16 radial
+functions, bf16 storage on both bf16 GEMM variants and the fallback for
+K not a multiple of 32.  Also: an open cell with isolated atoms (rows without
+incoming edges) and ghosts, and a graph with no edges at all.
+Tolerances as in test_gpu_parity.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import layer as olayer
+from tests.helpers import assert_close, desc_of, grid_box, oracle_graph
+
+pytestmark = pytest.mark.gpu
+
+eg = pytest.importorskip("equivariant_gnn_electronic_amd")
+
+VARIANTS = [
+    # lmax, mmax, C, n_rbf, storage
+    (1, 0, 8, 8, "f32"),
+    (1, 1, 16, 4, "f32"),
+    (2, 1, 96, 8, "f32"),
+    (3, 1, 24, 8, "f32"),
+    (3, 2, 8, 12, "f32"),
+    (2, 2, 8, 16, "f32"),
+    (4, 2, 128, 8, "f32"),
+    (4, 1, 32, 8, "f32"),
+    (4, 0, 16, 8, "f32"),
+    (3, 1, 32, 8, "bf16"),
+    (4, 2, 8, 8, "bf16"),
+    (2, 0, 64, 4, "bf16"),
+]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _graph(struct, dev):
+    lo, box = grid_box(struct)
+    pos = torch.from_numpy(struct.pos).to(dev)
+    return eg.egnn_build_graph(pos, struct.n_dst, lo, box, struct.periodic_mask, struct.r_cut)
+
+
+def _run(cfg, s, dev, backward):
+    x, ws = synth.make_layer_inputs(cfg)
+    g = _graph(s, dev)
+    storage = eg.EGNN_BF16 if cfg.storage == "bf16" else eg.EGNN_F32
+    desc = eg.layer_desc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut, storage)
+    geom = eg.egnn_edge_geom(desc, g)
+    xt = torch.from_numpy(x).to(dev)
+    if storage == eg.EGNN_BF16:
+        xt = xt.to(torch.bfloat16)
+    wt = torch.from_numpy(ws[0]).to(dev)
+    buf = eg.LayerBuffers(desc, g, train=backward)
+    (xo, _), buf = eg.egnn_layer_fwd(desc, g, geom, wt, xt, buffers=buf)
+    out = dict(g=g, x=x, w=ws[0], xo=xo.float().cpu().numpy())
+    if backward:
+        G = synth.make_cotangent(cfg, s.n_dst)
+        gx, gw = eg.egnn_layer_bwd(desc, g, geom, wt, xt, buf, torch.from_numpy(G).to(dev))
+        out.update(G=G, gx=gx.cpu().numpy(), gw=gw.cpu().numpy())
+    torch.cuda.synchronize()
+    return out
+
+
+def _check(cfg, s, r, backward):
+    og = oracle_graph(s)
+    x64, w64 = r["x"].astype(np.float64), r["w"].astype(np.float64)
+    fwd = olayer.layer_forward(og, x64, w64, desc_of(cfg))
+    tol = 2e-2 if cfg.storage == "bf16" else 1e-4
+    assert_close(r["xo"], fwd["x_out"], tol, "x_out")
+    if backward:
+        dx, dw = olayer.layer_backward(og, x64, w64, desc_of(cfg), fwd, r["G"].astype(np.float64))
+        assert_close(r["gx"], dx, 1e-4, "grad x")
+        o = 0
+        for name, shape in synth.layer_weight_sizes(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf):
+            n = int(np.prod(shape))
+            assert_close(r["gw"][o:o + n], dw[o:o + n], 1e-4, f"grad {name}")
+            o += n
+
+
+@pytest.mark.parametrize("lmax,mmax,C,n_rbf,storage", VARIANTS)
+def test_layer_shapes(dev, lmax, mmax, C, n_rbf, storage):
+    cfg = dataclasses.replace(synth.CONFIGS["tiny"], lmax=lmax, mmax=mmax, C=C, n_rbf=n_rbf, storage=storage)
+    s = synth.make_structure(cfg)
+    backward = storage == "f32"
+    r = _run(cfg, s, dev, backward)
+    _check(cfg, s, r, backward)
+
+
+OPEN_SPARSE = synth.Config("open_sparse", 12, (40,), (12.0, 12.0, 12.0), False, 3.2, 2, 1, 16, halo=3.2,
+                           note="open cell, sparse enough that some atoms have no neighbour; ghost shell")
+
+
+def test_open_cell_isolated_rows(dev):
+    cfg = OPEN_SPARSE
+    s = synth.make_structure(cfg)
+    assert s.n_src > s.n_dst
+    r = _run(cfg, s, dev, True)
+    indeg = np.diff(r["g"].row_ptr.cpu().numpy())
+    assert (indeg == 0).any() and (indeg > 0).any()
+    _check(cfg, s, r, True)
+    # rows without edges keep x, and their own gradient is G
+    empty = np.flatnonzero(indeg == 0)
+    np.testing.assert_array_equal(r["xo"][empty], r["x"][empty])
+
+
+def test_no_edges(dev):
+    cfg = dataclasses.replace(synth.CONFIGS["tiny"], name="far_apart")
+    pos = torch.tensor([[0.0, 0, 0], [40.0, 0, 0], [0, 40.0, 0], [40.0, 40.0, 40.0]], dtype=torch.float64, device=dev)
+    g = eg.egnn_build_graph(pos, 3, [0, 0, 0], [50.0, 50.0, 50.0], 0, cfg.r_cut)
+    assert g.n_edges == 0
+    desc = eg.layer_desc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut)
+    x, ws = synth.make_layer_inputs(cfg, n_src=4)
+    xt = torch.from_numpy(x).to(dev)
+    wt = torch.from_numpy(ws[0]).to(dev)
+    geom = eg.egnn_edge_geom(desc, g)
+    buf = eg.LayerBuffers(desc, g, train=True)
+    (xo, _), buf = eg.egnn_layer_fwd(desc, g, geom, wt, xt, buffers=buf)
+    G = torch.from_numpy(synth.make_cotangent(cfg, 3)).to(dev)
+    gx, gw = eg.egnn_layer_bwd(desc, g, geom, wt, xt, buf, G)
+    torch.cuda.synchronize()
+    assert torch.equal(xo, xt[:3])
+    assert torch.equal(gx[:3], G) and not gx[3].any()
+    assert not gw.any()
