@@ -134,3 +134,23 @@ def test_no_edges(dev):
     assert torch.equal(xo, xt[:3])
     assert torch.equal(gx[:3], G) and not gx[3].any()
     assert not gw.any()
+
+
+def test_hblocks_bf16_irreps(dev):
+    """Decode of bf16 irreps (the bf16 path's last layer, C 16, lmax 4) against
+    the oracle on the same bf16 values; fp32 arithmetic, so 1e-5."""
+    cfg = synth.CONFIGS["tiny_stack"]
+    s = synth.make_structure(cfg)
+    x, ws = synth.make_layer_inputs(cfg)
+    g = _graph(s, dev)
+    desc = eg.layer_desc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut, eg.EGNN_BF16)
+    geom = eg.egnn_edge_geom(desc, g)
+    (xo, eo), _ = eg.egnn_layer_fwd(desc, g, geom, torch.from_numpy(ws[0]).to(dev),
+                                    torch.from_numpy(x).to(dev).to(torch.bfloat16), edge_out=True)
+    we, wn = synth.make_decode_weights(cfg)
+    he, hn = eg.egnn_hblocks(cfg.lmax, cfg.C, torch.from_numpy(np.concatenate(we)).to(dev),
+                             torch.from_numpy(np.concatenate(wn)).to(dev), eo, xo, storage=eg.EGNN_BF16)
+    torch.cuda.synchronize()
+    from oracle import decode as odec
+    assert_close(he.cpu().numpy(), odec.hblocks(eo.float().cpu().numpy().astype(np.float64), we), 1e-5, "edge blocks")
+    assert_close(hn.cpu().numpy(), odec.hblocks(xo.float().cpu().numpy().astype(np.float64), wn), 1e-5, "on-site")
