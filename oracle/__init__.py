@@ -20,6 +20,22 @@ Every function follows a passage of the pages it is written from:
 Where the pages leave a step open the plainest reading is taken; each such
 reading is named in the docstring of the function that takes it.
 
+Parity unpinned: the *choice* of those readings.  The pages print no value
+that could decide between equally valid readings of these steps, so the
+tests pin each function's arithmetic for the reading taken (invariants,
+brute force, closed forms, finite differences), not the reading itself:
+  layer.radial_basis (centres and width of the Gaussians),
+  layer.gates (radial basis as per-(m, l, channel) input gates),
+  layer.trunc_mask (coefficients with |m| > mmax dropped),
+  layer.edge_forward (source-then-destination message channels; the
+      attention logit from the invariant output channels),
+  layer.layer_forward (residual update; the per-edge message as the edge
+      irreps of the decode),
+  layer.layer_backward (the loss <G, x'>),
+  decode.label_layout / labels_from_irreps / label_to_matrix (label order,
+      the 2s2p1d basis, no hermiticity symmetrisation),
+  so3.real_coupling (the sign rule of the real coupling).
+
 Modules:
   neighbors  -- brute-force periodic / open cutoff graph, destination-sorted CSR
   so3        -- real spherical harmonics, Wigner-D, edge frame, real CG couplings
