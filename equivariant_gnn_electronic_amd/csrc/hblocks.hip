@@ -276,6 +276,8 @@ constexpr int kTile = 16;  // rows per wave tile (the MFMA M dimension)
 // run of S channels of its row (vector loads, issued before the chain); W is
 // staged once per block in LDS (rows padded by 4 floats) and read in the same
 // channel order.
+__host__ __device__ inline int label_stride(int n_lab) { return n_lab + ((4 - n_lab % 16) + 16) % 16; }
+
 template <int S, typename T>
 __device__ inline void load_run(const T *p, float (&a)[S]) {
   if constexpr (sizeof(T) == 4 && S % 4 == 0) {
@@ -307,7 +309,10 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
   int *t_idx = reinterpret_cast<int *>(t_coef + n_terms);              // [n_terms]
   float *wl = reinterpret_cast<float *>(t_idx + n_terms);              // [n_w + 16][WLD] (zero rows after n_w)
   wl = reinterpret_cast<float *>((reinterpret_cast<uintptr_t>(wl) + 15) & ~uintptr_t(15));
-  float *hs_all = wl + (n_w + 16) * WLD;                               // [kWaves][kTile][n_lab]
+  // label rows padded to lab_ld = 4 (mod 16) floats: the four 16-lane groups
+  // of an MFMA result store then land on disjoint LDS bank ranges
+  const int lab_ld = label_stride(n_lab);
+  float *hs_all = wl + (n_w + 16) * WLD;                               // [kWaves][kTile][lab_ld]
   for (int i = threadIdx.x; i <= n_ent; i += blockDim.x) t_start[i] = tb.term_start[i];
   for (int i = threadIdx.x; i < n_terms; i += blockDim.x) {
     t_coef[i] = tb.term_coef[i];
@@ -319,7 +324,7 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
   }
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  float *hs = hs_all + wave * kTile * n_lab;
+  float *hs = hs_all + wave * kTile * lab_ld;
   const int grp = lane / 16, i16 = lane % 16;
   const int lmax_lab = tb.lmax_lab;
   const int64_t n_tiles = (rows + kTile - 1) / kTile;
@@ -349,7 +354,7 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
           const int k = 16 * t + i16;
           if (k < nL) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) hs[(4 * grp + r) * n_lab + hoff + (M + L) * nL + k] = acc[r];
+            for (int r = 0; r < 4; ++r) hs[(4 * grp + r) * lab_ld + hoff + (M + L) * nL + k] = acc[r];
           }
         }
       }
@@ -358,7 +363,7 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
     for (int q = lane; q < kTile * n_ent; q += kWave) {
       const int el = q / n_ent, ent = q - el * n_ent;
       if (e0 + el >= rows) break;
-      const float *h = hs + el * n_lab;
+      const float *h = hs + el * lab_ld;
       float acc = 0.0f;
       const int t1 = t_start[ent + 1];
       for (int t = t_start[ent]; t < t1; ++t) acc += t_coef[t] * h[t_idx[t]];
@@ -374,7 +379,7 @@ egnn_status launch_hblocks(int slot, int64_t rows, const void *irreps, int K, in
   if (rows <= 0) return EGNN_OK;
   const size_t smem = sizeof(float) * (static_cast<size_t>(n_ent + 1) + 2 * n_terms + 4 +
                                        static_cast<size_t>(n_w + 16) * (C + 4) +
-                                       static_cast<size_t>(kWaves) * kTile * n_lab);
+                                       static_cast<size_t>(kWaves) * kTile * label_stride(n_lab));
   if (smem > 150 * 1024) {
     set_error("decode needs %zu bytes of LDS; reduce C or the shell list", smem);
     return EGNN_E_UNSUPPORTED;
