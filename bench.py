@@ -36,6 +36,8 @@ WORKLOADS = {
                  desc="one GPU's share with ghost halo: graph + geometry + 1 layer fwd"),
     "gst": dict(cfg="gst", backward=False, decode=False, layers=3,
                 desc="GeSbTe-like 3-layer forward, bf16 storage"),
+    "gst_train": dict(cfg="gst", backward=True, decode=True, layers=1,
+                      desc="GeSbTe-like training step, bf16 storage: graph + geometry + 1 layer fwd/bwd + 13x13 blocks"),
 }
 
 
@@ -120,7 +122,7 @@ class Step:
                               grad_x=self.gx, grad_w=self.gw)
         if self.wl["decode"]:
             eg.egnn_hblocks(self.cfg.lmax, self.cfg.C, self.we, self.wn, self.edge_out[:self.E],
-                            self.xs[-1][:s.n_dst])
+                            self.xs[-1][:s.n_dst], storage=self.storage)
         return g
 
     def _fwd(self, g, i, eo):

@@ -29,4 +29,9 @@ hipError_t cgemm_f32(int M, int N, int K, const float *Up, const float *Um, int 
 hipError_t gemm_bf16_nt(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,
                         int ldc, bool c_bf16, hipStream_t stream);
 
+// Split-K form of gemm_bf16_nt with fp32 output: slice z of C (at C + z *
+// split_stride) holds the product over the z-th K range.  K % 32 == 0.
+hipError_t gemm_bf16_nt_splitk(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B, int ldb, float *C,
+                               int ldc, int splits, int64_t split_stride, hipStream_t stream);
+
 }  // namespace egnn

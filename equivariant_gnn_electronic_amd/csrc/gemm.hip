@@ -477,7 +477,8 @@ template <int BM, int BN, int BK, int WM, int WN, int S, int U, bool CBF16>
 __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, int N, int K,
                                                                       const uint16_t *__restrict__ A, int lda,
                                                                       const uint16_t *__restrict__ B, int ldb,
-                                                                      void *__restrict__ C, int ldc) {
+                                                                      void *__restrict__ C, int ldc, int splits,
+                                                                      int k_per_split, int64_t split_stride) {
   constexpr int NW = WM * WN, CPR = BK / 8;
   static_assert(S >= 2 && S <= 4, "stages");
   __shared__ uint16_t A0[BM * BK], A1[BM * BK], A2[S > 2 ? BM * BK : 8], A3[S > 3 ? BM * BK : 8];
@@ -495,8 +496,12 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, i
     else return B3;
   };
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n, 1);
+  const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n, splits);
   if (!tm.valid) return;
+  // split-K: this block's K range; its partial product goes to slice z of C
+  const int k_begin = tm.z * k_per_split;
+  const int k_len = max(0, min(K, k_begin + k_per_split) - k_begin);
+  C = static_cast<char *>(C) + tm.z * split_stride * (CBF16 ? 2 : 4);
   const int row0 = tm.mt * BM, col0 = tm.nt * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
@@ -511,13 +516,13 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, i
 #pragma unroll
   for (int h = 0; h < LA; ++h) {
     const int slot0 = (h * NW + wave) * 64, sl = slot0 + lane, r = sl / CPR;
-    ga[h] = A + static_cast<int64_t>(min(row0 + r, M - 1)) * lda + ((sl % CPR) ^ chunk_swizzle<CPR>(r)) * 8;
+    ga[h] = A + static_cast<int64_t>(min(row0 + r, M - 1)) * lda + k_begin + ((sl % CPR) ^ chunk_swizzle<CPR>(r)) * 8;
     la[h] = slot0 * 8;
   }
 #pragma unroll
   for (int h = 0; h < LB; ++h) {
     const int slot0 = (h * NW + wave) * 64, sl = slot0 + lane, r = sl / CPR;
-    gb[h] = B + static_cast<int64_t>(min(col0 + r, N - 1)) * ldb + ((sl % CPR) ^ chunk_swizzle<CPR>(r)) * 8;
+    gb[h] = B + static_cast<int64_t>(min(col0 + r, N - 1)) * ldb + k_begin + ((sl % CPR) ^ chunk_swizzle<CPR>(r)) * 8;
     lb[h] = slot0 * 8;
   }
   auto issue = [&](auto st, int kt) {
@@ -559,7 +564,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, i
     }
   };
   constexpr int L = LA + LB;  // direct loads per K-tile per wave
-  const int nk = K / BK;
+  const int nk = k_len / BK;
   // prologue: K-tiles 0 .. S-2 in flight, wait for tile 0
   static_for<0, S - 1>([&](auto st) {
     if (decltype(st)::value < nk) issue(st, decltype(st)::value);
@@ -690,28 +695,39 @@ hipError_t cgemm_f32(int M, int N, int K, const float *Up, const float *Um, int 
   return hipGetLastError();
 }
 
-hipError_t gemm_bf16_nt(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C, int ldc,
-                        bool c_bf16, hipStream_t stream) {
+namespace {
+
+hipError_t launch_bf16(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C, int ldc,
+                       bool c_bf16, int splits, int64_t split_stride, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0) return hipErrorInvalidValue;
   const bool aligned = (reinterpret_cast<uintptr_t>(A) % 16 == 0) && (reinterpret_cast<uintptr_t>(B) % 16 == 0);
   const int waste256 = (N + 255) / 256 * 256 - N, waste128 = (N + 127) / 128 * 128 - N;
   const int tiles_m = (M + 255) / 256;
+  // K per split: a multiple of the K tile
+  auto kps_for = [&](int bk) { return ((K + splits - 1) / splits + bk - 1) / bk * bk; };
   if (aligned && K % 64 == 0 && (waste128 < waste256 || K % 32 != 0)) {
     // 256 x 128 x 64, 8 waves (4 x 2, 64 x 64 each), 3 stages (144 KB LDS)
-    const int grid = tile_grid(tiles_m * ((N + 127) / 128), 1);
+    const int grid = tile_grid(tiles_m * ((N + 127) / 128), splits);
+    const int kps = kps_for(64);
     if (c_bf16)
-      gemm_bf16_lds_kernel<256, 128, 64, 4, 2, 3, 1, true><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+      gemm_bf16_lds_kernel<256, 128, 64, 4, 2, 3, 1, true>
+          <<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
     else
-      gemm_bf16_lds_kernel<256, 128, 64, 4, 2, 3, 1, false><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+      gemm_bf16_lds_kernel<256, 128, 64, 4, 2, 3, 1, false>
+          <<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
   } else if (aligned && K % 32 == 0) {
     // 256 x 256 x 32, 8 waves (2 x 4, 128 x 64 each), 4 stages (128 KB LDS), loop body of 4 rings
-    const int grid = tile_grid(tiles_m * ((N + 255) / 256), 1);
+    const int grid = tile_grid(tiles_m * ((N + 255) / 256), splits);
+    const int kps = kps_for(32);
     if (c_bf16)
-      gemm_bf16_lds_kernel<256, 256, 32, 2, 4, 4, 4, true><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+      gemm_bf16_lds_kernel<256, 256, 32, 2, 4, 4, 4, true>
+          <<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
     else
-      gemm_bf16_lds_kernel<256, 256, 32, 2, 4, 4, 4, false><<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
+      gemm_bf16_lds_kernel<256, 256, 32, 2, 4, 4, 4, false>
+          <<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
   } else {
+    if (splits != 1) return hipErrorInvalidValue;
     const int tiles = ((M + HBM_ - 1) / HBM_) * ((N + HBN - 1) / HBN);
     const int grid = tile_grid(tiles, 1);
     if (c_bf16)
@@ -720,6 +736,20 @@ hipError_t gemm_bf16_nt(int M, int N, int K, const uint16_t *A, int lda, const u
       gemm_bf16_kernel<false><<<grid, 256, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t gemm_bf16_nt(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C, int ldc,
+                        bool c_bf16, hipStream_t stream) {
+  return launch_bf16(M, N, K, A, lda, B, ldb, C, ldc, c_bf16, 1, 0, stream);
+}
+
+hipError_t gemm_bf16_nt_splitk(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B, int ldb, float *C,
+                               int ldc, int splits, int64_t split_stride, hipStream_t stream) {
+  if (splits < 1) splits = 1;
+  if (K % 32 != 0) return hipErrorInvalidValue;
+  return launch_bf16(M, N, K, A, lda, B, ldb, C, ldc, false, splits, split_stride, stream);
 }
 
 }  // namespace egnn

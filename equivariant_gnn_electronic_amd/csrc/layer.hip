@@ -114,6 +114,76 @@ __global__ void to_bf16_kernel(const float *in, int64_t n, uint16_t *out) {
   if (i < n) out[i] = f32_to_bf16(in[i]);
 }
 
+// bf16 backward helpers.
+// BT[k][n] = B[n][k] in bf16, the second operand of dX = dY B as a product
+// with both operands contiguous along its sum (n).  cplx: B is the expanded
+// [[W1, -W2], [W2, W1]] of W1, W2 [rows][cols]; else B = W0 [rows][cols].
+__global__ void expand_weights_t_kernel(const float *w1, const float *w2, int rows, int cols, bool cplx,
+                                        uint16_t *BT) {
+  const int R = cplx ? 2 * rows : rows, Cc = cplx ? 2 * cols : cols;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(R) * Cc) return;
+  const int k = static_cast<int>(i / R), n = static_cast<int>(i % R);
+  float v;
+  if (!cplx) {
+    v = w1[static_cast<int64_t>(n) * cols + k];
+  } else {
+    const int so = n / rows, no = n % rows, si = k / cols, ki = k % cols;
+    const int64_t o = static_cast<int64_t>(no) * cols + ki;
+    v = (so == si) ? w1[o] : (so == 0 ? -w2[o] : w2[o]);
+  }
+  BT[i] = f32_to_bf16(v);
+}
+
+// out[c][r] = in[r][c] (bf16) for r < R and 0 for R <= r < R_pad, in: R rows
+// of Cc bf16 values with row stride ld_in (a multiple of 8), Cc a multiple of
+// 8, R_pad a multiple of 64.  A 64 x 64 tile moves in 16-byte pieces on both
+// sides: each thread loads 8 consecutive columns of a row, scatters them into
+// an LDS tile stored column-major, then reads 8 consecutive rows of a column
+// and writes them as one 16-byte store.  Puts the edge index innermost for the
+// weight-gradient products, which sum over edges.
+__global__ void __launch_bounds__(256) transpose_bf16_kernel(const uint16_t *__restrict__ in, int64_t R, int Cc,
+                                                             int ld_in, int64_t R_pad, uint16_t *__restrict__ out) {
+  constexpr int TLD = 72;  // tile column of 64 rows + 8 (keeps 16-byte alignment)
+  __shared__ __align__(16) uint16_t tile[64 * TLD];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int c0 = blockIdx.y * 64;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int rr = (t >> 3) + 32 * h, cc = (t & 7) * 8;
+    const int64_t r = r0 + rr;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < R && c0 + cc < Cc) v = *reinterpret_cast<const uint4 *>(in + r * ld_in + c0 + cc);
+    uint16_t e[8];
+    memcpy(e, &v, sizeof(v));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[(cc + j) * TLD + rr] = e[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int cc = (t >> 3) + 32 * h, rr = (t & 7) * 8;
+    const int c = c0 + cc;
+    if (c < Cc && r0 + rr < R_pad)
+      *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(c) * R_pad + r0 + rr) =
+          *reinterpret_cast<const uint4 *>(&tile[cc * TLD + rr]);
+  }
+}
+
+// dW1 = dB(+,+) + dB(-,-) and dW2 = dB(-,+) - dB(+,-) from the gradient dB
+// [2 rows][2 cols] of the expanded matrix (the inverse of the expansion).
+__global__ void fold_expanded_kernel(const float *dB, int rows, int cols, float *dw1, float *dw2) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(rows) * cols) return;
+  const int n = static_cast<int>(i / cols), k = static_cast<int>(i % cols);
+  const int64_t ld = 2 * static_cast<int64_t>(cols);
+  const float pp = dB[n * ld + k], pm = dB[n * ld + cols + k];
+  const float mp = dB[(rows + n) * ld + k], mm = dB[(rows + n) * ld + cols + k];
+  dw1[i] = pp + mm;
+  dw2[i] = mp - pm;
+}
+
 // --------------------------------------------------------------- forward --
 // Node-centric edge work.  Every edge's message has a source half (slots
 // 0..C-1) and a destination half (slots C..2C-1).  A wave owns one
@@ -435,7 +505,7 @@ __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restri
 // w_att partial of the row = sum_e da_e SiLU(Y_e[0,0]).
 // One wave per row; lanes = channels (CPL per lane), geometry rows staged in
 // LDS in batches as in the forward aggregate.
-template <int LMAX, int MMAX, int CPL>
+template <int LMAX, int MMAX, int CPL, typename TY, typename TD>
 __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict__ row_ptr, int n_dst,
                                                            const float *__restrict__ geom, int gstride,
                                                            const float *__restrict__ alpha, CPtr3 Y, int C,
@@ -491,9 +561,9 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
 #pragma unroll
           for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
             const int mu = cabs(m);
-            const float *row = static_cast<const float *>(Y.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
+            const TY *row = static_cast<const TY *>(Y.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
             // gd is 0 on clamped lanes, so T is too
-            p += row[static_cast<uint32_t>(L::col(l, m) * C + cl[t])] * T[L::kidx(l, m)];
+            p += Store<TY>::ld(row + static_cast<uint32_t>(L::col(l, m) * C + cl[t])) * T[L::kidx(l, m)];
           }
       }
       p = wave_sum(p);
@@ -518,7 +588,7 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
         const int c = lane + kWave * t;
         float T[L::KEPT];
         edge_T(gr, t, T);
-        const float y00 = static_cast<const float *>(Y.p[0])[static_cast<int64_t>(e) * L::blocks(0) * C + cl[t]];
+        const float y00 = Store<TY>::ld(static_cast<const TY *>(Y.p[0]) + static_cast<int64_t>(e) * L::blocks(0) * C + cl[t]);
         const float wat = w_att[cl[t]];
 #pragma unroll
         for (int l = 0; l <= LMAX; ++l)
@@ -530,8 +600,8 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
               if (c < C) wacc[t] += da * silu(y00);
             }
             const int mu = cabs(m);
-            float *row = static_cast<float *>(dY.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
-            if (c < C) row[static_cast<uint32_t>(L::col(l, m) * C + c)] = v;
+            TD *row = static_cast<TD *>(dY.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
+            if (c < C) Store<TD>::st(row + static_cast<uint32_t>(L::col(l, m) * C + c), v);
           }
       }
     }
@@ -595,10 +665,10 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
 #pragma unroll
         for (int p = 0; p < L::NP; ++p) dg[p] = 0.0f;
         if (active) {
-          const float *rowp[MMAX + 1];  // wave-uniform row bases, 32-bit lane offsets
+          const T *rowp[MMAX + 1];  // wave-uniform row bases, 32-bit lane offsets; dA in the storage type
 #pragma unroll
           for (int mu = 0; mu <= MMAX; ++mu)
-            rowp[mu] = static_cast<const float *>(dA.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
+            rowp[mu] = static_cast<const T *>(dA.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
 #pragma unroll
           for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
@@ -606,7 +676,7 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
               float xt = 0.0f;
 #pragma unroll
               for (int mp = -l; mp <= l; ++mp) xt += gr[L::doff(l, m, mp)] * xv[l * l + l + mp];
-              const float dx = rowp[cabs(m)][static_cast<uint32_t>(L::col(l, m) * C2 + j)];
+              const float dx = Store<T>::ld(rowp[cabs(m)] + static_cast<uint32_t>(L::col(l, m) * C2 + j));
               dg[pair_index(cabs(m), l, LMAX)] += dx * xt;
             }
         }
@@ -629,12 +699,26 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
       if (k < n_rbf) part[((static_cast<int64_t>(stream) * n_rbf + k) * L::NP + p) * C2 + j] = acc[k][p];
 }
 
+// One channel of a gradient row, in two steps (load, then convert).  bf16:
+// the lane loads the aligned 32-bit word holding its channel pair and keeps
+// its half.
+template <typename T> struct RawOf { typedef uint32_t type; };
+template <> struct RawOf<float> { typedef float type; };
+__device__ inline float load_raw(const float *row, uint32_t off) { return row[off]; }
+__device__ inline uint32_t load_raw(const uint16_t *row, uint32_t off) {
+  return *reinterpret_cast<const uint32_t *>(row + (off & ~1u));
+}
+__device__ inline float from_raw(float v, uint32_t) { return v; }
+__device__ inline float from_raw(uint32_t v, uint32_t off) {
+  return __uint_as_float((off & 1u) ? (v & 0xFFFF0000u) : (v << 16));
+}
+
 // grad_x[n] = G[n] (owned rows) + sum over the node's incoming edges of
 // D_e^T (g_e * dX_e)[destination half] + sum over its outgoing edges of
 // D_e^T (g_e * dX_e)[source half], with dX the GEMM gradient of the gated
 // edge-frame input.  The waves of one node (two halves x channel chunks) sit
 // in one block and their partial sums are added through LDS in a fixed order.
-template <int LMAX, int MMAX, int NRBF>
+template <int LMAX, int MMAX, int NRBF, typename TdA>
 __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__restrict__ row_ptr,
                                                                const int *__restrict__ src_ptr,
                                                                const int *__restrict__ src_perm,
@@ -671,16 +755,25 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
         const int e = uniform(eids[wave][i]);
         const float *gr = gb + i * GS4 * 4;
         if (!active) continue;
-        const float *rowp[MMAX + 1];  // wave-uniform row bases, 32-bit lane offsets
+        const TdA *rowp[MMAX + 1];  // wave-uniform row bases, 32-bit lane offsets
 #pragma unroll
         for (int mu = 0; mu <= MMAX; ++mu)
-          rowp[mu] = static_cast<const float *>(dA.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
+          rowp[mu] = static_cast<const TdA *>(dA.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
+        // all of the edge's loads are issued before any is used (the barrier keeps
+        // the scheduler from pairing each load with its use)
+        typename RawOf<TdA>::type raw[L::KEPT];
+#pragma unroll
+        for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
+            raw[L::kidx(l, m)] = load_raw(rowp[cabs(m)], static_cast<uint32_t>(L::col(l, m) * C2 + j));
+        __builtin_amdgcn_sched_barrier(0);
         float dxt[L::KEPT];
 #pragma unroll
         for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
           for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
-            dxt[L::kidx(l, m)] = rowp[cabs(m)][static_cast<uint32_t>(L::col(l, m) * C2 + j)];
+            dxt[L::kidx(l, m)] = from_raw(raw[L::kidx(l, m)], static_cast<uint32_t>(L::col(l, m) * C2 + j));
         float g[L::NP];
 #pragma unroll
         for (int p = 0; p < L::NP; ++p) g[p] = 0.0f;
@@ -803,14 +896,21 @@ int dw_splits(int64_t E) {
 }
 
 struct BwdWs {
-  float *B[3];
-  float *dY[3];
-  float *dA[3];
+  float *B[3];       // fp32: V2, V3 of the conjugate complex product (m >= 1)
+  float *dY[3];      // fp32 storage
+  uint16_t *BT[3];   // bf16: transposed (expanded) weights of dX = dY B
+  uint16_t *dYb[3];  // bf16 storage: dY in bf16
+  float *dA[3];      // fp32 storage
+  uint16_t *dAb[3];  // bf16 storage: dA in bf16
   float *dalpha;
   float *watt_part;
-  float *P;        // split partials (real and imaginary parts for m >= 1)
+  float *P;          // split partials (real and imaginary parts for m >= 1)
   float *wrad_part;
+  uint16_t *dYT, *AT;  // bf16: dY_m^T and A_m^T [cols][E padded to 64], one |m| at a time
+  float *dWexp;        // bf16: summed gradient of the expanded weight of one |m|
 };
+
+int64_t pad64(int64_t E) { return (E + 63) / 64 * 64; }
 
 // node streams of the radial-weight gradient (fixed by the node count, so the
 // summation order of its partials is reproducible)
@@ -818,17 +918,34 @@ int wrad_streams(int n_src) { return n_src < 1024 ? (n_src > 0 ? n_src : 1) : 10
 
 BwdWs carve_bwd_ws(Carver &cv, const LayerShape &s, int64_t E, int n_dst, int n_src) {
   BwdWs w{};
-  size_t pmax = 0;
+  const bool bf = s.storage == EGNN_BF16;
+  size_t pmax = 0, kmax = 0, nmax = 0;
   for (int m = 0; m <= s.mmax; ++m) {
-    w.B[m] = m == 0 ? nullptr : cv.take<float>(static_cast<size_t>(s.Ng[m]) * s.Kg[m] / 2);
-    w.dY[m] = cv.take<float>(static_cast<size_t>(E) * s.Ng[m]);
-    w.dA[m] = cv.take<float>(static_cast<size_t>(E) * s.Kg[m]);
-    pmax = pmax > static_cast<size_t>(s.Ng[m]) * s.Kg[m] ? pmax : static_cast<size_t>(s.Ng[m]) * s.Kg[m];
+    const size_t ng = s.Ng[m], kg = s.Kg[m];
+    if (bf) {
+      w.BT[m] = cv.take<uint16_t>(ng * kg);
+      w.dYb[m] = cv.take<uint16_t>(static_cast<size_t>(E) * ng);
+    } else {
+      w.B[m] = m == 0 ? nullptr : cv.take<float>(ng * kg / 2);
+      w.dY[m] = cv.take<float>(static_cast<size_t>(E) * ng);
+    }
+    if (bf)
+      w.dAb[m] = cv.take<uint16_t>(static_cast<size_t>(E) * kg);
+    else
+      w.dA[m] = cv.take<float>(static_cast<size_t>(E) * kg);
+    pmax = pmax > ng * kg ? pmax : ng * kg;
+    kmax = kmax > kg ? kmax : kg;
+    nmax = nmax > ng ? nmax : ng;
   }
   w.dalpha = cv.take<float>(E);
   w.watt_part = cv.take<float>(static_cast<size_t>(n_dst > 0 ? n_dst : 1) * s.C);
   w.P = cv.take<float>(pmax * dw_splits(E));
   w.wrad_part = cv.take<float>(static_cast<size_t>(wrad_streams(n_src)) * s.n_rbf * s.n_pairs * 2 * s.C);
+  if (bf) {
+    w.dYT = cv.take<uint16_t>(nmax * pad64(E));
+    w.AT = cv.take<uint16_t>(kmax * pad64(E));
+    w.dWexp = cv.take<float>(pmax);
+  }
   return w;
 }
 
@@ -880,48 +997,76 @@ struct Launch {
     aggregate_kernel<LMAX, MMAX, T><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, s.nD + s.n_rbf,
                                                                a.alpha, Y, s.C, x, x_out, edge_out);
   }
-  static void bwd_row(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const float *G,
-                      const float *w_att, const BwdWs &w, hipStream_t st) {
+  template <typename TY>
+  static void bwd_row_t(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const float *G,
+                        const float *w_att, const BwdWs &w, hipStream_t st) {
     CPtr3 Y{{a.Y[0], a.Y[1], a.Y[2]}};
-    Ptr3 dY{{w.dY[0], w.dY[1], w.dY[2]}};
+    constexpr bool bf = std::is_same<TY, uint16_t>::value;
+    Ptr3 dY = bf ? Ptr3{{w.dYb[0], w.dYb[1], w.dYb[2]}} : Ptr3{{w.dY[0], w.dY[1], w.dY[2]}};
     const unsigned grid = ceil_div(g->n_dst, kWavesPerBlock);
     if (s.C <= 64)
-      bwd_row_kernel<LMAX, MMAX, 1><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C,
-                                                               G, w_att, dY, w.dalpha, w.watt_part);
+      bwd_row_kernel<LMAX, MMAX, 1, TY, TY><<<grid, kThreads, 0, st>>>(
+          g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C, G, w_att, dY, w.dalpha, w.watt_part);
     else if (s.C <= 128)
-      bwd_row_kernel<LMAX, MMAX, 2><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C,
-                                                               G, w_att, dY, w.dalpha, w.watt_part);
+      bwd_row_kernel<LMAX, MMAX, 2, TY, TY><<<grid, kThreads, 0, st>>>(
+          g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C, G, w_att, dY, w.dalpha, w.watt_part);
     else
-      bwd_row_kernel<LMAX, MMAX, 4><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C,
-                                                               G, w_att, dY, w.dalpha, w.watt_part);
+      bwd_row_kernel<LMAX, MMAX, 4, TY, TY><<<grid, kThreads, 0, st>>>(
+          g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C, G, w_att, dY, w.dalpha, w.watt_part);
   }
-  static void bwd_gate(const egnn_graph *g, const LayerShape &s, const float *geom, const float *x, const float *wrad,
-                       const BwdWs &w, hipStream_t st) {
-    (void)wrad;
-    CPtr3 dA{{w.dA[0], w.dA[1], w.dA[2]}};
+  // dY is written in the storage type (bf16 feeds the bf16 GEMMs directly)
+  static void bwd_row(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const float *G,
+                      const float *w_att, const BwdWs &w, hipStream_t st) {
+    if (s.storage == EGNN_BF16)
+      bwd_row_t<uint16_t>(g, s, geom, a, G, w_att, w, st);
+    else
+      bwd_row_t<float>(g, s, geom, a, G, w_att, w, st);
+  }
+  template <typename T>
+  static void bwd_gate_t(const egnn_graph *g, const LayerShape &s, const float *geom, const T *x, const BwdWs &w,
+                         hipStream_t st) {
+    constexpr bool bf = std::is_same<T, uint16_t>::value;
+    CPtr3 dA = bf ? CPtr3{{w.dAb[0], w.dAb[1], w.dAb[2]}} : CPtr3{{w.dA[0], w.dA[1], w.dA[2]}};
     const int nch = (s.C + kWave - 1) / kWave;
     const int ns = wrad_streams(g->n_src);
     const unsigned grid = ceil_div(static_cast<int64_t>(ns) * 2 * nch, kWavesPerBlock);
     if (s.n_rbf <= 8)
-      wrad_grad_kernel<LMAX, MMAX, 8, float><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom,
-                                                                        s.gstride, g->n_dst, g->n_src, x, s.C, s.n_rbf,
-                                                                        dA, ns, w.wrad_part);
+      wrad_grad_kernel<LMAX, MMAX, 8, T><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom,
+                                                                    s.gstride, g->n_dst, g->n_src, x, s.C, s.n_rbf,
+                                                                    dA, ns, w.wrad_part);
     else
-      wrad_grad_kernel<LMAX, MMAX, 16, float><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom,
-                                                                         s.gstride, g->n_dst, g->n_src, x, s.C, s.n_rbf,
-                                                                         dA, ns, w.wrad_part);
+      wrad_grad_kernel<LMAX, MMAX, 16, T><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom,
+                                                                     s.gstride, g->n_dst, g->n_src, x, s.C, s.n_rbf,
+                                                                     dA, ns, w.wrad_part);
   }
-  static void bwd_node(const egnn_graph *g, const LayerShape &s, const float *geom, const float *G, const float *wrad,
-                       const BwdWs &w, float *gx, hipStream_t st) {
-    CPtr3 dA{{w.dA[0], w.dA[1], w.dA[2]}};
+  static void bwd_gate(const egnn_graph *g, const LayerShape &s, const float *geom, const void *x, const float *wrad,
+                       const BwdWs &w, hipStream_t st) {
+    (void)wrad;
+    if (s.storage == EGNN_BF16)
+      bwd_gate_t<uint16_t>(g, s, geom, static_cast<const uint16_t *>(x), w, st);
+    else
+      bwd_gate_t<float>(g, s, geom, static_cast<const float *>(x), w, st);
+  }
+  template <typename TdA>
+  static void bwd_node_t(const egnn_graph *g, const LayerShape &s, const float *geom, const float *G,
+                         const float *wrad, CPtr3 dA, float *gx, hipStream_t st) {
     const int nch = (s.C + kWave - 1) / kWave;
     const unsigned grid = ceil_div(static_cast<int64_t>(g->n_src) * 2 * nch, kWavesPerBlock);
     if (s.n_rbf <= 8)
-      gather_grad_kernel<LMAX, MMAX, 8><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride,
-                                                                   g->n_dst, g->n_src, s.C, wrad, s.n_rbf, dA, G, gx);
+      gather_grad_kernel<LMAX, MMAX, 8, TdA><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom,
+                                                                        s.gstride, g->n_dst, g->n_src, s.C, wrad,
+                                                                        s.n_rbf, dA, G, gx);
     else
-      gather_grad_kernel<LMAX, MMAX, 16><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride,
-                                                                    g->n_dst, g->n_src, s.C, wrad, s.n_rbf, dA, G, gx);
+      gather_grad_kernel<LMAX, MMAX, 16, TdA><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom,
+                                                                         s.gstride, g->n_dst, g->n_src, s.C, wrad,
+                                                                         s.n_rbf, dA, G, gx);
+  }
+  static void bwd_node(const egnn_graph *g, const LayerShape &s, const float *geom, const float *G, const float *wrad,
+                       const BwdWs &w, float *gx, hipStream_t st) {
+    if (s.storage == EGNN_BF16)
+      bwd_node_t<uint16_t>(g, s, geom, G, wrad, CPtr3{{w.dAb[0], w.dAb[1], w.dAb[2]}}, gx, st);
+    else
+      bwd_node_t<float>(g, s, geom, G, wrad, CPtr3{{w.dA[0], w.dA[1], w.dA[2]}}, gx, st);
   }
 };
 
@@ -959,7 +1104,7 @@ void bwd_row_launch(const egnn_graph *g, const LayerShape &s, const float *geom,
   Launch<LMAX, MMAX>::bwd_row(g, s, geom, a, G, w_att, w, st);
 }
 template <int LMAX, int MMAX>
-void bwd_gate_launch(const egnn_graph *g, const LayerShape &s, const float *geom, const float *x, const float *wrad,
+void bwd_gate_launch(const egnn_graph *g, const LayerShape &s, const float *geom, const void *x, const float *wrad,
                      const BwdWs &w, hipStream_t st) {
   Launch<LMAX, MMAX>::bwd_gate(g, s, geom, x, wrad, w, st);
 }
@@ -1146,10 +1291,6 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
   EGNN_REQUIRE(make_shape(d, &s), "invalid layer description");
   egnn_status st = check_graph(g);
   if (st != EGNN_OK) return st;
-  if (s.storage != EGNN_F32) {
-    set_error("the backward pass supports fp32 storage only");
-    return EGNN_E_UNSUPPORTED;
-  }
   if (s.C > 128) {
     set_error("the backward pass supports C <= 128");
     return EGNN_E_UNSUPPORTED;
@@ -1168,13 +1309,24 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
   }
   const WOff wo = weight_offsets(s);
   const int T = 256;
-  const float *x = static_cast<const float *>(x_in);
+  const bool bf = s.storage == EGNN_BF16;
   fill_f32<<<ceil_div(wo.total, T), T, 0, stream>>>(grad_weights, wo.total, 0.0f);
-  for (int m = 1; m <= s.mmax; ++m) {
-    // input gradient multiplies by conj(W): V+ = W1, V- = -W2, so V2 = -W1 - W2, V3 = W1 - W2
-    const int64_t nb = static_cast<int64_t>(s.Ng[m] / 2) * (s.Kg[m] / 2);
-    combo_weights_kernel<<<ceil_div(nb, T), T, 0, stream>>>(weights + wo.W1[m], weights + wo.W2[m], nb, -1.f, -1.f,
-                                                            1.f, -1.f, w.B[m], w.B[m] + nb);
+  for (int m = 0; m <= s.mmax; ++m) {
+    if (bf) {
+      // bf16: B_m^T (expanded for m >= 1) for dA_m = dY_m B_m
+      const int64_t n = static_cast<int64_t>(s.Ng[m]) * s.Kg[m];
+      if (m == 0)
+        expand_weights_t_kernel<<<ceil_div(n, T), T, 0, stream>>>(weights + wo.W0, nullptr, s.Ng[0], s.Kg[0], false,
+                                                                  w.BT[0]);
+      else
+        expand_weights_t_kernel<<<ceil_div(n, T), T, 0, stream>>>(weights + wo.W1[m], weights + wo.W2[m],
+                                                                  s.Ng[m] / 2, s.Kg[m] / 2, true, w.BT[m]);
+    } else if (m > 0) {
+      // input gradient multiplies by conj(W): V+ = W1, V- = -W2, so V2 = -W1 - W2, V3 = W1 - W2
+      const int64_t nb = static_cast<int64_t>(s.Ng[m] / 2) * (s.Kg[m] / 2);
+      combo_weights_kernel<<<ceil_div(nb, T), T, 0, stream>>>(weights + wo.W1[m], weights + wo.W2[m], nb, -1.f, -1.f,
+                                                              1.f, -1.f, w.B[m], w.B[m] + nb);
+    }
   }
   double sumK = 0, sumN = 0;
   for (int m = 0; m <= s.mmax; ++m) {
@@ -1183,7 +1335,9 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
   }
   if (g->n_dst > 0 && E > 0) {
     {
-      const double bytes = double(g->n_dst) * s.K * s.C * 4.0 * 1.0 + double(E) * (2.0 * sumN * 4.0 + s.nD * 4.0 + 12.0) +
+      // G rows, Y read and dY written (storage type), D rows, alpha / dalpha, w_att partials
+      const double yb = bf ? 2.0 : 4.0;
+      const double bytes = double(g->n_dst) * s.K * s.C * 4.0 + double(E) * (2.0 * sumN * yb + s.nD * 4.0 + 12.0) +
                            double(g->n_dst) * s.C * 4.0;
       Timed t(stream, "bwd_row", 0.0, bytes);
       EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_row_launch, g, s, geom, acts, grad_out, weights + wo.watt, w, stream);
@@ -1191,7 +1345,53 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
     // w_att gradient: fixed-order sum of the per-row partials
     colsum_kernel<<<ceil_div(s.C, 64), 256, 0, stream>>>(w.watt_part, g->n_dst, s.C, s.C, grad_weights + wo.watt);
   }
-  if (E > 0) {
+  if (E > 0 && bf) {
+    // bf16 storage: both gradient products on bf16 MFMA, fp32 accumulate.
+    //   dA_m = dY_m B_m                 (dY in bf16 from bwd_row, B_m^T prepared above)
+    //   dB_m = sum_e dY_m[e]^T A_m[e]   (operands transposed so the edge index is
+    //                                    innermost; split over edges, summed in order)
+    // then dW_m1, dW_m2 folded out of dB_m for m >= 1.
+    const int splits = dw_splits(E);
+    const int64_t Ep = pad64(E);
+    for (int m = 0; m <= s.mmax; ++m) {
+      const int Ng = s.Ng[m], Kg = s.Kg[m];
+      hipError_t e;
+      {
+        Timed t(stream, "gemm_dx_bf16", 2.0 * double(E) * Ng * Kg, double(E) * (Ng + Kg) * 2.0);
+        e = gemm_bf16_nt(static_cast<int>(E), Kg, Ng, w.dYb[m], Ng, w.BT[m], Ng, w.dAb[m], Kg, true, stream);
+      }
+      if (e != hipSuccess) {
+        set_error("GEMM launch failed: %s", hipGetErrorString(e));
+        return EGNN_E_HIP;
+      }
+      {
+        Timed t(stream, "transpose_bf16", 0.0, double(E) * (Ng + Kg) * 2.0 + double(Ep) * (Ng + Kg) * 2.0);
+        const unsigned gx = static_cast<unsigned>(Ep / 64);
+        transpose_bf16_kernel<<<dim3(gx, ceil_div(Ng, 64)), 256, 0, stream>>>(w.dYb[m], E, Ng, Ng, Ep,
+                                                                                         w.dYT);
+        transpose_bf16_kernel<<<dim3(gx, ceil_div(Kg, 64)), 256, 0, stream>>>(
+            static_cast<const uint16_t *>(acts.A[m]), E, Kg, Kg, Ep, w.AT);
+      }
+      const int64_t pn = static_cast<int64_t>(Ng) * Kg;
+      {
+        Timed t(stream, "gemm_dw_bf16", 2.0 * double(E) * Ng * Kg, double(E) * (Ng + Kg) * 2.0 + double(splits) * pn * 4.0);
+        e = gemm_bf16_nt_splitk(Ng, Kg, static_cast<int>(Ep), w.dYT, static_cast<int>(Ep), w.AT, static_cast<int>(Ep),
+                                w.P, Kg, splits, pn, stream);
+      }
+      if (e != hipSuccess) {
+        set_error("GEMM launch failed: %s", hipGetErrorString(e));
+        return EGNN_E_HIP;
+      }
+      if (m == 0) {
+        colsum_kernel<<<ceil_div(pn, 64), 256, 0, stream>>>(w.P, splits, pn, pn, grad_weights + wo.W0);
+      } else {
+        colsum_kernel<<<ceil_div(pn, 64), 256, 0, stream>>>(w.P, splits, pn, pn, w.dWexp);
+        const int64_t nb = pn / 4;
+        fold_expanded_kernel<<<ceil_div(nb, T), T, 0, stream>>>(w.dWexp, Ng / 2, Kg / 2, grad_weights + wo.W1[m],
+                                                                grad_weights + wo.W2[m]);
+      }
+    }
+  } else if (E > 0) {
     const int splits = dw_splits(E);
     for (int m = 0; m <= s.mmax; ++m) {
       hipError_t e;
@@ -1249,13 +1449,16 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
       }
       colsum_kernel<<<ceil_div(pn, 64), 256, 0, stream>>>(w.P, splits, pn, pn, grad_weights + wo.W0);
     }
+  }
+  if (E > 0) {
     const int ncol = s.n_pairs * 2 * s.C;
     {
       // dA read once; the edge-frame input is recomputed from each node's own row
-      const double bytes = double(g->n_src) * s.K * s.C * 4.0 + double(E) * (s.nD + s.n_rbf + 1) * 4.0 + double(E) * 4.0 +
-                           double(E) * sumK * 4.0;
+      const double xb = bf ? 2.0 : 4.0;
+      const double bytes = double(g->n_src) * s.K * s.C * xb + double(E) * (s.nD + s.n_rbf + 1) * 4.0 + double(E) * 4.0 +
+                           double(E) * sumK * xb;
       Timed t(stream, "bwd_gate", 0.0, bytes);
-      EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_gate_launch, g, s, geom, x, weights + wo.wrad, w, stream);
+      EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_gate_launch, g, s, geom, x_in, weights + wo.wrad, w, stream);
     }
     const int64_t nw = static_cast<int64_t>(s.n_rbf) * ncol;
     const int ns = wrad_streams(g->n_src);
@@ -1270,7 +1473,7 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
         EGNN_TRY_HIP(hipMemcpyAsync(grad_x_in, grad_out, sizeof(float) * g->n_dst * s.K * s.C, hipMemcpyDeviceToDevice,
                                     stream));
     } else {
-      const double bytes = double(E) * (sumK * 4.0 + s.nD * 4.0 + 8.0) + double(g->n_dst) * s.K * s.C * 4.0 +
+      const double bytes = double(E) * (sumK * (bf ? 2.0 : 4.0) + s.nD * 4.0 + 8.0) + double(g->n_dst) * s.K * s.C * 4.0 +
                            double(g->n_src) * s.K * s.C * 4.0;
       Timed t(stream, "bwd_node", 0.0, bytes);
       EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_node_launch, g, s, geom, grad_out, weights + wo.wrad, w, grad_x_in, stream);

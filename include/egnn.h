@@ -194,7 +194,11 @@ egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph *g, const 
  *   grad_weights (fp32, packed like the weights, overwritten) = dL/dweights.
  * `saved` is what egnn_layer_fwd wrote for the same inputs; grad_out
  * [n_dst][K][C] fp32.  Reductions over edges run in a fixed order (no
- * floating-point atomics), so results are bit-identical between runs. */
+ * floating-point atomics), so results are bit-identical between runs.
+ * fp32 storage: every product in fp32 (MFMA).  bf16 storage: dL/dY is
+ * rounded to bf16 and both gradient products (input and weight) run on bf16
+ * MFMA with fp32 accumulation; x_in is the bf16 input; all gradients are fp32.
+ * C <= 128 (EGNN_E_UNSUPPORTED otherwise). */
 egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph *g, const float *geom,
                            const float *weights, const void *x_in, const void *saved,
                            const float *grad_out, float *grad_x_in, float *grad_weights,

@@ -130,9 +130,9 @@ def test_graph_argument_checks(lib):
     assert st == _lib.EGNN_E_WORKSPACE
 
 
-def test_backward_rejects_unsupported_storage(lib):
+def test_backward_rejects_unsupported_width(lib):
     from equivariant_gnn_electronic_amd import _lib
-    d = _desc(4, 2, 64, storage=1)
+    d = _desc(4, 2, 256, storage=1)  # the backward handles C <= 128
     g = _fake_graph(10, 10, 100)
     p = ct.c_void_p(0x1000)
     st = lib.egnn_layer_bwd(ct.byref(d), ct.byref(g), p, p, p, p, p, p, p, p, 1 << 30, None)

@@ -352,3 +352,54 @@ def test_hblocks_hfo2_sampled_edges(dev):
     ef = olayer.edge_forward(og, r["x"].astype(np.float64), olayer.unpack_weights(r["w"].astype(np.float64), desc_of(cfg)),
                              desc_of(cfg), r["x"][np.repeat(rows, np.diff(og["row_ptr"]))].astype(np.float64))
     assert_close(r["eo"][torch.from_numpy(sel).to(dev)].cpu().numpy(), ef["msg"], 1e-4, "edge messages")
+
+
+def _sampled_atom_grads(cfg, r, dev, n_nodes, seed, tol):
+    s = r["s"]
+    G = synth.make_cotangent(cfg, s.n_dst)
+    gx, _ = eg.egnn_layer_bwd(r["desc"], r["g"], r["geom"], r["wt"], r["xt"], r["buf"], torch.from_numpy(G).to(dev))
+    torch.cuda.synchronize()
+    gx = gx.cpu().numpy()
+    gg = host(r["g"])
+    dst = np.repeat(np.arange(s.n_dst), np.diff(gg["row_ptr"]))
+    nodes = sample_rows(s.n_dst, n_nodes, seed)
+    rows = np.unique(np.concatenate([nodes, dst[np.isin(gg["src"], nodes)]]))
+    perm, og = _relabelled_rows(s, rows)
+    x64, w64 = r["x"][perm].astype(np.float64), r["w"].astype(np.float64)
+    fwd = olayer.layer_forward(og, x64, w64, desc_of(cfg))
+    dx, _ = olayer.layer_backward(og, x64, w64, desc_of(cfg), fwd, G[rows].astype(np.float64))
+    assert_close(gx[nodes], dx[np.searchsorted(rows, nodes)], tol, "grad x of sampled atoms")
+
+
+def test_layer_backward_gst_bf16_sampled_nodes(dev):
+    """Backward of the 8,064-atom GeSbTe-like layer with bf16 storage (C 128,
+    1.1M edges): exact oracle gradients of sampled atoms, bf16 tolerance."""
+    cfg = synth.CONFIGS["gst"]
+    r = _gpu_forward(cfg, dev, train=True)
+    _sampled_atom_grads(cfg, r, dev, 2, 23, 2e-2)
+
+
+def test_weight_gradient_gst_bf16_directional(dev):
+    """bf16-storage weight gradient at full GST size (1.1M edges, C 128) against
+    the central difference of L(W) = <G, x'(W)> along a random direction.  L is
+    evaluated by the fp32-storage forward on the same (bf16-exact) inputs: the
+    bf16 forward rounds every activation, which makes its own differences too
+    rough, and the bf16 backward approximates this smooth L's gradient."""
+    cfg = synth.CONFIGS["gst"]
+    r = _gpu_forward(cfg, dev, train=True)
+    G = synth.make_cotangent(cfg, r["s"].n_dst)
+    Gt = torch.from_numpy(G).to(dev)
+    _, gw = eg.egnn_layer_bwd(r["desc"], r["g"], r["geom"], r["wt"], r["xt"], r["buf"], Gt)
+    d32 = eg.layer_desc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut, eg.EGNN_F32)
+    x32 = r["xt"].float()
+    v = torch.from_numpy(np.random.default_rng(4).standard_normal(r["w"].size).astype(np.float32)).to(dev)
+    v *= r["wt"].norm() / v.norm()
+    eps = 1e-3
+
+    def loss(w):
+        (xo, _), _ = eg.egnn_layer_fwd(d32, r["g"], r["geom"], w, x32)
+        return float((xo.double() * Gt.double()).sum())
+
+    fd = (loss(r["wt"] + eps * v) - loss(r["wt"] - eps * v)) / (2 * eps)
+    an = float((gw.double() * v.double()).sum())
+    assert abs(fd - an) <= 2e-2 * abs(an), (fd, an)
