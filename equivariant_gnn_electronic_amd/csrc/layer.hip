@@ -250,11 +250,17 @@ __device__ inline void stage_geom(const EdgeList &el, int base, int cnt, const f
 template <int LMAX, int MMAX, int NRBF>
 __device__ inline void load_wrad(const float *wrad, int n_rbf, int C2, int j, bool active, float (&wr)[NRBF][pair_count(LMAX, MMAX)]) {
   constexpr int NP = pair_count(LMAX, MMAX);
+  // unused slots read basis 0 / column 0 and are zeroed after: no branch per load
+  const int jc = active ? j : 0;
+  float v[NRBF][NP];
 #pragma unroll
   for (int k = 0; k < NRBF; ++k)
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
-      wr[k][p] = (active && k < n_rbf) ? wrad[(static_cast<int64_t>(k) * NP + p) * C2 + j] : 0.0f;
+    for (int p = 0; p < NP; ++p) v[k][p] = wrad[(static_cast<int64_t>(k < n_rbf ? k : 0) * NP + p) * C2 + jc];
+#pragma unroll
+  for (int k = 0; k < NRBF; ++k)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) wr[k][p] = (active && k < n_rbf) ? v[k][p] : 0.0f;
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -267,15 +273,24 @@ template <int LMAX, int MMAX, int NRBF>
 __device__ inline void load_wrad_bf16(const float *wrad, int n_rbf, int C2, int j, bool active,
                                       bf16x2 (&wr)[NRBF / 2][pair_count(LMAX, MMAX)]) {
   constexpr int NP = pair_count(LMAX, MMAX);
+  float v[NRBF][NP];
+  load_wrad<LMAX, MMAX, NRBF>(wrad, n_rbf, C2, j, active, v);
 #pragma unroll
   for (int q = 0; q < NRBF / 2; ++q)
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int k0 = 2 * q, k1 = 2 * q + 1;
-      const float w0 = (active && k0 < n_rbf) ? wrad[(static_cast<int64_t>(k0) * NP + p) * C2 + j] : 0.0f;
-      const float w1 = (active && k1 < n_rbf) ? wrad[(static_cast<int64_t>(k1) * NP + p) * C2 + j] : 0.0f;
-      wr[q][p] = bf16x2{static_cast<__bf16>(w0), static_cast<__bf16>(w1)};
-    }
+    for (int p = 0; p < NP; ++p) wr[q][p] = bf16x2{static_cast<__bf16>(v[2 * q][p]), static_cast<__bf16>(v[2 * q + 1][p])};
+}
+
+// The K entries of one channel of a node row.  Inactive lanes read channel 0
+// and discard it, so the loads carry no branch and issue back to back.
+template <int K, typename T>
+__device__ inline void load_node_row(const T *__restrict__ x, int node, int C, int c, bool active, float (&xv)[K]) {
+  const T *row = x + static_cast<int64_t>(node) * K * C + (active ? c : 0);
+  float v[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) v[k] = Store<T>::ld(row + static_cast<uint32_t>(k * C));
+#pragma unroll
+  for (int k = 0; k < K; ++k) xv[k] = active ? v[k] : 0.0f;
 }
 
 // A[e] = g_e * trunc(D_e x) for the wave's half of every edge of its node.
@@ -302,8 +317,7 @@ __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restr
   const bool active = c < C;
   const int j = nw.half * C + c;
   float xv[L::K];
-#pragma unroll
-  for (int k = 0; k < L::K; ++k) xv[k] = active ? Store<T>::ld(x + (static_cast<int64_t>(nw.node) * L::K + k) * C + c) : 0.0f;
+  load_node_row<L::K>(x, nw.node, C, c, active, xv);
   // fp32 storage: fp32 radial weights; bf16 storage: bf16 pairs (see load_wrad_bf16)
   constexpr bool kPacked = std::is_same<TA, uint16_t>::value;
   float wr[kPacked ? 1 : NRBF][kPacked ? 1 : L::NP];
@@ -614,6 +628,20 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
   }
 }
 
+// One channel of a gradient row, in two steps (load, then convert).  bf16:
+// the lane loads the aligned 32-bit word holding its channel pair and keeps
+// its half.
+template <typename T> struct RawOf { typedef uint32_t type; };
+template <> struct RawOf<float> { typedef float type; };
+__device__ inline float load_raw(const float *row, uint32_t off) { return row[off]; }
+__device__ inline uint32_t load_raw(const uint16_t *row, uint32_t off) {
+  return *reinterpret_cast<const uint32_t *>(row + (off & ~1u));
+}
+__device__ inline float from_raw(float v, uint32_t) { return v; }
+__device__ inline float from_raw(uint32_t v, uint32_t off) {
+  return __uint_as_float((off & 1u) ? (v & 0xFFFF0000u) : (v << 16));
+}
+
 // Radial-weight gradient: dW_rad[k][p][j] = sum_e phi_e[k] dg_e[p][j] with
 // dg_e[p] = sum_{+-m} dX_e[l,+-m] * Xt_e[l,+-m] (Xt = edge-frame input before
 // the gate).  Node-centric waves as in scatter_in; wave (node, half, chunk)
@@ -653,8 +681,7 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
     const EdgeList el = edge_list(node, half, n_dst, row_ptr, src_ptr, src_perm);
     if (el.count == 0) continue;
     float xv[L::K];
-#pragma unroll
-    for (int k = 0; k < L::K; ++k) xv[k] = active ? Store<T>::ld(x + (static_cast<int64_t>(node) * L::K + k) * C + c) : 0.0f;
+    load_node_row<L::K>(x, node, C, c, active, xv);
     for (int base = 0; base < el.count; base += kBatch) {
       const int cnt = min(kBatch, el.count - base);
       stage_geom(el, base, cnt, geom, gstride, gs4, GS4, gbuf[wave], eids[wave]);
@@ -669,6 +696,14 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
 #pragma unroll
           for (int mu = 0; mu <= MMAX; ++mu)
             rowp[mu] = static_cast<const T *>(dA.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
+          // all of the edge's loads before any use (see load_raw)
+          typename RawOf<T>::type raw[L::KEPT];
+#pragma unroll
+          for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
+              raw[L::kidx(l, m)] = load_raw(rowp[cabs(m)], static_cast<uint32_t>(L::col(l, m) * C2 + j));
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
@@ -676,7 +711,7 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
               float xt = 0.0f;
 #pragma unroll
               for (int mp = -l; mp <= l; ++mp) xt += gr[L::doff(l, m, mp)] * xv[l * l + l + mp];
-              const float dx = Store<T>::ld(rowp[cabs(m)] + static_cast<uint32_t>(L::col(l, m) * C2 + j));
+              const float dx = from_raw(raw[L::kidx(l, m)], static_cast<uint32_t>(L::col(l, m) * C2 + j));
               dg[pair_index(cabs(m), l, LMAX)] += dx * xt;
             }
         }
@@ -697,20 +732,6 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
 #pragma unroll
     for (int p = 0; p < L::NP; ++p)
       if (k < n_rbf) part[((static_cast<int64_t>(stream) * n_rbf + k) * L::NP + p) * C2 + j] = acc[k][p];
-}
-
-// One channel of a gradient row, in two steps (load, then convert).  bf16:
-// the lane loads the aligned 32-bit word holding its channel pair and keeps
-// its half.
-template <typename T> struct RawOf { typedef uint32_t type; };
-template <> struct RawOf<float> { typedef float type; };
-__device__ inline float load_raw(const float *row, uint32_t off) { return row[off]; }
-__device__ inline uint32_t load_raw(const uint16_t *row, uint32_t off) {
-  return *reinterpret_cast<const uint32_t *>(row + (off & ~1u));
-}
-__device__ inline float from_raw(float v, uint32_t) { return v; }
-__device__ inline float from_raw(uint32_t v, uint32_t off) {
-  return __uint_as_float((off & 1u) ? (v & 0xFFFF0000u) : (v << 16));
 }
 
 // grad_x[n] = G[n] (owned rows) + sum over the node's incoming edges of
