@@ -434,13 +434,15 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(int M, int N, int K, 
 
 // bf16, large tiles, operands brought into LDS by the gfx950 direct loads
 // (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS
-// base + 16 * lane, with no register staging).  S stages form a ring, so
-// S - 1 K-tiles are in flight while one is multiplied; every stage is its
-// own LDS object, which lets the compiler's wait-count pass see that reads
-// of one stage do not depend on the loads still filling the others.  A
-// wave's 1 KB of each load covers whole rows of the tile, so rows cannot be
-// padded; instead the 16-byte chunks of a row are XOR-swizzled by the row
-// index, which makes the 32-row fragment reads conflict-free.
+// base + 16 * lane, with no register staging).  S stages form a ring: the
+// stage of K-tile i - 1 is refilled with tile i + S - 1 before tile i is
+// multiplied, so S - 1 K-tiles are in flight during each product.  Every
+// stage (its A tile, then its B tile) is its own LDS object, which lets the
+// compiler's wait-count pass see that reads of one stage do not depend on
+// the loads still filling the others.  A wave's 1 KB of each load covers
+// whole rows of the tile, so rows cannot be padded; instead the 16-byte
+// chunks of a row are XOR-swizzled by the row index, which makes the 32-row
+// fragment reads conflict-free.
 // Requires K % BK == 0, lda and ldb multiples of 8, 16-byte aligned bases.
 template <int I, int N, typename F>
 __device__ inline void static_for(F &&f) {
@@ -473,28 +475,37 @@ __device__ inline int chunk_swizzle(int row) {
   return CPR == 4 ? ((row >> 2) & 3) : ((row >> 1) & 7);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int S, int U, bool CBF16>
+// STAGED (bf16 output only): the MFMA operands are swapped so that a lane
+// holds four consecutive output columns of one row; after the main loop each
+// wave packs its tile to bf16 in its own slice of the (then idle) ring, rows
+// of 128 bytes with XOR-swizzled 16-byte chunks, and writes it back as
+// 16-byte stores that cover whole 128-byte lines.  Requires WTN = 64,
+// N % 8 == 0, ldc % 8 == 0 and a 16-byte aligned C.  Otherwise each lane
+// stores its accumulators one element at a time.
+template <int BM, int BN, int BK, int WM, int WN, int S, int U, bool CBF16, bool STAGED>
 __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, int N, int K,
                                                                       const uint16_t *__restrict__ A, int lda,
                                                                       const uint16_t *__restrict__ B, int ldb,
                                                                       void *__restrict__ C, int ldc, int splits,
                                                                       int k_per_split, int64_t split_stride) {
-  constexpr int NW = WM * WN, CPR = BK / 8;
+  constexpr int NW = WM * WN, CPR = BK / 8, ST = (BM + BN) * BK;
   static_assert(S >= 2 && S <= 4, "stages");
-  __shared__ uint16_t A0[BM * BK], A1[BM * BK], A2[S > 2 ? BM * BK : 8], A3[S > 3 ? BM * BK : 8];
-  __shared__ uint16_t B0[BN * BK], B1[BN * BK], B2[S > 2 ? BN * BK : 8], B3[S > 3 ? BN * BK : 8];
-  auto as = [&](auto st) -> uint16_t * {
-    if constexpr (decltype(st)::value == 0) return A0;
-    else if constexpr (decltype(st)::value == 1) return A1;
-    else if constexpr (decltype(st)::value == 2) return A2;
-    else return A3;
+  static_assert(!STAGED || CBF16, "staged epilogue writes bf16");
+  __shared__ uint16_t T0[ST], T1[ST], T2[S > 2 ? ST : 8], T3[S > 3 ? ST : 8];
+  // The wait-count pass has been seen to leave the first direct LDS load it
+  // meets in program order without a per-object record, after which every
+  // read of that load's stage waits for all loads in flight.  This load never
+  // runs (K > 0); it only takes that first place.
+  __shared__ __attribute__((aligned(1024))) uint32_t dma_anchor[256];
+  if (K < 0) __builtin_amdgcn_global_load_lds(static_cast<const void *>(A), static_cast<void *>(dma_anchor), 16, 0, 0);
+  auto ts = [&](auto st) -> uint16_t * {
+    if constexpr (decltype(st)::value == 0) return T0;
+    else if constexpr (decltype(st)::value == 1) return T1;
+    else if constexpr (decltype(st)::value == 2) return T2;
+    else return T3;
   };
-  auto bs = [&](auto st) -> uint16_t * {
-    if constexpr (decltype(st)::value == 0) return B0;
-    else if constexpr (decltype(st)::value == 1) return B1;
-    else if constexpr (decltype(st)::value == 2) return B2;
-    else return B3;
-  };
+  auto as = [&](auto st) -> uint16_t * { return ts(st); };
+  auto bs = [&](auto st) -> uint16_t * { return ts(st) + BM * BK; };
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n, splits);
   if (!tm.valid) return;
@@ -542,26 +553,44 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, i
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  auto compute = [&](auto st) {
+  auto load_frag = [&](auto st, int s, bf16x8(&a)[TM], bf16x8(&b)[TN]) {
+    const int c = s * 2 + fh;
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      bf16x8 a[TM], b[TN];
-      const int c = s * 2 + fh;
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm + 32 * i + fr;
+      a[i] = *reinterpret_cast<const bf16x8 *>(as(st) + r * BK + (c ^ chunk_swizzle<CPR>(r)) * 8);
+    }
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm + 32 * i + fr;
-        a[i] = *reinterpret_cast<const bf16x8 *>(as(st) + r * BK + (c ^ chunk_swizzle<CPR>(r)) * 8);
-      }
+    for (int j = 0; j < TN; ++j) {
+      const int r = wn + 32 * j + fr;
+      b[j] = *reinterpret_cast<const bf16x8 *>(bs(st) + r * BK + (c ^ chunk_swizzle<CPR>(r)) * 8);
+    }
+  };
+  auto mma = [&](bf16x8(&a)[TM], bf16x8(&b)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int r = wn + 32 * j + fr;
-        b[j] = *reinterpret_cast<const bf16x8 *>(bs(st) + r * BK + (c ^ chunk_swizzle<CPR>(r)) * 8);
+        if constexpr (STAGED)  // output tile transposed: lane = row, registers = columns
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
+  };
+  // one K-tile: the fragments of 16-wide k-step s + 1 are read while step s multiplies
+  auto compute = [&](auto st) {
+    bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
+    load_frag(st, 0, a0, b0);
+    static_for<0, BK / 16>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      if constexpr (s % 2 == 0) {
+        if constexpr (s + 1 < BK / 16) load_frag(st, s + 1, a1, b1);
+        mma(a0, b0);
+      } else {
+        if constexpr (s + 1 < BK / 16) load_frag(st, s + 1, a0, b0);
+        mma(a1, b1);
+      }
+    });
   };
   constexpr int L = LA + LB;  // direct loads per K-tile per wave
   const int nk = k_len / BK;
@@ -572,8 +601,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, i
   if (nk >= S - 1) wait_vmcnt<(S - 2) * L>();
   else wait_vmcnt<0>();
   barrier_no_fence();
-  // iteration i multiplies stage i % S, then refills the stage of tile i - 1
-  // (free since the last barrier) with tile i + S - 1, then waits for tile i + 1.
+  // iteration i refills the stage of tile i - 1 (free since the last barrier)
+  // with tile i + S - 1, multiplies stage i % S, then waits for tile i + 1.
   // The loop body is U rounds of the ring: at the loop head the compiler's
   // wait-count tracking merges both paths and waits for every load in flight,
   // so a longer body drains the pipeline less often.
@@ -582,33 +611,64 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, i
       constexpr int dd = decltype(du)::value % S;
       const int i = it + decltype(du)::value;
       if (i >= nk) return;
+      if (i + S - 1 < nk) issue(std::integral_constant<int, (dd + S - 1) % S>{}, i + S - 1);
       compute(std::integral_constant<int, dd>{});
-      if (i + S - 1 < nk) {
-        issue(std::integral_constant<int, (dd + S - 1) % S>{}, i + S - 1);
-        wait_vmcnt<(S - 2) * L>();
-      } else {
-        wait_vmcnt<0>();
-      }
+      if (i + S - 1 < nk) wait_vmcnt<(S - 2) * L>();
+      else wait_vmcnt<0>();
       barrier_no_fence();
     });
   }
+  if constexpr (STAGED) {
+    // every wave is past the last barrier, so the ring is free
+    static_assert(WTN == 64, "staging rows are 128 bytes");
+    constexpr int WB = WTM * WTN;  // elements per wave
+    static_assert(NW * WB <= S * ST, "staging fits in the ring");
+    const int off = wave * WB;
+    uint16_t *stg = off < ST ? T0 + off : off < 2 * ST ? T1 + (off - ST) : off < 3 * ST ? T2 + (off - 2 * ST)
+                                                                                           : T3 + (off - 3 * ST);
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) {
+      const int r = 32 * i + fr;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = col0 + wn + 32 * j + fr;
-      if (col >= N) continue;
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + wm + 32 * i + 8 * (r >> 2) + 4 * fh + (r & 3);
-        if (row >= M) continue;
-        const int64_t o = static_cast<int64_t>(row) * ldc + col;
-        if (CBF16)
-          static_cast<uint16_t *>(C)[o] = f32_to_bf16(acc[i][j][r]);
-        else
-          static_cast<float *>(C)[o] = acc[i][j][r];
-      }
+        for (int q = 0; q < 4; ++q) {
+          // columns 32j + 8q + 4fh .. +3 of row r: half of 16-byte chunk 4j + q
+          const int chunk = (4 * j + q) ^ (r & 7);
+          uint2 v;
+          v.x = uint32_t(f32_to_bf16(acc[i][j][4 * q])) | (uint32_t(f32_to_bf16(acc[i][j][4 * q + 1])) << 16);
+          v.y = uint32_t(f32_to_bf16(acc[i][j][4 * q + 2])) | (uint32_t(f32_to_bf16(acc[i][j][4 * q + 3])) << 16);
+          *reinterpret_cast<uint2 *>(stg + r * WTN + chunk * 8 + 4 * fh) = v;
+        }
     }
+    // the staged rows are this wave's own: LDS operations of one wave complete in order
+#pragma unroll
+    for (int t = 0; t < WB / 8 / 64; ++t) {
+      const int idx = t * 64 + lane, r = idx >> 3, c = idx & 7;
+      const uint4 v = *reinterpret_cast<const uint4 *>(stg + r * WTN + (c ^ (r & 7)) * 8);
+      const int row = row0 + wm + r, col = col0 + wn + 8 * c;
+      if (row < M && col < N)
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(C) + static_cast<int64_t>(row) * ldc + col) = v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = col0 + wn + 32 * j + fr;
+        if (col >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + wm + 32 * i + 8 * (r >> 2) + 4 * fh + (r & 3);
+          if (row >= M) continue;
+          const int64_t o = static_cast<int64_t>(row) * ldc + col;
+          if (CBF16)
+            static_cast<uint16_t *>(C)[o] = f32_to_bf16(acc[i][j][r]);
+          else
+            static_cast<float *>(C)[o] = acc[i][j][r];
+        }
+      }
+  }
 }
 
 }  // namespace
@@ -706,26 +766,32 @@ hipError_t launch_bf16(int M, int N, int K, const uint16_t *A, int lda, const ui
   const int tiles_m = (M + 255) / 256;
   // K per split: a multiple of the K tile
   auto kps_for = [&](int bk) { return ((K + splits - 1) / splits + bk - 1) / bk * bk; };
-  if (aligned && K % 64 == 0 && (waste128 < waste256 || K % 32 != 0)) {
-    // 256 x 128 x 64, 8 waves (4 x 2, 64 x 64 each), 3 stages (144 KB LDS)
-    const int grid = tile_grid(tiles_m * ((N + 127) / 128), splits);
-    const int kps = kps_for(64);
-    if (c_bf16)
-      gemm_bf16_lds_kernel<256, 128, 64, 4, 2, 3, 1, true>
-          <<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
-    else
-      gemm_bf16_lds_kernel<256, 128, 64, 4, 2, 3, 1, false>
-          <<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
+  // bf16 output written through LDS as 16-byte rows (see gemm_bf16_lds_kernel)
+  const bool staged = c_bf16 && N % 8 == 0 && ldc % 8 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0;
+#define EGNN_B(BM_, BN_, BK_, WM_, WN_, S_, U_)                                                                    \
+  do {                                                                                                          \
+    const int grid = tile_grid(tiles_m * ((N + BN_ - 1) / BN_), splits);                                        \
+    const int kps = kps_for(BK_);                                                                               \
+    if (staged)                                                                                                 \
+      gemm_bf16_lds_kernel<BM_, BN_, BK_, WM_, WN_, S_, U_, true, true>                                         \
+          <<<grid, 64 * WM_ * WN_, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);    \
+    else if (c_bf16)                                                                                            \
+      gemm_bf16_lds_kernel<BM_, BN_, BK_, WM_, WN_, S_, U_, true, false>                                        \
+          <<<grid, 64 * WM_ * WN_, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);    \
+    else                                                                                                        \
+      gemm_bf16_lds_kernel<BM_, BN_, BK_, WM_, WN_, S_, U_, false, false>                                       \
+          <<<grid, 64 * WM_ * WN_, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);    \
+  } while (0)
+  if (aligned && K % 64 == 0 && waste128 < waste256) {
+    // 256 x 128 x 64, 8 waves (4 x 2, 64 x 64 each), 3 stages (144 KB LDS): N = 640 and the like
+    EGNN_B(256, 128, 64, 4, 2, 3, 1);
+  } else if (aligned && K % 64 == 0) {
+    // 256 x 256 x 64, 8 waves (2 x 4, 128 x 64 each), 2 stages (128 KB LDS): 128-byte rows per load
+    EGNN_B(256, 256, 64, 2, 4, 2, 2);
   } else if (aligned && K % 32 == 0) {
-    // 256 x 256 x 32, 8 waves (2 x 4, 128 x 64 each), 4 stages (128 KB LDS), loop body of 4 rings
-    const int grid = tile_grid(tiles_m * ((N + 255) / 256), splits);
-    const int kps = kps_for(32);
-    if (c_bf16)
-      gemm_bf16_lds_kernel<256, 256, 32, 2, 4, 4, 4, true>
-          <<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
-    else
-      gemm_bf16_lds_kernel<256, 256, 32, 2, 4, 4, 4, false>
-          <<<grid, 512, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);
+    // 256 x 256 x 32, 4 stages (128 KB LDS), loop body of 4 rings
+    EGNN_B(256, 256, 32, 2, 4, 4, 4);
+#undef EGNN_B
   } else {
     if (splits != 1) return hipErrorInvalidValue;
     const int tiles = ((M + HBM_ - 1) / HBM_) * ((N + HBN - 1) / HBN);
