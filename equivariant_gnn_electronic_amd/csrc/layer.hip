@@ -231,21 +231,107 @@ __device__ inline EdgeList edge_list(int node, int half, int n_dst, const int *r
   return l;
 }
 
-// Stage the geometry rows (first gs4 float4 of each) of edges [base, base+cnt)
-// of `el` into the wave's LDS buffer; edge ids go to eid[].
-__device__ inline void stage_geom(const EdgeList &el, int base, int cnt, const float *geom, int gstride, int gs4,
-                                  int lds_row, float4 *buf, int *eid) {
-  const int lane = threadIdx.x & (kWave - 1);
-  if (lane < cnt) eid[lane] = el.at(base + lane);
-  wave_lds_order();
-  const float4 *g4 = reinterpret_cast<const float4 *>(geom);
-  const int s4 = gstride / 4;
-  for (int t = lane; t < cnt * gs4; t += kWave) {
-    const int i = t / gs4, q = t - i * gs4;
-    buf[i * lds_row + q] = g4[static_cast<int64_t>(eid[i]) * s4 + q];
-  }
-  wave_lds_order();
+// One channel of a row, in two steps (load, then convert).  bf16:
+// the lane loads the aligned 32-bit word holding its channel pair and keeps
+// its half.
+template <typename T> struct RawOf { typedef uint32_t type; };
+template <> struct RawOf<float> { typedef float type; };
+__device__ inline float load_raw(const float *row, uint32_t off) { return row[off]; }
+__device__ inline uint32_t load_raw(const uint16_t *row, uint32_t off) {
+  return *reinterpret_cast<const uint32_t *>(row + (off & ~1u));
 }
+__device__ inline float from_raw(float v, uint32_t) { return v; }
+__device__ inline float from_raw(uint32_t v, uint32_t off) {
+  return __uint_as_float((off & 1u) ? (v & 0xFFFF0000u) : (v << 16));
+}
+
+// Geometry rows (the first gs4 float4 of each) of a wave's edge list move
+// global -> registers -> the wave's LDS buffer in batches of kBatch edges.
+// AHEAD: one batch ahead of their use (the loads of batch b + 1 are issued
+// before batch b is processed and written to LDS after it), at the price of
+// holding that batch in registers meanwhile; otherwise each batch is loaded
+// when the previous one is done.  Edge ids (one per lane, a load through
+// src_perm for source groups) run one batch ahead either way.  An optional per-edge value (extra[e]) rides along into xbuf.  The
+// LDS rows are GS4 float4 long; the first gs4 hold the row's data.
+template <int GS4, bool AHEAD = true>
+struct GeomPipe {
+  static constexpr int NQ = (kBatch * GS4 + kWave - 1) / kWave;  // float4 slots per lane
+  const EdgeList el;
+  typedef float v4 __attribute__((ext_vector_type(4)));  // plain vector: stays in registers
+  const v4 *g4;
+  const float *extra;
+  float4 *buf;
+  int *eid;
+  float *xbuf;
+  int s4, lane, gs4;
+  v4 q[NQ];
+  // slot u of this lane: edge t / GS4 of the batch, float4 t % GS4 of its row (t = lane + 64 u);
+  // columns from gs4 to GS4 - 1 (past the basis values in use) repeat column gs4 - 1
+  __device__ int si(int u) const { return (lane + kWave * u) / GS4; }
+  __device__ int sq(int u) const { return min((lane + kWave * u) % GS4, gs4 - 1); }
+  float xv;
+  int ids_cur, ids_next;
+
+  // this lane's edge id in the batch starting at base (clamped into the list)
+  __device__ int batch_edge(int base) const { return el.at(min(base + lane, el.count - 1)); }
+  __device__ void fetch(int ids, int cnt) {
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      // slots past the batch reload its last row, which commit discards
+      const int e = __shfl(ids, min(si(u), cnt - 1), kWave);
+      q[u] = g4[static_cast<int64_t>(e) * s4 + sq(u)];
+    }
+    if (extra) xv = extra[ids];
+  }
+  __device__ void commit(int ids, int cnt) {
+    if (lane < cnt) {
+      eid[lane] = ids;
+      if (extra) xbuf[lane] = xv;
+    }
+#pragma unroll
+    for (int u = 0; u < NQ; ++u)
+      if (si(u) < cnt) reinterpret_cast<v4 *>(buf)[lane + kWave * u] = q[u];
+  }
+  // Loads batch 0 into LDS and starts the ids of batch 1.  el.count > 0.
+  __device__ GeomPipe(const EdgeList &el_, const float *geom, int gstride, int gs4_, float4 *buf_, int *eid_,
+                      const float *extra_ = nullptr, float *xbuf_ = nullptr)
+      : el(el_), g4(reinterpret_cast<const v4 *>(geom)), extra(extra_), buf(buf_), eid(eid_), xbuf(xbuf_),
+        s4(gstride / 4), lane(static_cast<int>(threadIdx.x) & (kWave - 1)), gs4(gs4_), xv(0.0f) {
+    ids_cur = batch_edge(0);
+    const int cnt = min(kBatch, el.count);
+    fetch(ids_cur, cnt);
+    ids_next = kBatch < el.count ? batch_edge(kBatch) : 0;
+    commit(ids_cur, cnt);
+    wave_lds_order();
+  }
+  __device__ void next_ids(int nb) {
+    ids_cur = ids_next;
+    ids_next = nb + kBatch < el.count ? batch_edge(nb + kBatch) : 0;
+  }
+  // Before processing the batch at base: issue the loads of the next one
+  // (AHEAD), or nothing.
+  __device__ void prefetch(int base) {
+    const int nb = base + kBatch;
+    if (AHEAD && nb < el.count) {
+      fetch(ids_next, min(kBatch, el.count - nb));
+      next_ids(nb);
+    }
+  }
+  // After processing the batch at base: its LDS rows are free; store the next
+  // one (loaded now unless AHEAD).
+  __device__ void advance(int base) {
+    const int nb = base + kBatch;
+    wave_lds_order();
+    if (nb < el.count) {
+      if (!AHEAD) {
+        fetch(ids_next, min(kBatch, el.count - nb));
+        next_ids(nb);
+      }
+      commit(ids_cur, min(kBatch, el.count - nb));
+    }
+    wave_lds_order();
+  }
+};
 
 template <int LMAX, int MMAX, int NRBF>
 __device__ inline void load_wrad(const float *wrad, int n_rbf, int C2, int j, bool active, float (&wr)[NRBF][pair_count(LMAX, MMAX)]) {
@@ -327,9 +413,11 @@ __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restr
   else
     load_wrad<LMAX, MMAX, NRBF>(wrad, n_rbf, C2, j, active, wr);
   const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
+  // bf16: fewer registers for higher occupancy instead of the batch ahead
+  GeomPipe<GS4, std::is_same<T, float>::value> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave]);
   for (int base = 0; base < el.count; base += kBatch) {
     const int cnt = min(kBatch, el.count - base);
-    stage_geom(el, base, cnt, geom, gstride, gs4, GS4, gbuf[wave], eids[wave]);
+    gp.prefetch(base);
     for (int i = 0; i < cnt; ++i) {
       const int e = uniform(eids[wave][i]);
       const float *gr = gb + i * GS4 * 4;
@@ -374,7 +462,7 @@ __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restr
         }
       }
     }
-    wave_lds_order();
+    gp.advance(base);
   }
 }
 
@@ -473,36 +561,39 @@ __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restri
 #pragma unroll
   for (int k = 0; k < L::K; ++k) acc[k] = 0.0f;
   const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
-  for (int base = 0; base < el.count; base += kBatch) {
-    const int cnt = min(kBatch, el.count - base);
-    if (lane < cnt) abuf[wave][lane] = alpha[el.begin + base + lane];
-    stage_geom(el, base, cnt, geom, gstride, gs4, GS4, gbuf[wave], eids[wave]);
-    for (int i = 0; i < cnt; ++i) {
-      const int e = el.begin + base + i;
-      const float a = abuf[wave][i];
-      const float *gr = gb + i * GS4 * 4;
-      float y[L::KEPT];
+  if (el.count > 0) {
+    // not ahead: each edge's Y loads follow at once and wait for the geometry in any case
+    GeomPipe<GS4, false> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave], alpha, abuf[wave]);
+    for (int base = 0; base < el.count; base += kBatch) {
+      const int cnt = min(kBatch, el.count - base);
+      gp.prefetch(base);
+      for (int i = 0; i < cnt; ++i) {
+        const int e = el.begin + base + i;
+        const float a = abuf[wave][i];
+        const float *gr = gb + i * GS4 * 4;
+        float y[L::KEPT];
 #pragma unroll
-      for (int l = 0; l <= LMAX; ++l)
+        for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
-        for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
-          const int mu = cabs(m);
-          const T *row = static_cast<const T *>(Y.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
-          y[L::kidx(l, m)] = Store<T>::ld(row + L::col(l, m) * C + cl);
-        }
-      T *eo = edge_out ? edge_out + static_cast<int64_t>(e) * L::K * C : nullptr;
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+            const int mu = cabs(m);
+            const T *row = static_cast<const T *>(Y.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
+            y[L::kidx(l, m)] = Store<T>::ld(row + L::col(l, m) * C + cl);
+          }
+        T *eo = edge_out ? edge_out + static_cast<int64_t>(e) * L::K * C : nullptr;
 #pragma unroll
-      for (int l = 0; l <= LMAX; ++l)
+        for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
-        for (int mp = -l; mp <= l; ++mp) {
-          float msg = 0.0f;
+          for (int mp = -l; mp <= l; ++mp) {
+            float msg = 0.0f;
 #pragma unroll
-          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) msg += gr[L::doff(l, m, mp)] * y[L::kidx(l, m)];
-          acc[l * l + l + mp] += a * msg;
-          if (eo && on) Store<T>::st(eo + (l * l + l + mp) * C + c, msg);
-        }
+            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) msg += gr[L::doff(l, m, mp)] * y[L::kidx(l, m)];
+            acc[l * l + l + mp] += a * msg;
+            if (eo && on) Store<T>::st(eo + (l * l + l + mp) * C + c, msg);
+          }
+      }
+      gp.advance(base);
     }
-    wave_lds_order();
   }
   if (!on) return;
 #pragma unroll
@@ -559,87 +650,87 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
   };
   const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
   float s_row = 0.0f;
-  for (int base = 0; base < el.count; base += kBatch) {
-    const int cnt = min(kBatch, el.count - base);
-    stage_geom(el, base, cnt, geom, gstride, gs4, GS4, gbuf[wave], eids[wave]);
-    for (int i = 0; i < cnt; ++i) {
-      const int e = el.begin + base + i;
-      const float *gr = gb + i * GS4 * 4;
-      float p = 0.0f;
-#pragma unroll
-      for (int t = 0; t < CPL; ++t) {
-        float T[L::KEPT];
-        edge_T(gr, t, T);
-#pragma unroll
-        for (int l = 0; l <= LMAX; ++l)
-#pragma unroll
-          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
-            const int mu = cabs(m);
-            const TY *row = static_cast<const TY *>(Y.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
-            // gd is 0 on clamped lanes, so T is too
-            p += Store<TY>::ld(row + static_cast<uint32_t>(L::col(l, m) * C + cl[t])) * T[L::kidx(l, m)];
-          }
-      }
-      p = wave_sum(p);
-      dalpha[e] = p;  // every lane stores the same value and later reads its own store
-      s_row += alpha[e] * p;
-    }
-    wave_lds_order();
-  }
   float wacc[CPL];
 #pragma unroll
   for (int t = 0; t < CPL; ++t) wacc[t] = 0.0f;
-  for (int base = 0; base < el.count; base += kBatch) {
-    const int cnt = min(kBatch, el.count - base);
-    stage_geom(el, base, cnt, geom, gstride, gs4, GS4, gbuf[wave], eids[wave]);
-    for (int i = 0; i < cnt; ++i) {
-      const int e = el.begin + base + i;
-      const float *gr = gb + i * GS4 * 4;
-      const float a = alpha[e];
-      const float da = a * (dalpha[e] - s_row);
+  if (el.count > 0) {
+    GeomPipe<GS4> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave]);
+    for (int base = 0; base < el.count; base += kBatch) {
+      const int cnt = min(kBatch, el.count - base);
+      gp.prefetch(base);
+      for (int i = 0; i < cnt; ++i) {
+        const int e = el.begin + base + i;
+        const float *gr = gb + i * GS4 * 4;
+        float p = 0.0f;
+        // all of the edge's Y loads before any use (see load_raw)
+        typename RawOf<TY>::type yr[CPL][L::KEPT];
 #pragma unroll
-      for (int t = 0; t < CPL; ++t) {
-        const int c = lane + kWave * t;
-        float T[L::KEPT];
-        edge_T(gr, t, T);
-        const float y00 = Store<TY>::ld(static_cast<const TY *>(Y.p[0]) + static_cast<int64_t>(e) * L::blocks(0) * C + cl[t]);
-        const float wat = w_att[cl[t]];
+        for (int t = 0; t < CPL; ++t)
 #pragma unroll
-        for (int l = 0; l <= LMAX; ++l)
+          for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
-          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
-            float v = a * T[L::kidx(l, m)];
-            if (l == 0) {
-              v += da * wat * dsilu(y00);
-              if (c < C) wacc[t] += da * silu(y00);
+            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+              const int mu = cabs(m);
+              const TY *row = static_cast<const TY *>(Y.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
+              yr[t][L::kidx(l, m)] = load_raw(row, static_cast<uint32_t>(L::col(l, m) * C + cl[t]));
             }
-            const int mu = cabs(m);
-            TD *row = static_cast<TD *>(dY.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
-            if (c < C) Store<TD>::st(row + static_cast<uint32_t>(L::col(l, m) * C + c), v);
-          }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < CPL; ++t) {
+          float T[L::KEPT];
+          edge_T(gr, t, T);
+#pragma unroll
+          for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
+              // gd is 0 on clamped lanes, so T is too
+              p += from_raw(yr[t][L::kidx(l, m)], static_cast<uint32_t>(L::col(l, m) * C + cl[t])) * T[L::kidx(l, m)];
+        }
+        p = wave_sum(p);
+        dalpha[e] = p;  // every lane stores the same value and later reads its own store
+        s_row += alpha[e] * p;
       }
+      gp.advance(base);
     }
-    wave_lds_order();
+    GeomPipe<GS4> gp2(el, geom, gstride, gs4, gbuf[wave], eids[wave]);
+    for (int base = 0; base < el.count; base += kBatch) {
+      const int cnt = min(kBatch, el.count - base);
+      gp2.prefetch(base);
+      for (int i = 0; i < cnt; ++i) {
+        const int e = el.begin + base + i;
+        const float *gr = gb + i * GS4 * 4;
+        const float a = alpha[e];
+        const float da = a * (dalpha[e] - s_row);
+#pragma unroll
+        for (int t = 0; t < CPL; ++t) {
+          const int c = lane + kWave * t;
+          float T[L::KEPT];
+          edge_T(gr, t, T);
+          const float y00 = Store<TY>::ld(static_cast<const TY *>(Y.p[0]) + static_cast<int64_t>(e) * L::blocks(0) * C + cl[t]);
+          const float wat = w_att[cl[t]];
+#pragma unroll
+          for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+              float v = a * T[L::kidx(l, m)];
+              if (l == 0) {
+                v += da * wat * dsilu(y00);
+                if (c < C) wacc[t] += da * silu(y00);
+              }
+              const int mu = cabs(m);
+              TD *row = static_cast<TD *>(dY.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
+              if (c < C) Store<TD>::st(row + static_cast<uint32_t>(L::col(l, m) * C + c), v);
+            }
+        }
+      }
+      gp2.advance(base);
+    }
   }
 #pragma unroll
   for (int t = 0; t < CPL; ++t) {
     const int c = lane + kWave * t;
     if (c < C) watt_part[static_cast<int64_t>(d) * C + c] = wacc[t];
   }
-}
-
-// One channel of a gradient row, in two steps (load, then convert).  bf16:
-// the lane loads the aligned 32-bit word holding its channel pair and keeps
-// its half.
-template <typename T> struct RawOf { typedef uint32_t type; };
-template <> struct RawOf<float> { typedef float type; };
-__device__ inline float load_raw(const float *row, uint32_t off) { return row[off]; }
-__device__ inline uint32_t load_raw(const uint16_t *row, uint32_t off) {
-  return *reinterpret_cast<const uint32_t *>(row + (off & ~1u));
-}
-__device__ inline float from_raw(float v, uint32_t) { return v; }
-__device__ inline float from_raw(uint32_t v, uint32_t off) {
-  return __uint_as_float((off & 1u) ? (v & 0xFFFF0000u) : (v << 16));
 }
 
 // Radial-weight gradient: dW_rad[k][p][j] = sum_e phi_e[k] dg_e[p][j] with
@@ -682,9 +773,10 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
     if (el.count == 0) continue;
     float xv[L::K];
     load_node_row<L::K>(x, node, C, c, active, xv);
+    GeomPipe<GS4> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave]);
     for (int base = 0; base < el.count; base += kBatch) {
       const int cnt = min(kBatch, el.count - base);
-      stage_geom(el, base, cnt, geom, gstride, gs4, GS4, gbuf[wave], eids[wave]);
+      gp.prefetch(base);
       for (int i = 0; i < cnt; ++i) {
         const int e = uniform(eids[wave][i]);
         const float *gr = gb + i * GS4 * 4;
@@ -723,7 +815,7 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
           for (int p = 0; p < L::NP; ++p) acc[k][p] += ph * dg[p];
         }
       }
-      wave_lds_order();
+      gp.advance(base);
     }
   }
   if (!active) return;
@@ -769,54 +861,57 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
     float wr[NRBF][L::NP];
     load_wrad<LMAX, MMAX, NRBF>(wrad, n_rbf, C2, j, active, wr);
     const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
-    for (int base = 0; base < el.count; base += kBatch) {
-      const int cnt = min(kBatch, el.count - base);
-      stage_geom(el, base, cnt, geom, gstride, gs4, GS4, gbuf[wave], eids[wave]);
-      for (int i = 0; i < cnt; ++i) {
-        const int e = uniform(eids[wave][i]);
-        const float *gr = gb + i * GS4 * 4;
-        if (!active) continue;
-        const TdA *rowp[MMAX + 1];  // wave-uniform row bases, 32-bit lane offsets
+    if (el.count > 0) {
+      GeomPipe<GS4> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave]);
+      for (int base = 0; base < el.count; base += kBatch) {
+        const int cnt = min(kBatch, el.count - base);
+        gp.prefetch(base);
+        for (int i = 0; i < cnt; ++i) {
+          const int e = uniform(eids[wave][i]);
+          const float *gr = gb + i * GS4 * 4;
+          if (!active) continue;
+          const TdA *rowp[MMAX + 1];  // wave-uniform row bases, 32-bit lane offsets
 #pragma unroll
-        for (int mu = 0; mu <= MMAX; ++mu)
-          rowp[mu] = static_cast<const TdA *>(dA.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
-        // all of the edge's loads are issued before any is used (the barrier keeps
-        // the scheduler from pairing each load with its use)
-        typename RawOf<TdA>::type raw[L::KEPT];
+          for (int mu = 0; mu <= MMAX; ++mu)
+            rowp[mu] = static_cast<const TdA *>(dA.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
+          // all of the edge's loads are issued before any is used (the barrier keeps
+          // the scheduler from pairing each load with its use)
+          typename RawOf<TdA>::type raw[L::KEPT];
 #pragma unroll
-        for (int l = 0; l <= LMAX; ++l)
-#pragma unroll
-          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
-            raw[L::kidx(l, m)] = load_raw(rowp[cabs(m)], static_cast<uint32_t>(L::col(l, m) * C2 + j));
-        __builtin_amdgcn_sched_barrier(0);
-        float dxt[L::KEPT];
-#pragma unroll
-        for (int l = 0; l <= LMAX; ++l)
-#pragma unroll
-          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
-            dxt[L::kidx(l, m)] = from_raw(raw[L::kidx(l, m)], static_cast<uint32_t>(L::col(l, m) * C2 + j));
-        float g[L::NP];
-#pragma unroll
-        for (int p = 0; p < L::NP; ++p) g[p] = 0.0f;
-#pragma unroll
-        for (int k = 0; k < NRBF; ++k) {
-          const float raw = gr[L::ND + k];  // in the staged row; select, no branch
-          const float ph = k < n_rbf ? raw : 0.0f;
-#pragma unroll
-          for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[k][p];
-        }
-#pragma unroll
-        for (int l = 0; l <= LMAX; ++l)
-#pragma unroll
-          for (int mp = -l; mp <= l; ++mp) {
-            float s = 0.0f;
+          for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
             for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
-              s += gr[L::doff(l, m, mp)] * g[pair_index(cabs(m), l, LMAX)] * dxt[L::kidx(l, m)];
-            acc[l * l + l + mp] += s;
+              raw[L::kidx(l, m)] = load_raw(rowp[cabs(m)], static_cast<uint32_t>(L::col(l, m) * C2 + j));
+          __builtin_amdgcn_sched_barrier(0);
+          float dxt[L::KEPT];
+#pragma unroll
+          for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
+              dxt[L::kidx(l, m)] = from_raw(raw[L::kidx(l, m)], static_cast<uint32_t>(L::col(l, m) * C2 + j));
+          float g[L::NP];
+#pragma unroll
+          for (int p = 0; p < L::NP; ++p) g[p] = 0.0f;
+#pragma unroll
+          for (int k = 0; k < NRBF; ++k) {
+            const float raw = gr[L::ND + k];  // in the staged row; select, no branch
+            const float ph = k < n_rbf ? raw : 0.0f;
+#pragma unroll
+            for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[k][p];
           }
+#pragma unroll
+          for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+            for (int mp = -l; mp <= l; ++mp) {
+              float s = 0.0f;
+#pragma unroll
+              for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
+                s += gr[L::doff(l, m, mp)] * g[pair_index(cabs(m), l, LMAX)] * dxt[L::kidx(l, m)];
+              acc[l * l + l + mp] += s;
+            }
+        }
+        gp.advance(base);
       }
-      wave_lds_order();
     }
   }
   // half 1 hands its partial to half 0 of the same chunk
