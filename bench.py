@@ -236,12 +236,14 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_mib, argv):
 
 # timing family -> substring of its kernel's symbol name
 FAMILY_KERNELS = {
-    "cgemm_dw_f32": "cgemm_f32_kernel<false, false, false>",
-    "cgemm_fwd_f32": "cgemm_f32_kernel<true, true, true>",
-    "cgemm_dx_f32": "cgemm_f32_kernel<true, false, true>",
-    "gemm_tn_f32": "gemm_f32_kernel<false, false>",
-    "gemm_nt_f32": "gemm_f32_kernel<true, true>",
-    "gemm_nn_f32": "gemm_f32_kernel<true, false>",
+    # kernel-name pieces ("::" keeps gemm from matching cgemm; the GEMM templates carry
+    # tile widths after these arguments)
+    "cgemm_dw_f32": "::cgemm_f32_kernel<false, false, false,",
+    "cgemm_fwd_f32": "::cgemm_f32_kernel<true, true, true,",
+    "cgemm_dx_f32": "::cgemm_f32_kernel<true, false, true,",
+    "gemm_tn_f32": "::gemm_f32_kernel<false, false,",
+    "gemm_nt_f32": "::gemm_f32_kernel<true, true,",
+    "gemm_nn_f32": "::gemm_f32_kernel<true, false,",
     "gemm_nt_bf16": "gemm_bf16",
     "rotate_in": "scatter_in_kernel",
     "aggregate": "aggregate_kernel",
