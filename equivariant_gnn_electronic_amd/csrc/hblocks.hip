@@ -327,20 +327,28 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
   float *hs = hs_all + wave * kTile * lab_ld;
   const int grp = lane / 16, i16 = lane % 16;
   const int lmax_lab = tb.lmax_lab;
+  const int n_runs = (lmax_lab + 1) * (lmax_lab + 1);  // (L, M) runs of a row, in L^2 + L + M order
   const int64_t n_tiles = (rows + kTile - 1) / kTile;
-  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kWaves + wave; tile < n_tiles;
-       tile += static_cast<int64_t>(gridDim.x) * kWaves) {
+  const int64_t tile_step = static_cast<int64_t>(gridDim.x) * kWaves;
+  auto row_of = [&](int64_t tile) {
+    const int64_t ea = min(tile * kTile + i16, rows - 1);  // clamped row for loads
+    return irreps + ea * K * C + grp * S;
+  };
+  // The runs are loaded one ahead of their MFMA chain: run r + 1 while run r
+  // multiplies, and the next tile's first run before this tile's entries.
+  float a[S], an[S];
+  int64_t tile = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  if (tile < n_tiles) load_run<S>(row_of(tile), a);
+  for (; tile < n_tiles; tile += tile_step) {
     const int64_t e0 = tile * kTile;
-    const int64_t ea = min(e0 + i16, rows - 1);  // clamped row for loads
-    const T *frow = irreps + ea * K * C + grp * S;
+    const T *frow = row_of(tile);
     for (int L = 0; L <= lmax_lab; ++L) {
       const int nL = tb.nL[L];
-      if (nL == 0) continue;
       const int ntile = (nL + 15) / 16;
       const int woff = tb.woff[L], hoff = tb.hoff[L];
       for (int M = -L; M <= L; ++M) {
-        float a[S];
-        load_run<S>(frow + (L * L + L + M) * C, a);
+        const int r = L * L + L + M;
+        if (r + 1 < n_runs) load_run<S>(frow + (r + 1) * C, an);
         for (int t = 0; t < ntile; ++t) {
           // rows beyond n_L read the zero rows of the pad (or the next L's rows, discarded below)
           const float *brow = wl + (woff + 16 * t + i16) * WLD + grp * S;
@@ -354,11 +362,14 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
           const int k = 16 * t + i16;
           if (k < nL) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) hs[(4 * grp + r) * lab_ld + hoff + (M + L) * nL + k] = acc[r];
+            for (int q = 0; q < 4; ++q) hs[(4 * grp + q) * lab_ld + hoff + (M + L) * nL + k] = acc[q];
           }
         }
+#pragma unroll
+        for (int i = 0; i < S; ++i) a[i] = an[i];
       }
     }
+    if (tile + tile_step < n_tiles) load_run<S>(row_of(tile + tile_step), a);
     wave_lds_order();
     for (int q = lane; q < kTile * n_ent; q += kWave) {
       const int el = q / n_ent, ent = q - el * n_ent;
