@@ -34,4 +34,13 @@ hipError_t gemm_bf16_nt(int M, int N, int K, const uint16_t *A, int lda, const u
 hipError_t gemm_bf16_nt_splitk(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B, int ldb, float *C,
                                int ldc, int splits, int64_t split_stride, hipStream_t stream);
 
+// Split-K product over the rows of two row-major bf16 matrices: slice z of C
+// (at C + z * split_stride, row stride ldc) is C_z[m][n] = sum over the z-th
+// range of k of P[k][m] * Q[k][n], P [K][M] (row stride ldp), Q [K][N] (row
+// stride ldq), fp32 accumulate and output.  No transpose pass: the operands go
+// to LDS as they lie and are read with gfx950's transposing LDS loads.
+// M, N, ldp, ldq multiples of 8, P and Q 16-byte aligned.
+hipError_t gemm_bf16_tn_splitk(int M, int N, int K, const uint16_t *P, int ldp, const uint16_t *Q, int ldq, float *C,
+                               int ldc, int splits, int64_t split_stride, hipStream_t stream);
+
 }  // namespace egnn

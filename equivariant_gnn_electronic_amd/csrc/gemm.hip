@@ -671,6 +671,145 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, i
   }
 }
 
+// bf16 split-K product of two row-major operands over their rows (the weight
+// gradients sum over edges, and the edge index is the rows of both dY and the
+// saved GEMM input).  The tiles go to LDS as they lie in memory, [k][m] and
+// [k][n], 512-byte rows (BM = BN = 256), by the same direct loads and ring as
+// gemm_bf16_lds_kernel; MFMA fragments need eight consecutive k of one m, which
+// gfx950's transposing LDS read (ds_read_b64_tr_b16) delivers: within each
+// group of 16 lanes, lane i receives element i % 4 of the 8-byte reads of
+// lanes i / 4 + 4 j, j = 0..3.  So lanes 4q..4q+3 of a group read 32
+// consecutive bytes of row k0 + q, and lane i gets k0..k0+3 of column
+// base + i; two such reads (k0 and k0 + 4) make one bf16x8 fragment.  The
+// 16-byte chunks of row k are XOR-swizzled by tn_swizzle(k), which puts the
+// rows read together on distinct LDS banks.  Rows past the end of the K range
+// are read from a block of zeros.
+__device__ __align__(16) uint16_t g_zero_row[512] = {0};
+
+__device__ inline int tn_swizzle(int k) { return ((k & 3) << 2) | (((k >> 3) & 1) << 4); }
+
+template <int BK, int WM, int WN, int S>
+__global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_tn_kernel(int M, int N, int K,
+                                                                     const uint16_t *__restrict__ P, int ldp,
+                                                                     const uint16_t *__restrict__ Q, int ldq,
+                                                                     float *__restrict__ C, int ldc, int splits,
+                                                                     int k_per_split, int64_t split_stride) {
+  constexpr int BM = 256, BN = 256, NW = WM * WN, ST = (BM + BN) * BK;
+  static_assert(S == 2, "two-stage ring");
+  __shared__ uint16_t T0[ST], T1[ST];
+  // see gemm_bf16_lds_kernel: an unexecuted direct load placed first
+  __shared__ __attribute__((aligned(1024))) uint32_t dma_anchor[256];
+  if (K < 0) __builtin_amdgcn_global_load_lds(static_cast<const void *>(P), static_cast<void *>(dma_anchor), 16, 0, 0);
+  auto ts = [&](auto st) -> uint16_t * {
+    if constexpr (decltype(st)::value == 0) return T0;
+    else return T1;
+  };
+  auto ps = [&](auto st) -> uint16_t * { return ts(st); };
+  auto qs = [&](auto st) -> uint16_t * { return ts(st) + BK * BM; };
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const TileMap tm = map_tile(blockIdx.x, tiles_m, tiles_n, splits);
+  if (!tm.valid) return;
+  const int k_begin = tm.z * k_per_split, k_end = min(K, k_begin + k_per_split);
+  const int nk = max(0, k_end - k_begin + BK - 1) / BK;
+  C += tm.z * split_stride;
+  const int row0 = tm.mt * BM, col0 = tm.nt * BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+  const int wm = (wave / WN) * WTM, wn = (wave % WN) * WTN;
+  // direct loads: a BK x 32-chunk operand tile is BK / 2 wave loads (2 rows each), spread over the waves
+  constexpr int LA = BK * 32 / 64 / NW;
+  static_assert(LA >= 1 && (BK * 32) % (64 * NW) == 0, "tile");
+  int lrow[LA], lcol[LA], loff[LA];
+#pragma unroll
+  for (int h = 0; h < LA; ++h) {
+    const int slot0 = (h * NW + wave) * 64, sl = slot0 + lane, r = sl >> 5;
+    lrow[h] = r;
+    lcol[h] = ((sl & 31) ^ tn_swizzle(r)) * 8;  // first column of the chunk this lane fetches
+    loff[h] = slot0 * 8;
+  }
+  auto issue = [&](auto st, int kt) {
+#pragma unroll
+    for (int h = 0; h < LA; ++h) {
+      const int k = k_begin + kt * BK + lrow[h];
+      const bool in = k < k_end;
+      // columns past M (N) repeat the last chunk; those rows (columns) of C are not written
+      const uint16_t *gp = in ? P + static_cast<int64_t>(k) * ldp + min(row0 + lcol[h], M - 8) : g_zero_row + lcol[h];
+      const uint16_t *gq = in ? Q + static_cast<int64_t>(k) * ldq + min(col0 + lcol[h], N - 8) : g_zero_row + lcol[h];
+      __builtin_amdgcn_global_load_lds(static_cast<const void *>(gp), static_cast<void *>(ps(st) + loff[h]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void *>(gq), static_cast<void *>(qs(st) + loff[h]), 16, 0, 0);
+    }
+  };
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int grp = lane >> 4, gl = lane & 15;
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  // fragment of columns base..base+31 and k = kk..kk+15 of an LDS tile (lane: column base + lane % 32,
+  // k = kk + 8 (lane / 32) .. + 7)
+  auto frag = [&](const uint16_t *tile, int base, int kk) -> bf16x8 {
+    u32x2 h[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int k = kk + 8 * (grp >> 1) + 4 * u + (gl >> 2);
+      const int col = base + 16 * (grp & 1) + 4 * (gl & 3);
+      const int off = k * BM + (((col >> 3) ^ tn_swizzle(k)) << 3) + (col & 7);
+      h[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                           (__attribute__((address_space(3))) s16x4 *)(tile + off)));
+    }
+    // whole dwords: element-wise assembly was seen to drop half of each read
+    const u32x4 w = {h[0].x, h[0].y, h[1].x, h[1].y};
+    return __builtin_bit_cast(bf16x8, w);
+  };
+  auto compute = [&](auto st) {
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      bf16x8 a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[i] = frag(ps(st), wm + 32 * i, 16 * s);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[j] = frag(qs(st), wn + 32 * j, 16 * s);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // ring of two stages, refilled before each product (see gemm_bf16_lds_kernel)
+  if (nk > 0) issue(std::integral_constant<int, 0>{}, 0);
+  wait_vmcnt<0>();
+  barrier_no_fence();
+  for (int it = 0; it < nk; it += 2) {
+    static_for<0, 2>([&](auto du) {
+      constexpr int dd = decltype(du)::value;
+      const int i = it + dd;
+      if (i >= nk) return;
+      if (i + 1 < nk) issue(std::integral_constant<int, 1 - dd>{}, i + 1);
+      compute(std::integral_constant<int, dd>{});
+      wait_vmcnt<0>();
+      barrier_no_fence();
+    });
+  }
+  const int fr = lane & 31, fh = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = col0 + wn + 32 * j + fr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + wm + 32 * i + 8 * (r >> 2) + 4 * fh + (r & 3);
+        if (row < M) C[static_cast<int64_t>(row) * ldc + col] = acc[i][j][r];
+      }
+    }
+}
+
 }  // namespace
 
 namespace {
@@ -816,6 +955,22 @@ hipError_t gemm_bf16_nt_splitk(int M, int N, int K, const uint16_t *A, int lda, 
   if (splits < 1) splits = 1;
   if (K % 32 != 0) return hipErrorInvalidValue;
   return launch_bf16(M, N, K, A, lda, B, ldb, C, ldc, false, splits, split_stride, stream);
+}
+
+hipError_t gemm_bf16_tn_splitk(int M, int N, int K, const uint16_t *P, int ldp, const uint16_t *Q, int ldq, float *C,
+                               int ldc, int splits, int64_t split_stride, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (splits < 1) splits = 1;
+  if (M % 8 != 0 || N % 8 != 0 || ldp % 8 != 0 || ldq % 8 != 0 || K < 0 ||
+      reinterpret_cast<uintptr_t>(P) % 16 != 0 || reinterpret_cast<uintptr_t>(Q) % 16 != 0)
+    return hipErrorInvalidValue;
+  constexpr int BK = 64;
+  int kps = (K + splits - 1) / splits;
+  kps = (kps + BK - 1) / BK * BK;
+  const int grid = tile_grid(((M + 255) / 256) * ((N + 255) / 256), splits);
+  // 256 x 256 x 64, 8 waves (2 x 4, 128 x 64 each), 2 stages (128 KB LDS)
+  gemm_bf16_tn_kernel<BK, 2, 4, 2><<<grid, 512, 0, stream>>>(M, N, K, P, ldp, Q, ldq, C, ldc, splits, kps, split_stride);
+  return hipGetLastError();
 }
 
 }  // namespace egnn

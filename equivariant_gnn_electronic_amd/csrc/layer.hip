@@ -135,42 +135,6 @@ __global__ void expand_weights_t_kernel(const float *w1, const float *w2, int ro
   BT[i] = f32_to_bf16(v);
 }
 
-// out[c][r] = in[r][c] (bf16) for r < R and 0 for R <= r < R_pad, in: R rows
-// of Cc bf16 values with row stride ld_in (a multiple of 8), Cc a multiple of
-// 8, R_pad a multiple of 64.  A 64 x 64 tile moves in 16-byte pieces on both
-// sides: each thread loads 8 consecutive columns of a row, scatters them into
-// an LDS tile stored column-major, then reads 8 consecutive rows of a column
-// and writes them as one 16-byte store.  Puts the edge index innermost for the
-// weight-gradient products, which sum over edges.
-__global__ void __launch_bounds__(256) transpose_bf16_kernel(const uint16_t *__restrict__ in, int64_t R, int Cc,
-                                                             int ld_in, int64_t R_pad, uint16_t *__restrict__ out) {
-  constexpr int TLD = 72;  // tile column of 64 rows + 8 (keeps 16-byte alignment)
-  __shared__ __align__(16) uint16_t tile[64 * TLD];
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
-  const int c0 = blockIdx.y * 64;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int rr = (t >> 3) + 32 * h, cc = (t & 7) * 8;
-    const int64_t r = r0 + rr;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < R && c0 + cc < Cc) v = *reinterpret_cast<const uint4 *>(in + r * ld_in + c0 + cc);
-    uint16_t e[8];
-    memcpy(e, &v, sizeof(v));
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tile[(cc + j) * TLD + rr] = e[j];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int cc = (t >> 3) + 32 * h, rr = (t & 7) * 8;
-    const int c = c0 + cc;
-    if (c < Cc && r0 + rr < R_pad)
-      *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(c) * R_pad + r0 + rr) =
-          *reinterpret_cast<const uint4 *>(&tile[cc * TLD + rr]);
-  }
-}
-
 // dW1 = dB(+,+) + dB(-,-) and dW2 = dB(-,+) - dB(+,-) from the gradient dB
 // [2 rows][2 cols] of the expanded matrix (the inverse of the expansion).
 __global__ void fold_expanded_kernel(const float *dB, int rows, int cols, float *dw1, float *dw2) {
@@ -951,6 +915,8 @@ __global__ void fill_f32(float *p, int64_t n, float v) {
 // ------------------------------------------------------------ buffers --
 size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
 
+inline bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
 struct Carver {
   char *base;
   size_t off = 0;
@@ -1022,11 +988,8 @@ struct BwdWs {
   float *watt_part;
   float *P;          // split partials (real and imaginary parts for m >= 1)
   float *wrad_part;
-  uint16_t *dYT, *AT;  // bf16: dY_m^T and A_m^T [cols][E padded to 64], one |m| at a time
   float *dWexp;        // bf16: summed gradient of the expanded weight of one |m|
 };
-
-int64_t pad64(int64_t E) { return (E + 63) / 64 * 64; }
 
 // node streams of the radial-weight gradient (fixed by the node count, so the
 // summation order of its partials is reproducible)
@@ -1035,7 +998,7 @@ int wrad_streams(int n_src) { return n_src < 1024 ? (n_src > 0 ? n_src : 1) : 10
 BwdWs carve_bwd_ws(Carver &cv, const LayerShape &s, int64_t E, int n_dst, int n_src) {
   BwdWs w{};
   const bool bf = s.storage == EGNN_BF16;
-  size_t pmax = 0, kmax = 0, nmax = 0;
+  size_t pmax = 0;
   for (int m = 0; m <= s.mmax; ++m) {
     const size_t ng = s.Ng[m], kg = s.Kg[m];
     if (bf) {
@@ -1050,18 +1013,12 @@ BwdWs carve_bwd_ws(Carver &cv, const LayerShape &s, int64_t E, int n_dst, int n_
     else
       w.dA[m] = cv.take<float>(static_cast<size_t>(E) * kg);
     pmax = pmax > ng * kg ? pmax : ng * kg;
-    kmax = kmax > kg ? kmax : kg;
-    nmax = nmax > ng ? nmax : ng;
   }
   w.dalpha = cv.take<float>(E);
   w.watt_part = cv.take<float>(static_cast<size_t>(n_dst > 0 ? n_dst : 1) * s.C);
   w.P = cv.take<float>(pmax * dw_splits(E));
   w.wrad_part = cv.take<float>(static_cast<size_t>(wrad_streams(n_src)) * s.n_rbf * s.n_pairs * 2 * s.C);
-  if (bf) {
-    w.dYT = cv.take<uint16_t>(nmax * pad64(E));
-    w.AT = cv.take<uint16_t>(kmax * pad64(E));
-    w.dWexp = cv.take<float>(pmax);
-  }
+  if (bf) w.dWexp = cv.take<float>(pmax);
   return w;
 }
 
@@ -1282,6 +1239,7 @@ extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph
   if (st != EGNN_OK) return st;
   EGNN_REQUIRE(weights && x_in && x_out, "null pointer");
   EGNN_REQUIRE(x_in != x_out, "x_out must not alias x_in");
+  EGNN_REQUIRE(aligned16(ws) && aligned16(saved), "ws and saved must be 16-byte aligned");
   const int64_t E = g->n_edges;
   if (E > 0) EGNN_REQUIRE(geom, "geom is null");
   Carver cw{static_cast<char *>(ws)};
@@ -1413,6 +1371,7 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
   }
   EGNN_REQUIRE(weights && x_in && saved && grad_x_in && grad_weights, "null pointer");
   EGNN_REQUIRE(g->n_dst == 0 || grad_out, "grad_out is null");
+  EGNN_REQUIRE(aligned16(ws) && aligned16(saved), "ws and saved must be 16-byte aligned");
   const int64_t E = g->n_edges;
   if (E > 0) EGNN_REQUIRE(geom, "geom is null");
   Carver cs{static_cast<char *>(const_cast<void *>(saved))};
@@ -1464,11 +1423,10 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
   if (E > 0 && bf) {
     // bf16 storage: both gradient products on bf16 MFMA, fp32 accumulate.
     //   dA_m = dY_m B_m                 (dY in bf16 from bwd_row, B_m^T prepared above)
-    //   dB_m = sum_e dY_m[e]^T A_m[e]   (operands transposed so the edge index is
-    //                                    innermost; split over edges, summed in order)
+    //   dB_m = sum_e dY_m[e]^T A_m[e]   (both read as stored, edges as rows; split
+    //                                    over edges, summed in order)
     // then dW_m1, dW_m2 folded out of dB_m for m >= 1.
     const int splits = dw_splits(E);
-    const int64_t Ep = pad64(E);
     for (int m = 0; m <= s.mmax; ++m) {
       const int Ng = s.Ng[m], Kg = s.Kg[m];
       hipError_t e;
@@ -1480,18 +1438,10 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
         set_error("GEMM launch failed: %s", hipGetErrorString(e));
         return EGNN_E_HIP;
       }
-      {
-        Timed t(stream, "transpose_bf16", 0.0, double(E) * (Ng + Kg) * 2.0 + double(Ep) * (Ng + Kg) * 2.0);
-        const unsigned gx = static_cast<unsigned>(Ep / 64);
-        transpose_bf16_kernel<<<dim3(gx, ceil_div(Ng, 64)), 256, 0, stream>>>(w.dYb[m], E, Ng, Ng, Ep,
-                                                                                         w.dYT);
-        transpose_bf16_kernel<<<dim3(gx, ceil_div(Kg, 64)), 256, 0, stream>>>(
-            static_cast<const uint16_t *>(acts.A[m]), E, Kg, Kg, Ep, w.AT);
-      }
       const int64_t pn = static_cast<int64_t>(Ng) * Kg;
       {
         Timed t(stream, "gemm_dw_bf16", 2.0 * double(E) * Ng * Kg, double(E) * (Ng + Kg) * 2.0 + double(splits) * pn * 4.0);
-        e = gemm_bf16_nt_splitk(Ng, Kg, static_cast<int>(Ep), w.dYT, static_cast<int>(Ep), w.AT, static_cast<int>(Ep),
+        e = gemm_bf16_tn_splitk(Ng, Kg, static_cast<int>(E), w.dYb[m], Ng, static_cast<const uint16_t *>(acts.A[m]), Kg,
                                 w.P, Kg, splits, pn, stream);
       }
       if (e != hipSuccess) {

@@ -179,7 +179,8 @@ egnn_status egnn_edge_geom(const egnn_layer_desc *d, const egnn_graph *g, float 
  *   edge_out[e] = msg_e   (optional; the per-edge message an edge block consumes)
  * x_in [n_src][K][C], x_out [n_dst][K][C], edge_out [n_edges][K][C] or NULL,
  * weights packed fp32 (egnn_layer_weight_count).  `saved` (NULL for
- * inference) receives what egnn_layer_bwd needs; `ws` is scratch.
+ * inference) receives what egnn_layer_bwd needs; `ws` is scratch.  Both are
+ * 16-byte aligned (EGNN_E_ARG otherwise; hipMalloc and torch allocations are).
  * x_out must not alias x_in.
  * ------------------------------------------------------------------------- */
 egnn_status egnn_layer_sizes(const egnn_layer_desc *d, const egnn_graph *g,

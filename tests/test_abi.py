@@ -151,6 +151,21 @@ def test_workspace_too_small_rejected(lib):
     assert st == _lib.EGNN_E_ARG   # x_out aliases x_in
 
 
+def test_misaligned_workspace_rejected(lib):
+    """The split-K weight-gradient product reads the saved tensors with 16-byte
+    loads, so ws and saved must be 16-byte aligned; the host check says so."""
+    from equivariant_gnn_electronic_amd import _lib
+    d = _desc(4, 2, 64, storage=1)
+    g = _fake_graph(10, 10, 100)
+    p = ct.c_void_p(0x1000)
+    odd = ct.c_void_p(0x1008)
+    st = lib.egnn_layer_fwd(ct.byref(d), ct.byref(g), p, p, p, ct.c_void_p(0x2000), None, None, odd, 1 << 40, None)
+    assert st == _lib.EGNN_E_ARG
+    assert b"aligned" in lib.egnn_last_error()
+    st = lib.egnn_layer_bwd(ct.byref(d), ct.byref(g), p, p, p, odd, p, p, p, p, 1 << 40, None)
+    assert st == _lib.EGNN_E_ARG
+
+
 def test_decode_description_checks(lib):
     from equivariant_gnn_electronic_amd import _lib
     arr = (ct.c_int32 * 5)(0, 0, 1, 1, 2)
