@@ -114,6 +114,19 @@ __global__ void to_bf16_kernel(const float *in, int64_t n, uint16_t *out) {
   if (i < n) out[i] = f32_to_bf16(in[i]);
 }
 
+// Radial weights W_rad [n_rbf][np][2C] as bf16 pairs over the basis index:
+// out[q][p][j] = (bf16 W[2q][p][j], bf16 W[2q + 1][p][j]) for q < 8, zero past
+// n_rbf (the gate of the paired rotate-in is a sum of packed dot products).
+__global__ void pack_wrad_kernel(const float *w, int n_rbf, int np, int C2, uint32_t *out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(8) * np * C2) return;
+  const int q = static_cast<int>(i / (static_cast<int64_t>(np) * C2));
+  const int64_t r = i % (static_cast<int64_t>(np) * C2);
+  const float v0 = 2 * q < n_rbf ? w[static_cast<int64_t>(2 * q) * np * C2 + r] : 0.0f;
+  const float v1 = 2 * q + 1 < n_rbf ? w[static_cast<int64_t>(2 * q + 1) * np * C2 + r] : 0.0f;
+  out[i] = static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
+}
+
 // bf16 backward helpers.
 // BT[k][n] = B[n][k] in bf16, the second operand of dX = dY B as a product
 // with both operands contiguous along its sum (n).  cplx: B is the expanded
@@ -425,6 +438,106 @@ __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restr
           Store<TA>::st(rowp[cabs(m)] + static_cast<uint32_t>(L::col(l, m) * C2 + j), v);
         }
       }
+    }
+    gp.advance(base);
+  }
+}
+
+// bf16 storage, C a multiple of 128: as scatter_in_kernel with two adjacent
+// channels per lane (a wave covers 128 channels).  Each Wigner-D value read
+// from LDS feeds both channels, the node row and the radial weights come in as
+// channel pairs, and each output leaves as one packed conversion and one
+// 4-byte store.
+template <int LMAX, int MMAX, int NRBF>
+__global__ void __launch_bounds__(kThreads) scatter_in_pair_kernel(const int *__restrict__ row_ptr,
+                                                                   const int *__restrict__ src_ptr,
+                                                                   const int *__restrict__ src_perm,
+                                                                   const float *__restrict__ geom, int gstride,
+                                                                   int n_dst, int n_src,
+                                                                   const uint16_t *__restrict__ x, int C,
+                                                                   const uint32_t *__restrict__ wpk, int n_rbf, Ptr3 A) {
+  using L = Lay<LMAX, MMAX>;
+  constexpr int GS4 = (L::ND + NRBF + 3) / 4;
+  constexpr int NP = L::NP;
+  const int gs4 = (L::ND + n_rbf + 3) / 4;
+  __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
+  __shared__ int eids[kWavesPerBlock][kBatch];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int nch = C / (2 * kWave);
+  const NodeWave nw = node_wave(blockIdx.x * kWavesPerBlock + wave, nch);
+  if (nw.node >= n_src) return;
+  const EdgeList el = edge_list(nw.node, nw.half, n_dst, row_ptr, src_ptr, src_perm);
+  if (el.count == 0) return;
+  const int C2 = 2 * C;
+  const int c = nw.chunk * 2 * kWave + 2 * lane;  // channels c, c + 1 (always < C)
+  const int j = nw.half * C + c;
+  // the node row, both channels: one 32-bit load per coefficient
+  float xv[L::K][2];
+  {
+    const uint32_t *row = reinterpret_cast<const uint32_t *>(x + static_cast<int64_t>(nw.node) * L::K * C + c);
+    uint32_t raw[L::K];
+#pragma unroll
+    for (int k = 0; k < L::K; ++k) raw[k] = row[k * (C / 2)];
+#pragma unroll
+    for (int k = 0; k < L::K; ++k) {
+      xv[k][0] = __uint_as_float(raw[k] << 16);
+      xv[k][1] = __uint_as_float(raw[k] & 0xFFFF0000u);
+    }
+  }
+  // radial weights of both slots, pre-packed as bf16 pairs over the basis index (pack_wrad_kernel)
+  bf16x2 wp[2][NRBF / 2][NP];
+#pragma unroll
+  for (int q = 0; q < NRBF / 2; ++q)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const uint2 w = *reinterpret_cast<const uint2 *>(wpk + (static_cast<int64_t>(q) * NP + p) * C2 + j);
+      wp[0][q][p] = __builtin_bit_cast(bf16x2, w.x);
+      wp[1][q][p] = __builtin_bit_cast(bf16x2, w.y);
+    }
+  const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
+  GeomPipe<GS4, false> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave]);
+  for (int base = 0; base < el.count; base += kBatch) {
+    const int cnt = min(kBatch, el.count - base);
+    gp.prefetch(base);
+    for (int i = 0; i < cnt; ++i) {
+      const int e = uniform(eids[wave][i]);
+      const float *gr = gb + i * GS4 * 4;
+      bf16x2 ph[NRBF / 2];
+#pragma unroll
+      for (int q = 0; q < NRBF / 2; ++q) {
+        const float r0 = gr[L::ND + 2 * q], r1 = gr[L::ND + 2 * q + 1];
+        ph[q] = bf16x2{static_cast<__bf16>(2 * q < n_rbf ? r0 : 0.0f), static_cast<__bf16>(2 * q + 1 < n_rbf ? r1 : 0.0f)};
+      }
+      uint32_t *rowp[MMAX + 1];  // wave-uniform row bases; 32-bit lane offsets below
+#pragma unroll
+      for (int mu = 0; mu <= MMAX; ++mu)
+        rowp[mu] = reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(A.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2));
+      // pair by pair: the gate of (|m|, l), then its +m and -m rows
+#pragma unroll
+      for (int mu = 0; mu <= MMAX; ++mu)
+#pragma unroll
+        for (int l = mu; l <= LMAX; ++l) {
+          const int pi = pair_index(mu, l, LMAX);
+          float g0 = 0.0f, g1 = 0.0f;
+#pragma unroll
+          for (int q = 0; q < NRBF / 2; ++q) {
+            g0 = __builtin_amdgcn_fdot2_f32_bf16(ph[q], wp[0][q][pi], g0, false);
+            g1 = __builtin_amdgcn_fdot2_f32_bf16(ph[q], wp[1][q][pi], g1, false);
+          }
+#pragma unroll
+          for (int sg = 0; sg < (mu == 0 ? 1 : 2); ++sg) {
+            const int m = sg == 0 ? mu : -mu;
+            float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+            for (int mp = -l; mp <= l; ++mp) {
+              const float d = gr[L::doff(l, m, mp)];
+              v0 += d * xv[l * l + l + mp][0];
+              v1 += d * xv[l * l + l + mp][1];
+            }
+            const bf16x2 out{static_cast<__bf16>(v0 * g0), static_cast<__bf16>(v1 * g1)};
+            rowp[mu][static_cast<uint32_t>((L::col(l, m) * C2 + j) / 2)] = __builtin_bit_cast(uint32_t, out);
+          }
+        }
     }
     gp.advance(base);
   }
@@ -948,6 +1061,7 @@ Acts carve_acts(Carver &cv, const LayerShape &s, int64_t E) {
 struct FwdWs {
   void *B[3];      // expanded weights per m (B[0] may alias W0 for fp32)
   float *logit;
+  uint32_t *wpk;   // bf16: radial weights packed for the paired rotate-in (pack_wrad_kernel)
 };
 
 FwdWs carve_fwd_ws(Carver &cv, const LayerShape &s, int64_t E) {
@@ -964,6 +1078,7 @@ FwdWs carve_fwd_ws(Carver &cv, const LayerShape &s, int64_t E) {
     w.B[m] = cv.take<char>(n * bb);
   }
   w.logit = cv.take<float>(E);
+  w.wpk = s.storage == EGNN_BF16 ? cv.take<uint32_t>(static_cast<size_t>(8) * s.n_pairs * 2 * s.C) : nullptr;
   return w;
 }
 
@@ -1050,8 +1165,17 @@ template <int LMAX, int MMAX>
 struct Launch {
   template <typename T, typename TA>
   static void rotate_in(const egnn_graph *g, const LayerShape &s, const float *geom, const T *x, const float *wrad,
-                        const Acts &a, hipStream_t st) {
+                        const uint32_t *wpk, const Acts &a, hipStream_t st) {
     Ptr3 A{{a.A[0], a.A[1], a.A[2]}};
+    if constexpr (std::is_same<T, uint16_t>::value && std::is_same<TA, uint16_t>::value) {
+      if (wpk && s.C % (2 * kWave) == 0 && s.n_rbf <= 8) {  // channel pairs (16 basis functions would spill)
+        const int nch2 = s.C / (2 * kWave);
+        const unsigned grid2 = ceil_div(static_cast<int64_t>(g->n_src) * 2 * nch2, kWavesPerBlock);
+        scatter_in_pair_kernel<LMAX, MMAX, 8><<<grid2, kThreads, 0, st>>>(
+            g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride, g->n_dst, g->n_src, x, s.C, wpk, s.n_rbf, A);
+        return;
+      }
+    }
     const int nch = (s.C + kWave - 1) / kWave;
     const unsigned grid = ceil_div(static_cast<int64_t>(g->n_src) * 2 * nch, kWavesPerBlock);
     if (s.n_rbf <= 8)
@@ -1145,18 +1269,18 @@ struct Launch {
 
 template <int LMAX, int MMAX, typename T, typename TA>
 void launch_rotate_in(const egnn_graph *g, const LayerShape &s, const float *geom, const void *x, const float *wrad,
-                      const Acts &a, hipStream_t st) {
-  Launch<LMAX, MMAX>::template rotate_in<T, TA>(g, s, geom, static_cast<const T *>(x), wrad, a, st);
+                      const uint32_t *wpk, const Acts &a, hipStream_t st) {
+  Launch<LMAX, MMAX>::template rotate_in<T, TA>(g, s, geom, static_cast<const T *>(x), wrad, wpk, a, st);
 }
 template <int LMAX, int MMAX>
 void rotate_in_f32(const egnn_graph *g, const LayerShape &s, const float *geom, const void *x, const float *wrad,
-                   const Acts &a, hipStream_t st) {
-  launch_rotate_in<LMAX, MMAX, float, float>(g, s, geom, x, wrad, a, st);
+                   const uint32_t *wpk, const Acts &a, hipStream_t st) {
+  launch_rotate_in<LMAX, MMAX, float, float>(g, s, geom, x, wrad, wpk, a, st);
 }
 template <int LMAX, int MMAX>
 void rotate_in_bf16(const egnn_graph *g, const LayerShape &s, const float *geom, const void *x, const float *wrad,
-                    const Acts &a, hipStream_t st) {
-  launch_rotate_in<LMAX, MMAX, uint16_t, uint16_t>(g, s, geom, x, wrad, a, st);
+                    const uint32_t *wpk, const Acts &a, hipStream_t st) {
+  launch_rotate_in<LMAX, MMAX, uint16_t, uint16_t>(g, s, geom, x, wrad, wpk, a, st);
 }
 template <int LMAX, int MMAX>
 void aggregate_f32(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const void *x,
@@ -1280,6 +1404,10 @@ extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph
                                                               1.f, 1.f, v, v + nb);
     }
   }
+  if (bf) {
+    const int64_t n = static_cast<int64_t>(8) * s.n_pairs * 2 * s.C;
+    pack_wrad_kernel<<<ceil_div(n, T), T, 0, stream>>>(weights + wo.wrad, s.n_rbf, s.n_pairs, 2 * s.C, fw.wpk);
+  }
   const double xb = bf ? 2.0 : 4.0;
   double sumK = 0, sumN = 0;
   for (int m = 0; m <= s.mmax; ++m) {
@@ -1292,9 +1420,9 @@ extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph
                            double(E) * 4.0 + double(E) * sumK * xb;
       Timed t(stream, "rotate_in", 0.0, bytes);
       if (bf) {
-        EGNN_DISPATCH_LM(s.lmax, s.mmax, rotate_in_bf16, g, s, geom, x_in, weights + wo.wrad, acts, stream);
+        EGNN_DISPATCH_LM(s.lmax, s.mmax, rotate_in_bf16, g, s, geom, x_in, weights + wo.wrad, fw.wpk, acts, stream);
       } else {
-        EGNN_DISPATCH_LM(s.lmax, s.mmax, rotate_in_f32, g, s, geom, x_in, weights + wo.wrad, acts, stream);
+        EGNN_DISPATCH_LM(s.lmax, s.mmax, rotate_in_f32, g, s, geom, x_in, weights + wo.wrad, nullptr, acts, stream);
       }
     }
     for (int m = 0; m <= s.mmax; ++m) {

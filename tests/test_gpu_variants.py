@@ -3,9 +3,9 @@
 The 64-atom periodic cell (several images per pair) carries every
 (lmax, mmax, C, n_rbf, storage) combination below, so each kernel
 instantiation the ABI dispatches to is exercised: lmax 1-4, mmax 0-2, C with
-a partial 64-channel chunk (24, 96) and two chunks (128), 4/8/12/16 radial
+a partial 64-channel chunk (24, 96) and two chunks (128), 3/4/6/8/12/16 radial
 functions, bf16 storage on both bf16 GEMM variants and the fallback for
-K not a multiple of 32; forward and backward for every one.  Also: an open cell with isolated atoms (rows without
+K not a multiple of 32, and the channel-pair rotate-in (bf16, C = 128); forward and backward for every one.  Also: an open cell with isolated atoms (rows without
 incoming edges) and ghosts, and a graph with no edges at all.
 Tolerances as in test_gpu_parity.
 """
@@ -37,6 +37,8 @@ VARIANTS = [
     (3, 1, 32, 8, "bf16"),
     (4, 2, 8, 8, "bf16"),
     (2, 0, 64, 4, "bf16"),
+    (2, 1, 128, 6, "bf16"),   # two channels per lane in rotate-in (C a multiple of 128, n_rbf <= 8)
+    (4, 2, 128, 3, "bf16"),   # the same with an odd basis count (last basis pair half zero)
 ]
 
 
