@@ -680,6 +680,91 @@ __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restri
   }
 }
 
+// bf16 storage, C a multiple of 128: as aggregate_kernel with two adjacent
+// channels per lane (one 32-bit load per Y entry, each Wigner-D value used
+// for both channels, packed bf16 stores).
+template <int LMAX, int MMAX>
+__global__ void __launch_bounds__(kThreads) aggregate_pair_kernel(const int *__restrict__ row_ptr, int n_dst,
+                                                                  const float *__restrict__ geom, int gstride,
+                                                                  const float *__restrict__ alpha, CPtr3 Y, int C,
+                                                                  const uint16_t *__restrict__ x,
+                                                                  uint16_t *__restrict__ x_out,
+                                                                  uint16_t *__restrict__ edge_out) {
+  using L = Lay<LMAX, MMAX>;
+  constexpr int GS4 = (L::ND + 3) / 4;
+  __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
+  __shared__ int eids[kWavesPerBlock][kBatch];
+  __shared__ float abuf[kWavesPerBlock][kBatch];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int nch = C / (2 * kWave);
+  const int gw = uniform(blockIdx.x * kWavesPerBlock + wave);
+  const int d = gw / nch, chunk = gw % nch;
+  if (d >= n_dst) return;
+  const int c = chunk * 2 * kWave + 2 * lane;  // channels c, c + 1 (always < C)
+  EdgeList el;
+  el.perm = nullptr;
+  el.begin = uniform(row_ptr[d]);
+  el.count = uniform(row_ptr[d + 1]) - el.begin;
+  float acc[L::K][2];
+#pragma unroll
+  for (int k = 0; k < L::K; ++k) acc[k][0] = acc[k][1] = 0.0f;
+  const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
+  auto unpack = [](uint32_t v, float &lo, float &hi) {
+    lo = __uint_as_float(v << 16);
+    hi = __uint_as_float(v & 0xFFFF0000u);
+  };
+  auto pack = [](float lo, float hi) { return __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(lo), static_cast<__bf16>(hi)}); };
+  if (el.count > 0) {
+    GeomPipe<GS4, false> gp(el, geom, gstride, (L::ND + 3) / 4, gbuf[wave], eids[wave], alpha, abuf[wave]);
+    for (int base = 0; base < el.count; base += kBatch) {
+      const int cnt = min(kBatch, el.count - base);
+      gp.prefetch(base);
+      for (int i = 0; i < cnt; ++i) {
+        const int e = el.begin + base + i;
+        const float a = abuf[wave][i];
+        const float *gr = gb + i * GS4 * 4;
+        uint32_t yr[L::KEPT];
+#pragma unroll
+        for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+            const int mu = cabs(m);
+            const uint32_t *row = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(Y.p[mu]) +
+                                                                     static_cast<int64_t>(e) * L::blocks(mu) * C);
+            yr[L::kidx(l, m)] = row[static_cast<uint32_t>((L::col(l, m) * C + c) / 2)];
+          }
+        uint32_t *eo = edge_out ? reinterpret_cast<uint32_t *>(edge_out + static_cast<int64_t>(e) * L::K * C) : nullptr;
+#pragma unroll
+        for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+          for (int mp = -l; mp <= l; ++mp) {
+            float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+              const float dv = gr[L::doff(l, m, mp)];
+              float y0, y1;
+              unpack(yr[L::kidx(l, m)], y0, y1);
+              m0 += dv * y0;
+              m1 += dv * y1;
+            }
+            acc[l * l + l + mp][0] += a * m0;
+            acc[l * l + l + mp][1] += a * m1;
+            if (eo) eo[static_cast<uint32_t>(((l * l + l + mp) * C + c) / 2)] = pack(m0, m1);
+          }
+      }
+      gp.advance(base);
+    }
+  }
+  const uint32_t *xr = reinterpret_cast<const uint32_t *>(x + static_cast<int64_t>(d) * L::K * C + c);
+  uint32_t *xo = reinterpret_cast<uint32_t *>(x_out + static_cast<int64_t>(d) * L::K * C + c);
+#pragma unroll
+  for (int k = 0; k < L::K; ++k) {
+    float x0, x1;
+    unpack(xr[k * (C / 2)], x0, x1);
+    xo[k * (C / 2)] = pack(x0 + acc[k][0], x1 + acc[k][1]);
+  }
+}
+
 // -------------------------------------------------------------- backward --
 // Per destination row: T_e = trunc(D_e G_d); dalpha_e = <Y_e, T_e>;
 // da_e = alpha_e (dalpha_e - sum_row alpha dalpha);
@@ -1189,6 +1274,14 @@ struct Launch {
   static void aggregate(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const T *x,
                         T *x_out, T *edge_out, hipStream_t st) {
     CPtr3 Y{{a.Y[0], a.Y[1], a.Y[2]}};
+    if constexpr (std::is_same<T, uint16_t>::value) {
+      if (s.C % (2 * kWave) == 0) {  // channel pairs
+        const unsigned grid2 = ceil_div(static_cast<int64_t>(g->n_dst) * (s.C / (2 * kWave)), kWavesPerBlock);
+        aggregate_pair_kernel<LMAX, MMAX><<<grid2, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha,
+                                                                      Y, s.C, x, x_out, edge_out);
+        return;
+      }
+    }
     const int nch = (s.C + kWave - 1) / kWave;
     const unsigned grid = ceil_div(static_cast<int64_t>(g->n_dst) * nch, kWavesPerBlock);
     aggregate_kernel<LMAX, MMAX, T><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, s.nD + s.n_rbf,
