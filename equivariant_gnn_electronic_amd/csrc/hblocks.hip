@@ -304,15 +304,24 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
   extern __shared__ float smem[];
   const Table &tb = g_tables[slot];
   const int n_terms = tb.term_start[n_ent];
+  // every piece is addressed from smem by an index: a round trip through an
+  // integer address would lose the LDS address space and turn the reads into
+  // flat loads, which wait on global memory traffic too
   int *t_start = reinterpret_cast<int *>(smem);                        // [n_ent + 1]
-  float *t_coef = reinterpret_cast<float *>(t_start + n_ent + 1);     // [n_terms]
+  float *t_coef = smem + (n_ent + 1);                                  // [n_terms]
   int *t_idx = reinterpret_cast<int *>(t_coef + n_terms);              // [n_terms]
-  float *wl = reinterpret_cast<float *>(t_idx + n_terms);              // [n_w + 16][WLD] (zero rows after n_w)
-  wl = reinterpret_cast<float *>((reinterpret_cast<uintptr_t>(wl) + 15) & ~uintptr_t(15));
+  float *wl = smem + ((n_ent + 1 + 2 * n_terms + 3) & ~3);             // [n_w + 16][WLD], 16-byte aligned (zero rows after n_w)
   // label rows padded to lab_ld = 4 (mod 16) floats: the four 16-lane groups
   // of an MFMA result store then land on disjoint LDS bank ranges
   const int lab_ld = label_stride(n_lab);
   float *hs_all = wl + (n_w + 16) * WLD;                               // [kWaves][kTile][lab_ld]
+  // per-degree entries of the table, read once per (tile, L) in the label loop
+  __shared__ int l_n[2 * kMaxLab2 + 1], l_woff[2 * kMaxLab2 + 1], l_hoff[2 * kMaxLab2 + 1];
+  if (threadIdx.x <= 2 * kMaxLab2) {
+    l_n[threadIdx.x] = tb.nL[threadIdx.x];
+    l_woff[threadIdx.x] = tb.woff[threadIdx.x];
+    l_hoff[threadIdx.x] = tb.hoff[threadIdx.x];
+  }
   for (int i = threadIdx.x; i <= n_ent; i += blockDim.x) t_start[i] = tb.term_start[i];
   for (int i = threadIdx.x; i < n_terms; i += blockDim.x) {
     t_coef[i] = tb.term_coef[i];
@@ -334,53 +343,68 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
     const int64_t ea = min(tile * kTile + i16, rows - 1);  // clamped row for loads
     return irreps + ea * K * C + grp * S;
   };
-  // The runs are loaded one ahead of their MFMA chain: run r + 1 while run r
-  // multiplies, and the next tile's first run before this tile's entries.
-  float a[S], an[S];
-  int64_t tile = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
-  if (tile < n_tiles) load_run<S>(row_of(tile), a);
-  for (; tile < n_tiles; tile += tile_step) {
-    const int64_t e0 = tile * kTile;
-    const T *frow = row_of(tile);
-    for (int L = 0; L <= lmax_lab; ++L) {
-      const int nL = tb.nL[L];
-      const int ntile = (nL + 15) / 16;
-      const int woff = tb.woff[L], hoff = tb.hoff[L];
-      for (int M = -L; M <= L; ++M) {
-        const int r = L * L + L + M;
-        if (r + 1 < n_runs) load_run<S>(frow + (r + 1) * C, an);
-        for (int t = 0; t < ntile; ++t) {
-          // rows beyond n_L read the zero rows of the pad (or the next L's rows, discarded below)
-          const float *brow = wl + (woff + 16 * t + i16) * WLD + grp * S;
-          float b[S];
+  // The runs of this wave's tiles form one sequence q (tile q / n_runs, run
+  // q % n_runs).  Run q + 1 loads while run q multiplies, into the other of two
+  // named buffers (the loop is unrolled by two, so no register copies), and a
+  // tile's entries are formed after its last run, while the next tile's first
+  // run is in flight.
+  const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  // unconditional (past the last tile row_of clamps to the last row, and the
+  // run is never used): a branch here would make the compiler wait for every
+  // load in flight before each MFMA chain
+  auto issue = [&](int64_t q, float(&dst)[S]) {
+    load_run<S>(row_of(tile0 + (q / n_runs) * tile_step) + (q % n_runs) * C, dst);
+  };
+  auto run = [&](int64_t q, const float(&a)[S]) {
+    const int64_t tile = tile0 + (q / n_runs) * tile_step;
+    const int r = static_cast<int>(q % n_runs);
+    int L = static_cast<int>(sqrtf(static_cast<float>(r)));
+    while (L * L > r) --L;
+    while ((L + 1) * (L + 1) <= r) ++L;
+    const int M = r - L * L - L;
+    const int nL = l_n[L];
+    const int ntile = (nL + 15) / 16;
+    const int woff = l_woff[L], hoff = l_hoff[L];
+    for (int t = 0; t < ntile; ++t) {
+      // rows beyond n_L read the zero rows of the pad (or the next L's rows, discarded below)
+      const float *brow = wl + (woff + 16 * t + i16) * WLD + grp * S;
+      float b[S];
 #pragma unroll
-          for (int i = 0; i < S; ++i) b[i] = brow[i];
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < S; ++i) b[i] = brow[i];
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < S; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
-          // D[i][j]: row i = 4 * (lane / 16) + r, column j = lane % 16
-          const int k = 16 * t + i16;
-          if (k < nL) {
+      for (int i = 0; i < S; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+      // D[i][j]: row i = 4 * (lane / 16) + rr, column j = lane % 16
+      const int k = 16 * t + i16;
+      if (k < nL) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) hs[(4 * grp + q) * lab_ld + hoff + (M + L) * nL + k] = acc[q];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < S; ++i) a[i] = an[i];
+        for (int rr = 0; rr < 4; ++rr) hs[(4 * grp + rr) * lab_ld + hoff + (M + L) * nL + k] = acc[rr];
       }
     }
-    if (tile + tile_step < n_tiles) load_run<S>(row_of(tile + tile_step), a);
-    wave_lds_order();
-    for (int q = lane; q < kTile * n_ent; q += kWave) {
-      const int el = q / n_ent, ent = q - el * n_ent;
-      if (e0 + el >= rows) break;
-      const float *h = hs + el * lab_ld;
-      float acc = 0.0f;
-      const int t1 = t_start[ent + 1];
-      for (int t = t_start[ent]; t < t1; ++t) acc += t_coef[t] * h[t_idx[t]];
-      H[(e0 + el) * n_ent + ent] = acc;
+    if (r == n_runs - 1) {  // the tile's labels are complete: its entries
+      const int64_t e0 = tile * kTile;
+      wave_lds_order();
+      for (int qq = lane; qq < kTile * n_ent; qq += kWave) {
+        const int el = qq / n_ent, ent = qq - el * n_ent;
+        if (e0 + el >= rows) break;
+        const float *h = hs + el * lab_ld;
+        float acc = 0.0f;
+        const int t1 = t_start[ent + 1];
+        for (int t = t_start[ent]; t < t1; ++t) acc += t_coef[t] * h[t_idx[t]];
+        H[(e0 + el) * n_ent + ent] = acc;
+      }
+      wave_lds_order();
     }
-    wave_lds_order();
+  };
+  auto live = [&](int64_t q) { return tile0 + (q / n_runs) * tile_step < n_tiles; };
+  float a0[S], a1[S];
+  issue(0, a0);
+  for (int64_t q = 0; live(q); q += 2) {
+    issue(q + 1, a1);
+    run(q, a0);
+    if (!live(q + 1)) break;
+    issue(q + 2, a0);
+    run(q + 1, a1);
   }
 }
 
