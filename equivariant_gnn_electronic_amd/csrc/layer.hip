@@ -230,7 +230,7 @@ __device__ inline float from_raw(uint32_t v, uint32_t off) {
 // when the previous one is done.  Edge ids (one per lane, a load through
 // src_perm for source groups) run one batch ahead either way.  An optional per-edge value (extra[e]) rides along into xbuf.  The
 // LDS rows are GS4 float4 long; the first gs4 hold the row's data.
-template <int GS4, bool AHEAD = true>
+template <int GS4, bool AHEAD = true, bool EXTRA = false>
 struct GeomPipe {
   static constexpr int NQ = (kBatch * GS4 + kWave - 1) / kWave;  // float4 slots per lane
   const EdgeList el;
@@ -249,21 +249,26 @@ struct GeomPipe {
   float xv;
   int ids_cur, ids_next;
 
+  // The loads below carry no branches: past the end of the list they read
+  // its last edge again (ids clamp, cnt >= 1) and the results go unused.  A
+  // load under a branch makes the compiler copy its result where the paths
+  // meet, and that copy waits for every load in flight.
   // this lane's edge id in the batch starting at base (clamped into the list)
   __device__ int batch_edge(int base) const { return el.at(min(base + lane, el.count - 1)); }
   __device__ void fetch(int ids, int cnt) {
+    cnt = max(cnt, 1);
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
       // slots past the batch reload its last row, which commit discards
       const int e = __shfl(ids, min(si(u), cnt - 1), kWave);
       q[u] = g4[static_cast<int64_t>(e) * s4 + sq(u)];
     }
-    if (extra) xv = extra[ids];
+    if constexpr (EXTRA) xv = extra[ids];
   }
   __device__ void commit(int ids, int cnt) {
     if (lane < cnt) {
       eid[lane] = ids;
-      if (extra) xbuf[lane] = xv;
+      if constexpr (EXTRA) xbuf[lane] = xv;
     }
 #pragma unroll
     for (int u = 0; u < NQ; ++u)
@@ -277,19 +282,19 @@ struct GeomPipe {
     ids_cur = batch_edge(0);
     const int cnt = min(kBatch, el.count);
     fetch(ids_cur, cnt);
-    ids_next = kBatch < el.count ? batch_edge(kBatch) : 0;
+    ids_next = batch_edge(kBatch);
     commit(ids_cur, cnt);
     wave_lds_order();
   }
   __device__ void next_ids(int nb) {
     ids_cur = ids_next;
-    ids_next = nb + kBatch < el.count ? batch_edge(nb + kBatch) : 0;
+    ids_next = batch_edge(nb + kBatch);
   }
   // Before processing the batch at base: issue the loads of the next one
   // (AHEAD), or nothing.
   __device__ void prefetch(int base) {
-    const int nb = base + kBatch;
-    if (AHEAD && nb < el.count) {
+    if constexpr (AHEAD) {
+      const int nb = base + kBatch;
       fetch(ids_next, min(kBatch, el.count - nb));
       next_ids(nb);
     }
@@ -300,7 +305,7 @@ struct GeomPipe {
     const int nb = base + kBatch;
     wave_lds_order();
     if (nb < el.count) {
-      if (!AHEAD) {
+      if constexpr (!AHEAD) {
         fetch(ids_next, min(kBatch, el.count - nb));
         next_ids(nb);
       }
@@ -640,7 +645,7 @@ __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restri
   const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
   if (el.count > 0) {
     // not ahead: each edge's Y loads follow at once and wait for the geometry in any case
-    GeomPipe<GS4, false> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave], alpha, abuf[wave]);
+    GeomPipe<GS4, false, true> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave], alpha, abuf[wave]);
     for (int base = 0; base < el.count; base += kBatch) {
       const int cnt = min(kBatch, el.count - base);
       gp.prefetch(base);
@@ -715,7 +720,7 @@ __global__ void __launch_bounds__(kThreads) aggregate_pair_kernel(const int *__r
   };
   auto pack = [](float lo, float hi) { return __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(lo), static_cast<__bf16>(hi)}); };
   if (el.count > 0) {
-    GeomPipe<GS4, false> gp(el, geom, gstride, (L::ND + 3) / 4, gbuf[wave], eids[wave], alpha, abuf[wave]);
+    GeomPipe<GS4, false, true> gp(el, geom, gstride, (L::ND + 3) / 4, gbuf[wave], eids[wave], alpha, abuf[wave]);
     for (int base = 0; base < el.count; base += kBatch) {
       const int cnt = min(kBatch, el.count - base);
       gp.prefetch(base);
