@@ -245,8 +245,8 @@ FAMILY_KERNELS = {
     "gemm_nt_f32": "::gemm_f32_kernel<true, true,",
     "gemm_nn_f32": "::gemm_f32_kernel<true, false,",
     "gemm_nt_bf16": "gemm_bf16",
-    "rotate_in": "scatter_in_kernel",
-    "aggregate": "aggregate_kernel",
+    "rotate_in": "::scatter_in_",
+    "aggregate": "::aggregate_",
     "hblocks": "hblocks_kernel",
 }
 
