@@ -165,17 +165,24 @@ __global__ void __launch_bounds__(256, 2) gemm_f32_kernel(int M, int N, int K, c
     if (more) load(k0 + BK);
     const float *as = As[buf];
     const float *bs = Bs[buf];
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 2) {
-      float a[TMt], b[TNt];
+    // the fragments of k pair kk + 2 are read from LDS before the products of kk are issued
+    float fa[2][TMt], fb[2][TNt];
+    auto frag = [&](int kk, float(&a)[TMt], float(&b)[TNt]) {
 #pragma unroll
       for (int i = 0; i < TMt; ++i) a[i] = as[(kk + fk) * SA::LD + wm + 32 * i + fr];
 #pragma unroll
       for (int j = 0; j < TNt; ++j) b[j] = bs[(kk + fk) * SB::LD + wn + 32 * j + fr];
+    };
+    frag(0, fa[0], fb[0]);
+#pragma unroll
+    for (int st = 0; st < BK / 2; ++st) {
+      const int cur = st & 1;
+      if (st + 1 < BK / 2) frag(2 * (st + 1), fa[cur ^ 1], fb[cur ^ 1]);
 #pragma unroll
       for (int i = 0; i < TMt; ++i)
 #pragma unroll
-        for (int j = 0; j < TNt; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TNt; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
     }
     if (more) store(buf ^ 1);
     __syncthreads();
@@ -295,23 +302,29 @@ __global__ void __launch_bounds__(256, 2) cgemm_f32_kernel(int M, int N, int K, 
   for (int k0 = k_begin; k0 < k_end; k0 += CBK) {
     const bool more = k0 + CBK < k_end;
     if (more) load(k0 + CBK);
+    // steps (k pair, part) in order; the fragments of step s + 1 are read
+    // from LDS before the products of step s are issued
+    constexpr int NS = (CBK / 2) * 3;
+    auto frag = [&](int st, float(&a)[TMt], float(&b)[TNt]) {
+      const int kk = 2 * (st / 3), q = st % 3;
+      const float *us = Us[buf][q];
+      const float *vs = Vs[buf][q];
 #pragma unroll
-    for (int kk = 0; kk < CBK; kk += 2) {
+      for (int i = 0; i < TMt; ++i) a[i] = us[(kk + fk) * SU::LD + wm + 32 * i + fr];
 #pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        const float *us = Us[buf][q];
-        const float *vs = Vs[buf][q];
-        float a[TMt], b[TNt];
+      for (int j = 0; j < TNt; ++j) b[j] = vs[(kk + fk) * SV::LD + wn + 32 * j + fr];
+    };
+    float fa[2][TMt], fb[2][TNt];
+    frag(0, fa[0], fb[0]);
 #pragma unroll
-        for (int i = 0; i < TMt; ++i) a[i] = us[(kk + fk) * SU::LD + wm + 32 * i + fr];
+    for (int st = 0; st < NS; ++st) {
+      const int cur = st & 1, q = st % 3;
+      if (st + 1 < NS) frag(st + 1, fa[cur ^ 1], fb[cur ^ 1]);
 #pragma unroll
-        for (int j = 0; j < TNt; ++j) b[j] = vs[(kk + fk) * SV::LD + wn + 32 * j + fr];
+      for (int i = 0; i < TMt; ++i)
 #pragma unroll
-        for (int i = 0; i < TMt; ++i)
-#pragma unroll
-          for (int j = 0; j < TNt; ++j)
-            acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[q][i][j], 0, 0, 0);
-      }
+        for (int j = 0; j < TNt; ++j)
+          acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[cur][i], fb[cur][j], acc[q][i][j], 0, 0, 0);
     }
     if (more) store(buf ^ 1);
     __syncthreads();
