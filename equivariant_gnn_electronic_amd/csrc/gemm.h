@@ -24,6 +24,11 @@ hipError_t cgemm_f32(int M, int N, int K, const float *Up, const float *Um, int 
                      const float *V2, const float *V3, int ldv, bool v_kcontig, float vsign, float *Cre, float *Cim,
                      int ldc, int splits, int64_t split_stride, hipStream_t stream);
 
+// Output tiles of gemm_f32 / cgemm_f32 for an M x N result (their tile widths
+// are chosen per dimension), and of gemm_bf16_tn_splitk.
+int gemm_f32_tiles(int M, int N);
+int gemm_bf16_tn_tiles(int M, int N);
+
 // bf16 operands (raw 16-bit), fp32 accumulate; both operands K-contiguous.
 // C is written as bf16 when c_bf16, else fp32.
 hipError_t gemm_bf16_nt(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,

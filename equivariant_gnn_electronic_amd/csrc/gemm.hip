@@ -866,6 +866,13 @@ void launch_cgemm(int tmt, int tnt, int M, int N, int K, const float *Up, const 
 
 }  // namespace
 
+int gemm_f32_tiles(int M, int N) {
+  const int tmt = tile_count(M), tnt = tile_count(N);
+  return ((M + 64 * tmt - 1) / (64 * tmt)) * ((N + 64 * tnt - 1) / (64 * tnt));
+}
+
+int gemm_bf16_tn_tiles(int M, int N) { return ((M + 255) / 256) * ((N + 255) / 256); }
+
 hipError_t gemm_f32(int M, int N, int K, const float *A, int lda, bool a_kcontig, const float *B, int ldb,
                     bool b_kcontig, float *C, int ldc, int splits, int64_t split_stride, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;

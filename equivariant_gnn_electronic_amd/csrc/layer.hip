@@ -1182,6 +1182,23 @@ int dw_splits(int64_t E) {
   return static_cast<int>(s);
 }
 
+// Split count of one weight-gradient product with `tiles` output tiles and
+// `per_split` partial floats per split: at least dw_splits(E); more when the
+// output is small, up to ~1024 blocks in all (a few per CU), 128 splits and
+// 2048 edges per split, and within the partial buffer sized for dw_splits(E)
+// splits of the largest product (`cap_floats`).  A multiple of 8 from 8 up.
+int dw_splits_for(int64_t E, int tiles, int64_t per_split, int64_t cap_floats) {
+  int64_t s = dw_splits(E);
+  int64_t want = (1024 + tiles - 1) / (tiles > 0 ? tiles : 1);
+  want = want < 128 ? want : 128;
+  const int64_t by_edges = E / 2048, by_buffer = per_split > 0 ? cap_floats / per_split : s;
+  if (want > by_edges) want = by_edges;
+  if (want > by_buffer) want = by_buffer;
+  if (want > s) s = want;
+  if (s >= 8) s = s / 8 * 8;
+  return static_cast<int>(s < 1 ? 1 : s);
+}
+
 struct BwdWs {
   float *B[3];       // fp32: V2, V3 of the conjugate complex product (m >= 1)
   float *dY[3];      // fp32 storage
@@ -1192,6 +1209,7 @@ struct BwdWs {
   float *dalpha;
   float *watt_part;
   float *P;          // split partials (real and imaginary parts for m >= 1)
+  int64_t P_floats;  // its size
   float *wrad_part;
   float *dWexp;        // bf16: summed gradient of the expanded weight of one |m|
 };
@@ -1222,6 +1240,7 @@ BwdWs carve_bwd_ws(Carver &cv, const LayerShape &s, int64_t E, int n_dst, int n_
   w.dalpha = cv.take<float>(E);
   w.watt_part = cv.take<float>(static_cast<size_t>(n_dst > 0 ? n_dst : 1) * s.C);
   w.P = cv.take<float>(pmax * dw_splits(E));
+  w.P_floats = static_cast<int64_t>(pmax) * dw_splits(E);
   w.wrad_part = cv.take<float>(static_cast<size_t>(wrad_streams(n_src)) * s.n_rbf * s.n_pairs * 2 * s.C);
   if (bf) w.dWexp = cv.take<float>(pmax);
   return w;
@@ -1652,7 +1671,6 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
     //   dB_m = sum_e dY_m[e]^T A_m[e]   (both read as stored, edges as rows; split
     //                                    over edges, summed in order)
     // then dW_m1, dW_m2 folded out of dB_m for m >= 1.
-    const int splits = dw_splits(E);
     for (int m = 0; m <= s.mmax; ++m) {
       const int Ng = s.Ng[m], Kg = s.Kg[m];
       hipError_t e;
@@ -1665,6 +1683,7 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
         return EGNN_E_HIP;
       }
       const int64_t pn = static_cast<int64_t>(Ng) * Kg;
+      const int splits = dw_splits_for(E, gemm_bf16_tn_tiles(Ng, Kg), pn, w.P_floats);
       {
         Timed t(stream, "gemm_dw_bf16", 2.0 * double(E) * Ng * Kg, double(E) * (Ng + Kg) * 2.0 + double(splits) * pn * 4.0);
         e = gemm_bf16_tn_splitk(Ng, Kg, static_cast<int>(E), w.dYb[m], Ng, static_cast<const uint16_t *>(acts.A[m]), Kg,
@@ -1684,7 +1703,6 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
       }
     }
   } else if (E > 0) {
-    const int splits = dw_splits(E);
     for (int m = 0; m <= s.mmax; ++m) {
       hipError_t e;
       if (m > 0) {
@@ -1701,6 +1719,7 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
           set_error("GEMM launch failed: %s", hipGetErrorString(e));
           return EGNN_E_HIP;
         }
+        const int splits = dw_splits_for(E, gemm_f32_tiles(Np, Kp), 2 * nb, w.P_floats);
         {
           // dW1 + i dW2 = sum_e (dY+ + i dY-)^T (X+ - i X-), split over edges
           Timed t(stream, "cgemm_dw_f32", 2.0 * double(E) * s.Ng[m] * s.Kg[m],
@@ -1729,6 +1748,7 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
       }
       // dB_m = dY_m^T A_m, split over edges, then summed in order
       const int64_t pn = static_cast<int64_t>(s.Ng[m]) * s.Kg[m];
+      const int splits = dw_splits_for(E, gemm_f32_tiles(s.Ng[m], s.Kg[m]), pn, w.P_floats);
       {
         Timed t(stream, "gemm_tn_f32", 2.0 * double(E) * s.Ng[m] * s.Kg[m],
                 double(E) * (s.Ng[m] + s.Kg[m]) * 4.0 + double(splits) * pn * 4.0);
