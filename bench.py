@@ -419,9 +419,19 @@ def main():
     kernels = {}
     for k, v in sorted(timing.items(), key=lambda kv: -kv[1]["total_ms"]):
         sec = v["total_ms"] * 1e-3
+        gbs = v["bytes"] / sec / 1e9 if v["bytes"] > 0 else None
         kernels[k] = dict(launches_per_step=v["launches"] / args.steps, ms_per_step=round(v["total_ms"] / args.steps, 4),
                           tflops=round(v["flops"] / sec / 1e12, 2) if v["flops"] > 0 else None,
-                          algorithmic_gbs=round(v["bytes"] / sec / 1e9, 1) if v["bytes"] > 0 else None)
+                          algorithmic_gbs=round(gbs, 1) if gbs else None)
+        if v["flops"] > 0:
+            # MFMA kernels: the fraction of the dtype's dense peak (algorithmic FLOPs)
+            peak = MFMA_PEAK_TFLOPS["bf16" if "bf16" in k else "f32"]
+            kernels[k]["mfma_frac"] = round(v["flops"] / sec / 1e12 / peak, 4)
+        elif gbs:
+            # gather / segment / decode kernels: against the published HBM peak and the measured copy
+            kernels[k]["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+            if copy_gbs:
+                kernels[k]["copy_frac"] = round(gbs / copy_gbs, 4)
     out = {
         "metric": "edges/s per SO(2) message-passing layer (fwd+bwd) + % of HBM/MFMA roofline",
         "value": round(E * wl["layers"] * args.steps / (t1 - t0), 1),
