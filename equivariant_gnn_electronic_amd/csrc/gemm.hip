@@ -472,6 +472,15 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// vmcnt(n) and lgkmcnt(0), before a ring barrier: this wave's direct loads of
+// the next K-tile have landed, and its LDS reads of the current stage are
+// complete, since other waves start refilling that stage once past the barrier.
+template <int N>
+__device__ inline void wait_ring() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
 // Workgroup barrier without the release fence of __syncthreads (the fence
 // would wait for every outstanding direct load).  Each wave waits for its
 // own loads with wait_vmcnt before arriving; the empty asm statements keep
@@ -559,6 +568,16 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, i
       __builtin_amdgcn_global_load_lds(static_cast<const void *>(gb[h] + static_cast<int64_t>(kt) * BK),
                                        static_cast<void *>(bs(st) + lb[h]), 16, 0, 0);
   };
+  // direct load h of a K-tile (A loads first, then B)
+  auto issue_one = [&](auto st, int kt, auto hc) {
+    constexpr int h = decltype(hc)::value;
+    if constexpr (h < LA)
+      __builtin_amdgcn_global_load_lds(static_cast<const void *>(ga[h] + static_cast<int64_t>(kt) * BK),
+                                       static_cast<void *>(as(st) + la[h]), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(static_cast<const void *>(gb[h - LA] + static_cast<int64_t>(kt) * BK),
+                                       static_cast<void *>(bs(st) + lb[h - LA]), 16, 0, 0);
+  };
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -579,33 +598,39 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, i
       b[j] = *reinterpret_cast<const bf16x8 *>(bs(st) + r * BK + (c ^ chunk_swizzle<CPR>(r)) * 8);
     }
   };
-  auto mma = [&](bf16x8(&a)[TM], bf16x8(&b)[TN]) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        if constexpr (STAGED)  // output tile transposed: lane = row, registers = columns
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
+  // hook(q) runs before the q-th MFMA of the K-tile (q = s * TM * TN + i * TN + j)
+  auto mma = [&](bf16x8(&a)[TM], bf16x8(&b)[TN], auto sc, auto &&hook) {
+    static_for<0, TM * TN>([&](auto qc) {
+      constexpr int i = decltype(qc)::value / TN, j = decltype(qc)::value % TN;
+      hook(std::integral_constant<int, decltype(sc)::value * TM * TN + decltype(qc)::value>{});
+      if constexpr (STAGED)  // output tile transposed: lane = row, registers = columns
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    });
   };
   // one K-tile: the fragments of 16-wide k-step s + 1 are read while step s multiplies
-  auto compute = [&](auto st) {
+  auto compute = [&](auto st, auto &&hook) {
     bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
     load_frag(st, 0, a0, b0);
     static_for<0, BK / 16>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
       if constexpr (s % 2 == 0) {
         if constexpr (s + 1 < BK / 16) load_frag(st, s + 1, a1, b1);
-        mma(a0, b0);
+        mma(a0, b0, sc, hook);
       } else {
         if constexpr (s + 1 < BK / 16) load_frag(st, s + 1, a0, b0);
-        mma(a1, b1);
+        mma(a1, b1, sc, hook);
       }
     });
   };
   constexpr int L = LA + LB;  // direct loads per K-tile per wave
+  // The next K-tile's loads go out one at a time between the MFMAs of the first
+  // half of the current one: issued as one burst at the top of the tile they
+  // held the waves at the memory pipeline while the matrix cores idled.  Load
+  // h goes before MFMA slot(h).
+  constexpr int NMF = TM * TN * (BK / 16);
+  auto slot = [](int h) { return h * (NMF / 2) / L; };
   const int nk = k_len / BK;
   // prologue: K-tiles 0 .. S-2 in flight, wait for tile 0
   static_for<0, S - 1>([&](auto st) {
@@ -624,10 +649,17 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_lds_kernel(int M, i
       constexpr int dd = decltype(du)::value % S;
       const int i = it + decltype(du)::value;
       if (i >= nk) return;
-      if (i + S - 1 < nk) issue(std::integral_constant<int, (dd + S - 1) % S>{}, i + S - 1);
-      compute(std::integral_constant<int, dd>{});
-      if (i + S - 1 < nk) wait_vmcnt<(S - 2) * L>();
-      else wait_vmcnt<0>();
+      // the guard around each load also keeps the scheduler from gathering them
+      const bool more = i + S - 1 < nk;
+      compute(std::integral_constant<int, dd>{}, [&](auto qc) {
+        static_for<0, L>([&](auto hc) {
+          if constexpr (slot(decltype(hc)::value) == decltype(qc)::value) {
+            if (more) issue_one(std::integral_constant<int, (dd + S - 1) % S>{}, i + S - 1, hc);
+          }
+        });
+      });
+      if (more) wait_ring<(S - 2) * L>();
+      else wait_ring<0>();
       barrier_no_fence();
     });
   }
@@ -740,17 +772,21 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_tn_kernel(int M, in
     lcol[h] = ((sl & 31) ^ tn_swizzle(r)) * 8;  // first column of the chunk this lane fetches
     loff[h] = slot0 * 8;
   }
+  // direct load h of a K-tile: h < LA from P, then LA from Q.  Columns past M
+  // (N) repeat the last chunk (those rows and columns of C are not written);
+  // rows past the K range read zeros.
+  auto issue_one = [&](auto st, int kt, auto hc) {
+    constexpr int h = decltype(hc)::value % LA;
+    constexpr bool from_q = decltype(hc)::value >= LA;
+    const int k = k_begin + kt * BK + lrow[h];
+    const bool in = k < k_end;
+    const uint16_t *g = from_q ? (in ? Q + static_cast<int64_t>(k) * ldq + min(col0 + lcol[h], N - 8) : g_zero_row + lcol[h])
+                               : (in ? P + static_cast<int64_t>(k) * ldp + min(row0 + lcol[h], M - 8) : g_zero_row + lcol[h]);
+    __builtin_amdgcn_global_load_lds(static_cast<const void *>(g), static_cast<void *>((from_q ? qs(st) : ps(st)) + loff[h]),
+                                     16, 0, 0);
+  };
   auto issue = [&](auto st, int kt) {
-#pragma unroll
-    for (int h = 0; h < LA; ++h) {
-      const int k = k_begin + kt * BK + lrow[h];
-      const bool in = k < k_end;
-      // columns past M (N) repeat the last chunk; those rows (columns) of C are not written
-      const uint16_t *gp = in ? P + static_cast<int64_t>(k) * ldp + min(row0 + lcol[h], M - 8) : g_zero_row + lcol[h];
-      const uint16_t *gq = in ? Q + static_cast<int64_t>(k) * ldq + min(col0 + lcol[h], N - 8) : g_zero_row + lcol[h];
-      __builtin_amdgcn_global_load_lds(static_cast<const void *>(gp), static_cast<void *>(ps(st) + loff[h]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(static_cast<const void *>(gq), static_cast<void *>(qs(st) + loff[h]), 16, 0, 0);
-    }
+    static_for<0, 2 * LA>([&](auto hc) { issue_one(st, kt, hc); });
   };
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -779,21 +815,39 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_tn_kernel(int M, in
     const u32x4 w = {h[0].x, h[0].y, h[1].x, h[1].y};
     return __builtin_bit_cast(bf16x8, w);
   };
-  auto compute = [&](auto st) {
+  auto load_frag = [&](auto st, int s, bf16x8(&a)[TM], bf16x8(&b)[TN]) {
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      bf16x8 a[TM], b[TN];
+    for (int i = 0; i < TM; ++i) a[i] = frag(ps(st), wm + 32 * i, 16 * s);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) a[i] = frag(ps(st), wm + 32 * i, 16 * s);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) b[j] = frag(qs(st), wn + 32 * j, 16 * s);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
+    for (int j = 0; j < TN; ++j) b[j] = frag(qs(st), wn + 32 * j, 16 * s);
   };
-  // ring of two stages, refilled before each product (see gemm_bf16_lds_kernel)
+  // hook(q) runs before the q-th MFMA of the K-tile
+  auto mma = [&](bf16x8(&a)[TM], bf16x8(&b)[TN], auto sc, auto &&hook) {
+    static_for<0, TM * TN>([&](auto qc) {
+      constexpr int i = decltype(qc)::value / TN, j = decltype(qc)::value % TN;
+      hook(std::integral_constant<int, decltype(sc)::value * TM * TN + decltype(qc)::value>{});
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    });
+  };
+  // fragments of k-step s + 1 are read while step s multiplies
+  auto compute = [&](auto st, auto &&hook) {
+    bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
+    load_frag(st, 0, a0, b0);
+    static_for<0, BK / 16>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      if constexpr (s % 2 == 0) {
+        if constexpr (s + 1 < BK / 16) load_frag(st, s + 1, a1, b1);
+        mma(a0, b0, sc, hook);
+      } else {
+        if constexpr (s + 1 < BK / 16) load_frag(st, s + 1, a0, b0);
+        mma(a1, b1, sc, hook);
+      }
+    });
+  };
+  // ring of two stages; the next K-tile's loads go out one at a time between
+  // the products of the first half of the current one (see gemm_bf16_lds_kernel)
+  constexpr int L = 2 * LA, NMF = TM * TN * (BK / 16);
+  auto slot = [](int h) { return h * (NMF / 2) / L; };
   if (nk > 0) issue(std::integral_constant<int, 0>{}, 0);
   wait_vmcnt<0>();
   barrier_no_fence();
@@ -802,9 +856,15 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_tn_kernel(int M, in
       constexpr int dd = decltype(du)::value;
       const int i = it + dd;
       if (i >= nk) return;
-      if (i + 1 < nk) issue(std::integral_constant<int, 1 - dd>{}, i + 1);
-      compute(std::integral_constant<int, dd>{});
-      wait_vmcnt<0>();
+      const bool more = i + 1 < nk;
+      compute(std::integral_constant<int, dd>{}, [&](auto qc) {
+        static_for<0, L>([&](auto hc) {
+          if constexpr (slot(decltype(hc)::value) == decltype(qc)::value) {
+            if (more) issue_one(std::integral_constant<int, 1 - dd>{}, i + 1, hc);
+          }
+        });
+      });
+      wait_ring<0>();
       barrier_no_fence();
     });
   }
