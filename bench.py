@@ -244,7 +244,8 @@ FAMILY_KERNELS = {
     "gemm_tn_f32": "::gemm_f32_kernel<false, false,",
     "gemm_nt_f32": "::gemm_f32_kernel<true, true,",
     "gemm_nn_f32": "::gemm_f32_kernel<true, false,",
-    "gemm_nt_bf16": "gemm_bf16",
+    "gemm_nt_bf16": "gemm_bf16_lds_kernel",  # forward and input-gradient launches alike
+    "gemm_dw_bf16": "gemm_bf16_tn_kernel",
     "rotate_in": "::scatter_in_",
     "aggregate": "::aggregate_",
     "hblocks": "hblocks_kernel",
