@@ -906,6 +906,133 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
 // recomputes Xt of its half from its node's row.  Each wave walks a strided
 // stream of nodes and keeps its partial sums in registers; partials are
 // written per stream and summed later in a fixed order.
+// bwd_row for bf16 storage and C = 2 * 64: lane i owns channels 2i and 2i + 1,
+// so Y and dY move as packed pairs (one 32-bit access per entry instead of two
+// 16-bit ones), and each rotated entry is formed for both channels from the
+// same geometry value and used at once, with no per-channel array of T kept.
+template <int LMAX, int MMAX>
+__global__ void __launch_bounds__(kThreads) bwd_row_pair_kernel(const int *__restrict__ row_ptr, int n_dst,
+                                                                const float *__restrict__ geom, int gstride,
+                                                                const float *__restrict__ alpha, CPtr3 Y, int C,
+                                                                const float *__restrict__ G,
+                                                                const float *__restrict__ w_att, Ptr3 dY,
+                                                                float *dalpha, float *watt_part) {
+  using L = Lay<LMAX, MMAX>;
+  constexpr int GS4 = (L::ND + 3) / 4;
+  __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
+  __shared__ int eids[kWavesPerBlock][kBatch];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int d = uniform(blockIdx.x * kWavesPerBlock + wave);
+  if (d >= n_dst) return;
+  EdgeList el;
+  el.perm = nullptr;
+  el.begin = uniform(row_ptr[d]);
+  el.count = uniform(row_ptr[d + 1]) - el.begin;
+  const int gs4 = (L::ND + 3) / 4;
+  const int c = 2 * lane;
+  float gd[L::K][2];
+#pragma unroll
+  for (int k = 0; k < L::K; ++k) {
+    const float2 g = *reinterpret_cast<const float2 *>(G + (static_cast<int64_t>(d) * L::K + k) * C + c);
+    gd[k][0] = g.x;
+    gd[k][1] = g.y;
+  }
+  auto unpack = [](uint32_t v, float &lo, float &hi) {
+    lo = __uint_as_float(v << 16);
+    hi = __uint_as_float(v & 0xFFFF0000u);
+  };
+  auto pack = [](float lo, float hi) { return __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(lo), static_cast<__bf16>(hi)}); };
+  // entry (l, m) of T_e = trunc(D_e G_d) for both channels
+  auto entry = [&](const float *gr, int l, int m, float &v0, float &v1) {
+    v0 = v1 = 0.0f;
+#pragma unroll
+    for (int mp = -l; mp <= l; ++mp) {
+      const float dv = gr[L::doff(l, m, mp)];
+      v0 += dv * gd[l * l + l + mp][0];
+      v1 += dv * gd[l * l + l + mp][1];
+    }
+  };
+  auto yrow = [&](int e, int mu) {
+    return reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(Y.p[mu]) +
+                                              static_cast<int64_t>(e) * L::blocks(mu) * C);
+  };
+  const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
+  float s_row = 0.0f, wacc0 = 0.0f, wacc1 = 0.0f;
+  if (el.count > 0) {
+    GeomPipe<GS4> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave]);
+    for (int base = 0; base < el.count; base += kBatch) {
+      const int cnt = min(kBatch, el.count - base);
+      gp.prefetch(base);
+      for (int i = 0; i < cnt; ++i) {
+        const int e = el.begin + base + i;
+        const float *gr = gb + i * GS4 * 4;
+        // all of the edge's Y loads before any use (see load_raw)
+        uint32_t yr[L::KEPT];
+#pragma unroll
+        for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
+            yr[L::kidx(l, m)] = yrow(e, cabs(m))[static_cast<uint32_t>((L::col(l, m) * C + c) / 2)];
+        __builtin_amdgcn_sched_barrier(0);
+        float p = 0.0f;
+#pragma unroll
+        for (int l = 0; l <= LMAX; ++l) {
+#pragma unroll
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+            float v0, v1, y0, y1;
+            entry(gr, l, m, v0, v1);
+            unpack(yr[L::kidx(l, m)], y0, y1);
+            p += y0 * v0 + y1 * v1;
+          }
+          // one degree's geometry at a time in registers
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        p = wave_sum(p);
+        dalpha[e] = p;  // every lane stores the same value and later reads its own store
+        s_row += alpha[e] * p;
+      }
+      gp.advance(base);
+    }
+    const float2 wat = *reinterpret_cast<const float2 *>(w_att + c);
+    GeomPipe<GS4> gp2(el, geom, gstride, gs4, gbuf[wave], eids[wave]);
+    for (int base = 0; base < el.count; base += kBatch) {
+      const int cnt = min(kBatch, el.count - base);
+      gp2.prefetch(base);
+      for (int i = 0; i < cnt; ++i) {
+        const int e = el.begin + base + i;
+        const float *gr = gb + i * GS4 * 4;
+        const float a = alpha[e];
+        const float da = a * (dalpha[e] - s_row);
+        float y00, y01;
+        unpack(yrow(e, 0)[static_cast<uint32_t>((L::col(0, 0) * C + c) / 2)], y00, y01);
+#pragma unroll
+        for (int l = 0; l <= LMAX; ++l) {
+#pragma unroll
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+            float v0, v1;
+            entry(gr, l, m, v0, v1);
+            v0 *= a;
+            v1 *= a;
+            if (l == 0) {
+              v0 += da * wat.x * dsilu(y00);
+              v1 += da * wat.y * dsilu(y01);
+              wacc0 += da * silu(y00);
+              wacc1 += da * silu(y01);
+            }
+            const int mu = cabs(m);
+            uint32_t *row = reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(dY.p[mu]) +
+                                                         static_cast<int64_t>(e) * L::blocks(mu) * C);
+            row[static_cast<uint32_t>((L::col(l, m) * C + c) / 2)] = pack(v0, v1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      gp2.advance(base);
+    }
+  }
+  *reinterpret_cast<float2 *>(watt_part + static_cast<int64_t>(d) * C + c) = make_float2(wacc0, wacc1);
+}
+
 template <int LMAX, int MMAX, int NRBF, typename T>
 __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restrict__ row_ptr,
                                                              const int *__restrict__ src_ptr,
@@ -1066,14 +1193,20 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
 #pragma unroll
             for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[k][p];
           }
+          // gated entries h = g dxt once per (l, m), then one FMA per Wigner-D term
+          float h[L::KEPT];
+#pragma unroll
+          for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
+              h[L::kidx(l, m)] = g[pair_index(cabs(m), l, LMAX)] * dxt[L::kidx(l, m)];
 #pragma unroll
           for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
             for (int mp = -l; mp <= l; ++mp) {
               float s = 0.0f;
 #pragma unroll
-              for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
-                s += gr[L::doff(l, m, mp)] * g[pair_index(cabs(m), l, LMAX)] * dxt[L::kidx(l, m)];
+              for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) s += gr[L::doff(l, m, mp)] * h[L::kidx(l, m)];
               acc[l * l + l + mp] += s;
             }
         }
@@ -1318,7 +1451,10 @@ struct Launch {
     constexpr bool bf = std::is_same<TY, uint16_t>::value;
     Ptr3 dY = bf ? Ptr3{{w.dYb[0], w.dYb[1], w.dYb[2]}} : Ptr3{{w.dY[0], w.dY[1], w.dY[2]}};
     const unsigned grid = ceil_div(g->n_dst, kWavesPerBlock);
-    if (s.C <= 64)
+    if (bf && s.C == 2 * kWave)
+      bwd_row_pair_kernel<LMAX, MMAX><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C,
+                                                                 G, w_att, dY, w.dalpha, w.watt_part);
+    else if (s.C <= 64)
       bwd_row_kernel<LMAX, MMAX, 1, TY, TY><<<grid, kThreads, 0, st>>>(
           g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C, G, w_att, dY, w.dalpha, w.watt_part);
     else if (s.C <= 128)
