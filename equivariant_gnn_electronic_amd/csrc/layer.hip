@@ -1125,14 +1125,17 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
 // D_e^T (g_e * dX_e)[source half], with dX the GEMM gradient of the gated
 // edge-frame input.  The waves of one node (two halves x channel chunks) sit
 // in one block and their partial sums are added through LDS in a fixed order.
-template <int LMAX, int MMAX, int NRBF, typename TdA>
+// PK: the gates come from the radial weights packed as bf16 pairs over the
+// basis index and the basis values rounded to bf16 pairs, by the same packed
+// dot products as the paired rotate-in, so they are the gates that forward used.
+template <int LMAX, int MMAX, int NRBF, typename TdA, bool PK = false>
 __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__restrict__ row_ptr,
                                                                const int *__restrict__ src_ptr,
                                                                const int *__restrict__ src_perm,
                                                                const float *__restrict__ geom, int gstride, int n_dst,
                                                                int n_src, int C, const float *__restrict__ wrad,
-                                                               int n_rbf, CPtr3 dA, const float *__restrict__ G,
-                                                               float *__restrict__ gx) {
+                                                               const uint32_t *__restrict__ wpk, int n_rbf, CPtr3 dA,
+                                                               const float *__restrict__ G, float *__restrict__ gx) {
   using L = Lay<LMAX, MMAX>;
   constexpr int GS4 = (L::ND + NRBF + 3) / 4;
   const int gs4 = (L::ND + n_rbf + 3) / 4;
@@ -1152,8 +1155,17 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
   for (int k = 0; k < L::K; ++k) acc[k] = 0.0f;
   if (live) {
     const EdgeList el = edge_list(nw.node, nw.half, n_dst, row_ptr, src_ptr, src_perm);
-    float wr[NRBF][L::NP];
-    load_wrad<LMAX, MMAX, NRBF>(wrad, n_rbf, C2, j, active, wr);
+    float wr[PK ? 1 : NRBF][L::NP];
+    bf16x2 wp[PK ? NRBF / 2 : 1][L::NP];
+    if constexpr (PK) {
+#pragma unroll
+      for (int q = 0; q < NRBF / 2; ++q)
+#pragma unroll
+        for (int p = 0; p < L::NP; ++p)
+          wp[q][p] = __builtin_bit_cast(bf16x2, wpk[(static_cast<int64_t>(q) * L::NP + p) * C2 + (active ? j : 0)]);
+    } else {
+      load_wrad<LMAX, MMAX, NRBF>(wrad, n_rbf, C2, j, active, wr);
+    }
     const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
     if (el.count > 0) {
       GeomPipe<GS4> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave]);
@@ -1186,12 +1198,23 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
           float g[L::NP];
 #pragma unroll
           for (int p = 0; p < L::NP; ++p) g[p] = 0.0f;
+          if constexpr (PK) {
 #pragma unroll
-          for (int k = 0; k < NRBF; ++k) {
-            const float raw = gr[L::ND + k];  // in the staged row; select, no branch
-            const float ph = k < n_rbf ? raw : 0.0f;
+            for (int q = 0; q < NRBF / 2; ++q) {
+              const float r0 = gr[L::ND + 2 * q], r1 = gr[L::ND + 2 * q + 1];
+              const bf16x2 ph = {static_cast<__bf16>(2 * q < n_rbf ? r0 : 0.0f),
+                                 static_cast<__bf16>(2 * q + 1 < n_rbf ? r1 : 0.0f)};
 #pragma unroll
-            for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[k][p];
+              for (int p = 0; p < L::NP; ++p) g[p] = __builtin_amdgcn_fdot2_f32_bf16(ph, wp[q][p], g[p], false);
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < NRBF; ++k) {
+              const float raw = gr[L::ND + k];  // in the staged row; select, no branch
+              const float ph = k < n_rbf ? raw : 0.0f;
+#pragma unroll
+              for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[k][p];
+            }
           }
           // gated entries h = g dxt once per (l, m), then one FMA per Wigner-D term
           float h[L::KEPT];
@@ -1345,7 +1368,14 @@ struct BwdWs {
   int64_t P_floats;  // its size
   float *wrad_part;
   float *dWexp;        // bf16: summed gradient of the expanded weight of one |m|
+  uint32_t *wpk;       // bf16: radial weights packed as in the forward (pack_wrad_kernel)
 };
+
+// bf16 layers whose rotate-in runs on channel pairs, with the radial weights
+// packed as bf16 pairs (16 basis functions would spill there)
+inline bool paired_gates(const LayerShape &s) {
+  return s.storage == EGNN_BF16 && s.C % (2 * kWave) == 0 && s.n_rbf <= 8;
+}
 
 // node streams of the radial-weight gradient (fixed by the node count, so the
 // summation order of its partials is reproducible)
@@ -1376,6 +1406,7 @@ BwdWs carve_bwd_ws(Carver &cv, const LayerShape &s, int64_t E, int n_dst, int n_
   w.P_floats = static_cast<int64_t>(pmax) * dw_splits(E);
   w.wrad_part = cv.take<float>(static_cast<size_t>(wrad_streams(n_src)) * s.n_rbf * s.n_pairs * 2 * s.C);
   if (bf) w.dWexp = cv.take<float>(pmax);
+  w.wpk = bf ? cv.take<uint32_t>(static_cast<size_t>(8) * s.n_pairs * 2 * s.C) : nullptr;
   return w;
 }
 
@@ -1410,7 +1441,7 @@ struct Launch {
                         const uint32_t *wpk, const Acts &a, hipStream_t st) {
     Ptr3 A{{a.A[0], a.A[1], a.A[2]}};
     if constexpr (std::is_same<T, uint16_t>::value && std::is_same<TA, uint16_t>::value) {
-      if (wpk && s.C % (2 * kWave) == 0 && s.n_rbf <= 8) {  // channel pairs (16 basis functions would spill)
+      if (wpk && paired_gates(s)) {  // channel pairs
         const int nch2 = s.C / (2 * kWave);
         const unsigned grid2 = ceil_div(static_cast<int64_t>(g->n_src) * 2 * nch2, kWavesPerBlock);
         scatter_in_pair_kernel<LMAX, MMAX, 8><<<grid2, kThreads, 0, st>>>(
@@ -1497,26 +1528,31 @@ struct Launch {
     else
       bwd_gate_t<float>(g, s, geom, static_cast<const float *>(x), w, st);
   }
+  // wpk: packed radial weights where the forward used them (paired rotate-in), else null
   template <typename TdA>
   static void bwd_node_t(const egnn_graph *g, const LayerShape &s, const float *geom, const float *G,
-                         const float *wrad, CPtr3 dA, float *gx, hipStream_t st) {
+                         const float *wrad, const uint32_t *wpk, CPtr3 dA, float *gx, hipStream_t st) {
     const int nch = (s.C + kWave - 1) / kWave;
     const unsigned grid = ceil_div(static_cast<int64_t>(g->n_src) * 2 * nch, kWavesPerBlock);
-    if (s.n_rbf <= 8)
+    if (wpk)
+      gather_grad_kernel<LMAX, MMAX, 8, TdA, true><<<grid, kThreads, 0, st>>>(
+          g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride, g->n_dst, g->n_src, s.C, wrad, wpk, s.n_rbf, dA, G, gx);
+    else if (s.n_rbf <= 8)
       gather_grad_kernel<LMAX, MMAX, 8, TdA><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom,
                                                                         s.gstride, g->n_dst, g->n_src, s.C, wrad,
-                                                                        s.n_rbf, dA, G, gx);
+                                                                        nullptr, s.n_rbf, dA, G, gx);
     else
       gather_grad_kernel<LMAX, MMAX, 16, TdA><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom,
                                                                          s.gstride, g->n_dst, g->n_src, s.C, wrad,
-                                                                         s.n_rbf, dA, G, gx);
+                                                                         nullptr, s.n_rbf, dA, G, gx);
   }
   static void bwd_node(const egnn_graph *g, const LayerShape &s, const float *geom, const float *G, const float *wrad,
                        const BwdWs &w, float *gx, hipStream_t st) {
     if (s.storage == EGNN_BF16)
-      bwd_node_t<uint16_t>(g, s, geom, G, wrad, CPtr3{{w.dAb[0], w.dAb[1], w.dAb[2]}}, gx, st);
+      bwd_node_t<uint16_t>(g, s, geom, G, wrad, paired_gates(s) ? w.wpk : nullptr,
+                           CPtr3{{w.dAb[0], w.dAb[1], w.dAb[2]}}, gx, st);
     else
-      bwd_node_t<float>(g, s, geom, G, wrad, CPtr3{{w.dA[0], w.dA[1], w.dA[2]}}, gx, st);
+      bwd_node_t<float>(g, s, geom, G, wrad, nullptr, CPtr3{{w.dA[0], w.dA[1], w.dA[2]}}, gx, st);
   }
 };
 
@@ -1923,6 +1959,10 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
     } else {
       const double bytes = double(E) * (sumK * (bf ? 2.0 : 4.0) + s.nD * 4.0 + 8.0) + double(g->n_dst) * s.K * s.C * 4.0 +
                            double(g->n_src) * s.K * s.C * 4.0;
+      if (paired_gates(s)) {
+        const int64_t n = static_cast<int64_t>(8) * s.n_pairs * 2 * s.C;
+        pack_wrad_kernel<<<ceil_div(n, T), T, 0, stream>>>(weights + wo.wrad, s.n_rbf, s.n_pairs, 2 * s.C, w.wpk);
+      }
       Timed t(stream, "bwd_node", 0.0, bytes);
       EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_node_launch, g, s, geom, grad_out, weights + wo.wrad, w, grad_x_in, stream);
     }
