@@ -5,8 +5,11 @@ The 64-atom periodic cell (several images per pair) carries every
 instantiation the ABI dispatches to is exercised: lmax 1-4, mmax 0-2, C with
 a partial 64-channel chunk (24, 96) and two chunks (128), 3/4/6/8/12/16 radial
 functions, bf16 storage on both bf16 GEMM variants and the fallback for
-K not a multiple of 32, and the channel-pair rotate-in (bf16, C = 128); forward and backward for every one.  Also: an open cell with isolated atoms (rows without
-incoming edges) and ghosts, and a graph with no edges at all.
+K not a multiple of 32, and the channel-pair kernels (bf16, C = 128: rotate-in,
+aggregate, the backward row kernel at every (lmax, mmax), the node gradient with
+packed gates); forward and backward for every one.  Also: an open cell with
+isolated atoms (rows without incoming edges) and ghosts, in fp32 and on the bf16
+channel pairs, and a graph with no edges at all.
 Tolerances as in test_gpu_parity.
 """
 import dataclasses
@@ -39,6 +42,15 @@ VARIANTS = [
     (2, 0, 64, 4, "bf16"),
     (2, 1, 128, 6, "bf16"),   # two channels per lane in rotate-in (C a multiple of 128, n_rbf <= 8)
     (4, 2, 128, 3, "bf16"),   # the same with an odd basis count (last basis pair half zero)
+    (1, 0, 128, 8, "bf16"),   # channel pairs (bf16, C = 128) at every (lmax, mmax) of the backward row kernel
+    (1, 1, 128, 2, "bf16"),
+    (2, 0, 128, 8, "bf16"),
+    (2, 2, 128, 4, "bf16"),
+    (3, 0, 128, 8, "bf16"),
+    (3, 1, 128, 7, "bf16"),
+    (3, 2, 128, 8, "bf16"),
+    (4, 0, 128, 5, "bf16"),
+    (4, 1, 128, 16, "bf16"),  # pairs in the backward row kernel, per-channel rotate-in (16 basis functions)
 ]
 
 
@@ -104,8 +116,11 @@ OPEN_SPARSE = synth.Config("open_sparse", 12, (40,), (12.0, 12.0, 12.0), False, 
                            note="open cell, sparse enough that some atoms have no neighbour; ghost shell")
 
 
-def test_open_cell_isolated_rows(dev):
+@pytest.mark.parametrize("variant", ["f32", "bf16_pairs"])
+def test_open_cell_isolated_rows(dev, variant):
     cfg = OPEN_SPARSE
+    if variant == "bf16_pairs":
+        cfg = dataclasses.replace(cfg, C=128, storage="bf16")
     s = synth.make_structure(cfg)
     assert s.n_src > s.n_dst
     r = _run(cfg, s, dev, True)
@@ -114,7 +129,8 @@ def test_open_cell_isolated_rows(dev):
     _check(cfg, s, r, True)
     # rows without edges keep x, and their own gradient is G
     empty = np.flatnonzero(indeg == 0)
-    np.testing.assert_array_equal(r["xo"][empty], r["x"][empty])
+    kept = r["x"][empty] if cfg.storage == "f32" else synth.bf16_round(r["x"][empty])
+    np.testing.assert_array_equal(r["xo"][empty], kept)
 
 
 def test_no_edges(dev):
