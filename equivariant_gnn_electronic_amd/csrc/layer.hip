@@ -724,11 +724,11 @@ __global__ void __launch_bounds__(kThreads) aggregate_pair_kernel(const int *__r
     for (int base = 0; base < el.count; base += kBatch) {
       const int cnt = min(kBatch, el.count - base);
       gp.prefetch(base);
-      for (int i = 0; i < cnt; ++i) {
-        const int e = el.begin + base + i;
-        const float a = abuf[wave][i];
-        const float *gr = gb + i * GS4 * 4;
-        uint32_t yr[L::KEPT];
+      // the next edge's Y loads go out before this edge's products: two named
+      // buffers, two edges per round (the last round repeats an edge's loads
+      // and skips its products)
+      auto load_y = [&](int i, uint32_t(&yr)[L::KEPT]) {
+        const int e = el.begin + base + min(i, cnt - 1);
 #pragma unroll
         for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
@@ -738,6 +738,11 @@ __global__ void __launch_bounds__(kThreads) aggregate_pair_kernel(const int *__r
                                                                      static_cast<int64_t>(e) * L::blocks(mu) * C);
             yr[L::kidx(l, m)] = row[static_cast<uint32_t>((L::col(l, m) * C + c) / 2)];
           }
+      };
+      auto product = [&](int i, const uint32_t(&yr)[L::KEPT]) {
+        const int e = el.begin + base + i;
+        const float a = abuf[wave][i];
+        const float *gr = gb + i * GS4 * 4;
         uint32_t *eo = edge_out ? reinterpret_cast<uint32_t *>(edge_out + static_cast<int64_t>(e) * L::K * C) : nullptr;
 #pragma unroll
         for (int l = 0; l <= LMAX; ++l)
@@ -756,6 +761,14 @@ __global__ void __launch_bounds__(kThreads) aggregate_pair_kernel(const int *__r
             acc[l * l + l + mp][1] += a * m1;
             if (eo) eo[static_cast<uint32_t>(((l * l + l + mp) * C + c) / 2)] = pack(m0, m1);
           }
+      };
+      uint32_t ya[L::KEPT], yb[L::KEPT];
+      load_y(0, ya);
+      for (int i = 0; i < cnt; i += 2) {
+        load_y(i + 1, yb);
+        product(i, ya);
+        load_y(i + 2, ya);
+        if (i + 1 < cnt) product(i + 1, yb);
       }
       gp.advance(base);
     }
