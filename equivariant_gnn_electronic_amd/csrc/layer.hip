@@ -1084,42 +1084,61 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
     for (int base = 0; base < el.count; base += kBatch) {
       const int cnt = min(kBatch, el.count - base);
       gp.prefetch(base);
-      for (int i = 0; i < cnt; ++i) {
-        const int e = uniform(eids[wave][i]);
+      // the next edge's dA loads go out before this edge's products (two named
+      // buffers, two edges per round, as in gather_grad_kernel); idle lanes
+      // load a clamped channel and their sums are never written
+      using Raw = typename RawOf<T>::type;
+      const int jl = half * C + min(c, C - 1);
+      auto load_da = [&](int i, Raw(&raw)[L::KEPT]) {
+        const int e = uniform(eids[wave][min(i, cnt - 1)]);
+        const T *rowp[MMAX + 1];  // wave-uniform row bases, 32-bit lane offsets; dA in the storage type
+#pragma unroll
+        for (int mu = 0; mu <= MMAX; ++mu)
+          rowp[mu] = static_cast<const T *>(dA.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
+#pragma unroll
+        for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
+            raw[L::kidx(l, m)] = load_raw(rowp[cabs(m)], static_cast<uint32_t>(L::col(l, m) * C2 + jl));
+      };
+      auto product = [&](int i, const Raw(&raw)[L::KEPT]) {
         const float *gr = gb + i * GS4 * 4;
         float dg[L::NP];
 #pragma unroll
         for (int p = 0; p < L::NP; ++p) dg[p] = 0.0f;
-        if (active) {
-          const T *rowp[MMAX + 1];  // wave-uniform row bases, 32-bit lane offsets; dA in the storage type
 #pragma unroll
-          for (int mu = 0; mu <= MMAX; ++mu)
-            rowp[mu] = static_cast<const T *>(dA.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
-          // all of the edge's loads before any use (see load_raw)
-          typename RawOf<T>::type raw[L::KEPT];
+        for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
-          for (int l = 0; l <= LMAX; ++l)
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+            float xt = 0.0f;
 #pragma unroll
-            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
-              raw[L::kidx(l, m)] = load_raw(rowp[cabs(m)], static_cast<uint32_t>(L::col(l, m) * C2 + j));
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int l = 0; l <= LMAX; ++l)
-#pragma unroll
-            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
-              float xt = 0.0f;
-#pragma unroll
-              for (int mp = -l; mp <= l; ++mp) xt += gr[L::doff(l, m, mp)] * xv[l * l + l + mp];
-              const float dx = from_raw(raw[L::kidx(l, m)], static_cast<uint32_t>(L::col(l, m) * C2 + j));
-              dg[pair_index(cabs(m), l, LMAX)] += dx * xt;
-            }
-        }
+            for (int mp = -l; mp <= l; ++mp) xt += gr[L::doff(l, m, mp)] * xv[l * l + l + mp];
+            const float dx = from_raw(raw[L::kidx(l, m)], static_cast<uint32_t>(L::col(l, m) * C2 + jl));
+            dg[pair_index(cabs(m), l, LMAX)] += dx * xt;
+          }
 #pragma unroll
         for (int k = 0; k < NRBF; ++k) {
-          const float raw = gr[L::ND + k];  // in the staged row; select, no branch
-          const float ph = k < n_rbf ? raw : 0.0f;
+          const float rv = gr[L::ND + k];  // in the staged row; select, no branch
+          const float ph = k < n_rbf ? rv : 0.0f;
 #pragma unroll
           for (int p = 0; p < L::NP; ++p) acc[k][p] += ph * dg[p];
+        }
+      };
+      if constexpr (NRBF > 8) {  // 16 radial functions: no registers for a second buffer
+        for (int i = 0; i < cnt; ++i) {
+          Raw ra[L::KEPT];
+          load_da(i, ra);
+          __builtin_amdgcn_sched_barrier(0);
+          product(i, ra);
+        }
+      } else {
+        Raw ra[L::KEPT], rb[L::KEPT];
+        load_da(0, ra);
+        for (int i = 0; i < cnt; i += 2) {
+          load_da(i + 1, rb);
+          product(i, ra);
+          load_da(i + 2, ra);
+          if (i + 1 < cnt) product(i + 1, rb);
         }
       }
       gp.advance(base);
@@ -1185,29 +1204,32 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
       for (int base = 0; base < el.count; base += kBatch) {
         const int cnt = min(kBatch, el.count - base);
         gp.prefetch(base);
-        for (int i = 0; i < cnt; ++i) {
-          const int e = uniform(eids[wave][i]);
-          const float *gr = gb + i * GS4 * 4;
-          if (!active) continue;
+        // the next edge's dA loads go out before this edge's products: two named
+        // buffers, two edges per round (the last round repeats an edge's loads
+        // and skips its products).  Idle lanes load a clamped channel and their
+        // sums are never written.
+        using Raw = typename RawOf<TdA>::type;
+        const int jl = nw.half * C + min(c, C - 1);
+        auto load_da = [&](int i, Raw(&raw)[L::KEPT]) {
+          const int e = uniform(eids[wave][min(i, cnt - 1)]);
           const TdA *rowp[MMAX + 1];  // wave-uniform row bases, 32-bit lane offsets
 #pragma unroll
           for (int mu = 0; mu <= MMAX; ++mu)
             rowp[mu] = static_cast<const TdA *>(dA.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
-          // all of the edge's loads are issued before any is used (the barrier keeps
-          // the scheduler from pairing each load with its use)
-          typename RawOf<TdA>::type raw[L::KEPT];
 #pragma unroll
           for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
             for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
-              raw[L::kidx(l, m)] = load_raw(rowp[cabs(m)], static_cast<uint32_t>(L::col(l, m) * C2 + j));
-          __builtin_amdgcn_sched_barrier(0);
+              raw[L::kidx(l, m)] = load_raw(rowp[cabs(m)], static_cast<uint32_t>(L::col(l, m) * C2 + jl));
+        };
+        auto product = [&](int i, const Raw(&raw)[L::KEPT]) {
+          const float *gr = gb + i * GS4 * 4;
           float dxt[L::KEPT];
 #pragma unroll
           for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
             for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
-              dxt[L::kidx(l, m)] = from_raw(raw[L::kidx(l, m)], static_cast<uint32_t>(L::col(l, m) * C2 + j));
+              dxt[L::kidx(l, m)] = from_raw(raw[L::kidx(l, m)], static_cast<uint32_t>(L::col(l, m) * C2 + jl));
           float g[L::NP];
 #pragma unroll
           for (int p = 0; p < L::NP; ++p) g[p] = 0.0f;
@@ -1222,11 +1244,11 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
             }
           } else {
 #pragma unroll
-            for (int k = 0; k < NRBF; ++k) {
-              const float raw = gr[L::ND + k];  // in the staged row; select, no branch
-              const float ph = k < n_rbf ? raw : 0.0f;
+            for (int kk = 0; kk < NRBF; ++kk) {
+              const float rv = gr[L::ND + kk];  // in the staged row; select, no branch
+              const float ph = kk < n_rbf ? rv : 0.0f;
 #pragma unroll
-              for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[k][p];
+              for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[kk][p];
             }
           }
           // gated entries h = g dxt once per (l, m), then one FMA per Wigner-D term
@@ -1240,11 +1262,28 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
           for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
             for (int mp = -l; mp <= l; ++mp) {
-              float s = 0.0f;
+              float sum = 0.0f;
 #pragma unroll
-              for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) s += gr[L::doff(l, m, mp)] * h[L::kidx(l, m)];
-              acc[l * l + l + mp] += s;
+              for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) sum += gr[L::doff(l, m, mp)] * h[L::kidx(l, m)];
+              acc[l * l + l + mp] += sum;
             }
+        };
+        if constexpr (NRBF > 8) {  // 16 radial functions: no registers for a second buffer
+          for (int i = 0; i < cnt; ++i) {
+            Raw ra[L::KEPT];
+            load_da(i, ra);
+            __builtin_amdgcn_sched_barrier(0);
+            product(i, ra);
+          }
+        } else {
+          Raw ra[L::KEPT], rb[L::KEPT];
+          load_da(0, ra);
+          for (int i = 0; i < cnt; i += 2) {
+            load_da(i + 1, rb);
+            product(i, ra);
+            load_da(i + 2, ra);
+            if (i + 1 < cnt) product(i + 1, rb);
+          }
         }
         gp.advance(base);
       }
@@ -1501,11 +1540,8 @@ struct Launch {
     else if (s.C <= 64)
       bwd_row_kernel<LMAX, MMAX, 1, TY, TY><<<grid, kThreads, 0, st>>>(
           g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C, G, w_att, dY, w.dalpha, w.watt_part);
-    else if (s.C <= 128)
+    else  // C <= 128: egnn_layer_bwd rejects wider layers before any launch
       bwd_row_kernel<LMAX, MMAX, 2, TY, TY><<<grid, kThreads, 0, st>>>(
-          g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C, G, w_att, dY, w.dalpha, w.watt_part);
-    else
-      bwd_row_kernel<LMAX, MMAX, 4, TY, TY><<<grid, kThreads, 0, st>>>(
           g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C, G, w_att, dY, w.dalpha, w.watt_part);
   }
   // dY is written in the storage type (bf16 feeds the bf16 GEMMs directly)
