@@ -289,6 +289,19 @@ __device__ inline void load_run(const T *p, float (&a)[S]) {
       a[4 * i + 2] = v.z;
       a[4 * i + 3] = v.w;
     }
+  } else if constexpr (sizeof(T) == 2 && S % 8 == 0) {
+    // bf16: eight channels per 16-byte load (a run starts at a multiple of S
+    // channels of a row of K C, so it is 16-byte aligned)
+#pragma unroll
+    for (int i = 0; i < S / 8; ++i) {
+      const uint4 v = reinterpret_cast<const uint4 *>(p)[i];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        a[8 * i + 2 * h] = __uint_as_float(w[h] << 16);
+        a[8 * i + 2 * h + 1] = __uint_as_float(w[h] & 0xFFFF0000u);
+      }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < S; ++i) a[i] = Store<T>::ld(p + i);
@@ -475,6 +488,10 @@ extern "C" egnn_status egnn_hblocks(const egnn_hdesc *h, int64_t n_edges, int32_
   EGNN_REQUIRE(n_edges >= 0 && n_nodes >= 0, "negative row count");
   if (n_edges > 0) EGNN_REQUIRE(w_edge && edge_irreps && h_edge, "edge pointers are null");
   if (n_nodes > 0) EGNN_REQUIRE(w_node && node_irreps && h_onsite, "node pointers are null");
+  // each lane reads its channel run with 16-byte loads
+  auto aligned16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  if (n_edges > 0) EGNN_REQUIRE(aligned16(edge_irreps), "edge irreps must be 16-byte aligned");
+  if (n_nodes > 0) EGNN_REQUIRE(aligned16(node_irreps), "node irreps must be 16-byte aligned");
   if (n_edges == 0 && n_nodes == 0) return EGNN_OK;
   int slot = 0;
   Layout lay;

@@ -218,7 +218,8 @@ egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph *g, const 
  * Weights w_edge / w_node: fp32 [sum_L n_L][C], L ascending, rows k.
  * Edge blocks read edge irreps [n_edges][K][C] (rows = source orbitals,
  * columns = destination orbitals); on-site blocks read node irreps
- * [n_nodes][K][C].  Either part may be skipped with n = 0 / NULL.
+ * [n_nodes][K][C], both 16-byte aligned (EGNN_E_ARG otherwise; hipMalloc and
+ * torch allocations are).  Either part may be skipped with n = 0 / NULL.
  * Requires lmax >= 2*max(shell_l).
  * ------------------------------------------------------------------------- */
 typedef struct {

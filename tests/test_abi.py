@@ -181,6 +181,20 @@ def test_decode_description_checks(lib):
     assert lib.egnn_hblocks(ct.byref(h), 0, 0, None, None, None, None, None, None, None) == 0
 
 
+def test_decode_rejects_misaligned_irreps(lib):
+    """The decode reads each lane's channel run with 16-byte loads; the host
+    check rejects irreps that are not 16-byte aligned before anything runs."""
+    from equivariant_gnn_electronic_amd import _lib
+    arr = (ct.c_int32 * 5)(0, 0, 1, 1, 2)
+    h = _lib.EgnnHDesc(4, 64, 5, arr, 1)
+    p = ct.c_void_p(0x1000)
+    odd = ct.c_void_p(0x1008)
+    st = lib.egnn_hblocks(ct.byref(h), 10, 0, p, None, odd, None, p, None, None)
+    assert st == _lib.EGNN_E_ARG and b"aligned" in lib.egnn_last_error()
+    st = lib.egnn_hblocks(ct.byref(h), 0, 4, None, p, None, odd, None, p, None)
+    assert st == _lib.EGNN_E_ARG and b"aligned" in lib.egnn_last_error()
+
+
 def test_timing_collect_without_events(lib):
     from equivariant_gnn_electronic_amd import _lib
     out = (_lib.EgnnTimingEntry * 4)()
