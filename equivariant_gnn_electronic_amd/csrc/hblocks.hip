@@ -351,30 +351,34 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
   const int lmax_lab = tb.lmax_lab;
   const int n_runs = (lmax_lab + 1) * (lmax_lab + 1);  // (L, M) runs of a row, in L^2 + L + M order
   const int64_t n_tiles = (rows + kTile - 1) / kTile;
-  const int64_t tile_step = static_cast<int64_t>(gridDim.x) * kWaves;
   auto row_of = [&](int64_t tile) {
     const int64_t ea = min(tile * kTile + i16, rows - 1);  // clamped row for loads
     return irreps + ea * K * C + grp * S;
   };
-  // The runs of this wave's tiles form one sequence q (tile q / n_runs, run
-  // q % n_runs).  Run q + 1 loads while run q multiplies, into the other of two
-  // named buffers (the loop is unrolled by two, so no register copies), and a
-  // tile's entries are formed after its last run, while the next tile's first
-  // run is in flight.
-  const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  // The runs of this wave's tiles form one sequence (tile, run r of the tile,
+  // its degree L and order M), stepped one run at a time without divisions.
+  // Run k + 1 loads while run k multiplies, into the other of two named
+  // buffers (the loop is unrolled by two, so no register copies), and a tile's
+  // entries are formed after its last run, while the next tile's first run is
+  // in flight.
+  struct Pos {
+    int64_t tile;
+    int r, L, M;
+  };
+  auto next = [&](Pos p) {
+    if (++p.r == n_runs) return Pos{p.tile + static_cast<int64_t>(gridDim.x) * kWaves, 0, 0, 0};
+    if (++p.M > p.L) {
+      ++p.L;
+      p.M = -p.L;
+    }
+    return p;
+  };
   // unconditional (past the last tile row_of clamps to the last row, and the
   // run is never used): a branch here would make the compiler wait for every
   // load in flight before each MFMA chain
-  auto issue = [&](int64_t q, float(&dst)[S]) {
-    load_run<S>(row_of(tile0 + (q / n_runs) * tile_step) + (q % n_runs) * C, dst);
-  };
-  auto run = [&](int64_t q, const float(&a)[S]) {
-    const int64_t tile = tile0 + (q / n_runs) * tile_step;
-    const int r = static_cast<int>(q % n_runs);
-    int L = static_cast<int>(sqrtf(static_cast<float>(r)));
-    while (L * L > r) --L;
-    while ((L + 1) * (L + 1) <= r) ++L;
-    const int M = r - L * L - L;
+  auto issue = [&](const Pos &p, float(&dst)[S]) { load_run<S>(row_of(p.tile) + p.r * C, dst); };
+  auto run = [&](const Pos &p, const float(&a)[S]) {
+    const int L = p.L, M = p.M;
     const int nL = l_n[L];
     const int ntile = (nL + 15) / 16;
     const int woff = l_woff[L], hoff = l_hoff[L];
@@ -394,8 +398,8 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
         for (int rr = 0; rr < 4; ++rr) hs[(4 * grp + rr) * lab_ld + hoff + (M + L) * nL + k] = acc[rr];
       }
     }
-    if (r == n_runs - 1) {  // the tile's labels are complete: its entries
-      const int64_t e0 = tile * kTile;
+    if (p.r == n_runs - 1) {  // the tile's labels are complete: its entries
+      const int64_t e0 = p.tile * kTile;
       wave_lds_order();
       for (int qq = lane; qq < kTile * n_ent; qq += kWave) {
         const int el = qq / n_ent, ent = qq - el * n_ent;
@@ -409,15 +413,17 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
       wave_lds_order();
     }
   };
-  auto live = [&](int64_t q) { return tile0 + (q / n_runs) * tile_step < n_tiles; };
   float a0[S], a1[S];
-  issue(0, a0);
-  for (int64_t q = 0; live(q); q += 2) {
-    issue(q + 1, a1);
-    run(q, a0);
-    if (!live(q + 1)) break;
-    issue(q + 2, a0);
-    run(q + 1, a1);
+  Pos p0{static_cast<int64_t>(blockIdx.x) * kWaves + wave, 0, 0, 0};
+  issue(p0, a0);
+  while (p0.tile < n_tiles) {
+    const Pos p1 = next(p0);
+    issue(p1, a1);
+    run(p0, a0);
+    if (p1.tile >= n_tiles) break;
+    p0 = next(p1);
+    issue(p0, a0);
+    run(p1, a1);
   }
 }
 
