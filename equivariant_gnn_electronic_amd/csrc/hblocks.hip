@@ -399,16 +399,29 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
       }
     }
     if (p.r == n_runs - 1) {  // the tile's labels are complete: its entries
+      // lane = entry, eight rows of the tile at a time, so each term's
+      // coefficient and label index are read once per eight rows
+      constexpr int R = 8;
       const int64_t e0 = p.tile * kTile;
+      const int nrow = static_cast<int>(min(static_cast<int64_t>(kTile), rows - e0));
       wave_lds_order();
-      for (int qq = lane; qq < kTile * n_ent; qq += kWave) {
-        const int el = qq / n_ent, ent = qq - el * n_ent;
-        if (e0 + el >= rows) break;
-        const float *h = hs + el * lab_ld;
-        float acc = 0.0f;
-        const int t1 = t_start[ent + 1];
-        for (int t = t_start[ent]; t < t1; ++t) acc += t_coef[t] * h[t_idx[t]];
-        H[(e0 + el) * n_ent + ent] = acc;
+      for (int ent = lane; ent < n_ent; ent += kWave) {
+        const int t0 = t_start[ent], t1 = t_start[ent + 1];
+        for (int r0 = 0; r0 < nrow; r0 += R) {
+          float acc[R];
+#pragma unroll
+          for (int el = 0; el < R; ++el) acc[el] = 0.0f;
+#pragma unroll 1
+          for (int t = t0; t < t1; ++t) {
+            const float cf = t_coef[t];
+            const int ix = t_idx[t];
+#pragma unroll
+            for (int el = 0; el < R; ++el) acc[el] += cf * hs[(r0 + el) * lab_ld + ix];
+          }
+#pragma unroll
+          for (int el = 0; el < R; ++el)
+            if (r0 + el < nrow) H[(e0 + r0 + el) * n_ent + ent] = acc[el];
+        }
       }
       wave_lds_order();
     }
