@@ -1318,6 +1318,38 @@ __global__ void __launch_bounds__(256) colsum_kernel(const float *__restrict__ i
   if (ry == 0 && c < ncol) out[c] = (part[0][cx] + part[1][cx]) + (part[2][cx] + part[3][cx]);
 }
 
+// Rows [y RB, min(R, (y + 1) RB)) of the 64 columns of block x, summed in the
+// order of colsum_kernel, to out[y][c].
+__global__ void __launch_bounds__(256) colsum_chunk_kernel(const float *__restrict__ in, int R, int RB, int64_t ncol,
+                                                           int64_t ld, float *__restrict__ out) {
+  __shared__ float part[4][64];
+  const int cx = threadIdx.x & 63, ry = threadIdx.x >> 6;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + cx;
+  const int r0 = blockIdx.y * RB, r1 = min(R, r0 + RB);
+  float s = 0.0f;
+  if (c < ncol)
+    for (int r = r0 + ry; r < r1; r += 4) s += in[static_cast<int64_t>(r) * ld + c];
+  part[ry][cx] = s;
+  __syncthreads();
+  if (ry == 0 && c < ncol) out[static_cast<int64_t>(blockIdx.y) * ncol + c] = (part[0][cx] + part[1][cx]) + (part[2][cx] + part[3][cx]);
+}
+
+// out[c] = sum_{r < R} in[r*ld + c] in a fixed order.  Many rows over few
+// columns would leave most of the GPU idle while a few threads walk every
+// row, so rows are first summed in chunks of 64 by blocks of their own (the
+// chunk sums go to scratch, ceil(R / 64) * ncol floats), then the chunk sums.
+void colsum_fixed(const float *in, int R, int64_t ncol, int64_t ld, float *out, float *scratch, int64_t scratch_floats,
+                  hipStream_t st) {
+  constexpr int RB = 64;
+  const int nchunk = (R + RB - 1) / RB;
+  if (R <= RB || static_cast<int64_t>(nchunk) * ncol > scratch_floats) {
+    colsum_kernel<<<ceil_div(ncol, 64), 256, 0, st>>>(in, R, ncol, ld, out);
+    return;
+  }
+  colsum_chunk_kernel<<<dim3(ceil_div(ncol, 64), nchunk), 256, 0, st>>>(in, R, RB, ncol, ld, scratch);
+  colsum_kernel<<<ceil_div(ncol, 64), 256, 0, st>>>(scratch, nchunk, ncol, ncol, out);
+}
+
 __global__ void fill_f32(float *p, int64_t n, float v) {
   int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -1883,8 +1915,9 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
       Timed t(stream, "bwd_row", 0.0, bytes);
       EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_row_launch, g, s, geom, acts, grad_out, weights + wo.watt, w, stream);
     }
-    // w_att gradient: fixed-order sum of the per-row partials
-    colsum_kernel<<<ceil_div(s.C, 64), 256, 0, stream>>>(w.watt_part, g->n_dst, s.C, s.C, grad_weights + wo.watt);
+    // w_att gradient: fixed-order sum of the per-row partials (the split-K
+    // partial buffer is free until the weight-gradient products below)
+    colsum_fixed(w.watt_part, g->n_dst, s.C, s.C, grad_weights + wo.watt, w.P, w.P_floats, stream);
   }
   if (E > 0 && bf) {
     // bf16 storage: both gradient products on bf16 MFMA, fp32 accumulate.
@@ -1995,7 +2028,8 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
     }
     const int64_t nw = static_cast<int64_t>(s.n_rbf) * ncol;
     const int ns = wrad_streams(g->n_src);
-    colsum_kernel<<<ceil_div(nw, 64), 256, 0, stream>>>(w.wrad_part, ns, nw, nw, grad_weights + wo.wrad);
+    // (the split-K partial buffer is free again: its sums are done)
+    colsum_fixed(w.wrad_part, ns, nw, nw, grad_weights + wo.wrad, w.P, w.P_floats, stream);
   }
   if (g->n_src > 0) {
     if (E == 0) {
