@@ -13,11 +13,13 @@
 namespace egnn {
 namespace {
 
-// Destination row of every edge: one thread per row writes its edges.
+// Destination row of every edge: one wave per row, its lanes over the row's edges.
 __global__ void edge_dst_kernel(const int *row_ptr, int n_dst, int stride, int col, float *geom) {
-  int d = blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int d = static_cast<int>(t / 64), lane = static_cast<int>(t % 64);
   if (d >= n_dst) return;
-  for (int e = row_ptr[d]; e < row_ptr[d + 1]; ++e)
+  const int e1 = row_ptr[d + 1];
+  for (int e = row_ptr[d] + lane; e < e1; e += 64)
     reinterpret_cast<int *>(geom)[static_cast<int64_t>(e) * stride + col] = d;
 }
 
@@ -44,7 +46,8 @@ void launch_geom(const egnn_graph *g, const LayerShape &s, float *geom, hipStrea
   const int T = 256;
   edge_geom_kernel<LMAX, MMAX><<<ceil_div(g->n_edges, T), T, 0, st>>>(g->vec, g->dist, g->n_edges, s.n_rbf,
                                                                      s.r_cut, s.gstride, geom);
-  edge_dst_kernel<<<ceil_div(g->n_dst, T), T, 0, st>>>(g->row_ptr, g->n_dst, s.gstride, s.nD + s.n_rbf, geom);
+  edge_dst_kernel<<<ceil_div(static_cast<int64_t>(g->n_dst) * 64, T), T, 0, st>>>(g->row_ptr, g->n_dst, s.gstride,
+                                                                                 s.nD + s.n_rbf, geom);
 }
 
 }  // namespace
