@@ -1318,6 +1318,43 @@ __global__ void __launch_bounds__(256) colsum_kernel(const float *__restrict__ i
   if (ry == 0 && c < ncol) out[c] = (part[0][cx] + part[1][cx]) + (part[2][cx] + part[3][cx]);
 }
 
+// colsum_kernel on four adjacent columns per thread (16-byte loads and
+// stores; the same order of sums for every column).  nq = ncol / 4, ld a
+// multiple of 4, in and out 16-byte aligned.
+__global__ void __launch_bounds__(256) colsum4_kernel(const float *__restrict__ in, int R, int64_t nq, int64_t ld,
+                                                      float *__restrict__ out) {
+  __shared__ float4 part[4][64];
+  const int cx = threadIdx.x & 63, ry = threadIdx.x >> 6;
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 64 + cx;
+  float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (q < nq)
+    for (int r = ry; r < R; r += 4) {
+      const float4 v = reinterpret_cast<const float4 *>(in + static_cast<int64_t>(r) * ld)[q];
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+  part[ry][cx] = s;
+  __syncthreads();
+  if (ry == 0 && q < nq) {
+    const float4 a = part[0][cx], b = part[1][cx], c = part[2][cx], d = part[3][cx];
+    reinterpret_cast<float4 *>(out)[q] =
+        make_float4((a.x + b.x) + (c.x + d.x), (a.y + b.y) + (c.y + d.y), (a.z + b.z) + (c.z + d.z),
+                    (a.w + b.w) + (c.w + d.w));
+  }
+}
+
+// out[c] = sum_{r < R} in[r*ld + c] in a fixed order (four columns per thread where the layout allows)
+void colsum(const float *in, int R, int64_t ncol, int64_t ld, float *out, hipStream_t st) {
+  const bool quad = ncol % 4 == 0 && ld % 4 == 0 && (reinterpret_cast<uintptr_t>(in) & 15) == 0 &&
+                    (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+  if (quad)
+    colsum4_kernel<<<ceil_div(ncol / 4, 64), 256, 0, st>>>(in, R, ncol / 4, ld, out);
+  else
+    colsum_kernel<<<ceil_div(ncol, 64), 256, 0, st>>>(in, R, ncol, ld, out);
+}
+
 // Rows [y RB, min(R, (y + 1) RB)) of the 64 columns of block x, summed in the
 // order of colsum_kernel, to out[y][c].
 __global__ void __launch_bounds__(256) colsum_chunk_kernel(const float *__restrict__ in, int R, int RB, int64_t ncol,
@@ -1343,11 +1380,11 @@ void colsum_fixed(const float *in, int R, int64_t ncol, int64_t ld, float *out, 
   constexpr int RB = 64;
   const int nchunk = (R + RB - 1) / RB;
   if (R <= RB || static_cast<int64_t>(nchunk) * ncol > scratch_floats) {
-    colsum_kernel<<<ceil_div(ncol, 64), 256, 0, st>>>(in, R, ncol, ld, out);
+    colsum(in, R, ncol, ld, out, st);
     return;
   }
   colsum_chunk_kernel<<<dim3(ceil_div(ncol, 64), nchunk), 256, 0, st>>>(in, R, RB, ncol, ld, scratch);
-  colsum_kernel<<<ceil_div(ncol, 64), 256, 0, st>>>(scratch, nchunk, ncol, ncol, out);
+  colsum(scratch, nchunk, ncol, ncol, out, st);
 }
 
 __global__ void fill_f32(float *p, int64_t n, float v) {
@@ -1948,9 +1985,9 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
         return EGNN_E_HIP;
       }
       if (m == 0) {
-        colsum_kernel<<<ceil_div(pn, 64), 256, 0, stream>>>(w.P, splits, pn, pn, grad_weights + wo.W0);
+        colsum(w.P, splits, pn, pn, grad_weights + wo.W0, stream);
       } else {
-        colsum_kernel<<<ceil_div(pn, 64), 256, 0, stream>>>(w.P, splits, pn, pn, w.dWexp);
+        colsum(w.P, splits, pn, pn, w.dWexp, stream);
         const int64_t nb = pn / 4;
         fold_expanded_kernel<<<ceil_div(nb, T), T, 0, stream>>>(w.dWexp, Ng / 2, Kg / 2, grad_weights + wo.W1[m],
                                                                 grad_weights + wo.W2[m]);
@@ -1985,8 +2022,8 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
           set_error("GEMM launch failed: %s", hipGetErrorString(e));
           return EGNN_E_HIP;
         }
-        colsum_kernel<<<ceil_div(nb, 64), 256, 0, stream>>>(w.P, splits, nb, nb, grad_weights + wo.W1[m]);
-        colsum_kernel<<<ceil_div(nb, 64), 256, 0, stream>>>(w.P + splits * nb, splits, nb, nb, grad_weights + wo.W2[m]);
+        colsum(w.P, splits, nb, nb, grad_weights + wo.W1[m], stream);
+        colsum(w.P + splits * nb, splits, nb, nb, grad_weights + wo.W2[m], stream);
         continue;
       }
       const float *B = weights + wo.W0;
@@ -2013,7 +2050,7 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
         set_error("GEMM launch failed: %s", hipGetErrorString(e));
         return EGNN_E_HIP;
       }
-      colsum_kernel<<<ceil_div(pn, 64), 256, 0, stream>>>(w.P, splits, pn, pn, grad_weights + wo.W0);
+      colsum(w.P, splits, pn, pn, grad_weights + wo.W0, stream);
     }
   }
   if (E > 0) {
