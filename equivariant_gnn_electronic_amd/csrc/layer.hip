@@ -559,7 +559,7 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const int *__restri
                                                              const float *__restrict__ w_att, float *logit,
                                                              float *alpha) {
   constexpr int VW = 16 / sizeof(T);  // channels per 16-byte load
-  constexpr int U = 2;                // edge groups in flight per lane
+  constexpr int U = 4;                // edge groups in flight per lane
   const int lane = threadIdx.x & (kWave - 1);
   const int d = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (d >= n_dst) return;
@@ -570,18 +570,22 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const int *__restri
   for (int base = b; base < end; base += 4 * U) {
     float acc[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      acc[u] = 0.0f;
-      const int e = base + 4 * u + grp;
-      if (e < end) {
-        const T *y = Y0 + static_cast<int64_t>(e) * ldy0;
-        for (int c0 = sub * VW; c0 < C; c0 += 16 * VW) {
-          const uint4 raw = *reinterpret_cast<const uint4 *>(y + c0);
-          T v[VW];
-          memcpy(v, &raw, sizeof(raw));
+    for (int u = 0; u < U; ++u) acc[u] = 0.0f;
+    for (int c0 = sub * VW; c0 < C; c0 += 16 * VW) {  // one chunk per lane up to 16 VW channels
+      // every group's load before any use; past the row's end the last edge is
+      // read again and its sum not used (no branch around the loads)
+      uint4 raw[U];
 #pragma unroll
-          for (int j = 0; j < VW; ++j) acc[u] += w_att[c0 + j] * silu(Store<T>::ld(&v[j]));
-        }
+      for (int u = 0; u < U; ++u) {
+        const int e = min(base + 4 * u + grp, end - 1);
+        raw[u] = *reinterpret_cast<const uint4 *>(Y0 + static_cast<int64_t>(e) * ldy0 + c0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        T v[VW];
+        memcpy(v, &raw[u], sizeof(raw[u]));
+#pragma unroll
+        for (int j = 0; j < VW; ++j) acc[u] += w_att[c0 + j] * silu(Store<T>::ld(&v[j]));
       }
     }
 #pragma unroll
@@ -603,11 +607,11 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const int *__restri
   const float Mrow = wave_max(M);
   const float Srow = wave_sum(M == -INFINITY ? 0.0f : S * expf(M - Mrow));
   const float inv = 1.0f / Srow;
-  if (sub == 0)
-    for (int base = b; base < end; base += 4) {
-      const int e = base + grp;
-      if (e < end) alpha[e] = expf(logit[e] - Mrow) * inv;
-    }
+  // the row's logits were stored by the sub == 0 lanes; the waves of a block
+  // share the CU's vector cache, so a block-scope fence makes them visible to
+  // every lane of the wave, and all lanes share the last pass
+  __threadfence_block();
+  for (int e = b + lane; e < end; e += kWave) alpha[e] = expf(logit[e] - Mrow) * inv;
 }
 
 // x_out[d] = x[d] + sum_e alpha_e D_e^T Yhat_e ; edge_out[e] = D_e^T Yhat_e.
