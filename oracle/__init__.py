@@ -13,6 +13,7 @@ Every function follows a passage of the pages it is written from:
   over the edges directed into a node.
 * "MALOQ" (arXiv 2606.28911v1): Sec. III (workflow of Fig. 2(a)), Sec. III-B1
   Eq. (1) (Clebsch-Gordan decomposition of Hamiltonian sub-blocks),
+  Sec. III-B2 (Matrix <-> Label with orbital templates and padding),
   Sec. III-C1 and Fig. 3(b,c) (Wigner-D rotation of every edge to +y),
   Sec. III-D (messages n_i (+) n_j; target node owns its edges),
   Sec. II-B1 (SO(3) -> SO(2) reduction, eSCN).
@@ -34,11 +35,16 @@ brute force, closed forms, finite differences), not the reading itself:
   layer.layer_backward (the loss <G, x'>),
   decode.label_layout / labels_from_irreps / label_to_matrix (label order,
       the 2s2p1d basis, no hermiticity symmetrisation),
-  so3.real_coupling (the sign rule of the real coupling).
+  so3.real_coupling (the sign rule of the real coupling),
+  labels (each element's shells as a subset of one full list, padding at the
+      full list's label positions, matrices of a batch back to back, no
+      block for edges across structures or with an image shift).
 
 Modules:
   neighbors  -- brute-force periodic / open cutoff graph, destination-sorted CSR
   so3        -- real spherical harmonics, Wigner-D, edge frame, real CG couplings
   layer      -- layer forward and analytic backward
   decode     -- Label -> Matrix: Hamiltonian blocks from irreps
+  labels     -- Matrix <-> Label over whole matrices with per-element orbital
+                templates (MALOQ Sec. III-B2)
 """

@@ -27,7 +27,9 @@ import numpy as np
 
 __all__ = ["Config", "CONFIGS", "Structure", "make_structure", "make_layer_inputs",
            "make_decode_weights", "make_cotangent", "layer_weight_sizes",
-           "round_storage", "bf16_round"]
+           "round_storage", "bf16_round", "SVP_SHELLS", "SVP_ELEMENTS", "SVP_MASKS",
+           "SVP_FRACTIONS", "WATER_SHELLS", "WATER_MASKS", "MoleculeBatch", "make_molecule_batch",
+           "make_matrix_values", "make_label_values"]
 
 
 @dataclass(frozen=True)
@@ -343,3 +345,92 @@ def make_cotangent(cfg: Config | str, n_dst):
         cfg = CONFIGS[cfg]
     rng = np.random.default_rng((cfg.seed, 4))
     return round_storage(rng.standard_normal((n_dst, cfg.K, cfg.C)), "f32")
+
+
+# --------------------------------------------------------------------------
+# Molecule batches for Matrix <-> Label (MALOQ Sec. III-B2, Table II)
+#
+# Stand-in for a batch of the nabla^2 DFT small-molecule dataset: drug-like
+# molecules of up to 50 atoms over H, C, N, O, F, S, Cl, fully connected
+# graphs, described in a def2-SVP-like basis whose shell structure per
+# element is H [2s1p], C-F [3s2p1d], S, Cl [4s3p1d] (labels up to L = 4).
+# The full shell list is the union, 4s3p1d; an element's shells are a bit
+# mask over it.  Matrix values are N(0, 1) (no DFT matrices are available).
+# --------------------------------------------------------------------------
+
+SVP_SHELLS = (0, 0, 0, 0, 1, 1, 1, 2)
+SVP_ELEMENTS = ("H", "C", "N", "O", "F", "S", "Cl")
+SVP_MASKS = (0b00010011,                 # H: s s . . p . . .
+             0b10110111, 0b10110111,     # C, N: s s s . p p . d
+             0b10110111, 0b10110111,     # O, F
+             0b11111111, 0b11111111)     # S, Cl: s s s s p p p d
+SVP_FRACTIONS = (0.45, 0.33, 0.08, 0.08, 0.02, 0.02, 0.02)
+
+# the pages' toy example (Fig. 2(b)): water in a minimal basis, O [s p], H [s]
+WATER_SHELLS = (0, 1)
+WATER_MASKS = (0b11, 0b01)               # O, H
+
+
+@dataclass
+class MoleculeBatch:
+    mol_ptr: np.ndarray      # [n_mols + 1] int32, atoms of molecule b are mol_ptr[b]:mol_ptr[b+1]
+    species: np.ndarray      # [n_atoms] int32, index into the basis' element list
+    row_ptr: np.ndarray      # [n_atoms + 1] int32, destination-sorted CSR of the graph
+    src: np.ndarray          # [n_edges] int32, sources of each row in ascending order
+
+    @property
+    def n_atoms(self):
+        return int(self.species.shape[0])
+
+    @property
+    def n_mols(self):
+        return int(self.mol_ptr.shape[0] - 1)
+
+    @property
+    def n_edges(self):
+        return int(self.src.shape[0])
+
+    def dst(self):
+        return np.repeat(np.arange(self.n_atoms, dtype=np.int32), np.diff(self.row_ptr))
+
+
+def make_molecule_batch(seed, n_mols, min_atoms=10, max_atoms=50, fractions=SVP_FRACTIONS, keep=1.0):
+    """Seeded batch: sizes uniform in [min_atoms, max_atoms], species drawn by
+    `fractions`, and for each atom every other atom of its molecule as a
+    source (fully connected), each edge then kept with probability `keep`.
+
+    Stream (seed, 10): sizes, species, then the keep draws.
+    """
+    rng = np.random.default_rng((seed, 10))
+    sizes = rng.integers(min_atoms, max_atoms + 1, size=n_mols)
+    mol_ptr = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    n_atoms = int(mol_ptr[-1])
+    species = rng.choice(len(fractions), size=n_atoms, p=np.asarray(fractions) / np.sum(fractions)).astype(np.int32)
+    srcs, degs = [], np.zeros(n_atoms, np.int64)
+    for b in range(n_mols):
+        p, n = int(mol_ptr[b]), int(sizes[b])
+        grid = np.broadcast_to(np.arange(p, p + n, dtype=np.int32), (n, n))
+        off = ~np.eye(n, dtype=bool)
+        srcs.append(grid[off])                       # row j: every other atom, ascending
+        degs[p:p + n] = n - 1
+    src = np.concatenate(srcs) if srcs else np.zeros(0, np.int32)
+    row_ptr = np.concatenate([[0], np.cumsum(degs)])
+    if keep < 1.0:
+        kept = rng.random(src.shape[0]) < keep
+        dst = np.repeat(np.arange(n_atoms), degs)
+        src = src[kept]
+        degs = np.bincount(dst[kept], minlength=n_atoms)
+        row_ptr = np.concatenate([[0], np.cumsum(degs)])
+    return MoleculeBatch(mol_ptr, species, row_ptr.astype(np.int32), src.astype(np.int32))
+
+
+def make_matrix_values(seed, n_elems):
+    """N(0, 1) float32 values for a batch's matrices stored back to back (stream (seed, 11))."""
+    rng = np.random.default_rng((seed, 11))
+    return rng.standard_normal(int(n_elems), dtype=np.float32)
+
+
+def make_label_values(seed, n_rows, n_lab):
+    """N(0, 1) float32 labels [n_rows][n_lab] (stream (seed, 12))."""
+    rng = np.random.default_rng((seed, 12))
+    return rng.standard_normal((int(n_rows), int(n_lab)), dtype=np.float32)
