@@ -19,7 +19,9 @@ from ._lib import EGNN_BF16, EGNN_F32, EgnnError
 __all__ = ["Graph", "layer_desc", "egnn_build_graph", "egnn_edge_geom", "egnn_geom_stride",
            "egnn_layer_weight_count", "egnn_layer_sizes", "egnn_layer_fwd", "egnn_layer_bwd",
            "egnn_hblocks", "egnn_hblocks_label_rows", "egnn_timing_enable", "egnn_timing_collect",
-           "egnn_timing_reset", "GraphBuilder", "LayerBuffers", "EgnnError", "EGNN_F32", "EGNN_BF16"]
+           "egnn_timing_reset", "GraphBuilder", "LayerBuffers", "EgnnError", "EGNN_F32", "EGNN_BF16",
+           "Basis", "Orbitals", "egnn_label_width", "egnn_orbital_layout", "egnn_matrix_to_label",
+           "egnn_label_to_matrix"]
 
 _STORAGE = {EGNN_F32: torch.float32, EGNN_BF16: torch.bfloat16}
 
@@ -62,8 +64,16 @@ class Graph:
         g.capacity = self.src.numel()
         g.n_edges = self.n_edges
         for f in ("row_ptr", "src", "shift", "vec", "dist", "src_ptr", "src_perm"):
-            setattr(g, f, self.__dict__[f].data_ptr())
+            t = self.__dict__[f]
+            setattr(g, f, None if t is None else t.data_ptr())
         return g
+
+    @classmethod
+    def from_csr(cls, row_ptr, src, n_src=None, shift=None):
+        """A graph given only by its CSR (Matrix <-> Label reads row_ptr, src and shift)."""
+        n_dst = row_ptr.numel() - 1
+        return cls(n_dst, n_dst if n_src is None else n_src, src.numel(), row_ptr, src, shift,
+                   None, None, None, None)
 
 
 def layer_desc(lmax, mmax, C, n_rbf, r_cut, storage=EGNN_F32):
@@ -272,3 +282,99 @@ def egnn_hblocks(lmax, C, w_edge, w_node, edge_irreps, node_irreps, shell_l=(0, 
         _ptr(edge_irreps) if E else None, _ptr(node_irreps) if N else None, _ptr(he) if E else None,
         _ptr(hn) if N else None, _stream()))
     return he[:E], hn[:N]
+
+
+class Basis:
+    """Full shell list and per-element shell masks (orbital templates)."""
+
+    def __init__(self, shell_l, species_shells):
+        self.shell_l = tuple(int(l) for l in shell_l)
+        self.species_shells = tuple(int(m) for m in species_shells)
+        self._l = (ct.c_int32 * len(self.shell_l))(*self.shell_l)
+        self._m = (ct.c_uint32 * len(self.species_shells))(*self.species_shells)
+        self.c = _lib.EgnnBasis(len(self.shell_l), self._l, len(self.species_shells), self._m)
+
+
+@dataclass
+class Orbitals:
+    """Atom and structure layout of a batch of matrices (egnn_orbital_layout's outputs)."""
+    mol_ptr: torch.Tensor
+    species: torch.Tensor
+    atom_orb: torch.Tensor
+    atom_mol: torch.Tensor
+    mol_norb: torch.Tensor
+    mat_off: torch.Tensor
+
+    @property
+    def n_atoms(self):
+        return self.species.numel()
+
+    @property
+    def n_mols(self):
+        return self.mol_ptr.numel() - 1
+
+    def c_struct(self):
+        o = _lib.EgnnOrbitals()
+        o.n_mols, o.n_atoms = self.n_mols, self.n_atoms
+        for f in ("mol_ptr", "species", "atom_orb", "atom_mol", "mol_norb", "mat_off"):
+            setattr(o, f, self.__dict__[f].data_ptr())
+        return o
+
+
+def egnn_label_width(basis: Basis):
+    return int(_lib.load().egnn_label_width(ct.byref(basis.c)))
+
+
+def egnn_orbital_layout(basis: Basis, mol_ptr, species):
+    """Orbitals of a batch (mol_ptr [n_mols+1], species [n_atoms], int32 on the GPU) and
+    the count of invalid structures and element indices (int64 [1] on the GPU)."""
+    lib = _lib.load()
+    dev = species.device
+    n_mols, n_atoms = mol_ptr.numel() - 1, species.numel()
+    o = Orbitals(mol_ptr, species,
+                 torch.empty(max(n_atoms, 1), dtype=torch.int32, device=dev)[:n_atoms],
+                 torch.empty(max(n_atoms, 1), dtype=torch.int32, device=dev)[:n_atoms],
+                 torch.empty(max(n_mols, 1), dtype=torch.int32, device=dev)[:n_mols],
+                 torch.empty(n_mols + 1, dtype=torch.int64, device=dev))
+    bad = torch.empty(1, dtype=torch.int64, device=dev)
+    for t in (mol_ptr, species):
+        _ptr(t)                      # on the GPU and contiguous
+    c = o.c_struct()
+    _lib.check("egnn_orbital_layout", lib.egnn_orbital_layout(ct.byref(basis.c), ct.byref(c), _ptr(bad), _stream()))
+    return o, bad
+
+
+def egnn_matrix_to_label(basis: Basis, orbitals: Orbitals, graph, H, edges=True, nodes=True):
+    """Labels (h_edge [E][n_lab], h_node [n_atoms][n_lab]) of the batch's matrices H
+    (fp32, flat, mat_off[-1] entries) and the count of skipped blocks."""
+    lib = _lib.load()
+    n_lab = egnn_label_width(basis)
+    dev = H.device
+    E = graph.n_edges if (graph is not None and edges) else 0
+    he = torch.empty((max(E, 1), n_lab), dtype=torch.float32, device=dev)
+    hn = torch.empty((max(orbitals.n_atoms, 1), n_lab), dtype=torch.float32, device=dev)
+    skipped = torch.empty(1, dtype=torch.int64, device=dev)
+    g = graph.c_struct() if (graph is not None and edges) else None
+    o = orbitals.c_struct()
+    _lib.check("egnn_matrix_to_label", lib.egnn_matrix_to_label(
+        ct.byref(basis.c), ct.byref(o), ct.byref(g) if g is not None else None, _ptr(H), H.numel(),
+        _ptr(he) if g is not None else None, _ptr(hn) if nodes else None, _ptr(skipped), _stream()))
+    return he[:E], (hn[:orbitals.n_atoms] if nodes else None), skipped
+
+
+def egnn_label_to_matrix(basis: Basis, orbitals: Orbitals, graph, h_edge, h_node, H=None, h_elems=None):
+    """Writes the blocks of h_edge / h_node (either may be None) into H (zeros of
+    h_elems = mat_off[-1] entries when not given); returns (H, skipped count)."""
+    lib = _lib.load()
+    dev = orbitals.species.device
+    if H is None:
+        n = int(orbitals.mat_off[-1].item()) if h_elems is None else int(h_elems)
+        H = torch.zeros(max(n, 1), dtype=torch.float32, device=dev)[:n]
+    skipped = torch.empty(1, dtype=torch.int64, device=dev)
+    g = graph.c_struct() if (graph is not None and h_edge is not None) else None
+    o = orbitals.c_struct()
+    _lib.check("egnn_label_to_matrix", lib.egnn_label_to_matrix(
+        ct.byref(basis.c), ct.byref(o), ct.byref(g) if g is not None else None,
+        _ptr(h_edge) if g is not None else None, _ptr(h_node) if h_node is not None else None, _ptr(H),
+        H.numel(), _ptr(skipped), _stream()))
+    return H, skipped

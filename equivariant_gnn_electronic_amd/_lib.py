@@ -29,6 +29,16 @@ class EgnnHDesc(ct.Structure):
                 ("shell_l", ct.POINTER(ct.c_int32)), ("storage", ct.c_int32)]
 
 
+class EgnnBasis(ct.Structure):
+    _fields_ = [("n_shells", ct.c_int32), ("shell_l", ct.POINTER(ct.c_int32)), ("n_species", ct.c_int32),
+                ("species_shells", ct.POINTER(ct.c_uint32))]
+
+
+class EgnnOrbitals(ct.Structure):
+    _fields_ = [("n_mols", ct.c_int32), ("n_atoms", ct.c_int32), ("mol_ptr", _vp), ("species", _vp),
+                ("atom_orb", _vp), ("atom_mol", _vp), ("mol_norb", _vp), ("mat_off", _vp)]
+
+
 class EgnnTimingEntry(ct.Structure):
     _fields_ = [("name", ct.c_char * 48), ("launches", ct.c_int64), ("total_ms", ct.c_double),
                 ("flops", ct.c_double), ("bytes", ct.c_double)]
@@ -39,6 +49,8 @@ _G = ct.POINTER(EgnnGraph)
 _L = ct.POINTER(EgnnLayerDesc)
 _H = ct.POINTER(EgnnHDesc)
 _PSZ = ct.POINTER(ct.c_size_t)
+_B = ct.POINTER(EgnnBasis)
+_O = ct.POINTER(EgnnOrbitals)
 
 SIGNATURES = {
     "egnn_status_string": (ct.c_char_p, [ct.c_int]),
@@ -54,6 +66,10 @@ SIGNATURES = {
     "egnn_layer_bwd": (ct.c_int, [_L, _G, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "egnn_hblocks_label_rows": (ct.c_int32, [_H]),
     "egnn_hblocks": (ct.c_int, [_H, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "egnn_label_width": (ct.c_int32, [_B]),
+    "egnn_orbital_layout": (ct.c_int, [_B, _O, _vp, _vp]),
+    "egnn_matrix_to_label": (ct.c_int, [_B, _O, _G, _vp, _i64, _vp, _vp, _vp, _vp]),
+    "egnn_label_to_matrix": (ct.c_int, [_B, _O, _G, _vp, _vp, _vp, _i64, _vp, _vp]),
     "egnn_timing_enable": (ct.c_int, [ct.c_int]),
     "egnn_timing_collect": (ct.c_int, [ct.POINTER(EgnnTimingEntry), ct.c_int, ct.POINTER(ct.c_int64)]),
     "egnn_timing_reset": (None, []),

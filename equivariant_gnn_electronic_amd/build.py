@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libegnn.so")
 
-SOURCES = ["common.hip", "timing.hip", "graph.hip", "geom.hip", "gemm.hip", "layer.hip", "hblocks.hip"]
+SOURCES = ["common.hip", "timing.hip", "graph.hip", "geom.hip", "gemm.hip", "layer.hip", "hblocks.hip", "labels.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

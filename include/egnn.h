@@ -238,6 +238,86 @@ egnn_status egnn_hblocks(const egnn_hdesc *h, int64_t n_edges, int32_t n_nodes,
                          float *h_onsite /*[n_nodes][n_orb][n_orb]*/, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Matrix <-> Label over whole matrices  [MALOQ Sec. III-B1 Eq. (1), Sec. III-B2]
+ *
+ * Basis: one full shell list (each l <= 3, at most 32 orbitals: the largest
+ * element's basis, or the union of the per-degree maxima) and, per element,
+ * a bit mask of the full shells it carries (its orbital template).  An
+ * atom's orbitals are its shells in full-list order, m = -l..l each.
+ *
+ * Labels: n_lab = n_full^2 floats per node or edge, in the full list's
+ * layout: for ordered shell pairs (a, b) in lexicographic order and L =
+ * |la-lb|..la+lb ascending, channel k(a,b,L) counts the earlier pairs that
+ * carry L, and label q = off(L) + (M+L) * n_L + k with off(L) = sum over
+ * L' < L of (2L'+1) n_L'.  For a block between atoms i and j,
+ *   h[q(a,b,L,M,k)] = sum_{m_a,m_b} Q^{(la,lb,L)}[m_a][m_b][M] H_ij[a m_a][b m_b]
+ * with Q the real coupling of egnn_hblocks.  Labels of shell pairs that
+ * element i or j lacks are zero (the padding to the largest element).
+ *
+ * Matrices: a batch of structures (molecules) with contiguous atoms, atoms
+ * of structure s are mol_ptr[s]..mol_ptr[s+1]-1.  Structure s has one dense
+ * row-major fp32 matrix of n_s x n_s entries (n_s = its atoms' orbital
+ * counts summed), stored at element offset mat_off[s] of one array H of
+ * h_elems = mat_off[n_mols] floats; an atom's first orbital is the sum of
+ * the counts of the atoms before it in its structure.
+ *
+ * Blocks: the on-site block of every atom (h_node rows = atoms) and the
+ * block of every graph edge (h_edge rows = edges, in the graph's order; rows
+ * of H = the source atom's orbitals, columns = the destination's).  The
+ * graph is a destination-sorted CSR over the batch's atoms (n_dst = n_src =
+ * n_atoms; only row_ptr, src, shift and n_edges are read; shift may be
+ * NULL).  An edge whose ends lie in different structures, or with a nonzero
+ * image shift, has no block in a dense matrix: its labels are zero and
+ * nothing is written.  Each ordered atom pair must appear at most once.
+ *
+ * All arrays are device memory owned by the caller; the library keeps no
+ * pointer after a call.  Structure and atom arrays that the kernels read
+ * are bounds-checked against n_atoms, n_mols and h_elems, so inconsistent
+ * values cannot make a kernel leave the arrays; blocks that fail the checks
+ * count as skipped.  n_invalid / n_skipped (device int64, may be NULL) are
+ * overwritten with the count of structures with an invalid atom range plus
+ * atoms whose element index is outside the table / of blocks with no place
+ * in a matrix.  Asynchronous on `stream`.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t n_shells;                 /* full shell list, 1..16 shells          */
+  const int32_t *shell_l;           /* host [n_shells], each 0..3             */
+  int32_t n_species;                /* 1..64 elements                         */
+  const uint32_t *species_shells;   /* host [n_species]: bit a = carries full shell a */
+} egnn_basis;
+
+typedef struct {
+  int32_t n_mols, n_atoms;
+  const int32_t *mol_ptr;           /* [n_mols+1], non-decreasing, 0 .. n_atoms          */
+  const int32_t *species;           /* [n_atoms] element index into the basis            */
+  int32_t *atom_orb;                /* [n_atoms] first orbital of the atom in its matrix */
+  int32_t *atom_mol;                /* [n_atoms] structure of the atom (-1: none)        */
+  int32_t *mol_norb;                /* [n_mols]  orbitals (matrix side) per structure    */
+  int64_t *mat_off;                 /* [n_mols+1] element offset of each matrix in H     */
+} egnn_orbitals;
+
+/* Labels per node or edge (n_full^2) for the basis, 0 if it is invalid. */
+int32_t egnn_label_width(const egnn_basis *b);
+
+/* Fills atom_orb, atom_mol, mol_norb and mat_off from mol_ptr and species. */
+egnn_status egnn_orbital_layout(const egnn_basis *b, egnn_orbitals *o, int64_t *n_invalid /*device or NULL*/,
+                                hipStream_t stream);
+
+/* Matrix -> Label: h_edge [n_edges][n_lab] (NULL: skip edges, as does g ==
+ * NULL) and h_node [n_atoms][n_lab] (NULL: skip on-site blocks), both
+ * overwritten, from H [h_elems]. */
+egnn_status egnn_matrix_to_label(const egnn_basis *b, const egnn_orbitals *o, const egnn_graph *g,
+                                 const float *H, int64_t h_elems, float *h_edge, float *h_node,
+                                 int64_t *n_skipped /*device or NULL*/, hipStream_t stream);
+
+/* Label -> Matrix: writes the template entries of every block given by
+ * h_edge / h_node into H; entries of blocks not given are left as they are
+ * (start from a zeroed H for a matrix with only the graph's blocks). */
+egnn_status egnn_label_to_matrix(const egnn_basis *b, const egnn_orbitals *o, const egnn_graph *g,
+                                 const float *h_edge, const float *h_node, float *H, int64_t h_elems,
+                                 int64_t *n_skipped /*device or NULL*/, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Kernel timing (observability)
  *
  * When enabled, every entry point brackets each kernel launch with a pair of

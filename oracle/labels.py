@@ -83,7 +83,7 @@ def orbital_layout(mol_ptr, species, shell_l, species_shells):
 
 def flat_labels(h):
     """Labels h_L [N][2L+1][n_L] -> [N][n_lab] in (L, M, k) order."""
-    return np.concatenate([x.reshape(x.shape[0], -1) for x in h], axis=1)
+    return np.concatenate([x.reshape(x.shape[0], x.shape[1] * x.shape[2]) for x in h], axis=1)
 
 
 def unflat_labels(hf, shell_l):

@@ -210,3 +210,45 @@ def test_binding_refuses_host_tensors():
     import equivariant_gnn_electronic_amd as eg
     with pytest.raises(ValueError):
         eg._ptr(torch.zeros(3))
+
+
+def _basis(shells, masks):
+    from equivariant_gnn_electronic_amd import _lib
+    l = (ct.c_int32 * len(shells))(*shells)
+    m = (ct.c_uint32 * len(masks))(*masks)
+    b = _lib.EgnnBasis(len(shells), l, len(masks), m)
+    b._keep = (l, m)
+    return b
+
+
+def test_label_width_and_basis_checks(lib):
+    """Host-side table build: n_full^2 labels; degrees above 3, more than 32
+    orbitals or a mask naming a missing shell are refused (width 0)."""
+    assert lib.egnn_label_width(ct.byref(_basis(synth.WATER_SHELLS, synth.WATER_MASKS))) == 16
+    assert lib.egnn_label_width(ct.byref(_basis(synth.SVP_SHELLS, synth.SVP_MASKS))) == 18 * 18
+    assert lib.egnn_label_width(ct.byref(_basis((0, 1, 2, 3), (0b1111,)))) == 16 * 16
+    assert lib.egnn_label_width(ct.byref(_basis((0, 4), (0b11,)))) == 0
+    assert lib.egnn_label_width(ct.byref(_basis((3, 3, 3, 3, 3), (0b1,)))) == 0     # 35 orbitals
+    assert lib.egnn_label_width(ct.byref(_basis((0, 1), (0b111,)))) == 0
+    assert lib.egnn_label_width(None) == 0
+
+
+def test_label_calls_reject_bad_arguments(lib):
+    from equivariant_gnn_electronic_amd import _lib
+    b = _basis(synth.WATER_SHELLS, synth.WATER_MASKS)
+    assert lib.egnn_orbital_layout(ct.byref(b), None, None, None) == _lib.EGNN_E_ARG
+    o = _lib.EgnnOrbitals()
+    o.n_mols, o.n_atoms = 1, 3
+    assert lib.egnn_orbital_layout(ct.byref(b), ct.byref(o), None, None) == _lib.EGNN_E_ARG   # null arrays
+    assert b"null" in lib.egnn_last_error()
+    o.mol_ptr = o.species = o.atom_orb = o.atom_mol = o.mol_norb = o.mat_off = 16
+    g = _lib.EgnnGraph()
+    g.n_dst, g.n_src, g.n_edges = 4, 4, 0
+    # the graph's rows must be the layout's atoms
+    assert lib.egnn_matrix_to_label(ct.byref(b), ct.byref(o), ct.byref(g), 16, 9, 16, 16, None,
+                                    None) == _lib.EGNN_E_ARG
+    g.n_dst = g.n_src = 3
+    # an empty matrix with blocks to fill
+    assert lib.egnn_label_to_matrix(ct.byref(b), ct.byref(o), None, None, 16, 16, 0, None, None) == _lib.EGNN_E_ARG
+    assert lib.egnn_matrix_to_label(ct.byref(b), ct.byref(o), None, None, 9, None, 16, None,
+                                    None) == _lib.EGNN_E_ARG

@@ -217,3 +217,16 @@ def test_out_of_range_species_carries_nothing():
     species = np.array([0, 7, 1])               # 7 is not an element of the table
     atom_orb, atom_mol, mol_norb, mat_off = labels.orbital_layout(mol_ptr, species, sh, masks)
     assert list(atom_orb) == [0, 4, 4] and list(mol_norb) == [5]
+
+
+def test_no_edges():
+    _, species, sh, masks, lay, _, _ = _water()
+    H = np.arange(36, dtype=np.float64)
+    he, hn = labels.matrix_to_labels(H, np.zeros(0, np.int64), np.zeros(0, np.int64), None, species, lay, sh, masks)
+    assert he.shape == (0, 16) and hn.shape == (3, 16)
+    H2 = labels.labels_to_matrix(he, hn, np.zeros(0, np.int64), np.zeros(0, np.int64), None, species, lay, sh, masks)
+    # only the on-site blocks come back
+    Hm = H.reshape(6, 6)
+    ref = np.zeros((6, 6))
+    ref[:4, :4], ref[4, 4], ref[5, 5] = Hm[:4, :4], Hm[4, 4], Hm[5, 5]
+    np.testing.assert_allclose(H2.reshape(6, 6), ref, atol=1e-12)
