@@ -11,6 +11,10 @@ The default workload is the HfO2-like training step: 3,000 atoms (1,000 Hf +
 lmax 4, mmax 2, C 64, fp32, one layer forward + backward, then the decode
 into 13x13 orbital blocks.  `value` is edges per second of whole steps.
 
+The m2l / l2m workloads time Matrix -> Label and Label -> Matrix (MALOQ
+Sec. III-B2, Fig. 2(c, d)) over a batch of 4,096 small molecules; `value` is
+atoms per second there.
+
 Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
 """
 from __future__ import annotations
@@ -38,6 +42,11 @@ WORKLOADS = {
                 desc="GeSbTe-like 3-layer forward, bf16 storage"),
     "gst_train": dict(cfg="gst", backward=True, decode=True, layers=1,
                       desc="GeSbTe-like training step, bf16 storage: graph + geometry + 1 layer fwd/bwd + 13x13 blocks"),
+    "m2l": dict(labels="m2l", mols=4096, seed=40,
+                desc="Matrix -> Label over 4,096 nabla2DFT-like molecules (10-50 atoms of H C N O F S Cl, "
+                     "def2-SVP-like shells, fully connected): orbital layout + labels of every atom and edge"),
+    "l2m": dict(labels="l2m", mols=4096, seed=40,
+                desc="Label -> Matrix over the same 4,096 molecules: orbital layout + every block written back"),
 }
 
 
@@ -49,6 +58,7 @@ def parse():
     ap.add_argument("--workload", default="train", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=500, help="rows of the oracle's timed sample")
+    ap.add_argument("--cpu-mols", type=int, default=150, help="molecules of the oracle's timed sample (m2l, l2m)")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of the plain elementwise copy (y = -x, float32) timed before the steps; it gives "
                          "the measured copy bandwidth, and a counter run sees it as a kernel of known traffic")
@@ -136,6 +146,121 @@ class Step:
             eg._ptr(xout), eg._ptr(eo) if eo is not None else None,
             eg._ptr(self.buf.saved) if self.buf.saved is not None else None, eg._ptr(self.buf.ws),
             self.buf.ws.numel(), eg._stream()))
+
+
+class LabelStep:
+    """One pass of Matrix -> Label (or Label -> Matrix) over a batch of molecules,
+    inputs resident on the GPU."""
+
+    def __init__(self, wl, dev):
+        import torch
+        import synth
+        import equivariant_gnn_electronic_amd as eg
+        self.eg, self.wl = eg, wl
+        b = self.batch = synth.make_molecule_batch(wl["seed"], wl["mols"], 10, 50)
+        self.basis = eg.Basis(synth.SVP_SHELLS, synth.SVP_MASKS)
+        self.mol_ptr = torch.from_numpy(b.mol_ptr).to(dev)
+        self.species = torch.from_numpy(b.species).to(dev)
+        self.graph = eg.Graph.from_csr(torch.from_numpy(b.row_ptr).to(dev), torch.from_numpy(b.src).to(dev))
+        orb, bad = eg.egnn_orbital_layout(self.basis, self.mol_ptr, self.species)
+        assert int(bad.item()) == 0
+        self.h_elems = int(orb.mat_off[-1].item())
+        self.H = torch.from_numpy(synth.make_matrix_values(wl["seed"] + 1, self.h_elems)).to(dev)
+        self.he, self.hn, _ = eg.egnn_matrix_to_label(self.basis, orb, self.graph, self.H)
+        self.orb = orb
+        self.n_lab = eg.egnn_label_width(self.basis)
+        self.E = b.n_edges
+
+    def __call__(self):
+        eg = self.eg
+        orb, _ = eg.egnn_orbital_layout(self.basis, self.mol_ptr, self.species)
+        if self.wl["labels"] == "m2l":
+            eg.egnn_matrix_to_label(self.basis, orb, self.graph, self.H)
+        else:
+            eg.egnn_label_to_matrix(self.basis, orb, self.graph, self.he, self.hn, H=self.H)
+
+
+def cpu_baseline_labels(wl, n_mols):
+    """The fp64 oracle on the first `n_mols` molecules of the same batch (a prefix:
+    their atoms, edges and matrices are the first ones of the full arrays)."""
+    import synth
+    from oracle import labels
+    b = synth.make_molecule_batch(wl["seed"], wl["mols"], 10, 50)
+    k = min(n_mols, b.n_mols)
+    n_at = int(b.mol_ptr[k])
+    n_e = int(b.row_ptr[n_at])
+    sh, masks = synth.SVP_SHELLS, synth.SVP_MASKS
+    src, dst = b.src[:n_e].astype(np.int64), b.dst()[:n_e].astype(np.int64)
+    species = b.species[:n_at]
+    lay_full = labels.orbital_layout(b.mol_ptr[:k + 1], species, sh, masks)
+    H = synth.make_matrix_values(wl["seed"] + 1, lay_full[3][-1]).astype(np.float64)
+    t0 = time.perf_counter()
+    lay = labels.orbital_layout(b.mol_ptr[:k + 1], species, sh, masks)
+    he, hn = labels.matrix_to_labels(H, src, dst, None, species, lay, sh, masks)
+    if wl["labels"] == "l2m":
+        t0 = time.perf_counter()
+        lay = labels.orbital_layout(b.mol_ptr[:k + 1], species, sh, masks)
+        labels.labels_to_matrix(he, hn, src, dst, None, species, lay, sh, masks)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return dict(value=round(n_at / dt, 2), unit="atoms/s", cores=int(threads), kind="oracle",
+                sample=f"first {k} molecules of the batch ({n_at} atoms, {n_e} edges), fp64 numpy, {dt:.1f} s")
+
+
+def run_labels(args, wl, dev):
+    import torch
+    step = LabelStep(wl, dev)
+    copy_gbs = copy_bandwidth(torch, dev, args.copy_probe_mib)
+    eg = step.eg
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    eg.egnn_timing_reset()
+    eg.egnn_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    eg.egnn_timing_enable(False)
+    timing, dropped = eg.egnn_timing_collect()
+    fam, roof = roofline(timing, "f32", args.workload)
+    ms = (t1 - t0) * 1e3 / args.steps
+    b = step.batch
+    kernels = {k: dict(launches_per_step=v["launches"] / args.steps, ms_per_step=round(v["total_ms"] / args.steps, 4),
+                       algorithmic_gbs=round(v["bytes"] / (v["total_ms"] * 1e-3) / 1e9, 1))
+               for k, v in sorted(timing.items(), key=lambda kv: -kv[1]["total_ms"])}
+    name = "Matrix -> Label" if wl["labels"] == "m2l" else "Label -> Matrix"
+    out = {
+        "metric": f"atoms/s of {name} over a batch of molecules + % of HBM roofline",
+        "value": round(b.n_atoms * args.steps / (t1 - t0), 1),
+        "unit": "atoms/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded molecule sizes and elements, N(0,1) matrix entries)",
+        "config": {"workload": args.workload, "description": wl["desc"], "molecules": b.n_mols,
+                   "atoms": b.n_atoms, "edges": step.E, "labels_per_block": step.n_lab,
+                   "matrix_entries": step.h_elems,
+                   "blocks_per_s": round((b.n_atoms + step.E) * args.steps / (t1 - t0), 1)},
+        "roofline": dict(kernel=fam, **roof),
+        "hbm_copy_gbs": copy_gbs,
+        "kernels": kernels,
+        "timing_events_dropped": dropped,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_labels(wl, args.cpu_mols)
+    print(json.dumps(out), flush=True)
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -249,6 +374,8 @@ FAMILY_KERNELS = {
     "rotate_in": "::scatter_in_",
     "aggregate": "::aggregate_",
     "hblocks": "hblocks_kernel",
+    "matrix_to_label": "labels_kernel<8, true>",
+    "label_to_matrix": "labels_kernel<8, false>",
 }
 
 
@@ -396,6 +523,9 @@ def main():
         print(json.dumps(sweep(dev, max(args.warmup, 5), max(args.steps, 20))), flush=True)
         return
     wl = WORKLOADS[args.workload]
+    if "labels" in wl:
+        run_labels(args, wl, dev)
+        return
     step = Step(wl, dev)
     copy_gbs = copy_bandwidth(torch, dev, args.copy_probe_mib)
     eg = step.eg

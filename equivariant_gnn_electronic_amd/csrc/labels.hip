@@ -19,9 +19,11 @@
 // per lane in flight.  Lanes then run over labels (or entries) and sum the
 // sparse CG terms of each from an LDS copy of the table; each term is read
 // once for all CB blocks.
+#include <algorithm>
 #include <climits>
 #include <cstring>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "cg_real.h"
@@ -34,20 +36,31 @@ namespace {
 constexpr int kLSlots = 4;
 constexpr int kFullMax = 32;                 // orbitals of the full shell list
 constexpr int kEntMax = kFullMax * kFullMax;
-constexpr int kTermMax = 8192;
+constexpr int kPassMax = kEntMax / 64;       // 64-lane passes over a block's labels or entries
+constexpr int kRowMax = 256;                 // padded term rows of one direction
 constexpr int kSpeciesMax = 64;
 constexpr int kShellLMax = 3;                // s, p, d, f shells: labels up to L = 6
+
+// One direction of the transform (labels from entries, or entries from
+// labels) in lane-major form: the outputs are ordered by their number of CG
+// terms (most first) and dealt to the lanes of 64-wide passes; pass p reads
+// padded term rows prow[p] .. prow[p+1]-1, lane l taking coef / idx
+// [row][l] (zero coefficients pad the shorter lists), so every lane of a
+// pass runs the same number of terms and the reads are lane-contiguous.
+struct LDir {
+  int n_pass;
+  int prow[kPassMax + 1];
+  int16_t pos[kPassMax * 64];                // output of each lane of each pass, -1 if none
+  float coef[kRowMax * 64];
+  uint16_t idx[kRowMax * 64];                // input of each term (entry r * n_full + c, or label q)
+};
 
 struct LabelTable {
   int n_full, n_lab, n_species;
   int n_orb[kSpeciesMax + 1];                // the last row stands for an index outside the table
   int8_t omap[kSpeciesMax + 1][kFullMax];    // own orbital of each full orbital, -1 if absent
-  int lab_start[kEntMax + 1];                // Matrix -> Label: terms of label q ...
-  float lab_coef[kTermMax];
-  uint16_t lab_ent[kTermMax];                // ... over block entries r * n_full + c
-  int ent_start[kEntMax + 1];                // Label -> Matrix: terms of entry t ...
-  float ent_coef[kTermMax];
-  uint16_t ent_lab[kTermMax];                // ... over labels
+  LDir to_lab;                               // Matrix -> Label: label q from block entries
+  LDir to_ent;                               // Label -> Matrix: entry t from labels
 };
 
 __device__ LabelTable g_ltables[kLSlots];
@@ -111,24 +124,34 @@ const char *build_label_table(const egnn_basis *b, LabelTable *t) {
           by_ent[ent].push_back({static_cast<float>(c), q});
         }
   }
-  auto flatten = [&](const std::vector<std::vector<std::pair<float, int>>> &v, int *start, float *coef,
-                     uint16_t *idx) {
-    int n = 0;
-    for (size_t r = 0; r < v.size(); ++r) {
-      start[r] = n;
-      for (const auto &p : v[r]) {
-        if (n >= kTermMax) return false;
-        coef[n] = p.first;
-        idx[n] = static_cast<uint16_t>(p.second);
-        ++n;
+  auto deal = [&](const std::vector<std::vector<std::pair<float, int>>> &v, LDir *d) {
+    const int n = static_cast<int>(v.size());
+    std::vector<int> order(n);
+    for (int i = 0; i < n; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int c) { return v[a].size() > v[c].size(); });
+    d->n_pass = (n + 63) / 64;
+    int row = 0;
+    for (int p = 0; p < d->n_pass; ++p) {
+      size_t iters = 0;
+      for (int l = 0; l < 64; ++l) {
+        const int k = p * 64 + l;
+        d->pos[k] = static_cast<int16_t>(k < n ? order[k] : -1);
+        if (k < n) iters = std::max(iters, v[order[k]].size());
       }
+      d->prow[p] = row;
+      if (row + static_cast<int>(iters) > kRowMax) return false;
+      for (size_t it = 0; it < iters; ++it, ++row)
+        for (int l = 0; l < 64; ++l) {
+          const int k = p * 64 + l;
+          const bool has = k < n && it < v[order[k]].size();
+          d->coef[row * 64 + l] = has ? v[order[k]][it].first : 0.0f;
+          d->idx[row * 64 + l] = static_cast<uint16_t>(has ? v[order[k]][it].second : 0);
+        }
     }
-    start[v.size()] = n;
+    d->prow[d->n_pass] = row;
     return true;
   };
-  if (!flatten(by_lab, t->lab_start, t->lab_coef, t->lab_ent) ||
-      !flatten(by_ent, t->ent_start, t->ent_coef, t->ent_lab))
-    return "too many coupling terms for the table";
+  if (!deal(by_lab, &t->to_lab) || !deal(by_ent, &t->to_ent)) return "too many coupling terms for the table";
   return nullptr;
 }
 
@@ -138,7 +161,7 @@ struct LKey {
   uint32_t mask[kSpeciesMax];
 };
 struct LInfo {
-  int n_full, n_lab, n_species, lab_terms, ent_terms;
+  int n_full, n_lab, n_species, lab_rows, ent_rows, n_pass;
 };
 struct LCache {
   std::mutex mu;
@@ -190,8 +213,9 @@ egnn_status label_slot(const egnn_basis *b, int *slot, LInfo *info) {
   in.n_full = t[0].n_full;
   in.n_lab = t[0].n_lab;
   in.n_species = t[0].n_species;
-  in.lab_terms = t[0].lab_start[in.n_lab];
-  in.ent_terms = t[0].ent_start[in.n_lab];
+  in.lab_rows = t[0].to_lab.prow[t[0].to_lab.n_pass];
+  in.ent_rows = t[0].to_ent.prow[t[0].to_ent.n_pass];
+  in.n_pass = t[0].to_lab.n_pass;
   g_lcache.used[dev] = s + 1;
   *slot = s;
   *info = in;
@@ -328,7 +352,8 @@ __device__ inline Blk block_of(const Rows &R, int n_species, const int *norb, in
     mo = R.mat_off[mj];
   }
   const int oi = R.atom_orb[ic], oj = R.atom_orb[j];
-  ok = ok && ld >= 0 && oi >= 0 && oj >= 0 && oi + norb[k.zi] <= ld && oj + norb[k.zj] <= ld && mo >= 0 &&
+  // (ld < 2^26 keeps the 32-bit entry offsets r * ld + c of the kernels exact)
+  ok = ok && ld >= 0 && ld < (1 << 26) && oi >= 0 && oj >= 0 && oi + norb[k.zi] <= ld && oj + norb[k.zj] <= ld && mo >= 0 &&
        mo + static_cast<int64_t>(ld) * ld <= R.h_elems;
   k.ok = ok;
   k.ld = ok ? ld : 0;
@@ -336,12 +361,14 @@ __device__ inline Blk block_of(const Rows &R, int n_species, const int *norb, in
   return k;
 }
 
-// LDS: term table (start, coef, index), templates (omap, n_orb), then per wave CB label buffers.
-__host__ __device__ inline size_t lds_words(int n_lab, int n_terms, int n_species, int n_full) {
-  return (static_cast<size_t>(n_lab + 1) + 2 * n_terms + static_cast<size_t>(n_species + 1) * (n_full + 1) + 3) & ~3;
+// LDS: one direction's passes (prow, pos, coef, idx), templates (omap,
+// n_orb), then per wave CB staged blocks.
+__host__ __device__ inline size_t lds_words(int n_pass, int rows, int n_species, int n_full) {
+  return (static_cast<size_t>(n_pass + 1) + 64 * static_cast<size_t>(n_pass) + 128 * static_cast<size_t>(rows) +
+          static_cast<size_t>(n_species + 1) * (n_full + 1) + 3) & ~static_cast<size_t>(3);
 }
 
-template <int CB, bool TO_LABEL>
+template <int CB, int NT, bool TO_LABEL>
 __global__ void __launch_bounds__(kLW * kLWaves) labels_kernel(int slot, Rows R, const float *__restrict__ Hin,
                                                                 float *__restrict__ Hout,
                                                                 const float *__restrict__ lab_e_in,
@@ -349,23 +376,24 @@ __global__ void __launch_bounds__(kLW * kLWaves) labels_kernel(int slot, Rows R,
                                                                 float *__restrict__ lab_e_out,
                                                                 float *__restrict__ lab_n_out,
                                                                 unsigned long long *skipped) {
+  static_assert(NT * CB <= 64, "one presence bit per staged value");
   extern __shared__ float lsm[];
   const LabelTable &tb = g_ltables[slot];
   const int nf = tb.n_full, n_lab = tb.n_lab, nsp = tb.n_species;
-  const int *g_start = TO_LABEL ? tb.lab_start : tb.ent_start;
-  const float *g_coef = TO_LABEL ? tb.lab_coef : tb.ent_coef;
-  const uint16_t *g_idx = TO_LABEL ? tb.lab_ent : tb.ent_lab;
-  const int n_terms = g_start[n_lab];
-  int *t_start = reinterpret_cast<int *>(lsm);                     // [n_lab + 1]
-  float *t_coef = lsm + (n_lab + 1);                               // [n_terms]
-  int *t_idx = reinterpret_cast<int *>(t_coef + n_terms);          // [n_terms]
-  int *omap = t_idx + n_terms;                                     // [nsp + 1][nf]
+  const LDir &dir = TO_LABEL ? tb.to_lab : tb.to_ent;
+  const int n_pass = dir.n_pass, n_rows = dir.prow[n_pass];
+  int *s_prow = reinterpret_cast<int *>(lsm);                      // [n_pass + 1]
+  int *s_pos = s_prow + (n_pass + 1);                              // [n_pass][64]
+  float *s_coef = reinterpret_cast<float *>(s_pos + 64 * n_pass);  // [n_rows][64]
+  int *s_idx = reinterpret_cast<int *>(s_coef + 64 * n_rows);      // [n_rows][64]
+  int *omap = s_idx + 64 * n_rows;                                 // [nsp + 1][nf]
   int *norb = omap + (nsp + 1) * nf;                               // [nsp + 1]
-  float *buf_all = lsm + lds_words(n_lab, n_terms, nsp, nf);       // [kLWaves][CB][n_lab]
-  for (int i = threadIdx.x; i <= n_lab; i += blockDim.x) t_start[i] = g_start[i];
-  for (int i = threadIdx.x; i < n_terms; i += blockDim.x) {
-    t_coef[i] = g_coef[i];
-    t_idx[i] = g_idx[i];
+  float *buf_all = lsm + lds_words(n_pass, n_rows, nsp, nf);       // [kLWaves][CB][n_lab]
+  for (int i = threadIdx.x; i <= n_pass; i += blockDim.x) s_prow[i] = dir.prow[i];
+  for (int i = threadIdx.x; i < 64 * n_pass; i += blockDim.x) s_pos[i] = dir.pos[i];
+  for (int i = threadIdx.x; i < 64 * n_rows; i += blockDim.x) {
+    s_coef[i] = dir.coef[i];
+    s_idx[i] = dir.idx[i];
   }
   for (int i = threadIdx.x; i < (nsp + 1) * nf; i += blockDim.x) {
     const int z = i / nf;
@@ -375,101 +403,199 @@ __global__ void __launch_bounds__(kLW * kLWaves) labels_kernel(int slot, Rows R,
   __syncthreads();
   const int lane = threadIdx.x % kLW, wave = threadIdx.x / kLW;
   float *buf = buf_all + static_cast<size_t>(wave) * CB * n_lab;
-  for (int64_t j = static_cast<int64_t>(blockIdx.x) * kLWaves + wave; j < R.n_atoms;
-       j += static_cast<int64_t>(gridDim.x) * kLWaves) {
-    const int e0 = R.edges ? R.row_ptr[j] : 0;
-    const int nb = R.nodes + (R.edges ? R.row_ptr[j + 1] - e0 : 0);
-    for (int c0 = 0; c0 < nb; c0 += CB) {
-      const int nc = min(CB, nb - c0);
-      // lane b < nc describes block c0 + b; the wave reads the descriptions
-      // back as scalars
-      Blk mine{0, 0, 0, nsp, nsp, 0, 0};
-      if (lane < nc) mine = block_of(R, nsp, norb, j, c0 + lane, e0);
-      const unsigned long long bad = __ballot(lane < nc && !mine.ok);
-      if (lane == 0 && bad && skipped) atomicAdd(skipped, static_cast<unsigned long long>(__popcll(bad)));
-      int64_t base[CB], out[CB];
-      int ld[CB], zi[CB], zj[CB], ok[CB], node[CB];
+  // the entries (r, c) this lane stages, one per pass over the block
+  // (clamped to entry 0 past the block; `tin` bit it says the entry exists)
+  int rr[NT], cc[NT];
+  uint32_t tin = 0;
+#pragma unroll
+  for (int it = 0; it < NT; ++it) {
+    const int t = lane + kLW * it;
+    const bool in = t < n_lab;
+    rr[it] = in ? t / nf : 0;
+    cc[it] = in ? t - (t / nf) * nf : 0;
+    tin |= static_cast<uint32_t>(in) << it;
+  }
+  // Label -> Matrix: the entry (er, ec) each lane forms in each pass (-1: none)
+  int er[NT], ec[NT];
+#pragma unroll
+  for (int ps = 0; ps < NT; ++ps) {
+    const int t = ps < n_pass ? s_pos[ps * 64 + lane] : -1;
+    er[ps] = t >= 0 ? t / nf : -1;
+    ec[ps] = t >= 0 ? t - er[ps] * nf : 0;
+  }
+  (void)er;
+  (void)ec;
+  // Rows are dealt to the XCDs in contiguous ranges (workgroup g runs on XCD
+  // g % 8), so the rows of one structure, which read the same matrix lines,
+  // share one L2.  Each wave's chunks form one sequence (row j, first block
+  // c0); rows without blocks are passed over.  The blocks of a row are
+  // described 64 at a time (segment s0), one block per lane.
+  struct Pos {
+    int64_t j;
+    int e0, nb, s0, c0;
+  };
+  const bool by_xcd = gridDim.x % 8 == 0;
+  const int64_t xcd = blockIdx.x % 8, groups = by_xcd ? gridDim.x / 8 : gridDim.x;
+  const int64_t local = by_xcd ? blockIdx.x / 8 : blockIdx.x;
+  const int64_t j_end = by_xcd ? R.n_atoms * (xcd + 1) / 8 : R.n_atoms;
+  const int64_t j_begin = by_xcd ? R.n_atoms * xcd / 8 : 0;
+  const int64_t stride = groups * kLWaves;
+  auto row_at = [&](int64_t j) {
+    Pos p{j, 0, 0, 0, 0};
+    while (p.j < j_end) {
+      p.e0 = R.edges ? R.row_ptr[p.j] : 0;
+      p.nb = R.nodes + (R.edges ? R.row_ptr[p.j + 1] - p.e0 : 0);
+      if (p.nb > 0) break;
+      p.j += stride;
+    }
+    return p;
+  };
+  auto next = [&](Pos p) {
+    p.c0 += CB;
+    if (p.c0 >= p.nb) return row_at(p.j + stride);
+    if (p.c0 >= p.s0 + kLW) p.s0 += kLW;
+    return p;
+  };
+  // lane l describes block s0 + l of the row (blocks past the row are empty
+  // slots pointing at row 0 of a kind of block that exists: the on-site rows
+  // whenever they are requested, else the first edge)
+  auto describe = [&](const Pos &p) {
+    Blk k{0, 0, 0, nsp, nsp, 0, R.nodes};
+    const bool mine = p.j < j_end && p.s0 + lane < p.nb;
+    if (mine) k = block_of(R, nsp, norb, p.j, p.s0 + lane, p.e0);
+    const unsigned long long bad = __ballot(mine && !k.ok);
+    if (lane == 0 && bad && skipped) atomicAdd(skipped, static_cast<unsigned long long>(__popcll(bad)));
+    return k;
+  };
+  auto rl = [](int v, int l) { return __builtin_amdgcn_readlane(v, l); };
+  auto rl64 = [](int64_t v, int l) {
+    return (static_cast<int64_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), l)) << 32) |
+           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+  };
+  float v[NT][CB];
+  using Mask = typename std::conditional<(NT * CB <= 32), uint32_t, unsigned long long>::type;
+  Mask pres = 0;  // bit it * CB + b: value v[it][b] is a matrix entry (Matrix -> Label)
+  // issue every load of a chunk before any of them is used; each block's
+  // base is a wave-uniform pointer and the entries 32-bit offsets from it
+  auto issue = [&](const Blk &k, const Pos &p) {
+    const int l0 = p.c0 - p.s0;
+    if constexpr (TO_LABEL) {
+      pres = 0;
 #pragma unroll
       for (int b = 0; b < CB; ++b) {
-        base[b] = (static_cast<int64_t>(__builtin_amdgcn_readlane(static_cast<int>(mine.base >> 32), b)) << 32) |
-                  static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mine.base), b));
-        out[b] = (static_cast<int64_t>(__builtin_amdgcn_readlane(static_cast<int>(mine.out >> 32), b)) << 32) |
-                 static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mine.out), b));
-        ld[b] = __builtin_amdgcn_readlane(mine.ld, b);
-        zi[b] = __builtin_amdgcn_readlane(mine.zi, b);
-        zj[b] = __builtin_amdgcn_readlane(mine.zj, b);
-        ok[b] = __builtin_amdgcn_readlane(mine.ok, b);
-        node[b] = __builtin_amdgcn_readlane(mine.node, b);
+        const float *bp = Hin + rl64(k.base, l0 + b);
+        const int ld = rl(k.ld, l0 + b), oi = rl(k.zi, l0 + b) * nf, oj = rl(k.zj, l0 + b) * nf;
+        const bool ok = rl(k.ok, l0 + b) != 0;
+#pragma unroll
+        for (int it = 0; it < NT; ++it) {
+          const int lr = omap[oi + rr[it]], lc = omap[oj + cc[it]];
+          const bool pr = ok & ((tin >> it) & 1u) & (lr >= 0) & (lc >= 0);
+          // absent entries read the block's first element (element 0 of H for
+          // a block with no place) and are zeroed when staged
+          const uint32_t off = pr ? static_cast<uint32_t>(lr * ld + lc) : 0u;
+          v[it][b] = bp[off];
+          pres |= static_cast<Mask>(pr) << (it * CB + b);
+        }
       }
-      if constexpr (TO_LABEL) {
-        // (1) extract: entry t = (r, c) of the full shape, zero where the
-        // template has no orbital (clamped loads, then a select: no branch
-        // between the CB loads)
-        for (int t = lane; t < n_lab; t += kLW) {
-          const int r = t / nf, c = t - r * nf;
-          float v[CB];
-          bool p[CB];
+    } else {
 #pragma unroll
-          for (int b = 0; b < CB; ++b) {
-            const int lr = omap[zi[b] * nf + r], lc = omap[zj[b] * nf + c];
-            p[b] = b < nc && ok[b] && lr >= 0 && lc >= 0;
-            v[b] = Hin[p[b] ? base[b] + static_cast<int64_t>(lr) * ld[b] + lc : 0];
-          }
+      for (int b = 0; b < CB; ++b) {
+        const float *row = (rl(k.node, l0 + b) ? lab_n_in : lab_e_in) + rl64(k.out, l0 + b) * n_lab;
 #pragma unroll
-          for (int b = 0; b < CB; ++b) buf[b * n_lab + t] = p[b] ? v[b] : 0.0f;
-        }
-        wave_lds_order();
-        // (2) Eq. (1): label q of each block from its CG terms
-        for (int q = lane; q < n_lab; q += kLW) {
-          float acc[CB];
-#pragma unroll
-          for (int b = 0; b < CB; ++b) acc[b] = 0.0f;
-          const int t1 = t_start[q + 1];
-          for (int k = t_start[q]; k < t1; ++k) {
-            const float cf = t_coef[k];
-            const int ix = t_idx[k];
-#pragma unroll
-            for (int b = 0; b < CB; ++b) acc[b] += cf * buf[b * n_lab + ix];
-          }
-#pragma unroll
-          for (int b = 0; b < CB; ++b)
-            if (b < nc) (node[b] ? lab_n_out : lab_e_out)[out[b] * n_lab + q] = acc[b];
-        }
-        wave_lds_order();
-      } else {
-        // labels of the CB blocks into LDS (rows of n_lab floats)
-        for (int q = lane; q < n_lab; q += kLW) {
-          float v[CB];
-#pragma unroll
-          for (int b = 0; b < CB; ++b)
-            if (b < nc) v[b] = (node[b] ? lab_n_in : lab_e_in)[out[b] * n_lab + q];
-#pragma unroll
-          for (int b = 0; b < CB; ++b)
-            if (b < nc) buf[b * n_lab + q] = v[b];
-        }
-        wave_lds_order();
-        // entries from their CG terms, written where the template has an orbital
-        for (int t = lane; t < n_lab; t += kLW) {
-          const int r = t / nf, c = t - r * nf;
-          float acc[CB];
-#pragma unroll
-          for (int b = 0; b < CB; ++b) acc[b] = 0.0f;
-          const int t1 = t_start[t + 1];
-          for (int k = t_start[t]; k < t1; ++k) {
-            const float cf = t_coef[k];
-            const int ix = t_idx[k];
-#pragma unroll
-            for (int b = 0; b < CB; ++b) acc[b] += cf * buf[b * n_lab + ix];
-          }
-#pragma unroll
-          for (int b = 0; b < CB; ++b) {
-            const int lr = omap[zi[b] * nf + r], lc = omap[zj[b] * nf + c];
-            if (b < nc && ok[b] && lr >= 0 && lc >= 0) Hout[base[b] + static_cast<int64_t>(lr) * ld[b] + lc] = acc[b];
-          }
-        }
-        wave_lds_order();
+        for (int it = 0; it < NT; ++it) v[it][b] = row[static_cast<uint32_t>(min(lane + kLW * it, n_lab - 1))];
       }
     }
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int it = 0; it < NT; ++it) {
+      const int t = lane + kLW * it;
+      if (t < n_lab) {
+#pragma unroll
+        for (int b = 0; b < CB; ++b) {
+          float x = v[it][b];
+          if constexpr (TO_LABEL) x = ((pres >> (it * CB + b)) & 1u) ? x : 0.0f;
+          buf[b * n_lab + t] = x;
+        }
+      }
+    }
+  };
+  Pos p = row_at(j_begin + local * kLWaves + wave);
+  Blk k = describe(p);
+  if (p.j < j_end) issue(k, p);
+  while (p.j < j_end) {
+    const int nc = min(CB, p.nb - p.c0);
+    const int l0 = p.c0 - p.s0;
+    commit();
+    wave_lds_order();
+    // the next chunk's loads run while this chunk's outputs are formed
+    const Pos pn = next(p);
+    const Blk kn = (pn.j != p.j || pn.s0 != p.s0) ? describe(pn) : k;
+    if (pn.j < j_end) issue(kn, pn);
+    if constexpr (TO_LABEL) {
+      // Eq. (1): the labels of each block from their CG terms over the staged
+      // entries, one pass of 64 labels at a time
+      float *op[CB];
+#pragma unroll
+      for (int b = 0; b < CB; ++b)
+        op[b] = (rl(k.node, l0 + b) ? lab_n_out : lab_e_out) + rl64(k.out, l0 + b) * n_lab;
+      for (int ps = 0; ps < n_pass; ++ps) {
+        float acc[CB];
+#pragma unroll
+        for (int b = 0; b < CB; ++b) acc[b] = 0.0f;
+        const int r1 = s_prow[ps + 1];
+        for (int rw = s_prow[ps]; rw < r1; ++rw) {
+          const float cf = s_coef[rw * 64 + lane];
+          const int ix = s_idx[rw * 64 + lane];
+#pragma unroll
+          for (int b = 0; b < CB; ++b) acc[b] += cf * buf[b * n_lab + ix];
+        }
+        const int q = s_pos[ps * 64 + lane];
+        if (q >= 0) {
+#pragma unroll
+          for (int b = 0; b < CB; ++b)
+            if (b < nc) op[b][static_cast<uint32_t>(q)] = acc[b];
+        }
+      }
+    } else {
+      // entries from their CG terms over the staged labels, written where the
+      // template has an orbital
+      float *bp[CB];
+      int ldb[CB], oib[CB], ojb[CB];
+      bool okb[CB];
+#pragma unroll
+      for (int b = 0; b < CB; ++b) {
+        bp[b] = Hout + rl64(k.base, l0 + b);
+        ldb[b] = rl(k.ld, l0 + b);
+        oib[b] = rl(k.zi, l0 + b) * nf;
+        ojb[b] = rl(k.zj, l0 + b) * nf;
+        okb[b] = b < nc && rl(k.ok, l0 + b) != 0;
+      }
+#pragma unroll
+      for (int ps = 0; ps < NT; ++ps) {
+        if (ps >= n_pass) break;
+        float acc[CB];
+#pragma unroll
+        for (int b = 0; b < CB; ++b) acc[b] = 0.0f;
+        const int r1 = s_prow[ps + 1];
+        for (int rw = s_prow[ps]; rw < r1; ++rw) {
+          const float cf = s_coef[rw * 64 + lane];
+          const int ix = s_idx[rw * 64 + lane];
+#pragma unroll
+          for (int b = 0; b < CB; ++b) acc[b] += cf * buf[b * n_lab + ix];
+        }
+        if (er[ps] >= 0) {
+#pragma unroll
+          for (int b = 0; b < CB; ++b) {
+            const int lr = omap[oib[b] + er[ps]], lc = omap[ojb[b] + ec[ps]];
+            if (okb[b] && lr >= 0 && lc >= 0) bp[b][static_cast<uint32_t>(lr * ldb[b] + lc)] = acc[b];
+          }
+        }
+      }
+    }
+    wave_lds_order();
+    p = pn;
+    k = kn;
   }
 }
 
@@ -524,33 +650,42 @@ egnn_status run_labels(bool to_label, const egnn_basis *b, const egnn_orbitals *
   R.h_elems = h_elems;
   R.nodes = nodes ? 1 : 0;
   R.edges = edges ? 1 : 0;
-  const int n_terms = to_label ? info.lab_terms : info.ent_terms;
+  const int n_rows = to_label ? info.lab_rows : info.ent_rows;
   const int64_t rows = (edges ? g->n_edges : 0) + (nodes ? o->n_atoms : 0);
   // algorithmic bytes: every label row once, and every matrix entry once
   // when the graph covers each block (a fully connected structure)
   Timed tm(stream, to_label ? "matrix_to_label" : "label_to_matrix", 0.0,
            4.0 * (double(rows) * info.n_lab + double(h_elems)));
-  int64_t blocks = (static_cast<int64_t>(o->n_atoms) + kLWaves - 1) / kLWaves;
+  // a multiple of 8 workgroups: rows are dealt to the XCDs in contiguous ranges
+  int64_t blocks = ((static_cast<int64_t>(o->n_atoms) + kLWaves - 1) / kLWaves + 7) / 8 * 8;
   if (blocks > 2048) blocks = 2048;
-  const size_t base_words = lds_words(info.n_lab, n_terms, info.n_species, info.n_full);
-  auto launch = [&](auto cb) -> egnn_status {
-    constexpr int CB = decltype(cb)::value;
+  const size_t base_words = lds_words(info.n_pass, n_rows, info.n_species, info.n_full);
+  auto launch = [&](auto cb, auto nt) -> egnn_status {
+    constexpr int CB = decltype(cb)::value, NT = decltype(nt)::value;
     const size_t smem = 4 * (base_words + static_cast<size_t>(kLWaves) * CB * info.n_lab);
     if (smem > 160 * 1024) {
       set_error("Matrix <-> Label needs %zu bytes of LDS; reduce the basis", smem);
       return EGNN_E_UNSUPPORTED;
     }
     if (to_label)
-      labels_kernel<CB, true><<<static_cast<unsigned>(blocks), kLW * kLWaves, smem, stream>>>(
+      labels_kernel<CB, NT, true><<<static_cast<unsigned>(blocks), kLW * kLWaves, smem, stream>>>(
           slot, R, Hin, nullptr, nullptr, nullptr, le_out, ln_out, skip);
     else
-      labels_kernel<CB, false><<<static_cast<unsigned>(blocks), kLW * kLWaves, smem, stream>>>(
+      labels_kernel<CB, NT, false><<<static_cast<unsigned>(blocks), kLW * kLWaves, smem, stream>>>(
           slot, R, nullptr, Hout, le_in, ln_in, nullptr, nullptr, skip);
     EGNN_CHECK_LAUNCH();
     return EGNN_OK;
   };
-  if (info.n_lab <= 512) return launch(std::integral_constant<int, 8>{});
-  return launch(std::integral_constant<int, 4>{});
+  // NT passes of 64 entries cover a block; CB blocks per chunk keep NT * CB
+  // values in flight per lane
+  const int passes = (info.n_lab + kLW - 1) / kLW;
+  if (passes <= 1) return launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 1>{});
+  if (passes <= 2) return launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 2>{});
+  if (passes <= 4) return launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 4>{});
+  if (passes <= 6) return launch(std::integral_constant<int, 4>{}, std::integral_constant<int, 6>{});
+  if (passes <= 8) return launch(std::integral_constant<int, 4>{}, std::integral_constant<int, 8>{});
+  if (passes <= 12) return launch(std::integral_constant<int, 2>{}, std::integral_constant<int, 12>{});
+  return launch(std::integral_constant<int, 2>{}, std::integral_constant<int, 16>{});
 }
 
 }  // namespace
