@@ -13,12 +13,18 @@
 // -> Matrix applies the transpose and writes the template's entries back.
 //
 // The pages' CUDA kernel gives one thread per matrix element and one thread
-// block per node or edge.  Here one 64-lane wave owns a destination row.  It
-// takes the row's on-site block and its edges CB at a time and stages them
-// in LDS in the full shape, with lanes over entries and CB independent loads
-// per lane in flight.  Lanes then run over labels (or entries) and sum the
-// sparse CG terms of each from an LDS copy of the table; each term is read
-// once for all CB blocks.
+// block per node or edge, driven by an orbital template per element pair.
+// Here the templates are the distinct shell masks of the elements, and the
+// host builds, for every ordered template pair, the CG terms of exactly the
+// labels and entries that pair carries.  One 64-lane wave owns a destination
+// row.  It describes the row's blocks (its on-site block, then its edges) 64
+// at a time, one per lane, groups them by template pair, and takes each
+// group CB blocks at a time: their present entries (or labels) are loaded
+// with CB independent loads per lane in flight and staged in LDS, then lanes
+// run over the pair's outputs, dealt to them by term count so that every
+// lane of a pass runs the same number of terms, and each term is read once
+// for all CB blocks.  Labels a pair lacks are written as zeros.  The next
+// chunk's loads are issued before the current chunk's outputs are formed.
 #include <algorithm>
 #include <climits>
 #include <cstring>
@@ -35,32 +41,40 @@ namespace {
 
 constexpr int kLSlots = 4;
 constexpr int kFullMax = 32;                 // orbitals of the full shell list
-constexpr int kEntMax = kFullMax * kFullMax;
-constexpr int kPassMax = kEntMax / 64;       // 64-lane passes over a block's labels or entries
-constexpr int kRowMax = 256;                 // padded term rows of one direction
 constexpr int kSpeciesMax = 64;
 constexpr int kShellLMax = 3;                // s, p, d, f shells: labels up to L = 6
+constexpr int kTmplMax = 8;                  // distinct element bases (shell masks)
+constexpr int kPairN = (kTmplMax + 1) * (kTmplMax + 1);  // ordered template pairs, the empty template included
+constexpr int kRowMax = 2048;                // padded term rows per direction
+constexpr int kPosMax = 1 << 15;             // lane outputs over all passes
+constexpr int kPassTot = 4096;               // passes over all pairs and both directions
 
-// One direction of the transform (labels from entries, or entries from
-// labels) in lane-major form: the outputs are ordered by their number of CG
-// terms (most first) and dealt to the lanes of 64-wide passes; pass p reads
-// padded term rows prow[p] .. prow[p+1]-1, lane l taking coef / idx
-// [row][l] (zero coefficients pad the shorter lists), so every lane of a
-// pass runs the same number of terms and the reads are lane-contiguous.
-struct LDir {
-  int n_pass;
-  int prow[kPassMax + 1];
-  int16_t pos[kPassMax * 64];                // output of each lane of each pass, -1 if none
-  float coef[kRowMax * 64];
-  uint16_t idx[kRowMax * 64];                // input of each term (entry r * n_full + c, or label q)
+// Per ordered template pair (u: source / row side, w: destination / column
+// side).  The pair's own block is n_u x n_w, its entries p = lr * n_w + lc;
+// it carries P = n_u * n_w of the labels (one per own entry).
+struct PairInfo {
+  int P, n_w, magic;        // present entries; columns; ceil(2^16 / n_w) (p / n_w = p * magic >> 16, p < 2048)
+  int lpass, lprow, lpos;   // Matrix -> Label: passes over the present labels (pos: label q)
+  int zpass, zpos;          //   passes over the absent labels (pos: label q, written as zero)
+  int spass, spos;          // Label -> Matrix: staging passes (pos: label q of compact input i)
+  int epass, eprow, epos;   //   passes over the own entries (pos: entry p)
 };
+constexpr int kPairInts = sizeof(PairInfo) / sizeof(int);
 
+// Padded lane-major passes: pass ps of a pair reads term rows
+// prow[xprow + ps] .. prow[xprow + ps + 1] - 1, lane l taking coef / idx
+// [row][l] (zero coefficients pad the shorter term lists), and writes output
+// pos[xpos + ps * 64 + l] (-1: none).
 struct LabelTable {
-  int n_full, n_lab, n_species;
-  int n_orb[kSpeciesMax + 1];                // the last row stands for an index outside the table
-  int8_t omap[kSpeciesMax + 1][kFullMax];    // own orbital of each full orbital, -1 if absent
-  LDir to_lab;                               // Matrix -> Label: label q from block entries
-  LDir to_ent;                               // Label -> Matrix: entry t from labels
+  int n_full, n_lab, n_species, n_tmpl;
+  int n_orb[kSpeciesMax];                    // orbitals of each element
+  int tmpl[kSpeciesMax];                     // template of each element
+  PairInfo pair[kPairN];                     // [u * (n_tmpl + 1) + w], template n_tmpl = empty
+  int n_prow, n_pos, rows[2];                // used sizes; rows per direction (0: to labels, 1: to entries)
+  int prow[kPassTot];
+  int16_t pos[kPosMax];
+  float coef[2][kRowMax * 64];
+  uint16_t idx[2][kRowMax * 64];
 };
 
 __device__ LabelTable g_ltables[kLSlots];
@@ -70,9 +84,10 @@ const char *build_label_table(const egnn_basis *b, LabelTable *t) {
   if (!b || !b->shell_l || !b->species_shells) return "basis pointers are null";
   if (b->n_shells < 1 || b->n_shells > 16) return "n_shells must be 1..16";
   if (b->n_species < 1 || b->n_species > kSpeciesMax) return "n_species must be 1..64";
-  std::vector<int> off(b->n_shells);
+  const int ns = b->n_shells;
+  std::vector<int> off(ns);
   int o = 0, lmx = 0;
-  for (int a = 0; a < b->n_shells; ++a) {
+  for (int a = 0; a < ns; ++a) {
     const int l = b->shell_l[a];
     if (l < 0 || l > kShellLMax) return "shell degrees must be 0..3";
     off[a] = o;
@@ -81,77 +96,135 @@ const char *build_label_table(const egnn_basis *b, LabelTable *t) {
   }
   if (o > kFullMax) return "the full shell list has more than 32 orbitals";
   for (int z = 0; z < b->n_species; ++z)
-    if (b->species_shells[z] >> b->n_shells) return "a species mask names a shell beyond n_shells";
+    if (b->species_shells[z] >> ns) return "a species mask names a shell beyond n_shells";
   std::memset(t, 0, sizeof(*t));
-  std::memset(t->omap, 0xFF, sizeof(t->omap));
   t->n_full = o;
   t->n_lab = o * o;
   t->n_species = b->n_species;
+  // templates: the distinct masks, in order of first appearance
+  std::vector<uint32_t> masks;
   for (int z = 0; z < b->n_species; ++z) {
-    int oo = 0;
-    for (int a = 0; a < b->n_shells; ++a)
-      if ((b->species_shells[z] >> a) & 1u) {
-        const int l = b->shell_l[a];
-        for (int m = 0; m < 2 * l + 1; ++m) t->omap[z][off[a] + m] = static_cast<int8_t>(oo + m);
-        oo += 2 * l + 1;
-      }
-    t->n_orb[z] = oo;
+    const uint32_t m = b->species_shells[z];
+    int u = static_cast<int>(std::find(masks.begin(), masks.end(), m) - masks.begin());
+    if (u == static_cast<int>(masks.size())) {
+      if (u >= kTmplMax) return "more than 8 distinct element bases";
+      masks.push_back(m);
+    }
+    t->tmpl[z] = u;
   }
-  // label channels: ordered shell pairs in lexicographic order, L ascending
+  const int T = static_cast<int>(masks.size());
+  t->n_tmpl = T;
+  masks.push_back(0u);  // the empty template
+  // own orbital of each full orbital, per template (-1 if absent)
+  std::vector<std::vector<int>> omap(T + 1, std::vector<int>(o, -1));
+  std::vector<int> norb(T + 1, 0);
+  for (int u = 0; u <= T; ++u)
+    for (int a = 0; a < ns; ++a)
+      if ((masks[u] >> a) & 1u)
+        for (int m = 0; m < 2 * b->shell_l[a] + 1; ++m) omap[u][off[a] + m] = norb[u]++;
+  for (int z = 0; z < b->n_species; ++z) t->n_orb[z] = norb[t->tmpl[z]];
+  // label channels of the full list: ordered shell pairs, L ascending
   const int Lmax = 2 * lmx;
   std::vector<int> nL(Lmax + 1, 0), hoff(Lmax + 2, 0);
   struct Item { int a, b, L, k; };
   std::vector<Item> items;
-  for (int a = 0; a < b->n_shells; ++a)
-    for (int c = 0; c < b->n_shells; ++c)
+  for (int a = 0; a < ns; ++a)
+    for (int c = 0; c < ns; ++c)
       for (int L = std::abs(b->shell_l[a] - b->shell_l[c]); L <= b->shell_l[a] + b->shell_l[c]; ++L)
         items.push_back({a, c, L, nL[L]++});
   for (int L = 0; L <= Lmax; ++L) hoff[L + 1] = hoff[L] + (2 * L + 1) * nL[L];
   if (hoff[Lmax + 1] != o * o) return "internal: label count differs from the block size";
-  std::vector<std::vector<std::pair<float, int>>> by_lab(o * o), by_ent(o * o);
-  for (const Item &it : items) {
-    const int la = b->shell_l[it.a], lb = b->shell_l[it.b];
-    const std::vector<double> Q = cg::real_coupling(la, lb, it.L);
-    const int nb = 2 * lb + 1, nm = 2 * it.L + 1;
-    for (int i = 0; i < 2 * la + 1; ++i)
-      for (int j = 0; j < nb; ++j)
-        for (int M = 0; M < nm; ++M) {
-          const double c = Q[(i * nb + j) * nm + M];
-          if (std::fabs(c) < 1e-12) continue;
-          const int ent = (off[it.a] + i) * o + off[it.b] + j;
-          const int q = hoff[it.L] + M * nL[it.L] + it.k;
-          by_lab[q].push_back({static_cast<float>(c), ent});
-          by_ent[ent].push_back({static_cast<float>(c), q});
-        }
-  }
-  auto deal = [&](const std::vector<std::vector<std::pair<float, int>>> &v, LDir *d) {
-    const int n = static_cast<int>(v.size());
+  std::vector<std::vector<double>> Q(items.size());
+  for (size_t it = 0; it < items.size(); ++it)
+    Q[it] = cg::real_coupling(b->shell_l[items[it].a], b->shell_l[items[it].b], items[it].L);
+  typedef std::vector<std::pair<float, int>> Terms;
+  // deal outputs (id, terms) to padded lane-major passes of direction d
+  auto deal = [&](const std::vector<std::pair<int, Terms>> &outs, int d, int *npass, int *prow0, int *pos0) {
+    const int n = static_cast<int>(outs.size());
     std::vector<int> order(n);
     for (int i = 0; i < n; ++i) order[i] = i;
-    std::stable_sort(order.begin(), order.end(), [&](int a, int c) { return v[a].size() > v[c].size(); });
-    d->n_pass = (n + 63) / 64;
-    int row = 0;
-    for (int p = 0; p < d->n_pass; ++p) {
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int x, int y) { return outs[x].second.size() > outs[y].second.size(); });
+    *npass = (n + 63) / 64;
+    *prow0 = t->n_prow;
+    *pos0 = t->n_pos;
+    if (t->n_prow + *npass + 1 > kPassTot || t->n_pos + 64 * *npass > kPosMax) return false;
+    for (int ps = 0; ps < *npass; ++ps) {
       size_t iters = 0;
       for (int l = 0; l < 64; ++l) {
-        const int k = p * 64 + l;
-        d->pos[k] = static_cast<int16_t>(k < n ? order[k] : -1);
-        if (k < n) iters = std::max(iters, v[order[k]].size());
+        const int k = ps * 64 + l;
+        t->pos[t->n_pos + k] = static_cast<int16_t>(k < n ? outs[order[k]].first : -1);
+        if (k < n) iters = std::max(iters, outs[order[k]].second.size());
       }
-      d->prow[p] = row;
-      if (row + static_cast<int>(iters) > kRowMax) return false;
-      for (size_t it = 0; it < iters; ++it, ++row)
+      t->prow[t->n_prow + ps] = t->rows[d];
+      if (t->rows[d] + static_cast<int>(iters) > kRowMax) return false;
+      for (size_t it = 0; it < iters; ++it, ++t->rows[d])
         for (int l = 0; l < 64; ++l) {
-          const int k = p * 64 + l;
-          const bool has = k < n && it < v[order[k]].size();
-          d->coef[row * 64 + l] = has ? v[order[k]][it].first : 0.0f;
-          d->idx[row * 64 + l] = static_cast<uint16_t>(has ? v[order[k]][it].second : 0);
+          const int k = ps * 64 + l;
+          const bool has = k < n && it < outs[order[k]].second.size();
+          t->coef[d][t->rows[d] * 64 + l] = has ? outs[order[k]].second[it].first : 0.0f;
+          t->idx[d][t->rows[d] * 64 + l] = static_cast<uint16_t>(has ? outs[order[k]].second[it].second : 0);
         }
     }
-    d->prow[d->n_pass] = row;
+    t->prow[t->n_prow + *npass] = t->rows[d];
+    t->n_prow += *npass + 1;
+    t->n_pos += 64 * *npass;
     return true;
   };
-  if (!deal(by_lab, &t->to_lab) || !deal(by_ent, &t->to_ent)) return "too many coupling terms for the table";
+  auto plain = [&](const std::vector<int> &ids, int *npass, int *pos0) {
+    *npass = (static_cast<int>(ids.size()) + 63) / 64;
+    *pos0 = t->n_pos;
+    if (t->n_pos + 64 * *npass > kPosMax) return false;
+    for (int k = 0; k < 64 * *npass; ++k)
+      t->pos[t->n_pos + k] = static_cast<int16_t>(k < static_cast<int>(ids.size()) ? ids[k] : -1);
+    t->n_pos += 64 * *npass;
+    return true;
+  };
+  for (int u = 0; u <= T; ++u)
+    for (int w = 0; w <= T; ++w) {
+      PairInfo &pi = t->pair[u * (T + 1) + w];
+      pi.P = norb[u] * norb[w];
+      pi.n_w = std::max(norb[w], 1);
+      pi.magic = (65536 + pi.n_w - 1) / pi.n_w;
+      // labels the pair carries, with their terms over own entries p
+      std::vector<std::pair<int, Terms>> labs;
+      std::vector<int> absent;
+      std::vector<std::vector<std::pair<float, int>>> by_ent(pi.P);
+      std::vector<int> present_q;
+      for (size_t it = 0; it < items.size(); ++it) {
+        const Item &im = items[it];
+        const int la = b->shell_l[im.a], lb = b->shell_l[im.b], nb = 2 * lb + 1, nm = 2 * im.L + 1;
+        const bool has = ((masks[u] >> im.a) & 1u) && ((masks[w] >> im.b) & 1u);
+        for (int M = 0; M < nm; ++M) {
+          const int q = hoff[im.L] + M * nL[im.L] + im.k;
+          if (!has) {
+            absent.push_back(q);
+            continue;
+          }
+          Terms tr;
+          for (int i = 0; i < 2 * la + 1; ++i)
+            for (int j = 0; j < nb; ++j) {
+              const double c = Q[it][(i * nb + j) * nm + M];
+              if (std::fabs(c) < 1e-12) continue;
+              const int pe = omap[u][off[im.a] + i] * norb[w] + omap[w][off[im.b] + j];
+              tr.push_back({static_cast<float>(c), pe});
+            }
+          labs.push_back({q, tr});
+          present_q.push_back(q);
+        }
+      }
+      std::sort(present_q.begin(), present_q.end());
+      // Label -> Matrix: entries from the compact inputs i (labels in ascending q)
+      for (size_t i = 0; i < present_q.size(); ++i)
+        for (const auto &lq : labs)
+          if (lq.first == present_q[i])
+            for (const auto &tm : lq.second) by_ent[tm.second].push_back({tm.first, static_cast<int>(i)});
+      std::vector<std::pair<int, Terms>> ents;
+      for (int pe = 0; pe < pi.P; ++pe) ents.push_back({pe, by_ent[pe]});
+      if (!deal(labs, 0, &pi.lpass, &pi.lprow, &pi.lpos) || !plain(absent, &pi.zpass, &pi.zpos) ||
+          !plain(present_q, &pi.spass, &pi.spos) || !deal(ents, 1, &pi.epass, &pi.eprow, &pi.epos))
+        return "the basis needs more coupling terms than the table holds";
+    }
   return nullptr;
 }
 
@@ -161,7 +234,7 @@ struct LKey {
   uint32_t mask[kSpeciesMax];
 };
 struct LInfo {
-  int n_full, n_lab, n_species, lab_rows, ent_rows, n_pass;
+  int n_full, n_lab, n_species, n_tmpl, n_prow, n_pos, rows[2];
 };
 struct LCache {
   std::mutex mu;
@@ -213,9 +286,11 @@ egnn_status label_slot(const egnn_basis *b, int *slot, LInfo *info) {
   in.n_full = t[0].n_full;
   in.n_lab = t[0].n_lab;
   in.n_species = t[0].n_species;
-  in.lab_rows = t[0].to_lab.prow[t[0].to_lab.n_pass];
-  in.ent_rows = t[0].to_ent.prow[t[0].to_ent.n_pass];
-  in.n_pass = t[0].to_lab.n_pass;
+  in.n_tmpl = t[0].n_tmpl;
+  in.n_prow = t[0].n_prow;
+  in.n_pos = t[0].n_pos;
+  in.rows[0] = t[0].rows[0];
+  in.rows[1] = t[0].rows[1];
   g_lcache.used[dev] = s + 1;
   *slot = s;
   *info = in;
@@ -223,7 +298,7 @@ egnn_status label_slot(const egnn_basis *b, int *slot, LInfo *info) {
 }
 
 constexpr int kLW = 64;
-constexpr int kLWaves = 4;
+constexpr int kLWaves = 16;
 
 __global__ void fill_i32(int *p, int64_t n, int v) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -312,16 +387,19 @@ struct Rows {
   const int64_t *mat_off;
   int64_t h_elems;
   int nodes, edges;  // 1 = on-site blocks / edge blocks requested
+  int vec4;          // label rows are whole 16-byte units at 16-byte aligned addresses
 };
 
 // Block bi of destination row j: the on-site block first (when requested),
-// then the row's edges.  ok = 0 when the block has no place in a matrix.
+// then the row's edges.  A block with no place in a matrix gets the empty
+// template pair (all labels zero, nothing written).
 struct Blk {
   int64_t base, out;
-  int ld, zi, zj, ok, node;
+  int ld, pair, node;
 };
 
-__device__ inline Blk block_of(const Rows &R, int n_species, const int *norb, int64_t j, int bi, int e0) {
+__device__ inline Blk block_of(const Rows &R, const LabelTable &tb, int64_t j, int bi, int e0, bool *ok_out) {
+  const int T = tb.n_tmpl;
   Blk k;
   int i;
   if (R.nodes && bi == 0) {
@@ -343,8 +421,10 @@ __device__ inline Blk block_of(const Rows &R, int n_species, const int *norb, in
   const int mj = R.atom_mol[j], mi = R.atom_mol[ic];
   ok = ok && mj >= 0 && mj < R.n_mols && mi == mj;
   const int si = R.species[ic], sj = R.species[j];
-  k.zi = (si >= 0 && si < n_species) ? si : n_species;
-  k.zj = (sj >= 0 && sj < n_species) ? sj : n_species;
+  const int ui = (si >= 0 && si < tb.n_species) ? tb.tmpl[si] : T;
+  const int uj = (sj >= 0 && sj < tb.n_species) ? tb.tmpl[sj] : T;
+  const int ni = (si >= 0 && si < tb.n_species) ? tb.n_orb[si] : 0;
+  const int nj = (sj >= 0 && sj < tb.n_species) ? tb.n_orb[sj] : 0;
   int ld = 0;
   int64_t mo = 0;
   if (ok) {  // only then is mj a structure (there may be none)
@@ -353,19 +433,21 @@ __device__ inline Blk block_of(const Rows &R, int n_species, const int *norb, in
   }
   const int oi = R.atom_orb[ic], oj = R.atom_orb[j];
   // (ld < 2^26 keeps the 32-bit entry offsets r * ld + c of the kernels exact)
-  ok = ok && ld >= 0 && ld < (1 << 26) && oi >= 0 && oj >= 0 && oi + norb[k.zi] <= ld && oj + norb[k.zj] <= ld && mo >= 0 &&
+  ok = ok && ld >= 0 && ld < (1 << 26) && oi >= 0 && oj >= 0 && oi + ni <= ld && oj + nj <= ld && mo >= 0 &&
        mo + static_cast<int64_t>(ld) * ld <= R.h_elems;
-  k.ok = ok;
+  *ok_out = ok;
   k.ld = ok ? ld : 0;
   k.base = ok ? mo + static_cast<int64_t>(oi) * ld + oj : 0;
+  k.pair = ok ? ui * (T + 1) + uj : T * (T + 1) + T;
   return k;
 }
 
-// LDS: one direction's passes (prow, pos, coef, idx), templates (omap,
-// n_orb), then per wave CB staged blocks.
-__host__ __device__ inline size_t lds_words(int n_pass, int rows, int n_species, int n_full) {
-  return (static_cast<size_t>(n_pass + 1) + 64 * static_cast<size_t>(n_pass) + 128 * static_cast<size_t>(rows) +
-          static_cast<size_t>(n_species + 1) * (n_full + 1) + 3) & ~static_cast<size_t>(3);
+// LDS words: pair table, pass rows, lane outputs (int16, two per word), one
+// direction's term rows (coef, then idx as int16 pairs), then per wave CB
+// staged blocks.
+__host__ __device__ inline size_t lds_words(int n_pairs, int n_prow, int n_pos, int rows) {
+  return (static_cast<size_t>(n_pairs) * kPairInts + n_prow + (n_pos + 1) / 2 + 64 * static_cast<size_t>(rows) +
+          32 * static_cast<size_t>(rows) + 3) & ~static_cast<size_t>(3);
 }
 
 template <int CB, int NT, bool TO_LABEL>
@@ -376,63 +458,41 @@ __global__ void __launch_bounds__(kLW * kLWaves) labels_kernel(int slot, Rows R,
                                                                 float *__restrict__ lab_e_out,
                                                                 float *__restrict__ lab_n_out,
                                                                 unsigned long long *skipped) {
-  static_assert(NT * CB <= 64, "one presence bit per staged value");
   extern __shared__ float lsm[];
   const LabelTable &tb = g_ltables[slot];
-  const int nf = tb.n_full, n_lab = tb.n_lab, nsp = tb.n_species;
-  const LDir &dir = TO_LABEL ? tb.to_lab : tb.to_ent;
-  const int n_pass = dir.n_pass, n_rows = dir.prow[n_pass];
-  int *s_prow = reinterpret_cast<int *>(lsm);                      // [n_pass + 1]
-  int *s_pos = s_prow + (n_pass + 1);                              // [n_pass][64]
-  float *s_coef = reinterpret_cast<float *>(s_pos + 64 * n_pass);  // [n_rows][64]
-  int *s_idx = reinterpret_cast<int *>(s_coef + 64 * n_rows);      // [n_rows][64]
-  int *omap = s_idx + 64 * n_rows;                                 // [nsp + 1][nf]
-  int *norb = omap + (nsp + 1) * nf;                               // [nsp + 1]
-  float *buf_all = lsm + lds_words(n_pass, n_rows, nsp, nf);       // [kLWaves][CB][n_lab]
-  for (int i = threadIdx.x; i <= n_pass; i += blockDim.x) s_prow[i] = dir.prow[i];
-  for (int i = threadIdx.x; i < 64 * n_pass; i += blockDim.x) s_pos[i] = dir.pos[i];
-  for (int i = threadIdx.x; i < 64 * n_rows; i += blockDim.x) {
-    s_coef[i] = dir.coef[i];
-    s_idx[i] = dir.idx[i];
+  const int n_lab = tb.n_lab, T = tb.n_tmpl;
+  const int n_pairs = (T + 1) * (T + 1), n_prow = tb.n_prow, n_pos = tb.n_pos;
+  constexpr int D = TO_LABEL ? 0 : 1;
+  const int rows = tb.rows[D];
+  int *s_pair = reinterpret_cast<int *>(lsm);                          // [n_pairs][kPairInts]
+  int *s_prow = s_pair + n_pairs * kPairInts;                          // [n_prow]
+  int16_t *s_pos = reinterpret_cast<int16_t *>(s_prow + n_prow);       // [n_pos]
+  float *s_coef = reinterpret_cast<float *>(s_prow + n_prow + (n_pos + 1) / 2);  // [rows][64]
+  uint16_t *s_idx = reinterpret_cast<uint16_t *>(s_coef + 64 * rows);  // [rows][64]
+  float *buf_all = lsm + lds_words(n_pairs, n_prow, n_pos, rows);      // [kLWaves][CB][n_lab]
+  {
+    const int *gp = reinterpret_cast<const int *>(tb.pair);
+    for (int i = threadIdx.x; i < n_pairs * kPairInts; i += blockDim.x) s_pair[i] = gp[i];
+    for (int i = threadIdx.x; i < n_prow; i += blockDim.x) s_prow[i] = tb.prow[i];
+    for (int i = threadIdx.x; i < n_pos; i += blockDim.x) s_pos[i] = tb.pos[i];
+    for (int i = threadIdx.x; i < 64 * rows; i += blockDim.x) {
+      s_coef[i] = tb.coef[D][i];
+      s_idx[i] = tb.idx[D][i];
+    }
   }
-  for (int i = threadIdx.x; i < (nsp + 1) * nf; i += blockDim.x) {
-    const int z = i / nf;
-    omap[i] = tb.omap[z == nsp ? kSpeciesMax : z][i - z * nf];
-  }
-  for (int i = threadIdx.x; i <= nsp; i += blockDim.x) norb[i] = i == nsp ? 0 : tb.n_orb[i];
   __syncthreads();
   const int lane = threadIdx.x % kLW, wave = threadIdx.x / kLW;
+  // staged inputs, then (once every pass has read them) the outputs, written out in order
   float *buf = buf_all + static_cast<size_t>(wave) * CB * n_lab;
-  // the entries (r, c) this lane stages, one per pass over the block
-  // (clamped to entry 0 past the block; `tin` bit it says the entry exists)
-  int rr[NT], cc[NT];
-  uint32_t tin = 0;
-#pragma unroll
-  for (int it = 0; it < NT; ++it) {
-    const int t = lane + kLW * it;
-    const bool in = t < n_lab;
-    rr[it] = in ? t / nf : 0;
-    cc[it] = in ? t - (t / nf) * nf : 0;
-    tin |= static_cast<uint32_t>(in) << it;
-  }
-  // Label -> Matrix: the entry (er, ec) each lane forms in each pass (-1: none)
-  int er[NT], ec[NT];
-#pragma unroll
-  for (int ps = 0; ps < NT; ++ps) {
-    const int t = ps < n_pass ? s_pos[ps * 64 + lane] : -1;
-    er[ps] = t >= 0 ? t / nf : -1;
-    ec[ps] = t >= 0 ? t - er[ps] * nf : 0;
-  }
-  (void)er;
-  (void)ec;
+  auto pinfo = [&](int pr) { return reinterpret_cast<const PairInfo *>(s_pair + pr * kPairInts); };
   // Rows are dealt to the XCDs in contiguous ranges (workgroup g runs on XCD
   // g % 8), so the rows of one structure, which read the same matrix lines,
-  // share one L2.  Each wave's chunks form one sequence (row j, first block
-  // c0); rows without blocks are passed over.  The blocks of a row are
-  // described 64 at a time (segment s0), one block per lane.
+  // share one L2.  Each wave walks its rows; rows without blocks are passed
+  // over.  The blocks of a row are described 64 at a time (segment s0), one
+  // block per lane.
   struct Pos {
     int64_t j;
-    int e0, nb, s0, c0;
+    int e0, nb, s0;
   };
   const bool by_xcd = gridDim.x % 8 == 0;
   const int64_t xcd = blockIdx.x % 8, groups = by_xcd ? gridDim.x / 8 : gridDim.x;
@@ -441,7 +501,7 @@ __global__ void __launch_bounds__(kLW * kLWaves) labels_kernel(int slot, Rows R,
   const int64_t j_begin = by_xcd ? R.n_atoms * xcd / 8 : 0;
   const int64_t stride = groups * kLWaves;
   auto row_at = [&](int64_t j) {
-    Pos p{j, 0, 0, 0, 0};
+    Pos p{j, 0, 0, 0};
     while (p.j < j_end) {
       p.e0 = R.edges ? R.row_ptr[p.j] : 0;
       p.nb = R.nodes + (R.edges ? R.row_ptr[p.j + 1] - p.e0 : 0);
@@ -450,22 +510,59 @@ __global__ void __launch_bounds__(kLW * kLWaves) labels_kernel(int slot, Rows R,
     }
     return p;
   };
-  auto next = [&](Pos p) {
-    p.c0 += CB;
-    if (p.c0 >= p.nb) return row_at(p.j + stride);
-    if (p.c0 >= p.s0 + kLW) p.s0 += kLW;
-    return p;
+  auto next_seg = [&](Pos p) {
+    p.s0 += kLW;
+    return p.s0 < p.nb ? p : row_at(p.j + stride);
   };
-  // lane l describes block s0 + l of the row (blocks past the row are empty
-  // slots pointing at row 0 of a kind of block that exists: the on-site rows
-  // whenever they are requested, else the first edge)
-  auto describe = [&](const Pos &p) {
-    Blk k{0, 0, 0, nsp, nsp, 0, R.nodes};
+  // lane l describes block s0 + l of the row (lanes past the row: empty)
+  auto describe = [&](const Pos &p, unsigned long long *have) {
+    Blk k{0, 0, 0, T * (T + 1) + T, R.nodes};
     const bool mine = p.j < j_end && p.s0 + lane < p.nb;
-    if (mine) k = block_of(R, nsp, norb, p.j, p.s0 + lane, p.e0);
-    const unsigned long long bad = __ballot(mine && !k.ok);
+    bool ok = false;
+    if (mine) k = block_of(R, tb, p.j, p.s0 + lane, p.e0, &ok);
+    const unsigned long long bad = __ballot(mine && !ok);
     if (lane == 0 && bad && skipped) atomicAdd(skipped, static_cast<unsigned long long>(__popcll(bad)));
+    *have = __ballot(mine);
     return k;
+  };
+  // A chunk: up to CB blocks of one template pair from one segment.
+  struct Chunk {
+    Blk k;             // the segment's descriptions (one block per lane)
+    int lanes[CB];     // lanes of the chunk's blocks (repeats past nc)
+    int nc, pair;
+  };
+  struct Cursor {
+    Pos p;
+    Blk k;
+    unsigned long long rem, cm;  // lanes not yet taken; lanes of the current pair not yet taken
+    int cp;
+  };
+  auto advance = [&](Cursor &c, Chunk &ch) {
+    while (c.cm == 0 && c.rem == 0) {
+      c.p = next_seg(c.p);
+      if (c.p.j >= j_end) return false;
+      c.k = describe(c.p, &c.rem);
+    }
+    if (c.cm == 0) {
+      const int lead = __ffsll(c.rem) - 1;
+      c.cp = __builtin_amdgcn_readlane(c.k.pair, lead);
+      c.cm = __ballot(c.k.pair == c.cp) & c.rem;
+      c.rem &= ~c.cm;
+    }
+    ch.k = c.k;
+    ch.pair = c.cp;
+    ch.nc = 0;
+#pragma unroll
+    for (int b = 0; b < CB; ++b) {
+      if (c.cm) {
+        ch.lanes[b] = __ffsll(c.cm) - 1;
+        c.cm &= c.cm - 1;
+        ++ch.nc;
+      } else {
+        ch.lanes[b] = ch.lanes[0];
+      }
+    }
+    return true;
   };
   auto rl = [](int v, int l) { return __builtin_amdgcn_readlane(v, l); };
   auto rl64 = [](int64_t v, int l) {
@@ -473,129 +570,183 @@ __global__ void __launch_bounds__(kLW * kLWaves) labels_kernel(int slot, Rows R,
            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
   };
   float v[NT][CB];
-  using Mask = typename std::conditional<(NT * CB <= 32), uint32_t, unsigned long long>::type;
-  Mask pres = 0;  // bit it * CB + b: value v[it][b] is a matrix entry (Matrix -> Label)
   // issue every load of a chunk before any of them is used; each block's
-  // base is a wave-uniform pointer and the entries 32-bit offsets from it
-  auto issue = [&](const Blk &k, const Pos &p) {
-    const int l0 = p.c0 - p.s0;
+  // base is a wave-uniform pointer and its values 32-bit offsets from it
+  auto issue = [&](const Chunk &ch) {
+    const PairInfo &pi = *pinfo(ch.pair);
+    const int P = pi.P;
     if constexpr (TO_LABEL) {
-      pres = 0;
+      // the pair's own entries p = lr * n_w + lc, one per lane and pass
+      int lrs[NT], lcs[NT];
+#pragma unroll
+      for (int it = 0; it < NT; ++it) {
+        const int pe = lane + kLW * it;
+        const int lr = (pe * pi.magic) >> 16;
+        lrs[it] = pe < P ? lr : -1;
+        lcs[it] = pe - lr * pi.n_w;
+      }
 #pragma unroll
       for (int b = 0; b < CB; ++b) {
-        const float *bp = Hin + rl64(k.base, l0 + b);
-        const int ld = rl(k.ld, l0 + b), oi = rl(k.zi, l0 + b) * nf, oj = rl(k.zj, l0 + b) * nf;
-        const bool ok = rl(k.ok, l0 + b) != 0;
+        const float *bp = Hin + rl64(ch.k.base, ch.lanes[b]);
+        const int ld = rl(ch.k.ld, ch.lanes[b]);
 #pragma unroll
         for (int it = 0; it < NT; ++it) {
-          const int lr = omap[oi + rr[it]], lc = omap[oj + cc[it]];
-          const bool pr = ok & ((tin >> it) & 1u) & (lr >= 0) & (lc >= 0);
-          // absent entries read the block's first element (element 0 of H for
-          // a block with no place) and are zeroed when staged
-          const uint32_t off = pr ? static_cast<uint32_t>(lr * ld + lc) : 0u;
+          // lanes past the pair's entries read the block's first entry (unused)
+          const uint32_t off = lrs[it] >= 0 ? static_cast<uint32_t>(lrs[it] * ld + lcs[it]) : 0u;
           v[it][b] = bp[off];
-          pres |= static_cast<Mask>(pr) << (it * CB + b);
         }
       }
     } else {
+      // the labels the pair carries, in ascending label order (compact inputs i)
+      int qs[NT];
+#pragma unroll
+      for (int it = 0; it < NT; ++it) {
+        const int i = lane + kLW * it;
+        qs[it] = i < P ? s_pos[pi.spos + i] : 0;
+      }
 #pragma unroll
       for (int b = 0; b < CB; ++b) {
-        const float *row = (rl(k.node, l0 + b) ? lab_n_in : lab_e_in) + rl64(k.out, l0 + b) * n_lab;
+        const float *row = (rl(ch.k.node, ch.lanes[b]) ? lab_n_in : lab_e_in) + rl64(ch.k.out, ch.lanes[b]) * n_lab;
 #pragma unroll
-        for (int it = 0; it < NT; ++it) v[it][b] = row[static_cast<uint32_t>(min(lane + kLW * it, n_lab - 1))];
+        for (int it = 0; it < NT; ++it) v[it][b] = row[static_cast<uint32_t>(qs[it])];
       }
     }
   };
-  auto commit = [&]() {
+  auto commit = [&](const Chunk &ch) {
+    const int P = pinfo(ch.pair)->P;
 #pragma unroll
     for (int it = 0; it < NT; ++it) {
       const int t = lane + kLW * it;
-      if (t < n_lab) {
+      if (t < P) {
 #pragma unroll
-        for (int b = 0; b < CB; ++b) {
-          float x = v[it][b];
-          if constexpr (TO_LABEL) x = ((pres >> (it * CB + b)) & 1u) ? x : 0.0f;
-          buf[b * n_lab + t] = x;
-        }
+        for (int b = 0; b < CB; ++b) buf[b * n_lab + t] = v[it][b];
       }
     }
   };
-  Pos p = row_at(j_begin + local * kLWaves + wave);
-  Blk k = describe(p);
-  if (p.j < j_end) issue(k, p);
-  while (p.j < j_end) {
-    const int nc = min(CB, p.nb - p.c0);
-    const int l0 = p.c0 - p.s0;
-    commit();
-    wave_lds_order();
-    // the next chunk's loads run while this chunk's outputs are formed
-    const Pos pn = next(p);
-    const Blk kn = (pn.j != p.j || pn.s0 != p.s0) ? describe(pn) : k;
-    if (pn.j < j_end) issue(kn, pn);
+  auto outputs = [&](const Chunk &ch) {
+    const PairInfo &pi = *pinfo(ch.pair);
+    const int nc = ch.nc;
     if constexpr (TO_LABEL) {
-      // Eq. (1): the labels of each block from their CG terms over the staged
-      // entries, one pass of 64 labels at a time
       float *op[CB];
 #pragma unroll
       for (int b = 0; b < CB; ++b)
-        op[b] = (rl(k.node, l0 + b) ? lab_n_out : lab_e_out) + rl64(k.out, l0 + b) * n_lab;
-      for (int ps = 0; ps < n_pass; ++ps) {
-        float acc[CB];
-#pragma unroll
-        for (int b = 0; b < CB; ++b) acc[b] = 0.0f;
-        const int r1 = s_prow[ps + 1];
-        for (int rw = s_prow[ps]; rw < r1; ++rw) {
-          const float cf = s_coef[rw * 64 + lane];
-          const int ix = s_idx[rw * 64 + lane];
-#pragma unroll
-          for (int b = 0; b < CB; ++b) acc[b] += cf * buf[b * n_lab + ix];
-        }
-        const int q = s_pos[ps * 64 + lane];
-        if (q >= 0) {
-#pragma unroll
-          for (int b = 0; b < CB; ++b)
-            if (b < nc) op[b][static_cast<uint32_t>(q)] = acc[b];
-        }
-      }
-    } else {
-      // entries from their CG terms over the staged labels, written where the
-      // template has an orbital
-      float *bp[CB];
-      int ldb[CB], oib[CB], ojb[CB];
-      bool okb[CB];
-#pragma unroll
-      for (int b = 0; b < CB; ++b) {
-        bp[b] = Hout + rl64(k.base, l0 + b);
-        ldb[b] = rl(k.ld, l0 + b);
-        oib[b] = rl(k.zi, l0 + b) * nf;
-        ojb[b] = rl(k.zj, l0 + b) * nf;
-        okb[b] = b < nc && rl(k.ok, l0 + b) != 0;
-      }
+        op[b] = (rl(ch.k.node, ch.lanes[b]) ? lab_n_out : lab_e_out) + rl64(ch.k.out, ch.lanes[b]) * n_lab;
+      // Eq. (1): the labels the pair carries, from their CG terms over the
+      // staged entries (at most NT passes)
+      float acc[NT][CB];
 #pragma unroll
       for (int ps = 0; ps < NT; ++ps) {
-        if (ps >= n_pass) break;
-        float acc[CB];
 #pragma unroll
-        for (int b = 0; b < CB; ++b) acc[b] = 0.0f;
-        const int r1 = s_prow[ps + 1];
-        for (int rw = s_prow[ps]; rw < r1; ++rw) {
-          const float cf = s_coef[rw * 64 + lane];
-          const int ix = s_idx[rw * 64 + lane];
+        for (int b = 0; b < CB; ++b) acc[ps][b] = 0.0f;
+        if (ps < pi.lpass) {
+          const int r1 = s_prow[pi.lprow + ps + 1];
+          for (int rw = s_prow[pi.lprow + ps]; rw < r1; ++rw) {
+            const float cf = s_coef[rw * 64 + lane];
+            const int ix = s_idx[rw * 64 + lane];
 #pragma unroll
-          for (int b = 0; b < CB; ++b) acc[b] += cf * buf[b * n_lab + ix];
-        }
-        if (er[ps] >= 0) {
-#pragma unroll
-          for (int b = 0; b < CB; ++b) {
-            const int lr = omap[oib[b] + er[ps]], lc = omap[ojb[b] + ec[ps]];
-            if (okb[b] && lr >= 0 && lc >= 0) bp[b][static_cast<uint32_t>(lr * ldb[b] + lc)] = acc[b];
+            for (int b = 0; b < CB; ++b) acc[ps][b] += cf * buf[b * n_lab + ix];
           }
         }
       }
+      wave_lds_order();
+      // the output rows take the place of the staged entries
+#pragma unroll
+      for (int ps = 0; ps < NT; ++ps)
+        if (ps < pi.lpass) {
+          const int q = s_pos[pi.lpos + ps * 64 + lane];
+          if (q >= 0) {
+#pragma unroll
+            for (int b = 0; b < CB; ++b) buf[b * n_lab + q] = acc[ps][b];
+          }
+        }
+      // the labels of shell pairs the elements lack: the padding
+      for (int ps = 0; ps < pi.zpass; ++ps) {
+        const int q = s_pos[pi.zpos + ps * 64 + lane];
+        if (q >= 0) {
+#pragma unroll
+          for (int b = 0; b < CB; ++b) buf[b * n_lab + q] = 0.0f;
+        }
+      }
+      wave_lds_order();
+      // whole rows out, 16 bytes per lane where the rows allow it
+      if (R.vec4) {
+        const int n4 = n_lab / 4;
+#pragma unroll
+        for (int b = 0; b < CB; ++b)
+          if (b < nc)
+            for (int c4 = lane; c4 < n4; c4 += kLW)
+              reinterpret_cast<float4 *>(op[b])[c4] = reinterpret_cast<const float4 *>(buf + b * n_lab)[c4];
+      } else {
+#pragma unroll
+        for (int b = 0; b < CB; ++b)
+          if (b < nc)
+            for (int q = lane; q < n_lab; q += kLW) op[b][q] = buf[b * n_lab + q];
+      }
+    } else {
+      float *bp[CB];
+      int ldb[CB];
+#pragma unroll
+      for (int b = 0; b < CB; ++b) {
+        bp[b] = Hout + rl64(ch.k.base, ch.lanes[b]);
+        ldb[b] = rl(ch.k.ld, ch.lanes[b]);
+      }
+      // the pair's own entries from their CG terms over the staged labels
+      // (at most NT passes), then in place of the staged labels
+      float acc[NT][CB];
+#pragma unroll
+      for (int ps = 0; ps < NT; ++ps) {
+#pragma unroll
+        for (int b = 0; b < CB; ++b) acc[ps][b] = 0.0f;
+        if (ps < pi.epass) {
+          const int r1 = s_prow[pi.eprow + ps + 1];
+          for (int rw = s_prow[pi.eprow + ps]; rw < r1; ++rw) {
+            const float cf = s_coef[rw * 64 + lane];
+            const int ix = s_idx[rw * 64 + lane];
+#pragma unroll
+            for (int b = 0; b < CB; ++b) acc[ps][b] += cf * buf[b * n_lab + ix];
+          }
+        }
+      }
+      wave_lds_order();
+#pragma unroll
+      for (int ps = 0; ps < NT; ++ps)
+        if (ps < pi.epass) {
+          const int pe = s_pos[pi.epos + ps * 64 + lane];
+          if (pe >= 0) {
+#pragma unroll
+            for (int b = 0; b < CB; ++b) buf[b * n_lab + pe] = acc[ps][b];
+          }
+        }
+      wave_lds_order();
+      // then out in row-major order: consecutive lanes write consecutive
+      // columns of a block row
+      const int P = pi.P;
+      for (int pe = lane; pe < P; pe += kLW) {
+        const int lr = (pe * pi.magic) >> 16, lc = pe - lr * pi.n_w;
+#pragma unroll
+        for (int b = 0; b < CB; ++b)
+          if (b < nc) bp[b][static_cast<uint32_t>(lr * ldb[b] + lc)] = buf[b * n_lab + pe];
+      }
     }
+  };
+  Cursor c;
+  c.p = row_at(j_begin + local * kLWaves + wave);
+  c.k = describe(c.p, &c.rem);
+  c.cm = 0;
+  c.cp = 0;
+  Chunk cur, nxt;
+  bool have = advance(c, cur);
+  if (have) issue(cur);
+  while (have) {
+    commit(cur);
     wave_lds_order();
-    p = pn;
-    k = kn;
+    // the next chunk's loads run while this chunk's outputs are formed
+    const bool have_n = advance(c, nxt);
+    if (have_n) issue(nxt);
+    outputs(cur);
+    wave_lds_order();
+    cur = nxt;
+    have = have_n;
   }
 }
 
@@ -650,23 +801,26 @@ egnn_status run_labels(bool to_label, const egnn_basis *b, const egnn_orbitals *
   R.h_elems = h_elems;
   R.nodes = nodes ? 1 : 0;
   R.edges = edges ? 1 : 0;
-  const int n_rows = to_label ? info.lab_rows : info.ent_rows;
+  {
+    auto a16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    R.vec4 = info.n_lab % 4 == 0 && (!le_out || a16(le_out)) && (!ln_out || a16(ln_out)) ? 1 : 0;
+  }
+  const int n_rows = info.rows[to_label ? 0 : 1];
   const int64_t rows = (edges ? g->n_edges : 0) + (nodes ? o->n_atoms : 0);
-  // algorithmic bytes: every label row once, and every matrix entry once
-  // when the graph covers each block (a fully connected structure)
+  // algorithmic bytes when the graph covers every block once (a fully
+  // connected structure): Matrix -> Label reads each matrix entry and writes
+  // every label row; Label -> Matrix reads the labels the blocks carry (as
+  // many as the matrix has entries) and writes each entry
   Timed tm(stream, to_label ? "matrix_to_label" : "label_to_matrix", 0.0,
-           4.0 * (double(rows) * info.n_lab + double(h_elems)));
+           to_label ? 4.0 * (double(rows) * info.n_lab + double(h_elems)) : 8.0 * double(h_elems));
   // a multiple of 8 workgroups: rows are dealt to the XCDs in contiguous ranges
   int64_t blocks = ((static_cast<int64_t>(o->n_atoms) + kLWaves - 1) / kLWaves + 7) / 8 * 8;
   if (blocks > 2048) blocks = 2048;
-  const size_t base_words = lds_words(info.n_pass, n_rows, info.n_species, info.n_full);
+  const size_t base_words = lds_words((info.n_tmpl + 1) * (info.n_tmpl + 1), info.n_prow, info.n_pos, n_rows);
+  auto smem_for = [&](int cb) { return 4 * (base_words + static_cast<size_t>(kLWaves) * cb * info.n_lab); };
   auto launch = [&](auto cb, auto nt) -> egnn_status {
     constexpr int CB = decltype(cb)::value, NT = decltype(nt)::value;
-    const size_t smem = 4 * (base_words + static_cast<size_t>(kLWaves) * CB * info.n_lab);
-    if (smem > 160 * 1024) {
-      set_error("Matrix <-> Label needs %zu bytes of LDS; reduce the basis", smem);
-      return EGNN_E_UNSUPPORTED;
-    }
+    const size_t smem = smem_for(CB);
     if (to_label)
       labels_kernel<CB, NT, true><<<static_cast<unsigned>(blocks), kLW * kLWaves, smem, stream>>>(
           slot, R, Hin, nullptr, nullptr, nullptr, le_out, ln_out, skip);
@@ -676,16 +830,32 @@ egnn_status run_labels(bool to_label, const egnn_basis *b, const egnn_orbitals *
     EGNN_CHECK_LAUNCH();
     return EGNN_OK;
   };
-  // NT passes of 64 entries cover a block; CB blocks per chunk keep NT * CB
-  // values in flight per lane
+  // NT passes of 64 cover a block; CB blocks per chunk keep NT * CB values in
+  // flight per lane.  CB is the largest whose staging fits in LDS, capped so
+  // that the next chunk's values and this chunk's outputs fit in registers
+  // (128 per lane at 16 waves): 4 up to 2 passes, 2 up to 12, 1 beyond.
+  constexpr size_t kLds = 160 * 1024;
   const int passes = (info.n_lab + kLW - 1) / kLW;
-  if (passes <= 1) return launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 1>{});
-  if (passes <= 2) return launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 2>{});
-  if (passes <= 4) return launch(std::integral_constant<int, 8>{}, std::integral_constant<int, 4>{});
-  if (passes <= 6) return launch(std::integral_constant<int, 4>{}, std::integral_constant<int, 6>{});
-  if (passes <= 8) return launch(std::integral_constant<int, 4>{}, std::integral_constant<int, 8>{});
-  if (passes <= 12) return launch(std::integral_constant<int, 2>{}, std::integral_constant<int, 12>{});
-  return launch(std::integral_constant<int, 2>{}, std::integral_constant<int, 16>{});
+  int cb = passes <= 2 ? 4 : passes <= 12 ? 2 : 1;
+  while (cb > 1 && smem_for(cb) > kLds) cb /= 2;
+  if (smem_for(cb) > kLds) {
+    set_error("Matrix <-> Label needs %zu bytes of LDS; reduce the basis", smem_for(cb));
+    return EGNN_E_UNSUPPORTED;
+  }
+  using std::integral_constant;
+  auto with_cb = [&](auto nt) -> egnn_status {
+    constexpr int NT = decltype(nt)::value;
+    if (cb == 4 && NT <= 2) return launch(integral_constant<int, (NT <= 2 ? 4 : 1)>{}, nt);
+    if (cb >= 2 && NT <= 12) return launch(integral_constant<int, (NT <= 12 ? 2 : 1)>{}, nt);
+    return launch(integral_constant<int, 1>{}, nt);
+  };
+  if (passes <= 1) return with_cb(integral_constant<int, 1>{});
+  if (passes <= 2) return with_cb(integral_constant<int, 2>{});
+  if (passes <= 4) return with_cb(integral_constant<int, 4>{});
+  if (passes <= 6) return with_cb(integral_constant<int, 6>{});
+  if (passes <= 8) return with_cb(integral_constant<int, 8>{});
+  if (passes <= 12) return with_cb(integral_constant<int, 12>{});
+  return with_cb(integral_constant<int, 16>{});
 }
 
 }  // namespace
