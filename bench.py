@@ -324,7 +324,8 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_mib, argv):
     copy_bytes = copy_mib * 2 ** 20
 
     def pick(tab, tag):
-        return [v for name, v in tab.values() if tag in name]
+        pieces = (tag,) if isinstance(tag, str) else tag
+        return [v for name, v in tab.values() if all(t in name for t in pieces)]
 
     cf, cw = pick(fetch, COPY_KERNEL_TAG), pick(write, COPY_KERNEL_TAG)
     if not cf or not cw:
@@ -350,7 +351,8 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_mib, argv):
         if not kf or len(kf) != len(kw):
             continue
         f_kib, w_kib = float(np.mean(kf)), float(np.mean(kw))
-        lines.append(f"# {fam}: {len(kf)} dispatches of {tag}; per dispatch FETCH_SIZE {f_kib:.0f} KiB, "
+        lines.append(f"# {fam}: {len(kf)} dispatches of {tag if isinstance(tag, str) else ' ... '.join(tag)}; "
+                     f"per dispatch FETCH_SIZE {f_kib:.0f} KiB, "
                      f"WRITE_SIZE {w_kib:.0f} KiB")
         lines.append(f"traffic_bytes_per_launch[{fam}]: {(f_kib * sf + w_kib * sw) * 1024:.0f}")
     os.makedirs(os.path.dirname(traffic_path(workload)), exist_ok=True)
@@ -359,7 +361,7 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_mib, argv):
     print("\n".join(lines))
 
 
-# timing family -> substring of its kernel's symbol name
+# timing family -> piece (or pieces, all present) of its kernel's symbol name
 FAMILY_KERNELS = {
     # kernel-name pieces ("::" keeps gemm from matching cgemm; the GEMM templates carry
     # tile widths after these arguments)
@@ -374,8 +376,8 @@ FAMILY_KERNELS = {
     "rotate_in": "::scatter_in_",
     "aggregate": "::aggregate_",
     "hblocks": "hblocks_kernel",
-    "matrix_to_label": "labels_kernel<8, true>",
-    "label_to_matrix": "labels_kernel<8, false>",
+    "matrix_to_label": ("::labels_kernel<", ", true>"),   # every (chunk, pass) instantiation
+    "label_to_matrix": ("::labels_kernel<", ", false>"),
 }
 
 

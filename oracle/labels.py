@@ -14,17 +14,17 @@ buffers, then transform (Matrix -> Label); transform back, then place
 (Label -> Matrix).
 
 Readings (the pages leave these open):
-  R-B1 basis: one full shell list (the largest element's basis, or the union
+  R26 basis: one full shell list (the largest element's basis, or the union
        of the per-degree maxima); each element carries a subset of its
        shells, given as a bit mask.  An atom's orbitals are its shells in
        full-list order, each as m = -l..l.
-  R-B2 padding: a label vector always has the layout of the full list (the
+  R27 padding: a label vector always has the layout of the full list (the
        channel k(a, b, L) of decode.label_layout, flattened in (L, M, k)
        order), and labels of shell pairs absent from (Z_i, Z_j) are zero.
-  R-B3 matrices of a batch are stored back to back, each row-major
+  R28 matrices of a batch are stored back to back, each row-major
        N_orb x N_orb; atoms of a structure are contiguous and in order, so
        an atom's first orbital is the sum of the orbital counts before it.
-  R-B4 which blocks: the on-site block of every atom and the block of every
+  R29 which blocks: the on-site block of every atom and the block of every
        edge of the graph (rows = source atom's orbitals, columns =
        destination's, as in decode).  Edges with a nonzero periodic image
        shift, or whose ends lie in different structures, have no block in a
@@ -62,7 +62,7 @@ def species_rows(species, species_shells):
 
 
 def orbital_layout(mol_ptr, species, shell_l, species_shells):
-    """(atom_orb, atom_mol, mol_norb, mat_off) of R-B3."""
+    """(atom_orb, atom_mol, mol_norb, mat_off) of R28."""
     _, n_orb = species_templates(shell_l, species_shells)
     mol_ptr = np.asarray(mol_ptr, np.int64)
     species = species_rows(species, species_shells)
