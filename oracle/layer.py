@@ -336,6 +336,20 @@ def layer_backward(graph, x, w, d: LayerDesc, fwd, G):
     y00 = Y[:, 0, :]
     dY[:, 0, :] += da[:, None] * W["w_att"][None, :] * dsilu(y00)
     dw_att = silu(y00).T @ da
+    dx, dW = _backward_from_dY(graph, x, W, d, fwd, dY)
+    dW["w_att"] = dw_att
+    dx[:n_dst] += G
+    return dx, pack_weights(dW, d)
+
+
+def _backward_from_dY(graph, x, W, d: LayerDesc, fwd, dY):
+    """The steps shared by the node and edge blocks, from the edge-frame output
+    gradient dY: (dX, dW) = SO(2) backward, dXt = g * dX, dg = sum_{+-m} dX * Xt,
+    dx_src += D_e^T dXt[:, :C], dx_dst += D_e^T dXt[:, C:].  Returns dx and the
+    weight gradients (w_att zero)."""
+    C = d.C
+    n_dst = len(graph["row_ptr"]) - 1
+    D = fwd["D"]
     dX, dW = so2_conv_bwd(fwd["X"], dY, W, d)
     dXt = fwd["g"] * dX
     dgfull = dX * fwd["Xt"]                                     # [E][K][2C]
@@ -345,10 +359,38 @@ def layer_backward(graph, x, w, d: LayerDesc, fwd, G):
         if m > 0:
             dgp[:, p, :] += dgfull[:, so3.coeff_index(l, -m), :]
     dW["W_rad"] = np.einsum("ek,epc->kpc", fwd["phi"], dgp)
-    dW["w_att"] = dw_att
+    dW["w_att"] = np.zeros_like(W["w_att"])
     back = rotate_out(D, dXt, d)                                # [E][K][2C]
     dx = np.zeros_like(x)
     np.add.at(dx, graph["src"], back[:, :, :C])
     dx[:n_dst] += segment_sum(back[:, :, C:], graph["row_ptr"])
-    dx[:n_dst] += G
-    return dx, pack_weights(dW, d)
+    return dx, dW
+
+
+def edge_update_forward(graph, x, e, w, d: LayerDesc, roll=None):
+    """Edge-update block (MALOQ Sec. III-D: after the eSCN convolution the
+    messages n_i (+) n_j either aggregate onto node j or update the edge
+    embedding e_ij; Sec. III / Fig. 3(b) rotate edge embeddings like node
+    embeddings).
+
+    Reading R30: e'_e = e_e + D_e^T Yhat_e, with Yhat_e the SO(2) convolution
+    of the gated edge-frame message of the node block (same weights, no
+    attention).  e: [E][K][C].  Returns the forward dict with e_out.
+    """
+    W = unpack_weights(w, d)
+    x = np.asarray(x, np.float64)
+    dst = dst_of_edges(graph["row_ptr"])
+    ef = edge_forward(graph, x, W, d, x[dst], roll)
+    ef["e_out"] = np.asarray(e, np.float64) + ef["msg"]
+    return ef
+
+
+def edge_update_backward(graph, x, w, d: LayerDesc, fwd, Ge):
+    """Gradients of <Ge, e'> with respect to x [n_src][K][C], e and the packed
+    weights: de = Ge; dY = D_e Ge (truncated); the rest as the node block."""
+    W = unpack_weights(w, d)
+    x = np.asarray(x, np.float64)
+    Ge = np.asarray(Ge, np.float64)
+    dY = rotate_in(fwd["D"], Ge, d) * trunc_mask(d)[None, :, None]
+    dx, dW = _backward_from_dY(graph, x, W, d, fwd, dY)
+    return dx, Ge.copy(), pack_weights(dW, d)

@@ -29,7 +29,7 @@ __all__ = ["Config", "CONFIGS", "Structure", "make_structure", "make_layer_input
            "make_decode_weights", "make_cotangent", "layer_weight_sizes",
            "round_storage", "bf16_round", "SVP_SHELLS", "SVP_ELEMENTS", "SVP_MASKS",
            "SVP_FRACTIONS", "WATER_SHELLS", "WATER_MASKS", "MoleculeBatch", "make_molecule_batch",
-           "make_matrix_values", "make_label_values"]
+           "make_matrix_values", "make_label_values", "make_edge_embeddings", "make_edge_cotangent"]
 
 
 @dataclass(frozen=True)
@@ -434,3 +434,20 @@ def make_label_values(seed, n_rows, n_lab):
     """N(0, 1) float32 labels [n_rows][n_lab] (stream (seed, 12))."""
     rng = np.random.default_rng((seed, 12))
     return rng.standard_normal((int(n_rows), int(n_lab)), dtype=np.float32)
+
+
+def make_edge_embeddings(cfg: Config | str, n_edges):
+    """Seeded edge embeddings e [E][K][C] for the edge-update block (stream (seed, 5)),
+    N(0, 1), held as the storage type holds them."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    rng = np.random.default_rng((cfg.seed, 5))
+    return round_storage(rng.standard_normal((int(n_edges), cfg.K, cfg.C)), cfg.storage)
+
+
+def make_edge_cotangent(cfg: Config | str, n_edges):
+    """Seeded cotangent Ge = dL/de' [E][K][C] of the edge-update block (stream (seed, 6))."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    rng = np.random.default_rng((cfg.seed, 6))
+    return round_storage(rng.standard_normal((int(n_edges), cfg.K, cfg.C)), "f32")
