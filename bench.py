@@ -42,6 +42,8 @@ WORKLOADS = {
                 desc="GeSbTe-like 3-layer forward, bf16 storage"),
     "gst_train": dict(cfg="gst", backward=True, decode=True, layers=1,
                       desc="GeSbTe-like training step, bf16 storage: graph + geometry + 1 layer fwd/bwd + 13x13 blocks"),
+    "edge_train": dict(cfg="train", backward=True, decode=False, layers=1, edge=True,
+                       desc="HfO2-like edge-update block: graph + geometry + edge update fwd/bwd"),
     "m2l": dict(labels="m2l", mols=4096, seed=40,
                 desc="Matrix -> Label over 4,096 nabla2DFT-like molecules (10-50 atoms of H C N O F S Cl, "
                      "def2-SVP-like shells, fully connected): orbital layout + labels of every atom and edge"),
@@ -113,6 +115,10 @@ class Step:
             self.G = torch.from_numpy(synth.make_cotangent(cfg, s.n_dst)).to(dev)
             self.gx = torch.empty((s.n_src, K, cfg.C), dtype=torch.float32, device=dev)
             self.gw = torch.empty(eg.egnn_layer_weight_count(self.desc), dtype=torch.float32, device=dev)
+        if wl.get("edge"):
+            self.e = torch.from_numpy(synth.make_edge_embeddings(cfg, self.E)).to(dev).to(dt)
+            self.e_out = torch.empty_like(self.e)
+            self.Ge = torch.from_numpy(synth.make_edge_cotangent(cfg, self.E)).to(dev)
         if wl["decode"]:
             we, wn = synth.make_decode_weights(cfg)
             self.we = torch.from_numpy(np.concatenate(we)).to(dev)
@@ -123,6 +129,12 @@ class Step:
         s = self.struct
         g = self.builder.build(self.pos)
         eg.egnn_edge_geom(self.desc, g, out=self.geom)
+        if self.wl.get("edge"):
+            eg.egnn_edge_update_fwd(self.desc, g, self.geom, self.w[0], self.xs[0], self.e, e_out=self.e_out,
+                                    buffers=self.buf)
+            eg.egnn_edge_update_bwd(self.desc, g, self.geom, self.w[0], self.xs[0], self.buf, self.Ge,
+                                    grad_x=self.gx, grad_w=self.gw)
+            return g
         for i in range(self.wl["layers"]):
             last = i == self.wl["layers"] - 1
             eo = self.edge_out if (last and self.wl["decode"]) else None
@@ -418,6 +430,14 @@ def cpu_baseline(wl, rows_n):
     d = layer.LayerDesc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut)
     t0 = time.perf_counter()
     g = neighbors.build_graph(pos, len(rows), s.box, s.periodic_mask, s.r_cut)
+    if wl.get("edge"):
+        e = synth.make_edge_embeddings(cfg, len(g["src"])).astype(np.float64)
+        f = layer.edge_update_forward(g, xp, e, ws[0].astype(np.float64), d)
+        layer.edge_update_backward(g, xp, ws[0].astype(np.float64), d, f, np.ones_like(e))
+        dt = time.perf_counter() - t0
+        E = len(g["src"])
+        return dict(value=round(E / dt, 2), unit="edges/s", cores=len(os.sched_getaffinity(0)), kind="oracle",
+                    sample=f"{len(rows)} destination rows ({E} edges) of the same structure, fp64 numpy, {dt:.1f} s")
     xl = xp
     for i in range(wl["layers"]):
         f = layer.layer_forward(g, xl, ws[i].astype(np.float64), d)

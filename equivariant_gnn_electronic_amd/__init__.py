@@ -21,7 +21,7 @@ __all__ = ["Graph", "layer_desc", "egnn_build_graph", "egnn_edge_geom", "egnn_ge
            "egnn_hblocks", "egnn_hblocks_label_rows", "egnn_timing_enable", "egnn_timing_collect",
            "egnn_timing_reset", "GraphBuilder", "LayerBuffers", "EgnnError", "EGNN_F32", "EGNN_BF16",
            "Basis", "Orbitals", "egnn_label_width", "egnn_orbital_layout", "egnn_matrix_to_label",
-           "egnn_label_to_matrix"]
+           "egnn_label_to_matrix", "egnn_edge_update_fwd", "egnn_edge_update_bwd"]
 
 _STORAGE = {EGNN_F32: torch.float32, EGNN_BF16: torch.bfloat16}
 
@@ -252,6 +252,35 @@ def egnn_layer_bwd(desc, graph: Graph, geom, weights, x, buffers, grad_out, grad
     g = graph.c_struct()
     _lib.check("egnn_layer_bwd", lib.egnn_layer_bwd(
         ct.byref(desc), ct.byref(g), _ptr(geom), _ptr(weights), _ptr(x), _ptr(buffers.saved), _ptr(grad_out),
+        _ptr(grad_x), _ptr(grad_w), _ptr(buffers.ws), buffers.ws.numel(), _stream()))
+    return grad_x, grad_w
+
+
+def egnn_edge_update_fwd(desc, graph: Graph, geom, weights, x, e_in, e_out=None, buffers=None):
+    """Edge-update block: e_out = e_in + the per-edge message (in place when e_out is e_in).
+    Returns (e_out, buffers); buffers keep the activations the backward reads."""
+    lib = _lib.load()
+    if buffers is None:
+        buffers = LayerBuffers(desc, graph, train=True)
+    if e_out is None:
+        e_out = torch.empty_like(e_in)
+    g = graph.c_struct()
+    _lib.check("egnn_edge_update_fwd", lib.egnn_edge_update_fwd(
+        ct.byref(desc), ct.byref(g), _ptr(geom), _ptr(weights), _ptr(x), _ptr(e_in), _ptr(e_out),
+        _ptr(buffers.saved) if buffers.saved is not None else None, _ptr(buffers.ws), buffers.ws.numel(), _stream()))
+    return e_out, buffers
+
+
+def egnn_edge_update_bwd(desc, graph: Graph, geom, weights, x, buffers, grad_e_out, grad_x=None, grad_w=None):
+    """Gradients of <grad_e_out, e_out> w.r.t. x and the packed weights (that w.r.t. e_in is grad_e_out)."""
+    lib = _lib.load()
+    if grad_x is None:
+        grad_x = torch.empty((graph.n_src,) + tuple(x.shape[1:]), dtype=torch.float32, device=x.device)
+    if grad_w is None:
+        grad_w = torch.empty(egnn_layer_weight_count(desc), dtype=torch.float32, device=x.device)
+    g = graph.c_struct()
+    _lib.check("egnn_edge_update_bwd", lib.egnn_edge_update_bwd(
+        ct.byref(desc), ct.byref(g), _ptr(geom), _ptr(weights), _ptr(x), _ptr(buffers.saved), _ptr(grad_e_out),
         _ptr(grad_x), _ptr(grad_w), _ptr(buffers.ws), buffers.ws.numel(), _stream()))
     return grad_x, grad_w
 

@@ -64,6 +64,8 @@ SIGNATURES = {
     "egnn_layer_sizes": (ct.c_int, [_L, _G, _PSZ, _PSZ, _PSZ]),
     "egnn_layer_fwd": (ct.c_int, [_L, _G, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "egnn_layer_bwd": (ct.c_int, [_L, _G, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "egnn_edge_update_fwd": (ct.c_int, [_L, _G, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "egnn_edge_update_bwd": (ct.c_int, [_L, _G, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "egnn_hblocks_label_rows": (ct.c_int32, [_H]),
     "egnn_hblocks": (ct.c_int, [_H, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "egnn_label_width": (ct.c_int32, [_B]),

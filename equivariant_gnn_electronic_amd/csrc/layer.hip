@@ -917,6 +917,93 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
   }
 }
 
+// ------------------------------------------------------- edge-update block --
+// e_out[e] = e_in[e] + D_e^T Yhat_e: the node block's per-edge message added to
+// the edge embedding instead of being aggregated.  One wave per edge (grid
+// stride), lanes over channels; the edge's Wigner rows are staged in LDS and
+// read as broadcasts.  e_out may be e_in: a lane reads its entries of the edge
+// before it writes them.
+template <int LMAX, int MMAX, int CPL, typename T>
+__global__ void __launch_bounds__(kThreads) edge_update_kernel(int64_t E, const float *__restrict__ geom, int gstride,
+                                                               CPtr3 Y, int C, const T *e_in, T *e_out) {
+  using L = Lay<LMAX, MMAX>;
+  __shared__ float dsm[kWavesPerBlock][L::ND];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave; e < E;
+       e += static_cast<int64_t>(gridDim.x) * kWavesPerBlock) {
+    const float *gr = geom + e * gstride;
+    for (int i = lane; i < L::ND; i += kWave) dsm[wave][i] = gr[i];
+    wave_lds_order();
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      const int c = lane + kWave * t;
+      if (c < C) {
+        float y[L::KEPT], ev[L::K];
+#pragma unroll
+        for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+            const int mu = cabs(m);
+            const T *row = static_cast<const T *>(Y.p[mu]) + e * L::blocks(mu) * C;
+            y[L::kidx(l, m)] = Store<T>::ld(row + L::col(l, m) * C + c);
+          }
+        const T *ei = e_in + e * L::K * C + c;
+#pragma unroll
+        for (int k = 0; k < L::K; ++k) ev[k] = Store<T>::ld(ei + k * C);
+        T *eo = e_out + e * L::K * C + c;
+#pragma unroll
+        for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+          for (int mp = -l; mp <= l; ++mp) {
+            float v = ev[l * l + l + mp];
+#pragma unroll
+            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) v += dsm[wave][L::doff(l, m, mp)] * y[L::kidx(l, m)];
+            Store<T>::st(eo + (l * l + l + mp) * C, v);
+          }
+      }
+    }
+    wave_lds_order();
+  }
+}
+
+// Backward of the edge-update block, first step: dY_e = trunc(D_e dE_e), in
+// the layout of Y and the storage type (TD), for the shared SO(2) backward.
+template <int LMAX, int MMAX, int CPL, typename TD>
+__global__ void __launch_bounds__(kThreads) edge_dy_kernel(int64_t E, const float *__restrict__ geom, int gstride,
+                                                           const float *__restrict__ dE, int C, Ptr3 dY) {
+  using L = Lay<LMAX, MMAX>;
+  __shared__ float dsm[kWavesPerBlock][L::ND];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave; e < E;
+       e += static_cast<int64_t>(gridDim.x) * kWavesPerBlock) {
+    const float *gr = geom + e * gstride;
+    for (int i = lane; i < L::ND; i += kWave) dsm[wave][i] = gr[i];
+    wave_lds_order();
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      const int c = lane + kWave * t;
+      if (c < C) {
+        float de[L::K];
+        const float *di = dE + e * L::K * C + c;
+#pragma unroll
+        for (int k = 0; k < L::K; ++k) de[k] = di[k * C];
+#pragma unroll
+        for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+            float v = 0.0f;
+#pragma unroll
+            for (int mp = -l; mp <= l; ++mp) v += dsm[wave][L::doff(l, m, mp)] * de[l * l + l + mp];
+            const int mu = cabs(m);
+            TD *row = static_cast<TD *>(dY.p[mu]) + e * L::blocks(mu) * C;
+            Store<TD>::st(row + L::col(l, m) * C + c, v);
+          }
+      }
+    }
+    wave_lds_order();
+  }
+}
+
 // Radial-weight gradient: dW_rad[k][p][j] = sum_e phi_e[k] dg_e[p][j] with
 // dg_e[p] = sum_{+-m} dX_e[l,+-m] * Xt_e[l,+-m] (Xt = edge-frame input before
 // the gate).  Node-centric waves as in scatter_in; wave (node, half, chunk)
@@ -1156,7 +1243,7 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
       if (k < n_rbf) part[((static_cast<int64_t>(stream) * n_rbf + k) * L::NP + p) * C2 + j] = acc[k][p];
 }
 
-// grad_x[n] = G[n] (owned rows) + sum over the node's incoming edges of
+// grad_x[n] = G[n] (owned rows; none when G is null) + sum over the node's incoming edges of
 // D_e^T (g_e * dX_e)[destination half] + sum over its outgoing edges of
 // D_e^T (g_e * dX_e)[source half], with dX the GEMM gradient of the gated
 // edge-frame input.  The waves of one node (two halves x channel chunks) sit
@@ -1302,7 +1389,7 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
 #pragma unroll
     for (int k = 0; k < L::K; ++k) {
       const int64_t o = (static_cast<int64_t>(nw.node) * L::K + k) * C + c;
-      const float g0 = nw.node < n_dst ? G[o] : 0.0f;
+      const float g0 = (G && nw.node < n_dst) ? G[o] : 0.0f;  // no G: the edge block has no node residual
       gx[o] = g0 + (acc[k] + red[partner][k * kWave + lane]);
     }
   }
@@ -1722,6 +1809,51 @@ void bwd_node_launch(const egnn_graph *g, const LayerShape &s, const float *geom
   Launch<LMAX, MMAX>::bwd_node(g, s, geom, G, wrad, w, gx, st);
 }
 
+template <int LMAX, int MMAX>
+void edge_update_launch(int64_t E, const LayerShape &s, const float *geom, const Acts &a, const void *e_in, void *e_out,
+                        hipStream_t st) {
+  CPtr3 Y{{a.Y[0], a.Y[1], a.Y[2]}};
+  int64_t blocks = (E + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > 8192) blocks = 8192;
+  const unsigned grid = static_cast<unsigned>(blocks);
+  auto go = [&](auto cpl) {
+    constexpr int CPL = decltype(cpl)::value;
+    if (s.storage == EGNN_BF16)
+      edge_update_kernel<LMAX, MMAX, CPL, uint16_t><<<grid, kThreads, 0, st>>>(
+          E, geom, s.gstride, Y, s.C, static_cast<const uint16_t *>(e_in), static_cast<uint16_t *>(e_out));
+    else
+      edge_update_kernel<LMAX, MMAX, CPL, float><<<grid, kThreads, 0, st>>>(
+          E, geom, s.gstride, Y, s.C, static_cast<const float *>(e_in), static_cast<float *>(e_out));
+  };
+  if (s.C <= kWave)
+    go(std::integral_constant<int, 1>{});
+  else if (s.C <= 2 * kWave)
+    go(std::integral_constant<int, 2>{});
+  else
+    go(std::integral_constant<int, 4>{});
+}
+template <int LMAX, int MMAX>
+void edge_dy_launch(int64_t E, const LayerShape &s, const float *geom, const float *dE, const BwdWs &w,
+                    hipStream_t st) {
+  int64_t blocks = (E + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > 8192) blocks = 8192;
+  const unsigned grid = static_cast<unsigned>(blocks);
+  const bool bf = s.storage == EGNN_BF16;
+  Ptr3 dY = bf ? Ptr3{{w.dYb[0], w.dYb[1], w.dYb[2]}} : Ptr3{{w.dY[0], w.dY[1], w.dY[2]}};
+  auto go = [&](auto cpl) {
+    constexpr int CPL = decltype(cpl)::value;
+    if (bf)
+      edge_dy_kernel<LMAX, MMAX, CPL, uint16_t><<<grid, kThreads, 0, st>>>(E, geom, s.gstride, dE, s.C, dY);
+    else
+      edge_dy_kernel<LMAX, MMAX, CPL, float><<<grid, kThreads, 0, st>>>(E, geom, s.gstride, dE, s.C, dY);
+  };
+  // C <= 128: the backward rejects wider layers before any launch
+  if (s.C <= kWave)
+    go(std::integral_constant<int, 1>{});
+  else
+    go(std::integral_constant<int, 2>{});
+}
+
 egnn_status check_graph(const egnn_graph *g) {
   EGNN_REQUIRE(g, "graph is null");
   EGNN_REQUIRE(g->n_dst >= 0 && g->n_src >= g->n_dst, "graph sizes invalid");
@@ -1764,16 +1896,25 @@ extern "C" egnn_status egnn_layer_sizes(const egnn_layer_desc *d, const egnn_gra
   return EGNN_OK;
 }
 
-extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph *g, const float *geom,
-                                      const float *weights, const void *x_in, void *x_out, void *edge_out,
-                                      void *saved, void *ws, size_t ws_bytes, hipStream_t stream) {
+// The node block (attention + aggregation onto the destination) and the edge
+// block (the per-edge message added to the edge embedding) share every step up
+// to the SO(2) products.
+static egnn_status layer_fwd_impl(bool edge_block, const egnn_layer_desc *d, const egnn_graph *g, const float *geom,
+                                  const float *weights, const void *x_in, void *x_out, void *edge_out,
+                                  const void *e_in, void *e_out, void *saved, void *ws, size_t ws_bytes,
+                                  hipStream_t stream) {
   clear_error();
   LayerShape s;
   EGNN_REQUIRE(make_shape(d, &s), "invalid layer description");
   egnn_status st = check_graph(g);
   if (st != EGNN_OK) return st;
-  EGNN_REQUIRE(weights && x_in && x_out, "null pointer");
-  EGNN_REQUIRE(x_in != x_out, "x_out must not alias x_in");
+  EGNN_REQUIRE(weights && x_in, "null pointer");
+  if (edge_block) {
+    EGNN_REQUIRE(g->n_edges == 0 || (e_in && e_out), "edge embeddings are null");
+  } else {
+    EGNN_REQUIRE(x_out, "null pointer");
+    EGNN_REQUIRE(x_in != x_out, "x_out must not alias x_in");
+  }
   EGNN_REQUIRE(aligned16(ws) && aligned16(saved), "ws and saved must be 16-byte aligned");
   const int64_t E = g->n_edges;
   if (E > 0) EGNN_REQUIRE(geom, "geom is null");
@@ -1870,7 +2011,13 @@ extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph
       }
     }
   }
-  if (g->n_dst > 0) {
+  if (edge_block) {
+    if (E > 0) {
+      // Y read, e read and written, D rows
+      Timed t(stream, "edge_update", 0.0, double(E) * (sumN * xb + 2.0 * s.K * s.C * xb + s.nD * 4.0));
+      EGNN_DISPATCH_LM(s.lmax, s.mmax, edge_update_launch, E, s, geom, acts, e_in, e_out, stream);
+    }
+  } else if (g->n_dst > 0) {
     if (E > 0) {
       Timed t(stream, "attention", 0.0, double(E) * (s.C * 4.0 + 8.0));
       if (bf)
@@ -1895,10 +2042,27 @@ extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph
   return EGNN_OK;
 }
 
-extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph *g, const float *geom,
-                                      const float *weights, const void *x_in, const void *saved,
-                                      const float *grad_out, float *grad_x_in, float *grad_weights, void *ws,
-                                      size_t ws_bytes, hipStream_t stream) {
+extern "C" egnn_status egnn_layer_fwd(const egnn_layer_desc *d, const egnn_graph *g, const float *geom,
+                                      const float *weights, const void *x_in, void *x_out, void *edge_out,
+                                      void *saved, void *ws, size_t ws_bytes, hipStream_t stream) {
+  return layer_fwd_impl(false, d, g, geom, weights, x_in, x_out, edge_out, nullptr, nullptr, saved, ws, ws_bytes,
+                        stream);
+}
+
+extern "C" egnn_status egnn_edge_update_fwd(const egnn_layer_desc *d, const egnn_graph *g, const float *geom,
+                                            const float *weights, const void *x_in, const void *e_in, void *e_out,
+                                            void *saved, void *ws, size_t ws_bytes, hipStream_t stream) {
+  return layer_fwd_impl(true, d, g, geom, weights, x_in, nullptr, nullptr, e_in, e_out, saved, ws, ws_bytes, stream);
+}
+
+// Node block: grad_out = dL/dx' [n_dst][K][C].  Edge block: grad_out =
+// dL/de' [n_edges][K][C]; its first step is dY = trunc(D dE) in place of the
+// attention-weighted row kernel, there is no w_att gradient and no node
+// residual.
+static egnn_status layer_bwd_impl(bool edge_block, const egnn_layer_desc *d, const egnn_graph *g, const float *geom,
+                                  const float *weights, const void *x_in, const void *saved, const float *grad_out,
+                                  float *grad_x_in, float *grad_weights, void *ws, size_t ws_bytes,
+                                  hipStream_t stream) {
   clear_error();
   LayerShape s;
   EGNN_REQUIRE(make_shape(d, &s), "invalid layer description");
@@ -1909,7 +2073,7 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
     return EGNN_E_UNSUPPORTED;
   }
   EGNN_REQUIRE(weights && x_in && saved && grad_x_in && grad_weights, "null pointer");
-  EGNN_REQUIRE(g->n_dst == 0 || grad_out, "grad_out is null");
+  EGNN_REQUIRE((edge_block ? g->n_edges : g->n_dst) == 0 || grad_out, "grad_out is null");
   EGNN_REQUIRE(aligned16(ws) && aligned16(saved), "ws and saved must be 16-byte aligned");
   const int64_t E = g->n_edges;
   if (E > 0) EGNN_REQUIRE(geom, "geom is null");
@@ -1947,7 +2111,12 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
     sumK += s.Kg[m];
     sumN += s.Ng[m];
   }
-  if (g->n_dst > 0 && E > 0) {
+  if (edge_block && E > 0) {
+    // dE read, dY written (storage type), D rows
+    Timed t(stream, "edge_dy", 0.0, double(E) * (s.K * s.C * 4.0 + sumN * (bf ? 2.0 : 4.0) + s.nD * 4.0));
+    EGNN_DISPATCH_LM(s.lmax, s.mmax, edge_dy_launch, E, s, geom, grad_out, w, stream);
+  }
+  if (!edge_block && g->n_dst > 0 && E > 0) {
     {
       // G rows, Y read and dY written (storage type), D rows, alpha / dalpha, w_att partials
       const double yb = bf ? 2.0 : 4.0;
@@ -2077,7 +2246,7 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
       // no edges: dx = G on owned rows, 0 on ghosts
       const int64_t n = static_cast<int64_t>(g->n_src) * s.K * s.C;
       fill_f32<<<ceil_div(n, T), T, 0, stream>>>(grad_x_in, n, 0.0f);
-      if (g->n_dst > 0)
+      if (g->n_dst > 0 && !edge_block)
         EGNN_TRY_HIP(hipMemcpyAsync(grad_x_in, grad_out, sizeof(float) * g->n_dst * s.K * s.C, hipMemcpyDeviceToDevice,
                                     stream));
     } else {
@@ -2088,9 +2257,26 @@ extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph
         pack_wrad_kernel<<<ceil_div(n, T), T, 0, stream>>>(weights + wo.wrad, s.n_rbf, s.n_pairs, 2 * s.C, w.wpk);
       }
       Timed t(stream, "bwd_node", 0.0, bytes);
-      EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_node_launch, g, s, geom, grad_out, weights + wo.wrad, w, grad_x_in, stream);
+      EGNN_DISPATCH_LM(s.lmax, s.mmax, bwd_node_launch, g, s, geom, edge_block ? nullptr : grad_out,
+                       weights + wo.wrad, w, grad_x_in, stream);
     }
   }
   EGNN_CHECK_LAUNCH();
   return EGNN_OK;
+}
+
+extern "C" egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph *g, const float *geom,
+                                      const float *weights, const void *x_in, const void *saved,
+                                      const float *grad_out, float *grad_x_in, float *grad_weights, void *ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  return layer_bwd_impl(false, d, g, geom, weights, x_in, saved, grad_out, grad_x_in, grad_weights, ws, ws_bytes,
+                        stream);
+}
+
+extern "C" egnn_status egnn_edge_update_bwd(const egnn_layer_desc *d, const egnn_graph *g, const float *geom,
+                                            const float *weights, const void *x_in, const void *saved,
+                                            const float *grad_e_out, float *grad_x_in, float *grad_weights, void *ws,
+                                            size_t ws_bytes, hipStream_t stream) {
+  return layer_bwd_impl(true, d, g, geom, weights, x_in, saved, grad_e_out, grad_x_in, grad_weights, ws, ws_bytes,
+                        stream);
 }

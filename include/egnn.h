@@ -206,6 +206,33 @@ egnn_status egnn_layer_bwd(const egnn_layer_desc *d, const egnn_graph *g, const 
                            void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Edge-update block  [MALOQ Sec. III-D: after the eSCN convolution the
+ * messages n_i (+) n_j either aggregate onto node j (the node block above) or
+ * update the edge embedding e_ij; Sec. III, Fig. 3(b): edge embeddings are
+ * rotated like node embeddings]
+ *
+ *   e_out[e] = e_in[e] + D_e^T Yhat_e
+ *
+ * where Yhat_e is the SO(2) convolution of the gated edge-frame message, the
+ * same per-edge message as egnn_layer_fwd's edge_out (same packed weights;
+ * w_att is not used).  e_in / e_out: [n_edges][K][C] in the storage type,
+ * 16-byte aligned; e_out may be e_in.  saved (for the backward) and the
+ * workspace take the sizes egnn_layer_sizes returns for the layer.
+ *
+ * egnn_edge_update_bwd: gradients of <G_e, e_out> for grad_e_out = G_e, fp32
+ * [n_edges][K][C]: grad_x_in [n_src][K][C] and grad_weights (packed, w_att
+ * part zero) are overwritten.  The gradient with respect to e_in is G_e itself
+ * (the update is a residual) and is not written.  C <= 128.
+ * ------------------------------------------------------------------------- */
+egnn_status egnn_edge_update_fwd(const egnn_layer_desc *d, const egnn_graph *g, const float *geom,
+                                 const float *weights, const void *x_in, const void *e_in, void *e_out,
+                                 void *saved, void *ws, size_t ws_bytes, hipStream_t stream);
+egnn_status egnn_edge_update_bwd(const egnn_layer_desc *d, const egnn_graph *g, const float *geom,
+                                 const float *weights, const void *x_in, const void *saved,
+                                 const float *grad_e_out, float *grad_x_in, float *grad_weights,
+                                 void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Label -> Matrix: Hamiltonian blocks  [MALOQ Sec. III-B1 Eq. (1), Sec. III-B2]
  *
  * Shells (host list shell_l, each l <= 2; n_orb = sum(2l+1) <= 32).  For
