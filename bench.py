@@ -36,6 +36,10 @@ WORKLOADS = {
                   desc="HfO2-like training step: graph + geometry + 1 layer fwd/bwd + 13x13 blocks"),
     "hfo2": dict(cfg="hfo2", backward=False, decode=False, layers=1,
                  desc="HfO2-like forward: graph + geometry + 1 layer fwd"),
+    "hfo2_l6": dict(cfg="hfo2_l6", backward=False, decode=False, layers=1,
+                    desc="HfO2-like forward at lmax 6 / mmax 2: graph + geometry + 1 layer fwd"),
+    "hfo2_l8": dict(cfg="hfo2_l8", backward=False, decode=False, layers=1,
+                    desc="HfO2-like forward at lmax 8 / mmax 2: graph + geometry + 1 layer fwd"),
     "halo": dict(cfg="halo", backward=False, decode=False, layers=1,
                  desc="one GPU's share with ghost halo: graph + geometry + 1 layer fwd"),
     "gst": dict(cfg="gst", backward=False, decode=False, layers=3,

@@ -138,6 +138,12 @@ inline unsigned ceil_div(int64_t a, int64_t b) { return static_cast<unsigned>((a
     case 40: FN<4, 0>(__VA_ARGS__); break;                                        \
     case 41: FN<4, 1>(__VA_ARGS__); break;                                        \
     case 42: FN<4, 2>(__VA_ARGS__); break;                                        \
+    case 60: FN<6, 0>(__VA_ARGS__); break;                                        \
+    case 61: FN<6, 1>(__VA_ARGS__); break;                                        \
+    case 62: FN<6, 2>(__VA_ARGS__); break;                                        \
+    case 80: FN<8, 0>(__VA_ARGS__); break;                                        \
+    case 81: FN<8, 1>(__VA_ARGS__); break;                                        \
+    case 82: FN<8, 2>(__VA_ARGS__); break;                                        \
     default: break;                                                               \
   }
 

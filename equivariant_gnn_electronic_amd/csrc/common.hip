@@ -19,7 +19,7 @@ void clear_error() { g_err[0] = '\0'; }
 
 bool make_shape(const egnn_layer_desc *d, LayerShape *s) {
   if (!d) return false;
-  if (d->lmax < 1 || d->lmax > 4) return false;
+  if (d->lmax < 1 || d->lmax > 8 || (d->lmax > 4 && d->lmax != 6 && d->lmax != 8)) return false;  // 1..4, 6, 8
   if (d->mmax < 0 || d->mmax > d->lmax || d->mmax > 2) return false;
   if (d->C < 8 || d->C > 256 || d->C % 8 != 0) return false;
   if (d->n_rbf < 2 || d->n_rbf > 16) return false;

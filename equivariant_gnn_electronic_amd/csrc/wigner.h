@@ -74,35 +74,44 @@ __host__ __device__ inline void ir_level(const float (&R1)[3][3], const float *D
   }
 }
 
+// Rows |m| <= MMAX of D^L stored in the layout of egnn_edge_geom.
+template <int L, int MMAX>
+__host__ __device__ inline void store_rows(const float *Dl, float *out) {
+  constexpr int mr = cmin(L, MMAX);
+  constexpr int off = d_block_offset(L, MMAX);
+#pragma unroll
+  for (int m = -mr; m <= mr; ++m)
+#pragma unroll
+    for (int mp = -L; mp <= L; ++mp) out[off + (m + mr) * (2 * L + 1) + (mp + L)] = Dl[(m + L) * (2 * L + 1) + (mp + L)];
+}
+
+// Level L of the recursion and the levels above it.  Level L is needed in
+// rows |m| <= MMAX for storage and, for each later level, in one more row
+// than that level needs: rows |m| <= min(L, MMAX + LMAX - L).
+template <int L, int LMAX, int MMAX>
+__host__ __device__ inline void wigner_up(const float (&R)[3][3], const float *Dp, float *out) {
+  if constexpr (L <= LMAX) {
+    constexpr int ROWS = cmin(L, MMAX + (LMAX - L));
+    float Dl[(2 * L + 1) * (2 * L + 1)];
+    ir_level<L, ROWS>(R, Dp, Dl);
+    store_rows<L, MMAX>(Dl, out);
+    wigner_up<L + 1, LMAX, MMAX>(R, Dl, out);
+  }
+}
+
 // Stored rows |m| <= MMAX of D^l(R), l = 0..LMAX, in the layout of egnn_edge_geom.
 template <int LMAX, int MMAX>
 __host__ __device__ inline void wigner_rows(const float (&R)[3][3], float *out) {
   out[0] = 1.0f;
-  if (LMAX < 1) return;
-  float D1[9], D2[25], D3[49], D4[81];
+  if constexpr (LMAX >= 1) {
+    float D1[9];
 #pragma unroll
-  for (int i = 0; i < 3; ++i)
+    for (int i = 0; i < 3; ++i)
 #pragma unroll
-    for (int j = 0; j < 3; ++j) D1[i * 3 + j] = R[i][j];
-  auto store = [&](int l, const float *Dl) {
-    const int mr = cmin(l, MMAX);
-    const int off = d_block_offset(l, MMAX);
-#pragma unroll
-    for (int m = -mr; m <= mr; ++m)
-#pragma unroll
-      for (int mp = -l; mp <= l; ++mp)
-        out[off + (m + mr) * (2 * l + 1) + (mp + l)] = Dl[(m + l) * (2 * l + 1) + (mp + l)];
-  };
-  store(1, D1);
-  if (LMAX < 2) return;
-  ir_level<2, (LMAX > 2 ? 2 : cmin(2, MMAX))>(R, D1, D2);
-  store(2, D2);
-  if (LMAX < 3) return;
-  ir_level<3, (LMAX > 3 ? 3 : cmin(3, MMAX))>(R, D2, D3);
-  store(3, D3);
-  if (LMAX < 4) return;
-  ir_level<4, cmin(4, MMAX)>(R, D3, D4);
-  store(4, D4);
+      for (int j = 0; j < 3; ++j) D1[i * 3 + j] = R[i][j];
+    store_rows<1, MMAX>(D1, out);
+    wigner_up<2, LMAX, MMAX>(R, D1, out);
+  }
 }
 
 // Gaussian radial basis with cosine envelope.

@@ -128,7 +128,7 @@ egnn_status egnn_build_graph(const double *pos, const double lo[3] /*host*/,
  * Layer description
  * ------------------------------------------------------------------------- */
 typedef struct {
-  int32_t lmax;     /* degrees 0..lmax, K = (lmax+1)^2 coefficients; 1 <= lmax <= 4            */
+  int32_t lmax;     /* degrees 0..lmax, K = (lmax+1)^2 coefficients; 1..4, 6 or 8             */
   int32_t mmax;     /* orders kept in the edge frame, 0 <= mmax <= min(lmax, 2)               */
   int32_t C;        /* channels per coefficient; multiple of 8, 8 <= C <= 256                 */
   int32_t n_rbf;    /* Gaussian radial basis size, 2 <= n_rbf <= 16                            */

@@ -65,6 +65,8 @@ CONFIGS = {
                    note="64 atoms, 2 species Bernoulli(1/2), 9 A periodic cube, r_c 5 A"),
     "tiny_l4": Config("tiny_l4", 1, (32, 32), (9.0, 9.0, 9.0), True, 5.0, 4, 2, 8,
                       note="tiny geometry at lmax 4 / mmax 2 / C 8 (m-truncation, decode)"),
+    "tiny_l6": Config("tiny_l6", 1, (32, 32), (9.0, 9.0, 9.0), True, 5.0, 6, 2, 8,
+                      note="tiny geometry at lmax 6 / mmax 2 / C 8 (f-orbital degrees)"),
     "tiny_stack": Config("tiny_stack", 1, (32, 32), (9.0, 9.0, 9.0), True, 5.0, 4, 2, 16, storage="bf16",
                          layers=3, note="tiny geometry, 3 stacked layers, bf16 storage"),
     "hfo2": Config("hfo2", 2, (1000, 2000), (32.8, 32.8, 32.8), True, 8.0, 4, 2, 64,
@@ -76,6 +78,10 @@ CONFIGS = {
                    halo=8.0,
                    note="one GPU's share: 30,000 owned atoms in a 100x100x60 A slab, "
                         "ghost sources in the 8 A shell, open boundary"),
+    "hfo2_l6": Config("hfo2_l6", 6, (1000, 2000), (32.8, 32.8, 32.8), True, 8.0, 6, 2, 64, geometry_seed=2,
+                      note="HfO2-like geometry at lmax 6 (f-orbital degrees)"),
+    "hfo2_l8": Config("hfo2_l8", 7, (1000, 2000), (32.8, 32.8, 32.8), True, 8.0, 8, 2, 64, geometry_seed=2,
+                      note="HfO2-like geometry at lmax 8 (g-orbital degrees)"),
     "train": Config("train", 5, (1000, 2000), (32.8, 32.8, 32.8), True, 8.0, 4, 2, 64,
                     geometry_seed=2,
                     note="HfO2-like training step: fwd + bwd + Hamiltonian blocks"),
@@ -83,7 +89,7 @@ CONFIGS = {
 
 # Species are drawn as a random assignment of the fixed counts, except for the
 # tiny cell whose two species are Bernoulli(1/2).
-_BERNOULLI = {"tiny", "tiny_l4", "tiny_stack"}
+_BERNOULLI = {"tiny", "tiny_l4", "tiny_l6", "tiny_stack"}
 
 
 def bf16_round(a):

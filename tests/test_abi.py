@@ -61,14 +61,14 @@ def test_weight_count_matches_packed_layout(lib, name):
 
 def test_geom_stride(lib):
     # rows |m| <= mmax of D^l for l <= lmax, then n_rbf, then the destination, padded to 16
-    for lmax, mmax in [(1, 0), (2, 2), (3, 1), (4, 2), (4, 0)]:
+    for lmax, mmax in [(1, 0), (2, 2), (3, 1), (4, 2), (4, 0), (6, 2), (8, 1)]:
         nd = sum((2 * min(l, mmax) + 1) * (2 * l + 1) for l in range(lmax + 1))
         d = _desc(lmax, mmax, 16)
         assert lib.egnn_geom_stride(ct.byref(d)) == (nd + 8 + 1 + 15) // 16 * 16
-    assert nd == 25 and lib.egnn_geom_stride(ct.byref(_desc(4, 2, 64))) == 128
+    assert lib.egnn_geom_stride(ct.byref(_desc(4, 2, 64))) == 128   # 115 Wigner rows + 8 + 1, padded
 
 
-@pytest.mark.parametrize("bad", [dict(lmax=5), dict(lmax=0), dict(mmax=3), dict(C=12), dict(C=0),
+@pytest.mark.parametrize("bad", [dict(lmax=5), dict(lmax=7), dict(lmax=9), dict(lmax=0), dict(mmax=3), dict(C=12), dict(C=0),
                                  dict(n_rbf=1), dict(n_rbf=17), dict(storage=7)])
 def test_invalid_layer_desc_rejected(lib, bad):
     from equivariant_gnn_electronic_amd import _lib

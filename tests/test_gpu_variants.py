@@ -2,7 +2,7 @@
 
 The 64-atom periodic cell (several images per pair) carries every
 (lmax, mmax, C, n_rbf, storage) combination below, so each kernel
-instantiation the ABI dispatches to is exercised: lmax 1-4, mmax 0-2, C with
+instantiation the ABI dispatches to is exercised: lmax 1-4, 6 and 8, mmax 0-2, C with
 a partial 64-channel chunk (24, 96) and two chunks (128), 3/4/6/8/12/16 radial
 functions, bf16 storage on both bf16 GEMM variants and the fallback for
 K not a multiple of 32, and the channel-pair kernels (bf16, C = 128: rotate-in,
@@ -51,6 +51,12 @@ VARIANTS = [
     (3, 2, 128, 8, "bf16"),
     (4, 0, 128, 5, "bf16"),
     (4, 1, 128, 16, "bf16"),  # pairs in the backward row kernel, per-channel rotate-in (16 basis functions)
+    (6, 2, 8, 8, "f32"),      # higher degrees: f (lmax 6) and g (lmax 8) orbital labels need them
+    (6, 1, 64, 8, "f32"),
+    (6, 2, 128, 8, "bf16"),
+    (8, 2, 16, 8, "f32"),
+    (8, 0, 8, 4, "f32"),
+    (8, 1, 32, 8, "bf16"),
 ]
 
 

@@ -91,7 +91,7 @@ def _rotate_irreps(a, Q, lmax):
     return out
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_l4"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_l4", "tiny_l6"])
 def test_layer_equivariance(name):
     cfg, s, g, x, w, d = _setup(name)
     base = layer.layer_forward(g, x, w, d)
@@ -149,7 +149,7 @@ def _loss(g, x, w, d, G):
     return float(np.sum(layer.layer_forward(g, x, w, d)["x_out"] * G))
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_l4"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_l4", "tiny_l6"])
 def test_backward_matches_finite_differences(name):
     cfg, s, g, x, w, d = _setup(name)
     G = synth.make_cotangent(cfg, s.n_dst).astype(np.float64)

@@ -11,7 +11,7 @@ from scipy.spatial.transform import Rotation as Rot
 
 from oracle import so3
 
-LMAX = 4
+LMAX = 8   # the degrees the layer is built for go up to 8 (f and g orbital labels)
 
 
 def _unit(n, seed):
