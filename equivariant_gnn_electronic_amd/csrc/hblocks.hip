@@ -30,14 +30,15 @@ constexpr int kMaxEntries = kMaxOrb * kMaxOrb;
 constexpr int kMaxTerms = 8192;
 constexpr int kMaxLab = kMaxEntries;
 
-constexpr int kMaxLab2 = 4;            // labels up to L = 2 * 2
+constexpr int kMaxShellL = 3;          // shells up to f
+constexpr int kMaxLabL = 2 * kMaxShellL;  // labels up to L = 6 (irreps lmax >= 6)
 constexpr int kMaxNL = 64;             // label channels per degree (4 MFMA column tiles)
 
 struct Table {
   int lmax_lab;                        // 2 * max shell degree
-  int nL[2 * kMaxLab2 + 1];            // label channels per L
-  int woff[2 * kMaxLab2 + 2];          // first weight row of L
-  int hoff[2 * kMaxLab2 + 2];          // first label of L in the (L, M, k) order
+  int nL[kMaxLabL + 1];                // label channels per L
+  int woff[kMaxLabL + 2];              // first weight row of L
+  int hoff[kMaxLabL + 2];              // first label of L in the (L, M, k) order
   int term_start[kMaxEntries + 1];
   float term_coef[kMaxTerms];
   unsigned short term_idx[kMaxTerms];
@@ -59,7 +60,7 @@ bool build_layout(const int *shell_l, int n_shells, Layout *out) {
   std::vector<int> off(n_shells);
   int o = 0, lmx = 0;
   for (int a = 0; a < n_shells; ++a) {
-    if (shell_l[a] < 0 || shell_l[a] > 2) return false;
+    if (shell_l[a] < 0 || shell_l[a] > kMaxShellL) return false;
     off[a] = o;
     o += 2 * shell_l[a] + 1;
     lmx = std::max(lmx, shell_l[a]);
@@ -151,7 +152,7 @@ egnn_status table_slot(const int *shell_l, int n_shells, int *slot, Layout *lay)
     return EGNN_E_UNSUPPORTED;
   }
   if (!build_layout(shell_l, n_shells, lay)) {
-    set_error("shell list not supported (each l <= 2, at most %d orbitals)", kMaxOrb);
+    set_error("shell list not supported (each l <= 3, at most %d orbitals)", kMaxOrb);
     return EGNN_E_UNSUPPORTED;
   }
   std::lock_guard<std::mutex> lock(g_cache.mu);
@@ -244,8 +245,8 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
   const int lab_ld = label_stride(n_lab);
   float *hs_all = wl + (n_w + 16) * WLD;                               // [kWaves][kTile][lab_ld]
   // per-degree entries of the table, read once per (tile, L) in the label loop
-  __shared__ int l_n[2 * kMaxLab2 + 1], l_woff[2 * kMaxLab2 + 1], l_hoff[2 * kMaxLab2 + 1];
-  if (threadIdx.x <= 2 * kMaxLab2) {
+  __shared__ int l_n[kMaxLabL + 1], l_woff[kMaxLabL + 1], l_hoff[kMaxLabL + 1];
+  if (threadIdx.x <= kMaxLabL) {
     l_n[threadIdx.x] = tb.nL[threadIdx.x];
     l_woff[threadIdx.x] = tb.woff[threadIdx.x];
     l_hoff[threadIdx.x] = tb.hoff[threadIdx.x];
@@ -401,7 +402,7 @@ static bool valid_hdesc(const egnn_hdesc *h) {
   if (h->storage != EGNN_F32 && h->storage != EGNN_BF16) return false;
   int lmx = 0;
   for (int i = 0; i < h->n_shells; ++i) {
-    if (h->shell_l[i] < 0 || h->shell_l[i] > 2) return false;
+    if (h->shell_l[i] < 0 || h->shell_l[i] > kMaxShellL) return false;
     lmx = std::max(lmx, h->shell_l[i]);
   }
   return h->lmax >= 2 * lmx;

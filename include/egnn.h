@@ -235,7 +235,7 @@ egnn_status egnn_edge_update_bwd(const egnn_layer_desc *d, const egnn_graph *g, 
 /* ---------------------------------------------------------------------------
  * Label -> Matrix: Hamiltonian blocks  [MALOQ Sec. III-B1 Eq. (1), Sec. III-B2]
  *
- * Shells (host list shell_l, each l <= 2; n_orb = sum(2l+1) <= 32).  For
+ * Shells (host list shell_l, each l <= 3; n_orb = sum(2l+1) <= 32).  For
  * ordered shell pairs (a, b) in lexicographic order and L = |la-lb|..la+lb
  * ascending, label channel k(a,b,L) counts the earlier pairs carrying L;
  * n_L = number of pairs carrying L.  Labels are h_L = W_L f^L (C -> n_L) and

@@ -174,9 +174,12 @@ def test_decode_description_checks(lib):
     h_small = _lib.EgnnHDesc(3, 64, 5, arr, 0)          # lmax must cover 2 * max shell l
     assert lib.egnn_hblocks_label_rows(ct.byref(h_small)) == 0
     assert lib.egnn_hblocks(ct.byref(h_small), 1, 1, None, None, None, None, None, None, None) == _lib.EGNN_E_ARG
-    arr3 = (ct.c_int32 * 1)(3)                            # f shells are not supported
-    h3 = _lib.EgnnHDesc(8, 64, 1, arr3, 0)
-    assert lib.egnn_hblocks_label_rows(ct.byref(h3)) == 0
+    arr3 = (ct.c_int32 * 1)(3)                            # f x f: one label channel for each L = 0..6
+    assert lib.egnn_hblocks_label_rows(ct.byref(_lib.EgnnHDesc(8, 64, 1, arr3, 0))) == 7
+    assert lib.egnn_hblocks_label_rows(ct.byref(_lib.EgnnHDesc(6, 64, 1, arr3, 0))) == 7
+    assert lib.egnn_hblocks_label_rows(ct.byref(_lib.EgnnHDesc(4, 64, 1, arr3, 0))) == 0   # lmax < 6
+    arr4 = (ct.c_int32 * 1)(4)                            # g shells are not supported
+    assert lib.egnn_hblocks_label_rows(ct.byref(_lib.EgnnHDesc(8, 64, 1, arr4, 0))) == 0
     # nothing to do is fine
     assert lib.egnn_hblocks(ct.byref(h), 0, 0, None, None, None, None, None, None, None) == 0
 

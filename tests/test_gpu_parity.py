@@ -194,6 +194,24 @@ def test_hblocks(dev):
     assert_close(hn.cpu().numpy(), hn_ref, 1e-5, "on-site blocks")
 
 
+def test_hblocks_f_shells(dev):
+    """Decode with f shells (s s p p d f, 20 orbitals, labels up to L = 6) from
+    lmax-6 irreps: the layer's edge messages and outputs at lmax 6."""
+    cfg = synth.CONFIGS["tiny_l6"]
+    r = _gpu_forward(cfg, dev, edge_out=True)
+    shells = (0, 0, 1, 1, 2, 3)
+    _, n = odec.label_layout(shells)
+    rng = np.random.default_rng(61)
+    we = [(rng.standard_normal((c, cfg.C)) / np.sqrt(cfg.C)).astype(np.float32) for c in n]
+    wn = [(rng.standard_normal((c, cfg.C)) / np.sqrt(cfg.C)).astype(np.float32) for c in n]
+    he, hn = eg.egnn_hblocks(6, cfg.C, torch.from_numpy(np.concatenate(we)).to(dev),
+                             torch.from_numpy(np.concatenate(wn)).to(dev), r["eo"], r["xo"], shell_l=shells)
+    torch.cuda.synchronize()
+    assert he.shape[1:] == (20, 20)
+    assert_close(he.cpu().numpy(), odec.hblocks(r["eo"].cpu().numpy(), we, shells), 1e-5, "edge blocks")
+    assert_close(hn.cpu().numpy(), odec.hblocks(r["xo"].cpu().numpy(), wn, shells), 1e-5, "on-site blocks")
+
+
 def _rotate_irreps(a, Q, lmax):
     out = np.empty_like(a)
     for l in range(lmax + 1):

@@ -61,3 +61,26 @@ def test_hamiltonian_blocks_covariant():
     for o, l in zip(off, decode.SHELL_L):
         Dorb[o:o + 2 * l + 1, o:o + 2 * l + 1] = so3.wigner_d(l, Q)
     np.testing.assert_allclose(decode.hblocks(fr, w), Dorb @ decode.hblocks(f, w) @ Dorb.T, atol=1e-12)
+
+
+def test_f_shell_blocks_covariant():
+    """With f shells (s s p p d f: 20 orbitals, labels up to L = 6, irreps at
+    lmax 6) the blocks still transform as D^{la} H D^{lb}^T."""
+    shells = (0, 0, 1, 1, 2, 3)
+    rng = np.random.default_rng(12)
+    C = 3
+    f = rng.standard_normal((4, 49, C))
+    _, n = decode.label_layout(shells)
+    assert sum((2 * L + 1) * c for L, c in enumerate(n)) == 20 * 20 and len(n) == 7
+    w = [rng.standard_normal((c, C)) for c in n]
+    Q = Rot.random(random_state=13).as_matrix()
+    fr = np.empty_like(f)
+    for l in range(7):
+        sl = slice(l * l, (l + 1) ** 2)
+        fr[:, sl, :] = np.einsum("mn,enc->emc", so3.wigner_d(l, Q), f[:, sl, :])
+    off, n_orb = decode.orbital_offsets(shells)
+    Dorb = np.zeros((n_orb, n_orb))
+    for o, l in zip(off, shells):
+        Dorb[o:o + 2 * l + 1, o:o + 2 * l + 1] = so3.wigner_d(l, Q)
+    np.testing.assert_allclose(decode.hblocks(fr, w, shells), Dorb @ decode.hblocks(f, w, shells) @ Dorb.T,
+                               atol=1e-11)
