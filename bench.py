@@ -392,6 +392,8 @@ FAMILY_KERNELS = {
     "rotate_in": "::scatter_in_",
     "aggregate": "::aggregate_",
     "hblocks": "hblocks_kernel",
+    "edge_update": "::edge_update_kernel<",
+    "edge_dy": "::edge_dy_kernel<",
     "matrix_to_label": ("::labels_kernel<", ", true>"),   # every (chunk, pass) instantiation
     "label_to_matrix": ("::labels_kernel<", ", false>"),
 }
