@@ -11,9 +11,12 @@ The default workload is the HfO2-like training step: 3,000 atoms (1,000 Hf +
 lmax 4, mmax 2, C 64, fp32, one layer forward + backward, then the decode
 into 13x13 orbital blocks.  `value` is edges per second of whole steps.
 
-The m2l / l2m workloads time Matrix -> Label and Label -> Matrix (MALOQ
-Sec. III-B2, Fig. 2(c, d)) over a batch of 4,096 small molecules; `value` is
-atoms per second there.
+Other workloads (--workload): hfo2, halo, gst (forwards; GST is three bf16
+layers), gst_train (bf16 training step), hfo2_l6 / hfo2_l8 (forwards at
+lmax 6 and 8), edge_train (the edge-update block's training step), and m2l /
+l2m, which time Matrix -> Label and Label -> Matrix (MALOQ Sec. III-B2,
+Fig. 2(c, d)) over a batch of 4,096 small molecules; `value` is atoms per
+second there.
 
 Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
 """
