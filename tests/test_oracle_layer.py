@@ -208,3 +208,110 @@ def test_backward_with_ghost_sources():
         v = rng.standard_normal(w.shape)
         fd = (_loss(g, x, w + h * v, d, G) - _loss(g, x, w - h * v, d, G)) / (2 * h)
         assert abs(fd - dw @ v) <= 1e-6 * max(1.0, abs(fd))
+
+
+@pytest.mark.parametrize("n_rbf,r_cut", [(8, 5.0), (8, 10.0), (4, 6.0), (16, 8.0)])
+def test_radial_basis_closed_forms(n_rbf, r_cut):
+    """Reading R11 worked by hand, with no call into the oracle for the expected
+    values: n Gaussians with centres k r_c/(n-1) and width r_c/(n-1), times the
+    cosine envelope (1 + cos(pi d / r_c))/2.  So at d = 0 the envelope is 1 and
+    phi_k = exp(-k^2/2); at its own centre phi_k equals the envelope there; one
+    width either side it is exp(-1/2) times the envelope; the envelope is 1/2 at
+    r_c/2 and 0 at r_c.  A different width, centre spacing or envelope (e.g.
+    sigma = r_c/n, or cos(pi d / 2r_c)) fails one of these."""
+    import math
+    d = layer.LayerDesc(2, 2, 8, n_rbf, r_cut)
+    phi0 = layer.radial_basis(np.array([0.0]), d)[0]
+    np.testing.assert_allclose(phi0, [math.exp(-k * k / 2.0) for k in range(n_rbf)], rtol=1e-12, atol=0)
+    step = r_cut / (n_rbf - 1)
+    for k in range(n_rbf):
+        mu = k * step
+        env = 0.5 * (1.0 + math.cos(math.pi * mu / r_cut))
+        got = layer.radial_basis(np.array([mu]), d)[0]
+        assert abs(got[k] - env) <= 1e-14
+        # neighbouring centres sit one width away
+        if k + 1 < n_rbf:
+            assert abs(got[k + 1] - math.exp(-0.5) * env) <= 1e-14
+        if k > 0:
+            assert abs(got[k - 1] - math.exp(-0.5) * env) <= 1e-14
+        for sgn in (-1.0, 1.0):
+            r = mu + sgn * step
+            if 0.0 <= r <= r_cut:
+                e2 = 0.5 * (1.0 + math.cos(math.pi * r / r_cut))
+                assert abs(layer.radial_basis(np.array([r]), d)[0][k] - math.exp(-0.5) * e2) <= 1e-14
+    half = layer.radial_basis(np.array([r_cut / 2]), d)[0]
+    np.testing.assert_allclose(half, [0.5 * math.exp(-((r_cut / 2 - k * step) ** 2) / (2 * step * step))
+                                      for k in range(n_rbf)], rtol=1e-14, atol=1e-300)
+    np.testing.assert_allclose(layer.radial_basis(np.array([r_cut]), d)[0], 0.0, atol=1e-15)
+
+
+def _open_cell_with_ghosts():
+    rng = np.random.default_rng(8)
+    pos = rng.random((40, 3)) * np.array([10.0, 10.0, 6.0])
+    n_dst = 25
+    d = layer.LayerDesc(lmax=2, mmax=1, C=4, n_rbf=8, r_cut=4.0)
+    x = rng.standard_normal((40, d.K, d.C))
+    n_w = sum(int(np.prod(sh)) for _, sh in synth.layer_weight_sizes(d.lmax, d.mmax, d.C, d.n_rbf))
+    w = rng.standard_normal(n_w) * 0.3
+    return pos, n_dst, np.array([10.0, 10.0, 6.0]), d, x, w
+
+
+@pytest.mark.parametrize("case", ["tiny", "tiny_l4", "open_ghosts"])
+@pytest.mark.parametrize("chunk_edges", [1, 150, 16384])
+def test_forward_rows_equals_forward(case, chunk_edges):
+    """The chunked, row-sampled forward used at full size gives the same x' and
+    alpha as the whole-graph forward: on all rows, and on a subset of rows built
+    alone (as the large-structure parity tests build them)."""
+    if case == "open_ghosts":
+        pos, n_dst, box, d, x, w = _open_cell_with_ghosts()
+        mask, rc = 0, d.r_cut
+    else:
+        cfg, s, _, x, w, d = _setup(case)
+        pos, n_dst, box, mask, rc = s.pos, s.n_dst, s.box, s.periodic_mask, s.r_cut
+    g = neighbors.build_graph(pos, n_dst, box, mask, rc)
+    ref = layer.layer_forward(g, x, w, d)
+    xo, alpha = layer.layer_forward_rows(g, x, w, d, chunk_edges=chunk_edges)
+    np.testing.assert_allclose(xo, ref["x_out"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(alpha, ref["alpha"], rtol=0, atol=1e-13)
+    rows = np.sort(np.random.default_rng(17).choice(n_dst, size=n_dst // 3, replace=False))
+    gs = neighbors.build_graph(pos, n_dst, box, mask, rc, rows=rows)
+    xs, alpha_s = layer.layer_forward_rows(gs, x, w, d, chunk_edges=chunk_edges)
+    np.testing.assert_allclose(xs, ref["x_out"][rows], rtol=0, atol=1e-13)
+    sel = np.concatenate([np.arange(g["row_ptr"][r], g["row_ptr"][r + 1]) for r in rows])
+    np.testing.assert_allclose(alpha_s, ref["alpha"][sel], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("case", ["tiny", "open_ghosts"])
+def test_aggregation_equals_dense_adjacency_product(case):
+    """Attention and aggregation as dense matrix algebra: each edge's destination is
+    found from geometry alone (the atom at x_src + S L + vec), the logits fill an
+    [n_dst][E] matrix with -inf off the adjacency, scipy's softmax along each row
+    gives alpha, and x' - x is that matrix times the per-edge messages.  This
+    checks the CSR segment softmax and segment sum (and empty rows) independently."""
+    from scipy.special import softmax
+    if case == "open_ghosts":
+        pos, n_dst, box, d, x, w = _open_cell_with_ghosts()
+        pos = pos.copy()
+        pos[3] = [30.0, 30.0, 30.0]                               # an owned atom with no neighbour
+        mask, rc = 0, d.r_cut
+    else:
+        cfg, s, _, x, w, d = _setup(case)
+        pos, n_dst, box, mask, rc = s.pos, s.n_dst, s.box, s.periodic_mask, s.r_cut
+    g = neighbors.build_graph(pos, n_dst, box, mask, rc)
+    out = layer.layer_forward(g, x, w, d)
+    E = len(g["src"])
+    tip = pos[g["src"]] + g["shift"].astype(np.float64) * box + g["vec"].astype(np.float64)
+    d2 = ((tip[:, None, :] - pos[None, :n_dst, :]) ** 2).sum(-1)
+    dst = np.argmin(d2, axis=1)
+    assert np.sqrt(d2[np.arange(E), dst]).max() < 1e-5          # the tip lands on an owned atom
+    A = np.full((n_dst, E), -np.inf)
+    A[dst, np.arange(E)] = out["logits"]
+    has = np.isfinite(A).any(axis=1)
+    alpha = np.zeros_like(A)
+    alpha[has] = softmax(A[has], axis=1)
+    np.testing.assert_allclose(alpha[dst, np.arange(E)], out["alpha"], rtol=0, atol=1e-14)
+    agg = (alpha @ out["msg"].reshape(E, -1)).reshape(n_dst, d.K, d.C)
+    np.testing.assert_allclose(out["x_out"] - x[:n_dst], agg, rtol=0, atol=1e-12)
+    if case == "open_ghosts":
+        assert (~has).any()
+        np.testing.assert_array_equal(out["x_out"][~has], x[:n_dst][~has])
