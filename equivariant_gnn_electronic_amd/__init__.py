@@ -44,6 +44,39 @@ def _d3(v):
     return (ct.c_double * 3)(*[float(a) for a in v])
 
 
+def _expect(t, name, dtype, shape, min_rows=None):
+    """Reject a tensor whose dtype or shape differs from what the kernels read.
+
+    The C ABI sees plain pointers, so this is the only place a wrong buffer can be
+    caught before a kernel reads or writes past it.  `shape` lists the expected
+    sizes (None = any); `min_rows`, when given, replaces an exact first size by a
+    lower bound.  Runs before the device check, so it needs no GPU.
+    """
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != len(shape):
+        raise ValueError(f"{name} must have {len(shape)} dimensions, got shape {tuple(t.shape)}")
+    for i, (got, want) in enumerate(zip(t.shape, shape)):
+        if i == 0 and min_rows is not None:
+            if got < min_rows:
+                raise ValueError(f"{name} needs at least {min_rows} rows, got {got}")
+        elif want is not None and got != want:
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _expect_bytes(t, name, n):
+    if n > 0 and (t is None or t.numel() * t.element_size() < n):
+        have = 0 if t is None else t.numel() * t.element_size()
+        raise ValueError(f"{name} holds {have} bytes, needs {n}")
+
+
 @dataclass
 class Graph:
     """Destination-sorted CSR (incoming-edge layout) held in torch tensors."""
@@ -87,8 +120,11 @@ def egnn_build_graph(pos, n_dst, lo, box, periodic_mask, r_cut, capacity=None):
     unless given), then the fill into arrays of exactly that size.
     """
     lib = _lib.load()
+    _expect(pos, "pos", torch.float64, (None, 3))
     dev = pos.device
     n_src = pos.shape[0]
+    if not 0 <= n_dst <= n_src:
+        raise ValueError(f"n_dst ({n_dst}) must lie in [0, n_src = {n_src}]")
     row_ptr = torch.empty(n_dst + 1, dtype=torch.int32, device=dev)
     cap = 0 if capacity is None else int(capacity)
 
@@ -155,6 +191,7 @@ class GraphBuilder:
             setattr(g, f, getattr(self, f).data_ptr())
 
     def build(self, pos):
+        _expect(pos, "pos", torch.float64, (self.n_src, 3))
         _lib.check("egnn_build_graph", _lib.load().egnn_build_graph(
             _ptr(pos), self.lo3, self.box3, self.mask, self.r_cut, ct.byref(self.g), _ptr(self.ws),
             self.ws.numel(), _stream()))
@@ -196,8 +233,11 @@ def egnn_edge_geom(desc, graph: Graph, out=None):
     """Per-edge Wigner rows, radial basis and destination row: [E][stride] float32."""
     lib = _lib.load()
     stride = egnn_geom_stride(desc)
+    if stride <= 0:
+        raise ValueError("invalid layer description")
     if out is None:
         out = torch.empty((max(graph.n_edges, 1), stride), dtype=torch.float32, device=graph.row_ptr.device)
+    _expect(out, "out", torch.float32, (None, stride), min_rows=graph.n_edges)
     g = graph.c_struct()
     _lib.check("egnn_edge_geom", lib.egnn_edge_geom(ct.byref(desc), ct.byref(g), _ptr(out), _stream()))
     return out
@@ -222,17 +262,40 @@ class LayerBuffers:
         self.ws = torch.empty(max(wsf, wsb if train else 0, 1), dtype=torch.uint8, device=dev)
 
 
+def _check_layer_args(desc, graph: Graph, geom, weights, x):
+    """dtype and shape of the inputs every layer call reads; returns (K, storage dtype)."""
+    if desc.storage not in _STORAGE:
+        raise ValueError(f"unknown storage type {desc.storage}")
+    K = (desc.lmax + 1) ** 2
+    dt = _STORAGE[desc.storage]
+    n_w = egnn_layer_weight_count(desc)
+    if n_w == 0:
+        raise ValueError("invalid layer description")
+    _expect(weights, "weights", torch.float32, (n_w,))
+    _expect(geom, "geom", torch.float32, (None, egnn_geom_stride(desc)), min_rows=graph.n_edges)
+    _expect(x, "x", dt, (None, K, desc.C), min_rows=graph.n_src)
+    return K, dt
+
+
+def _check_buffers(desc, graph: Graph, buffers, train, bwd):
+    saved, wsf, wsb = egnn_layer_sizes(desc, graph)
+    if train or bwd:
+        if buffers.saved is None:
+            raise ValueError("the backward needs buffers made with train=True")
+        _expect_bytes(buffers.saved, "buffers.saved", saved)
+    _expect_bytes(buffers.ws, "buffers.ws", wsb if bwd else wsf)
+
+
 def egnn_layer_fwd(desc, graph: Graph, geom, weights, x, x_out=None, edge_out=False, buffers=None):
     """x_out [n_dst][K][C] (and edge_out [E][K][C] if requested) of one layer."""
     lib = _lib.load()
-    K = (desc.lmax + 1) ** 2
-    dt = _STORAGE[desc.storage]
-    if x.dtype != dt or weights.dtype != torch.float32:
-        raise ValueError("x must use the storage dtype and weights float32")
+    K, dt = _check_layer_args(desc, graph, geom, weights, x)
     if buffers is None:
         buffers = LayerBuffers(desc, graph, train=False)
+    _check_buffers(desc, graph, buffers, train=buffers.saved is not None, bwd=False)
     if x_out is None:
         x_out = torch.empty((graph.n_dst, K, desc.C), dtype=dt, device=x.device)
+    _expect(x_out, "x_out", dt, (graph.n_dst, K, desc.C))
     eo = torch.empty((max(graph.n_edges, 1), K, desc.C), dtype=dt, device=x.device) if edge_out else None
     g = graph.c_struct()
     _lib.check("egnn_layer_fwd", lib.egnn_layer_fwd(
@@ -244,11 +307,15 @@ def egnn_layer_fwd(desc, graph: Graph, geom, weights, x, x_out=None, edge_out=Fa
 def egnn_layer_bwd(desc, graph: Graph, geom, weights, x, buffers, grad_out, grad_x=None, grad_w=None):
     """(dL/dx [n_src][K][C], dL/dweights) for the loss <grad_out, x_out>."""
     lib = _lib.load()
-    K = (desc.lmax + 1) ** 2
+    K, _ = _check_layer_args(desc, graph, geom, weights, x)
+    _check_buffers(desc, graph, buffers, train=True, bwd=True)
+    _expect(grad_out, "grad_out", torch.float32, (graph.n_dst, K, desc.C))
     if grad_x is None:
         grad_x = torch.empty((graph.n_src, K, desc.C), dtype=torch.float32, device=x.device)
     if grad_w is None:
         grad_w = torch.empty(egnn_layer_weight_count(desc), dtype=torch.float32, device=x.device)
+    _expect(grad_x, "grad_x", torch.float32, (graph.n_src, K, desc.C))
+    _expect(grad_w, "grad_w", torch.float32, (egnn_layer_weight_count(desc),))
     g = graph.c_struct()
     _lib.check("egnn_layer_bwd", lib.egnn_layer_bwd(
         ct.byref(desc), ct.byref(g), _ptr(geom), _ptr(weights), _ptr(x), _ptr(buffers.saved), _ptr(grad_out),
@@ -260,10 +327,14 @@ def egnn_edge_update_fwd(desc, graph: Graph, geom, weights, x, e_in, e_out=None,
     """Edge-update block: e_out = e_in + the per-edge message (in place when e_out is e_in).
     Returns (e_out, buffers); buffers keep the activations the backward reads."""
     lib = _lib.load()
+    K, dt = _check_layer_args(desc, graph, geom, weights, x)
+    _expect(e_in, "e_in", dt, (graph.n_edges, K, desc.C))
     if buffers is None:
         buffers = LayerBuffers(desc, graph, train=True)
+    _check_buffers(desc, graph, buffers, train=buffers.saved is not None, bwd=False)
     if e_out is None:
         e_out = torch.empty_like(e_in)
+    _expect(e_out, "e_out", dt, (graph.n_edges, K, desc.C))
     g = graph.c_struct()
     _lib.check("egnn_edge_update_fwd", lib.egnn_edge_update_fwd(
         ct.byref(desc), ct.byref(g), _ptr(geom), _ptr(weights), _ptr(x), _ptr(e_in), _ptr(e_out),
@@ -274,10 +345,15 @@ def egnn_edge_update_fwd(desc, graph: Graph, geom, weights, x, e_in, e_out=None,
 def egnn_edge_update_bwd(desc, graph: Graph, geom, weights, x, buffers, grad_e_out, grad_x=None, grad_w=None):
     """Gradients of <grad_e_out, e_out> w.r.t. x and the packed weights (that w.r.t. e_in is grad_e_out)."""
     lib = _lib.load()
+    K, _ = _check_layer_args(desc, graph, geom, weights, x)
+    _check_buffers(desc, graph, buffers, train=True, bwd=True)
+    _expect(grad_e_out, "grad_e_out", torch.float32, (graph.n_edges, K, desc.C))
     if grad_x is None:
-        grad_x = torch.empty((graph.n_src,) + tuple(x.shape[1:]), dtype=torch.float32, device=x.device)
+        grad_x = torch.empty((graph.n_src, K, desc.C), dtype=torch.float32, device=x.device)
     if grad_w is None:
         grad_w = torch.empty(egnn_layer_weight_count(desc), dtype=torch.float32, device=x.device)
+    _expect(grad_x, "grad_x", torch.float32, (graph.n_src, K, desc.C))
+    _expect(grad_w, "grad_w", torch.float32, (egnn_layer_weight_count(desc),))
     g = graph.c_struct()
     _lib.check("egnn_edge_update_bwd", lib.egnn_edge_update_bwd(
         ct.byref(desc), ct.byref(g), _ptr(geom), _ptr(weights), _ptr(x), _ptr(buffers.saved), _ptr(grad_e_out),
@@ -301,8 +377,22 @@ def egnn_hblocks(lmax, C, w_edge, w_node, edge_irreps, node_irreps, shell_l=(0, 
     lib = _lib.load()
     h = _hdesc(lmax, C, shell_l, storage)
     n_orb = sum(2 * l + 1 for l in shell_l)
+    if storage not in _STORAGE:
+        raise ValueError(f"unknown storage type {storage}")
+    rows = egnn_hblocks_label_rows(lmax, C, shell_l, storage)
+    if rows <= 0:
+        raise ValueError("invalid decode description")
+    K = (lmax + 1) ** 2
+    if edge_irreps is None and node_irreps is None:
+        raise ValueError("edge_irreps or node_irreps is required")
     E = 0 if edge_irreps is None else edge_irreps.shape[0]
     N = 0 if node_irreps is None else node_irreps.shape[0]
+    if E:
+        _expect(edge_irreps, "edge_irreps", _STORAGE[storage], (E, K, C))
+        _expect(w_edge, "w_edge", torch.float32, (rows * C,))
+    if N:
+        _expect(node_irreps, "node_irreps", _STORAGE[storage], (N, K, C))
+        _expect(w_node, "w_node", torch.float32, (rows * C,))
     dev = (edge_irreps if edge_irreps is not None else node_irreps).device
     he = torch.empty((max(E, 1), n_orb, n_orb), dtype=torch.float32, device=dev)
     hn = torch.empty((max(N, 1), n_orb, n_orb), dtype=torch.float32, device=dev)
@@ -358,6 +448,8 @@ def egnn_orbital_layout(basis: Basis, mol_ptr, species):
     """Orbitals of a batch (mol_ptr [n_mols+1], species [n_atoms], int32 on the GPU) and
     the count of invalid structures and element indices (int64 [1] on the GPU)."""
     lib = _lib.load()
+    _expect(mol_ptr, "mol_ptr", torch.int32, (None,), min_rows=1)
+    _expect(species, "species", torch.int32, (None,))
     dev = species.device
     n_mols, n_atoms = mol_ptr.numel() - 1, species.numel()
     o = Orbitals(mol_ptr, species,
@@ -378,6 +470,9 @@ def egnn_matrix_to_label(basis: Basis, orbitals: Orbitals, graph, H, edges=True,
     (fp32, flat, mat_off[-1] entries) and the count of skipped blocks."""
     lib = _lib.load()
     n_lab = egnn_label_width(basis)
+    if n_lab <= 0:
+        raise ValueError("invalid basis")
+    _expect(H, "H", torch.float32, (None,))
     dev = H.device
     E = graph.n_edges if (graph is not None and edges) else 0
     he = torch.empty((max(E, 1), n_lab), dtype=torch.float32, device=dev)
@@ -395,10 +490,18 @@ def egnn_label_to_matrix(basis: Basis, orbitals: Orbitals, graph, h_edge, h_node
     """Writes the blocks of h_edge / h_node (either may be None) into H (zeros of
     h_elems = mat_off[-1] entries when not given); returns (H, skipped count)."""
     lib = _lib.load()
+    n_lab = egnn_label_width(basis)
+    if n_lab <= 0:
+        raise ValueError("invalid basis")
+    if h_edge is not None and graph is not None:
+        _expect(h_edge, "h_edge", torch.float32, (graph.n_edges, n_lab))
+    if h_node is not None:
+        _expect(h_node, "h_node", torch.float32, (orbitals.n_atoms, n_lab))
     dev = orbitals.species.device
     if H is None:
         n = int(orbitals.mat_off[-1].item()) if h_elems is None else int(h_elems)
         H = torch.zeros(max(n, 1), dtype=torch.float32, device=dev)[:n]
+    _expect(H, "H", torch.float32, (None,))
     skipped = torch.empty(1, dtype=torch.int64, device=dev)
     g = graph.c_struct() if (graph is not None and h_edge is not None) else None
     o = orbitals.c_struct()

@@ -255,3 +255,107 @@ def test_label_calls_reject_bad_arguments(lib):
     assert lib.egnn_label_to_matrix(ct.byref(b), ct.byref(o), None, None, 16, 16, 0, None, None) == _lib.EGNN_E_ARG
     assert lib.egnn_matrix_to_label(ct.byref(b), ct.byref(o), None, None, 9, None, 16, None,
                                     None) == _lib.EGNN_E_ARG
+
+
+def _cpu_graph(n_dst=6, n_src=8, E=20):
+    import torch
+    import equivariant_gnn_electronic_amd as eg
+    rp = torch.linspace(0, E, n_dst + 1).round().to(torch.int32)
+    return eg.Graph(n_dst, n_src, E, rp, torch.zeros(E, dtype=torch.int32), torch.zeros((E, 3), dtype=torch.int8),
+                    torch.ones((E, 3)), torch.ones(E), torch.zeros(n_src + 1, dtype=torch.int32),
+                    torch.zeros(E, dtype=torch.int32))
+
+
+def _layer_args(storage=0, lmax=2, mmax=2, C=16):
+    import torch
+    import equivariant_gnn_electronic_amd as eg
+    g = _cpu_graph()
+    desc = eg.layer_desc(lmax, mmax, C, 8, 5.0, storage)
+    K = (lmax + 1) ** 2
+    dt = torch.bfloat16 if storage else torch.float32
+    geom = torch.zeros((g.n_edges, eg.egnn_geom_stride(desc)))
+    w = torch.zeros(eg.egnn_layer_weight_count(desc))
+    x = torch.zeros((g.n_src, K, C), dtype=dt)
+    return eg, g, desc, geom, w, x, K, C, dt
+
+
+def test_binding_rejects_wrong_dtypes_and_shapes(lib):
+    """The binding is the only guard against a buffer of the wrong type or size
+    (the C ABI sees plain pointers): every wrapper raises before any call."""
+    import torch
+    eg, g, desc, geom, w, x, K, C, dt = _layer_args()
+    buf = eg.LayerBuffers(desc, g, train=True)
+    G = torch.zeros((g.n_dst, K, C))
+    with pytest.raises(ValueError, match="grad_out"):
+        eg.egnn_layer_bwd(desc, g, geom, w, x, buf, G.to(torch.bfloat16))
+    with pytest.raises(ValueError, match="grad_out"):
+        eg.egnn_layer_bwd(desc, g, geom, w, x, buf, G[:-1].contiguous())
+    with pytest.raises(ValueError, match="grad_x"):
+        eg.egnn_layer_bwd(desc, g, geom, w, x, buf, G, grad_x=torch.zeros((g.n_dst, K, C)))
+    with pytest.raises(ValueError, match="grad_w"):
+        eg.egnn_layer_bwd(desc, g, geom, w, x, buf, G, grad_w=torch.zeros(w.numel() - 1))
+    with pytest.raises(ValueError, match="train=True"):
+        eg.egnn_layer_bwd(desc, g, geom, w, x, eg.LayerBuffers(desc, g, train=False), G)
+    with pytest.raises(ValueError, match="weights"):
+        eg.egnn_layer_fwd(desc, g, geom, w[:-1].contiguous(), x)
+    with pytest.raises(ValueError, match="weights"):
+        eg.egnn_layer_fwd(desc, g, geom, w.double(), x)
+    with pytest.raises(ValueError, match="x "):
+        eg.egnn_layer_fwd(desc, g, geom, w, x[:-1].contiguous())
+    with pytest.raises(ValueError, match="x "):
+        eg.egnn_layer_fwd(desc, g, geom, w, x.to(torch.bfloat16))
+    with pytest.raises(ValueError, match="geom"):
+        eg.egnn_layer_fwd(desc, g, geom[:-1].contiguous(), w, x)
+    with pytest.raises(ValueError, match="x_out"):
+        eg.egnn_layer_fwd(desc, g, geom, w, x, x_out=torch.zeros((g.n_dst, K, C + 1)))
+    with pytest.raises(ValueError, match="contiguous"):
+        eg.egnn_layer_fwd(desc, g, geom, w, torch.zeros((g.n_src, C, K)).transpose(1, 2))
+    # edge-update block: e_in / e_out in the storage type, grad_e_out fp32
+    e = torch.zeros((g.n_edges, K, C))
+    with pytest.raises(ValueError, match="e_in"):
+        eg.egnn_edge_update_fwd(desc, g, geom, w, x, e.to(torch.bfloat16))
+    with pytest.raises(ValueError, match="e_out"):
+        eg.egnn_edge_update_fwd(desc, g, geom, w, x, e, e_out=e[:-1].contiguous())
+    with pytest.raises(ValueError, match="grad_e_out"):
+        eg.egnn_edge_update_bwd(desc, g, geom, w, x, buf, e.to(torch.bfloat16))
+    # bf16 storage: x must be bf16, grads stay fp32
+    eg, g, desc16, geom16, w16, x16, K, C, dt = _layer_args(storage=1)
+    with pytest.raises(ValueError, match="x "):
+        eg.egnn_layer_fwd(desc16, g, geom16, w16, x16.float())
+    buf16 = eg.LayerBuffers(desc16, g, train=True)
+    with pytest.raises(ValueError, match="grad_out"):
+        eg.egnn_layer_bwd(desc16, g, geom16, w16, x16, buf16, torch.zeros((g.n_dst, K, C), dtype=torch.bfloat16))
+    # everything right but on the host: the device check fires last
+    with pytest.raises(ValueError, match="GPU"):
+        eg.egnn_layer_bwd(desc16, g, geom16, w16, x16, buf16, torch.zeros((g.n_dst, K, C)))
+
+
+def test_binding_rejects_wrong_decode_and_label_buffers(lib):
+    import torch
+    import equivariant_gnn_electronic_amd as eg
+    lmax, C = 4, 16
+    K = (lmax + 1) ** 2
+    rows = eg.egnn_hblocks_label_rows(lmax, C)
+    assert rows == 9 + 17 + 13 + 5 + 1
+    we = torch.zeros(rows * C)
+    eo = torch.zeros((10, K, C))
+    xo = torch.zeros((4, K, C))
+    with pytest.raises(ValueError, match="edge_irreps"):
+        eg.egnn_hblocks(lmax, C, we, we, eo.to(torch.bfloat16), xo)
+    with pytest.raises(ValueError, match="node_irreps"):
+        eg.egnn_hblocks(lmax, C, we, we, eo, xo.to(torch.bfloat16))
+    with pytest.raises(ValueError, match="edge_irreps"):
+        eg.egnn_hblocks(lmax, C, we, we, eo, xo, storage=eg.EGNN_BF16)
+    with pytest.raises(ValueError, match="w_edge"):
+        eg.egnn_hblocks(lmax, C, we[:-1].contiguous(), we, eo, xo)
+    with pytest.raises(ValueError, match="edge_irreps"):
+        eg.egnn_hblocks(lmax, C, we, we, torch.zeros((10, K, C + 8)), xo)
+    with pytest.raises(ValueError, match="GPU"):
+        eg.egnn_hblocks(lmax, C, we, we, eo, xo)
+    basis = eg.Basis((0, 1), (0b11, 0b01))
+    with pytest.raises(ValueError, match="species"):
+        eg.egnn_orbital_layout(basis, torch.tensor([0, 2], dtype=torch.int32), torch.tensor([0, 1]))
+    with pytest.raises(ValueError, match="pos"):
+        eg.egnn_build_graph(torch.zeros((4, 3), dtype=torch.float32), 4, [0, 0, 0], [9, 9, 9], 7, 5.0)
+    with pytest.raises(ValueError, match="n_dst"):
+        eg.egnn_build_graph(torch.zeros((4, 3), dtype=torch.float64), 5, [0, 0, 0], [9, 9, 9], 7, 5.0)

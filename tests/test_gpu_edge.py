@@ -4,6 +4,8 @@ Tolerances as for the node block: fp32 <= 1e-4 normwise relative and max-abs
 <= 1e-4 * max|ref|; bf16 storage <= 2e-2 against the oracle on the
 bf16-rounded inputs and weights.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -48,9 +50,24 @@ def _oracle_edges_in_gpu_order(r):
     return og
 
 
-@pytest.mark.parametrize("name,tol", [("tiny", 1e-4), ("tiny_l4", 1e-4), ("tiny_stack", 2e-2)])
+EDGE_CASES = {
+    "tiny": synth.CONFIGS["tiny"],
+    "tiny_l4": synth.CONFIGS["tiny_l4"],
+    "tiny_stack": synth.CONFIGS["tiny_stack"],
+    "tiny_l6": synth.CONFIGS["tiny_l6"],
+    # degree 8 (g-orbital labels), fp32 and bf16 channel pairs
+    "tiny_l8": dataclasses.replace(synth.CONFIGS["tiny"], name="tiny_l8", lmax=8, mmax=2, C=16),
+    "tiny_l8_bf16": dataclasses.replace(synth.CONFIGS["tiny"], name="tiny_l8_bf16", lmax=8, mmax=1, C=128,
+                                        storage="bf16"),
+    "tiny_l6_bf16": dataclasses.replace(synth.CONFIGS["tiny"], name="tiny_l6_bf16", lmax=6, mmax=2, C=32,
+                                        storage="bf16"),
+}
+
+
+@pytest.mark.parametrize("name,tol", [("tiny", 1e-4), ("tiny_l4", 1e-4), ("tiny_stack", 2e-2), ("tiny_l6", 1e-4),
+                                      ("tiny_l8", 1e-4), ("tiny_l8_bf16", 2e-2), ("tiny_l6_bf16", 2e-2)])
 def test_edge_update_forward_backward(dev, name, tol):
-    cfg = synth.CONFIGS[name]
+    cfg = EDGE_CASES[name]
     print(f"[edge] {name}", flush=True)
     r = _setup(cfg, dev)
     eo, buf = eg.egnn_edge_update_fwd(r["desc"], r["g"], r["geom"], r["wt"], r["xt"], r["et"])
@@ -61,6 +78,8 @@ def test_edge_update_forward_backward(dev, name, tol):
     x64, w64, e64 = r["x"].astype(np.float64), r["w"].astype(np.float64), r["e"].astype(np.float64)
     fwd = olayer.edge_update_forward(og, x64, e64, w64, desc_of(cfg))
     assert_close(eo.float().cpu().numpy(), fwd["e_out"], tol, "e_out")
+    if cfg.storage == "f32":
+        assert_close(eo.cpu().numpy() - e64, fwd["e_out"] - e64, tol, "e_out - e")
     dx, de, dw = olayer.edge_update_backward(og, x64, w64, desc_of(cfg), fwd, Ge.astype(np.float64))
     assert_close(gx.cpu().numpy(), dx, tol, "grad x")
     o = 0

@@ -5,6 +5,8 @@ Wigner rows and radial basis <= 1e-6 absolute; fp32 layer outputs and
 gradients <= 1e-4 normwise relative and max-abs <= 1e-4 * max|ref|;
 bf16 storage <= 2e-2 normwise against the oracle on the bf16-rounded inputs.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -99,9 +101,16 @@ def _oracle_geom_rows(vec, dist, cfg):
     return np.concatenate(parts, axis=1), olayer.radial_basis(dist, d)
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_l4", "hfo2"])
+GEOM_CASES = {n: synth.CONFIGS[n] for n in ("tiny", "tiny_l4", "tiny_l6", "hfo2", "hfo2_l6", "hfo2_l8")}
+GEOM_CASES["tiny_l8"] = dataclasses.replace(synth.CONFIGS["tiny"], name="tiny_l8", lmax=8, mmax=2, C=16)
+GEOM_CASES["tiny_l8_m1"] = dataclasses.replace(synth.CONFIGS["tiny"], name="tiny_l8_m1", lmax=8, mmax=1, C=16)
+
+
+@pytest.mark.parametrize("name", list(GEOM_CASES))
 def test_edge_geom(dev, name):
-    cfg = synth.CONFIGS[name]
+    """Wigner rows |m| <= mmax of every degree (to lmax 8) and the radial basis
+    against the oracle's least-squares Wigner-D, 1e-6 absolute."""
+    cfg = GEOM_CASES[name]
     s = synth.make_structure(cfg)
     g = gpu_graph(s, dev)
     desc = eg.layer_desc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut)
@@ -233,9 +242,13 @@ def _run_stack(cfg, dev, g, geom, x_t, ws):
 
 def test_layer_stack_bf16_tiny(dev):
     """Three layers with bf16 storage against the oracle on the same bf16 inputs."""
+    from tests.test_gpu_variants import _message_scaled
     cfg = synth.CONFIGS["tiny_stack"]
     s = synth.make_structure(cfg)
     x, ws = synth.make_layer_inputs(cfg)
+    # weights (but w_att) doubled: the three layers' messages are then ~20% of
+    # x', so x' - x is compared well above the bf16 rounding of x' (~1% of it)
+    ws = [_message_scaled(w, cfg, 2.0) for w in ws]
     g = gpu_graph(s, dev)
     desc = eg.layer_desc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut, eg.EGNN_BF16)
     geom = eg.egnn_edge_geom(desc, g)
@@ -245,17 +258,28 @@ def test_layer_stack_bf16_tiny(dev):
     for w in ws:
         xr = olayer.layer_forward(og, xr, w.astype(np.float64), desc_of(cfg))["x_out"]
     assert_close(xo, xr, 2e-2, "3-layer bf16 x_out")
+    x_dst = x[:s.n_dst].astype(np.float64)
+    assert_close(xo - x_dst, xr - x_dst, 2e-2, "3-layer bf16 x_out - x")
 
 
 def test_layer_forward_gst_bf16_sampled_rows(dev):
     """First layer of the 8,064-atom GeSbTe-like cell (bf16 storage, C 128) on sampled rows."""
     cfg = synth.CONFIGS["gst"]
-    r = _gpu_forward(cfg, dev)
+    r = _gpu_forward(cfg, dev, edge_out=True)
     rows = sample_rows(r["s"].n_dst, 120, 7)
     og = oracle_graph(r["s"], rows=rows)
     xo_ref, _ = olayer.layer_forward_rows(og, r["x"].astype(np.float64), r["w"].astype(np.float64), desc_of(cfg))
     xo = r["xo"].float().cpu().numpy()[rows]
     assert_close(xo, xo_ref, 2e-2, "gst x_out rows")
+    # the per-edge messages (no residual) of 40 of these rows, element by element
+    gg = host(r["g"])
+    sub = rows[:40]
+    og40 = oracle_graph(r["s"], rows=sub)
+    sel = np.concatenate([np.arange(gg["row_ptr"][q], gg["row_ptr"][q + 1]) for q in sub])
+    ef = olayer.edge_forward(og40, r["x"].astype(np.float64), olayer.unpack_weights(r["w"].astype(np.float64), desc_of(cfg)),
+                             desc_of(cfg), r["x"][np.repeat(sub, np.diff(og40["row_ptr"]))].astype(np.float64))
+    eo = r["eo"][torch.from_numpy(sel).to(dev)].float().cpu().numpy()
+    assert_close(eo, ef["msg"], 2e-2, "gst edge messages")
 
 
 def test_layer_forward_halo_sampled_rows(dev):
@@ -322,6 +346,7 @@ def test_layer_backward_hfo2_sampled_nodes(dev):
     dx, _ = olayer.layer_backward(og, x64, w64, desc_of(cfg), fwd, G[rows].astype(np.float64))
     where = np.searchsorted(rows, nodes)  # sampled atoms sit at these relabelled positions
     assert_close(gx[nodes], dx[where], 1e-4, "grad x of sampled atoms")
+    assert_close(gx[nodes] - G[nodes], dx[where] - G[nodes], 1e-4, "grad x of sampled atoms - G")
 
 
 def test_weight_gradient_hfo2_directional(dev):
@@ -387,6 +412,8 @@ def _sampled_atom_grads(cfg, r, dev, n_nodes, seed, tol):
     fwd = olayer.layer_forward(og, x64, w64, desc_of(cfg))
     dx, _ = olayer.layer_backward(og, x64, w64, desc_of(cfg), fwd, G[rows].astype(np.float64))
     assert_close(gx[nodes], dx[np.searchsorted(rows, nodes)], tol, "grad x of sampled atoms")
+    assert_close(gx[nodes] - G[nodes], dx[np.searchsorted(rows, nodes)] - G[nodes], tol,
+                 "grad x of sampled atoms - G")
 
 
 def test_layer_backward_gst_bf16_sampled_nodes(dev):
@@ -421,3 +448,111 @@ def test_weight_gradient_gst_bf16_directional(dev):
     fd = (loss(r["wt"] + eps * v) - loss(r["wt"] - eps * v)) / (2 * eps)
     an = float((gw.double() * v.double()).sum())
     assert abs(fd - an) <= 2e-2 * abs(an), (fd, an)
+
+
+def _masked_cotangent(cfg, n_dst, rows):
+    """The seeded cotangent G kept on `rows` only, zero on every other row."""
+    G = synth.make_cotangent(cfg, n_dst)
+    Gm = np.zeros_like(G)
+    Gm[rows] = G[rows]
+    return Gm
+
+
+def _oracle_backward_on_rows(cfg, s, x, w, rows, G):
+    """Exact oracle gradients of <G, x'> when G is zero outside `rows`.
+
+    Every term of the backward starts from G_d of an edge's destination, so
+    only the edges of `rows` contribute: the oracle runs the layer on those
+    rows alone (relabelled to destinations 0..len(rows)-1, every atom still a
+    source) and its gradients are the full-size ones.  Returns dx in the
+    original atom order and the packed weight gradient."""
+    perm, og = _relabelled_rows(s, rows)
+    x64, w64 = x[perm].astype(np.float64), w.astype(np.float64)
+    d = desc_of(cfg)
+    fwd = olayer.layer_forward(og, x64, w64, d)
+    dxp, dw = olayer.layer_backward(og, x64, w64, d, fwd, G[rows].astype(np.float64))
+    dx = np.empty_like(dxp)
+    dx[perm] = dxp
+    return dx, dw
+
+
+def _compare_full_backward(cfg, r, dev, rows, tol):
+    s = r["s"]
+    G = _masked_cotangent(cfg, s.n_dst, rows)
+    gx, gw = eg.egnn_layer_bwd(r["desc"], r["g"], r["geom"], r["wt"], r["xt"], r["buf"], torch.from_numpy(G).to(dev))
+    torch.cuda.synchronize()
+    gx, gw = gx.cpu().numpy(), gw.cpu().numpy()
+    dx, dw = _oracle_backward_on_rows(cfg, s, r["x"], r["w"], rows, G)   # x, w already storage-rounded
+    # the message part of grad x, without the residual [G; 0] that both carry
+    resid = np.zeros_like(dx)
+    resid[:s.n_dst] = G
+    assert_close(gx - resid, dx - resid, tol, "grad x (message part)")
+    assert_close(gx, dx, tol, "grad x")
+    o = 0
+    for bname, shape in synth.layer_weight_sizes(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf):
+        n = int(np.prod(shape))
+        assert_close(gw[o:o + n], dw[o:o + n], tol, f"grad {bname}")
+        o += n
+
+
+def test_layer_backward_hfo2_full_size_masked_rows(dev):
+    """The training step's backward launch at full size (544k edges: every split-K
+    split of the weight-gradient products, two-level column sums of the attention
+    and radial-weight gradients) with G kept on 200 rows spread over the row
+    range: every weight-gradient block and grad x of every atom against the
+    oracle's exact values, element by element at the fp32 bar."""
+    cfg = synth.CONFIGS["train"]
+    r = _gpu_forward(cfg, dev, train=True)
+    rows = np.unique(np.linspace(0, r["s"].n_dst - 1, 200).round().astype(np.int64))
+    _compare_full_backward(cfg, r, dev, rows, 1e-4)
+
+
+def test_layer_backward_gst_bf16_full_size_masked_rows(dev):
+    """The same on the 8,064-atom GeSbTe-like layer (bf16 storage, C 128, 1.1M
+    edges: the transposed-read bf16 split-K products and their fold), at the
+    bf16 bar against the oracle on the bf16-rounded inputs."""
+    cfg = synth.CONFIGS["gst"]
+    r = _gpu_forward(cfg, dev, train=True)
+    rows = np.unique(np.linspace(0, r["s"].n_dst - 1, 128).round().astype(np.int64))
+    _compare_full_backward(cfg, r, dev, rows, 2e-2)
+
+
+def test_hblocks_gst_bf16_c128_sampled(dev):
+    """The decode that the 8,064-atom training step runs: bf16 irreps with C 128
+    (the GeSbTe-like layer's own edge messages and outputs, 1.1M edges) into
+    13 x 13 blocks, on 3,000 sampled edges and 300 atoms against the oracle's
+    Label -> Matrix on the same bf16 values (fp32 arithmetic, so 1e-5)."""
+    cfg = synth.CONFIGS["gst"]
+    r = _gpu_forward(cfg, dev, edge_out=True)
+    we, wn = synth.make_decode_weights(cfg)
+    wet = torch.from_numpy(np.concatenate(we)).to(dev)
+    wnt = torch.from_numpy(np.concatenate(wn)).to(dev)
+    he, hn = eg.egnn_hblocks(cfg.lmax, cfg.C, wet, wnt, r["eo"], r["xo"], storage=eg.EGNN_BF16)
+    torch.cuda.synchronize()
+    ei = torch.from_numpy(sample_rows(r["g"].n_edges, 3000, 15)).to(dev)
+    ni = torch.from_numpy(sample_rows(r["s"].n_dst, 300, 16)).to(dev)
+    eo = r["eo"][ei].float().cpu().numpy().astype(np.float64)
+    xo = r["xo"][ni].float().cpu().numpy().astype(np.float64)
+    assert_close(he[ei].cpu().numpy(), odec.hblocks(eo, we), 1e-5, "edge blocks")
+    assert_close(hn[ni].cpu().numpy(), odec.hblocks(xo, wn), 1e-5, "on-site blocks")
+
+
+@pytest.mark.parametrize("C,storage", [(32, "f32"), (32, "bf16"), (256, "f32"), (256, "bf16"), (8, "bf16")])
+def test_hblocks_channel_counts(dev, C, storage):
+    """Decode instantiations at C 32 and 256 (and bf16 at C 8): seeded irreps on
+    the 64-atom cell's edge count, every block against the oracle at 1e-5."""
+    rng = np.random.default_rng(C + (storage == "bf16"))
+    E, N, lmax = 2836, 64, 4
+    K = (lmax + 1) ** 2
+    eo = synth.round_storage(rng.standard_normal((E, K, C)), storage)
+    xo = synth.round_storage(rng.standard_normal((N, K, C)), storage)
+    cfg = dataclasses.replace(synth.CONFIGS["tiny_l4"], C=C)
+    we, wn = synth.make_decode_weights(cfg)
+    dt = torch.bfloat16 if storage == "bf16" else torch.float32
+    st = eg.EGNN_BF16 if storage == "bf16" else eg.EGNN_F32
+    he, hn = eg.egnn_hblocks(lmax, C, torch.from_numpy(np.concatenate(we)).to(dev),
+                             torch.from_numpy(np.concatenate(wn)).to(dev),
+                             torch.from_numpy(eo).to(dev).to(dt), torch.from_numpy(xo).to(dev).to(dt), storage=st)
+    torch.cuda.synchronize()
+    assert_close(he.cpu().numpy(), odec.hblocks(eo.astype(np.float64), we), 1e-5, "edge blocks")
+    assert_close(hn.cpu().numpy(), odec.hblocks(xo.astype(np.float64), wn), 1e-5, "on-site blocks")

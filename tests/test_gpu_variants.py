@@ -73,8 +73,25 @@ def _graph(struct, dev):
     return eg.egnn_build_graph(pos, struct.n_dst, lo, box, struct.periodic_mask, struct.r_cut)
 
 
+def _message_scaled(w, cfg, f=4.0):
+    """Weights with every block but w_att scaled by f (a power of two, so bf16
+    values stay exact).  With f = 4 the aggregated message is about as large as
+    the residual x, so comparing x' - x tests the message itself even after the
+    bf16 rounding of x' (which is then ~0.2% of the message instead of 5-15%)."""
+    w = w.copy()
+    o = 0
+    for name, shape in synth.layer_weight_sizes(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf):
+        n = int(np.prod(shape))
+        if name != "w_att":
+            w[o:o + n] *= f
+        o += n
+    return w
+
+
 def _run(cfg, s, dev, backward):
     x, ws = synth.make_layer_inputs(cfg)
+    if cfg.storage == "bf16":
+        ws = [_message_scaled(ws[0], cfg)]
     g = _graph(s, dev)
     storage = eg.EGNN_BF16 if cfg.storage == "bf16" else eg.EGNN_F32
     desc = eg.layer_desc(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf, cfg.r_cut, storage)
@@ -84,8 +101,8 @@ def _run(cfg, s, dev, backward):
         xt = xt.to(torch.bfloat16)
     wt = torch.from_numpy(ws[0]).to(dev)
     buf = eg.LayerBuffers(desc, g, train=backward)
-    (xo, _), buf = eg.egnn_layer_fwd(desc, g, geom, wt, xt, buffers=buf)
-    out = dict(g=g, x=x, w=ws[0], xo=xo.float().cpu().numpy())
+    (xo, eo), buf = eg.egnn_layer_fwd(desc, g, geom, wt, xt, edge_out=True, buffers=buf)
+    out = dict(g=g, x=x, w=ws[0], xo=xo.float().cpu().numpy(), eo=eo.float().cpu().numpy())
     if backward:
         G = synth.make_cotangent(cfg, s.n_dst)
         gx, gw = eg.egnn_layer_bwd(desc, g, geom, wt, xt, buf, torch.from_numpy(G).to(dev))
@@ -99,10 +116,18 @@ def _check(cfg, s, r, backward):
     x64, w64 = r["x"].astype(np.float64), r["w"].astype(np.float64)
     fwd = olayer.layer_forward(og, x64, w64, desc_of(cfg))
     tol = 2e-2 if cfg.storage == "bf16" else 1e-4
+    x_dst = x64[:s.n_dst]
     assert_close(r["xo"], fwd["x_out"], tol, "x_out")
+    # the aggregated message and the per-edge messages, without the residual
+    assert_close(r["xo"] - x_dst, fwd["x_out"] - x_dst, tol, "x_out - x")
+    if len(og["src"]):
+        assert_close(r["eo"], fwd["edge_out"], tol, "edge_out")
     if backward:
         dx, dw = olayer.layer_backward(og, x64, w64, desc_of(cfg), fwd, r["G"].astype(np.float64))
+        resid = np.zeros_like(dx)
+        resid[:s.n_dst] = r["G"]
         assert_close(r["gx"], dx, tol, "grad x")
+        assert_close(r["gx"] - resid, dx - resid, tol, "grad x - [G; 0]")
         o = 0
         for name, shape in synth.layer_weight_sizes(cfg.lmax, cfg.mmax, cfg.C, cfg.n_rbf):
             n = int(np.prod(shape))
