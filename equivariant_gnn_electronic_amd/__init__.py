@@ -389,10 +389,12 @@ def egnn_hblocks(lmax, C, w_edge, w_node, edge_irreps, node_irreps, shell_l=(0, 
     N = 0 if node_irreps is None else node_irreps.shape[0]
     if E:
         _expect(edge_irreps, "edge_irreps", _STORAGE[storage], (E, K, C))
-        _expect(w_edge, "w_edge", torch.float32, (rows * C,))
+        _expect(w_edge.reshape(-1) if isinstance(w_edge, torch.Tensor) else w_edge, "w_edge", torch.float32,
+                (rows * C,))
     if N:
         _expect(node_irreps, "node_irreps", _STORAGE[storage], (N, K, C))
-        _expect(w_node, "w_node", torch.float32, (rows * C,))
+        _expect(w_node.reshape(-1) if isinstance(w_node, torch.Tensor) else w_node, "w_node", torch.float32,
+                (rows * C,))
     dev = (edge_irreps if edge_irreps is not None else node_irreps).device
     he = torch.empty((max(E, 1), n_orb, n_orb), dtype=torch.float32, device=dev)
     hn = torch.empty((max(N, 1), n_orb, n_orb), dtype=torch.float32, device=dev)

@@ -45,19 +45,28 @@ def _compile(src):
     return obj, err
 
 
-def build(verbose=True):
-    """Compile and link; returns the library path.  Always recompiles."""
+def build(verbose=True, only=None):
+    """Compile and link; returns the library path.  Always recompiles every
+    source, or only the listed ones (their objects from an earlier build are
+    reused for the rest)."""
     if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
         raise RuntimeError("hipcc not found")
     os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    todo = SOURCES if not only else [s for s in SOURCES if s in only]
+    if only and len(todo) != len(set(only)):
+        raise ValueError(f"unknown sources: {sorted(set(only) - set(SOURCES))}")
+    jobs = min(len(todo), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    for (obj, err), src in zip(results, SOURCES):
+        results = list(ex.map(_compile, todo))
+    for (obj, err), src in zip(results, todo):
         if err.strip() and verbose:
             print(f"[{src}]\n{err}", file=sys.stderr)
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"objects missing (run a full build): {missing}")
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in results]]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
@@ -68,4 +77,7 @@ def build(verbose=True):
 
 
 if __name__ == "__main__":
-    build()
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--only", nargs="*", help="recompile only these csrc/*.hip files, then link")
+    build(only=ap.parse_args().only)

@@ -359,3 +359,4 @@ def test_binding_rejects_wrong_decode_and_label_buffers(lib):
         eg.egnn_build_graph(torch.zeros((4, 3), dtype=torch.float32), 4, [0, 0, 0], [9, 9, 9], 7, 5.0)
     with pytest.raises(ValueError, match="n_dst"):
         eg.egnn_build_graph(torch.zeros((4, 3), dtype=torch.float64), 5, [0, 0, 0], [9, 9, 9], 7, 5.0)
+
