@@ -16,7 +16,7 @@ import torch
 from . import _lib
 from ._lib import EGNN_BF16, EGNN_F32, EgnnError
 
-__all__ = ["Graph", "layer_desc", "egnn_build_graph", "egnn_edge_geom", "egnn_geom_stride",
+__all__ = ["Graph", "layer_desc", "egnn_build_graph", "egnn_build_graph_noalloc", "egnn_edge_geom", "egnn_geom_stride",
            "egnn_layer_weight_count", "egnn_layer_sizes", "egnn_layer_fwd", "egnn_layer_bwd",
            "egnn_hblocks", "egnn_hblocks_label_rows", "egnn_timing_enable", "egnn_timing_collect",
            "egnn_timing_reset", "GraphBuilder", "LayerBuffers", "EgnnError", "EGNN_F32", "EGNN_BF16",
@@ -159,6 +159,41 @@ def egnn_build_graph(pos, n_dst, lo, box, periodic_mask, r_cut, capacity=None):
         return Graph(n_dst, n_src, E, row_ptr, a["src"][:E], a["shift"][:E], a["vec"][:E], a["dist"][:E],
                      a["src_ptr"], a["src_perm"][:E])
     raise RuntimeError("egnn_build_graph: edge count changed between the two passes")
+
+
+def egnn_build_graph_noalloc(pos, n_dst, lo, box, periodic_mask, r_cut, capacity=None):
+    """egnn_build_graph through the allocation-free entry point (the library's
+    static workspace instead of one from torch).  The output arrays are still
+    the caller's: they are allocated here, as in egnn_build_graph."""
+    lib = _lib.load()
+    _expect(pos, "pos", torch.float64, (None, 3))
+    dev = pos.device
+    n_src = pos.shape[0]
+    if not 0 <= n_dst <= n_src:
+        raise ValueError(f"n_dst ({n_dst}) must lie in [0, n_src = {n_src}]")
+    row_ptr = torch.empty(n_dst + 1, dtype=torch.int32, device=dev)
+    src_ptr = torch.empty(n_src + 1, dtype=torch.int32, device=dev)
+    cap = 0 if capacity is None else int(capacity)
+    lo3, box3 = _d3(lo), _d3(box)
+    for _ in range(2):
+        a = {f: torch.empty(sh, dtype=dt, device=dev) for f, sh, dt in (
+            ("src", (max(cap, 1),), torch.int32), ("shift", (max(cap, 1), 3), torch.int8),
+            ("vec", (max(cap, 1), 3), torch.float32), ("dist", (max(cap, 1),), torch.float32),
+            ("src_perm", (max(cap, 1),), torch.int32))}
+        g = _lib.EgnnGraph()
+        g.n_dst, g.n_src, g.capacity = n_dst, n_src, cap
+        g.row_ptr, g.src_ptr = row_ptr.data_ptr(), src_ptr.data_ptr()
+        for f in a:
+            setattr(g, f, a[f].data_ptr() if cap > 0 else None)
+        st = lib.egnn_build_graph_noalloc(_ptr(pos), lo3, box3, periodic_mask, float(r_cut), ct.byref(g), _stream())
+        if st == _lib.EGNN_E_CAPACITY:
+            cap = int(g.n_edges)
+            continue
+        _lib.check("egnn_build_graph_noalloc", st)
+        E = int(g.n_edges)
+        return Graph(n_dst, n_src, E, row_ptr, a["src"][:E], a["shift"][:E], a["vec"][:E], a["dist"][:E],
+                     src_ptr, a["src_perm"][:E])
+    raise RuntimeError("egnn_build_graph_noalloc: edge count changed between the two passes")
 
 
 class GraphBuilder:

@@ -15,6 +15,8 @@
 // fill order use integer atomics.
 #pragma clang fp contract(off)
 
+#include <mutex>
+
 #include "common.h"
 #include "timing.h"
 
@@ -340,10 +342,76 @@ extern "C" egnn_status egnn_build_graph_workspace(int32_t n_dst, int32_t n_src, 
   return EGNN_OK;
 }
 
+namespace egnn {
+namespace {
+
+// Scratch of the allocation-free variant: one copy per GPU, held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (in host
+// code the name is a host-side stand-in); it asks the runtime for the
+// device's address once per device and uses that address only.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices];
+
+// Address of the current device's scratch (looked up on its first use there).
+egnn_status noalloc_scratch(void **out) {
+  int dev = -1;
+  EGNN_TRY_HIP(hipGetDevice(&dev));
+  EGNN_REQUIRE(dev >= 0 && dev < kMaxDevices, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void *p = nullptr;
+    EGNN_TRY_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    EGNN_REQUIRE(p != nullptr, "no device address for the scratch array");
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return EGNN_OK;
+}
+
+egnn_status build_graph_impl(const double *pos, const double lo[3], const double box[3], uint32_t periodic_mask,
+                             double r_cut, egnn_graph *gr, void *ws, size_t ws_bytes, hipStream_t stream);
+
+}  // namespace
+}  // namespace egnn
+
 extern "C" egnn_status egnn_build_graph(const double *pos, const double lo[3], const double box[3],
                                         uint32_t periodic_mask, double r_cut, egnn_graph *gr, void *ws,
                                         size_t ws_bytes, hipStream_t stream) {
   clear_error();
+  return build_graph_impl(pos, lo, box, periodic_mask, r_cut, gr, ws, ws_bytes, stream);
+}
+
+extern "C" egnn_status egnn_build_graph_noalloc(const double *pos, const double lo[3], const double box[3],
+                                                uint32_t periodic_mask, double r_cut, egnn_graph *gr,
+                                                hipStream_t stream) {
+  clear_error();
+  EGNN_REQUIRE(gr && lo && box, "null argument");
+  EGNN_REQUIRE(gr->n_dst >= 0 && gr->n_src >= gr->n_dst, "need 0 <= n_dst <= n_src (got %d, %d)", gr->n_dst,
+               gr->n_src);
+  EGNN_REQUIRE(gr->capacity >= 0, "negative capacity");
+  Grid g;
+  EGNN_REQUIRE(make_grid(lo, box, periodic_mask, r_cut, &g), "box and r_cut must be positive");
+  const size_t need = carve(nullptr, gr->n_dst, gr->n_src, g.n_cells, gr->capacity).bytes;
+  if (need > kNoAllocScratchBytes) {
+    set_error("needs %zu bytes of workspace; the allocation-free variant has %zu (fewer edges of capacity, "
+              "fewer atoms or cells, or egnn_build_graph with a workspace)", need, kNoAllocScratchBytes);
+    return EGNN_E_WORKSPACE;
+  }
+  void *ws = nullptr;
+  egnn_status st = noalloc_scratch(&ws);
+  if (st != EGNN_OK) return st;
+  return build_graph_impl(pos, lo, box, periodic_mask, r_cut, gr, ws, kNoAllocScratchBytes, stream);
+}
+
+namespace egnn {
+namespace {
+
+egnn_status build_graph_impl(const double *pos, const double lo[3], const double box[3], uint32_t periodic_mask,
+                             double r_cut, egnn_graph *gr, void *ws, size_t ws_bytes, hipStream_t stream) {
   EGNN_REQUIRE(gr && lo && box, "null argument");
   const int n_dst = gr->n_dst, n_src = gr->n_src;
   EGNN_REQUIRE(n_dst >= 0 && n_src >= n_dst, "need 0 <= n_dst <= n_src (got %d, %d)", n_dst, n_src);
@@ -429,3 +497,6 @@ extern "C" egnn_status egnn_build_graph(const double *pos, const double lo[3], c
   EGNN_CHECK_LAUNCH();
   return EGNN_OK;
 }
+
+}  // namespace
+}  // namespace egnn

@@ -124,6 +124,22 @@ egnn_status egnn_build_graph(const double *pos, const double lo[3] /*host*/,
                              egnn_graph *g /*host struct, device arrays*/, void *ws, size_t ws_bytes,
                              hipStream_t stream);
 
+/* Allocation-free egnn_build_graph, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and results as egnn_build_graph (the
+ * capacity protocol included), without the workspace: the library's own
+ * 32 MiB static device array serves as workspace, one copy per GPU it runs
+ * on, held until the process ends.  The need is what
+ * egnn_build_graph_workspace reports (about 8 bytes per edge of capacity,
+ * 28 per atom and 12 per cell); a larger need returns EGNN_E_WORKSPACE
+ * before any launch.  Calls on one GPU share that array, so calls that
+ * overlap on one GPU (several streams or threads) race: the caller
+ * serialises them.  The call's kernels clear whatever must start at zero.
+ * Synchronises once to read the edge count, like egnn_build_graph. */
+egnn_status egnn_build_graph_noalloc(const double *pos, const double lo[3] /*host*/,
+                                     const double box[3] /*host*/, uint32_t periodic_mask, double r_cut,
+                                     egnn_graph *g /*host struct, device arrays*/, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Layer description
  * ------------------------------------------------------------------------- */

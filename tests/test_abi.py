@@ -360,3 +360,17 @@ def test_binding_rejects_wrong_decode_and_label_buffers(lib):
     with pytest.raises(ValueError, match="n_dst"):
         eg.egnn_build_graph(torch.zeros((4, 3), dtype=torch.float64), 5, [0, 0, 0], [9, 9, 9], 7, 5.0)
 
+
+def test_noalloc_graph_rejects_on_the_host(lib):
+    """The allocation-free graph build refuses a workspace need above its static
+    array before touching the GPU (EGNN_E_WORKSPACE), and the usual argument errors."""
+    from equivariant_gnn_electronic_amd import _lib
+    box = (ct.c_double * 3)(9.0, 9.0, 9.0)
+    lo = (ct.c_double * 3)(0.0, 0.0, 0.0)
+    g = _fake_graph(64, 64, 5_000_000)
+    st = lib.egnn_build_graph_noalloc(None, lo, box, 7, 5.0, ct.byref(g), None)
+    assert st == _lib.EGNN_E_WORKSPACE
+    assert b"allocation-free" in lib.egnn_last_error()
+    g2 = _fake_graph(64, 32, 0)
+    assert lib.egnn_build_graph_noalloc(None, lo, box, 7, 5.0, ct.byref(g2), None) == _lib.EGNN_E_ARG
+    assert lib.egnn_build_graph_noalloc(None, lo, box, 7, -1.0, ct.byref(g), None) == _lib.EGNN_E_ARG
