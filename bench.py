@@ -9,7 +9,11 @@ with inputs already resident in HBM:
 The default workload is the HfO2-like training step: 3,000 atoms (1,000 Hf +
 2,000 O) in a 32.8 A periodic cube, cutoff 8 A (~547k directed edges),
 lmax 4, mmax 2, C 64, fp32, one layer forward + backward, then the decode
-into 13x13 orbital blocks.  `value` is edges per second of whole steps.
+into 13x13 orbital blocks.  `value` is edges per second of whole steps
+(wall clock over the timed steps); the median of per-step HIP-event times
+is reported beside it.  The default run also times the 8,064-atom
+GeSbTe-like configuration (bf16 storage, C 128): its 3-layer forward and its
+training step, under the key "gst" (skip with --no-gst).
 
 Other workloads (--workload): hfo2, halo, gst (forwards; GST is three bf16
 layers), gst_train (bf16 training step), hfo2_l6 / hfo2_l8 (forwards at
@@ -62,8 +66,11 @@ WORKLOADS = {
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-gst", action="store_true",
+                    help="(train workload) skip the GeSbTe-like 3-layer forward and training step that the "
+                         "default run also measures")
     ap.add_argument("--workload", default="train", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=500, help="rows of the oracle's timed sample")
@@ -235,29 +242,14 @@ def run_labels(args, wl, dev):
     step = LabelStep(wl, dev)
     copy_gbs = copy_bandwidth(torch, dev, args.copy_probe_mib)
     eg = step.eg
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    eg.egnn_timing_reset()
-    eg.egnn_timing_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    eg.egnn_timing_enable(False)
-    timing, dropped = eg.egnn_timing_collect()
+    ms, med, timing, dropped = timed_steps(torch, eg, step, args.steps, args.warmup)
     fam, roof = roofline(timing, "f32", args.workload)
-    ms = (t1 - t0) * 1e3 / args.steps
     b = step.batch
-    kernels = {k: dict(launches_per_step=v["launches"] / args.steps, ms_per_step=round(v["total_ms"] / args.steps, 4),
-                       algorithmic_gbs=round(v["bytes"] / (v["total_ms"] * 1e-3) / 1e9, 1))
-               for k, v in sorted(timing.items(), key=lambda kv: -kv[1]["total_ms"])}
+    kernels = kernel_table(timing, args.steps, copy_gbs)
     name = "Matrix -> Label" if wl["labels"] == "m2l" else "Label -> Matrix"
     out = {
         "metric": f"atoms/s of {name} over a batch of molecules + % of HBM roofline",
-        "value": round(b.n_atoms * args.steps / (t1 - t0), 1),
+        "value": round(b.n_atoms / (ms * 1e-3), 1),
         "unit": "atoms/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -271,7 +263,8 @@ def run_labels(args, wl, dev):
         "config": {"workload": args.workload, "description": wl["desc"], "molecules": b.n_mols,
                    "atoms": b.n_atoms, "edges": step.E, "labels_per_block": step.n_lab,
                    "matrix_entries": step.h_elems,
-                   "blocks_per_s": round((b.n_atoms + step.E) * args.steps / (t1 - t0), 1)},
+                   "blocks_per_s": round((b.n_atoms + step.E) / (ms * 1e-3), 1),
+                   "median_step_ms": round(med, 4)},
         "roofline": dict(kernel=fam, **roof),
         "hbm_copy_gbs": copy_gbs,
         "kernels": kernels,
@@ -535,6 +528,73 @@ def sweep(dev, warmup, reps):
                 points=points)
 
 
+def timed_steps(torch, eg, step, steps, warmup):
+    """Run `warmup` untimed steps, then `steps` timed ones with per-launch HIP-event
+    timing on (egnn_timing_*) and one pair of events around each step on the launch
+    stream.  Returns (wall ms per step, median event ms per step, timing, dropped)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    eg.egnn_timing_reset()
+    eg.egnn_timing_enable(True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    eg.egnn_timing_enable(False)
+    timing, dropped = eg.egnn_timing_collect()
+    med = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    return (t1 - t0) * 1e3 / steps, med, timing, dropped
+
+
+def kernel_table(timing, steps, copy_gbs):
+    """Per timing family: launches and ms per step, rate, and the fraction of the
+    MFMA peak of its dtype (GEMM families) or of the HBM peak and the measured copy."""
+    kernels = {}
+    for k, v in sorted(timing.items(), key=lambda kv: -kv[1]["total_ms"]):
+        sec = v["total_ms"] * 1e-3
+        gbs = v["bytes"] / sec / 1e9 if v["bytes"] > 0 else None
+        kernels[k] = dict(launches_per_step=v["launches"] / steps, ms_per_step=round(v["total_ms"] / steps, 4),
+                          tflops=round(v["flops"] / sec / 1e12, 2) if v["flops"] > 0 else None,
+                          algorithmic_gbs=round(gbs, 1) if gbs else None)
+        if v["flops"] > 0:
+            peak = MFMA_PEAK_TFLOPS["bf16" if "bf16" in k else "f32"]
+            kernels[k]["mfma_frac"] = round(v["flops"] / sec / 1e12 / peak, 4)
+        elif gbs:
+            kernels[k]["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+            if copy_gbs:
+                kernels[k]["copy_frac"] = round(gbs / copy_gbs, 4)
+    return kernels
+
+
+def gst_extra(torch, dev, steps, warmup, copy_gbs):
+    """The 8,064-atom GeSbTe-like configuration (bf16 storage, C 128): the 3-layer
+    forward and the training step, each timed like the headline step."""
+    out = {}
+    for name in ("gst", "gst_train"):
+        wl = WORKLOADS[name]
+        step = Step(wl, dev)
+        ms, med, timing, dropped = timed_steps(torch, step.eg, step, steps, warmup)
+        L = wl["layers"]
+        fam, roof = roofline(timing, "bf16", name)
+        out["forward_3_layers" if name == "gst" else "train_step"] = {
+            "description": wl["desc"], "edges": step.E, "atoms": step.struct.n_dst, "layers": L,
+            "ms_per_step": round(ms, 3), "median_step_ms": round(med, 3),
+            "edges_per_s_per_layer": round(step.E * L / (ms * 1e-3), 1),
+            "edges_per_s_per_layer_median": round(step.E * L / (med * 1e-3), 1),
+            "nodes_per_s_per_layer": round(step.struct.n_dst * L / (ms * 1e-3), 1),
+            "roofline": dict(kernel=fam, **roof), "kernels": kernel_table(timing, steps, copy_gbs),
+            "timing_events_dropped": dropped}
+        del step
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
@@ -559,44 +619,15 @@ def main():
         return
     step = Step(wl, dev)
     copy_gbs = copy_bandwidth(torch, dev, args.copy_probe_mib)
-    eg = step.eg
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    eg.egnn_timing_reset()
-    eg.egnn_timing_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    eg.egnn_timing_enable(False)
-    timing, dropped = eg.egnn_timing_collect()
-    ms = (t1 - t0) * 1e3 / args.steps
+    ms, med, timing, dropped = timed_steps(torch, step.eg, step, args.steps, args.warmup)
     E = step.E
     cfg = step.cfg
     dtype = "bf16" if cfg.storage == "bf16" else "f32"
     fam, roof = roofline(timing, dtype, args.workload)
-    kernels = {}
-    for k, v in sorted(timing.items(), key=lambda kv: -kv[1]["total_ms"]):
-        sec = v["total_ms"] * 1e-3
-        gbs = v["bytes"] / sec / 1e9 if v["bytes"] > 0 else None
-        kernels[k] = dict(launches_per_step=v["launches"] / args.steps, ms_per_step=round(v["total_ms"] / args.steps, 4),
-                          tflops=round(v["flops"] / sec / 1e12, 2) if v["flops"] > 0 else None,
-                          algorithmic_gbs=round(gbs, 1) if gbs else None)
-        if v["flops"] > 0:
-            # MFMA kernels: the fraction of the dtype's dense peak (algorithmic FLOPs)
-            peak = MFMA_PEAK_TFLOPS["bf16" if "bf16" in k else "f32"]
-            kernels[k]["mfma_frac"] = round(v["flops"] / sec / 1e12 / peak, 4)
-        elif gbs:
-            # gather / segment / decode kernels: against the published HBM peak and the measured copy
-            kernels[k]["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
-            if copy_gbs:
-                kernels[k]["copy_frac"] = round(gbs / copy_gbs, 4)
+    kernels = kernel_table(timing, args.steps, copy_gbs)
     out = {
         "metric": "edges/s per SO(2) message-passing layer (fwd+bwd) + % of HBM/MFMA roofline",
-        "value": round(E * wl["layers"] * args.steps / (t1 - t0), 1),
+        "value": round(E * wl["layers"] / (ms * 1e-3), 1),
         "unit": "edges/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -610,13 +641,19 @@ def main():
         "config": {"workload": args.workload, "description": wl["desc"], "atoms": step.struct.n_dst,
                    "sources": step.struct.n_src, "edges": E, "lmax": cfg.lmax, "mmax": cfg.mmax, "C": cfg.C,
                    "layers": wl["layers"], "r_cut": cfg.r_cut, "storage": cfg.storage,
-                   "nodes_per_s": round(step.struct.n_dst * wl["layers"] * args.steps / (t1 - t0), 1),
-                   "ms_per_layer": round(ms / wl["layers"], 3)},
+                   "nodes_per_s": round(step.struct.n_dst * wl["layers"] / (ms * 1e-3), 1),
+                   "ms_per_layer": round(ms / wl["layers"], 3),
+                   "median_step_ms": round(med, 3),
+                   "edges_per_s_median": round(E * wl["layers"] / (med * 1e-3), 1)},
         "roofline": dict(kernel=fam, **roof),
         "hbm_copy_gbs": copy_gbs,
         "kernels": kernels,
         "timing_events_dropped": dropped,
     }
+    if args.workload == "train" and not args.no_gst:
+        del step
+        torch.cuda.empty_cache()
+        out["gst"] = gst_extra(torch, dev, args.steps, args.warmup, copy_gbs)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
     print(json.dumps(out), flush=True)
