@@ -30,8 +30,8 @@ constexpr int kMaxEntries = kMaxOrb * kMaxOrb;
 constexpr int kMaxTerms = 8192;
 constexpr int kMaxLab = kMaxEntries;
 
-constexpr int kMaxShellL = 3;          // shells up to f
-constexpr int kMaxLabL = 2 * kMaxShellL;  // labels up to L = 6 (irreps lmax >= 6)
+constexpr int kMaxShellL = 4;          // shells up to g
+constexpr int kMaxLabL = 2 * kMaxShellL;  // labels up to L = 8 (irreps lmax 8)
 constexpr int kMaxNL = 64;             // label channels per degree (4 MFMA column tiles)
 
 struct Table {
@@ -152,7 +152,7 @@ egnn_status table_slot(const int *shell_l, int n_shells, int *slot, Layout *lay)
     return EGNN_E_UNSUPPORTED;
   }
   if (!build_layout(shell_l, n_shells, lay)) {
-    set_error("shell list not supported (each l <= 3, at most %d orbitals)", kMaxOrb);
+    set_error("shell list not supported (each l <= %d, at most %d orbitals)", kMaxShellL, kMaxOrb);
     return EGNN_E_UNSUPPORTED;
   }
   std::lock_guard<std::mutex> lock(g_cache.mu);
@@ -180,7 +180,6 @@ egnn_status table_slot(const int *shell_l, int n_shells, int *slot, Layout *lay)
 }
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kTile = 16;  // rows per wave tile (the MFMA M dimension)
@@ -224,10 +223,14 @@ __device__ inline void load_run(const T *p, float (&a)[S]) {
   }
 }
 
-template <int S, typename T>
-__global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64_t rows, const T *__restrict__ irreps,
-                                                                  int K, const float *__restrict__ W, int n_w,
-                                                                  int n_lab, int n_ent, float *__restrict__ H) {
+// NW waves per workgroup share the staged template and weights; each wave has
+// its own label tile, so large shell lists (g shells: 625 labels per row) run
+// with fewer waves per workgroup to fit in LDS.
+template <int S, int NW, typename T>
+__global__ void __launch_bounds__(kWave * NW) hblocks_kernel(int slot, int64_t rows, const T *__restrict__ irreps,
+                                                              int K, const float *__restrict__ W, int n_w,
+                                                              int n_lab, int n_ent, float *__restrict__ H) {
+  constexpr int kWaves = NW;
   constexpr int C = 4 * S;
   constexpr int WLD = C + 4;  // padded LDS row of W
   extern __shared__ float smem[];
@@ -356,31 +359,46 @@ __global__ void __launch_bounds__(kWave * kWaves) hblocks_kernel(int slot, int64
   }
 }
 
+template <int S, typename T>
+void launch_hblocks_nw(int nw, unsigned g, size_t smem, hipStream_t stream, int slot, int64_t rows, const T *irr,
+                       int K, const float *W, int n_w, int n_lab, int n_ent, float *H) {
+  if (nw == 4)
+    hblocks_kernel<S, 4, T><<<g, kWave * 4, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H);
+  else if (nw == 2)
+    hblocks_kernel<S, 2, T><<<g, kWave * 2, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H);
+  else
+    hblocks_kernel<S, 1, T><<<g, kWave * 1, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H);
+}
+
 template <typename T>
 egnn_status launch_hblocks(int slot, int64_t rows, const void *irreps, int K, int C, const float *W, int n_w,
                            int n_lab, int n_ent, int n_terms, float *H, hipStream_t stream) {
   if (rows <= 0) return EGNN_OK;
-  const size_t smem = sizeof(float) * (static_cast<size_t>(n_ent + 1) + 2 * n_terms + 4 +
-                                       static_cast<size_t>(n_w + 16) * (C + 4) +
-                                       static_cast<size_t>(kWaves) * kTile * label_stride(n_lab));
+  auto smem_for = [&](int nw) {
+    return sizeof(float) * (static_cast<size_t>(n_ent + 1) + 2 * n_terms + 4 + static_cast<size_t>(n_w + 16) * (C + 4) +
+                            static_cast<size_t>(nw) * kTile * label_stride(n_lab));
+  };
+  // the most waves per workgroup whose label tiles fit
+  int nw = 4;
+  while (nw > 1 && smem_for(nw) > 150 * 1024) nw /= 2;
+  const size_t smem = smem_for(nw);
   if (smem > 150 * 1024) {
     set_error("decode needs %zu bytes of LDS; reduce C or the shell list", smem);
     return EGNN_E_UNSUPPORTED;
   }
   Timed t(stream, "hblocks", 0.0,
           double(rows) * (double(K) * C * sizeof(T) + double(n_ent) * 4.0) + double(C) * n_w * 4.0);
-  int64_t blocks = ((rows + kTile - 1) / kTile + kWaves - 1) / kWaves;
-  if (blocks > 2048) blocks = 2048;
+  int64_t blocks = ((rows + kTile - 1) / kTile + nw - 1) / nw;
+  if (blocks > 2048 * 4 / nw) blocks = 2048 * 4 / nw;
   const unsigned g = static_cast<unsigned>(blocks);
-  const unsigned nt = kWave * kWaves;
   const T *irr = static_cast<const T *>(irreps);
   switch (C) {
-    case 8: hblocks_kernel<2, T><<<g, nt, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
-    case 16: hblocks_kernel<4, T><<<g, nt, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
-    case 32: hblocks_kernel<8, T><<<g, nt, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
-    case 64: hblocks_kernel<16, T><<<g, nt, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
-    case 128: hblocks_kernel<32, T><<<g, nt, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
-    case 256: hblocks_kernel<64, T><<<g, nt, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
+    case 8: launch_hblocks_nw<2, T>(nw, g, smem, stream, slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
+    case 16: launch_hblocks_nw<4, T>(nw, g, smem, stream, slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
+    case 32: launch_hblocks_nw<8, T>(nw, g, smem, stream, slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
+    case 64: launch_hblocks_nw<16, T>(nw, g, smem, stream, slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
+    case 128: launch_hblocks_nw<32, T>(nw, g, smem, stream, slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
+    case 256: launch_hblocks_nw<64, T>(nw, g, smem, stream, slot, rows, irr, K, W, n_w, n_lab, n_ent, H); break;
     default:
       set_error("decode supports C in {8, 16, 32, 64, 128, 256}");
       return EGNN_E_UNSUPPORTED;

@@ -42,7 +42,7 @@ namespace {
 constexpr int kLSlots = 4;
 constexpr int kFullMax = 32;                 // orbitals of the full shell list
 constexpr int kSpeciesMax = 64;
-constexpr int kShellLMax = 3;                // s, p, d, f shells: labels up to L = 6
+constexpr int kShellLMax = 4;                // s, p, d, f, g shells: labels up to L = 8
 constexpr int kTmplMax = 8;                  // distinct element bases (shell masks)
 constexpr int kPairN = (kTmplMax + 1) * (kTmplMax + 1);  // ordered template pairs, the empty template included
 constexpr int kRowMax = 2048;                // padded term rows per direction
@@ -89,7 +89,7 @@ const char *build_label_table(const egnn_basis *b, LabelTable *t) {
   int o = 0, lmx = 0;
   for (int a = 0; a < ns; ++a) {
     const int l = b->shell_l[a];
-    if (l < 0 || l > kShellLMax) return "shell degrees must be 0..3";
+    if (l < 0 || l > kShellLMax) return "shell degrees must be 0..4";
     off[a] = o;
     o += 2 * l + 1;
     lmx = std::max(lmx, l);

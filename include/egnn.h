@@ -251,7 +251,7 @@ egnn_status egnn_edge_update_bwd(const egnn_layer_desc *d, const egnn_graph *g, 
 /* ---------------------------------------------------------------------------
  * Label -> Matrix: Hamiltonian blocks  [MALOQ Sec. III-B1 Eq. (1), Sec. III-B2]
  *
- * Shells (host list shell_l, each l <= 3; n_orb = sum(2l+1) <= 32).  For
+ * Shells (host list shell_l, each l <= 4; n_orb = sum(2l+1) <= 32).  For
  * ordered shell pairs (a, b) in lexicographic order and L = |la-lb|..la+lb
  * ascending, label channel k(a,b,L) counts the earlier pairs carrying L;
  * n_L = number of pairs carrying L.  Labels are h_L = W_L f^L (C -> n_L) and
@@ -283,7 +283,7 @@ egnn_status egnn_hblocks(const egnn_hdesc *h, int64_t n_edges, int32_t n_nodes,
 /* ---------------------------------------------------------------------------
  * Matrix <-> Label over whole matrices  [MALOQ Sec. III-B1 Eq. (1), Sec. III-B2]
  *
- * Basis: one full shell list (each l <= 3, at most 32 orbitals: the largest
+ * Basis: one full shell list (each l <= 4, at most 32 orbitals: the largest
  * element's basis, or the union of the per-degree maxima) and, per element,
  * a bit mask of the full shells it carries (its orbital template).  An
  * atom's orbitals are its shells in full-list order, m = -l..l each.
@@ -324,7 +324,7 @@ egnn_status egnn_hblocks(const egnn_hdesc *h, int64_t n_edges, int32_t n_nodes,
  * ------------------------------------------------------------------------- */
 typedef struct {
   int32_t n_shells;                 /* full shell list, 1..16 shells          */
-  const int32_t *shell_l;           /* host [n_shells], each 0..3             */
+  const int32_t *shell_l;           /* host [n_shells], each 0..4             */
   int32_t n_species;                /* 1..64 elements                         */
   const uint32_t *species_shells;   /* host [n_species]: bit a = carries full shell a */
 } egnn_basis;

@@ -28,7 +28,7 @@ import numpy as np
 __all__ = ["Config", "CONFIGS", "Structure", "make_structure", "make_layer_inputs",
            "make_decode_weights", "make_cotangent", "layer_weight_sizes",
            "round_storage", "bf16_round", "SVP_SHELLS", "SVP_ELEMENTS", "SVP_MASKS",
-           "SVP_FRACTIONS", "WATER_SHELLS", "WATER_MASKS", "MoleculeBatch", "make_molecule_batch",
+           "SVP_FRACTIONS", "G_SHELLS", "G_MASKS", "G_FRACTIONS", "WATER_SHELLS", "WATER_MASKS", "MoleculeBatch", "make_molecule_batch",
            "make_matrix_values", "make_label_values", "make_edge_embeddings", "make_edge_cotangent"]
 
 
@@ -373,6 +373,13 @@ SVP_MASKS = (0b00010011,                 # H: s s . . p . . .
 SVP_FRACTIONS = (0.45, 0.33, 0.08, 0.08, 0.02, 0.02, 0.02)
 
 # the pages' toy example (Fig. 2(b)): water in a minimal basis, O [s p], H [s]
+# A basis with g shells (labels up to L = 8, the metal-organic case of MALOQ
+# Table II): full list s p d f g; light elements s p, second-row s p d, a
+# metal all five shells.
+G_SHELLS = (0, 1, 2, 3, 4)
+G_MASKS = (0b00011, 0b00111, 0b11111)
+G_FRACTIONS = (0.5, 0.35, 0.15)
+
 WATER_SHELLS = (0, 1)
 WATER_MASKS = (0b11, 0b01)               # O, H
 

@@ -178,8 +178,13 @@ def test_decode_description_checks(lib):
     assert lib.egnn_hblocks_label_rows(ct.byref(_lib.EgnnHDesc(8, 64, 1, arr3, 0))) == 7
     assert lib.egnn_hblocks_label_rows(ct.byref(_lib.EgnnHDesc(6, 64, 1, arr3, 0))) == 7
     assert lib.egnn_hblocks_label_rows(ct.byref(_lib.EgnnHDesc(4, 64, 1, arr3, 0))) == 0   # lmax < 6
-    arr4 = (ct.c_int32 * 1)(4)                            # g shells are not supported
-    assert lib.egnn_hblocks_label_rows(ct.byref(_lib.EgnnHDesc(8, 64, 1, arr4, 0))) == 0
+    arr4 = (ct.c_int32 * 1)(4)                            # g x g: one label channel for each L = 0..8
+    assert lib.egnn_hblocks_label_rows(ct.byref(_lib.EgnnHDesc(8, 64, 1, arr4, 0))) == 9
+    assert lib.egnn_hblocks_label_rows(ct.byref(_lib.EgnnHDesc(6, 64, 1, arr4, 0))) == 0   # lmax < 8
+    arr_g = (ct.c_int32 * 5)(0, 1, 2, 3, 4)               # s p d f g
+    assert lib.egnn_hblocks_label_rows(ct.byref(_lib.EgnnHDesc(8, 16, 5, arr_g, 0))) == 85
+    arr5 = (ct.c_int32 * 1)(5)                            # h shells are not supported
+    assert lib.egnn_hblocks_label_rows(ct.byref(_lib.EgnnHDesc(8, 64, 1, arr5, 0))) == 0
     # nothing to do is fine
     assert lib.egnn_hblocks(ct.byref(h), 0, 0, None, None, None, None, None, None, None) == 0
 
@@ -230,7 +235,9 @@ def test_label_width_and_basis_checks(lib):
     assert lib.egnn_label_width(ct.byref(_basis(synth.WATER_SHELLS, synth.WATER_MASKS))) == 16
     assert lib.egnn_label_width(ct.byref(_basis(synth.SVP_SHELLS, synth.SVP_MASKS))) == 18 * 18
     assert lib.egnn_label_width(ct.byref(_basis((0, 1, 2, 3), (0b1111,)))) == 16 * 16
-    assert lib.egnn_label_width(ct.byref(_basis((0, 4), (0b11,)))) == 0
+    assert lib.egnn_label_width(ct.byref(_basis((0, 4), (0b11,)))) == 10 * 10
+    assert lib.egnn_label_width(ct.byref(_basis(synth.G_SHELLS, synth.G_MASKS))) == 25 * 25
+    assert lib.egnn_label_width(ct.byref(_basis((0, 5), (0b11,)))) == 0              # h shells
     assert lib.egnn_label_width(ct.byref(_basis((3, 3, 3, 3, 3), (0b1,)))) == 0     # 35 orbitals
     assert lib.egnn_label_width(ct.byref(_basis((0, 1), (0b111,)))) == 0
     assert lib.egnn_label_width(None) == 0

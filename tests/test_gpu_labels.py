@@ -68,6 +68,9 @@ CASES = {
     # f shells (labels up to L = 6): full list s s p p d f, three elements
     "spdf": (lambda: synth.make_molecule_batch(23, 12, 1, 9, fractions=(0.4, 0.3, 0.3)),
              (0, 0, 1, 1, 2, 3), (0b000101, 0b010111, 0b111111)),
+    # g shells (labels up to L = 8): full list s p d f g, three elements
+    "spdfg": (lambda: synth.make_molecule_batch(25, 12, 1, 8, fractions=synth.G_FRACTIONS),
+              synth.G_SHELLS, synth.G_MASKS),
 }
 
 

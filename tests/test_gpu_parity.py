@@ -221,6 +221,30 @@ def test_hblocks_f_shells(dev):
     assert_close(hn.cpu().numpy(), odec.hblocks(r["xo"].cpu().numpy(), wn, shells), 1e-5, "on-site blocks")
 
 
+@pytest.mark.parametrize("C,storage", [(16, "f32"), (32, "bf16")])
+def test_hblocks_g_shells(dev, C, storage):
+    """Decode with g shells (s p d f g, 25 orbitals, labels up to L = 8) from
+    lmax-8 irreps: the layer's edge messages and outputs at lmax 8."""
+    cfg = dataclasses.replace(synth.CONFIGS["tiny"], name=f"tiny_l8_{storage}", lmax=8, mmax=2, C=C,
+                              storage=storage)
+    r = _gpu_forward(cfg, dev, edge_out=True)
+    shells = synth.G_SHELLS
+    _, n = odec.label_layout(shells)
+    rng = np.random.default_rng(62)
+    we = [(rng.standard_normal((c, C)) / np.sqrt(C)).astype(np.float32) for c in n]
+    wn = [(rng.standard_normal((c, C)) / np.sqrt(C)).astype(np.float32) for c in n]
+    st = eg.EGNN_BF16 if storage == "bf16" else eg.EGNN_F32
+    he, hn = eg.egnn_hblocks(8, C, torch.from_numpy(np.concatenate(we)).to(dev),
+                             torch.from_numpy(np.concatenate(wn)).to(dev), r["eo"], r["xo"], shell_l=shells,
+                             storage=st)
+    torch.cuda.synchronize()
+    assert he.shape[1:] == (25, 25)
+    eo = r["eo"].float().cpu().numpy().astype(np.float64)
+    xo = r["xo"].float().cpu().numpy().astype(np.float64)
+    assert_close(he.cpu().numpy(), odec.hblocks(eo, we, shells), 1e-5, "edge blocks")
+    assert_close(hn.cpu().numpy(), odec.hblocks(xo, wn, shells), 1e-5, "on-site blocks")
+
+
 def _rotate_irreps(a, Q, lmax):
     out = np.empty_like(a)
     for l in range(lmax + 1):

@@ -84,3 +84,57 @@ def test_f_shell_blocks_covariant():
         Dorb[o:o + 2 * l + 1, o:o + 2 * l + 1] = so3.wigner_d(l, Q)
     np.testing.assert_allclose(decode.hblocks(fr, w, shells), Dorb @ decode.hblocks(f, w, shells) @ Dorb.T,
                                atol=1e-11)
+
+
+G_SHELLS = (0, 1, 2, 3, 4)      # s p d f g: 25 orbitals, labels up to L = 8 (irreps at lmax 8)
+
+
+def test_g_shell_label_counts_and_round_trips():
+    items, n = decode.label_layout(G_SHELLS)
+    # n_L = ordered shell pairs (la, lb) with |la - lb| <= L <= la + lb, counted by hand
+    assert n == [5, 12, 16, 17, 15, 10, 6, 3, 1]
+    assert sum((2 * L + 1) * c for L, c in enumerate(n)) == 25 * 25
+    rng = np.random.default_rng(20)
+    H = rng.standard_normal((4, 25, 25))
+    np.testing.assert_allclose(decode.label_to_matrix(decode.matrix_to_label(H, G_SHELLS), G_SHELLS), H, atol=1e-12)
+    h = [rng.standard_normal((4, 2 * L + 1, c)) for L, c in enumerate(n)]
+    for a, b in zip(decode.matrix_to_label(decode.label_to_matrix(h, G_SHELLS), G_SHELLS), h):
+        np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+def test_g_g_block_trace_and_ss_entry():
+    """The degree-0 part of l (x) l is the identity over 2l + 1: the trace of the
+    g-g block (offset 16, 9 x 9) is sqrt(9) = 3 times its L = 0 label, and the s-s
+    entry is the first L = 0 label itself."""
+    rng = np.random.default_rng(21)
+    C = 4
+    f = rng.standard_normal((3, 81, C))
+    _, n = decode.label_layout(G_SHELLS)
+    w = [rng.standard_normal((c, C)) for c in n]
+    H = decode.hblocks(f, w, G_SHELLS)
+    items, _ = decode.label_layout(G_SHELLS)
+    h0 = np.einsum("ec,kc->ek", f[:, 0, :], w[0])
+    k_gg = next(k for a, b, L, k in items if (a, b, L) == (4, 4, 0))
+    blk = H[:, 16:25, 16:25]
+    np.testing.assert_allclose(np.trace(blk, axis1=1, axis2=2), 3.0 * h0[:, k_gg], atol=1e-12)
+    np.testing.assert_allclose(H[:, 0, 0], h0[:, 0], atol=1e-13)
+
+
+def test_g_shell_blocks_covariant():
+    """s p d f g blocks from lmax-8 irreps transform as D^{la} H D^{lb}^T."""
+    rng = np.random.default_rng(22)
+    C = 3
+    f = rng.standard_normal((4, 81, C))
+    _, n = decode.label_layout(G_SHELLS)
+    w = [rng.standard_normal((c, C)) for c in n]
+    Q = Rot.random(random_state=23).as_matrix()
+    fr = np.empty_like(f)
+    for l in range(9):
+        sl = slice(l * l, (l + 1) ** 2)
+        fr[:, sl, :] = np.einsum("mn,enc->emc", so3.wigner_d(l, Q), f[:, sl, :])
+    off, n_orb = decode.orbital_offsets(G_SHELLS)
+    Dorb = np.zeros((n_orb, n_orb))
+    for o, l in zip(off, G_SHELLS):
+        Dorb[o:o + 2 * l + 1, o:o + 2 * l + 1] = so3.wigner_d(l, Q)
+    np.testing.assert_allclose(decode.hblocks(fr, w, G_SHELLS), Dorb @ decode.hblocks(f, w, G_SHELLS) @ Dorb.T,
+                               atol=1e-10)

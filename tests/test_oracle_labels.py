@@ -6,6 +6,7 @@ covariance under a rotation of each molecule, the padding of absent shells,
 and agreement with direct slicing when every element carries every shell.
 """
 import numpy as np
+import pytest
 from scipy.spatial.transform import Rotation as Rot
 
 import synth
@@ -151,11 +152,38 @@ def test_uniform_basis_is_direct_slicing():
     np.testing.assert_allclose(he, ref, atol=1e-13)
 
 
-def test_labels_covariant():
+def _g_batch(seed, n_mols=2):
+    b = synth.make_molecule_batch(seed, n_mols, 2, 6, fractions=synth.G_FRACTIONS)
+    return b, labels.orbital_layout(b.mol_ptr, b.species, synth.G_SHELLS, synth.G_MASKS)
+
+
+def test_g_shell_counts_round_trips_and_norm():
+    """s p d f g full list (labels up to L = 8): 5 / 9 / 25 orbitals per element,
+    625 labels per block, T orthogonal (norm kept, both round trips)."""
+    _, n_orb = labels.species_templates(synth.G_SHELLS, synth.G_MASKS)
+    assert list(n_orb[:-1]) == [4, 9, 25]
+    b, lay = _g_batch(9, 3)
+    sh, masks = synth.G_SHELLS, synth.G_MASKS
+    src, dst = _edges(b)
+    H = synth.make_matrix_values(9, lay[3][-1]).astype(np.float64)
+    he, hn = labels.matrix_to_labels(H, src, dst, None, b.species, lay, sh, masks)
+    assert he.shape[1] == 625
+    assert np.isclose(np.sum(he * he) + np.sum(hn * hn), np.sum(H * H), rtol=1e-12)
+    np.testing.assert_allclose(labels.labels_to_matrix(he, hn, src, dst, None, b.species, lay, sh, masks), H,
+                               atol=1e-12)
+
+
+@pytest.mark.parametrize("basis", ["svp", "g"])
+def test_labels_covariant(basis):
     """Rotating a molecule's orbitals (H -> D H D^T, D block-diagonal per atom's
-    own shells) rotates every label's degree-L part by D^L."""
-    b, lay = _svp_batch(seed=8, n_mols=2)
-    sh, masks = synth.SVP_SHELLS, synth.SVP_MASKS
+    own shells) rotates every label's degree-L part by D^L (def2-SVP-like
+    shells, and the s p d f g list with labels up to L = 8)."""
+    if basis == "svp":
+        b, lay = _svp_batch(seed=8, n_mols=2)
+        sh, masks = synth.SVP_SHELLS, synth.SVP_MASKS
+    else:
+        b, lay = _g_batch(10, 2)
+        sh, masks = synth.G_SHELLS, synth.G_MASKS
     src, dst = _edges(b)
     atom_orb, atom_mol, mol_norb, mat_off = lay
     H = synth.make_matrix_values(8, mat_off[-1]).astype(np.float64)
