@@ -11,9 +11,12 @@ The default workload is the HfO2-like training step: 3,000 atoms (1,000 Hf +
 lmax 4, mmax 2, C 64, fp32, one layer forward + backward, then the decode
 into 13x13 orbital blocks.  `value` is edges per second of whole steps
 (wall clock over the timed steps); the median of per-step HIP-event times
-is reported beside it.  The default run also times the 8,064-atom
-GeSbTe-like configuration (bf16 storage, C 128): its 3-layer forward and its
-training step, under the key "gst" (skip with --no-gst).
+is reported beside it.  The default run also times, each the same way:
+the 8,064-atom GeSbTe-like configuration (bf16 storage, C 128), its 3-layer
+forward and its training step (key "gst"); the HfO2-like forward and the
+one-GPU-share (halo) forward ("other_configs"); and the saturation sweep of
+one layer forward against edge count ("saturation_sweep").  --no-extra
+skips them.
 
 Other workloads (--workload): hfo2, halo, gst (forwards; GST is three bf16
 layers), gst_train (bf16 training step), hfo2_l6 / hfo2_l8 (forwards at
@@ -68,9 +71,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--no-gst", action="store_true",
-                    help="(train workload) skip the GeSbTe-like 3-layer forward and training step that the "
-                         "default run also measures")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="(train workload) skip the other configurations the default run also measures: the "
+                         "GeSbTe-like 3-layer forward and training step, the HfO2-like and one-GPU-share "
+                         "forwards, and the saturation sweep")
     ap.add_argument("--workload", default="train", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=500, help="rows of the oracle's timed sample")
@@ -572,17 +576,17 @@ def kernel_table(timing, steps, copy_gbs):
     return kernels
 
 
-def gst_extra(torch, dev, steps, warmup, copy_gbs):
-    """The 8,064-atom GeSbTe-like configuration (bf16 storage, C 128): the 3-layer
-    forward and the training step, each timed like the headline step."""
+def extra_workloads(torch, dev, names, steps, warmup, copy_gbs):
+    """Other configurations timed like the headline step, each with its own
+    per-family roofline fractions: {name: result}."""
     out = {}
-    for name in ("gst", "gst_train"):
+    for name in names:
         wl = WORKLOADS[name]
         step = Step(wl, dev)
         ms, med, timing, dropped = timed_steps(torch, step.eg, step, steps, warmup)
         L = wl["layers"]
-        fam, roof = roofline(timing, "bf16", name)
-        out["forward_3_layers" if name == "gst" else "train_step"] = {
+        fam, roof = roofline(timing, "bf16" if step.cfg.storage == "bf16" else "f32", name)
+        out[name] = {
             "description": wl["desc"], "edges": step.E, "atoms": step.struct.n_dst, "layers": L,
             "ms_per_step": round(ms, 3), "median_step_ms": round(med, 3),
             "edges_per_s_per_layer": round(step.E * L / (ms * 1e-3), 1),
@@ -590,6 +594,7 @@ def gst_extra(torch, dev, steps, warmup, copy_gbs):
             "nodes_per_s_per_layer": round(step.struct.n_dst * L / (ms * 1e-3), 1),
             "roofline": dict(kernel=fam, **roof), "kernels": kernel_table(timing, steps, copy_gbs),
             "timing_events_dropped": dropped}
+        print(f"[bench] {name}: {ms:.3f} ms per step", file=sys.stderr, flush=True)
         del step
         torch.cuda.empty_cache()
     return out
@@ -650,10 +655,13 @@ def main():
         "kernels": kernels,
         "timing_events_dropped": dropped,
     }
-    if args.workload == "train" and not args.no_gst:
+    if args.workload == "train" and not args.no_extra:
         del step
         torch.cuda.empty_cache()
-        out["gst"] = gst_extra(torch, dev, args.steps, args.warmup, copy_gbs)
+        ex = extra_workloads(torch, dev, ("gst", "gst_train", "hfo2", "halo"), args.steps, args.warmup, copy_gbs)
+        out["gst"] = {"forward_3_layers": ex["gst"], "train_step": ex["gst_train"]}
+        out["other_configs"] = {"hfo2_forward": ex["hfo2"], "halo_forward": ex["halo"]}
+        out["saturation_sweep"] = sweep(dev, 5, 20)["points"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
     print(json.dumps(out), flush=True)
