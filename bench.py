@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="(no GPU) turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script into "
                          "the traffic summary under profiles/ and exit")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("PASS1_DIR", "PASS2_DIR"),
+                    help="(no GPU) turn two rocprofv3 --pmc runs of this script (the SQ counter sets named in "
+                         "the summary it writes) into profiles/sq_<workload>.txt and exit")
     ap.add_argument("--sweep", action="store_true",
                     help="saturation sweep: layer forward and edge geometry time vs edge count, on the first "
                          "rows of the one-GPU-share (halo) graph; prints one JSON line")
@@ -377,6 +380,77 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_mib, argv):
     print("\n".join(lines))
 
 
+SQ_PASS1 = ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
+            "SQ_INSTS_VALU", "SQ_ACTIVE_INST_ANY")
+SQ_PASS2 = ("GRBM_GUI_ACTIVE", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
+            "SQ_ACTIVE_INST_LDS", "SQ_INST_CYCLES_VMEM", "SQ_WAIT_INST_LDS")
+
+
+def summarize_sq(d1, d2, workload, argv):
+    """profiles/sq_<workload>.txt: per kernel, instruction mix per wave and the
+    VALU issue fraction = SQ_INSTS_VALU x 4 cycles (a wave64 VALU instruction on a
+    16-lane SIMD) / (1024 SIMDs x the kernel's cycles, GRBM_GUI_ACTIVE / 8 XCDs)."""
+    import collections
+    import csv
+    import glob
+    import re
+
+    def load(d):
+        per = collections.defaultdict(collections.Counter)
+        meta = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                k = (path, r["Dispatch_Id"])
+                per[k][r["Counter_Name"]] += float(r["Counter_Value"])
+                meta[k] = (r["Kernel_Name"], r["VGPR_Count"], r["Accum_VGPR_Count"], r["LDS_Block_Size"])
+        by = collections.defaultdict(collections.Counter)
+        n = collections.Counter()
+        m = {}
+        for k, c in per.items():
+            by[meta[k][0]].update(c)
+            n[meta[k][0]] += 1
+            m[meta[k][0]] = meta[k]
+        return by, n, m
+
+    a, na, ma = load(d1)
+    b, _, _ = load(d2)
+    cmd = f"python bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --copy-probe-mib 256"
+    lines = [f"# SQ counters per kernel of the {workload} step (sums over every dispatch of the run), from rocprofv3",
+             "# made by (from the repository root, on one MI355X):",
+             f"#   rocprofv3 --pmc {' '.join(SQ_PASS1)} --output-format csv -d <PASS1_DIR> -o run -- {cmd}",
+             f"#   rocprofv3 --pmc {' '.join(SQ_PASS2)} --output-format csv -d <PASS2_DIR> -o run -- {cmd}",
+             f"#   python {' '.join(argv)}",
+             "# valu_issue = SQ_INSTS_VALU * 4 / (1024 * GRBM_GUI_ACTIVE / 8): the fraction of SIMD cycles issuing VALU",
+             "# (wave64 on 16-lane SIMDs; GRBM_GUI_ACTIVE summed over the 8 XCDs); per-wave figures are means",
+             f"workload: {workload}"]
+    rows = []
+    for name, c in a.items():
+        gui = b.get(name, {}).get("GRBM_GUI_ACTIVE", 0.0)
+        if gui < 1e6 or c["SQ_WAVES"] <= 0:
+            continue
+        rows.append((gui, name, c, b.get(name, collections.Counter())))
+    rows.sort(key=lambda r: -r[0])
+    for gui, name, c, c2 in rows[:16]:
+        short = name.replace("egnn::(anonymous namespace)::", "").replace("void ", "")
+        mt = re.match(r"([A-Za-z0-9_:]+)(<[^(]*>)?", short)
+        short = (mt.group(1) + (mt.group(2) or "")) if mt else short[:80]
+        w = c["SQ_WAVES"]
+        wc = c["SQ_WAVE_CYCLES"]
+        vg, ag, lds = ma[name][1:]
+        lines.append(f"kernel: {short}  dispatches {na[name]}  vgpr {vg} agpr {ag} lds {lds} B")
+        lines.append(f"  per wave: VALU {c['SQ_INSTS_VALU'] / w:.0f}, VMEM rd {c2['SQ_INSTS_VMEM_RD'] / w:.0f}, "
+                     f"VMEM wr {c2['SQ_INSTS_VMEM_WR'] / w:.0f}, LDS {c2['SQ_INSTS_LDS'] / w:.0f}, "
+                     f"SALU {c2['SQ_INSTS_SALU'] / w:.0f}, wave cycles {wc / w:.0f}")
+        lines.append(f"  valu_issue {c['SQ_INSTS_VALU'] * 4 / (1024 * gui / 8):.3f}; of wave cycles: active VALU "
+                     f"{c['SQ_ACTIVE_INST_VALU'] / wc:.3f}, active any {c['SQ_ACTIVE_INST_ANY'] / wc:.3f}, "
+                     f"waiting (any) {c['SQ_WAIT_ANY'] / wc:.3f}, waiting to issue {c['SQ_WAIT_INST_ANY'] / wc:.3f}, "
+                     f"active LDS {c2['SQ_ACTIVE_INST_LDS'] / wc:.3f}")
+    path = os.path.join(ROOT, "profiles", f"sq_{workload}.txt")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # timing family -> piece (or pieces, all present) of its kernel's symbol name
 FAMILY_KERNELS = {
     # kernel-name pieces ("::" keeps gemm from matching cgemm; the GEMM templates carry
@@ -605,6 +679,9 @@ def main():
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.workload,
                           args.copy_probe_mib, sys.argv)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq[0], args.summarize_sq[1], args.workload, sys.argv)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is not built",
