@@ -208,19 +208,16 @@ __device__ inline EdgeList edge_list(int node, int half, int n_dst, const int *r
   return l;
 }
 
-// One channel of a row, in two steps (load, then convert).  bf16:
-// the lane loads the aligned 32-bit word holding its channel pair and keeps
-// its half.
+// One channel of a row, in two steps (load, then convert).  bf16: a 16-bit
+// load (zero-extended), then one shift into the high half.  (Loading the
+// aligned 32-bit word of the channel pair and selecting the lane's half took
+// three VALU operations per value.)
 template <typename T> struct RawOf { typedef uint32_t type; };
 template <> struct RawOf<float> { typedef float type; };
 __device__ inline float load_raw(const float *row, uint32_t off) { return row[off]; }
-__device__ inline uint32_t load_raw(const uint16_t *row, uint32_t off) {
-  return *reinterpret_cast<const uint32_t *>(row + (off & ~1u));
-}
+__device__ inline uint32_t load_raw(const uint16_t *row, uint32_t off) { return row[off]; }
 __device__ inline float from_raw(float v, uint32_t) { return v; }
-__device__ inline float from_raw(uint32_t v, uint32_t off) {
-  return __uint_as_float((off & 1u) ? (v & 0xFFFF0000u) : (v << 16));
-}
+__device__ inline float from_raw(uint32_t v, uint32_t) { return __uint_as_float(v << 16); }
 
 // Geometry rows (the first gs4 float4 of each) of a wave's edge list move
 // global -> registers -> the wave's LDS buffer in batches of kBatch edges.
