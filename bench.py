@@ -5,11 +5,12 @@ One step is one pass of the whole hot path over one synthetic structure,
 with inputs already resident in HBM:
   neighbour graph build -> edge geometry (Wigner rows, radial basis) ->
   layer forward (saving activations) -> layer backward -> Hamiltonian blocks
-  (edge and on-site).
+  (edge and on-site) -> the periodic Hamiltonian as one block-sparse row
+  structure over the image shifts.
 The default workload is the HfO2-like training step: 3,000 atoms (1,000 Hf +
 2,000 O) in a 32.8 A periodic cube, cutoff 8 A (~547k directed edges),
 lmax 4, mmax 2, C 64, fp32, one layer forward + backward, then the decode
-into 13x13 orbital blocks.  `value` is edges per second of whole steps
+into 13x13 orbital blocks and their assembly into the sparse H(S).  `value` is edges per second of whole steps
 (wall clock over the timed steps); the median of per-step HIP-event times
 is reported beside it.  The default run also times, each the same way:
 the 8,064-atom GeSbTe-like configuration (bf16 storage, C 128), its 3-layer
@@ -43,7 +44,7 @@ FP32_VALU_PEAK_TFLOPS = 78.6   # 256 CU x 4 SIMD x 16 lanes x 2 FLOP x 2.4 GHz (
 
 WORKLOADS = {
     "train": dict(cfg="train", backward=True, decode=True, layers=1,
-                  desc="HfO2-like training step: graph + geometry + 1 layer fwd/bwd + 13x13 blocks"),
+                  desc="HfO2-like training step: graph + geometry + 1 layer fwd/bwd + 13x13 blocks + sparse H(S)"),
     "hfo2": dict(cfg="hfo2", backward=False, decode=False, layers=1,
                  desc="HfO2-like forward: graph + geometry + 1 layer fwd"),
     "hfo2_l6": dict(cfg="hfo2_l6", backward=False, decode=False, layers=1,
@@ -55,7 +56,8 @@ WORKLOADS = {
     "gst": dict(cfg="gst", backward=False, decode=False, layers=3,
                 desc="GeSbTe-like 3-layer forward, bf16 storage"),
     "gst_train": dict(cfg="gst", backward=True, decode=True, layers=1,
-                      desc="GeSbTe-like training step, bf16 storage: graph + geometry + 1 layer fwd/bwd + 13x13 blocks"),
+                      desc="GeSbTe-like training step, bf16 storage: graph + geometry + 1 layer fwd/bwd + 13x13 blocks "
+                           "+ sparse H(S)"),
     "edge_train": dict(cfg="train", backward=True, decode=False, layers=1, edge=True,
                        desc="HfO2-like edge-update block: graph + geometry + edge update fwd/bwd"),
     "m2l": dict(labels="m2l", mols=4096, seed=40,
@@ -164,8 +166,10 @@ class Step:
             eg.egnn_layer_bwd(self.desc, g, self.geom, self.w[0], self.xs[0], self.buf, self.G,
                               grad_x=self.gx, grad_w=self.gw)
         if self.wl["decode"]:
-            eg.egnn_hblocks(self.cfg.lmax, self.cfg.C, self.we, self.wn, self.edge_out[:self.E],
-                            self.xs[-1][:s.n_dst], storage=self.storage)
+            he, hn = eg.egnn_hblocks(self.cfg.lmax, self.cfg.C, self.we, self.wn, self.edge_out[:self.E],
+                                     self.xs[-1][:s.n_dst], storage=self.storage)
+            # the periodic Hamiltonian: every block in one block-sparse row structure over the image shifts
+            eg.egnn_assemble_bsr(g, he, hn)
         return g
 
     def _fwd(self, g, i, eo):

@@ -21,7 +21,7 @@ __all__ = ["Graph", "layer_desc", "egnn_build_graph", "egnn_build_graph_noalloc"
            "egnn_hblocks", "egnn_hblocks_label_rows", "egnn_timing_enable", "egnn_timing_collect",
            "egnn_timing_reset", "GraphBuilder", "LayerBuffers", "EgnnError", "EGNN_F32", "EGNN_BF16",
            "Basis", "Orbitals", "egnn_label_width", "egnn_orbital_layout", "egnn_matrix_to_label",
-           "egnn_label_to_matrix", "egnn_edge_update_fwd", "egnn_edge_update_bwd"]
+           "egnn_label_to_matrix", "egnn_edge_update_fwd", "egnn_edge_update_bwd", "egnn_assemble_bsr"]
 
 _STORAGE = {EGNN_F32: torch.float32, EGNN_BF16: torch.bfloat16}
 
@@ -438,6 +438,29 @@ def egnn_hblocks(lmax, C, w_edge, w_node, edge_irreps, node_irreps, shell_l=(0, 
         _ptr(edge_irreps) if E else None, _ptr(node_irreps) if N else None, _ptr(he) if E else None,
         _ptr(hn) if N else None, _stream()))
     return he[:E], hn[:N]
+
+
+def egnn_assemble_bsr(graph: Graph, h_edge, h_onsite=None):
+    """One block-sparse-row matrix over all image shifts from the decode's blocks:
+    (row_ptr [n_src+1], col [nnzb], shift [nnzb][3] int8, val [nnzb][n_orb][n_orb])."""
+    lib = _lib.load()
+    _expect(h_edge, "h_edge", torch.float32, (graph.n_edges, None, None))
+    n_orb = h_edge.shape[1]
+    if h_edge.shape[2] != n_orb:
+        raise ValueError("h_edge blocks must be square")
+    if h_onsite is not None:
+        _expect(h_onsite, "h_onsite", torch.float32, (graph.n_dst, n_orb, n_orb))
+    dev = graph.row_ptr.device
+    nnzb = graph.n_edges + (graph.n_dst if h_onsite is not None else 0)
+    rp = torch.empty(graph.n_src + 1, dtype=torch.int32, device=dev)
+    col = torch.empty(max(nnzb, 1), dtype=torch.int32, device=dev)
+    sh = torch.empty((max(nnzb, 1), 3), dtype=torch.int8, device=dev)
+    val = torch.empty((max(nnzb, 1), n_orb, n_orb), dtype=torch.float32, device=dev)
+    g = graph.c_struct()
+    _lib.check("egnn_assemble_bsr", lib.egnn_assemble_bsr(
+        ct.byref(g), n_orb, _ptr(h_edge) if graph.n_edges else None,
+        _ptr(h_onsite) if h_onsite is not None else None, _ptr(rp), _ptr(col), _ptr(sh), _ptr(val), _stream()))
+    return rp, col[:nnzb], sh[:nnzb], val[:nnzb]
 
 
 class Basis:

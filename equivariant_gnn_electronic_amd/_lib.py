@@ -69,6 +69,7 @@ SIGNATURES = {
     "egnn_edge_update_bwd": (ct.c_int, [_L, _G, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "egnn_hblocks_label_rows": (ct.c_int32, [_H]),
     "egnn_hblocks": (ct.c_int, [_H, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "egnn_assemble_bsr": (ct.c_int, [_G, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "egnn_label_width": (ct.c_int32, [_B]),
     "egnn_orbital_layout": (ct.c_int, [_B, _O, _vp, _vp]),
     "egnn_matrix_to_label": (ct.c_int, [_B, _O, _G, _vp, _i64, _vp, _vp, _vp, _vp]),

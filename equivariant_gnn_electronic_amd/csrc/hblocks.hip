@@ -407,10 +407,124 @@ egnn_status launch_hblocks(int slot, int64_t rows, const void *irreps, int K, in
   return EGNN_OK;
 }
 
+// Periodic assembly: one wave per block row (source atom).  The row's blocks
+// are its source group's edges, already in ascending (destination, shift)
+// order because edge ids run destination-major and each destination row is
+// sorted by (source, shift), plus the on-site block of an owned atom, placed
+// where (i, 0, 0, 0) falls in that order.  The lanes then stream the row's
+// values as one contiguous output range.
+__device__ inline int dst_of_edge(const int *row_ptr, int n_dst, int e) {
+  int lo = 0, hi = n_dst;  // largest d with row_ptr[d] <= e
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (row_ptr[mid] <= e) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ void __launch_bounds__(256) assemble_bsr_kernel(const int *__restrict__ row_ptr, int n_dst,
+                                                           const int *__restrict__ src_ptr,
+                                                           const int *__restrict__ src_perm,
+                                                           const int8_t *__restrict__ shift, int n_src, int64_t E,
+                                                           int nb2, const float *__restrict__ h_edge,
+                                                           const float *__restrict__ h_onsite, int *__restrict__ brp,
+                                                           int *__restrict__ bcol, int8_t *__restrict__ bsh,
+                                                           float *__restrict__ bval) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  if (i >= n_src) return;
+  const int g0 = src_ptr[i], cnt = src_ptr[i + 1] - g0;
+  const bool on = h_onsite != nullptr && i < n_dst;
+  const int64_t base = g0 + (h_onsite != nullptr ? min(i, n_dst) : 0);
+  if (lane == 0) {
+    brp[i] = static_cast<int>(base);
+    if (i == n_src - 1) brp[n_src] = static_cast<int>(E + (h_onsite != nullptr ? n_dst : 0));
+  }
+  int before = 0;  // edges of the group ordered before (i, 0, 0, 0)
+  if (on) {
+    for (int t0 = 0; t0 < cnt; t0 += kWave) {
+      const int t = t0 + lane;
+      bool lt = false;
+      if (t < cnt) {
+        const int e = src_perm[g0 + t];
+        const int d = dst_of_edge(row_ptr, n_dst, e);
+        const int8_t *sv = shift + 3 * static_cast<int64_t>(e);
+        const int s0 = sv[0], s1 = sv[1], s2 = sv[2];
+        lt = d < i || (d == i && (s0 < 0 || (s0 == 0 && (s1 < 0 || (s1 == 0 && s2 < 0)))));
+      }
+      before += __popcll(__ballot(lt));
+    }
+  }
+  const int nout = cnt + (on ? 1 : 0);
+  // column and shift of every block of the row
+  for (int u = lane; u < nout; u += kWave) {
+    const bool is_on = on && u == before;
+    const int t = (on && u > before) ? u - 1 : u;
+    int col = i, s0 = 0, s1 = 0, s2 = 0;
+    if (!is_on) {
+      const int e = src_perm[g0 + t];
+      col = dst_of_edge(row_ptr, n_dst, e);
+      const int8_t *sv = shift + 3 * static_cast<int64_t>(e);
+      s0 = sv[0];
+      s1 = sv[1];
+      s2 = sv[2];
+    }
+    bcol[base + u] = col;
+    int8_t *o = bsh + 3 * (base + u);
+    o[0] = static_cast<int8_t>(s0);
+    o[1] = static_cast<int8_t>(s1);
+    o[2] = static_cast<int8_t>(s2);
+  }
+  // values: the row's blocks are one contiguous output range
+  float *out = bval + base * nb2;
+  int u = 0, r = lane;  // block and offset of this lane's value, stepped without divisions
+  while (r >= nb2 && u < nout) {
+    r -= nb2;
+    ++u;
+  }
+  for (; u < nout;) {
+    const bool is_on = on && u == before;
+    const int t = (on && u > before) ? u - 1 : u;
+    const float *in = is_on ? h_onsite + static_cast<int64_t>(i) * nb2
+                            : h_edge + static_cast<int64_t>(src_perm[g0 + t]) * nb2;
+    out[static_cast<int64_t>(u) * nb2 + r] = in[r];
+    r += kWave;
+    while (r >= nb2 && u < nout) {
+      r -= nb2;
+      ++u;
+    }
+  }
+}
+
 }  // namespace
 }  // namespace egnn
 
 using namespace egnn;
+
+extern "C" egnn_status egnn_assemble_bsr(const egnn_graph *g, int32_t n_orb, const float *h_edge,
+                                         const float *h_onsite, int32_t *bsr_row_ptr, int32_t *bsr_col,
+                                         int8_t *bsr_shift, float *bsr_val, hipStream_t stream) {
+  clear_error();
+  EGNN_REQUIRE(g, "graph is null");
+  EGNN_REQUIRE(g->n_dst >= 0 && g->n_src >= g->n_dst, "need 0 <= n_dst <= n_src");
+  EGNN_REQUIRE(g->n_edges >= 0 && g->n_edges <= g->capacity, "graph n_edges out of range");
+  EGNN_REQUIRE(n_orb >= 1 && n_orb <= kMaxOrb, "n_orb must be 1..%d", kMaxOrb);
+  const int64_t nnzb = g->n_edges + (h_onsite ? g->n_dst : 0);
+  EGNN_REQUIRE(nnzb <= INT32_MAX, "more than 2^31 - 1 blocks");
+  EGNN_REQUIRE(bsr_row_ptr && g->src_ptr, "row pointers are null");
+  if (g->n_src == 0) return EGNN_OK;
+  if (g->n_edges > 0)
+    EGNN_REQUIRE(h_edge && g->row_ptr && g->src_perm && g->shift, "edge pointers are null");
+  if (nnzb > 0) EGNN_REQUIRE(bsr_col && bsr_shift && bsr_val, "block arrays are null");
+  const int nb2 = n_orb * n_orb;
+  Timed t(stream, "assemble_bsr", 0.0, double(nnzb) * (2.0 * 4.0 * nb2 + 4.0 + 3.0 + 8.0) + 4.0 * g->n_src);
+  const int T = 256;
+  assemble_bsr_kernel<<<ceil_div(static_cast<int64_t>(g->n_src) * kWave, T), T, 0, stream>>>(
+      g->row_ptr, g->n_dst, g->src_ptr, g->src_perm, g->shift, g->n_src, g->n_edges, nb2, h_edge, h_onsite,
+      bsr_row_ptr, bsr_col, bsr_shift, bsr_val);
+  EGNN_CHECK_LAUNCH();
+  return EGNN_OK;
+}
 
 static bool valid_hdesc(const egnn_hdesc *h) {
   if (!h || !h->shell_l) return false;

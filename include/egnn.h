@@ -281,6 +281,29 @@ egnn_status egnn_hblocks(const egnn_hdesc *h, int64_t n_edges, int32_t n_nodes,
                          float *h_onsite /*[n_nodes][n_orb][n_orb]*/, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Periodic Hamiltonian assembly  [MALOQ Sec. III Fig. 2(a), Sec. III-B2]
+ *
+ * The blocks of egnn_hblocks for a periodic structure form one matrix H(S)
+ * per image shift S: the block of edge e (source atom s seen at image S,
+ * destination d in the home cell) is H(S)[s, d], rows = source orbitals;
+ * the on-site block of owned atom i is H(0)[i, i].  All images are written
+ * as one block-sparse-row structure: block rows are the sources
+ * 0..n_src-1; a row lists its blocks in ascending (destination, S_x, S_y,
+ * S_z) order, each with its column (destination atom) and shift; an owned
+ * atom's on-site block sits in that order at (i, 0, 0, 0).
+ *   h_edge    [n_edges][n_orb][n_orb] fp32 (graph edge order)
+ *   h_onsite  [n_dst][n_orb][n_orb] fp32, or NULL (no on-site blocks)
+ *   nnzb    = n_edges (+ n_dst with on-site blocks)
+ *   bsr_row_ptr [n_src + 1], bsr_col [nnzb], bsr_shift [nnzb][3] (int8),
+ *   bsr_val [nnzb][n_orb][n_orb]: outputs, caller-allocated.
+ * Needs the graph's row_ptr, shift, src_ptr and src_perm (as egnn_build_graph
+ * makes them).  n_orb 1..32.  Asynchronous; a pure gather, bit-exact.
+ * ------------------------------------------------------------------------- */
+egnn_status egnn_assemble_bsr(const egnn_graph *g, int32_t n_orb, const float *h_edge, const float *h_onsite,
+                              int32_t *bsr_row_ptr, int32_t *bsr_col, int8_t *bsr_shift, float *bsr_val,
+                              hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Matrix <-> Label over whole matrices  [MALOQ Sec. III-B1 Eq. (1), Sec. III-B2]
  *
  * Basis: one full shell list (each l <= 4, at most 32 orbitals: the largest

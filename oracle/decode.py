@@ -96,3 +96,37 @@ def matrix_to_label(H, shell_l=SHELL_L):
 def hblocks(f, w_dec, shell_l=SHELL_L):
     """Hamiltonian blocks [N][13][13] from irreps f [N][K][C] and W_dec,L [n_L][C]."""
     return label_to_matrix(labels_from_irreps(f, w_dec), shell_l)
+
+
+def assemble_bsr(src, dst, shift, h_edge, h_onsite, n_src):
+    """Label -> Matrix for a periodic structure (MALOQ Sec. III, Fig. 2(a): the
+    predicted blocks become the Hamiltonian; Sec. III-B2: matrix assembly).
+
+    The periodic Hamiltonian is one matrix H(S) per image shift S; the block
+    of edge e (source atom s at image S, destination atom d in the home cell,
+    rows = source orbitals, columns = destination orbitals) is H(S)[s, d], and
+    the on-site block of owned atom i is H(0)[i, i].
+
+    Reading R32: all images are held in one block-sparse row (BSR) structure:
+    block rows are source atoms 0..n_src-1, a row lists its blocks in
+    ascending (destination, S_x, S_y, S_z) order, each with its column
+    (destination atom) and its shift; owned atoms (i < len(h_onsite)) carry
+    their on-site block in that order at (i, 0, 0, 0).
+
+    Returns row_ptr [n_src + 1], col [nnzb], shift [nnzb][3] (int8) and
+    val [nnzb][n_orb][n_orb].
+    """
+    src = np.asarray(src, np.int64)
+    dst = np.asarray(dst, np.int64)
+    shift = np.asarray(shift, np.int64).reshape(-1, 3)
+    h_edge = np.asarray(h_edge)
+    h_onsite = np.asarray(h_onsite)
+    n_on = h_onsite.shape[0]
+    rows = np.concatenate([src, np.arange(n_on)])
+    cols = np.concatenate([dst, np.arange(n_on)])
+    sh = np.concatenate([shift, np.zeros((n_on, 3), np.int64)])
+    val = np.concatenate([h_edge, h_onsite]) if n_on else h_edge
+    order = np.lexsort((sh[:, 2], sh[:, 1], sh[:, 0], cols, rows))
+    counts = np.bincount(rows, minlength=n_src) if len(rows) else np.zeros(n_src, np.int64)
+    row_ptr = np.concatenate([[0], np.cumsum(counts)])
+    return row_ptr, cols[order], sh[order].astype(np.int8), val[order]

@@ -138,3 +138,73 @@ def test_g_shell_blocks_covariant():
         Dorb[o:o + 2 * l + 1, o:o + 2 * l + 1] = so3.wigner_d(l, Q)
     np.testing.assert_allclose(decode.hblocks(fr, w, G_SHELLS), Dorb @ decode.hblocks(f, w, G_SHELLS) @ Dorb.T,
                                atol=1e-10)
+
+
+def _periodic_graph_and_blocks(seed=30, n_orb=13):
+    import synth
+    from oracle import neighbors
+    s = synth.make_structure("tiny")
+    g = neighbors.build_graph(s.pos, s.n_dst, s.box, s.periodic_mask, s.r_cut)
+    dst = neighbors.dst_of_edges(g["row_ptr"])
+    rng = np.random.default_rng(seed)
+    he = rng.standard_normal((len(g["src"]), n_orb, n_orb))
+    hn = rng.standard_normal((s.n_dst, n_orb, n_orb))
+    return s, g, dst, he, hn
+
+
+def test_bsr_assembly_equals_dense_images():
+    """Every image's dense matrix H(S) (blocks placed by hand: edge (s -> d, S)
+    at rows of s and columns of d, on-site blocks on the S = 0 diagonal) equals
+    the BSR expanded image by image; rows are sorted and every block is kept once."""
+    s, g, dst, he, hn = _periodic_graph_and_blocks()
+    n = he.shape[1]
+    rp, col, sh, val = decode.assemble_bsr(g["src"], dst, g["shift"], he, hn, s.n_src)
+    assert rp[-1] == len(g["src"]) + s.n_dst == len(col)
+    keys = {tuple(k) for k in np.unique(g["shift"].astype(np.int64), axis=0)} | {(0, 0, 0)}
+    N = s.n_src * n
+    for S in keys:
+        dense = np.zeros((N, N))
+        for e in range(len(g["src"])):
+            if tuple(g["shift"][e]) == S:
+                a, b = g["src"][e] * n, dst[e] * n
+                dense[a:a + n, b:b + n] += he[e]
+        if S == (0, 0, 0):
+            for i in range(s.n_dst):
+                dense[i * n:(i + 1) * n, i * n:(i + 1) * n] += hn[i]
+        got = np.zeros((N, N))
+        for i in range(s.n_src):
+            for b in range(rp[i], rp[i + 1]):
+                if tuple(int(v) for v in sh[b]) == S:
+                    got[i * n:(i + 1) * n, col[b] * n:(col[b] + 1) * n] += val[b]
+        np.testing.assert_array_equal(got, dense)
+    for i in range(s.n_src):
+        k = [(int(col[b]),) + tuple(int(v) for v in sh[b]) for b in range(rp[i], rp[i + 1])]
+        assert k == sorted(k) and len(set(k)) == len(k)
+
+
+def test_bsr_bloch_sum_hermitian_for_symmetric_pairs():
+    """Blocks built as f(|r|) B(Z_s, Z_d) with B(Z_d, Z_s) = B(Z_s, Z_d)^T and
+    symmetric on-site blocks: the Bloch sum H(k) = sum_S H(S) exp(2 pi i k.S)
+    of the assembled matrix is Hermitian at every k (the reverse edge
+    (d -> s, -S) carries the transposed block)."""
+    import synth
+    s, g, dst, _, _ = _periodic_graph_and_blocks()
+    species = synth.make_structure("tiny").species
+    n = 4
+    rng = np.random.default_rng(31)
+    B = rng.standard_normal((2, 2, n, n))
+    B[1, 0] = B[0, 1].T
+    B[0, 0] = B[0, 0] + B[0, 0].T
+    B[1, 1] = B[1, 1] + B[1, 1].T
+    d = np.asarray(g["dist"], np.float64)
+    he = np.exp(-d)[:, None, None] * B[species[g["src"]], species[dst]]
+    hn = np.stack([B[species[i], species[i]] for i in range(s.n_dst)])
+    rp, col, sh, val = decode.assemble_bsr(g["src"], dst, g["shift"], he, hn, s.n_src)
+    for k in rng.uniform(-0.5, 0.5, (3, 3)):
+        H = np.zeros((s.n_src * n, s.n_src * n), complex)
+        for i in range(s.n_src):
+            for b in range(rp[i], rp[i + 1]):
+                ph = np.exp(2j * np.pi * float(k @ sh[b].astype(np.float64)))
+                H[i * n:(i + 1) * n, col[b] * n:(col[b] + 1) * n] += ph * val[b]
+        np.testing.assert_allclose(H, H.conj().T, atol=1e-12)
+        assert np.abs(H.imag).max() > 1e-3
