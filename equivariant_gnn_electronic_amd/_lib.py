@@ -4,7 +4,9 @@ from __future__ import annotations
 import ctypes as ct
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libegnn.so")
+# EGNN_LIBRARY names another build of the same ABI (the host-only sanitizer
+# build that the host-code tests load); the default is the in-tree library.
+LIB_PATH = os.environ.get("EGNN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libegnn.so")
 
 EGNN_OK, EGNN_E_ARG, EGNN_E_CAPACITY, EGNN_E_HIP, EGNN_E_UNSUPPORTED, EGNN_E_WORKSPACE = range(6)
 EGNN_F32, EGNN_BF16 = 0, 1
