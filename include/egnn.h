@@ -176,6 +176,9 @@ size_t egnn_layer_weight_count(const egnn_layer_desc *d);
  *   for l = 0..lmax, rows m = -min(l,mmax)..min(l,mmax), columns m' = -l..l
  *   (row-major within l, l blocks consecutive), then phi[0..n_rbf), then the
  *   edge's destination row as int32 bits, then zero padding.
+ * geom must be 16-byte aligned (EGNN_E_ARG otherwise; hipMalloc and torch
+ * allocations are).  The rotation is formed in fp64 and rounded once; the
+ * recursion runs in fp32.
  * One geometry serves every layer on the same graph.
  * ------------------------------------------------------------------------- */
 int32_t egnn_geom_stride(const egnn_layer_desc *d);     /* floats per edge, 0 if invalid */

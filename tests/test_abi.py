@@ -381,3 +381,11 @@ def test_noalloc_graph_rejects_on_the_host(lib):
     g2 = _fake_graph(64, 32, 0)
     assert lib.egnn_build_graph_noalloc(None, lo, box, 7, 5.0, ct.byref(g2), None) == _lib.EGNN_E_ARG
     assert lib.egnn_build_graph_noalloc(None, lo, box, 7, -1.0, ct.byref(g), None) == _lib.EGNN_E_ARG
+
+
+def test_edge_geom_rejects_misaligned_output(lib):
+    from equivariant_gnn_electronic_amd import _lib
+    d = _desc(4, 2, 64)
+    g = _fake_graph(10, 10, 100)
+    st = lib.egnn_edge_geom(ct.byref(d), ct.byref(g), ct.c_void_p(0x1004), None)
+    assert st == _lib.EGNN_E_ARG and b"aligned" in lib.egnn_last_error()
