@@ -607,3 +607,16 @@ def test_assemble_bsr(dev, name, onsite):
     np.testing.assert_array_equal(col.cpu().numpy(), ref[1])
     np.testing.assert_array_equal(sh.cpu().numpy(), ref[2])
     np.testing.assert_array_equal(val.cpu().numpy(), ref[3])
+
+
+def test_layer_backward_halo_full_size_masked_rows(dev):
+    """One GPU's share at full size (30,000 owned rows, 21,133 ghost sources,
+    open boundary, 3.15M edges, fp32): the backward with the cotangent on 150
+    rows spread over the row range, every weight block and grad x of every
+    atom (ghosts included: they receive gradient only through their outgoing
+    edges) against the oracle's exact values."""
+    cfg = synth.CONFIGS["halo"]
+    r = _gpu_forward(cfg, dev, train=True)
+    assert r["g"].n_src > r["g"].n_dst
+    rows = np.unique(np.linspace(0, r["s"].n_dst - 1, 150).round().astype(np.int64))
+    _compare_full_backward(cfg, r, dev, rows, 1e-4)
