@@ -354,7 +354,7 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_mib, argv):
     if not cf or not cw:
         raise SystemExit("no copy-probe dispatch in the counter runs")
     sf, sw = copy_bytes / (cf[0] * 1024), copy_bytes / (cw[0] * 1024)
-    cmd = (f"python bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline "
+    cmd = (f"python bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --no-extra "
            f"--copy-probe-mib {copy_mib}")
     lines = [
         f"# HBM traffic per launch of the main kernels of the {workload} step, from rocprofv3 counters",
@@ -418,7 +418,7 @@ def summarize_sq(d1, d2, workload, argv):
 
     a, na, ma = load(d1)
     b, _, _ = load(d2)
-    cmd = f"python bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --copy-probe-mib 256"
+    cmd = f"python bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --no-extra --copy-probe-mib 256"
     lines = [f"# SQ counters per kernel of the {workload} step (sums over every dispatch of the run), from rocprofv3",
              "# made by (from the repository root, on one MI355X):",
              f"#   rocprofv3 --pmc {' '.join(SQ_PASS1)} --output-format csv -d <PASS1_DIR> -o run -- {cmd}",
@@ -470,6 +470,7 @@ FAMILY_KERNELS = {
     "rotate_in": "::scatter_in_",
     "aggregate": "::aggregate_",
     "hblocks": "hblocks_kernel",
+    "assemble_bsr": "assemble_bsr_kernel",
     "edge_update": "::edge_update_kernel<",
     "edge_dy": "::edge_dy_kernel<",
     "matrix_to_label": ("::labels_kernel<", ", true>"),   # every (chunk, pass) instantiation
