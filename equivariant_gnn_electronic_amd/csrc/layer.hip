@@ -358,6 +358,18 @@ __device__ inline void load_node_row(const T *__restrict__ x, int node, int C, i
   for (int k = 0; k < K; ++k) xv[k] = active ? v[k] : 0.0f;
 }
 
+// Coefficients KB..KB+KR-1 of one channel of a node row (rows of K coefficients).
+template <int KR, typename T>
+__device__ inline void load_node_range(const T *__restrict__ x, int node, int K, int KB, int C, int c, bool active,
+                                       float (&xv)[KR]) {
+  const T *row = x + (static_cast<int64_t>(node) * K + KB) * C + (active ? c : 0);
+  float v[KR];
+#pragma unroll
+  for (int k = 0; k < KR; ++k) v[k] = Store<T>::ld(row + static_cast<uint32_t>(k * C));
+#pragma unroll
+  for (int k = 0; k < KR; ++k) xv[k] = active ? v[k] : 0.0f;
+}
+
 // A[e] = g_e * trunc(D_e x) for the wave's half of every edge of its node.
 template <int LMAX, int MMAX, int NRBF, typename T, typename TA>
 __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restrict__ row_ptr,
@@ -1133,7 +1145,78 @@ __global__ void __launch_bounds__(kThreads) bwd_row_pair_kernel(const int *__res
   *reinterpret_cast<float2 *>(watt_part + static_cast<int64_t>(d) * C + c) = make_float2(wacc0, wacc1);
 }
 
-template <int LMAX, int MMAX, int NRBF, typename T>
+// Degree parts.  At high degree one wave cannot hold a node's whole
+// per-channel state (the radial weights of every gate pair, accumulators for
+// every coefficient, the next edge's loads) in registers, and the backward
+// node kernels spilled.  Their work separates by degree, so the degrees are
+// dealt to parts, each launched as its own grid over every (node, half,
+// chunk): part p owns degrees Parts::lo(p)..Parts::hi(p), its coefficients,
+// kept entries and gate pairs.  Degrees up to 4 are one part.
+template <int LMAX, int NRBF>
+struct Parts {
+  static constexpr int N = LMAX <= 4 ? 1 : LMAX <= 6 ? (NRBF <= 8 ? 2 : 3) : (NRBF <= 8 ? 3 : 4);
+  __host__ __device__ static constexpr int lo(int p) {
+    return N == 1 ? 0
+           : LMAX <= 6 ? (N == 2 ? (p == 0 ? 0 : 4) : (p == 0 ? 0 : p == 1 ? 4 : 6))
+                       : (N == 3 ? (p == 0 ? 0 : p == 1 ? 5 : 7) : (p == 0 ? 0 : p == 1 ? 4 : p == 2 ? 6 : 8));
+  }
+  __host__ __device__ static constexpr int hi(int p) { return p == N - 1 ? LMAX : lo(p + 1) - 1; }
+};
+
+// Index ranges of degrees L0..L1: coefficients k = l^2 + l + m from KB, kept
+// (l, m) entries from QB (their running index), and the gate pairs (m, l)
+// with l in the range, numbered m-major from 0.
+template <int LMAX, int MMAX, int L0, int L1>
+struct Rng {
+  static constexpr int KB = L0 * L0;
+  static constexpr int KR = (L1 + 1) * (L1 + 1) - KB;
+  static constexpr int QB = Lay<LMAX, MMAX>::kidx(L0, -cmin(L0, MMAX));
+  static constexpr int QR = Lay<LMAX, MMAX>::kidx(L1, cmin(L1, MMAX)) + 1 - QB;
+  __host__ __device__ static constexpr int lpair(int m, int l) {
+    int n = 0;
+    for (int j = 0; j < m; ++j) {
+      const int a = j > L0 ? j : L0;
+      if (a <= L1) n += L1 - a + 1;
+    }
+    return n + l - (m > L0 ? m : L0);
+  }
+  static constexpr int NP = lpair(MMAX + 1, MMAX + 1 > L0 ? MMAX + 1 : L0);
+  // global pair index (pair_index) of local pair q
+  __host__ __device__ static constexpr int gpair(int q) {
+    for (int m = 0; m <= MMAX; ++m) {
+      const int a = m > L0 ? m : L0;
+      if (a > L1) continue;
+      if (q <= L1 - a) return pair_index(m, a + q, LMAX);
+      q -= L1 - a + 1;
+    }
+    return -1;
+  }
+};
+
+// Radial weights of the gate pairs of degrees L0..L1 for one lane's slot j
+// (unused slots read column 0 and are zeroed after: no branch per load).
+template <int LMAX, int MMAX, int NRBF, int L0, int L1>
+__device__ inline void load_wrad_range(const float *wrad, int n_rbf, int C2, int j, bool active,
+                                       float (&wr)[NRBF][Rng<LMAX, MMAX, L0, L1>::NP]) {
+  using R = Rng<LMAX, MMAX, L0, L1>;
+  constexpr int NPG = pair_count(LMAX, MMAX);
+  const int jc = active ? j : 0;
+  float v[NRBF][R::NP];
+#pragma unroll
+  for (int k = 0; k < NRBF; ++k)
+#pragma unroll
+    for (int m = 0; m <= MMAX; ++m)
+#pragma unroll
+      for (int l = (m > L0 ? m : L0); l <= L1; ++l)
+        v[k][R::lpair(m, l)] = wrad[(static_cast<int64_t>(k < n_rbf ? k : 0) * NPG + pair_index(m, l, LMAX)) * C2 + jc];
+#pragma unroll
+  for (int k = 0; k < NRBF; ++k)
+#pragma unroll
+    for (int p = 0; p < R::NP; ++p) wr[k][p] = (active && k < n_rbf) ? v[k][p] : 0.0f;
+}
+
+
+template <int LMAX, int MMAX, int NRBF, typename T, int L0 = 0, int L1 = LMAX>
 __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restrict__ row_ptr,
                                                              const int *__restrict__ src_ptr,
                                                              const int *__restrict__ src_perm,
@@ -1141,6 +1224,7 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
                                                              int n_src, const T *__restrict__ x, int C, int n_rbf,
                                                              CPtr3 dA, int n_streams, float *__restrict__ part) {
   using L = Lay<LMAX, MMAX>;
+  using R = Rng<LMAX, MMAX, L0, L1>;  // this launch's degrees
   constexpr int GS4 = (L::ND + NRBF + 3) / 4;
   const int gs4 = (L::ND + n_rbf + 3) / 4;
   __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
@@ -1156,17 +1240,17 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
   const int c = chunk * kWave + lane;
   const bool active = c < C;
   const int j = half * C + c;
-  float acc[NRBF][L::NP];
+  float acc[NRBF][R::NP];
 #pragma unroll
   for (int k = 0; k < NRBF; ++k)
 #pragma unroll
-    for (int p = 0; p < L::NP; ++p) acc[k][p] = 0.0f;
+    for (int p = 0; p < R::NP; ++p) acc[k][p] = 0.0f;
   const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
   for (int node = stream; node < n_src; node += n_streams) {
     const EdgeList el = edge_list(node, half, n_dst, row_ptr, src_ptr, src_perm);
     if (el.count == 0) continue;
-    float xv[L::K];
-    load_node_row<L::K>(x, node, C, c, active, xv);
+    float xv[R::KR];  // the node row's degrees L0..L1
+    load_node_range<R::KR>(x, node, L::K, R::KB, C, c, active, xv);
     GeomPipe<GS4> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave]);
     for (int base = 0; base < el.count; base += kBatch) {
       const int cnt = min(kBatch, el.count - base);
@@ -1176,50 +1260,50 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
       // load a clamped channel and their sums are never written
       using Raw = typename RawOf<T>::type;
       const int jl = half * C + min(c, C - 1);
-      auto load_da = [&](int i, Raw(&raw)[L::KEPT]) {
+      auto load_da = [&](int i, Raw(&raw)[R::QR]) {
         const int e = uniform(eids[wave][min(i, cnt - 1)]);
         const T *rowp[MMAX + 1];  // wave-uniform row bases, 32-bit lane offsets; dA in the storage type
 #pragma unroll
         for (int mu = 0; mu <= MMAX; ++mu)
           rowp[mu] = static_cast<const T *>(dA.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
 #pragma unroll
-        for (int l = 0; l <= LMAX; ++l)
+        for (int l = L0; l <= L1; ++l)
 #pragma unroll
           for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
-            raw[L::kidx(l, m)] = load_raw(rowp[cabs(m)], static_cast<uint32_t>(L::col(l, m) * C2 + jl));
+            raw[L::kidx(l, m) - R::QB] = load_raw(rowp[cabs(m)], static_cast<uint32_t>(L::col(l, m) * C2 + jl));
       };
-      auto product = [&](int i, const Raw(&raw)[L::KEPT]) {
+      auto product = [&](int i, const Raw(&raw)[R::QR]) {
         const float *gr = gb + i * GS4 * 4;
-        float dg[L::NP];
+        float dg[R::NP];
 #pragma unroll
-        for (int p = 0; p < L::NP; ++p) dg[p] = 0.0f;
+        for (int p = 0; p < R::NP; ++p) dg[p] = 0.0f;
 #pragma unroll
-        for (int l = 0; l <= LMAX; ++l)
+        for (int l = L0; l <= L1; ++l)
 #pragma unroll
           for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
             float xt = 0.0f;
 #pragma unroll
-            for (int mp = -l; mp <= l; ++mp) xt += gr[L::doff(l, m, mp)] * xv[l * l + l + mp];
-            const float dx = from_raw(raw[L::kidx(l, m)], static_cast<uint32_t>(L::col(l, m) * C2 + jl));
-            dg[pair_index(cabs(m), l, LMAX)] += dx * xt;
+            for (int mp = -l; mp <= l; ++mp) xt += gr[L::doff(l, m, mp)] * xv[l * l + l + mp - R::KB];
+            const float dx = from_raw(raw[L::kidx(l, m) - R::QB], static_cast<uint32_t>(L::col(l, m) * C2 + jl));
+            dg[R::lpair(cabs(m), l)] += dx * xt;
           }
 #pragma unroll
         for (int k = 0; k < NRBF; ++k) {
           const float rv = gr[L::ND + k];  // in the staged row; select, no branch
           const float ph = k < n_rbf ? rv : 0.0f;
 #pragma unroll
-          for (int p = 0; p < L::NP; ++p) acc[k][p] += ph * dg[p];
+          for (int p = 0; p < R::NP; ++p) acc[k][p] += ph * dg[p];
         }
       };
       if constexpr (NRBF > 8) {  // 16 radial functions: no registers for a second buffer
         for (int i = 0; i < cnt; ++i) {
-          Raw ra[L::KEPT];
+          Raw ra[R::QR];
           load_da(i, ra);
           __builtin_amdgcn_sched_barrier(0);
           product(i, ra);
         }
       } else {
-        Raw ra[L::KEPT], rb[L::KEPT];
+        Raw ra[R::QR], rb[R::QR];
         load_da(0, ra);
         for (int i = 0; i < cnt; i += 2) {
           load_da(i + 1, rb);
@@ -1235,8 +1319,8 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
 #pragma unroll
   for (int k = 0; k < NRBF; ++k)
 #pragma unroll
-    for (int p = 0; p < L::NP; ++p)
-      if (k < n_rbf) part[((static_cast<int64_t>(stream) * n_rbf + k) * L::NP + p) * C2 + j] = acc[k][p];
+    for (int q = 0; q < R::NP; ++q)
+      if (k < n_rbf) part[((static_cast<int64_t>(stream) * n_rbf + k) * L::NP + R::gpair(q)) * C2 + j] = acc[k][q];
 }
 
 // grad_x[n] = G[n] (owned rows; none when G is null) + sum over the node's incoming edges of
@@ -1247,7 +1331,7 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
 // PK: the gates come from the radial weights packed as bf16 pairs over the
 // basis index and the basis values rounded to bf16 pairs, by the same packed
 // dot products as the paired rotate-in, so they are the gates that forward used.
-template <int LMAX, int MMAX, int NRBF, typename TdA, bool PK = false>
+template <int LMAX, int MMAX, int NRBF, typename TdA, bool PK = false, int L0 = 0, int L1 = LMAX>
 __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__restrict__ row_ptr,
                                                                const int *__restrict__ src_ptr,
                                                                const int *__restrict__ src_perm,
@@ -1256,11 +1340,12 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
                                                                const uint32_t *__restrict__ wpk, int n_rbf, CPtr3 dA,
                                                                const float *__restrict__ G, float *__restrict__ gx) {
   using L = Lay<LMAX, MMAX>;
+  using R = Rng<LMAX, MMAX, L0, L1>;  // this launch's degrees
   constexpr int GS4 = (L::ND + NRBF + 3) / 4;
   const int gs4 = (L::ND + n_rbf + 3) / 4;
   __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
   __shared__ int eids[kWavesPerBlock][kBatch];
-  __shared__ float red[kWavesPerBlock][L::K * kWave];
+  __shared__ float red[kWavesPerBlock][R::KR * kWave];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int nch = (C + kWave - 1) / kWave;
   const NodeWave nw = node_wave(blockIdx.x * kWavesPerBlock + wave, nch);
@@ -1269,21 +1354,24 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
   const int c = nw.chunk * kWave + lane;
   const bool active = live && c < C;
   const int j = nw.half * C + c;
-  float acc[L::K];
+  float acc[R::KR];
 #pragma unroll
-  for (int k = 0; k < L::K; ++k) acc[k] = 0.0f;
+  for (int k = 0; k < R::KR; ++k) acc[k] = 0.0f;
   if (live) {
     const EdgeList el = edge_list(nw.node, nw.half, n_dst, row_ptr, src_ptr, src_perm);
-    float wr[PK ? 1 : NRBF][L::NP];
-    bf16x2 wp[PK ? NRBF / 2 : 1][L::NP];
+    float wr[PK ? 1 : NRBF][R::NP];
+    bf16x2 wp[PK ? NRBF / 2 : 1][R::NP];
     if constexpr (PK) {
 #pragma unroll
       for (int q = 0; q < NRBF / 2; ++q)
 #pragma unroll
-        for (int p = 0; p < L::NP; ++p)
-          wp[q][p] = __builtin_bit_cast(bf16x2, wpk[(static_cast<int64_t>(q) * L::NP + p) * C2 + (active ? j : 0)]);
+        for (int m = 0; m <= MMAX; ++m)
+#pragma unroll
+          for (int l = (m > L0 ? m : L0); l <= L1; ++l)
+            wp[q][R::lpair(m, l)] = __builtin_bit_cast(
+                bf16x2, wpk[(static_cast<int64_t>(q) * L::NP + pair_index(m, l, LMAX)) * C2 + (active ? j : 0)]);
     } else {
-      load_wrad<LMAX, MMAX, NRBF>(wrad, n_rbf, C2, j, active, wr);
+      load_wrad_range<LMAX, MMAX, NRBF, L0, L1>(wrad, n_rbf, C2, j, active, wr);
     }
     const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
     if (el.count > 0) {
@@ -1297,29 +1385,26 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
         // sums are never written.
         using Raw = typename RawOf<TdA>::type;
         const int jl = nw.half * C + min(c, C - 1);
-        auto load_da = [&](int i, Raw(&raw)[L::KEPT]) {
+        auto load_da = [&](int i, Raw(&raw)[R::QR]) {
           const int e = uniform(eids[wave][min(i, cnt - 1)]);
           const TdA *rowp[MMAX + 1];  // wave-uniform row bases, 32-bit lane offsets
 #pragma unroll
           for (int mu = 0; mu <= MMAX; ++mu)
             rowp[mu] = static_cast<const TdA *>(dA.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
 #pragma unroll
-          for (int l = 0; l <= LMAX; ++l)
+          for (int l = L0; l <= L1; ++l)
 #pragma unroll
             for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
-              raw[L::kidx(l, m)] = load_raw(rowp[cabs(m)], static_cast<uint32_t>(L::col(l, m) * C2 + jl));
+              raw[L::kidx(l, m) - R::QB] = load_raw(rowp[cabs(m)], static_cast<uint32_t>(L::col(l, m) * C2 + jl));
         };
-        auto product = [&](int i, const Raw(&raw)[L::KEPT]) {
+        auto product = [&](int i, const Raw(&raw)[R::QR]) {
           const float *gr = gb + i * GS4 * 4;
-          float dxt[L::KEPT];
+          float dxt[R::QR];
 #pragma unroll
-          for (int l = 0; l <= LMAX; ++l)
+          for (int q = 0; q < R::QR; ++q) dxt[q] = from_raw(raw[q], 0u);
+          float g[R::NP];
 #pragma unroll
-            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
-              dxt[L::kidx(l, m)] = from_raw(raw[L::kidx(l, m)], static_cast<uint32_t>(L::col(l, m) * C2 + jl));
-          float g[L::NP];
-#pragma unroll
-          for (int p = 0; p < L::NP; ++p) g[p] = 0.0f;
+          for (int p = 0; p < R::NP; ++p) g[p] = 0.0f;
           if constexpr (PK) {
 #pragma unroll
             for (int q = 0; q < NRBF / 2; ++q) {
@@ -1327,7 +1412,7 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
               const bf16x2 ph = {static_cast<__bf16>(2 * q < n_rbf ? r0 : 0.0f),
                                  static_cast<__bf16>(2 * q + 1 < n_rbf ? r1 : 0.0f)};
 #pragma unroll
-              for (int p = 0; p < L::NP; ++p) g[p] = __builtin_amdgcn_fdot2_f32_bf16(ph, wp[q][p], g[p], false);
+              for (int p = 0; p < R::NP; ++p) g[p] = __builtin_amdgcn_fdot2_f32_bf16(ph, wp[q][p], g[p], false);
             }
           } else {
 #pragma unroll
@@ -1335,35 +1420,36 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
               const float rv = gr[L::ND + kk];  // in the staged row; select, no branch
               const float ph = kk < n_rbf ? rv : 0.0f;
 #pragma unroll
-              for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[kk][p];
+              for (int p = 0; p < R::NP; ++p) g[p] += ph * wr[kk][p];
             }
           }
           // gated entries h = g dxt once per (l, m), then one FMA per Wigner-D term
-          float h[L::KEPT];
+          float h[R::QR];
 #pragma unroll
-          for (int l = 0; l <= LMAX; ++l)
+          for (int l = L0; l <= L1; ++l)
 #pragma unroll
             for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
-              h[L::kidx(l, m)] = g[pair_index(cabs(m), l, LMAX)] * dxt[L::kidx(l, m)];
+              h[L::kidx(l, m) - R::QB] = g[R::lpair(cabs(m), l)] * dxt[L::kidx(l, m) - R::QB];
 #pragma unroll
-          for (int l = 0; l <= LMAX; ++l)
+          for (int l = L0; l <= L1; ++l)
 #pragma unroll
             for (int mp = -l; mp <= l; ++mp) {
               float sum = 0.0f;
 #pragma unroll
-              for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) sum += gr[L::doff(l, m, mp)] * h[L::kidx(l, m)];
-              acc[l * l + l + mp] += sum;
+              for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
+                sum += gr[L::doff(l, m, mp)] * h[L::kidx(l, m) - R::QB];
+              acc[l * l + l + mp - R::KB] += sum;
             }
         };
         if constexpr (NRBF > 8) {  // 16 radial functions: no registers for a second buffer
           for (int i = 0; i < cnt; ++i) {
-            Raw ra[L::KEPT];
+            Raw ra[R::QR];
             load_da(i, ra);
             __builtin_amdgcn_sched_barrier(0);
             product(i, ra);
           }
         } else {
-          Raw ra[L::KEPT], rb[L::KEPT];
+          Raw ra[R::QR], rb[R::QR];
           load_da(0, ra);
           for (int i = 0; i < cnt; i += 2) {
             load_da(i + 1, rb);
@@ -1378,13 +1464,13 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
   }
   // half 1 hands its partial to half 0 of the same chunk
 #pragma unroll
-  for (int k = 0; k < L::K; ++k) red[wave][k * kWave + lane] = acc[k];
+  for (int k = 0; k < R::KR; ++k) red[wave][k * kWave + lane] = acc[k];
   __syncthreads();
   if (active && nw.half == 0) {
     const int partner = wave + nch;  // same node, same chunk, half 1
 #pragma unroll
-    for (int k = 0; k < L::K; ++k) {
-      const int64_t o = (static_cast<int64_t>(nw.node) * L::K + k) * C + c;
+    for (int k = 0; k < R::KR; ++k) {
+      const int64_t o = (static_cast<int64_t>(nw.node) * L::K + R::KB + k) * C + c;
       const float g0 = (G && nw.node < n_dst) ? G[o] : 0.0f;  // no G: the edge block has no node residual
       gx[o] = g0 + (acc[k] + red[partner][k * kWave + lane]);
     }
@@ -1642,13 +1728,25 @@ WOff weight_offsets(const LayerShape &s) {
 }
 
 // ------------------------------------------------------------ launchers --
+// f(lo, hi) for every degree part of Parts<LMAX, NRBF>, in order
+template <int LMAX, int NRBF, int P = 0, typename F>
+void for_parts(F &&f) {
+  if constexpr (P < Parts<LMAX, NRBF>::N) {
+    f(std::integral_constant<int, Parts<LMAX, NRBF>::lo(P)>{}, std::integral_constant<int, Parts<LMAX, NRBF>::hi(P)>{});
+    for_parts<LMAX, NRBF, P + 1>(f);
+  }
+}
+
 template <int LMAX, int MMAX>
 struct Launch {
   template <typename T, typename TA>
   static void rotate_in(const egnn_graph *g, const LayerShape &s, const float *geom, const T *x, const float *wrad,
                         const uint32_t *wpk, const Acts &a, hipStream_t st) {
     Ptr3 A{{a.A[0], a.A[1], a.A[2]}};
-    if constexpr (std::is_same<T, uint16_t>::value && std::is_same<TA, uint16_t>::value) {
+    // channel pairs up to degree 6 (at degree 8 the pair kernel's node row and
+    // radial weights for two channels spill; the per-channel kernel, with
+    // the same packed gates, does not)
+    if constexpr (std::is_same<T, uint16_t>::value && std::is_same<TA, uint16_t>::value && LMAX <= 6) {
       if (wpk && paired_gates(s)) {  // channel pairs
         const int nch2 = s.C / (2 * kWave);
         const unsigned grid2 = ceil_div(static_cast<int64_t>(g->n_src) * 2 * nch2, kWavesPerBlock);
@@ -1670,7 +1768,7 @@ struct Launch {
   static void aggregate(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const T *x,
                         T *x_out, T *edge_out, hipStream_t st) {
     CPtr3 Y{{a.Y[0], a.Y[1], a.Y[2]}};
-    if constexpr (std::is_same<T, uint16_t>::value) {
+    if constexpr (std::is_same<T, uint16_t>::value && LMAX <= 6) {  // (at degree 8 the pair kernel spills)
       if (s.C % (2 * kWave) == 0) {  // channel pairs
         const unsigned grid2 = ceil_div(static_cast<int64_t>(g->n_dst) * (s.C / (2 * kWave)), kWavesPerBlock);
         aggregate_pair_kernel<LMAX, MMAX><<<grid2, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha,
@@ -1716,14 +1814,19 @@ struct Launch {
     const int nch = (s.C + kWave - 1) / kWave;
     const int ns = wrad_streams(g->n_src);
     const unsigned grid = ceil_div(static_cast<int64_t>(ns) * 2 * nch, kWavesPerBlock);
+    // one launch per degree part (each writes its own gate pairs' partials)
+    auto go = [&](auto nrbf) {
+      constexpr int NR = decltype(nrbf)::value;
+      for_parts<LMAX, NR>([&](auto lo, auto hi) {
+        wrad_grad_kernel<LMAX, MMAX, NR, T, decltype(lo)::value, decltype(hi)::value><<<grid, kThreads, 0, st>>>(
+            g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride, g->n_dst, g->n_src, x, s.C, s.n_rbf, dA, ns,
+            w.wrad_part);
+      });
+    };
     if (s.n_rbf <= 8)
-      wrad_grad_kernel<LMAX, MMAX, 8, T><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom,
-                                                                    s.gstride, g->n_dst, g->n_src, x, s.C, s.n_rbf,
-                                                                    dA, ns, w.wrad_part);
+      go(std::integral_constant<int, 8>{});
     else
-      wrad_grad_kernel<LMAX, MMAX, 16, T><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom,
-                                                                     s.gstride, g->n_dst, g->n_src, x, s.C, s.n_rbf,
-                                                                     dA, ns, w.wrad_part);
+      go(std::integral_constant<int, 16>{});
   }
   static void bwd_gate(const egnn_graph *g, const LayerShape &s, const float *geom, const void *x, const float *wrad,
                        const BwdWs &w, hipStream_t st) {
@@ -1739,17 +1842,22 @@ struct Launch {
                          const float *wrad, const uint32_t *wpk, CPtr3 dA, float *gx, hipStream_t st) {
     const int nch = (s.C + kWave - 1) / kWave;
     const unsigned grid = ceil_div(static_cast<int64_t>(g->n_src) * 2 * nch, kWavesPerBlock);
+    // one launch per degree part (each writes its own coefficient rows of gx)
+    auto go = [&](auto nrbf, auto pk) {
+      constexpr int NR = decltype(nrbf)::value;
+      constexpr bool P = decltype(pk)::value;
+      for_parts<LMAX, NR>([&](auto lo, auto hi) {
+        gather_grad_kernel<LMAX, MMAX, NR, TdA, P, decltype(lo)::value, decltype(hi)::value>
+            <<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride, g->n_dst, g->n_src, s.C,
+                                        wrad, P ? wpk : nullptr, s.n_rbf, dA, G, gx);
+      });
+    };
     if (wpk)
-      gather_grad_kernel<LMAX, MMAX, 8, TdA, true><<<grid, kThreads, 0, st>>>(
-          g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride, g->n_dst, g->n_src, s.C, wrad, wpk, s.n_rbf, dA, G, gx);
+      go(std::integral_constant<int, 8>{}, std::true_type{});
     else if (s.n_rbf <= 8)
-      gather_grad_kernel<LMAX, MMAX, 8, TdA><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom,
-                                                                        s.gstride, g->n_dst, g->n_src, s.C, wrad,
-                                                                        nullptr, s.n_rbf, dA, G, gx);
+      go(std::integral_constant<int, 8>{}, std::false_type{});
     else
-      gather_grad_kernel<LMAX, MMAX, 16, TdA><<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom,
-                                                                         s.gstride, g->n_dst, g->n_src, s.C, wrad,
-                                                                         nullptr, s.n_rbf, dA, G, gx);
+      go(std::integral_constant<int, 16>{}, std::false_type{});
   }
   static void bwd_node(const egnn_graph *g, const LayerShape &s, const float *geom, const float *G, const float *wrad,
                        const BwdWs &w, float *gx, hipStream_t st) {
