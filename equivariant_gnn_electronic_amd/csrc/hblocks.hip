@@ -407,12 +407,17 @@ egnn_status launch_hblocks(int slot, int64_t rows, const void *irreps, int K, in
   return EGNN_OK;
 }
 
-// Periodic assembly: one wave per block row (source atom).  The row's blocks
-// are its source group's edges, already in ascending (destination, shift)
-// order because edge ids run destination-major and each destination row is
-// sorted by (source, shift), plus the on-site block of an owned atom, placed
-// where (i, 0, 0, 0) falls in that order.  The lanes then stream the row's
-// values as one contiguous output range.
+// Periodic assembly, in two passes.  Pass 1 (one wave per block row = source
+// atom) writes the row pointers, columns and shifts.  The row's blocks are
+// its source group's edges, already in ascending (destination, shift) order
+// because edge ids run destination-major and each destination row is sorted
+// by (source, shift), plus the on-site block of an owned atom, placed where
+// (i, 0, 0, 0) falls in that order: an edge lands one slot later when it
+// sorts after the on-site block, and the on-site block's slot is the count of
+// edges that sort before it.  Pass 2 copies the values: each wave takes
+// kBsrChunk consecutive output blocks (one contiguous output range), finds
+// each block's input from the columns and shifts of pass 1, and streams the
+// range with several independent loads per lane in flight.
 __device__ inline int dst_of_edge(const int *row_ptr, int n_dst, int e) {
   int lo = 0, hi = n_dst;  // largest d with row_ptr[d] <= e
   while (hi - lo > 1) {
@@ -422,76 +427,108 @@ __device__ inline int dst_of_edge(const int *row_ptr, int n_dst, int e) {
   return lo;
 }
 
-__global__ void __launch_bounds__(256) assemble_bsr_kernel(const int *__restrict__ row_ptr, int n_dst,
-                                                           const int *__restrict__ src_ptr,
-                                                           const int *__restrict__ src_perm,
-                                                           const int8_t *__restrict__ shift, int n_src, int64_t E,
-                                                           int nb2, const float *__restrict__ h_edge,
-                                                           const float *__restrict__ h_onsite, int *__restrict__ brp,
-                                                           int *__restrict__ bcol, int8_t *__restrict__ bsh,
-                                                           float *__restrict__ bval) {
+// (col, s) after (i, 0, 0, 0) in (destination, S_x, S_y, S_z) order
+__device__ inline bool after_onsite(int col, int s0, int s1, int s2, int i) {
+  return col > i || (col == i && (s0 > 0 || (s0 == 0 && (s1 > 0 || (s1 == 0 && s2 > 0)))));
+}
+
+__global__ void __launch_bounds__(256) bsr_index_kernel(const int *__restrict__ row_ptr, int n_dst,
+                                                        const int *__restrict__ src_ptr,
+                                                        const int *__restrict__ src_perm,
+                                                        const int8_t *__restrict__ shift, int n_src, int64_t E,
+                                                        bool onsite, int *__restrict__ brp, int *__restrict__ bcol,
+                                                        int8_t *__restrict__ bsh) {
   const int lane = threadIdx.x & (kWave - 1);
   const int i = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
   if (i >= n_src) return;
   const int g0 = src_ptr[i], cnt = src_ptr[i + 1] - g0;
-  const bool on = h_onsite != nullptr && i < n_dst;
-  const int64_t base = g0 + (h_onsite != nullptr ? min(i, n_dst) : 0);
+  const bool on = onsite && i < n_dst;
+  const int64_t base = g0 + (onsite ? min(i, n_dst) : 0);
   if (lane == 0) {
     brp[i] = static_cast<int>(base);
-    if (i == n_src - 1) brp[n_src] = static_cast<int>(E + (h_onsite != nullptr ? n_dst : 0));
+    if (i == n_src - 1) brp[n_src] = static_cast<int>(E + (onsite ? n_dst : 0));
   }
   int before = 0;  // edges of the group ordered before (i, 0, 0, 0)
-  if (on) {
-    for (int t0 = 0; t0 < cnt; t0 += kWave) {
-      const int t = t0 + lane;
-      bool lt = false;
-      if (t < cnt) {
-        const int e = src_perm[g0 + t];
-        const int d = dst_of_edge(row_ptr, n_dst, e);
-        const int8_t *sv = shift + 3 * static_cast<int64_t>(e);
-        const int s0 = sv[0], s1 = sv[1], s2 = sv[2];
-        lt = d < i || (d == i && (s0 < 0 || (s0 == 0 && (s1 < 0 || (s1 == 0 && s2 < 0)))));
-      }
-      before += __popcll(__ballot(lt));
-    }
-  }
-  const int nout = cnt + (on ? 1 : 0);
-  // column and shift of every block of the row
-  for (int u = lane; u < nout; u += kWave) {
-    const bool is_on = on && u == before;
-    const int t = (on && u > before) ? u - 1 : u;
-    int col = i, s0 = 0, s1 = 0, s2 = 0;
-    if (!is_on) {
+  for (int t0 = 0; t0 < cnt; t0 += kWave) {
+    const int t = t0 + lane;
+    bool lt = false;
+    if (t < cnt) {
       const int e = src_perm[g0 + t];
-      col = dst_of_edge(row_ptr, n_dst, e);
+      const int d = dst_of_edge(row_ptr, n_dst, e);
       const int8_t *sv = shift + 3 * static_cast<int64_t>(e);
-      s0 = sv[0];
-      s1 = sv[1];
-      s2 = sv[2];
+      const int s0 = sv[0], s1 = sv[1], s2 = sv[2];
+      const bool late = on && after_onsite(d, s0, s1, s2, i);
+      lt = on && !late;
+      const int64_t u = base + t + (late ? 1 : 0);
+      bcol[u] = d;
+      int8_t *o = bsh + 3 * u;
+      o[0] = static_cast<int8_t>(s0);
+      o[1] = static_cast<int8_t>(s1);
+      o[2] = static_cast<int8_t>(s2);
     }
-    bcol[base + u] = col;
-    int8_t *o = bsh + 3 * (base + u);
-    o[0] = static_cast<int8_t>(s0);
-    o[1] = static_cast<int8_t>(s1);
-    o[2] = static_cast<int8_t>(s2);
+    before += __popcll(__ballot(lt));
   }
-  // values: the row's blocks are one contiguous output range
-  float *out = bval + base * nb2;
-  int u = 0, r = lane;  // block and offset of this lane's value, stepped without divisions
-  while (r >= nb2 && u < nout) {
-    r -= nb2;
-    ++u;
+  if (on && lane == 0) {
+    const int64_t u = base + before;
+    bcol[u] = i;
+    bsh[3 * u] = 0;
+    bsh[3 * u + 1] = 0;
+    bsh[3 * u + 2] = 0;
   }
-  for (; u < nout;) {
-    const bool is_on = on && u == before;
-    const int t = (on && u > before) ? u - 1 : u;
-    const float *in = is_on ? h_onsite + static_cast<int64_t>(i) * nb2
-                            : h_edge + static_cast<int64_t>(src_perm[g0 + t]) * nb2;
-    out[static_cast<int64_t>(u) * nb2 + r] = in[r];
-    r += kWave;
-    while (r >= nb2 && u < nout) {
-      r -= nb2;
-      ++u;
+}
+
+constexpr int kBsrChunk = 16;  // output blocks per wave in the value pass
+constexpr int kBsrLoads = 8;   // loads in flight per lane
+
+__global__ void __launch_bounds__(256) bsr_values_kernel(const int *__restrict__ brp, int n_src, int n_dst,
+                                                         const int *__restrict__ src_ptr,
+                                                         const int *__restrict__ src_perm,
+                                                         const int *__restrict__ bcol,
+                                                         const int8_t *__restrict__ bsh, int64_t nnzb, int nb2,
+                                                         const float *__restrict__ h_edge,
+                                                         const float *__restrict__ h_onsite,
+                                                         float *__restrict__ bval) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t b0 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave * kBsrChunk;
+  if (b0 >= nnzb) return;
+  const int nb = static_cast<int>(min(static_cast<int64_t>(kBsrChunk), nnzb - b0));
+  // lanes 0..nb-1: the input block of output block b0 + lane
+  int64_t src_blk = 0;  // element offset of the input block; on-site blocks are tagged by the sign
+  if (lane < nb) {
+    const int b = static_cast<int>(b0 + lane);
+    int lo = 0, hi = n_src;  // row: largest i with brp[i] <= b
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (brp[mid] <= b) lo = mid; else hi = mid;
+    }
+    const int i = lo, u = b - brp[i];
+    const int col = bcol[b];
+    const int s0 = bsh[3 * static_cast<int64_t>(b)], s1 = bsh[3 * static_cast<int64_t>(b) + 1],
+              s2 = bsh[3 * static_cast<int64_t>(b) + 2];
+    const bool on = h_onsite != nullptr && i < n_dst;
+    if (on && col == i && s0 == 0 && s1 == 0 && s2 == 0) {
+      src_blk = -1 - static_cast<int64_t>(i) * nb2;
+    } else {
+      const int t = u - ((on && after_onsite(col, s0, s1, s2, i)) ? 1 : 0);
+      src_blk = static_cast<int64_t>(src_perm[src_ptr[i] + t]) * nb2;
+    }
+  }
+  const int total = nb * nb2;
+  float *out = bval + b0 * nb2;
+  for (int o0 = 0; o0 < total; o0 += kWave * kBsrLoads) {
+    float v[kBsrLoads];
+#pragma unroll
+    for (int k = 0; k < kBsrLoads; ++k) {
+      const int o = o0 + k * kWave + lane;
+      const int blk = o / nb2, r = o - blk * nb2;
+      const int64_t sb = __shfl(src_blk, min(blk, kBsrChunk - 1));
+      v[k] = 0.0f;
+      if (o < total) v[k] = sb >= 0 ? h_edge[sb + r] : h_onsite[-1 - sb + r];
+    }
+#pragma unroll
+    for (int k = 0; k < kBsrLoads; ++k) {
+      const int o = o0 + k * kWave + lane;
+      if (o < total) out[o] = v[k];
     }
   }
 }
@@ -519,10 +556,16 @@ extern "C" egnn_status egnn_assemble_bsr(const egnn_graph *g, int32_t n_orb, con
   const int nb2 = n_orb * n_orb;
   Timed t(stream, "assemble_bsr", 0.0, double(nnzb) * (2.0 * 4.0 * nb2 + 4.0 + 3.0 + 8.0) + 4.0 * g->n_src);
   const int T = 256;
-  assemble_bsr_kernel<<<ceil_div(static_cast<int64_t>(g->n_src) * kWave, T), T, 0, stream>>>(
-      g->row_ptr, g->n_dst, g->src_ptr, g->src_perm, g->shift, g->n_src, g->n_edges, nb2, h_edge, h_onsite,
-      bsr_row_ptr, bsr_col, bsr_shift, bsr_val);
+  bsr_index_kernel<<<ceil_div(static_cast<int64_t>(g->n_src) * kWave, T), T, 0, stream>>>(
+      g->row_ptr, g->n_dst, g->src_ptr, g->src_perm, g->shift, g->n_src, g->n_edges, h_onsite != nullptr,
+      bsr_row_ptr, bsr_col, bsr_shift);
   EGNN_CHECK_LAUNCH();
+  if (nnzb > 0) {
+    bsr_values_kernel<<<ceil_div(ceil_div(nnzb, kBsrChunk) * kWave, T), T, 0, stream>>>(
+        bsr_row_ptr, g->n_src, g->n_dst, g->src_ptr, g->src_perm, bsr_col, bsr_shift, nnzb, nb2, h_edge, h_onsite,
+        bsr_val);
+    EGNN_CHECK_LAUNCH();
+  }
   return EGNN_OK;
 }
 
