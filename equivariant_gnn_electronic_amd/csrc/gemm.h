@@ -29,6 +29,16 @@ hipError_t cgemm_f32(int M, int N, int K, const float *Up, const float *Um, int 
 int gemm_f32_tiles(int M, int N);
 int gemm_bf16_tn_tiles(int M, int N);
 
+// Workgroups of the split-K weight-gradient kernels that one CU holds at once
+// (the runtime's occupancy figure for the instantiation that the shape
+// selects; at least 1): gemm_f32 and cgemm_f32 with neither operand
+// K-contiguous (cgemm with V from data), and gemm_bf16_tn_splitk.
+int gemm_f32_tn_blocks_per_cu(int M, int N);
+int cgemm_f32_dw_blocks_per_cu(int M, int N);
+int gemm_bf16_tn_blocks_per_cu();
+// CUs per XCD of the current device (its CU count / 8).
+int xcd_cus();
+
 // bf16 operands (raw 16-bit), fp32 accumulate; both operands K-contiguous.
 // C is written as bf16 when c_bf16, else fp32.
 hipError_t gemm_bf16_nt(int M, int N, int K, const uint16_t *A, int lda, const uint16_t *B, int ldb, void *C,

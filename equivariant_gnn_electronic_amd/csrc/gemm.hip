@@ -933,6 +933,47 @@ int gemm_f32_tiles(int M, int N) {
 
 int gemm_bf16_tn_tiles(int M, int N) { return ((M + 255) / 256) * ((N + 255) / 256); }
 
+namespace {
+template <typename F>
+int blocks_per_cu(F kernel, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(kernel), threads, 0) !=
+          hipSuccess ||
+      n < 1)
+    n = 1;
+  return n;
+}
+}  // namespace
+
+int gemm_f32_tn_blocks_per_cu(int M, int N) {
+  static const int o[4] = {blocks_per_cu(gemm_f32_kernel<false, false, 1, 1>, 256),
+                           blocks_per_cu(gemm_f32_kernel<false, false, 1, 2>, 256),
+                           blocks_per_cu(gemm_f32_kernel<false, false, 2, 1>, 256),
+                           blocks_per_cu(gemm_f32_kernel<false, false, 2, 2>, 256)};
+  return o[(tile_count(M) - 1) * 2 + (tile_count(N) - 1)];
+}
+
+int cgemm_f32_dw_blocks_per_cu(int M, int N) {
+  static const int o[4] = {blocks_per_cu(cgemm_f32_kernel<false, false, false, 1, 1>, 256),
+                           blocks_per_cu(cgemm_f32_kernel<false, false, false, 1, 2>, 256),
+                           blocks_per_cu(cgemm_f32_kernel<false, false, false, 2, 1>, 256),
+                           blocks_per_cu(cgemm_f32_kernel<false, false, false, 2, 2>, 256)};
+  return o[(tile_count(M) - 1) * 2 + (tile_count(N) - 1)];
+}
+
+int gemm_bf16_tn_blocks_per_cu() {
+  static const int o = blocks_per_cu(gemm_bf16_tn_kernel<64, 2, 4, 2>, 512);
+  return o;
+}
+
+int xcd_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || n < kXcd)
+    return 32;
+  return n / kXcd;
+}
+
 hipError_t gemm_f32(int M, int N, int K, const float *A, int lda, bool a_kcontig, const float *B, int ldb,
                     bool b_kcontig, float *C, int ldc, int splits, int64_t split_stride, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;

@@ -1633,20 +1633,45 @@ int dw_splits(int64_t E) {
 }
 
 // Split count of one weight-gradient product with `tiles` output tiles and
-// `per_split` partial floats per split: at least dw_splits(E); more when the
-// output is small, up to ~1024 blocks in all (a few per CU), 128 splits and
-// 2048 edges per split, and within the partial buffer sized for dw_splits(E)
-// splits of the largest product (`cap_floats`).  A multiple of 8 from 8 up.
-int dw_splits_for(int64_t E, int tiles, int64_t per_split, int64_t cap_floats) {
+// `per_split` partial floats per split, for a kernel of which a CU holds `occ`
+// workgroups, on XCDs of `cus` CUs.  The bounds: at most 128 splits, at least
+// 2048 edges per split, within the partial buffer sized for dw_splits(E)
+// splits of the largest product (`cap_floats`).  Below 8 splits: dw_splits(E),
+// raised toward ~1024 blocks in all.  From 8 up the count is 8 q: split z runs
+// on XCD z % 8, so each XCD runs q * tiles equal blocks of E / (8 q) edges on
+// its CUs; the busiest CU runs ceil(q * tiles / cus) of them, and the product
+// takes time in proportion to ceil(q * tiles / cus) / q.  q minimises that
+// among the q that keep min(3, occ) blocks per CU on average (with fewer the
+// products wait on memory), ties to fewer splits (fewer partials to sum).
+// On the 25-tile fp32 m = 0 product of the HfO2 step, splits 16, 32, 48, 56
+// and 64 took 2.85, 2.57, 2.18, 2.23 and 2.34 ms, in line with this.
+int dw_splits_for(int64_t E, int tiles, int64_t per_split, int64_t cap_floats, int occ, int cus) {
   int64_t s = dw_splits(E);
-  int64_t want = (1024 + tiles - 1) / (tiles > 0 ? tiles : 1);
+  tiles = tiles > 0 ? tiles : 1;
+  int64_t want = (1024 + tiles - 1) / tiles;
   want = want < 128 ? want : 128;
   const int64_t by_edges = E / 2048, by_buffer = per_split > 0 ? cap_floats / per_split : s;
   if (want > by_edges) want = by_edges;
   if (want > by_buffer) want = by_buffer;
   if (want > s) s = want;
-  if (s >= 8) s = s / 8 * 8;
-  return static_cast<int>(s < 1 ? 1 : s);
+  if (s < 8) return static_cast<int>(s < 1 ? 1 : s);
+  int64_t hi = 128;
+  if (hi > by_edges) hi = by_edges;
+  if (hi > by_buffer) hi = by_buffer;
+  const int64_t q_hi = hi / 8 > 0 ? hi / 8 : 1;
+  cus = cus > 0 ? cus : 1;
+  const int64_t need = static_cast<int64_t>(occ < 3 ? (occ > 0 ? occ : 1) : 3) * cus;
+  int64_t q_lo = (need + tiles - 1) / tiles;
+  if (q_lo > q_hi) q_lo = q_hi;
+  int64_t best = q_lo, best_busy = (q_lo * tiles + cus - 1) / cus;
+  for (int64_t q = q_lo + 1; q <= q_hi; ++q) {
+    const int64_t busy = (q * tiles + cus - 1) / cus;
+    if (busy * best < best_busy * q) {  // busy / q < best_busy / best
+      best = q;
+      best_busy = busy;
+    }
+  }
+  return static_cast<int>(8 * best);
 }
 
 struct BwdWs {
@@ -2251,7 +2276,8 @@ static egnn_status layer_bwd_impl(bool edge_block, const egnn_layer_desc *d, con
         return EGNN_E_HIP;
       }
       const int64_t pn = static_cast<int64_t>(Ng) * Kg;
-      const int splits = dw_splits_for(E, gemm_bf16_tn_tiles(Ng, Kg), pn, w.P_floats);
+      const int splits =
+          dw_splits_for(E, gemm_bf16_tn_tiles(Ng, Kg), pn, w.P_floats, gemm_bf16_tn_blocks_per_cu(), xcd_cus());
       {
         Timed t(stream, "gemm_dw_bf16", 2.0 * double(E) * Ng * Kg, double(E) * (Ng + Kg) * 2.0 + double(splits) * pn * 4.0);
         e = gemm_bf16_tn_splitk(Ng, Kg, static_cast<int>(E), w.dYb[m], Ng, static_cast<const uint16_t *>(acts.A[m]), Kg,
@@ -2287,7 +2313,8 @@ static egnn_status layer_bwd_impl(bool edge_block, const egnn_layer_desc *d, con
           set_error("GEMM launch failed: %s", hipGetErrorString(e));
           return EGNN_E_HIP;
         }
-        const int splits = dw_splits_for(E, gemm_f32_tiles(Np, Kp), 2 * nb, w.P_floats);
+        const int splits = dw_splits_for(E, gemm_f32_tiles(Np, Kp), 2 * nb, w.P_floats,
+                                         cgemm_f32_dw_blocks_per_cu(Np, Kp), xcd_cus());
         {
           // dW1 + i dW2 = sum_e (dY+ + i dY-)^T (X+ - i X-), split over edges
           Timed t(stream, "cgemm_dw_f32", 2.0 * double(E) * s.Ng[m] * s.Kg[m],
@@ -2316,7 +2343,8 @@ static egnn_status layer_bwd_impl(bool edge_block, const egnn_layer_desc *d, con
       }
       // dB_m = dY_m^T A_m, split over edges, then summed in order
       const int64_t pn = static_cast<int64_t>(s.Ng[m]) * s.Kg[m];
-      const int splits = dw_splits_for(E, gemm_f32_tiles(s.Ng[m], s.Kg[m]), pn, w.P_floats);
+      const int splits = dw_splits_for(E, gemm_f32_tiles(s.Ng[m], s.Kg[m]), pn, w.P_floats,
+                                       gemm_f32_tn_blocks_per_cu(s.Ng[m], s.Kg[m]), xcd_cus());
       {
         Timed t(stream, "gemm_tn_f32", 2.0 * double(E) * s.Ng[m] * s.Kg[m],
                 double(E) * (s.Ng[m] + s.Kg[m]) * 4.0 + double(splits) * pn * 4.0);
