@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=500, help="rows of the oracle's timed sample")
     ap.add_argument("--cpu-mols", type=int, default=150, help="molecules of the oracle's timed sample (m2l, l2m)")
+    ap.add_argument("--label-order", choices=("src", "dst"), default="dst",
+                    help="m2l / l2m: blocks taken per destination atom, or per source atom (the graph's source "
+                         "grouping, made before the timed steps)")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of the plain elementwise copy (y = -x, float32) timed before the steps; it gives "
                          "the measured copy bandwidth, and a counter run sees it as a kernel of known traffic")
@@ -189,7 +192,7 @@ class LabelStep:
     """One pass of Matrix -> Label (or Label -> Matrix) over a batch of molecules,
     inputs resident on the GPU."""
 
-    def __init__(self, wl, dev):
+    def __init__(self, wl, dev, by_source=True):
         import torch
         import synth
         import equivariant_gnn_electronic_amd as eg
@@ -198,7 +201,9 @@ class LabelStep:
         self.basis = eg.Basis(synth.SVP_SHELLS, synth.SVP_MASKS)
         self.mol_ptr = torch.from_numpy(b.mol_ptr).to(dev)
         self.species = torch.from_numpy(b.species).to(dev)
-        self.graph = eg.Graph.from_csr(torch.from_numpy(b.row_ptr).to(dev), torch.from_numpy(b.src).to(dev))
+        # the source grouping is made once with the graph (outside the timed steps)
+        self.graph = eg.Graph.from_csr(torch.from_numpy(b.row_ptr).to(dev), torch.from_numpy(b.src).to(dev),
+                                       group=by_source)
         orb, bad = eg.egnn_orbital_layout(self.basis, self.mol_ptr, self.species)
         assert int(bad.item()) == 0
         self.h_elems = int(orb.mat_off[-1].item())
@@ -250,7 +255,7 @@ def cpu_baseline_labels(wl, n_mols):
 
 def run_labels(args, wl, dev):
     import torch
-    step = LabelStep(wl, dev)
+    step = LabelStep(wl, dev, by_source=args.label_order == "src")
     copy_gbs = copy_bandwidth(torch, dev, args.copy_probe_mib)
     eg = step.eg
     ms, med, timing, dropped = timed_steps(torch, eg, step, args.steps, args.warmup)
@@ -271,7 +276,8 @@ def run_labels(args, wl, dev):
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded molecule sizes and elements, N(0,1) matrix entries)",
-        "config": {"workload": args.workload, "description": wl["desc"], "molecules": b.n_mols,
+        "config": {"workload": args.workload, "description": wl["desc"], "order": args.label_order,
+                   "molecules": b.n_mols,
                    "atoms": b.n_atoms, "edges": step.E, "labels_per_block": step.n_lab,
                    "matrix_entries": step.h_elems,
                    "blocks_per_s": round((b.n_atoms + step.E) / (ms * 1e-3), 1),

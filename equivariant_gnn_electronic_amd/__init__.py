@@ -102,11 +102,37 @@ class Graph:
         return g
 
     @classmethod
-    def from_csr(cls, row_ptr, src, n_src=None, shift=None):
-        """A graph given only by its CSR (Matrix <-> Label reads row_ptr, src and shift)."""
+    def from_csr(cls, row_ptr, src, n_src=None, shift=None, group=False):
+        """A graph given by its CSR (row_ptr, src, optional shift).  With
+        group=True its source grouping (src_ptr, src_perm) is made by
+        egnn_group_sources, so Matrix <-> Label takes the source-grouped order."""
         n_dst = row_ptr.numel() - 1
-        return cls(n_dst, n_dst if n_src is None else n_src, src.numel(), row_ptr, src, shift,
-                   None, None, None, None)
+        _expect(row_ptr, "row_ptr", torch.int32, (n_dst + 1,))
+        _expect(src, "src", torch.int32, (None,))
+        if shift is not None:
+            _expect(shift, "shift", torch.int8, (src.numel(), 3))
+        g = cls(n_dst, n_dst if n_src is None else n_src, src.numel(), row_ptr, src, shift,
+                None, None, None, None)
+        if group:
+            egnn_group_sources(g)
+        return g
+
+
+def egnn_group_sources(graph: Graph):
+    """Write graph.src_ptr [n_src + 1] and graph.src_perm [n_edges]: the edge ids
+    of each source in ascending order (sources outside [0, n_src) in no group)."""
+    lib = _lib.load()
+    _expect(graph.src, "src", torch.int32, (graph.n_edges,))
+    dev = graph.src.device
+    graph.src_ptr = torch.empty(graph.n_src + 1, dtype=torch.int32, device=dev)
+    graph.src_perm = torch.empty(max(graph.n_edges, 1), dtype=torch.int32, device=dev)
+    nbytes = ct.c_size_t(0)
+    _lib.check("egnn_group_sources_workspace",
+               lib.egnn_group_sources_workspace(graph.n_src, graph.n_edges, ct.byref(nbytes)))
+    ws = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=dev)
+    g = graph.c_struct()
+    _lib.check("egnn_group_sources", lib.egnn_group_sources(ct.byref(g), _ptr(ws), nbytes.value, _stream()))
+    return graph
 
 
 def layer_desc(lmax, mmax, C, n_rbf, r_cut, storage=EGNN_F32):

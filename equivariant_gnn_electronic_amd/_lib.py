@@ -61,6 +61,8 @@ SIGNATURES = {
     "egnn_build_graph_workspace": (ct.c_int, [_i32, _i32, _D3, _D3, _u32, _f64, _i64, _PSZ]),
     "egnn_build_graph": (ct.c_int, [_vp, _D3, _D3, _u32, _f64, _G, _vp, _sz, _vp]),
     "egnn_build_graph_noalloc": (ct.c_int, [_vp, _D3, _D3, _u32, _f64, _G, _vp]),
+    "egnn_group_sources_workspace": (ct.c_int, [_i32, _i64, _PSZ]),
+    "egnn_group_sources": (ct.c_int, [_G, _vp, _sz, _vp]),
     "egnn_layer_weight_count": (ct.c_size_t, [_L]),
     "egnn_geom_stride": (ct.c_int32, [_L]),
     "egnn_edge_geom": (ct.c_int, [_L, _G, _vp, _vp]),

@@ -15,6 +15,7 @@
 // fill order use integer atomics.
 #pragma clang fp contract(off)
 
+#include <climits>
 #include <mutex>
 
 #include "common.h"
@@ -323,6 +324,41 @@ __global__ void __launch_bounds__(256) src_sort_kernel(int n_src, const int *src
 
 constexpr int kMaxGroup = 65535;
 
+// Source grouping of a caller's CSR: sources outside [0, n_src) are left out.
+__global__ void src_count_checked(const int *src, int64_t E, int n_src, int *src_count) {
+  int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  const int s = src[e];
+  if (s >= 0 && s < n_src) atomicAdd(&src_count[s], 1);
+}
+
+__global__ void src_fill_checked(const int *src, int64_t E, int n_src, const int *src_ptr, int *src_cursor,
+                                 int *tmp) {
+  int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  const int s = src[e];
+  if (s < 0 || s >= n_src) return;
+  const int slot = atomicAdd(&src_cursor[s], 1);
+  tmp[src_ptr[s] + slot] = static_cast<int>(e);
+}
+
+struct GroupWs {
+  int *src_count, *src_cursor, *tmp;
+  size_t bytes;
+};
+
+GroupWs carve_group(void *base, int n_src, int64_t E) {
+  GroupWs w{};
+  char *p = static_cast<char *>(base);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { char *r = p ? p + o : nullptr; o += align256(bytes); return r; };
+  w.src_count = reinterpret_cast<int *>(take(sizeof(int) * (n_src + 1)));
+  w.src_cursor = reinterpret_cast<int *>(take(sizeof(int) * (n_src + 1)));
+  w.tmp = reinterpret_cast<int *>(take(sizeof(int) * (E > 0 ? E : 1)));
+  w.bytes = o;
+  return w;
+}
+
 }  // namespace
 }  // namespace egnn
 
@@ -500,3 +536,41 @@ egnn_status build_graph_impl(const double *pos, const double lo[3], const double
 
 }  // namespace
 }  // namespace egnn
+
+extern "C" egnn_status egnn_group_sources_workspace(int32_t n_src, int64_t n_edges, size_t *bytes) {
+  clear_error();
+  EGNN_REQUIRE(bytes, "null argument");
+  EGNN_REQUIRE(n_src >= 0, "negative source count");
+  EGNN_REQUIRE(n_edges >= 0 && n_edges <= INT_MAX, "n_edges must be 0..2^31 - 1");
+  *bytes = carve_group(nullptr, n_src, n_edges).bytes;
+  return EGNN_OK;
+}
+
+extern "C" egnn_status egnn_group_sources(egnn_graph *gr, void *ws, size_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  EGNN_REQUIRE(gr, "graph is null");
+  EGNN_REQUIRE(gr->n_src >= 0, "negative source count");
+  EGNN_REQUIRE(gr->n_edges >= 0 && gr->n_edges <= INT_MAX, "n_edges must be 0..2^31 - 1");
+  EGNN_REQUIRE(gr->src_ptr, "src_ptr is null");
+  const int n_src = gr->n_src;
+  const int64_t E = gr->n_edges;
+  if (E > 0) EGNN_REQUIRE(gr->src && gr->src_perm, "src or src_perm is null");
+  GroupWs w = carve_group(ws, n_src, E);
+  if (!ws || ws_bytes < w.bytes) {
+    set_error("workspace of %zu bytes, need %zu", ws_bytes, w.bytes);
+    return EGNN_E_WORKSPACE;
+  }
+  constexpr int T = 256;
+  const int rows_per_block = T / kWave;
+  Timed t(stream, "group_sources", 0.0, double(E) * 4.0 * 3.0 + double(n_src) * 4.0);
+  fill_int<<<ceil_div(n_src + 1, T), T, 0, stream>>>(w.src_count, n_src + 1, 0);
+  fill_int<<<ceil_div(n_src + 1, T), T, 0, stream>>>(w.src_cursor, n_src + 1, 0);
+  if (E > 0) src_count_checked<<<ceil_div(E, T), T, 0, stream>>>(gr->src, E, n_src, w.src_count);
+  scan_exclusive<<<1, kScanThreads, 0, stream>>>(w.src_count, gr->src_ptr, n_src, nullptr, nullptr);
+  if (E > 0 && n_src > 0) {
+    src_fill_checked<<<ceil_div(E, T), T, 0, stream>>>(gr->src, E, n_src, gr->src_ptr, w.src_cursor, w.tmp);
+    src_sort_kernel<<<ceil_div(n_src, rows_per_block), T, 0, stream>>>(n_src, gr->src_ptr, w.tmp, gr->src_perm);
+  }
+  EGNN_CHECK_LAUNCH();
+  return EGNN_OK;
+}

@@ -306,6 +306,32 @@ __global__ void fill_i32(int *p, int64_t n, int v) {
 }
 __global__ void zero_u64(unsigned long long *p) { *p = 0ull; }
 
+// Source-grouped order: an edge whose source is no atom is in no group, so the
+// main kernel never meets it.  It is a skipped block: counted here, and in
+// Matrix -> Label its label row is zeroed here.
+__global__ void __launch_bounds__(256) ungrouped_kernel(const int *__restrict__ src, int n_edges, int n_atoms,
+                                                        int n_lab, float *__restrict__ lab_e_out,
+                                                        unsigned long long *skipped) {
+  const int lane = threadIdx.x & (kLW - 1);
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  bool bad = false;
+  if (e < n_edges) {
+    const int s = src[e];
+    bad = s < 0 || s >= n_atoms;
+  }
+  const unsigned long long m = __ballot(bad);
+  if (lane == 0 && m && skipped) atomicAdd(skipped, static_cast<unsigned long long>(__popcll(m)));
+  if (lab_e_out) {
+    unsigned long long rem = m;
+    while (rem) {  // the wave zeroes each such row together
+      const int l = __ffsll(rem) - 1;
+      rem &= rem - 1;
+      const int64_t eb = static_cast<int64_t>(blockIdx.x) * blockDim.x + (threadIdx.x - lane) + l;
+      for (int q = lane; q < n_lab; q += kLW) lab_e_out[eb * n_lab + q] = 0.0f;
+    }
+  }
+}
+
 // One wave per structure: each atom's first orbital is an exclusive scan of
 // the orbital counts over the structure's atoms, 64 at a time.
 __global__ void __launch_bounds__(256) layout_kernel(int slot, int n_mols, int n_atoms, const int *__restrict__ mol_ptr,
@@ -383,41 +409,72 @@ struct Rows {
   int n_atoms, n_mols;
   const int *row_ptr, *src;
   const int8_t *shift;
+  const int *src_ptr, *src_perm;  // grouped: the rows are source atoms, their blocks in src_perm order
+  const int *mol_ptr;
   const int *species, *atom_orb, *atom_mol, *mol_norb;
   const int64_t *mat_off;
   int64_t h_elems;
+  int n_edges;
   int nodes, edges;  // 1 = on-site blocks / edge blocks requested
+  int grouped;
   int vec4;          // label rows are whole 16-byte units at 16-byte aligned addresses
 };
 
-// Block bi of destination row j: the on-site block first (when requested),
-// then the row's edges.  A block with no place in a matrix gets the empty
-// template pair (all labels zero, nothing written).
+// Block bi of row r: the on-site block first (when requested), then the
+// row's edges.  By destination rows (r = j): edge row_ptr[j] + t, source
+// src[e].  By source rows (r = i): edge src_perm[src_ptr[i] + t], whose
+// destination is the row of the CSR that holds it, searched among the atoms
+// of i's structure (an edge outside them has no block anyway).  A block with
+// no place in a matrix gets the empty template pair (all labels zero,
+// nothing written).
 struct Blk {
   int64_t base, out;
   int ld, pair, node;
 };
 
-__device__ inline Blk block_of(const Rows &R, const LabelTable &tb, int64_t j, int bi, int e0, bool *ok_out) {
+__device__ inline Blk block_of(const Rows &R, const LabelTable &tb, int64_t r, int bi, int e0, bool *ok_out) {
   const int T = tb.n_tmpl;
   Blk k;
-  int i;
+  int i, j;
+  bool ok = true;
   if (R.nodes && bi == 0) {
-    i = static_cast<int>(j);
+    i = j = static_cast<int>(r);
     k.node = 1;
-    k.out = j;
-  } else {
+    k.out = r;
+  } else if (!R.grouped) {
     const int64_t e = static_cast<int64_t>(e0) + bi - R.nodes;
+    j = static_cast<int>(r);
     i = R.src[e];
     k.node = 0;
     k.out = e;
+  } else {
+    const int e = R.src_perm[static_cast<int64_t>(e0) + bi - R.nodes];
+    i = static_cast<int>(r);
+    j = -1;
+    ok = e >= 0 && e < R.n_edges;
+    k.node = 0;
+    k.out = ok ? e : 0;
+    const int mi = R.atom_mol[i];
+    if (ok && mi >= 0 && mi < R.n_mols) {
+      const int a0 = min(max(R.mol_ptr[mi], 0), R.n_atoms);
+      const int a1 = min(max(R.mol_ptr[mi + 1], a0), R.n_atoms);
+      if (e >= R.row_ptr[a0] && e < R.row_ptr[a1]) {
+        int lo = a0, hi = a1;  // the largest j < a1 with row_ptr[j] <= e
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (R.row_ptr[mid] <= e) lo = mid; else hi = mid;
+        }
+        j = lo;
+      }
+    }
   }
-  bool ok = i >= 0 && i < R.n_atoms;
+  ok = ok && i >= 0 && i < R.n_atoms && j >= 0 && j < R.n_atoms;
   if (!k.node && R.shift) {
     const int8_t *s = R.shift + 3 * k.out;
     ok = ok && s[0] == 0 && s[1] == 0 && s[2] == 0;
   }
   const int ic = ok ? i : 0;
+  j = ok ? j : 0;
   const int mj = R.atom_mol[j], mi = R.atom_mol[ic];
   ok = ok && mj >= 0 && mj < R.n_mols && mi == mj;
   const int si = R.species[ic], sj = R.species[j];
@@ -503,8 +560,17 @@ __global__ void __launch_bounds__(kLW * kLWaves) labels_kernel(int slot, Rows R,
   auto row_at = [&](int64_t j) {
     Pos p{j, 0, 0, 0};
     while (p.j < j_end) {
-      p.e0 = R.edges ? R.row_ptr[p.j] : 0;
-      p.nb = R.nodes + (R.edges ? R.row_ptr[p.j + 1] - p.e0 : 0);
+      int e1 = 0;
+      if (!R.edges) {
+        p.e0 = 0;
+      } else if (!R.grouped) {
+        p.e0 = R.row_ptr[p.j];
+        e1 = R.row_ptr[p.j + 1];
+      } else {  // a group's range, kept inside src_perm
+        p.e0 = min(max(R.src_ptr[p.j], 0), R.n_edges);
+        e1 = min(max(R.src_ptr[p.j + 1], p.e0), R.n_edges);
+      }
+      p.nb = R.nodes + (e1 - p.e0);
       if (p.nb > 0) break;
       p.j += stride;
     }
@@ -787,12 +853,21 @@ egnn_status run_labels(bool to_label, const egnn_basis *b, const egnn_orbitals *
     EGNN_CHECK_LAUNCH();
   }
   if (!work) return EGNN_OK;
+  // the source-grouped order when the graph carries it (one wave then owns a
+  // source atom's row strip of the matrix: whole matrix rows for a fully
+  // connected structure)
+  const bool grouped = edges && g->src_ptr != nullptr && (g->n_edges == 0 || g->src_perm != nullptr);
   Rows R;
   R.n_atoms = o->n_atoms;
   R.n_mols = o->n_mols;
   R.row_ptr = edges ? g->row_ptr : nullptr;
   R.src = edges ? g->src : nullptr;
   R.shift = edges ? g->shift : nullptr;
+  R.src_ptr = grouped ? g->src_ptr : nullptr;
+  R.src_perm = grouped ? g->src_perm : nullptr;
+  R.mol_ptr = o->mol_ptr;
+  R.n_edges = edges ? static_cast<int>(g->n_edges) : 0;
+  R.grouped = grouped ? 1 : 0;
   R.species = o->species;
   R.atom_orb = o->atom_orb;
   R.atom_mol = o->atom_mol;
@@ -813,6 +888,12 @@ egnn_status run_labels(bool to_label, const egnn_basis *b, const egnn_orbitals *
   // many as the matrix has entries) and writes each entry
   Timed tm(stream, to_label ? "matrix_to_label" : "label_to_matrix", 0.0,
            to_label ? 4.0 * (double(rows) * info.n_lab + double(h_elems)) : 8.0 * double(h_elems));
+  if (grouped && g->n_edges > 0 && (skip || to_label)) {
+    ungrouped_kernel<<<ceil_div(g->n_edges, 256), 256, 0, stream>>>(g->src, static_cast<int>(g->n_edges),
+                                                                    o->n_atoms, info.n_lab,
+                                                                    to_label ? le_out : nullptr, skip);
+    EGNN_CHECK_LAUNCH();
+  }
   // a multiple of 8 workgroups: rows are dealt to the XCDs in contiguous ranges
   int64_t blocks = ((static_cast<int64_t>(o->n_atoms) + kLWaves - 1) / kLWaves + 7) / 8 * 8;
   if (blocks > 2048) blocks = 2048;

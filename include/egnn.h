@@ -141,6 +141,26 @@ egnn_status egnn_build_graph_noalloc(const double *pos, const double lo[3] /*hos
                                      egnn_graph *g /*host struct, device arrays*/, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Source grouping of a graph given by its CSR  [review of arXiv 2507.03840,
+ * "What carries the argument": the backward's reverse pattern; MALOQ Sec.
+ * III-B2: Matrix <-> Label over a source atom's row strip of a matrix]
+ *
+ * egnn_build_graph writes src_ptr / src_perm itself.  For a graph made
+ * elsewhere (row_ptr, src, n_src, n_edges), this writes them from src:
+ * src_perm[src_ptr[s] .. src_ptr[s+1]) lists the edge ids of source s in
+ * ascending order, s = 0..n_src-1.  Edges whose src lies outside [0, n_src)
+ * are in no group: src_ptr[n_src] counts the grouped edges, and src_perm
+ * past it is left as it was.  src_ptr [n_src + 1] and src_perm [n_edges] are
+ * the caller's; n_edges <= 2^31 - 1.  A group is ordered by counting ranks,
+ * quadratic in its size (fine for atom-sized groups).  The workspace (from the query) is the
+ * caller's too, needs no clearing, and is not used after the call's kernels
+ * end.  Asynchronous on `stream`; EGNN_E_WORKSPACE when ws_bytes is short.
+ * ------------------------------------------------------------------------- */
+egnn_status egnn_group_sources_workspace(int32_t n_src, int64_t n_edges, size_t *bytes /*host out*/);
+egnn_status egnn_group_sources(egnn_graph *g /*host struct, device arrays*/, void *ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Layer description
  * ------------------------------------------------------------------------- */
 typedef struct {
@@ -334,8 +354,12 @@ egnn_status egnn_assemble_bsr(const egnn_graph *g, int32_t n_orb, const float *h
  * block of every graph edge (h_edge rows = edges, in the graph's order; rows
  * of H = the source atom's orbitals, columns = the destination's).  The
  * graph is a destination-sorted CSR over the batch's atoms (n_dst = n_src =
- * n_atoms; only row_ptr, src, shift and n_edges are read; shift may be
- * NULL).  An edge whose ends lie in different structures, or with a nonzero
+ * n_atoms; row_ptr, src, shift and n_edges are read; shift may be NULL).
+ * When it also carries src_ptr and src_perm (both non-NULL), they must group
+ * its edges by source as egnn_group_sources writes them; the blocks are then
+ * taken one source atom at a time, so one wave reads (writes) that atom's
+ * rows of the matrix, whole rows for a fully connected structure.  The
+ * results are the same either way; edges in no group count as skipped.  An edge whose ends lie in different structures, or with a nonzero
  * image shift, has no block in a dense matrix: its labels are zero and
  * nothing is written.  Each ordered atom pair must appear at most once.
  *

@@ -389,3 +389,38 @@ def test_edge_geom_rejects_misaligned_output(lib):
     g = _fake_graph(10, 10, 100)
     st = lib.egnn_edge_geom(ct.byref(d), ct.byref(g), ct.c_void_p(0x1004), None)
     assert st == _lib.EGNN_E_ARG and b"aligned" in lib.egnn_last_error()
+
+
+def test_group_sources_host_checks(lib):
+    """Source grouping: the workspace query grows with sources and edges, and the
+    call refuses bad arguments and a short workspace before any launch."""
+    from equivariant_gnn_electronic_amd import _lib
+    a, b = ct.c_size_t(), ct.c_size_t()
+    assert lib.egnn_group_sources_workspace(100, 1000, ct.byref(a)) == 0
+    assert lib.egnn_group_sources_workspace(100, 2000, ct.byref(b)) == 0
+    assert b.value >= a.value + 4 * 1000 - 256 and a.value >= 4 * (2 * 101 + 1000)
+    assert lib.egnn_group_sources_workspace(-1, 10, ct.byref(a)) == _lib.EGNN_E_ARG
+    assert lib.egnn_group_sources_workspace(10, -1, ct.byref(a)) == _lib.EGNN_E_ARG
+    assert lib.egnn_group_sources_workspace(10, 2 ** 31, ct.byref(a)) == _lib.EGNN_E_ARG
+    assert lib.egnn_group_sources(None, None, 0, None) == _lib.EGNN_E_ARG
+    g = _fake_graph(10, 10, 100)
+    assert lib.egnn_group_sources_workspace(10, 100, ct.byref(a)) == 0
+    st = lib.egnn_group_sources(ct.byref(g), ct.c_void_p(0x1000), a.value - 1, None)
+    assert st == _lib.EGNN_E_WORKSPACE and b"workspace" in lib.egnn_last_error()
+    g.src_ptr = None
+    assert lib.egnn_group_sources(ct.byref(g), ct.c_void_p(0x1000), a.value, None) == _lib.EGNN_E_ARG
+    g = _fake_graph(10, 10, 100)
+    g.src_perm = None
+    assert lib.egnn_group_sources(ct.byref(g), ct.c_void_p(0x1000), a.value, None) == _lib.EGNN_E_ARG
+
+
+def test_binding_group_rejects_bad_csr():
+    import torch
+    import equivariant_gnn_electronic_amd as eg
+    rp = torch.tensor([0, 1, 2], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        eg.Graph.from_csr(rp.to(torch.int64), torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        eg.Graph.from_csr(rp, torch.zeros(2, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        eg.Graph.from_csr(rp, torch.zeros(2, dtype=torch.int32), shift=torch.zeros((3, 3), dtype=torch.int8))

@@ -31,7 +31,9 @@ def _t(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def _setup(batch, shells, masks, dev, shift=None, src=None, row_ptr=None):
+def _setup(batch, shells, masks, dev, shift=None, src=None, row_ptr=None, group=False):
+    """Basis, layout and graph; group=True gives the graph its source grouping,
+    so the kernels take the blocks one source atom at a time."""
     basis = eg.Basis(shells, masks)
     mol_ptr = _t(batch.mol_ptr.astype(np.int32), dev)
     species = _t(batch.species.astype(np.int32), dev)
@@ -39,8 +41,11 @@ def _setup(batch, shells, masks, dev, shift=None, src=None, row_ptr=None):
     rp = batch.row_ptr if row_ptr is None else row_ptr
     sr = batch.src if src is None else src
     g = eg.Graph.from_csr(_t(rp.astype(np.int32), dev), _t(sr.astype(np.int32), dev),
-                          shift=None if shift is None else _t(shift.astype(np.int8), dev))
+                          shift=None if shift is None else _t(shift.astype(np.int8), dev), group=group)
     return basis, orb, bad, g
+
+
+ORDERS = {"by_dst": False, "by_src": True}
 
 
 def _check_layout(orb, batch, shells, masks):
@@ -74,12 +79,13 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("order", list(ORDERS))
 @pytest.mark.parametrize("case", list(CASES))
-def test_matrix_to_label_and_back(dev, case):
+def test_matrix_to_label_and_back(dev, case, order):
     make, shells, masks = CASES[case]
     batch = make()
-    print(f"[labels] case={case} atoms={batch.n_atoms} edges={batch.n_edges}", flush=True)
-    basis, orb, bad, g = _setup(batch, shells, masks, dev)
+    print(f"[labels] case={case} order={order} atoms={batch.n_atoms} edges={batch.n_edges}", flush=True)
+    basis, orb, bad, g = _setup(batch, shells, masks, dev, group=ORDERS[order])
     lay = _check_layout(orb, batch, shells, masks)
     assert int(bad.item()) == 0
     n = int(lay[3][-1])
@@ -123,7 +129,8 @@ def test_nodes_only_and_edges_only(dev):
     assert_close(Hg.cpu().numpy(), Href, TOL, "H on-site")
 
 
-def test_skipped_edges(dev):
+@pytest.mark.parametrize("order", list(ORDERS))
+def test_skipped_edges(dev, order):
     """Edges across structures and edges with an image shift have no block."""
     batch = synth.make_molecule_batch(25, 6, 2, 8)
     shells, masks = synth.SVP_SHELLS, synth.SVP_MASKS
@@ -133,7 +140,8 @@ def test_skipped_edges(dev):
     row_ptr[1:] += 1
     shift = np.zeros((len(src), 3), np.int8)
     shift[2, 0] = -1                                  # and shift an ordinary edge
-    basis, orb, _, g = _setup(batch, shells, masks, dev, shift=shift, src=src, row_ptr=row_ptr)
+    basis, orb, _, g = _setup(batch, shells, masks, dev, shift=shift, src=src, row_ptr=row_ptr,
+                              group=ORDERS[order])
     lay = olab.orbital_layout(batch.mol_ptr, batch.species, shells, masks)
     H = synth.make_matrix_values(35, lay[3][-1])
     dst = _dst(row_ptr)
@@ -183,14 +191,15 @@ def test_invalid_structure_range_is_counted(dev):
     assert orb.mol_norb.cpu().numpy()[1] == 0
 
 
-def test_bench_batch_sampled(dev):
+@pytest.mark.parametrize("order", list(ORDERS))
+def test_bench_batch_sampled(dev, order):
     """The benchmark's batch (4,096 molecules of 10-50 atoms, fully connected):
     the whole layout exactly, and sampled label rows and matrix entries
     against the oracle run on those rows only."""
     batch = synth.make_molecule_batch(40, 4096, 10, 50)
     shells, masks = synth.SVP_SHELLS, synth.SVP_MASKS
-    print(f"[labels] bench batch atoms={batch.n_atoms} edges={batch.n_edges}", flush=True)
-    basis, orb, bad, g = _setup(batch, shells, masks, dev)
+    print(f"[labels] bench batch order={order} atoms={batch.n_atoms} edges={batch.n_edges}", flush=True)
+    basis, orb, bad, g = _setup(batch, shells, masks, dev, group=ORDERS[order])
     lay = _check_layout(orb, batch, shells, masks)
     H = synth.make_matrix_values(41, lay[3][-1])
     Hd = _t(H, dev)
@@ -213,3 +222,49 @@ def test_bench_batch_sampled(dev):
     nr = float(d.norm() / Hd.double().norm())
     ma = float(d.abs().max() / Hd.abs().max())
     assert nr <= TOL and ma <= TOL, (nr, ma)
+
+
+def test_group_sources_matches_stable_order(dev):
+    """egnn_group_sources: src_ptr counts each source's edges and src_perm lists
+    them in ascending edge order (a stable sort by source); sources outside
+    [0, n_src) are in no group."""
+    rng = np.random.default_rng(44)
+    n, E = 300, 5000
+    src = rng.integers(0, n, E).astype(np.int32)
+    src[rng.choice(E, 7, replace=False)] = n + 3            # out of range: in no group
+    src[rng.choice(E, 5, replace=False)] = -2
+    row_ptr = np.linspace(0, E, n + 1).round().astype(np.int32)
+    g = eg.Graph.from_csr(_t(row_ptr, dev), _t(src, dev), group=True)
+    ok = (src >= 0) & (src < n)
+    want_ptr = np.concatenate([[0], np.cumsum(np.bincount(src[ok], minlength=n))])
+    want_perm = np.nonzero(ok)[0][np.argsort(src[ok], kind="stable")]
+    got_ptr = g.src_ptr.cpu().numpy()
+    np.testing.assert_array_equal(got_ptr, want_ptr)
+    np.testing.assert_array_equal(g.src_perm[:int(got_ptr[-1])].cpu().numpy(), want_perm)
+
+
+@pytest.mark.parametrize("order", list(ORDERS))
+def test_out_of_range_source_is_skipped(dev, order):
+    """An edge whose source is no atom has no block: counted once as skipped in
+    both orders (in the source order it is in no group); every other block as usual."""
+    batch = synth.make_molecule_batch(26, 5, 2, 7)
+    shells, masks = synth.SVP_SHELLS, synth.SVP_MASKS
+    src = batch.src.astype(np.int32).copy()
+    bad_e = len(src) // 2
+    src[bad_e] = batch.n_atoms + 5
+    basis, orb, _, g = _setup(batch, shells, masks, dev, src=src, group=ORDERS[order])
+    lay = olab.orbital_layout(batch.mol_ptr, batch.species, shells, masks)
+    H = synth.make_matrix_values(37, lay[3][-1])
+    he, hn, skipped = eg.egnn_matrix_to_label(basis, orb, g, _t(H, dev))
+    assert int(skipped.item()) == 1
+    keep = np.arange(len(src)) != bad_e
+    dst = batch.dst()
+    ref_e, ref_n = olab.matrix_to_labels(H, src[keep], dst[keep], None, batch.species, lay, shells, masks)
+    got = he.cpu().numpy()
+    assert np.all(got[bad_e] == 0)
+    assert_close(got[keep], ref_e, TOL, "h_edge")
+    assert_close(hn.cpu().numpy(), ref_n, TOL, "h_node")
+    Hg, skipped = eg.egnn_label_to_matrix(basis, orb, g, he, hn)
+    assert int(skipped.item()) == 1
+    Href = olab.labels_to_matrix(ref_e, ref_n, src[keep], dst[keep], None, batch.species, lay, shells, masks)
+    assert_close(Hg.cpu().numpy(), Href, TOL, "H")
