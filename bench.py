@@ -90,7 +90,7 @@ def parse():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="(no GPU) turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script into "
                          "the traffic summary under profiles/ and exit")
-    ap.add_argument("--summarize-sq", nargs=2, metavar=("PASS1_DIR", "PASS2_DIR"),
+    ap.add_argument("--summarize-sq", nargs="+", metavar="PASS_DIR",
                     help="(no GPU) turn two rocprofv3 --pmc runs of this script (the SQ counter sets named in "
                          "the summary it writes) into profiles/sq_<workload>.txt and exit")
     ap.add_argument("--sweep", action="store_true",
@@ -394,9 +394,10 @@ SQ_PASS1 = ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_W
             "SQ_INSTS_VALU", "SQ_ACTIVE_INST_ANY")
 SQ_PASS2 = ("GRBM_GUI_ACTIVE", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
             "SQ_ACTIVE_INST_LDS", "SQ_INST_CYCLES_VMEM", "SQ_WAIT_INST_LDS")
+SQ_PASS3 = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES")
 
 
-def summarize_sq(d1, d2, workload, argv):
+def summarize_sq(d1, d2, workload, argv, d3=None):
     """profiles/sq_<workload>.txt: per kernel, instruction mix per wave and the
     VALU issue fraction = SQ_INSTS_VALU x 4 cycles (a wave64 VALU instruction on a
     16-lane SIMD) / (1024 SIMDs x the kernel's cycles, GRBM_GUI_ACTIVE / 8 XCDs)."""
@@ -408,30 +409,39 @@ def summarize_sq(d1, d2, workload, argv):
     def load(d):
         per = collections.defaultdict(collections.Counter)
         meta = {}
+        span = {}
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(path)):
                 k = (path, r["Dispatch_Id"])
                 per[k][r["Counter_Name"]] += float(r["Counter_Value"])
                 meta[k] = (r["Kernel_Name"], r["VGPR_Count"], r["Accum_VGPR_Count"], r["LDS_Block_Size"])
+                if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                    span[k] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
         by = collections.defaultdict(collections.Counter)
         n = collections.Counter()
         m = {}
         for k, c in per.items():
             by[meta[k][0]].update(c)
+            by[meta[k][0]]["_ns"] += span.get(k, 0)
             n[meta[k][0]] += 1
             m[meta[k][0]] = meta[k]
         return by, n, m
 
     a, na, ma = load(d1)
     b, _, _ = load(d2)
+    c3 = load(d3)[0] if d3 else {}
     cmd = f"python bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --no-extra --copy-probe-mib 256"
     lines = [f"# SQ counters per kernel of the {workload} step (sums over every dispatch of the run), from rocprofv3",
              "# made by (from the repository root, on one MI355X):",
              f"#   rocprofv3 --pmc {' '.join(SQ_PASS1)} --output-format csv -d <PASS1_DIR> -o run -- {cmd}",
              f"#   rocprofv3 --pmc {' '.join(SQ_PASS2)} --output-format csv -d <PASS2_DIR> -o run -- {cmd}",
+             *([f"#   rocprofv3 --pmc {' '.join(SQ_PASS3)} --output-format csv -d <PASS3_DIR> -o run -- {cmd}",
+                "# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 * 256 CUs * 4 SIMDs), both from pass 3"]
+               if d3 else []),
              f"#   python {' '.join(argv)}",
              "# valu_issue = SQ_INSTS_VALU * 4 / (1024 * GRBM_GUI_ACTIVE / 8): the fraction of SIMD cycles issuing VALU",
-             "# (wave64 on 16-lane SIMDs; GRBM_GUI_ACTIVE summed over the 8 XCDs); per-wave figures are means",
+             "# (wave64 on 16-lane SIMDs; GRBM_GUI_ACTIVE summed over the 8 XCDs); per-wave figures are means;",
+             "# clock = GRBM_GUI_ACTIVE / 8 over the dispatches' time (End - Start), the shader clock the kernel ran at",
              f"workload: {workload}"]
     rows = []
     for name, c in a.items():
@@ -447,7 +457,9 @@ def summarize_sq(d1, d2, workload, argv):
         w = c["SQ_WAVES"]
         wc = c["SQ_WAVE_CYCLES"]
         vg, ag, lds = ma[name][1:]
-        lines.append(f"kernel: {short}  dispatches {na[name]}  vgpr {vg} agpr {ag} lds {lds} B")
+        ns = c2.get("_ns", 0)
+        clk = f"  clock {gui / 8 / ns:.2f} GHz" if ns > 0 else ""
+        lines.append(f"kernel: {short}  dispatches {na[name]}  vgpr {vg} agpr {ag} lds {lds} B{clk}")
         lines.append(f"  per wave: VALU {c['SQ_INSTS_VALU'] / w:.0f}, VMEM rd {c2['SQ_INSTS_VMEM_RD'] / w:.0f}, "
                      f"VMEM wr {c2['SQ_INSTS_VMEM_WR'] / w:.0f}, LDS {c2['SQ_INSTS_LDS'] / w:.0f}, "
                      f"SALU {c2['SQ_INSTS_SALU'] / w:.0f}, wave cycles {wc / w:.0f}")
@@ -455,6 +467,9 @@ def summarize_sq(d1, d2, workload, argv):
                      f"{c['SQ_ACTIVE_INST_VALU'] / wc:.3f}, active any {c['SQ_ACTIVE_INST_ANY'] / wc:.3f}, "
                      f"waiting (any) {c['SQ_WAIT_ANY'] / wc:.3f}, waiting to issue {c['SQ_WAIT_INST_ANY'] / wc:.3f}, "
                      f"active LDS {c2['SQ_ACTIVE_INST_LDS'] / wc:.3f}")
+        m3 = c3.get(name) if d3 else None
+        if m3 and m3.get("GRBM_GUI_ACTIVE", 0) > 0:
+            lines.append(f"  mfma_busy {m3['SQ_VALU_MFMA_BUSY_CYCLES'] / (m3['GRBM_GUI_ACTIVE'] / 8 * 1024):.3f}")
     path = os.path.join(ROOT, "profiles", f"sq_{workload}.txt")
     with open(path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -692,7 +707,10 @@ def main():
                           args.copy_probe_mib, sys.argv)
         return
     if args.summarize_sq:
-        summarize_sq(args.summarize_sq[0], args.summarize_sq[1], args.workload, sys.argv)
+        if len(args.summarize_sq) not in (2, 3):
+            raise SystemExit("--summarize-sq takes PASS1_DIR PASS2_DIR [PASS3_DIR]")
+        summarize_sq(*args.summarize_sq[:2], args.workload, sys.argv,
+                     args.summarize_sq[2] if len(args.summarize_sq) == 3 else None)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is not built",
