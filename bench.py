@@ -258,7 +258,8 @@ def run_labels(args, wl, dev):
     step = LabelStep(wl, dev, by_source=args.label_order == "src")
     copy_gbs = copy_bandwidth(torch, dev, args.copy_probe_mib)
     eg = step.eg
-    ms, med, timing, dropped = timed_steps(torch, eg, step, args.steps, args.warmup)
+    ts = timed_steps(torch, eg, step, args.steps, args.warmup)
+    ms, med, timing, dropped = ts
     fam, roof = roofline(timing, "f32", args.workload)
     b = step.batch
     kernels = kernel_table(timing, args.steps, copy_gbs)
@@ -281,7 +282,8 @@ def run_labels(args, wl, dev):
                    "atoms": b.n_atoms, "edges": step.E, "labels_per_block": step.n_lab,
                    "matrix_entries": step.h_elems,
                    "blocks_per_s": round((b.n_atoms + step.E) / (ms * 1e-3), 1),
-                   "median_step_ms": round(med, 4)},
+                   "median_step_ms": round(med, 4),
+                   "ms_per_step_without_kernel_events": round(ts.ms_no_kernel_events, 4)},
         "roofline": dict(kernel=fam, **roof),
         "hbm_copy_gbs": copy_gbs,
         "kernels": kernels,
@@ -632,10 +634,18 @@ def sweep(dev, warmup, reps):
                 points=points)
 
 
+class TimedSteps(tuple):
+    """(wall ms per step, median event ms per step, timing, dropped), plus
+    `.ms_no_kernel_events`: the wall ms per step of the same number of steps run
+    again right after, with the per-launch events off (their cost = the difference)."""
+    ms_no_kernel_events = None
+
+
 def timed_steps(torch, eg, step, steps, warmup):
     """Run `warmup` untimed steps, then `steps` timed ones with per-launch HIP-event
     timing on (egnn_timing_*) and one pair of events around each step on the launch
-    stream.  Returns (wall ms per step, median event ms per step, timing, dropped)."""
+    stream.  Then the same number of steps again with the per-launch events off,
+    outside the timed region, to state what the events cost."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -653,7 +663,15 @@ def timed_steps(torch, eg, step, steps, warmup):
     eg.egnn_timing_enable(False)
     timing, dropped = eg.egnn_timing_collect()
     med = float(np.median([a.elapsed_time(b) for a, b in ev]))
-    return (t1 - t0) * 1e3 / steps, med, timing, dropped
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    out = TimedSteps(((t1 - t0) * 1e3 / steps, med, timing, dropped))
+    out.ms_no_kernel_events = (t3 - t2) * 1e3 / steps
+    return out
 
 
 def kernel_table(timing, steps, copy_gbs):
@@ -683,12 +701,14 @@ def extra_workloads(torch, dev, names, steps, warmup, copy_gbs):
     for name in names:
         wl = WORKLOADS[name]
         step = Step(wl, dev)
-        ms, med, timing, dropped = timed_steps(torch, step.eg, step, steps, warmup)
+        ts = timed_steps(torch, step.eg, step, steps, warmup)
+        ms, med, timing, dropped = ts
         L = wl["layers"]
         fam, roof = roofline(timing, "bf16" if step.cfg.storage == "bf16" else "f32", name)
         out[name] = {
             "description": wl["desc"], "edges": step.E, "atoms": step.struct.n_dst, "layers": L,
             "ms_per_step": round(ms, 3), "median_step_ms": round(med, 3),
+            "ms_per_step_without_kernel_events": round(ts.ms_no_kernel_events, 3),
             "edges_per_s_per_layer": round(step.E * L / (ms * 1e-3), 1),
             "edges_per_s_per_layer_median": round(step.E * L / (med * 1e-3), 1),
             "nodes_per_s_per_layer": round(step.struct.n_dst * L / (ms * 1e-3), 1),
@@ -730,7 +750,8 @@ def main():
         return
     step = Step(wl, dev)
     copy_gbs = copy_bandwidth(torch, dev, args.copy_probe_mib)
-    ms, med, timing, dropped = timed_steps(torch, step.eg, step, args.steps, args.warmup)
+    ts = timed_steps(torch, step.eg, step, args.steps, args.warmup)
+    ms, med, timing, dropped = ts
     E = step.E
     cfg = step.cfg
     dtype = "bf16" if cfg.storage == "bf16" else "f32"
@@ -755,7 +776,8 @@ def main():
                    "nodes_per_s": round(step.struct.n_dst * wl["layers"] / (ms * 1e-3), 1),
                    "ms_per_layer": round(ms / wl["layers"], 3),
                    "median_step_ms": round(med, 3),
-                   "edges_per_s_median": round(E * wl["layers"] / (med * 1e-3), 1)},
+                   "edges_per_s_median": round(E * wl["layers"] / (med * 1e-3), 1),
+                   "ms_per_step_without_kernel_events": round(ts.ms_no_kernel_events, 3)},
         "roofline": dict(kernel=fam, **roof),
         "hbm_copy_gbs": copy_gbs,
         "kernels": kernels,
