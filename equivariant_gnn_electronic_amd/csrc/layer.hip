@@ -1691,9 +1691,11 @@ struct BwdWs {
 };
 
 // bf16 layers whose rotate-in runs on channel pairs, with the radial weights
-// packed as bf16 pairs (16 basis functions would spill there)
+// packed as bf16 pairs (16 basis functions would spill there, and so would
+// degree 8).  The backward node gradient takes its gates the same way, so it
+// differentiates the gates that the forward applied.
 inline bool paired_gates(const LayerShape &s) {
-  return s.storage == EGNN_BF16 && s.C % (2 * kWave) == 0 && s.n_rbf <= 8;
+  return s.storage == EGNN_BF16 && s.C % (2 * kWave) == 0 && s.n_rbf <= 8 && s.lmax <= 6;
 }
 
 // node streams of the radial-weight gradient (fixed by the node count, so the
@@ -1768,9 +1770,9 @@ struct Launch {
   static void rotate_in(const egnn_graph *g, const LayerShape &s, const float *geom, const T *x, const float *wrad,
                         const uint32_t *wpk, const Acts &a, hipStream_t st) {
     Ptr3 A{{a.A[0], a.A[1], a.A[2]}};
-    // channel pairs up to degree 6 (at degree 8 the pair kernel's node row and
-    // radial weights for two channels spill; the per-channel kernel, with
-    // the same packed gates, does not)
+    // channel pairs up to degree 6 (paired_gates): at degree 8 the pair
+    // kernel's node row and radial weights for two channels spill, and the
+    // per-channel kernel with fp32 radial weights runs instead
     if constexpr (std::is_same<T, uint16_t>::value && std::is_same<TA, uint16_t>::value && LMAX <= 6) {
       if (wpk && paired_gates(s)) {  // channel pairs
         const int nch2 = s.C / (2 * kWave);
