@@ -541,6 +541,36 @@ def test_layer_backward_gst_bf16_full_size_masked_rows(dev):
     _compare_full_backward(cfg, r, dev, rows, 2e-2)
 
 
+@pytest.mark.parametrize("name,n_rows,storage", [("hfo2_l6", 32, "f32"), ("hfo2_l8", 24, "f32"),
+                                                  ("gst_l6", 16, "bf16")])
+def test_layer_higher_degree_full_size_masked_rows(dev, name, n_rows, storage):
+    """The degree-part launches of the backward node kernels (one launch per
+    range of degrees at lmax 6 and 8) at full size: the HfO2-like graph (544k
+    edges, fp32, C 64) at lmax 6 and 8, and the GeSbTe-like graph (1.1M edges,
+    bf16, C 128: channel-pair forward kernels and packed gates) at lmax 6.
+    x' of the sampled rows (its message part at the fp32 bar), then, with the
+    cotangent on those rows only, every weight block and grad x of every atom
+    against the oracle's exact values."""
+    if name == "gst_l6":
+        cfg = dataclasses.replace(synth.CONFIGS["gst"], name="gst_l6", lmax=6, layers=1)
+    else:
+        cfg = synth.CONFIGS[name]
+    assert cfg.storage == storage
+    r = _gpu_forward(cfg, dev, train=True)
+    s = r["s"]
+    rows = np.unique(np.linspace(0, s.n_dst - 1, n_rows).round().astype(np.int64))
+    print(f"[parity] {name} lmax={cfg.lmax} rows={len(rows)} edges={r['g'].n_edges}", flush=True)
+    perm, og = _relabelled_rows(s, rows)
+    x64 = r["x"][perm].astype(np.float64)
+    ref = olayer.layer_forward(og, x64, r["w"].astype(np.float64), desc_of(cfg))
+    xo = r["xo"].float().cpu().numpy()[rows]
+    tol = 2e-2 if storage == "bf16" else 1e-4
+    assert_close(xo, ref["x_out"], tol, "x_out rows")
+    if storage == "f32":
+        assert_close(xo - r["x"][rows], ref["x_out"] - x64[:len(rows)], tol, "x_out rows - x")
+    _compare_full_backward(cfg, r, dev, rows, tol)
+
+
 def test_hblocks_gst_bf16_c128_sampled(dev):
     """The decode that the 8,064-atom training step runs: bf16 irreps with C 128
     (the GeSbTe-like layer's own edge messages and outputs, 1.1M edges) into
