@@ -12,7 +12,9 @@ The default workload is the HfO2-like training step: 3,000 atoms (1,000 Hf +
 lmax 4, mmax 2, C 64, fp32, one layer forward + backward, then the decode
 into 13x13 orbital blocks and their assembly into the sparse H(S).
 `value` is edges per second of whole steps (wall clock over the timed
-steps); the median of per-step HIP-event times is reported beside it.  The default run also times, each the same way:
+steps); the median of per-step HIP-event times is reported beside it, and so
+is the step time of as many steps again with the per-launch timing events
+off (their cost).  The default run also times, each the same way:
 the 8,064-atom GeSbTe-like configuration (bf16 storage, C 128), its 3-layer
 forward and its training step (key "gst"); the HfO2-like forward and the
 one-GPU-share (halo) forward ("other_configs"); and the saturation sweep of
