@@ -495,7 +495,7 @@ FAMILY_KERNELS = {
     "rotate_in": "::scatter_in_",
     "aggregate": "::aggregate_",
     "hblocks": "hblocks_kernel",
-    "assemble_bsr": "assemble_bsr_kernel",
+    "assemble_bsr": "::bsr_values_kernel",   # the value copy (the index pass moves ~15 B per block)
     "edge_update": "::edge_update_kernel<",
     "edge_dy": "::edge_dy_kernel<",
     "matrix_to_label": ("::labels_kernel<", ", true>"),   # every (chunk, pass) instantiation
