@@ -1691,9 +1691,11 @@ struct BwdWs {
 };
 
 // bf16 layers whose rotate-in runs on channel pairs, with the radial weights
-// packed as bf16 pairs (16 basis functions would spill there, and so would
-// degree 8).  The backward node gradient takes its gates the same way, so it
-// differentiates the gates that the forward applied.
+// packed once per call as bf16 pairs (16 basis functions would spill there,
+// and so would degree 8).  Every bf16 rotate-in forms its gates from bf16
+// radial weights and basis values by packed dot products (the per-channel
+// kernel converts the weights itself, with the same rounding), and the
+// backward node gradient of every bf16 layer takes its gates the same way.
 inline bool paired_gates(const LayerShape &s) {
   return s.storage == EGNN_BF16 && s.C % (2 * kWave) == 0 && s.n_rbf <= 8 && s.lmax <= 6;
 }
@@ -1863,7 +1865,8 @@ struct Launch {
     else
       bwd_gate_t<float>(g, s, geom, static_cast<const float *>(x), w, st);
   }
-  // wpk: packed radial weights where the forward used them (paired rotate-in), else null
+  // bf16 storage: the gates from wpk, the radial weights packed as bf16 pairs
+  // (as every bf16 forward forms them); fp32: from wrad
   template <typename TdA>
   static void bwd_node_t(const egnn_graph *g, const LayerShape &s, const float *geom, const float *G,
                          const float *wrad, const uint32_t *wpk, CPtr3 dA, float *gx, hipStream_t st) {
@@ -1879,18 +1882,22 @@ struct Launch {
                                         wrad, P ? wpk : nullptr, s.n_rbf, dA, G, gx);
       });
     };
-    if (wpk)
-      go(std::integral_constant<int, 8>{}, std::true_type{});
-    else if (s.n_rbf <= 8)
-      go(std::integral_constant<int, 8>{}, std::false_type{});
-    else
-      go(std::integral_constant<int, 16>{}, std::false_type{});
+    if constexpr (std::is_same<TdA, uint16_t>::value) {
+      if (s.n_rbf <= 8)
+        go(std::integral_constant<int, 8>{}, std::true_type{});
+      else
+        go(std::integral_constant<int, 16>{}, std::true_type{});
+    } else {
+      if (s.n_rbf <= 8)
+        go(std::integral_constant<int, 8>{}, std::false_type{});
+      else
+        go(std::integral_constant<int, 16>{}, std::false_type{});
+    }
   }
   static void bwd_node(const egnn_graph *g, const LayerShape &s, const float *geom, const float *G, const float *wrad,
                        const BwdWs &w, float *gx, hipStream_t st) {
     if (s.storage == EGNN_BF16)
-      bwd_node_t<uint16_t>(g, s, geom, G, wrad, paired_gates(s) ? w.wpk : nullptr,
-                           CPtr3{{w.dAb[0], w.dAb[1], w.dAb[2]}}, gx, st);
+      bwd_node_t<uint16_t>(g, s, geom, G, wrad, w.wpk, CPtr3{{w.dAb[0], w.dAb[1], w.dAb[2]}}, gx, st);
     else
       bwd_node_t<float>(g, s, geom, G, wrad, nullptr, CPtr3{{w.dA[0], w.dA[1], w.dA[2]}}, gx, st);
   }
@@ -2386,7 +2393,7 @@ static egnn_status layer_bwd_impl(bool edge_block, const egnn_layer_desc *d, con
     } else {
       const double bytes = double(E) * (sumK * (bf ? 2.0 : 4.0) + s.nD * 4.0 + 8.0) + double(g->n_dst) * s.K * s.C * 4.0 +
                            double(g->n_src) * s.K * s.C * 4.0;
-      if (paired_gates(s)) {
+      if (bf) {  // the gates of every bf16 forward: bf16 radial weights (8 basis pairs: up to 16 functions)
         const int64_t n = static_cast<int64_t>(8) * s.n_pairs * 2 * s.C;
         pack_wrad_kernel<<<ceil_div(n, T), T, 0, stream>>>(weights + wo.wrad, s.n_rbf, s.n_pairs, 2 * s.C, w.wpk);
       }
