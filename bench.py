@@ -23,7 +23,8 @@ skips them.
 
 Other workloads (--workload): hfo2, halo, gst (forwards; GST is three bf16
 layers), gst_train (bf16 training step), hfo2_l6 / hfo2_l8 (forwards at
-lmax 6 and 8), edge_train (the edge-update block's training step), and m2l /
+lmax 6 and 8) and hfo2_l6_train / hfo2_l8_train (their training steps,
+without the decode), edge_train (the edge-update block's training step), and m2l /
 l2m, which time Matrix -> Label and Label -> Matrix (MALOQ Sec. III-B2,
 Fig. 2(c, d)) over a batch of 4,096 small molecules; `value` is atoms per
 second there.
@@ -53,6 +54,10 @@ WORKLOADS = {
                     desc="HfO2-like forward at lmax 6 / mmax 2: graph + geometry + 1 layer fwd"),
     "hfo2_l8": dict(cfg="hfo2_l8", backward=False, decode=False, layers=1,
                     desc="HfO2-like forward at lmax 8 / mmax 2: graph + geometry + 1 layer fwd"),
+    "hfo2_l6_train": dict(cfg="hfo2_l6", backward=True, decode=False, layers=1,
+                          desc="HfO2-like training step at lmax 6 / mmax 2: graph + geometry + 1 layer fwd/bwd"),
+    "hfo2_l8_train": dict(cfg="hfo2_l8", backward=True, decode=False, layers=1,
+                          desc="HfO2-like training step at lmax 8 / mmax 2: graph + geometry + 1 layer fwd/bwd"),
     "halo": dict(cfg="halo", backward=False, decode=False, layers=1,
                  desc="one GPU's share with ghost halo: graph + geometry + 1 layer fwd"),
     "gst": dict(cfg="gst", backward=False, decode=False, layers=3,

@@ -225,9 +225,13 @@ __device__ inline float from_raw(uint32_t v, uint32_t) { return __uint_as_float(
 // before batch b is processed and written to LDS after it), at the price of
 // holding that batch in registers meanwhile; otherwise each batch is loaded
 // when the previous one is done.  Edge ids (one per lane, a load through
-// src_perm for source groups) run one batch ahead either way.  An optional per-edge value (extra[e]) rides along into xbuf.  The
-// LDS rows are GS4 float4 long; the first gs4 hold the row's data.
-template <int GS4, bool AHEAD = true, bool EXTRA = false>
+// src_perm for source groups) run one batch ahead either way.  An optional
+// per-edge value (extra[e]) rides along into xbuf.  The LDS rows are GS4
+// float4 long; the first gs4 hold the row's data.  By default LDS column t is
+// float4 column t of the geometry row; a degree part stages two ranges
+// instead: NA4 columns from OA4 (its Wigner-D entries), then the columns from
+// OB4 (the radial basis values) (see PartCols).
+template <int GS4, bool AHEAD = true, bool EXTRA = false, int OA4 = 0, int NA4 = GS4, int OB4 = 0>
 struct GeomPipe {
   static constexpr int NQ = (kBatch * GS4 + kWave - 1) / kWave;  // float4 slots per lane
   const EdgeList el;
@@ -242,7 +246,13 @@ struct GeomPipe {
   // slot u of this lane: edge t / GS4 of the batch, float4 t % GS4 of its row (t = lane + 64 u);
   // columns from gs4 to GS4 - 1 (past the basis values in use) repeat column gs4 - 1
   __device__ int si(int u) const { return (lane + kWave * u) / GS4; }
-  __device__ int sq(int u) const { return min((lane + kWave * u) % GS4, gs4 - 1); }
+  __device__ int sq(int u) const {
+    const int t = min((lane + kWave * u) % GS4, gs4 - 1);
+    if constexpr (NA4 >= GS4 && OA4 == 0)
+      return t;
+    else
+      return t < NA4 ? OA4 + t : OB4 + (t - NA4);
+  }
   float xv;
   int ids_cur, ids_next;
 
@@ -312,51 +322,7 @@ struct GeomPipe {
   }
 };
 
-template <int LMAX, int MMAX, int NRBF>
-__device__ inline void load_wrad(const float *wrad, int n_rbf, int C2, int j, bool active, float (&wr)[NRBF][pair_count(LMAX, MMAX)]) {
-  constexpr int NP = pair_count(LMAX, MMAX);
-  // unused slots read basis 0 / column 0 and are zeroed after: no branch per load
-  const int jc = active ? j : 0;
-  float v[NRBF][NP];
-#pragma unroll
-  for (int k = 0; k < NRBF; ++k)
-#pragma unroll
-    for (int p = 0; p < NP; ++p) v[k][p] = wrad[(static_cast<int64_t>(k < n_rbf ? k : 0) * NP + p) * C2 + jc];
-#pragma unroll
-  for (int k = 0; k < NRBF; ++k)
-#pragma unroll
-    for (int p = 0; p < NP; ++p) wr[k][p] = (active && k < n_rbf) ? v[k][p] : 0.0f;
-}
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Radial weights of one lane's slot as bf16 pairs over the basis index
-// (k = 2q, 2q + 1), for the bf16-storage forward: the gate then takes
-// NRBF / 2 packed dot products (v_dot2_f32_bf16, fp32 accumulate) per pair
-// and half the registers of the fp32 form.
-template <int LMAX, int MMAX, int NRBF>
-__device__ inline void load_wrad_bf16(const float *wrad, int n_rbf, int C2, int j, bool active,
-                                      bf16x2 (&wr)[NRBF / 2][pair_count(LMAX, MMAX)]) {
-  constexpr int NP = pair_count(LMAX, MMAX);
-  float v[NRBF][NP];
-  load_wrad<LMAX, MMAX, NRBF>(wrad, n_rbf, C2, j, active, v);
-#pragma unroll
-  for (int q = 0; q < NRBF / 2; ++q)
-#pragma unroll
-    for (int p = 0; p < NP; ++p) wr[q][p] = bf16x2{static_cast<__bf16>(v[2 * q][p]), static_cast<__bf16>(v[2 * q + 1][p])};
-}
-
-// The K entries of one channel of a node row.  Inactive lanes read channel 0
-// and discard it, so the loads carry no branch and issue back to back.
-template <int K, typename T>
-__device__ inline void load_node_row(const T *__restrict__ x, int node, int C, int c, bool active, float (&xv)[K]) {
-  const T *row = x + static_cast<int64_t>(node) * K * C + (active ? c : 0);
-  float v[K];
-#pragma unroll
-  for (int k = 0; k < K; ++k) v[k] = Store<T>::ld(row + static_cast<uint32_t>(k * C));
-#pragma unroll
-  for (int k = 0; k < K; ++k) xv[k] = active ? v[k] : 0.0f;
-}
 
 // Coefficients KB..KB+KR-1 of one channel of a node row (rows of K coefficients).
 template <int KR, typename T>
@@ -370,8 +336,128 @@ __device__ inline void load_node_range(const T *__restrict__ x, int node, int K,
   for (int k = 0; k < KR; ++k) xv[k] = active ? v[k] : 0.0f;
 }
 
-// A[e] = g_e * trunc(D_e x) for the wave's half of every edge of its node.
-template <int LMAX, int MMAX, int NRBF, typename T, typename TA>
+// Degree parts.  At high degree one wave cannot hold a node's whole
+// per-channel state (the radial weights of every gate pair, accumulators for
+// every coefficient, the next edge's loads) in registers: the node kernels
+// spilled or ran one wave per SIMD.  Their work separates by degree (the
+// rotation mixes m only within a degree), so the degrees are dealt to parts,
+// each launched as its own grid over the same waves: part p owns degrees
+// lo(p)..hi(p), its coefficients, kept entries and gate pairs, and reads
+// every edge's geometry again.  Split<LMAX, N> deals 0..LMAX to N parts
+// (degrees up to 4 are always one part); each kernel family picks its N.
+template <int LMAX, int NP>
+struct Split {
+  static constexpr int N = LMAX <= 4 ? 1 : NP;
+  static_assert(N >= 1 && N <= 4 && (LMAX > 6 || N <= 3), "no such degree split");
+  __host__ __device__ static constexpr int lo(int p) {
+    return N == 1 ? 0
+           : LMAX <= 6 ? (N == 2 ? (p == 0 ? 0 : 4) : (p == 0 ? 0 : p == 1 ? 4 : 6))
+           : N == 2    ? (p == 0 ? 0 : 6)
+           : N == 3    ? (p == 0 ? 0 : p == 1 ? 5 : 7)
+                       : (p == 0 ? 0 : p == 1 ? 4 : p == 2 ? 6 : 8);
+  }
+  __host__ __device__ static constexpr int hi(int p) { return p == N - 1 ? LMAX : lo(p + 1) - 1; }
+};
+
+// Backward node kernels (radial-weight gradient, gather): the split grows
+// with the number of radial basis functions, whose weights each lane holds.
+template <int LMAX, int NRBF>
+using Parts = Split<LMAX, LMAX <= 6 ? (NRBF <= 8 ? 2 : 3) : (NRBF <= 8 ? 3 : 4)>;
+// Per-channel rotate-in (it holds the gate weights as well)
+template <int LMAX, int NRBF>
+using InParts = Split<LMAX, LMAX <= 6 ? (NRBF <= 8 ? 2 : 3) : (NRBF <= 8 ? 3 : 4)>;
+// Per-channel aggregate (accumulators and one edge's kept entries only)
+template <int LMAX>
+using AggParts = Split<LMAX, LMAX <= 6 ? 1 : 2>;
+
+// The geometry columns a degree part stages (GeomPipe): its degrees' Wigner-D
+// entries, which sit together in the row (degree-major), and, with NRBF > 0,
+// the radial basis values after all of D, each range in whole float4 columns.
+// In the LDS row, D entry o is at o - DOFF and basis value k at RB + k.
+template <int LMAX, int MMAX, int L0, int L1, int NRBF>
+struct PartCols {
+  static constexpr int ND = d_count(LMAX, MMAX);
+  static constexpr int OA4 = d_block_offset(L0, MMAX) / 4;
+  static constexpr int NA4 = (d_block_offset(L1 + 1, MMAX) + 3) / 4 - OA4;
+  static constexpr int OB4 = ND / 4;
+  static constexpr int DOFF = OA4 * 4;
+  static constexpr int RB = NA4 * 4 + ND - OB4 * 4;
+  static constexpr int GS4 = NRBF == 0 ? NA4 : NA4 + (ND - OB4 * 4 + NRBF + 3) / 4;
+  // columns in use for n_rbf basis functions (n_rbf <= NRBF)
+  __device__ static int gs4(int n_rbf) { return NRBF == 0 ? NA4 : NA4 + (ND - OB4 * 4 + n_rbf + 3) / 4; }
+};
+
+// Index ranges of degrees L0..L1: coefficients k = l^2 + l + m from KB, kept
+// (l, m) entries from QB (their running index), and the gate pairs (m, l)
+// with l in the range, numbered m-major from 0.
+template <int LMAX, int MMAX, int L0, int L1>
+struct Rng {
+  static constexpr int KB = L0 * L0;
+  static constexpr int KR = (L1 + 1) * (L1 + 1) - KB;
+  static constexpr int QB = Lay<LMAX, MMAX>::kidx(L0, -cmin(L0, MMAX));
+  static constexpr int QR = Lay<LMAX, MMAX>::kidx(L1, cmin(L1, MMAX)) + 1 - QB;
+  __host__ __device__ static constexpr int lpair(int m, int l) {
+    int n = 0;
+    for (int j = 0; j < m; ++j) {
+      const int a = j > L0 ? j : L0;
+      if (a <= L1) n += L1 - a + 1;
+    }
+    return n + l - (m > L0 ? m : L0);
+  }
+  static constexpr int NP = lpair(MMAX + 1, MMAX + 1 > L0 ? MMAX + 1 : L0);
+  // global pair index (pair_index) of local pair q
+  __host__ __device__ static constexpr int gpair(int q) {
+    for (int m = 0; m <= MMAX; ++m) {
+      const int a = m > L0 ? m : L0;
+      if (a > L1) continue;
+      if (q <= L1 - a) return pair_index(m, a + q, LMAX);
+      q -= L1 - a + 1;
+    }
+    return -1;
+  }
+};
+
+// Radial weights of the gate pairs of degrees L0..L1 for one lane's slot j
+// (unused slots read column 0 and are zeroed after: no branch per load).
+template <int LMAX, int MMAX, int NRBF, int L0, int L1>
+__device__ inline void load_wrad_range(const float *wrad, int n_rbf, int C2, int j, bool active,
+                                       float (&wr)[NRBF][Rng<LMAX, MMAX, L0, L1>::NP]) {
+  using R = Rng<LMAX, MMAX, L0, L1>;
+  constexpr int NPG = pair_count(LMAX, MMAX);
+  const int jc = active ? j : 0;
+  float v[NRBF][R::NP];
+#pragma unroll
+  for (int k = 0; k < NRBF; ++k)
+#pragma unroll
+    for (int m = 0; m <= MMAX; ++m)
+#pragma unroll
+      for (int l = (m > L0 ? m : L0); l <= L1; ++l)
+        v[k][R::lpair(m, l)] = wrad[(static_cast<int64_t>(k < n_rbf ? k : 0) * NPG + pair_index(m, l, LMAX)) * C2 + jc];
+#pragma unroll
+  for (int k = 0; k < NRBF; ++k)
+#pragma unroll
+    for (int p = 0; p < R::NP; ++p) wr[k][p] = (active && k < n_rbf) ? v[k][p] : 0.0f;
+}
+
+// The same as bf16 pairs over the basis index (k = 2q, 2q + 1), rounded as
+// pack_wrad_kernel rounds them, for the bf16-storage rotate-in: its gate then
+// takes NRBF / 2 packed dot products (v_dot2_f32_bf16, fp32 accumulate) per
+// pair, with half the registers of the fp32 form.
+template <int LMAX, int MMAX, int NRBF, int L0, int L1>
+__device__ inline void load_wrad_bf16_range(const float *wrad, int n_rbf, int C2, int j, bool active,
+                                            bf16x2 (&wp)[NRBF / 2][Rng<LMAX, MMAX, L0, L1>::NP]) {
+  using R = Rng<LMAX, MMAX, L0, L1>;
+  float v[NRBF][R::NP];
+  load_wrad_range<LMAX, MMAX, NRBF, L0, L1>(wrad, n_rbf, C2, j, active, v);
+#pragma unroll
+  for (int q = 0; q < NRBF / 2; ++q)
+#pragma unroll
+    for (int p = 0; p < R::NP; ++p) wp[q][p] = bf16x2{static_cast<__bf16>(v[2 * q][p]), static_cast<__bf16>(v[2 * q + 1][p])};
+}
+
+// A[e] = g_e * trunc(D_e x) for the wave's half of every edge of its node
+// (degrees L0..L1 of it: one degree part).
+template <int LMAX, int MMAX, int NRBF, typename T, typename TA, int L0 = 0, int L1 = LMAX>
 __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restrict__ row_ptr,
                                                               const int *__restrict__ src_ptr,
                                                               const int *__restrict__ src_perm,
@@ -379,8 +465,10 @@ __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restr
                                                               int n_src, const T *__restrict__ x, int C,
                                                               const float *__restrict__ wrad, int n_rbf, Ptr3 A) {
   using L = Lay<LMAX, MMAX>;
-  constexpr int GS4 = (L::ND + NRBF + 3) / 4;
-  const int gs4 = (L::ND + n_rbf + 3) / 4;
+  using R = Rng<LMAX, MMAX, L0, L1>;  // this launch's degrees
+  using P = PartCols<LMAX, MMAX, L0, L1, NRBF>;  // and their geometry columns
+  constexpr int GS4 = P::GS4;
+  const int gs4 = P::gs4(n_rbf);
   __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
   __shared__ int eids[kWavesPerBlock][kBatch];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
@@ -393,46 +481,47 @@ __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restr
   const int c = nw.chunk * kWave + lane;
   const bool active = c < C;
   const int j = nw.half * C + c;
-  float xv[L::K];
-  load_node_row<L::K>(x, nw.node, C, c, active, xv);
-  // fp32 storage: fp32 radial weights; bf16 storage: bf16 pairs (see load_wrad_bf16)
+  float xv[R::KR];  // the node row's degrees L0..L1
+  load_node_range<R::KR>(x, nw.node, L::K, R::KB, C, c, active, xv);
+  // fp32 storage: fp32 radial weights; bf16 storage: bf16 pairs (see load_wrad_bf16_range)
   constexpr bool kPacked = std::is_same<TA, uint16_t>::value;
-  float wr[kPacked ? 1 : NRBF][kPacked ? 1 : L::NP];
-  bf16x2 wp[kPacked ? NRBF / 2 : 1][kPacked ? L::NP : 1];
+  float wr[kPacked ? 1 : NRBF][kPacked ? 1 : R::NP];
+  bf16x2 wp[kPacked ? NRBF / 2 : 1][kPacked ? R::NP : 1];
   if constexpr (kPacked)
-    load_wrad_bf16<LMAX, MMAX, NRBF>(wrad, n_rbf, C2, j, active, wp);
+    load_wrad_bf16_range<LMAX, MMAX, NRBF, L0, L1>(wrad, n_rbf, C2, j, active, wp);
   else
-    load_wrad<LMAX, MMAX, NRBF>(wrad, n_rbf, C2, j, active, wr);
+    load_wrad_range<LMAX, MMAX, NRBF, L0, L1>(wrad, n_rbf, C2, j, active, wr);
   const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
   // bf16: fewer registers for higher occupancy instead of the batch ahead
-  GeomPipe<GS4, std::is_same<T, float>::value> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave]);
+  GeomPipe<GS4, std::is_same<T, float>::value, false, P::OA4, P::NA4, P::OB4> gp(el, geom, gstride, gs4, gbuf[wave],
+                                                                                eids[wave]);
   for (int base = 0; base < el.count; base += kBatch) {
     const int cnt = min(kBatch, el.count - base);
     gp.prefetch(base);
     for (int i = 0; i < cnt; ++i) {
       const int e = uniform(eids[wave][i]);
       const float *gr = gb + i * GS4 * 4;
-      float g[L::NP];
+      float g[R::NP];
 #pragma unroll
-      for (int p = 0; p < L::NP; ++p) g[p] = 0.0f;
+      for (int p = 0; p < R::NP; ++p) g[p] = 0.0f;
       if constexpr (kPacked) {
 #pragma unroll
         for (int q = 0; q < NRBF / 2; ++q) {
           // unconditional LDS reads, then selects: no branch per basis function
-          const float r0 = gr[L::ND + 2 * q], r1 = gr[L::ND + 2 * q + 1];
+          const float r0 = gr[P::RB + 2 * q], r1 = gr[P::RB + 2 * q + 1];
           const bf16x2 ph{static_cast<__bf16>(2 * q < n_rbf ? r0 : 0.0f),
                           static_cast<__bf16>(2 * q + 1 < n_rbf ? r1 : 0.0f)};
 #pragma unroll
-          for (int p = 0; p < L::NP; ++p) g[p] = __builtin_amdgcn_fdot2_f32_bf16(ph, wp[q][p], g[p], false);
+          for (int p = 0; p < R::NP; ++p) g[p] = __builtin_amdgcn_fdot2_f32_bf16(ph, wp[q][p], g[p], false);
         }
       } else {
 #pragma unroll
         for (int k = 0; k < NRBF; ++k) {
           // unconditional LDS read, then select: no branch per basis function
-          const float raw = gr[L::ND + k];
+          const float raw = gr[P::RB + k];
           const float ph = k < n_rbf ? raw : 0.0f;
 #pragma unroll
-          for (int p = 0; p < L::NP; ++p) g[p] += ph * wr[k][p];
+          for (int p = 0; p < R::NP; ++p) g[p] += ph * wr[k][p];
         }
       }
       if (!active) continue;
@@ -442,13 +531,13 @@ __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restr
       for (int mu = 0; mu <= MMAX; ++mu)
         rowp[mu] = static_cast<TA *>(A.p[mu]) + static_cast<int64_t>(e) * (L::blocks(mu) * C2);
 #pragma unroll
-      for (int l = 0; l <= LMAX; ++l) {
+      for (int l = L0; l <= L1; ++l) {
 #pragma unroll
         for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
           float v = 0.0f;
 #pragma unroll
-          for (int mp = -l; mp <= l; ++mp) v += gr[L::doff(l, m, mp)] * xv[l * l + l + mp];
-          v *= g[pair_index(cabs(m), l, LMAX)];
+          for (int mp = -l; mp <= l; ++mp) v += gr[L::doff(l, m, mp) - P::DOFF] * xv[l * l + l + mp - R::KB];
+          v *= g[R::lpair(cabs(m), l)];
           Store<TA>::st(rowp[cabs(m)] + static_cast<uint32_t>(L::col(l, m) * C2 + j), v);
         }
       }
@@ -627,14 +716,17 @@ __global__ void __launch_bounds__(kThreads) attention_kernel(const int *__restri
 // One wave per (destination row, 64-channel chunk): it walks the row's
 // contiguous edges, staging their geometry rows (and alpha) into LDS in
 // batches; the accumulator stays in registers (no atomics, no partials).
-template <int LMAX, int MMAX, typename T>
+// Degrees L0..L1 only (one degree part: see Parts).
+template <int LMAX, int MMAX, typename T, int L0 = 0, int L1 = LMAX>
 __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restrict__ row_ptr, int n_dst,
                                                              const float *__restrict__ geom, int gstride, int nd_rbf,
                                                              const float *__restrict__ alpha, CPtr3 Y, int C,
                                                              const T *__restrict__ x, T *__restrict__ x_out,
                                                              T *__restrict__ edge_out) {
   using L = Lay<LMAX, MMAX>;
-  constexpr int GS4 = (L::ND + 3) / 4;
+  using R = Rng<LMAX, MMAX, L0, L1>;  // this launch's degrees
+  using P = PartCols<LMAX, MMAX, L0, L1, 0>;  // and their Wigner-D columns
+  constexpr int GS4 = P::GS4;
   __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
   __shared__ int eids[kWavesPerBlock][kBatch];
   __shared__ float abuf[kWavesPerBlock][kBatch];
@@ -650,15 +742,14 @@ __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restri
   el.perm = nullptr;
   el.begin = uniform(row_ptr[d]);
   el.count = uniform(row_ptr[d + 1]) - el.begin;
-  const int gs4 = (L::ND + 3) / 4;
   (void)nd_rbf;
-  float acc[L::K];
+  float acc[R::KR];
 #pragma unroll
-  for (int k = 0; k < L::K; ++k) acc[k] = 0.0f;
+  for (int k = 0; k < R::KR; ++k) acc[k] = 0.0f;
   const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
   if (el.count > 0) {
     // not ahead: each edge's Y loads follow at once and wait for the geometry in any case
-    GeomPipe<GS4, false, true> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave], alpha, abuf[wave]);
+    GeomPipe<GS4, false, true, P::OA4, P::NA4> gp(el, geom, gstride, GS4, gbuf[wave], eids[wave], alpha, abuf[wave]);
     for (int base = 0; base < el.count; base += kBatch) {
       const int cnt = min(kBatch, el.count - base);
       gp.prefetch(base);
@@ -666,24 +757,25 @@ __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restri
         const int e = el.begin + base + i;
         const float a = abuf[wave][i];
         const float *gr = gb + i * GS4 * 4;
-        float y[L::KEPT];
+        float y[R::QR];
 #pragma unroll
-        for (int l = 0; l <= LMAX; ++l)
+        for (int l = L0; l <= L1; ++l)
 #pragma unroll
           for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
             const int mu = cabs(m);
             const T *row = static_cast<const T *>(Y.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
-            y[L::kidx(l, m)] = Store<T>::ld(row + L::col(l, m) * C + cl);
+            y[L::kidx(l, m) - R::QB] = Store<T>::ld(row + L::col(l, m) * C + cl);
           }
         T *eo = edge_out ? edge_out + static_cast<int64_t>(e) * L::K * C : nullptr;
 #pragma unroll
-        for (int l = 0; l <= LMAX; ++l)
+        for (int l = L0; l <= L1; ++l)
 #pragma unroll
           for (int mp = -l; mp <= l; ++mp) {
             float msg = 0.0f;
 #pragma unroll
-            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) msg += gr[L::doff(l, m, mp)] * y[L::kidx(l, m)];
-            acc[l * l + l + mp] += a * msg;
+            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
+              msg += gr[L::doff(l, m, mp) - P::DOFF] * y[L::kidx(l, m) - R::QB];
+            acc[l * l + l + mp - R::KB] += a * msg;
             if (eo && on) Store<T>::st(eo + (l * l + l + mp) * C + c, msg);
           }
       }
@@ -692,8 +784,8 @@ __global__ void __launch_bounds__(kThreads) aggregate_kernel(const int *__restri
   }
   if (!on) return;
 #pragma unroll
-  for (int k = 0; k < L::K; ++k) {
-    const int64_t o = (static_cast<int64_t>(d) * L::K + k) * C + c;
+  for (int k = 0; k < R::KR; ++k) {
+    const int64_t o = (static_cast<int64_t>(d) * L::K + R::KB + k) * C + c;
     Store<T>::st(x_out + o, Store<T>::ld(x + o) + acc[k]);
   }
 }
@@ -1145,75 +1237,6 @@ __global__ void __launch_bounds__(kThreads) bwd_row_pair_kernel(const int *__res
   *reinterpret_cast<float2 *>(watt_part + static_cast<int64_t>(d) * C + c) = make_float2(wacc0, wacc1);
 }
 
-// Degree parts.  At high degree one wave cannot hold a node's whole
-// per-channel state (the radial weights of every gate pair, accumulators for
-// every coefficient, the next edge's loads) in registers, and the backward
-// node kernels spilled.  Their work separates by degree, so the degrees are
-// dealt to parts, each launched as its own grid over every (node, half,
-// chunk): part p owns degrees Parts::lo(p)..Parts::hi(p), its coefficients,
-// kept entries and gate pairs.  Degrees up to 4 are one part.
-template <int LMAX, int NRBF>
-struct Parts {
-  static constexpr int N = LMAX <= 4 ? 1 : LMAX <= 6 ? (NRBF <= 8 ? 2 : 3) : (NRBF <= 8 ? 3 : 4);
-  __host__ __device__ static constexpr int lo(int p) {
-    return N == 1 ? 0
-           : LMAX <= 6 ? (N == 2 ? (p == 0 ? 0 : 4) : (p == 0 ? 0 : p == 1 ? 4 : 6))
-                       : (N == 3 ? (p == 0 ? 0 : p == 1 ? 5 : 7) : (p == 0 ? 0 : p == 1 ? 4 : p == 2 ? 6 : 8));
-  }
-  __host__ __device__ static constexpr int hi(int p) { return p == N - 1 ? LMAX : lo(p + 1) - 1; }
-};
-
-// Index ranges of degrees L0..L1: coefficients k = l^2 + l + m from KB, kept
-// (l, m) entries from QB (their running index), and the gate pairs (m, l)
-// with l in the range, numbered m-major from 0.
-template <int LMAX, int MMAX, int L0, int L1>
-struct Rng {
-  static constexpr int KB = L0 * L0;
-  static constexpr int KR = (L1 + 1) * (L1 + 1) - KB;
-  static constexpr int QB = Lay<LMAX, MMAX>::kidx(L0, -cmin(L0, MMAX));
-  static constexpr int QR = Lay<LMAX, MMAX>::kidx(L1, cmin(L1, MMAX)) + 1 - QB;
-  __host__ __device__ static constexpr int lpair(int m, int l) {
-    int n = 0;
-    for (int j = 0; j < m; ++j) {
-      const int a = j > L0 ? j : L0;
-      if (a <= L1) n += L1 - a + 1;
-    }
-    return n + l - (m > L0 ? m : L0);
-  }
-  static constexpr int NP = lpair(MMAX + 1, MMAX + 1 > L0 ? MMAX + 1 : L0);
-  // global pair index (pair_index) of local pair q
-  __host__ __device__ static constexpr int gpair(int q) {
-    for (int m = 0; m <= MMAX; ++m) {
-      const int a = m > L0 ? m : L0;
-      if (a > L1) continue;
-      if (q <= L1 - a) return pair_index(m, a + q, LMAX);
-      q -= L1 - a + 1;
-    }
-    return -1;
-  }
-};
-
-// Radial weights of the gate pairs of degrees L0..L1 for one lane's slot j
-// (unused slots read column 0 and are zeroed after: no branch per load).
-template <int LMAX, int MMAX, int NRBF, int L0, int L1>
-__device__ inline void load_wrad_range(const float *wrad, int n_rbf, int C2, int j, bool active,
-                                       float (&wr)[NRBF][Rng<LMAX, MMAX, L0, L1>::NP]) {
-  using R = Rng<LMAX, MMAX, L0, L1>;
-  constexpr int NPG = pair_count(LMAX, MMAX);
-  const int jc = active ? j : 0;
-  float v[NRBF][R::NP];
-#pragma unroll
-  for (int k = 0; k < NRBF; ++k)
-#pragma unroll
-    for (int m = 0; m <= MMAX; ++m)
-#pragma unroll
-      for (int l = (m > L0 ? m : L0); l <= L1; ++l)
-        v[k][R::lpair(m, l)] = wrad[(static_cast<int64_t>(k < n_rbf ? k : 0) * NPG + pair_index(m, l, LMAX)) * C2 + jc];
-#pragma unroll
-  for (int k = 0; k < NRBF; ++k)
-#pragma unroll
-    for (int p = 0; p < R::NP; ++p) wr[k][p] = (active && k < n_rbf) ? v[k][p] : 0.0f;
-}
 
 
 template <int LMAX, int MMAX, int NRBF, typename T, int L0 = 0, int L1 = LMAX>
@@ -1225,8 +1248,9 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
                                                              CPtr3 dA, int n_streams, float *__restrict__ part) {
   using L = Lay<LMAX, MMAX>;
   using R = Rng<LMAX, MMAX, L0, L1>;  // this launch's degrees
-  constexpr int GS4 = (L::ND + NRBF + 3) / 4;
-  const int gs4 = (L::ND + n_rbf + 3) / 4;
+  using P = PartCols<LMAX, MMAX, L0, L1, NRBF>;  // and their geometry columns
+  constexpr int GS4 = P::GS4;
+  const int gs4 = P::gs4(n_rbf);
   __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
   __shared__ int eids[kWavesPerBlock][kBatch];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
@@ -1251,7 +1275,7 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
     if (el.count == 0) continue;
     float xv[R::KR];  // the node row's degrees L0..L1
     load_node_range<R::KR>(x, node, L::K, R::KB, C, c, active, xv);
-    GeomPipe<GS4> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave]);
+    GeomPipe<GS4, true, false, P::OA4, P::NA4, P::OB4> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave]);
     for (int base = 0; base < el.count; base += kBatch) {
       const int cnt = min(kBatch, el.count - base);
       gp.prefetch(base);
@@ -1283,13 +1307,13 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
           for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
             float xt = 0.0f;
 #pragma unroll
-            for (int mp = -l; mp <= l; ++mp) xt += gr[L::doff(l, m, mp)] * xv[l * l + l + mp - R::KB];
+            for (int mp = -l; mp <= l; ++mp) xt += gr[L::doff(l, m, mp) - P::DOFF] * xv[l * l + l + mp - R::KB];
             const float dx = from_raw(raw[L::kidx(l, m) - R::QB], static_cast<uint32_t>(L::col(l, m) * C2 + jl));
             dg[R::lpair(cabs(m), l)] += dx * xt;
           }
 #pragma unroll
         for (int k = 0; k < NRBF; ++k) {
-          const float rv = gr[L::ND + k];  // in the staged row; select, no branch
+          const float rv = gr[P::RB + k];  // in the staged row; select, no branch
           const float ph = k < n_rbf ? rv : 0.0f;
 #pragma unroll
           for (int p = 0; p < R::NP; ++p) acc[k][p] += ph * dg[p];
@@ -1341,8 +1365,9 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
                                                                const float *__restrict__ G, float *__restrict__ gx) {
   using L = Lay<LMAX, MMAX>;
   using R = Rng<LMAX, MMAX, L0, L1>;  // this launch's degrees
-  constexpr int GS4 = (L::ND + NRBF + 3) / 4;
-  const int gs4 = (L::ND + n_rbf + 3) / 4;
+  using P = PartCols<LMAX, MMAX, L0, L1, NRBF>;  // and their geometry columns
+  constexpr int GS4 = P::GS4;
+  const int gs4 = P::gs4(n_rbf);
   __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
   __shared__ int eids[kWavesPerBlock][kBatch];
   __shared__ float red[kWavesPerBlock][R::KR * kWave];
@@ -1375,7 +1400,7 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
     }
     const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
     if (el.count > 0) {
-      GeomPipe<GS4> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave]);
+      GeomPipe<GS4, true, false, P::OA4, P::NA4, P::OB4> gp(el, geom, gstride, gs4, gbuf[wave], eids[wave]);
       for (int base = 0; base < el.count; base += kBatch) {
         const int cnt = min(kBatch, el.count - base);
         gp.prefetch(base);
@@ -1408,7 +1433,7 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
           if constexpr (PK) {
 #pragma unroll
             for (int q = 0; q < NRBF / 2; ++q) {
-              const float r0 = gr[L::ND + 2 * q], r1 = gr[L::ND + 2 * q + 1];
+              const float r0 = gr[P::RB + 2 * q], r1 = gr[P::RB + 2 * q + 1];
               const bf16x2 ph = {static_cast<__bf16>(2 * q < n_rbf ? r0 : 0.0f),
                                  static_cast<__bf16>(2 * q + 1 < n_rbf ? r1 : 0.0f)};
 #pragma unroll
@@ -1417,7 +1442,7 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
           } else {
 #pragma unroll
             for (int kk = 0; kk < NRBF; ++kk) {
-              const float rv = gr[L::ND + kk];  // in the staged row; select, no branch
+              const float rv = gr[P::RB + kk];  // in the staged row; select, no branch
               const float ph = kk < n_rbf ? rv : 0.0f;
 #pragma unroll
               for (int p = 0; p < R::NP; ++p) g[p] += ph * wr[kk][p];
@@ -1437,7 +1462,7 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
               float sum = 0.0f;
 #pragma unroll
               for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m)
-                sum += gr[L::doff(l, m, mp)] * h[L::kidx(l, m) - R::QB];
+                sum += gr[L::doff(l, m, mp) - P::DOFF] * h[L::kidx(l, m) - R::QB];
               acc[l * l + l + mp - R::KB] += sum;
             }
         };
@@ -1757,12 +1782,13 @@ WOff weight_offsets(const LayerShape &s) {
 }
 
 // ------------------------------------------------------------ launchers --
-// f(lo, hi) for every degree part of Parts<LMAX, NRBF>, in order
-template <int LMAX, int NRBF, int P = 0, typename F>
+// f(lo, hi) for each part of the degree split S in order, lo and hi as
+// integral constants
+template <typename S, int P = 0, typename F>
 void for_parts(F &&f) {
-  if constexpr (P < Parts<LMAX, NRBF>::N) {
-    f(std::integral_constant<int, Parts<LMAX, NRBF>::lo(P)>{}, std::integral_constant<int, Parts<LMAX, NRBF>::hi(P)>{});
-    for_parts<LMAX, NRBF, P + 1>(f);
+  if constexpr (P < S::N) {
+    f(std::integral_constant<int, S::lo(P)>{}, std::integral_constant<int, S::hi(P)>{});
+    for_parts<S, P + 1>(f);
   }
 }
 
@@ -1786,12 +1812,18 @@ struct Launch {
     }
     const int nch = (s.C + kWave - 1) / kWave;
     const unsigned grid = ceil_div(static_cast<int64_t>(g->n_src) * 2 * nch, kWavesPerBlock);
+    // one launch per degree part (each writes its own degrees' rows of A)
+    auto go = [&](auto nrbf) {
+      constexpr int NR = decltype(nrbf)::value;
+      for_parts<InParts<LMAX, NR>>([&](auto lo, auto hi) {
+        scatter_in_kernel<LMAX, MMAX, NR, T, TA, decltype(lo)::value, decltype(hi)::value><<<grid, kThreads, 0, st>>>(
+            g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride, g->n_dst, g->n_src, x, s.C, wrad, s.n_rbf, A);
+      });
+    };
     if (s.n_rbf <= 8)
-      scatter_in_kernel<LMAX, MMAX, 8, T, TA><<<grid, kThreads, 0, st>>>(
-          g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride, g->n_dst, g->n_src, x, s.C, wrad, s.n_rbf, A);
+      go(std::integral_constant<int, 8>{});
     else
-      scatter_in_kernel<LMAX, MMAX, 16, T, TA><<<grid, kThreads, 0, st>>>(
-          g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride, g->n_dst, g->n_src, x, s.C, wrad, s.n_rbf, A);
+      go(std::integral_constant<int, 16>{});
   }
   template <typename T>
   static void aggregate(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const T *x,
@@ -1807,8 +1839,11 @@ struct Launch {
     }
     const int nch = (s.C + kWave - 1) / kWave;
     const unsigned grid = ceil_div(static_cast<int64_t>(g->n_dst) * nch, kWavesPerBlock);
-    aggregate_kernel<LMAX, MMAX, T><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, s.nD + s.n_rbf,
-                                                               a.alpha, Y, s.C, x, x_out, edge_out);
+    // one launch per degree part (each writes its own coefficients of x_out and edge_out)
+    for_parts<AggParts<LMAX>>([&](auto lo, auto hi) {
+      aggregate_kernel<LMAX, MMAX, T, decltype(lo)::value, decltype(hi)::value><<<grid, kThreads, 0, st>>>(
+          g->row_ptr, g->n_dst, geom, s.gstride, s.nD + s.n_rbf, a.alpha, Y, s.C, x, x_out, edge_out);
+    });
   }
   template <typename TY>
   static void bwd_row_t(const egnn_graph *g, const LayerShape &s, const float *geom, const Acts &a, const float *G,
@@ -1846,7 +1881,7 @@ struct Launch {
     // one launch per degree part (each writes its own gate pairs' partials)
     auto go = [&](auto nrbf) {
       constexpr int NR = decltype(nrbf)::value;
-      for_parts<LMAX, NR>([&](auto lo, auto hi) {
+      for_parts<Parts<LMAX, NR>>([&](auto lo, auto hi) {
         wrad_grad_kernel<LMAX, MMAX, NR, T, decltype(lo)::value, decltype(hi)::value><<<grid, kThreads, 0, st>>>(
             g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride, g->n_dst, g->n_src, x, s.C, s.n_rbf, dA, ns,
             w.wrad_part);
@@ -1876,7 +1911,7 @@ struct Launch {
     auto go = [&](auto nrbf, auto pk) {
       constexpr int NR = decltype(nrbf)::value;
       constexpr bool P = decltype(pk)::value;
-      for_parts<LMAX, NR>([&](auto lo, auto hi) {
+      for_parts<Parts<LMAX, NR>>([&](auto lo, auto hi) {
         gather_grad_kernel<LMAX, MMAX, NR, TdA, P, decltype(lo)::value, decltype(hi)::value>
             <<<grid, kThreads, 0, st>>>(g->row_ptr, g->src_ptr, g->src_perm, geom, s.gstride, g->n_dst, g->n_src, s.C,
                                         wrad, P ? wpk : nullptr, s.n_rbf, dA, G, gx);

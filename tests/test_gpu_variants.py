@@ -57,7 +57,7 @@ VARIANTS = [
     (8, 2, 16, 8, "f32"),
     (8, 0, 8, 4, "f32"),
     (8, 1, 32, 8, "bf16"),
-    (8, 1, 128, 8, "bf16"),   # bf16 C = 128 at lmax 8: per-channel rotate-in and node gradient, fp32 gates both ways
+    (8, 1, 128, 8, "bf16"),   # bf16 C = 128 at lmax 8: per-channel rotate-in and node gradient, packed bf16 gates both ways
     (6, 2, 16, 16, "f32"),    # three degree parts at lmax 6 (16 radial functions)
     (8, 2, 16, 16, "f32"),    # four degree parts at lmax 8
 ]
