@@ -369,6 +369,9 @@ using InParts = Split<LMAX, LMAX <= 6 ? (NRBF <= 8 ? 2 : 3) : (NRBF <= 8 ? 3 : 4
 // Per-channel aggregate (accumulators and one edge's kept entries only)
 template <int LMAX>
 using AggParts = Split<LMAX, LMAX <= 6 ? 1 : 2>;
+// Row backward at lmax 6 and 8 (bwd_row_dot_kernel, bwd_row_grad_kernel)
+template <int LMAX>
+using RowParts = Split<LMAX, LMAX <= 6 ? 2 : 3>;
 
 // The geometry columns a degree part stages (GeomPipe): its degrees' Wigner-D
 // entries, which sit together in the row (degree-major), and, with NRBF > 0,
@@ -1014,6 +1017,171 @@ __global__ void __launch_bounds__(kThreads) bwd_row_kernel(const int *__restrict
   for (int t = 0; t < CPL; ++t) {
     const int c = lane + kWave * t;
     if (c < C) watt_part[static_cast<int64_t>(d) * C + c] = wacc[t];
+  }
+}
+
+// The row backward in degree parts (lmax 6 and 8, where one wave cannot hold
+// G_d and an edge's kept entries for every degree and channel slot).  The dot
+// dalpha_e sums over degrees, so it is built in part order: part 0 writes its
+// share, each later part adds its own (bwd_row_dot_kernel).  Then each part
+// forms its degrees' dY from the finished dalpha (bwd_row_grad_kernel); the
+// part holding degree 0 also adds the attention term and writes the w_att
+// partial.  Same waves, lanes and staging as bwd_row_kernel; each part stages
+// only its degrees' Wigner-D columns.
+template <int LMAX, int MMAX, int CPL, typename TY, int L0, int L1>
+__global__ void __launch_bounds__(kThreads) bwd_row_dot_kernel(const int *__restrict__ row_ptr, int n_dst,
+                                                               const float *__restrict__ geom, int gstride, CPtr3 Y,
+                                                               int C, const float *__restrict__ G,
+                                                               float *__restrict__ dalpha) {
+  using L = Lay<LMAX, MMAX>;
+  using R = Rng<LMAX, MMAX, L0, L1>;
+  using P = PartCols<LMAX, MMAX, L0, L1, 0>;
+  constexpr int GS4 = P::GS4;
+  __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
+  __shared__ int eids[kWavesPerBlock][kBatch];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int d = uniform(blockIdx.x * kWavesPerBlock + wave);
+  if (d >= n_dst) return;
+  EdgeList el;
+  el.perm = nullptr;
+  el.begin = uniform(row_ptr[d]);
+  el.count = uniform(row_ptr[d + 1]) - el.begin;
+  if (el.count == 0) return;
+  float gd[CPL][R::KR];
+  int cl[CPL];
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) {
+    const int c = lane + kWave * t;
+    cl[t] = c < C ? c : C - 1;
+#pragma unroll
+    for (int k = 0; k < R::KR; ++k)
+      gd[t][k] = c < C ? G[(static_cast<int64_t>(d) * L::K + R::KB + k) * C + c] : 0.0f;
+  }
+  const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
+  GeomPipe<GS4, true, false, P::OA4, P::NA4> gp(el, geom, gstride, GS4, gbuf[wave], eids[wave]);
+  for (int base = 0; base < el.count; base += kBatch) {
+    const int cnt = min(kBatch, el.count - base);
+    gp.prefetch(base);
+    for (int i = 0; i < cnt; ++i) {
+      const int e = el.begin + base + i;
+      const float *gr = gb + i * GS4 * 4;
+      // all of the edge's Y loads before any use (see load_raw)
+      typename RawOf<TY>::type yr[CPL][R::QR];
+#pragma unroll
+      for (int t = 0; t < CPL; ++t)
+#pragma unroll
+        for (int l = L0; l <= L1; ++l)
+#pragma unroll
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+            const int mu = cabs(m);
+            const TY *row = static_cast<const TY *>(Y.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
+            yr[t][L::kidx(l, m) - R::QB] = load_raw(row, static_cast<uint32_t>(L::col(l, m) * C + cl[t]));
+          }
+      const float prev = L0 == 0 ? 0.0f : dalpha[e];
+      __builtin_amdgcn_sched_barrier(0);
+      float p = 0.0f;
+#pragma unroll
+      for (int t = 0; t < CPL; ++t)
+#pragma unroll
+        for (int l = L0; l <= L1; ++l)
+#pragma unroll
+          for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+            float v = 0.0f;  // T(l, m); gd is 0 on clamped lanes, so T is too
+#pragma unroll
+            for (int mp = -l; mp <= l; ++mp) v += gr[L::doff(l, m, mp) - P::DOFF] * gd[t][l * l + l + mp - R::KB];
+            p += from_raw(yr[t][L::kidx(l, m) - R::QB], static_cast<uint32_t>(L::col(l, m) * C + cl[t])) * v;
+          }
+      p = wave_sum(p);
+      dalpha[e] = prev + p;  // every lane stores the same value
+    }
+    gp.advance(base);
+  }
+}
+
+template <int LMAX, int MMAX, int CPL, typename TY, typename TD, int L0, int L1>
+__global__ void __launch_bounds__(kThreads) bwd_row_grad_kernel(const int *__restrict__ row_ptr, int n_dst,
+                                                                const float *__restrict__ geom, int gstride,
+                                                                const float *__restrict__ alpha, CPtr3 Y, int C,
+                                                                const float *__restrict__ G,
+                                                                const float *__restrict__ w_att, Ptr3 dY,
+                                                                const float *__restrict__ dalpha,
+                                                                float *__restrict__ watt_part) {
+  using L = Lay<LMAX, MMAX>;
+  using R = Rng<LMAX, MMAX, L0, L1>;
+  using P = PartCols<LMAX, MMAX, L0, L1, 0>;
+  constexpr int GS4 = P::GS4;
+  __shared__ float4 gbuf[kWavesPerBlock][kBatch * GS4];
+  __shared__ int eids[kWavesPerBlock][kBatch];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int d = uniform(blockIdx.x * kWavesPerBlock + wave);
+  if (d >= n_dst) return;
+  EdgeList el;
+  el.perm = nullptr;
+  el.begin = uniform(row_ptr[d]);
+  el.count = uniform(row_ptr[d + 1]) - el.begin;
+  float wacc[CPL];
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) wacc[t] = 0.0f;
+  if (el.count > 0) {
+    float gd[CPL][R::KR];
+    int cl[CPL];
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      const int c = lane + kWave * t;
+      cl[t] = c < C ? c : C - 1;
+#pragma unroll
+      for (int k = 0; k < R::KR; ++k)
+        gd[t][k] = c < C ? G[(static_cast<int64_t>(d) * L::K + R::KB + k) * C + c] : 0.0f;
+    }
+    // sum over the row of alpha dalpha: lanes over edges, then the wave (the same value in every part)
+    float s = 0.0f;
+    for (int i = lane; i < el.count; i += kWave) s += alpha[el.begin + i] * dalpha[el.begin + i];
+    const float s_row = wave_sum(s);
+    const float *gb = reinterpret_cast<const float *>(gbuf[wave]);
+    GeomPipe<GS4, true, false, P::OA4, P::NA4> gp(el, geom, gstride, GS4, gbuf[wave], eids[wave]);
+    for (int base = 0; base < el.count; base += kBatch) {
+      const int cnt = min(kBatch, el.count - base);
+      gp.prefetch(base);
+      for (int i = 0; i < cnt; ++i) {
+        const int e = el.begin + base + i;
+        const float *gr = gb + i * GS4 * 4;
+        const float a = alpha[e];
+        const float da = a * (dalpha[e] - s_row);
+#pragma unroll
+        for (int t = 0; t < CPL; ++t) {
+          const int c = lane + kWave * t;
+          float y00 = 0.0f, wat = 0.0f;
+          if constexpr (L0 == 0) {
+            y00 = Store<TY>::ld(static_cast<const TY *>(Y.p[0]) + static_cast<int64_t>(e) * L::blocks(0) * C + cl[t]);
+            wat = w_att[cl[t]];
+          }
+#pragma unroll
+          for (int l = L0; l <= L1; ++l)
+#pragma unroll
+            for (int m = -cmin(l, MMAX); m <= cmin(l, MMAX); ++m) {
+              float T = 0.0f;
+#pragma unroll
+              for (int mp = -l; mp <= l; ++mp) T += gr[L::doff(l, m, mp) - P::DOFF] * gd[t][l * l + l + mp - R::KB];
+              float v = a * T;
+              if (l == 0) {
+                v += da * wat * dsilu(y00);
+                if (c < C) wacc[t] += da * silu(y00);
+              }
+              const int mu = cabs(m);
+              TD *row = static_cast<TD *>(dY.p[mu]) + static_cast<int64_t>(e) * L::blocks(mu) * C;
+              if (c < C) Store<TD>::st(row + static_cast<uint32_t>(L::col(l, m) * C + c), v);
+            }
+        }
+      }
+      gp.advance(base);
+    }
+  }
+  if constexpr (L0 == 0) {
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      const int c = lane + kWave * t;
+      if (c < C) watt_part[static_cast<int64_t>(d) * C + c] = wacc[t];
+    }
   }
 }
 
@@ -1855,7 +2023,23 @@ struct Launch {
     if (bf && s.C == 2 * kWave)
       bwd_row_pair_kernel<LMAX, MMAX><<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C,
                                                                  G, w_att, dY, w.dalpha, w.watt_part);
-    else if (s.C <= 64)
+    else if constexpr (LMAX >= 6) {  // degree parts: every dot first, then each part's dY
+      auto go = [&](auto cpl) {
+        constexpr int CP = decltype(cpl)::value;
+        for_parts<RowParts<LMAX>>([&](auto lo, auto hi) {
+          bwd_row_dot_kernel<LMAX, MMAX, CP, TY, decltype(lo)::value, decltype(hi)::value>
+              <<<grid, kThreads, 0, st>>>(g->row_ptr, g->n_dst, geom, s.gstride, Y, s.C, G, w.dalpha);
+        });
+        for_parts<RowParts<LMAX>>([&](auto lo, auto hi) {
+          bwd_row_grad_kernel<LMAX, MMAX, CP, TY, TY, decltype(lo)::value, decltype(hi)::value><<<grid, kThreads, 0, st>>>(
+              g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C, G, w_att, dY, w.dalpha, w.watt_part);
+        });
+      };
+      if (s.C <= 64)
+        go(std::integral_constant<int, 1>{});
+      else  // C <= 128: egnn_layer_bwd rejects wider layers before any launch
+        go(std::integral_constant<int, 2>{});
+    } else if (s.C <= 64)
       bwd_row_kernel<LMAX, MMAX, 1, TY, TY><<<grid, kThreads, 0, st>>>(
           g->row_ptr, g->n_dst, geom, s.gstride, a.alpha, Y, s.C, G, w_att, dY, w.dalpha, w.watt_part);
     else  // C <= 128: egnn_layer_bwd rejects wider layers before any launch

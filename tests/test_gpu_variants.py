@@ -60,6 +60,8 @@ VARIANTS = [
     (8, 1, 128, 8, "bf16"),   # bf16 C = 128 at lmax 8: per-channel rotate-in and node gradient, packed bf16 gates both ways
     (6, 2, 16, 16, "f32"),    # three degree parts at lmax 6 (16 radial functions)
     (8, 2, 16, 16, "f32"),    # four degree parts at lmax 8
+    (6, 2, 96, 8, "f32"),     # row backward in degree parts with two channel slots per lane
+    (8, 1, 80, 8, "bf16"),    # the same at lmax 8 in bf16 (64 < C < 128: no channel pairs)
 ]
 
 
