@@ -376,18 +376,23 @@ using RowParts = Split<LMAX, LMAX <= 6 ? 2 : 3>;
 // The geometry columns a degree part stages (GeomPipe): its degrees' Wigner-D
 // entries, which sit together in the row (degree-major), and, with NRBF > 0,
 // the radial basis values after all of D, each range in whole float4 columns.
-// In the LDS row, D entry o is at o - DOFF and basis value k at RB + k.
+// A launch over every degree stages the row's first columns as one range, as
+// the single-part kernels always did.  In the LDS row, D entry o is at
+// o - DOFF and basis value k at RB + k.
 template <int LMAX, int MMAX, int L0, int L1, int NRBF>
 struct PartCols {
   static constexpr int ND = d_count(LMAX, MMAX);
-  static constexpr int OA4 = d_block_offset(L0, MMAX) / 4;
-  static constexpr int NA4 = (d_block_offset(L1 + 1, MMAX) + 3) / 4 - OA4;
+  static constexpr bool kWhole = L0 == 0 && L1 == LMAX;
+  static constexpr int OA4 = kWhole ? 0 : d_block_offset(L0, MMAX) / 4;
+  static constexpr int NA4 = kWhole ? (ND + NRBF + 3) / 4 : (d_block_offset(L1 + 1, MMAX) + 3) / 4 - OA4;
   static constexpr int OB4 = ND / 4;
   static constexpr int DOFF = OA4 * 4;
-  static constexpr int RB = NA4 * 4 + ND - OB4 * 4;
-  static constexpr int GS4 = NRBF == 0 ? NA4 : NA4 + (ND - OB4 * 4 + NRBF + 3) / 4;
+  static constexpr int RB = kWhole ? ND : NA4 * 4 + ND - OB4 * 4;
+  static constexpr int GS4 = kWhole || NRBF == 0 ? NA4 : NA4 + (ND - OB4 * 4 + NRBF + 3) / 4;
   // columns in use for n_rbf basis functions (n_rbf <= NRBF)
-  __device__ static int gs4(int n_rbf) { return NRBF == 0 ? NA4 : NA4 + (ND - OB4 * 4 + n_rbf + 3) / 4; }
+  __device__ static int gs4(int n_rbf) {
+    return kWhole ? (ND + n_rbf + 3) / 4 : NRBF == 0 ? NA4 : NA4 + (ND - OB4 * 4 + n_rbf + 3) / 4;
+  }
 };
 
 // Index ranges of degrees L0..L1: coefficients k = l^2 + l + m from KB, kept
