@@ -183,6 +183,7 @@ constexpr int kWave = 64;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kTile = 16;  // rows per wave tile (the MFMA M dimension)
+constexpr int kValuLabels = 2;  // label channels of one degree up to which the VALU forms them
 
 // Labels by MFMA, entries from the LDS-resident template.  For each (L, M),
 // the 16 rows x C channels of the tile times W_L^T (C x n_L) is a chain of
@@ -301,20 +302,38 @@ __global__ void __launch_bounds__(kWave * NW) hblocks_kernel(int slot, int64_t r
     const int nL = l_n[L];
     const int ntile = (nL + 15) / 16;
     const int woff = l_woff[L], hoff = l_hoff[L];
-    for (int t = 0; t < ntile; ++t) {
-      // rows beyond n_L read the zero rows of the pad (or the next L's rows, discarded below)
-      const float *brow = wl + (woff + 16 * t + i16) * WLD + grp * S;
-      float b[S];
+    bool valu = false;
+    if constexpr (S >= 32) valu = nL <= kValuLabels;
+    if (valu) {
+      // a few label channels of a wide row: dot products on the VALU (an MFMA
+      // tile would compute 16 columns for them), each lane over its run of S
+      // channels, then the four channel groups of a row summed across lanes.
+      // (At S = 16 the 16-step MFMA chain was the faster of the two.)
+      for (int k = 0; k < nL; ++k) {
+        const float *wrow = wl + (woff + k) * WLD + grp * S;
+        float part = 0.0f;
 #pragma unroll
-      for (int i = 0; i < S; ++i) b[i] = brow[i];
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < S; ++i) part += a[i] * wrow[i];
+        part += __shfl_xor(part, 16, kWave);
+        part += __shfl_xor(part, 32, kWave);
+        if (grp == 0) hs[i16 * lab_ld + hoff + (M + L) * nL + k] = part;
+      }
+    } else {
+      for (int t = 0; t < ntile; ++t) {
+        // rows beyond n_L read the zero rows of the pad (or the next L's rows, discarded below)
+        const float *brow = wl + (woff + 16 * t + i16) * WLD + grp * S;
+        float b[S];
 #pragma unroll
-      for (int i = 0; i < S; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
-      // D[i][j]: row i = 4 * (lane / 16) + rr, column j = lane % 16
-      const int k = 16 * t + i16;
-      if (k < nL) {
+        for (int i = 0; i < S; ++i) b[i] = brow[i];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) hs[(4 * grp + rr) * lab_ld + hoff + (M + L) * nL + k] = acc[rr];
+        for (int i = 0; i < S; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+        // D[i][j]: row i = 4 * (lane / 16) + rr, column j = lane % 16
+        const int k = 16 * t + i16;
+        if (k < nL) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) hs[(4 * grp + rr) * lab_ld + hoff + (M + L) * nL + k] = acc[rr];
+        }
       }
     }
     if (p.r == n_runs - 1) {  // the tile's labels are complete: its entries
