@@ -120,10 +120,11 @@ def test_wigner_matches_sympy_small_d(l):
     so the complex-basis matrix is d(beta) itself and the real one U d U^H.
     """
     import sympy
-    from sympy.physics.quantum.spin import Rotation as SRot
+    from sympy.physics.wigner import wigner_d_small
     beta = 0.7314
-    d = np.array([[complex(SRot.d(l, m, mp, sympy.Float(beta, 30)).doit().evalf(30))
-                   for mp in range(-l, l + 1)] for m in range(-l, l + 1)])
+    # sympy's d^l_{m m'}(beta), rows and columns m = -l..l (the same matrix as
+    # sympy.physics.quantum.spin.Rotation.d, which is minutes slower at l = 8)
+    d = np.array(wigner_d_small(l, sympy.Float(beta, 30)).evalf(30).tolist(), dtype=complex)
     assert np.abs(d.imag).max() < 1e-12
     d = d.real
     c, s = np.cos(beta), np.sin(beta)
