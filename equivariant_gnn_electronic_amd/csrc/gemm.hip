@@ -174,6 +174,8 @@ __global__ void __launch_bounds__(256, 2) gemm_f32_kernel(int M, int N, int K, c
       for (int j = 0; j < TNt; ++j) b[j] = bs[(kk + fk) * SB::LD + wn + 32 * j + fr];
     };
     frag(0, fa[0], fb[0]);
+    // the products issue ahead of the other workgroup's loads and LDS stores
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int st = 0; st < BK / 2; ++st) {
       const int cur = st & 1;
@@ -184,6 +186,7 @@ __global__ void __launch_bounds__(256, 2) gemm_f32_kernel(int M, int N, int K, c
         for (int j = 0; j < TNt; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
     if (more) store(buf ^ 1);
     __syncthreads();
     buf ^= 1;
@@ -833,6 +836,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_tn_kernel(int M, in
   auto compute = [&](auto st, auto &&hook) {
     bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
     load_frag(st, 0, a0, b0);
+    __builtin_amdgcn_s_setprio(1);  // the products issue ahead of the other wave's memory work
     static_for<0, BK / 16>([&](auto sc) {
       constexpr int s = decltype(sc)::value;
       if constexpr (s % 2 == 0) {
@@ -843,6 +847,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_bf16_tn_kernel(int M, in
         mma(a1, b1, sc, hook);
       }
     });
+    __builtin_amdgcn_s_setprio(0);
   };
   // ring of two stages; the next K-tile's loads go out one at a time between
   // the products of the first half of the current one (see gemm_bf16_lds_kernel)
