@@ -43,7 +43,6 @@ VARIANTS = [
     (2, 1, 128, 6, "bf16"),   # two channels per lane in rotate-in (C a multiple of 128, n_rbf <= 8)
     (4, 2, 128, 3, "bf16"),   # the same with an odd basis count (last basis pair half zero)
     (4, 2, 128, 8, "bf16"),   # the GeSbTe layer's shape (channel pairs, eight basis functions)
-    (4, 2, 256, 8, "bf16"),   # the same with two 128-channel chunks per edge side
     (1, 0, 128, 8, "bf16"),   # channel pairs (bf16, C = 128) at every (lmax, mmax) of the backward row kernel
     (1, 1, 128, 2, "bf16"),
     (2, 0, 128, 8, "bf16"),
