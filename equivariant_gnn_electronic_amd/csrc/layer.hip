@@ -515,19 +515,18 @@ __global__ void __launch_bounds__(kThreads) scatter_in_kernel(const int *__restr
       if constexpr (kPacked) {
 #pragma unroll
         for (int q = 0; q < NRBF / 2; ++q) {
-          // unconditional LDS reads, then selects: no branch per basis function
+          // basis slots past n_rbf hold finite copies (GeomPipe) and meet zero
+          // weights, so they add nothing: no select or branch per basis function
           const float r0 = gr[P::RB + 2 * q], r1 = gr[P::RB + 2 * q + 1];
-          const bf16x2 ph{static_cast<__bf16>(2 * q < n_rbf ? r0 : 0.0f),
-                          static_cast<__bf16>(2 * q + 1 < n_rbf ? r1 : 0.0f)};
+          const bf16x2 ph{static_cast<__bf16>(r0), static_cast<__bf16>(r1)};
 #pragma unroll
           for (int p = 0; p < R::NP; ++p) g[p] = __builtin_amdgcn_fdot2_f32_bf16(ph, wp[q][p], g[p], false);
         }
       } else {
 #pragma unroll
         for (int k = 0; k < NRBF; ++k) {
-          // unconditional LDS read, then select: no branch per basis function
-          const float raw = gr[P::RB + k];
-          const float ph = k < n_rbf ? raw : 0.0f;
+          // (slots past n_rbf: finite values times zero weights)
+          const float ph = gr[P::RB + k];
 #pragma unroll
           for (int p = 0; p < R::NP; ++p) g[p] += ph * wr[k][p];
         }
@@ -616,8 +615,9 @@ __global__ void __launch_bounds__(kThreads) scatter_in_pair_kernel(const int *__
       bf16x2 ph[NRBF / 2];
 #pragma unroll
       for (int q = 0; q < NRBF / 2; ++q) {
+        // (slots past n_rbf: finite values times the zero weights pack_wrad_kernel wrote)
         const float r0 = gr[L::ND + 2 * q], r1 = gr[L::ND + 2 * q + 1];
-        ph[q] = bf16x2{static_cast<__bf16>(2 * q < n_rbf ? r0 : 0.0f), static_cast<__bf16>(2 * q + 1 < n_rbf ? r1 : 0.0f)};
+        ph[q] = bf16x2{static_cast<__bf16>(r0), static_cast<__bf16>(r1)};
       }
       uint32_t *rowp[MMAX + 1];  // wave-uniform row bases; 32-bit lane offsets below
 #pragma unroll
@@ -1486,8 +1486,8 @@ __global__ void __launch_bounds__(kThreads) wrad_grad_kernel(const int *__restri
           }
 #pragma unroll
         for (int k = 0; k < NRBF; ++k) {
-          const float rv = gr[P::RB + k];  // in the staged row; select, no branch
-          const float ph = k < n_rbf ? rv : 0.0f;
+          // in the staged row (finite); sums of slots past n_rbf are never written
+          const float ph = gr[P::RB + k];
 #pragma unroll
           for (int p = 0; p < R::NP; ++p) acc[k][p] += ph * dg[p];
         }
@@ -1607,16 +1607,15 @@ __global__ void __launch_bounds__(kThreads) gather_grad_kernel(const int *__rest
 #pragma unroll
             for (int q = 0; q < NRBF / 2; ++q) {
               const float r0 = gr[P::RB + 2 * q], r1 = gr[P::RB + 2 * q + 1];
-              const bf16x2 ph = {static_cast<__bf16>(2 * q < n_rbf ? r0 : 0.0f),
-                                 static_cast<__bf16>(2 * q + 1 < n_rbf ? r1 : 0.0f)};
+              // (slots past n_rbf: finite values times zero weights)
+              const bf16x2 ph = {static_cast<__bf16>(r0), static_cast<__bf16>(r1)};
 #pragma unroll
               for (int p = 0; p < R::NP; ++p) g[p] = __builtin_amdgcn_fdot2_f32_bf16(ph, wp[q][p], g[p], false);
             }
           } else {
 #pragma unroll
             for (int kk = 0; kk < NRBF; ++kk) {
-              const float rv = gr[P::RB + kk];  // in the staged row; select, no branch
-              const float ph = kk < n_rbf ? rv : 0.0f;
+              const float ph = gr[P::RB + kk];  // (slots past n_rbf: finite values times zero weights)
 #pragma unroll
               for (int p = 0; p < R::NP; ++p) g[p] += ph * wr[kk][p];
             }
