@@ -381,7 +381,9 @@ __global__ void __launch_bounds__(kWave * NW) hblocks_kernel(int slot, int64_t r
 template <int S, typename T>
 void launch_hblocks_nw(int nw, unsigned g, size_t smem, hipStream_t stream, int slot, int64_t rows, const T *irr,
                        int K, const float *W, int n_w, int n_lab, int n_ent, float *H) {
-  if (nw == 4)
+  if (nw == 8)
+    hblocks_kernel<S, 8, T><<<g, kWave * 8, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H);
+  else if (nw == 4)
     hblocks_kernel<S, 4, T><<<g, kWave * 4, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H);
   else if (nw == 2)
     hblocks_kernel<S, 2, T><<<g, kWave * 2, smem, stream>>>(slot, rows, irr, K, W, n_w, n_lab, n_ent, H);
@@ -397,14 +399,28 @@ egnn_status launch_hblocks(int slot, int64_t rows, const void *irreps, int K, in
     return sizeof(float) * (static_cast<size_t>(n_ent + 1) + 2 * n_terms + 4 + static_cast<size_t>(n_w + 16) * (C + 4) +
                             static_cast<size_t>(nw) * kTile * label_stride(n_lab));
   };
-  // the most waves per workgroup whose label tiles fit
-  int nw = 4;
-  while (nw > 1 && smem_for(nw) > 150 * 1024) nw /= 2;
-  const size_t smem = smem_for(nw);
-  if (smem > 150 * 1024) {
-    set_error("decode needs %zu bytes of LDS; reduce C or the shell list", smem);
+  // Waves per workgroup: the count that puts the most waves on a CU, where a
+  // CU's 160 KB of LDS holds whole workgroups (the staged weights are shared
+  // by a workgroup's waves, the label tiles are per wave).  Four waves win
+  // ties.  At C 128 the weights take ~32 KB, so four waves (84 KB) leave room
+  // for one workgroup and eight (130 KB) put twice the waves on the CU.
+  constexpr size_t kCuLds = 160 * 1024, kMaxLds = 150 * 1024;
+  int nw = 0;
+  size_t best = 0;
+  for (const int c : {4, 8, 2, 1}) {
+    const size_t sm = smem_for(c);
+    if (sm > kMaxLds) continue;
+    const size_t waves = static_cast<size_t>(c) * (kCuLds / sm);
+    if (waves > best) {
+      best = waves;
+      nw = c;
+    }
+  }
+  if (nw == 0) {
+    set_error("decode needs %zu bytes of LDS; reduce C or the shell list", smem_for(1));
     return EGNN_E_UNSUPPORTED;
   }
+  const size_t smem = smem_for(nw);
   Timed t(stream, "hblocks", 0.0,
           double(rows) * (double(K) * C * sizeof(T) + double(n_ent) * 4.0) + double(C) * n_w * 4.0);
   int64_t blocks = ((rows + kTile - 1) / kTile + nw - 1) / nw;
