@@ -1048,11 +1048,13 @@ hipError_t launch_bf16(int M, int N, int K, const uint16_t *A, int lda, const ui
           <<<grid, 64 * WM_ * WN_, 0, stream>>>(M, N, K, A, lda, B, ldb, C, ldc, splits, kps, split_stride);    \
   } while (0)
   if (aligned && K % 64 == 0 && waste128 < waste256) {
-    // 256 x 128 x 64, 8 waves (4 x 2, 64 x 64 each), 3 stages (144 KB LDS): N = 640 and the like
-    EGNN_B(256, 128, 64, 4, 2, 3, 1);
+    // 256 x 128 x 64, 8 waves (4 x 2, 64 x 64 each), 3 stages (144 KB LDS): N = 640 and the like;
+    // loop body of two ring rounds
+    EGNN_B(256, 128, 64, 4, 2, 3, 2);
   } else if (aligned && K % 64 == 0) {
-    // 256 x 256 x 64, 8 waves (2 x 4, 128 x 64 each), 2 stages (128 KB LDS): 128-byte rows per load
-    EGNN_B(256, 256, 64, 2, 4, 2, 2);
+    // 256 x 256 x 64, 8 waves (2 x 4, 128 x 64 each), 2 stages (128 KB LDS): 128-byte rows per load;
+    // loop body of four ring rounds (eight K-tiles: 0.5-2.5% faster than four on the layer's shapes)
+    EGNN_B(256, 256, 64, 2, 4, 2, 4);
   } else if (aligned && K % 32 == 0) {
     // 256 x 256 x 32, 4 stages (128 KB LDS), loop body of 4 rings
     EGNN_B(256, 256, 32, 2, 4, 4, 4);
